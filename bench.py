@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Throughput of the sparse MoE layer hot path on one MI355X.
+
+One step = one moe_forward call (router GEMM, softmax/top-k, permute,
+grouped gate|up+SwiGLU and down FFN, combine) over one batch of seeded
+synthetic input already resident in HBM.  W untimed warm-up steps, then
+exactly K timed steps bracketed by torch.cuda.synchronize().  Prints one JSON
+line.
+
+Default workload: one decode step of a Qwen-3.5-like layer (T=64 tokens,
+H=4096, E=512 experts, top-10, I=1024, bf16 experts, fp32 router).
+
+Also reported:
+  roofline      the dominant kernel (largest summed duration), timed with HIP
+                events on its own launch stream over the timed region, against
+                the HBM (or bf16 MFMA) peak; traffic from committed rocprofv3
+                counter summaries when they match the current kernel source.
+  cpu_baseline  the CPU oracle timed on this host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", default="decode",
+                   help="workload: decode (default), prefill, prefill_long, skew, ling, tiny")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample", type=int, default=64, help="tokens in the oracle's sample")
+    p.add_argument("--no-copy-calibration", action="store_true",
+                   help="skip the untimed 1 GiB reference copy used to scale rocprof counters")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "expert_ffn_layer_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel: str, workload: str, src_hash: str):
+    """HBM bytes per launch from profiles/<kernel>__<workload>.traffic.json,
+    or None when absent or taken on a different kernel source."""
+    path = os.path.join(PROFILES, f"{kernel}__{workload}.traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from expert_ffn_layer_amd import moe, synth
+
+    cfg = synth.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] workload {synth.workload_name(cfg)}: generating", file=sys.stderr, flush=True)
+    layer = synth.make_layer(cfg, seed=args.seed, device=dev)
+    if cfg.fp32_values:
+        layer = layer.rounded_to_bf16()
+    m = moe.MoELayer(layer)
+    s = m.shape
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=dev)
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
+    w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
+    counts = torch.empty((cfg.E,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        moe.forward(s, layer.x, layer.wg, layer.bias, layer.w_gu, layer.w_dn, layer.ws_gu,
+                    layer.ws_dn, out, m.workspace, ids, w, counts, stream=stream)
+
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+
+    # Untimed pass: per-kernel durations, to name the dominant kernel.
+    per_kernel = {}
+    for name in moe.KERNELS:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(2)]
+        for a, b in ev:
+            moe.profile_kernel(name, a, b)
+            step()
+        moe.profile_kernel(None)
+        torch.cuda.synchronize()
+        try:
+            per_kernel[name] = sum(a.elapsed_time(b) for a, b in ev) / len(ev) * 1e3  # us
+        except RuntimeError:
+            pass  # not launched for this workload
+    dominant = max(per_kernel, key=per_kernel.get)
+
+    # Timed region: K steps; the dominant kernel bracketed by events each step.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps (dominant kernel {dominant})", file=sys.stderr,
+          flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        moe.profile_kernel(dominant, a, b)
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    moe.profile_kernel(None)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kern_us = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3
+    value = cfg.T / (ms_per_step / 1e3)
+
+    # Algorithmic work, from this run's own routing.
+    cnt = counts.cpu().numpy().astype(np.int64)
+    touched = int((cnt > 0).sum())
+    light_rows = int(cnt[(cnt > 0) & (cnt <= 16)].sum())
+    light_experts = int(((cnt > 0) & (cnt <= 16)).sum())
+    A = cfg.T * cfg.k
+    H, I = cfg.H, cfg.I
+    x_bytes = cfg.T * H * 2
+    if dominant == "gateup_light":
+        alg = light_experts * 2 * I * H * 2 + x_bytes + light_rows * I * 2
+        flops = 4 * light_rows * H * I
+    elif dominant == "down_light":
+        alg = light_experts * H * I * 2 + light_rows * (I + H) * 2
+        flops = 2 * light_rows * H * I
+    elif dominant == "gateup_heavy":
+        he = touched - light_experts
+        hr = A - light_rows
+        alg = he * 2 * I * H * 2 + x_bytes + hr * I * 2
+        flops = 4 * hr * H * I
+    elif dominant == "down_heavy":
+        he = touched - light_experts
+        hr = A - light_rows
+        alg = he * H * I * 2 + hr * (I + H) * 2
+        flops = 2 * hr * H * I
+    elif dominant == "router_gemm":
+        alg = x_bytes + H * cfg.E * 4
+        flops = 2 * cfg.T * H * cfg.E
+    else:
+        alg, flops = 0, 0
+    t_k = kern_us * 1e-6
+    t_hbm = alg / (HBM_PEAK_GBS * 1e9)
+    peak_flops = FP32_PEAK_TFLOPS if dominant == "router_gemm" else BF16_PEAK_TFLOPS
+    t_mfma = flops / (peak_flops * 1e12)
+    src_hash = kernel_source_hash()
+    workload = synth.workload_name(cfg)
+    traffic = committed_traffic(dominant, workload, src_hash)
+    if t_mfma > t_hbm:
+        achieved = flops / t_k / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_flops,
+                "unit": "TFLOP/s", "frac": round(achieved / peak_flops, 4)}
+    else:
+        achieved = alg / t_k / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof.update({"traffic": traffic, "kernel": dominant, "kernel_us": round(kern_us, 2),
+                 "algorithmic_bytes": int(alg), "flops": int(flops)})
+
+    # Whole-layer roofline (weights of touched experts + x + router + out).
+    layer_bytes = touched * 3 * H * I * 2 + x_bytes + H * cfg.E * 4 + cfg.T * H * 4
+    if cfg.I_shared:
+        layer_bytes += 3 * H * cfg.I_shared * 2
+    layer_flops = 6 * A * H * I + (6 * cfg.T * H * cfg.I_shared if cfg.I_shared else 0)
+    t_step = ms_per_step / 1e3
+    layer = dict(hbm_frac=round(layer_bytes / t_step / (HBM_PEAK_GBS * 1e9), 4),
+                 mfma_frac=round(layer_flops / t_step / (BF16_PEAK_TFLOPS * 1e12), 4),
+                 algorithmic_bytes=int(layer_bytes), expert_flops=int(layer_flops),
+                 touched_experts=touched, light_experts=light_experts)
+
+    # Untimed reference copy: 1 GiB read + 1 GiB written by one elementwise
+    # kernel, the yardstick for rocprof FETCH_SIZE / WRITE_SIZE.
+    if not args.no_copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(layer_obj=m.layer, cfg=cfg, n=args.cpu_sample, gpu_out=out)
+
+    rec = {
+        "metric": "MoE-layer tokens/s",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal draws, random-init weights)",
+        "config": {"workload": workload, "tokens": cfg.T, "hidden": H, "experts": cfg.E,
+                   "top_k": cfg.k, "intermediate": I, "shared_intermediate": cfg.I_shared,
+                   "seed": args.seed},
+        "roofline": roof,
+        "layer_roofline": layer,
+        "kernels_us": {k: round(v, 2) for k, v in per_kernel.items()},
+        "kernel_source_hash": src_hash,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(layer_obj, cfg, n, gpu_out):
+    """The oracle (plain fp32 C loops, OpenMP over rows) on the first n tokens
+    of the same layer, weights already on the host; also reports its
+    agreement with the GPU output on those tokens."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    n = min(n, cfg.T)
+    o = oracle.Oracle()
+    x = layer_obj.x[:n].cpu()
+    wg = layer_obj.wg.cpu()
+    bias = None if layer_obj.bias is None else layer_obj.bias.cpu()
+    print(f"[bench] cpu baseline: copying weights to host", file=sys.stderr, flush=True)
+    w_gu = layer_obj.w_gu.cpu()
+    w_dn = layer_obj.w_dn.cpu()
+    ws_gu = None if layer_obj.ws_gu is None else layer_obj.ws_gu.cpu()
+    ws_dn = None if layer_obj.ws_dn is None else layer_obj.ws_dn.cpu()
+    print(f"[bench] cpu baseline: oracle on {n} tokens", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    ref = o.forward(x, wg, bias, w_gu, w_dn, cfg.k, cfg.renorm, ws_gu, ws_dn, permute=False)
+    wall = time.perf_counter() - t0
+    g = gpu_out[:n].cpu().numpy().astype(np.float64)
+    d = g - ref["out"].astype(np.float64)
+    del w_gu, w_dn
+    torch.cuda.synchronize()
+    return {"value": round(n / wall, 3), "unit": "tokens/s", "cores": o.max_threads(),
+            "kind": "oracle",
+            "sample": f"first {n} of {cfg.T} tokens of the same layer (routing, all their expert "
+                      f"FFN rows, combine); fp32 C loops; expert weights pre-copied to host",
+            "wall_s": round(wall, 3),
+            "gpu_vs_oracle": {"max_abs": float(np.abs(d).max()),
+                              "rel_l2": float(np.linalg.norm(d) / np.linalg.norm(ref["out"]))}}
+
+
+if __name__ == "__main__":
+    main()

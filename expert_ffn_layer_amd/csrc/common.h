@@ -1,0 +1,75 @@
+// Device-side helpers shared by the MoE kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t v16) {
+    return __uint_as_float(v16 << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// 16-byte global load of 8 bf16 values as an MFMA operand.
+__device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t* p) {
+    return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
+}
+
+__device__ __forceinline__ bf16x8_t zero_bf16x8() {
+    return __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u});
+}
+
+// D = A(16x32) * B(32x16) + C on bf16 inputs, fp32 accumulate.
+// Lane l supplies A row (l % 16), B column (l % 16), both at K slots
+// 8*(l/16) .. 8*(l/16)+7; D lane l holds rows 4*(l/16)+r, column l % 16.
+__device__ __forceinline__ floatx4_t mfma_16x16x32(bf16x8_t a, bf16x8_t b, floatx4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// SwiGLU of one (gate, up) pair.  Every path that produces h uses this one
+// function, so the light and heavy loops round identically.
+__device__ __forceinline__ float swiglu(float g, float u) {
+#pragma clang fp contract(off)
+    const float s = g / (1.0f + expf(-g));
+    return s * u;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const T w = __shfl_xor(v, o, kWave);
+        v = w > v ? w : v;
+    }
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) {
+    return (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+}
+
+}  // namespace moe

@@ -1,0 +1,395 @@
+// C ABI of libmoe.so: argument validation, workspace carving and kernel
+// launches on the caller's stream.  No allocation, no host synchronisation,
+// no reads of device memory on the host.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+
+#include "launch.h"
+#include "moe.h"
+
+static_assert((int)moe::K_COUNT == (int)MOE_K_COUNT, "kernel ids out of sync");
+static_assert((int)moe::K_GATEUP_LIGHT == (int)MOE_K_GATEUP_LIGHT, "kernel ids out of sync");
+static_assert((int)moe::K_COMBINE == (int)MOE_K_COMBINE, "kernel ids out of sync");
+
+namespace moe {
+ProfileHook g_profile;
+}
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+    g_last_error = msg;
+    return code;
+}
+
+constexpr size_t kAlign = 256;
+
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+    int splits = 1, nchunks = 1, light_max = 16, max_tiles = 0, max_light = 0;
+    size_t part = 0, ids = 0, w = 0, chunk = 0, counts = 0, offsets = 0, sorted = 0, inv = 0,
+           plan = 0, h = 0, y = 0, hs = 0, total = 0;
+};
+
+int router_splits(int T, int H, int E) {
+    const long long base = (long long)((E + moe::kRouterBE - 1) / moe::kRouterBE) *
+                           ((T + moe::kRouterBT - 1) / moe::kRouterBT);
+    int s = 1;
+    while (base * s < 512 && H % (2 * s * moe::kRouterBK) == 0 && H / (2 * s) >= 64) s *= 2;
+    return s;
+}
+
+int check_shape(const moe_shape* s) {
+    if (!s) return fail(MOE_ERR_NULL, "shape is NULL");
+    if (s->T < 0 || s->H <= 0 || s->E <= 0 || s->k <= 0 || s->I <= 0 || s->I_shared < 0)
+        return fail(MOE_ERR_SHAPE, "sizes must be T >= 0 and H, E, k, I > 0, I_shared >= 0");
+    if (s->k > s->E) return fail(MOE_ERR_SHAPE, "k > E");
+    if ((long long)s->T * s->k >= (1LL << 31)) return fail(MOE_ERR_SHAPE, "T*k >= 2^31");
+    if ((long long)s->T * s->H >= (1LL << 40)) return fail(MOE_ERR_SHAPE, "T*H too large");
+    if (s->H % 64) return fail(MOE_ERR_UNSUPPORTED, "H must be a multiple of 64");
+    if (s->I % 32) return fail(MOE_ERR_UNSUPPORTED, "I must be a multiple of 32");
+    if (s->I_shared % 32) return fail(MOE_ERR_UNSUPPORTED, "I_shared must be a multiple of 32");
+    if (s->E > 1024) return fail(MOE_ERR_UNSUPPORTED, "E must be <= 1024");
+    if (s->k > 32) return fail(MOE_ERR_UNSUPPORTED, "k must be <= 32");
+    if (s->renorm != 0 && s->renorm != 1) return fail(MOE_ERR_UNSUPPORTED, "renorm must be 0 or 1");
+    if (s->light_max_rows < -1 || s->light_max_rows > moe::kLightRowsMax)
+        return fail(MOE_ERR_UNSUPPORTED, "light_max_rows must be -1 or in [0, 16]");
+    return MOE_OK;
+}
+
+Layout layout(const moe_shape* s) {
+    Layout L;
+    const long long T = s->T, H = s->H, E = s->E, k = s->k, I = s->I, A = T * k;
+    L.splits = router_splits(s->T, s->H, s->E);
+    L.nchunks = (int)std::max<long long>(1, (A + moe::kPermChunk - 1) / moe::kPermChunk);
+    L.light_max = s->light_max_rows < 0 ? moe::kLightRowsMax : s->light_max_rows;
+    L.max_tiles = moe::max_heavy_tiles(A, s->E, L.light_max);
+    L.max_light = L.light_max > 0 ? (int)std::min<long long>(E, A) : 0;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += up(bytes);
+        return at;
+    };
+    L.part = take((size_t)L.splits * T * E * 4);
+    L.ids = take((size_t)A * 4);
+    L.w = take((size_t)A * 4);
+    L.chunk = take((size_t)L.nchunks * E * 4);
+    L.counts = take((size_t)E * 4);
+    L.offsets = take((size_t)(E + 1) * 4);
+    L.sorted = take((size_t)A * 4);
+    L.inv = take((size_t)A * 4);
+    L.plan = take((size_t)(moe::kPlanHeader + E + 2LL * L.max_tiles) * 4);
+    L.h = take((size_t)A * I * 2);
+    L.y = take((size_t)A * H * 2);
+    L.hs = take((size_t)T * s->I_shared * 2);
+    L.total = off;
+    return L;
+}
+
+bool aligned(const void* p, size_t a = 16) { return ((uintptr_t)p % a) == 0; }
+
+int check_ws(const moe_shape* s, const void* ws, size_t ws_bytes) {
+    if (!ws) return fail(MOE_ERR_NULL, "workspace is NULL");
+    if (!aligned(ws, kAlign)) return fail(MOE_ERR_ALIGN, "workspace must be 256-byte aligned");
+    const size_t need = layout(s).total;
+    if (ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) +
+                                           " bytes, got " + std::to_string(ws_bytes));
+    return MOE_OK;
+}
+
+#define REQUIRE_PTR(p)                                                     \
+    do {                                                                   \
+        if (!(p)) return fail(MOE_ERR_NULL, #p " is NULL");                \
+        if (!aligned(p)) return fail(MOE_ERR_ALIGN, #p " is not 16-byte aligned"); \
+    } while (0)
+#define OPTIONAL_PTR(p)                                                    \
+    do {                                                                   \
+        if ((p) && !aligned(p)) return fail(MOE_ERR_ALIGN, #p " is not 16-byte aligned"); \
+    } while (0)
+#define HIP_TRY(expr, what)                                                \
+    do {                                                                   \
+        hipError_t e_ = (expr);                                            \
+        if (e_ != hipSuccess)                                              \
+            return fail(MOE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e_)); \
+    } while (0)
+
+int device_cu_count(int* out) {
+    static std::mutex mu;
+    static std::unordered_map<int, int> cache;
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(dev);
+    if (it == cache.end()) {
+        int n = 0;
+        HIP_TRY(hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev),
+                "hipDeviceGetAttribute");
+        it = cache.emplace(dev, std::max(n, 1)).first;
+    }
+    *out = it->second;
+    return MOE_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+    return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+int run_router(const moe_shape* s, const Layout& L, const uint16_t* x, const float* wr,
+               const float* bias, int32_t* ids, float* w, float* probs, void* ws,
+               hipStream_t st) {
+    float* part = at<float>(ws, L.part);
+    HIP_TRY(moe::launch_router_gemm(x, wr, part, s->T, s->H, s->E, L.splits, st), "router gemm");
+    HIP_TRY(moe::launch_router_select(part, L.splits, bias, s->T, s->E, s->k, s->renorm, ids, w,
+                                      probs, st),
+            "router select");
+    return MOE_OK;
+}
+
+int run_permute(const moe_shape* s, const Layout& L, const int32_t* ids, int32_t* counts,
+                int32_t* offsets, int32_t* sorted, int32_t* inv, void* ws, hipStream_t st) {
+    HIP_TRY(moe::launch_permute(ids, s->T, s->k, s->E, at<int32_t>(ws, L.chunk), L.nchunks,
+                                counts, offsets, sorted, inv, st),
+            "permute");
+    return MOE_OK;
+}
+
+int run_ffn(const moe_shape* s, const Layout& L, const uint16_t* x, const int32_t* sorted,
+            const int32_t* offsets, const uint16_t* wgu, const uint16_t* wdn, uint16_t* h,
+            uint16_t* y, void* ws, hipStream_t st) {
+    int ncu = 0;
+    if (int rc = device_cu_count(&ncu)) return rc;
+    int32_t* plan = at<int32_t>(ws, L.plan);
+    HIP_TRY(moe::launch_ffn_plan(offsets, s->E, L.light_max, plan, st), "ffn plan");
+    moe::FfnArgs a{};
+    a.x = x;
+    a.sorted_ids = sorted;
+    a.offsets = offsets;
+    a.w_gu = wgu;
+    a.w_dn = wdn;
+    a.h = h ? h : at<uint16_t>(ws, L.h);
+    a.y = y;
+    a.y32 = nullptr;
+    a.plan = plan;
+    a.T = s->T;
+    a.H = s->H;
+    a.I = s->I;
+    a.E = s->E;
+    a.dense_rows = 0;
+    a.max_tiles = L.max_tiles;
+    a.max_light = L.max_light;
+    a.num_cu = ncu;
+    HIP_TRY(moe::launch_ffn_gateup(a, st), "ffn gate|up");
+    HIP_TRY(moe::launch_ffn_down(a, st), "ffn down");
+    return MOE_OK;
+}
+
+int run_shared(const moe_shape* s, const Layout& L, const uint16_t* x, const uint16_t* wgu,
+               const uint16_t* wdn, float* out, void* ws, hipStream_t st) {
+    int ncu = 0;
+    if (int rc = device_cu_count(&ncu)) return rc;
+    moe::FfnArgs a{};
+    a.x = x;
+    a.sorted_ids = nullptr;
+    a.offsets = nullptr;
+    a.w_gu = wgu;
+    a.w_dn = wdn;
+    a.h = at<uint16_t>(ws, L.hs);
+    a.y = nullptr;
+    a.y32 = out;
+    a.plan = nullptr;
+    a.T = s->T;
+    a.H = s->H;
+    a.I = s->I_shared;
+    a.E = 1;
+    a.dense_rows = s->T;
+    a.max_tiles = 0;
+    a.max_light = 0;
+    a.num_cu = ncu;
+    HIP_TRY(moe::launch_ffn_gateup(a, st), "shared gate|up");
+    HIP_TRY(moe::launch_ffn_down(a, st), "shared down");
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_shape* shape) {
+    if (check_shape(shape) != MOE_OK) return 0;
+    return layout(shape).total;
+}
+
+const char* moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_NULL: return "a required pointer is NULL";
+        case MOE_ERR_SHAPE: return "invalid shape";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape";
+        case MOE_ERR_ALIGN: return "misaligned pointer";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int moe_profile_kernel(int kernel, void* start, void* stop) {
+    g_last_error.clear();
+    if (kernel == -1) {
+        moe::g_profile = moe::ProfileHook{};
+        return MOE_OK;
+    }
+    if (kernel < 0 || kernel >= MOE_K_COUNT) return fail(MOE_ERR_SHAPE, "unknown kernel id");
+    if (!start || !stop) return fail(MOE_ERR_NULL, "profile events are NULL");
+    moe::g_profile.kernel = kernel;
+    moe::g_profile.start = (hipEvent_t)start;
+    moe::g_profile.stop = (hipEvent_t)stop;
+    return MOE_OK;
+}
+
+int moe_router(const moe_shape* shape, const uint16_t* x, const float* w_router,
+               const float* bias, int32_t* topk_ids, float* topk_w, float* probs,
+               void* workspace, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    if (int rc = check_shape(shape)) return rc;
+    if (shape->T == 0) return MOE_OK;
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(w_router);
+    REQUIRE_PTR(topk_ids);
+    REQUIRE_PTR(topk_w);
+    OPTIONAL_PTR(bias);
+    OPTIONAL_PTR(probs);
+    if (int rc = check_ws(shape, workspace, ws_bytes)) return rc;
+    return run_router(shape, layout(shape), x, w_router, bias, topk_ids, topk_w, probs, workspace,
+                      (hipStream_t)stream);
+}
+
+int moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t* counts,
+                int32_t* offsets, int32_t* sorted_token_ids, int32_t* inv_pos, void* workspace,
+                size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    if (int rc = check_shape(shape)) return rc;
+    REQUIRE_PTR(counts);
+    REQUIRE_PTR(offsets);
+    if (shape->T > 0) {
+        REQUIRE_PTR(topk_ids);
+        REQUIRE_PTR(sorted_token_ids);
+        REQUIRE_PTR(inv_pos);
+    }
+    if (int rc = check_ws(shape, workspace, ws_bytes)) return rc;
+    return run_permute(shape, layout(shape), topk_ids, counts, offsets, sorted_token_ids, inv_pos,
+                       workspace, (hipStream_t)stream);
+}
+
+int moe_grouped_ffn(const moe_shape* shape, const uint16_t* x, const int32_t* sorted_token_ids,
+                    const int32_t* offsets, const uint16_t* w_gate_up, const uint16_t* w_down,
+                    uint16_t* h, uint16_t* y, void* workspace, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    if (int rc = check_shape(shape)) return rc;
+    if (shape->T == 0) return MOE_OK;
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(sorted_token_ids);
+    REQUIRE_PTR(offsets);
+    REQUIRE_PTR(w_gate_up);
+    REQUIRE_PTR(w_down);
+    REQUIRE_PTR(y);
+    OPTIONAL_PTR(h);
+    if (int rc = check_ws(shape, workspace, ws_bytes)) return rc;
+    return run_ffn(shape, layout(shape), x, sorted_token_ids, offsets, w_gate_up, w_down, h, y,
+                   workspace, (hipStream_t)stream);
+}
+
+int moe_shared_ffn(const moe_shape* shape, const uint16_t* x, const uint16_t* ws_gate_up,
+                   const uint16_t* ws_down, float* out, void* workspace, size_t ws_bytes,
+                   void* stream) {
+    g_last_error.clear();
+    if (int rc = check_shape(shape)) return rc;
+    if (shape->I_shared <= 0) return fail(MOE_ERR_SHAPE, "moe_shared_ffn needs I_shared > 0");
+    if (shape->T == 0) return MOE_OK;
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(ws_gate_up);
+    REQUIRE_PTR(ws_down);
+    REQUIRE_PTR(out);
+    if (int rc = check_ws(shape, workspace, ws_bytes)) return rc;
+    return run_shared(shape, layout(shape), x, ws_gate_up, ws_down, out, workspace,
+                      (hipStream_t)stream);
+}
+
+int moe_combine(const moe_shape* shape, const uint16_t* y, const int32_t* inv_pos,
+                const float* topk_w, int32_t accumulate, float* out, void* stream) {
+    g_last_error.clear();
+    if (int rc = check_shape(shape)) return rc;
+    if (shape->T == 0) return MOE_OK;
+    REQUIRE_PTR(y);
+    REQUIRE_PTR(inv_pos);
+    REQUIRE_PTR(topk_w);
+    REQUIRE_PTR(out);
+    HIP_TRY(moe::launch_combine(y, inv_pos, topk_w, shape->T, shape->H, shape->k,
+                                accumulate ? 1 : 0, out, (hipStream_t)stream),
+            "combine");
+    return MOE_OK;
+}
+
+int moe_forward(const moe_shape* shape, const uint16_t* x, const float* w_router,
+                const float* bias, const uint16_t* w_gate_up, const uint16_t* w_down,
+                const uint16_t* ws_gate_up, const uint16_t* ws_down, float* out,
+                int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, void* workspace,
+                size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    if (int rc = check_shape(shape)) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    if (shape->T == 0) {
+        // Nothing routed: only the optional counts are written (all zero).
+        OPTIONAL_PTR(counts_out);
+        if (!counts_out) return MOE_OK;
+        if (int rc = check_ws(shape, workspace, ws_bytes)) return rc;
+        const Layout L0 = layout(shape);
+        return run_permute(shape, L0, nullptr, counts_out, at<int32_t>(workspace, L0.offsets),
+                           nullptr, nullptr, workspace, st);
+    }
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(w_router);
+    REQUIRE_PTR(w_gate_up);
+    REQUIRE_PTR(w_down);
+    REQUIRE_PTR(out);
+    OPTIONAL_PTR(bias);
+    OPTIONAL_PTR(topk_ids_out);
+    OPTIONAL_PTR(topk_w_out);
+    OPTIONAL_PTR(counts_out);
+    if (shape->I_shared > 0) {
+        REQUIRE_PTR(ws_gate_up);
+        REQUIRE_PTR(ws_down);
+    }
+    if (int rc = check_ws(shape, workspace, ws_bytes)) return rc;
+    const Layout L = layout(shape);
+    int32_t* counts = counts_out ? counts_out : at<int32_t>(workspace, L.counts);
+    int32_t* offsets = at<int32_t>(workspace, L.offsets);
+    int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(workspace, L.ids);
+    float* w = topk_w_out ? topk_w_out : at<float>(workspace, L.w);
+    int32_t* sorted = at<int32_t>(workspace, L.sorted);
+    int32_t* inv = at<int32_t>(workspace, L.inv);
+    uint16_t* y = at<uint16_t>(workspace, L.y);
+    if (int rc = run_router(shape, L, x, w_router, bias, ids, w, nullptr, workspace, st)) return rc;
+    if (int rc = run_permute(shape, L, ids, counts, offsets, sorted, inv, workspace, st)) return rc;
+    if (int rc = run_ffn(shape, L, x, sorted, offsets, w_gate_up, w_down, nullptr, y, workspace, st))
+        return rc;
+    if (shape->I_shared > 0)
+        if (int rc = run_shared(shape, L, x, ws_gate_up, ws_down, out, workspace, st)) return rc;
+    HIP_TRY(moe::launch_combine(y, inv, w, shape->T, shape->H, shape->k, shape->I_shared > 0 ? 1 : 0,
+                                out, st),
+            "combine");
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,180 @@
+// Permute: histogram -> exclusive scan -> stable scatter of the routed rows.
+//
+// Only int32 row indices move; activation rows are gathered later inside
+// the expert GEMM, so no padded [E x capacity] buffer ever exists (the pages
+// gather routed token rows into a contiguous buffer without materialising a
+// padded intermediate because top_k = 10 is not a power of 2: pwwt.cn
+// article on Qwen 3.5-397B MoE on Ironwood, section 4.2).
+//
+// Assignments a = t*k + j are split into chunks of kPermChunk.  Block c
+// counts its chunk (LDS integer atomics: the count does not depend on
+// order); one block turns the [chunk][expert] counts into the global
+// offsets and each chunk's first slot per expert; block c then ranks its
+// chunk's assignments in assignment order (wave ballots match equal expert
+// ids) and writes each to its slot.  Integer arithmetic throughout, so the
+// result is exact and deterministic.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kPerThread = kPermChunk / kThreads;  // 16
+constexpr int kWavesPerBlock = kThreads / 64;
+
+__device__ __forceinline__ bool valid_id(int e, int E) { return e >= 0 && e < E; }
+
+__global__ __launch_bounds__(kThreads) void perm_count_kernel(const int32_t* __restrict__ ids,
+                                                             long long A, int E,
+                                                             int32_t* __restrict__ chunk_counts) {
+    extern __shared__ int32_t cnt[];
+    for (int e = threadIdx.x; e < E; e += kThreads) cnt[e] = 0;
+    __syncthreads();
+    const long long base = (long long)blockIdx.x * kPermChunk;
+#pragma unroll 4
+    for (int q = 0; q < kPerThread; ++q) {
+        const long long a = base + q * kThreads + threadIdx.x;
+        if (a < A) {
+            const int e = ids[a];
+            if (valid_id(e, E)) atomicAdd(&cnt[e], 1);
+        }
+    }
+    __syncthreads();
+    int32_t* out = chunk_counts + (size_t)blockIdx.x * E;
+    for (int e = threadIdx.x; e < E; e += kThreads) out[e] = cnt[e];
+}
+
+// Single block, one thread per expert (E <= 1024).
+// In: chunk_counts[c][e].  Out: counts[e], offsets[0..E], and
+// chunk_counts[c][e] replaced by the first slot of chunk c's rows of e.
+__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ chunk_counts,
+                                                         int nchunks, int E,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets) {
+    __shared__ int32_t wsum[16];
+    const int e = threadIdx.x;
+    int run = 0;
+    if (e < E) {
+        int c = 0;
+        for (; c + 8 <= nchunks; c += 8) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = chunk_counts[(size_t)(c + u) * E + e];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                chunk_counts[(size_t)(c + u) * E + e] = run;
+                run += v[u];
+            }
+        }
+        for (; c < nchunks; ++c) {
+            const int v = chunk_counts[(size_t)c * E + e];
+            chunk_counts[(size_t)c * E + e] = run;
+            run += v;
+        }
+        counts[e] = run;
+    }
+    // Block-wide exclusive scan of run over e.
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    const int excl = before + incl - run;
+    if (e < E) {
+        offsets[e] = excl;
+        if (e == E - 1) offsets[E] = excl + run;
+#pragma unroll 8
+        for (int c = 0; c < nchunks; ++c) chunk_counts[(size_t)c * E + e] += excl;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void perm_scatter_kernel(
+    const int32_t* __restrict__ ids, long long A, int k, int E, int nbits,
+    const int32_t* __restrict__ chunk_base, int32_t* __restrict__ sorted_ids,
+    int32_t* __restrict__ inv_pos) {
+    extern __shared__ int32_t wcnt[];  // [kWavesPerBlock][E]
+    for (int i = threadIdx.x; i < kWavesPerBlock * E; i += kThreads) wcnt[i] = 0;
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const long long base = (long long)blockIdx.x * kPermChunk + (long long)wave * (kPermChunk / kWavesPerBlock);
+    const uint64_t lt = lanemask_lt(lane);
+    int32_t* my = wcnt + wave * E;
+
+    int local[kPerThread];
+    int eid[kPerThread];
+    // Each wave walks its quarter of the chunk in assignment order, 64 at a
+    // time; lanes holding the same expert id are matched with ballots.  The
+    // group's last lane advances my[e] for the next 64; a wave's own LDS
+    // accesses complete in program order.
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+        const long long a = base + (long long)q * 64 + lane;
+        const int e = (a < A) ? ids[a] : -1;
+        const bool ok = valid_id(e, E);
+        uint64_t match = __ballot(ok);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t bal = __ballot(bit);
+            match &= bit ? bal : ~bal;
+        }
+        const int rank = __popcll(match & lt);
+        const int n = __popcll(match);
+        int loc = 0;
+        if (ok) {
+            loc = my[e] + rank;
+            if (rank == n - 1) my[e] = loc + 1;
+        }
+        local[q] = loc;
+        eid[q] = ok ? e : -1;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+        const long long a = base + (long long)q * 64 + lane;
+        if (a >= A) continue;
+        const int e = eid[q];
+        if (e < 0) {
+            inv_pos[a] = -1;
+            continue;
+        }
+        int pos = chunk_base[(size_t)blockIdx.x * E + e] + local[q];
+        for (int w = 0; w < wave; ++w) pos += wcnt[w * E + e];
+        sorted_ids[pos] = (int32_t)a / k;
+        inv_pos[a] = pos;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* chunk_counts,
+                          int nchunks, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
+                          int32_t* inv_pos, hipStream_t st) {
+    const long long A = (long long)T * k;
+    int nbits = 1;
+    while ((1 << nbits) < E) ++nbits;
+    prof_begin(K_PERM_COUNT, st);
+    perm_count_kernel<<<nchunks, kThreads, E * sizeof(int32_t), st>>>(ids, A, E, chunk_counts);
+    prof_end(K_PERM_COUNT, st);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    prof_begin(K_PERM_SCAN, st);
+    perm_scan_kernel<<<1, 1024, 0, st>>>(chunk_counts, nchunks, E, counts, offsets);
+    prof_end(K_PERM_SCAN, st);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    prof_begin(K_PERM_SCATTER, st);
+    perm_scatter_kernel<<<nchunks, kThreads, kWavesPerBlock * E * sizeof(int32_t), st>>>(
+        ids, A, k, E, nbits, chunk_counts, sorted_ids, inv_pos);
+    prof_end(K_PERM_SCATTER, st);
+    return hipGetLastError();
+}
+
+}  // namespace moe

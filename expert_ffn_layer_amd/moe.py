@@ -1,0 +1,238 @@
+"""ctypes binding of libmoe.so (declared in include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  Tensors are torch tensors on the current HIP device; bf16 tensors
+are passed as their raw 16-bit patterns.  The binding checks dtypes, devices,
+contiguity and sizes against the shape (the C ABI cannot see buffer sizes),
+then calls the entry point of the same name on the current torch stream.
+Importing this module does not load the library; the first call does, and
+raises if ``libmoe.so`` has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+MOE_OK = 0
+MOE_ERR_NULL = 1
+MOE_ERR_SHAPE = 2
+MOE_ERR_UNSUPPORTED = 3
+MOE_ERR_ALIGN = 4
+MOE_ERR_WORKSPACE = 5
+MOE_ERR_HIP = 6
+
+EXPORTED = ("moe_workspace_bytes", "moe_status_string", "moe_last_error", "moe_router",
+            "moe_permute", "moe_grouped_ffn", "moe_shared_ffn", "moe_combine", "moe_forward",
+            "moe_profile_kernel")
+
+# enum moe_kernel
+KERNELS = ("router_gemm", "router_select", "perm_count", "perm_scan", "perm_scatter", "ffn_plan",
+           "gateup_light", "gateup_heavy", "down_light", "down_heavy", "combine")
+KERNEL_ID = {n: i for i, n in enumerate(KERNELS)}
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("I", ctypes.c_int32), ("I_shared", ctypes.c_int32),
+                ("renorm", ctypes.c_int32), ("light_max_rows", ctypes.c_int32)]
+
+    def __repr__(self):
+        return ("MoeShape(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__(text)
+        self.status = status
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_sp = ctypes.POINTER(MoeShape)
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m expert_ffn_layer_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.moe_workspace_bytes.argtypes = [_sp]
+        L.moe_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_last_error.argtypes = []
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_router.argtypes = [_sp] + [_vp] * 7 + [ctypes.c_size_t, _vp]
+        L.moe_permute.argtypes = [_sp] + [_vp] * 6 + [ctypes.c_size_t, _vp]
+        L.moe_grouped_ffn.argtypes = [_sp] + [_vp] * 8 + [ctypes.c_size_t, _vp]
+        L.moe_shared_ffn.argtypes = [_sp] + [_vp] * 5 + [ctypes.c_size_t, _vp]
+        L.moe_combine.argtypes = [_sp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp]
+        L.moe_forward.argtypes = [_sp] + [_vp] * 12 + [ctypes.c_size_t, _vp]
+        L.moe_profile_kernel.argtypes = [ctypes.c_int, _vp, _vp]
+        for name in ("moe_router", "moe_permute", "moe_grouped_ffn", "moe_shared_ffn",
+                     "moe_combine", "moe_forward", "moe_profile_kernel"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+def last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != MOE_OK:
+        raise MoeError(rc, f"{status_string(rc)}: {last_error()}")
+
+
+def make_shape(T, H, E, k, I, I_shared=0, renorm=1, light_max_rows=-1) -> MoeShape:
+    return MoeShape(T, H, E, k, I, I_shared, renorm, light_max_rows)
+
+
+def workspace_bytes(shape: MoeShape) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(shape)))
+
+
+def alloc_workspace(shape: MoeShape, device=None) -> torch.Tensor:
+    n = workspace_bytes(shape)
+    if n == 0:
+        raise MoeError(MOE_ERR_SHAPE, f"invalid shape {shape}")
+    return torch.empty(n, dtype=torch.uint8, device=device or torch.device("cuda"))
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype, numel: Optional[int] = None,
+         optional: bool = False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
+    return t.data_ptr()
+
+
+def _ws(ws: torch.Tensor, shape: MoeShape):
+    need = workspace_bytes(shape)
+    if ws is None or not ws.is_cuda or ws.dtype != torch.uint8:
+        raise ValueError("workspace must be a uint8 device tensor")
+    if ws.numel() < need:
+        raise MoeError(MOE_ERR_WORKSPACE, f"workspace has {ws.numel()} bytes, needs {need}")
+    return ws.data_ptr(), ws.numel()
+
+
+def _stream(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+BF16, F32, I32 = torch.bfloat16, torch.float32, torch.int32
+
+
+def router(shape, x, w_router, bias, topk_ids, topk_w, probs, workspace, stream=None):
+    T, H, E, k = shape.T, shape.H, shape.E, shape.k
+    args = [_ptr(x, "x", BF16, T * H), _ptr(w_router, "w_router", F32, H * E),
+            _ptr(bias, "bias", F32, E, optional=True), _ptr(topk_ids, "topk_ids", I32, T * k),
+            _ptr(topk_w, "topk_w", F32, T * k), _ptr(probs, "probs", F32, T * E, optional=True)]
+    wp, wn = _ws(workspace, shape)
+    _check(lib().moe_router(ctypes.byref(shape), *args, wp, wn, _stream(stream)))
+
+
+def permute(shape, topk_ids, counts, offsets, sorted_token_ids, inv_pos, workspace, stream=None):
+    A, E = shape.T * shape.k, shape.E
+    args = [_ptr(topk_ids, "topk_ids", I32, A), _ptr(counts, "counts", I32, E),
+            _ptr(offsets, "offsets", I32, E + 1),
+            _ptr(sorted_token_ids, "sorted_token_ids", I32, A), _ptr(inv_pos, "inv_pos", I32, A)]
+    wp, wn = _ws(workspace, shape)
+    _check(lib().moe_permute(ctypes.byref(shape), *args, wp, wn, _stream(stream)))
+
+
+def grouped_ffn(shape, x, sorted_token_ids, offsets, w_gate_up, w_down, h, y, workspace,
+                stream=None):
+    T, H, E, I, A = shape.T, shape.H, shape.E, shape.I, shape.T * shape.k
+    args = [_ptr(x, "x", BF16, T * H), _ptr(sorted_token_ids, "sorted_token_ids", I32, A),
+            _ptr(offsets, "offsets", I32, E + 1), _ptr(w_gate_up, "w_gate_up", BF16, E * 2 * I * H),
+            _ptr(w_down, "w_down", BF16, E * H * I), _ptr(h, "h", BF16, A * I, optional=True),
+            _ptr(y, "y", BF16, A * H)]
+    wp, wn = _ws(workspace, shape)
+    _check(lib().moe_grouped_ffn(ctypes.byref(shape), *args, wp, wn, _stream(stream)))
+
+
+def shared_ffn(shape, x, ws_gate_up, ws_down, out, workspace, stream=None):
+    T, H, Is = shape.T, shape.H, shape.I_shared
+    args = [_ptr(x, "x", BF16, T * H), _ptr(ws_gate_up, "ws_gate_up", BF16, 2 * Is * H),
+            _ptr(ws_down, "ws_down", BF16, H * Is), _ptr(out, "out", F32, T * H)]
+    wp, wn = _ws(workspace, shape)
+    _check(lib().moe_shared_ffn(ctypes.byref(shape), *args, wp, wn, _stream(stream)))
+
+
+def combine(shape, y, inv_pos, topk_w, accumulate, out, stream=None):
+    T, H, A = shape.T, shape.H, shape.T * shape.k
+    args = [_ptr(y, "y", BF16, A * H), _ptr(inv_pos, "inv_pos", I32, A),
+            _ptr(topk_w, "topk_w", F32, A)]
+    _check(lib().moe_combine(ctypes.byref(shape), *args, int(bool(accumulate)),
+                             _ptr(out, "out", F32, T * H), _stream(stream)))
+
+
+def forward(shape, x, w_router, bias, w_gate_up, w_down, ws_gate_up, ws_down, out, workspace,
+            topk_ids_out=None, topk_w_out=None, counts_out=None, stream=None):
+    T, H, E, k, I, Is = shape.T, shape.H, shape.E, shape.k, shape.I, shape.I_shared
+    args = [_ptr(x, "x", BF16, T * H), _ptr(w_router, "w_router", F32, H * E),
+            _ptr(bias, "bias", F32, E, optional=True),
+            _ptr(w_gate_up, "w_gate_up", BF16, E * 2 * I * H),
+            _ptr(w_down, "w_down", BF16, E * H * I),
+            _ptr(ws_gate_up, "ws_gate_up", BF16, 2 * Is * H, optional=True),
+            _ptr(ws_down, "ws_down", BF16, H * Is, optional=True),
+            _ptr(out, "out", F32, T * H),
+            _ptr(topk_ids_out, "topk_ids_out", I32, T * k, optional=True),
+            _ptr(topk_w_out, "topk_w_out", F32, T * k, optional=True),
+            _ptr(counts_out, "counts_out", I32, E, optional=True)]
+    wp, wn = _ws(workspace, shape)
+    _check(lib().moe_forward(ctypes.byref(shape), *args, wp, wn, _stream(stream)))
+
+
+def profile_kernel(name: Optional[str], start=None, stop=None) -> None:
+    """Bracket every launch of kernel ``name`` with the two torch.cuda.Event
+    (or None to turn the hook off)."""
+    if name is None:
+        _check(lib().moe_profile_kernel(-1, None, None))
+        return
+    _check(lib().moe_profile_kernel(KERNEL_ID[name], start.cuda_event, stop.cuda_event))
+
+
+class MoELayer:
+    """Convenience holder: weights + one workspace; ``__call__`` runs
+    moe_forward and returns (out, topk_ids, topk_w, counts)."""
+
+    def __init__(self, layer, light_max_rows: int = -1):
+        c = layer.cfg
+        self.layer = layer
+        self.shape = make_shape(c.T, c.H, c.E, c.k, c.I, c.I_shared, c.renorm, light_max_rows)
+        self.workspace = alloc_workspace(self.shape, layer.x.device)
+
+    def __call__(self, x=None, out=None, want_routing=True):
+        L, s = self.layer, self.shape
+        x = L.x if x is None else x
+        dev = x.device
+        out = torch.empty((s.T, s.H), dtype=F32, device=dev) if out is None else out
+        ids = torch.empty((s.T, s.k), dtype=I32, device=dev) if want_routing else None
+        w = torch.empty((s.T, s.k), dtype=F32, device=dev) if want_routing else None
+        counts = torch.empty((s.E,), dtype=I32, device=dev) if want_routing else None
+        forward(s, x, L.wg, L.bias, L.w_gu, L.w_dn, L.ws_gu, L.ws_dn, out, self.workspace,
+                ids, w, counts)
+        return out, ids, w, counts

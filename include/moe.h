@@ -1,0 +1,201 @@
+/*
+ * moe.h -- C ABI of libmoe.so, the MI355X (gfx950) sparse mixture-of-experts
+ * layer: router GEMM -> softmax -> top-k -> permute -> grouped SwiGLU expert
+ * FFN (gate|up, then down) -> weighted gather-combine.
+ *
+ * The calls follow the statement of the problem on the source pages:
+ *  - pwwt.cn article on optimising Qwen 3.5-397B MoE on Ironwood (TPU v7x):
+ *      section 8.2  router logits are computed, then top-k selects experts;
+ *      section 4.2  top_k = 10 is not a power of 2, so permuting the routed
+ *                   rows must not pad; token rows are gathered by routing
+ *                   index into one contiguous buffer without a padded
+ *                   intermediate; the grouped expert GEMM fuses SwiGLU into
+ *                   its matmul and bounds each expert's slice by its own
+ *                   token count;
+ *      section 7.2  the routed rows are un-permuted and gather-reduced back
+ *                   into token order.
+ *  - lumevalley.com article on SGLang-JAX serving Ling-2.6-1T, opening
+ *    paragraph: top-8 routing plus an always-on shared expert.
+ *  - yuxiaoba.github.io summary of "Optimizing Muse Spark Open on TPU v7
+ *    with SGLang-TorchTPU", section on changing dependencies: experts with
+ *    few rows run a loop of their own, separate from the heavy-row loop, and
+ *    the output stays bitwise identical.
+ *
+ * Conventions shared by every call
+ *  - Shapes: T tokens, H hidden, E routed experts, k experts per token,
+ *    I expert intermediate size, A = T*k routed rows.  All arrays are dense
+ *    row-major.  "bf16" arrays hold raw bfloat16 bit patterns (uint16_t).
+ *  - Pointers are DEVICE pointers (HIP device memory, 16-byte aligned) unless
+ *    stated otherwise; `shape` is a HOST pointer.  The caller owns every
+ *    buffer; the library allocates nothing and keeps no state between calls
+ *    except a per-device cache of the compute-unit count.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued asynchronously; no call synchronises the stream or
+ *    reads device memory on the host.  A fault inside a kernel surfaces at
+ *    the caller's next synchronisation, as usual for HIP.
+ *  - Scratch memory comes from `workspace` (device, 256-byte aligned) of at
+ *    least moe_workspace_bytes(shape) bytes.  Calls on one stream may reuse
+ *    one workspace; calls that may overlap need separate workspaces.
+ *  - Return value: MOE_OK, or an error code below; on error nothing has
+ *    been enqueued (argument errors) or the failing launch is reported
+ *    (MOE_ERR_HIP).  moe_last_error() gives a text for the calling thread.
+ *  - Results are bitwise deterministic for identical inputs, shape, device
+ *    and build: no floating-point atomics are used anywhere.
+ *  - Supported sizes: T >= 0 (T == 0 is a no-op), H % 64 == 0,
+ *    I % 32 == 0, 1 <= k <= min(E, 32), E <= 1024, T*k < 2^31,
+ *    I_shared % 32 == 0 (or 0).  With T == 0 the activation and output
+ *    pointers may be NULL; only moe_permute (and moe_forward's counts_out)
+ *    write anything: all-zero counts and offsets.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,        /* a required pointer is NULL */
+    MOE_ERR_SHAPE = 2,       /* a size is negative/zero where it must not be, k > E, T*k overflow */
+    MOE_ERR_UNSUPPORTED = 3, /* valid but outside the supported sizes listed above */
+    MOE_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned (workspace: 256) */
+    MOE_ERR_WORKSPACE = 5,   /* ws_bytes < moe_workspace_bytes(shape) */
+    MOE_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed */
+};
+
+typedef struct moe_shape {
+    int32_t T;              /* tokens */
+    int32_t H;              /* hidden size */
+    int32_t E;              /* routed experts */
+    int32_t k;              /* experts per token */
+    int32_t I;              /* routed expert intermediate size */
+    int32_t I_shared;       /* shared expert intermediate size; 0 = no shared expert */
+    int32_t renorm;         /* 1: selected weights renormalised to sum to 1; 0: raw probabilities */
+    int32_t light_max_rows; /* experts with 1..light_max_rows rows take the light-row loop;
+                               -1 = library default (16); 0 = every expert takes the
+                               heavy tiles; at most 16 */
+} moe_shape;
+
+/* Bytes of workspace every call below needs for `shape` (host-only, pure;
+ * returns 0 for an invalid shape). */
+size_t moe_workspace_bytes(const moe_shape* shape);
+
+/* Static text for a status code. */
+const char* moe_status_string(int status);
+
+/* Text describing the calling thread's most recent failed call ("" if none). */
+const char* moe_last_error(void);
+
+/* Router: logits = x . w_router (+ bias) in fp32; softmax over the E experts;
+ * top-k by descending probability, the lower expert index winning ties;
+ * weights renormalised over the k selected (shape->renorm).
+ * (pwwt.cn article, sections 4.2 and 8.2.)
+ *   x        bf16 [T,H]
+ *   w_router fp32 [H,E]
+ *   bias     fp32 [E] added to the logits, or NULL
+ *   topk_ids int32 [T,k] out: expert ids in descending-probability order,
+ *            distinct, in [0,E) for every input (NaN logits count as -inf)
+ *   topk_w   fp32 [T,k] out: routing weights
+ *   probs    fp32 [T,E] out: softmax probabilities, or NULL
+ */
+int moe_router(const moe_shape* shape, const uint16_t* x, const float* w_router,
+               const float* bias, int32_t* topk_ids, float* topk_w, float* probs,
+               void* workspace, size_t ws_bytes, void* stream);
+
+/* Permute: per-expert histogram, exclusive scan, stable scatter of the
+ * routed rows into expert-major order (no padding; pwwt.cn section 4.2).
+ *   topk_ids         int32 [T,k] in: ids in [0,E) (others are skipped:
+ *                    not counted, inv_pos = -1)
+ *   counts           int32 [E]   out: rows per expert
+ *   offsets          int32 [E+1] out: exclusive prefix of counts
+ *   sorted_token_ids int32 [T*k] out: token of each expert-major row; within
+ *                    an expert, rows keep ascending assignment order t*k+j
+ *   inv_pos          int32 [T*k] out: expert-major row of assignment t*k+j
+ */
+int moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t* counts,
+                int32_t* offsets, int32_t* sorted_token_ids, int32_t* inv_pos,
+                void* workspace, size_t ws_bytes, void* stream);
+
+/* Grouped expert FFN over the expert-major rows (pwwt.cn section 4.2):
+ *   h[r,:] = bf16( silu(x[tok_r] . W_gate[e]) * (x[tok_r] . W_up[e]) )
+ *   y[r,:] = bf16( h[r,:] . W_down[e] )           for rows r of expert e,
+ * bf16 MFMA with fp32 accumulation; token rows are gathered inside the GEMM.
+ * Experts with 1..light_max_rows rows run the light-row loop, the others
+ * the heavy tiles; both give bitwise identical rows.
+ *   x                bf16 [T,H]
+ *   sorted_token_ids int32 [T*k], offsets int32 [E+1]  (from moe_permute)
+ *   w_gate_up        bf16 [E,2I,H]: rows 0..I-1 = W_gate^T, I..2I-1 = W_up^T
+ *   w_down           bf16 [E,H,I]:  W_down^T
+ *   h                bf16 [T*k,I] out, or NULL (then kept in the workspace)
+ *   y                bf16 [T*k,H] out
+ */
+int moe_grouped_ffn(const moe_shape* shape, const uint16_t* x,
+                    const int32_t* sorted_token_ids, const int32_t* offsets,
+                    const uint16_t* w_gate_up, const uint16_t* w_down, uint16_t* h,
+                    uint16_t* y, void* workspace, size_t ws_bytes, void* stream);
+
+/* Shared expert (lumevalley.com Ling-2.6-1T article): one dense SwiGLU FFN
+ * over all T tokens through the same GEMM kernels, written in fp32:
+ *   out[t,:] = W_down_s^T-product of bf16(silu(x W_gate_s) * (x W_up_s))
+ *   ws_gate_up bf16 [2*I_shared,H], ws_down bf16 [H,I_shared], out fp32 [T,H]
+ * Requires shape->I_shared > 0. */
+int moe_shared_ffn(const moe_shape* shape, const uint16_t* x, const uint16_t* ws_gate_up,
+                   const uint16_t* ws_down, float* out, void* workspace, size_t ws_bytes,
+                   void* stream);
+
+/* Weighted gather-combine back to token order (pwwt.cn section 7.2):
+ *   s[t,c]   = sum_{j<k} topk_w[t,j] * y[inv_pos[t*k+j], c]   (ascending j,
+ *              fp32; rows with inv_pos < 0 are skipped)
+ *   out[t,c] = accumulate ? out[t,c] + s[t,c] : s[t,c]
+ *   y bf16 [T*k,H], inv_pos int32 [T*k], topk_w fp32 [T,k], out fp32 [T,H].
+ * No workspace. */
+int moe_combine(const moe_shape* shape, const uint16_t* y, const int32_t* inv_pos,
+                const float* topk_w, int32_t accumulate, float* out, void* stream);
+
+/* The whole layer: router, permute, grouped FFN, shared expert (when
+ * shape->I_shared > 0), combine.  out fp32 [T,H]:
+ *   out[t] = sum_j w[t,j] FFN_{ids[t,j]}(x[t])  (+ FFN_shared(x[t]))
+ * ws_gate_up / ws_down are required iff I_shared > 0.  topk_ids_out [T,k],
+ * topk_w_out [T,k] and counts_out [E] are optional copies of the routing
+ * (NULL = not written). */
+int moe_forward(const moe_shape* shape, const uint16_t* x, const float* w_router,
+                const float* bias, const uint16_t* w_gate_up, const uint16_t* w_down,
+                const uint16_t* ws_gate_up, const uint16_t* ws_down, float* out,
+                int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out,
+                void* workspace, size_t ws_bytes, void* stream);
+
+/* Kernels of the layer, for moe_profile_kernel. */
+enum moe_kernel {
+    MOE_K_ROUTER_GEMM = 0,
+    MOE_K_ROUTER_SELECT = 1,
+    MOE_K_PERM_COUNT = 2,
+    MOE_K_PERM_SCAN = 3,
+    MOE_K_PERM_SCATTER = 4,
+    MOE_K_FFN_PLAN = 5,
+    MOE_K_GATEUP_LIGHT = 6,
+    MOE_K_GATEUP_HEAVY = 7,
+    MOE_K_DOWN_LIGHT = 8,
+    MOE_K_DOWN_HEAVY = 9,
+    MOE_K_COMBINE = 10,
+    MOE_K_COUNT = 11
+};
+
+/* Measurement hook (process-wide, not thread-safe): from now on every launch
+ * of kernel `kernel` (an enum moe_kernel value) is bracketed by
+ * hipEventRecord(start) and hipEventRecord(stop) on the stream it is launched
+ * on.  `start` and `stop` are caller-created hipEvent_t handles passed as
+ * void*.  kernel = -1 turns the hook off.  If a call launches the kernel more
+ * than once (the shared expert reuses the heavy kernels), the events bracket
+ * the last launch.  Returns MOE_OK, or MOE_ERR_SHAPE for an unknown kernel,
+ * MOE_ERR_NULL for a NULL event while turning the hook on. */
+int moe_profile_kernel(int kernel, void* start, void* stop);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

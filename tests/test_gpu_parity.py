@@ -1,0 +1,320 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Sizes span several tiles and ragged tails; full-size
+workloads compare every token's routing and a sample of tokens' outputs."""
+import numpy as np
+import pytest
+import torch
+
+from expert_ffn_layer_amd import moe, synth
+from tests import gpu_helpers as gh
+
+pytestmark = pytest.mark.gpu
+
+
+def layer_on_gpu(cfg, seed=0):
+    lay = synth.make_layer(cfg, seed=seed, device=gh.DEV)
+    return lay.rounded_to_bf16() if cfg.fp32_values else lay
+
+
+def custom(name, **kw):
+    return synth.custom_config(name, **kw)
+
+
+def log(name, rep):
+    ma, rel = rep["err"]
+    print(f"[parity] {name}: near_ties={rep['near_ties']} max_abs={ma:.3e} relL2={rel:.3e}", flush=True)
+
+
+# ------------------------------------------------------------ end to end
+SMALL = {
+    # tiny workload (fp32 values rounded to bf16 for the GPU; oracle gets the same)
+    "tiny": synth.CONFIGS["tiny"],
+    # light-row experts only (~2.5 rows each), several N blocks
+    "light": custom("light", T=40, H=256, E=64, k=4, I=192),
+    # heavy tiles with ragged tails (75 rows per expert, BM=128), K tail in down
+    "heavy_ragged": custom("heavy_ragged", T=300, H=320, E=16, k=4, I=96),
+    # mixed light / heavy experts, non-power-of-2 k
+    "mixed": custom("mixed", T=203, H=256, E=48, k=10, I=128, zipf_s=1.2, zipf_alpha=0.6),
+    # max sizes of the ABI: E=1024, k=32
+    "max_e_k": custom("max_e_k", T=33, H=128, E=1024, k=32, I=64),
+    # k == E
+    "k_eq_e": custom("k_eq_e", T=17, H=64, E=8, k=8, I=32),
+    # single token
+    "one_token": custom("one_token", T=1, H=512, E=128, k=10, I=256),
+    # shared expert
+    "shared": custom("shared", T=150, H=256, E=32, k=8, I=128, I_shared=160),
+    # raw (not renormalised) routing weights
+    "no_renorm": custom("no_renorm", T=70, H=192, E=24, k=6, I=64, renorm=0),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_small(oracle_lib, name):
+    print(f"[case] forward {name}", flush=True)
+    rep = gh.check_layer(oracle_lib, layer_on_gpu(SMALL[name]))
+    log(name, rep)
+
+
+@pytest.mark.parametrize("name", ["tiny", "light", "mixed"])
+def test_forward_heavy_only(oracle_lib, name):
+    """Every expert through the heavy tiles (light loop off)."""
+    print(f"[case] forward heavy-only {name}", flush=True)
+    rep = gh.check_layer(oracle_lib, layer_on_gpu(SMALL[name]), light_max_rows=0)
+    log(name + "/heavy", rep)
+
+
+# ------------------------------------------------------------ full size
+@pytest.mark.parametrize("name,sample", [("decode", None), ("prefill", 64), ("skew", 64),
+                                         ("ling", 48)])
+def test_forward_full_size(oracle_lib, name, sample):
+    print(f"[case] full-size {name}", flush=True)
+    cfg = synth.CONFIGS[name]
+    lay = layer_on_gpu(cfg)
+    tokens = None
+    if sample:
+        tokens = np.sort(np.random.default_rng(1).choice(cfg.T, sample, replace=False))
+    rep = gh.check_layer(oracle_lib, lay, tokens=tokens)
+    log(name, rep)
+    counts = rep["gpu"]["counts"]
+    assert counts.sum() == cfg.T * cfg.k
+    if name == "prefill":
+        assert counts.sum() == 81920  # the pages' [81920, 4096] permuted rows
+    del lay
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------ stages
+def _ids_tensor(rng, T, E, k):
+    return torch.as_tensor(np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32),
+                           device=gh.DEV)
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 4, 1), (500, 64, 10), (1000, 512, 10), (4096, 8, 2),
+                                   (333, 1024, 32)])
+def test_permute_stage(oracle_lib, T, E, k):
+    """Bit-exact against the oracle's permutation (several chunks, ragged)."""
+    print(f"[case] permute T={T} E={E} k={k}", flush=True)
+    rng = np.random.default_rng(T + E)
+    ids = _ids_tensor(rng, T, E, k)
+    s = moe.make_shape(T, 64, E, k, 32)
+    ws = moe.alloc_workspace(s)
+    counts = torch.empty(E, dtype=torch.int32, device=gh.DEV)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=gh.DEV)
+    srt = torch.empty(T * k, dtype=torch.int32, device=gh.DEV)
+    inv = torch.empty(T * k, dtype=torch.int32, device=gh.DEV)
+    moe.permute(s, ids, counts, offsets, srt, inv, ws)
+    torch.cuda.synchronize()
+    ref = oracle_lib.permute(ids.cpu().numpy(), E)
+    assert np.array_equal(counts.cpu().numpy(), ref["counts"])
+    assert np.array_equal(offsets.cpu().numpy(), ref["offsets"])
+    assert np.array_equal(srt.cpu().numpy(), ref["sorted_token_ids"])
+    assert np.array_equal(inv.cpu().numpy(), ref["inv_pos"])
+
+
+def test_permute_skips_invalid_ids():
+    """Ids outside [0, E) are not counted and get inv_pos = -1; the rest keep
+    their stable expert-major order (numpy stable argsort)."""
+    rng = np.random.default_rng(5)
+    T, E, k = 700, 40, 6
+    ids_np = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    bad = rng.random(ids_np.shape) < 0.05
+    ids_np[bad] = np.where(rng.random(bad.sum()) < 0.5, -1, E + 3)
+    s = moe.make_shape(T, 64, E, k, 32)
+    ws = moe.alloc_workspace(s)
+    t = lambda n: torch.empty(n, dtype=torch.int32, device=gh.DEV)
+    counts, offsets, srt, inv = t(E), t(E + 1), t(T * k), t(T * k)
+    moe.permute(s, torch.as_tensor(ids_np, device=gh.DEV), counts, offsets, srt, inv, ws)
+    torch.cuda.synchronize()
+    flat = ids_np.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    assert np.array_equal(counts.cpu().numpy(), np.bincount(flat[valid], minlength=E))
+    inv_np = inv.cpu().numpy()
+    assert np.all(inv_np[~valid] == -1)
+    order = np.nonzero(valid)[0][np.argsort(flat[valid], kind="stable")]
+    n = valid.sum()
+    assert np.array_equal(srt.cpu().numpy()[:n], order // k)
+    assert np.array_equal(inv_np[order], np.arange(n))
+
+
+@pytest.mark.parametrize("cfg", [SMALL["light"], SMALL["mixed"], SMALL["max_e_k"]],
+                         ids=lambda c: c.name)
+def test_router_stage(oracle_lib, cfg):
+    print(f"[case] router {cfg.name}", flush=True)
+    lay = layer_on_gpu(cfg)
+    s = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, renorm=cfg.renorm)
+    ws = moe.alloc_workspace(s)
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=gh.DEV)
+    w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=gh.DEV)
+    probs = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=gh.DEV)
+    moe.router(s, lay.x, lay.wg, lay.bias, ids, w, probs, ws)
+    torch.cuda.synchronize()
+    ref = oracle_lib.route(oracle_lib.logits(lay.x, lay.wg, lay.bias), cfg.k, cfg.renorm)
+    gh.check_routing(ids.cpu().numpy(), w.cpu().numpy(), ref)
+    assert np.abs(probs.cpu().numpy() - ref["probs"]).max() <= 1e-6
+
+
+def test_router_nonfinite(oracle_lib):
+    """NaN and +/-inf in the bias: the same ids as the oracle, all distinct
+    and in range (NaN counts as -inf; +inf entries share the mass)."""
+    cfg = custom("nonfinite", T=8, H=64, E=96, k=6, I=32)
+    lay = layer_on_gpu(cfg)
+    b = torch.zeros(cfg.E)
+    b[3] = float("nan")
+    b[17] = float("inf")
+    b[40] = float("inf")
+    b[50:60] = float("-inf")
+    lay.bias = b.to(gh.DEV)
+    x0 = lay.x.clone()
+    x0[0] = float("nan")  # a token whose every logit is NaN
+    lay.x = x0
+    s = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I)
+    ws = moe.alloc_workspace(s)
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=gh.DEV)
+    w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=gh.DEV)
+    moe.router(s, lay.x, lay.wg, lay.bias, ids, w, None, ws)
+    torch.cuda.synchronize()
+    ref = oracle_lib.route(oracle_lib.logits(lay.x, lay.wg, lay.bias), cfg.k, 1)
+    g = ids.cpu().numpy()
+    assert np.array_equal(g[:, :2], ref["ids"][:, :2])
+    assert np.array_equal(g[0], np.arange(cfg.k))
+    for row in g:
+        assert len(set(row.tolist())) == cfg.k and row.min() >= 0 and row.max() < cfg.E
+    assert np.array_equal(g, ref["ids"])
+
+
+def test_light_heavy_bitwise():
+    """The same expert rows through the light loop and the heavy tiles give
+    bitwise identical h and y."""
+    cfg = custom("lh", T=96, H=512, E=64, k=8, I=256)
+    lay = layer_on_gpu(cfg)
+    outs = []
+    for lm in (16, 0):
+        s = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, light_max_rows=lm)
+        ws = moe.alloc_workspace(s)
+        A = cfg.T * cfg.k
+        ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=gh.DEV)
+        w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=gh.DEV)
+        moe.router(s, lay.x, lay.wg, None, ids, w, None, ws)
+        t = lambda n: torch.empty(n, dtype=torch.int32, device=gh.DEV)
+        counts, offsets, srt, inv = t(cfg.E), t(cfg.E + 1), t(A), t(A)
+        moe.permute(s, ids, counts, offsets, srt, inv, ws)
+        h = torch.empty((A, cfg.I), dtype=torch.bfloat16, device=gh.DEV)
+        y = torch.empty((A, cfg.H), dtype=torch.bfloat16, device=gh.DEV)
+        moe.grouped_ffn(s, lay.x, srt, offsets, lay.w_gu, lay.w_dn, h, y, ws)
+        torch.cuda.synchronize()
+        outs.append((counts.cpu().numpy(), h.view(torch.int16).cpu().numpy(),
+                     y.view(torch.int16).cpu().numpy()))
+    (c0, h0, y0), (c1, h1, y1) = outs
+    assert np.array_equal(c0, c1)
+    assert (c0 <= 16).sum() > 0 and (c0 > 0).sum() > 10
+    assert np.array_equal(h0, h1), "h differs between light and heavy loops"
+    assert np.array_equal(y0, y1), "y differs between light and heavy loops"
+
+
+def test_ffn_stage_rows(oracle_lib):
+    """Grouped FFN rows (bf16 y) against the oracle's per-row expert FFN."""
+    cfg = SMALL["mixed"]
+    lay = layer_on_gpu(cfg)
+    s = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I)
+    ws = moe.alloc_workspace(s)
+    A = cfg.T * cfg.k
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=gh.DEV)
+    w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=gh.DEV)
+    moe.router(s, lay.x, lay.wg, lay.bias, ids, w, None, ws)
+    t = lambda n: torch.empty(n, dtype=torch.int32, device=gh.DEV)
+    counts, offsets, srt, inv = t(cfg.E), t(cfg.E + 1), t(A), t(A)
+    moe.permute(s, ids, counts, offsets, srt, inv, ws)
+    y = torch.empty((A, cfg.H), dtype=torch.bfloat16, device=gh.DEV)
+    moe.grouped_ffn(s, lay.x, srt, offsets, lay.w_gu, lay.w_dn, None, y, ws)
+    torch.cuda.synchronize()
+    off = offsets.cpu().numpy()
+    srt_np = srt.cpu().numpy()
+    y_np = y.float().cpu().numpy()
+    for e in range(cfg.E):
+        rows = np.arange(off[e], off[e + 1])
+        if rows.size == 0:
+            continue
+        ref = oracle_lib.expert_ffn(lay.x[torch.as_tensor(srt_np[rows], device=gh.DEV)],
+                                    lay.w_gu[e], lay.w_dn[e])
+        gh.assert_close(y_np[rows], ref, f"expert {e}")
+
+
+def test_combine_stage():
+    """Combine against a float64 numpy weighted sum of the same bf16 rows."""
+    rng = np.random.default_rng(9)
+    T, H, k, E = 77, 320, 5, 20
+    A = T * k
+    y = torch.randn((A, H), device=gh.DEV).to(torch.bfloat16)
+    perm = rng.permutation(A).astype(np.int32)
+    perm[3] = -1  # skipped row
+    w = torch.rand((T, k), device=gh.DEV)
+    s = moe.make_shape(T, H, E, k, 32)
+    for acc in (0, 1):
+        out = torch.randn((T, H), device=gh.DEV)
+        prev = out.cpu().numpy().astype(np.float64)
+        moe.combine(s, y, torch.as_tensor(perm, device=gh.DEV), w, acc, out)
+        torch.cuda.synchronize()
+        yv = y.float().cpu().numpy().astype(np.float64)
+        wv = w.cpu().numpy().astype(np.float64)
+        ref = np.zeros((T, H))
+        for t in range(T):
+            for j in range(k):
+                p = perm[t * k + j]
+                if p >= 0:
+                    ref[t] += wv[t, j] * yv[p]
+        if acc:
+            ref += prev
+        assert np.abs(out.cpu().numpy() - ref).max() <= 1e-5 * max(1.0, np.abs(ref).max())
+
+
+def test_shared_stage(oracle_lib):
+    cfg = SMALL["shared"]
+    lay = layer_on_gpu(cfg)
+    s = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_shared)
+    ws = moe.alloc_workspace(s)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=gh.DEV)
+    moe.shared_ffn(s, lay.x, lay.ws_gu, lay.ws_dn, out, ws)
+    torch.cuda.synchronize()
+    ref = oracle_lib.expert_ffn(lay.x, lay.ws_gu, lay.ws_dn)
+    gh.assert_close(out.cpu().numpy(), ref, "shared expert")
+
+
+# ------------------------------------------------------------ properties
+def test_determinism_and_equivariance():
+    cfg = SMALL["mixed"]
+    lay = layer_on_gpu(cfg)
+    a = gh.gpu_forward(lay)
+    b = gh.gpu_forward(lay)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), f"{key} not deterministic"
+    perm = torch.as_tensor(np.random.default_rng(3).permutation(cfg.T), device=gh.DEV)
+    lay_p = synth.Layer(cfg, lay.x[perm].contiguous(), lay.wg, lay.bias, lay.w_gu, lay.w_dn)
+    c = gh.gpu_forward(lay_p)
+    pn = perm.cpu().numpy()
+    assert np.array_equal(a["out"][pn], c["out"]), "token permutation changed output bits"
+    assert np.array_equal(a["ids"][pn], c["ids"])
+
+
+def test_exact_scaling_and_zero():
+    cfg = SMALL["mixed"]
+    lay = layer_on_gpu(cfg)
+    a = gh.gpu_forward(lay)
+    lay2 = synth.Layer(cfg, lay.x, lay.wg, lay.bias, lay.w_gu, (lay.w_dn * 2).contiguous())
+    b = gh.gpu_forward(lay2)
+    assert np.array_equal(2 * a["out"], b["out"])
+    lay0 = synth.Layer(cfg, lay.x, lay.wg, lay.bias, lay.w_gu, torch.zeros_like(lay.w_dn))
+    z = gh.gpu_forward(lay0)
+    assert np.all(z["out"] == 0)
+
+
+def test_empty_batch():
+    cfg = custom("empty", T=0, H=64, E=8, k=2, I=32)
+    s = moe.make_shape(0, 64, 8, 2, 32)
+    ws = moe.alloc_workspace(s)
+    lay = layer_on_gpu(custom("e1", T=1, H=64, E=8, k=2, I=32))
+    counts = torch.full((8,), 7, dtype=torch.int32, device=gh.DEV)
+    out = torch.empty((0, 64), dtype=torch.float32, device=gh.DEV)
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=gh.DEV)
+    moe.forward(s, x, lay.wg, None, lay.w_gu, lay.w_dn, None, None, out, ws, counts_out=counts)
+    torch.cuda.synchronize()
+    assert cfg.T == 0 and np.all(counts.cpu().numpy() == 0)
