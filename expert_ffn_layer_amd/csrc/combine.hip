@@ -9,7 +9,7 @@ namespace moe {
 namespace {
 
 // grid (T, ceil(H / 2048)); each thread owns 8 consecutive columns.
-__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                      const int32_t* __restrict__ inv_pos,
                                                      const float* __restrict__ w, int H, int k,
                                                      int accumulate, float* __restrict__ out) {
@@ -23,12 +23,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
         const int p = inv_pos[(size_t)t * k + j];
         if (p < 0) continue;
         const float wj = w[(size_t)t * k + j];
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(y + (size_t)p * H + c0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            acc[2 * q] += wj * bf16_bits_to_f32(v[q] & 0xffffu);
-            acc[2 * q + 1] += wj * bf16_bits_to_f32(v[q] >> 16);
-        }
+        const float4* src = reinterpret_cast<const float4*>(y + (size_t)p * H + c0);
+        const float4 v0 = src[0], v1 = src[1];
+        acc[0] += wj * v0.x;
+        acc[1] += wj * v0.y;
+        acc[2] += wj * v0.z;
+        acc[3] += wj * v0.w;
+        acc[4] += wj * v1.x;
+        acc[5] += wj * v1.y;
+        acc[6] += wj * v1.z;
+        acc[7] += wj * v1.w;
     }
     float4* o = reinterpret_cast<float4*>(out + (size_t)t * H + c0);
     float4 lo = {acc[0], acc[1], acc[2], acc[3]};
@@ -44,7 +48,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 
 }  // namespace
 
-hipError_t launch_combine(const uint16_t* y, const int32_t* inv_pos, const float* w, int T,
+hipError_t launch_combine(const float* y, const int32_t* inv_pos, const float* w, int T,
                           int H, int k, int accumulate, float* out, hipStream_t st) {
     dim3 grid(T, (H + 2047) / 2048);
     prof_begin(K_COMBINE, st);

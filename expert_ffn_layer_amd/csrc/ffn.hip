@@ -1,7 +1,7 @@
 // Grouped expert FFN on bf16 MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulate).
 //
 //   gate|up:  h[r, i] = bf16( silu(x[tok_r] . Wg[e,i]) * (x[tok_r] . Wu[e,i]) )
-//   down:     y[r, c] = bf16( h[r] . Wd[e,c] )
+//   down:     y[r, c] = h[r] . Wd[e,c]            (fp32)
 //
 // for the expert-major rows r of expert e (pwwt.cn article on Qwen 3.5-397B
 // MoE on Ironwood, section 4.2: grouped GEMM with SwiGLU fused into the
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void down_light_kernel(FfnArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 4 * g + r;
-                if (row < n) a.y[(size_t)(r0 + row) * a.H + c] = (uint16_t)f32_to_bf16_bits(acc[t][r]);
+                if (row < n) a.y[(size_t)(r0 + row) * a.H + c] = acc[t][r];
             }
         }
     }
@@ -246,7 +246,9 @@ __global__ __launch_bounds__(kThreads) void ffn_heavy_kernel(FfnArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][HBN][HLDK];
 
     const int N = (M == Mode::GateUp) ? 2 * a.I : a.H;
-    const int K = (M == Mode::GateUp) ? a.H : a.I;
+    // split_h: the down GEMM's K runs over [hi | lo] (2I) against W_down twice.
+    const int K = (M == Mode::GateUp) ? a.H : (a.split_h ? 2 * a.I : a.I);
+    const int hstride = a.split_h ? 2 * a.I : a.I;  // row pitch of h
     const int nblk = (N + HBN - 1) / HBN;
     const int ntiles = a.plan ? a.plan[1] : (a.dense_rows + HBM_ - 1) / HBM_;
     const long long nwork = (long long)ntiles * nblk;
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void ffn_heavy_kernel(FfnArgs a) {
                 const int wr = ((r & 15) < 8) ? hc : a.I + hc;
                 brow[q] = a.w_gu + ((size_t)e * 2 * a.I + (bok[q] ? wr : 0)) * a.H + ld_k;
             } else {
-                arow[q] = a.h + (size_t)(r0 + m0 + rr) * a.I + ld_k;
+                arow[q] = a.h + (size_t)(r0 + m0 + rr) * hstride + ld_k;
                 const int c = nb * HBN + r;
                 bok[q] = c < a.H;
                 brow[q] = a.w_dn + ((size_t)e * a.H + (bok[q] ? c : 0)) * a.I + ld_k;
@@ -301,11 +303,13 @@ __global__ __launch_bounds__(kThreads) void ffn_heavy_kernel(FfnArgs a) {
         auto gload = [&](int st) {
             const int kk = st * HBK;
             const bool kin = kk + ld_k < K;
+            // down with split_h: K columns past I wrap back onto W_down
+            const int kb = (M == Mode::Down && kk + ld_k >= a.I) ? kk - a.I : kk;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 ra[q] = (aok[q] && kin) ? *reinterpret_cast<const u32x4_t*>(arow[q] + kk)
                                         : u32x4_t{0u, 0u, 0u, 0u};
-                rb[q] = (bok[q] && kin) ? *reinterpret_cast<const u32x4_t*>(brow[q] + kk)
+                rb[q] = (bok[q] && kin) ? *reinterpret_cast<const u32x4_t*>(brow[q] + kb)
                                         : u32x4_t{0u, 0u, 0u, 0u};
             }
         };
@@ -368,17 +372,17 @@ __global__ __launch_bounds__(kThreads) void ffn_heavy_kernel(FfnArgs a) {
                     if (M == Mode::GateUp) {
                         const float up = __shfl_down(v, 8, 64);
                         const int hc = nb * (HBN / 2) + (wn * 4 + j) * 8 + l16;
-                        if (l16 < 8 && row < rows && hc < a.I)
-                            a.h[(size_t)(r0 + m0 + row) * a.I + hc] =
-                                (uint16_t)f32_to_bf16_bits(swiglu(v, up));
+                        if (l16 < 8 && row < rows && hc < a.I) {
+                            const float hv = swiglu(v, up);
+                            const uint32_t hi = f32_to_bf16_bits(hv);
+                            uint16_t* hr = a.h + (size_t)(r0 + m0 + row) * hstride;
+                            hr[hc] = (uint16_t)hi;
+                            if (a.split_h)
+                                hr[a.I + hc] = (uint16_t)f32_to_bf16_bits(hv - bf16_bits_to_f32(hi));
+                        }
                     } else {
                         const int c = nb * HBN + wn * 64 + j * 16 + l16;
-                        if (row < rows && c < a.H) {
-                            if (a.y32)
-                                a.y32[(size_t)(r0 + m0 + row) * a.H + c] = v;
-                            else
-                                a.y[(size_t)(r0 + m0 + row) * a.H + c] = (uint16_t)f32_to_bf16_bits(v);
-                        }
+                        if (row < rows && c < a.H) a.y[(size_t)(r0 + m0 + row) * a.H + c] = v;
                     }
                 }
             }

@@ -64,12 +64,13 @@ struct FfnArgs {
     const int32_t* offsets;      // [E+1] or nullptr for a dense group
     const uint16_t* w_gu;        // [E,2I,H]
     const uint16_t* w_dn;        // [E,H,I]
-    uint16_t* h;                 // [rows,I]
-    uint16_t* y;                 // [rows,H] bf16, or nullptr when y32 is used
-    float* y32;                  // [rows,H] fp32 (dense group output)
+    uint16_t* h;                 // [rows,I] bf16 ([rows,2I] when split_h)
+    float* y;                    // [rows,H] fp32
     const int32_t* plan;         // device plan, or nullptr for a dense group
     int T, H, I, E;
     int dense_rows;              // rows of a dense group (plan == nullptr)
+    int split_h;                 // 1: h rows hold [hi | lo] bf16 halves (2I wide) and the
+                                 //    down GEMM runs over both against the same weights
     int max_tiles;               // grid bound for heavy tiles
     int max_light;               // grid bound for light experts
     int num_cu;
@@ -79,7 +80,7 @@ hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st);
 
 // ---- combine ------------------------------------------------------------
-hipError_t launch_combine(const uint16_t* y, const int32_t* inv_pos, const float* w, int T,
+hipError_t launch_combine(const float* y, const int32_t* inv_pos, const float* w, int T,
                           int H, int k, int accumulate, float* out, hipStream_t st);
 
 }  // namespace moe

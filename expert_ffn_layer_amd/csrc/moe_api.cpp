@@ -88,8 +88,8 @@ Layout layout(const moe_shape* s) {
     L.inv = take((size_t)A * 4);
     L.plan = take((size_t)(moe::kPlanHeader + E + 2LL * L.max_tiles) * 4);
     L.h = take((size_t)A * I * 2);
-    L.y = take((size_t)A * H * 2);
-    L.hs = take((size_t)T * s->I_shared * 2);
+    L.y = take((size_t)A * H * 4);
+    L.hs = take((size_t)T * 2 * s->I_shared * 2);  // [hi | lo] rows
     L.total = off;
     return L;
 }
@@ -165,7 +165,7 @@ int run_permute(const moe_shape* s, const Layout& L, const int32_t* ids, int32_t
 
 int run_ffn(const moe_shape* s, const Layout& L, const uint16_t* x, const int32_t* sorted,
             const int32_t* offsets, const uint16_t* wgu, const uint16_t* wdn, uint16_t* h,
-            uint16_t* y, void* ws, hipStream_t st) {
+            float* y, void* ws, hipStream_t st) {
     int ncu = 0;
     if (int rc = device_cu_count(&ncu)) return rc;
     int32_t* plan = at<int32_t>(ws, L.plan);
@@ -178,13 +178,13 @@ int run_ffn(const moe_shape* s, const Layout& L, const uint16_t* x, const int32_
     a.w_dn = wdn;
     a.h = h ? h : at<uint16_t>(ws, L.h);
     a.y = y;
-    a.y32 = nullptr;
     a.plan = plan;
     a.T = s->T;
     a.H = s->H;
     a.I = s->I;
     a.E = s->E;
     a.dense_rows = 0;
+    a.split_h = 0;
     a.max_tiles = L.max_tiles;
     a.max_light = L.max_light;
     a.num_cu = ncu;
@@ -204,14 +204,16 @@ int run_shared(const moe_shape* s, const Layout& L, const uint16_t* x, const uin
     a.w_gu = wgu;
     a.w_dn = wdn;
     a.h = at<uint16_t>(ws, L.hs);
-    a.y = nullptr;
-    a.y32 = out;
+    a.y = out;
     a.plan = nullptr;
     a.T = s->T;
     a.H = s->H;
     a.I = s->I_shared;
     a.E = 1;
     a.dense_rows = s->T;
+    // The shared expert's output enters the sum with weight 1, so its h
+    // carries a bf16 hi/lo pair: h = hi + lo to ~16 bits.
+    a.split_h = 1;
     a.max_tiles = 0;
     a.max_light = 0;
     a.num_cu = ncu;
@@ -294,7 +296,7 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t* counts
 
 int moe_grouped_ffn(const moe_shape* shape, const uint16_t* x, const int32_t* sorted_token_ids,
                     const int32_t* offsets, const uint16_t* w_gate_up, const uint16_t* w_down,
-                    uint16_t* h, uint16_t* y, void* workspace, size_t ws_bytes, void* stream) {
+                    uint16_t* h, float* y, void* workspace, size_t ws_bytes, void* stream) {
     g_last_error.clear();
     if (int rc = check_shape(shape)) return rc;
     if (shape->T == 0) return MOE_OK;
@@ -326,7 +328,7 @@ int moe_shared_ffn(const moe_shape* shape, const uint16_t* x, const uint16_t* ws
                       (hipStream_t)stream);
 }
 
-int moe_combine(const moe_shape* shape, const uint16_t* y, const int32_t* inv_pos,
+int moe_combine(const moe_shape* shape, const float* y, const int32_t* inv_pos,
                 const float* topk_w, int32_t accumulate, float* out, void* stream) {
     g_last_error.clear();
     if (int rc = check_shape(shape)) return rc;
@@ -379,7 +381,7 @@ int moe_forward(const moe_shape* shape, const uint16_t* x, const float* w_router
     float* w = topk_w_out ? topk_w_out : at<float>(workspace, L.w);
     int32_t* sorted = at<int32_t>(workspace, L.sorted);
     int32_t* inv = at<int32_t>(workspace, L.inv);
-    uint16_t* y = at<uint16_t>(workspace, L.y);
+    float* y = at<float>(workspace, L.y);
     if (int rc = run_router(shape, L, x, w_router, bias, ids, w, nullptr, workspace, st)) return rc;
     if (int rc = run_permute(shape, L, ids, counts, offsets, sorted, inv, workspace, st)) return rc;
     if (int rc = run_ffn(shape, L, x, sorted, offsets, w_gate_up, w_down, nullptr, y, workspace, st))

@@ -137,17 +137,36 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
 
 constexpr int kMaxPerLane = 16;  // E <= 1024 = 16 * 64
 
-// One wave per token: reduce the split partials in ascending split order,
-// add the bias, softmax over E, then k rounds of a wave-wide argmax over
-// (probability, -expert id) keys held in registers.  Any k <= 32 works
-// without padding k to a power of 2.
+// One 256-thread block per token.  All threads reduce the split partials
+// (ascending split order) and add the bias into LDS; wave 0 then runs the
+// softmax over E and k rounds of a wave-wide argmax over (probability,
+// -expert id) keys held in registers.  Any k <= 32 works without padding k
+// to a power of 2.
 __global__ __launch_bounds__(256) void router_select_kernel(
     const float* __restrict__ part, int splits, const float* __restrict__ bias, int T, int E,
     int k, int renorm, int32_t* __restrict__ ids, float* __restrict__ w_out,
     float* __restrict__ probs) {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
+    __shared__ float lg[64 * kMaxPerLane];
+    const int t = blockIdx.x;
+    const size_t plane = (size_t)T * E;
+    for (int e = threadIdx.x; e < E; e += 256) {
+        const float* src = part + (size_t)t * E + e;
+        float acc = 0.f;
+        int s = 0;
+        for (; s + 8 <= splits; s += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(s + u) * plane];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc += v[u];
+        }
+        for (; s < splits; ++s) acc += src[(size_t)s * plane];
+        if (bias) acc += bias[e];
+        lg[e] = __builtin_isnan(acc) ? -INFINITY : acc;
+    }
+    __syncthreads();
+    if (threadIdx.x >= 64) return;
+    const int lane = threadIdx.x;
     const int nv = (E + 63) >> 6;
 
     float p[kMaxPerLane];
@@ -155,13 +174,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(
 #pragma unroll
     for (int i = 0; i < kMaxPerLane; ++i) {
         const int e = lane + 64 * i;
-        float l = -INFINITY;
-        if (i < nv && e < E) {
-            float acc = 0.f;
-            for (int s = 0; s < splits; ++s) acc += part[((size_t)s * T + t) * E + e];
-            if (bias) acc += bias[e];
-            l = __builtin_isnan(acc) ? -INFINITY : acc;
-        }
+        const float l = (i < nv && e < E) ? lg[e] : -INFINITY;
         p[i] = l;
         mx = fmaxf(mx, l);
     }
@@ -249,8 +262,7 @@ hipError_t launch_router_select(const float* part, int splits, const float* bias
                                 int k, int renorm, int32_t* ids, float* w, float* probs,
                                 hipStream_t st) {
     prof_begin(K_ROUTER_SELECT, st);
-    router_select_kernel<<<(T + 3) / 4, 256, 0, st>>>(part, splits, bias, T, E, k, renorm, ids, w,
-                                                      probs);
+    router_select_kernel<<<T, 256, 0, st>>>(part, splits, bias, T, E, k, renorm, ids, w, probs);
     prof_end(K_ROUTER_SELECT, st);
     return hipGetLastError();
 }

@@ -168,7 +168,7 @@ def grouped_ffn(shape, x, sorted_token_ids, offsets, w_gate_up, w_down, h, y, wo
     args = [_ptr(x, "x", BF16, T * H), _ptr(sorted_token_ids, "sorted_token_ids", I32, A),
             _ptr(offsets, "offsets", I32, E + 1), _ptr(w_gate_up, "w_gate_up", BF16, E * 2 * I * H),
             _ptr(w_down, "w_down", BF16, E * H * I), _ptr(h, "h", BF16, A * I, optional=True),
-            _ptr(y, "y", BF16, A * H)]
+            _ptr(y, "y", F32, A * H)]
     wp, wn = _ws(workspace, shape)
     _check(lib().moe_grouped_ffn(ctypes.byref(shape), *args, wp, wn, _stream(stream)))
 
@@ -183,7 +183,7 @@ def shared_ffn(shape, x, ws_gate_up, ws_down, out, workspace, stream=None):
 
 def combine(shape, y, inv_pos, topk_w, accumulate, out, stream=None):
     T, H, A = shape.T, shape.H, shape.T * shape.k
-    args = [_ptr(y, "y", BF16, A * H), _ptr(inv_pos, "inv_pos", I32, A),
+    args = [_ptr(y, "y", F32, A * H), _ptr(inv_pos, "inv_pos", I32, A),
             _ptr(topk_w, "topk_w", F32, A)]
     _check(lib().moe_combine(ctypes.byref(shape), *args, int(bool(accumulate)),
                              _ptr(out, "out", F32, T * H), _stream(stream)))
@@ -212,6 +212,9 @@ def profile_kernel(name: Optional[str], start=None, stop=None) -> None:
     if name is None:
         _check(lib().moe_profile_kernel(-1, None, None))
         return
+    for ev in (start, stop):
+        if not ev.cuda_event:  # torch creates the HIP event on first record
+            ev.record()
     _check(lib().moe_profile_kernel(KERNEL_ID[name], start.cuda_event, stop.cuda_event))
 
 

@@ -122,7 +122,7 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t* counts
 
 /* Grouped expert FFN over the expert-major rows (pwwt.cn section 4.2):
  *   h[r,:] = bf16( silu(x[tok_r] . W_gate[e]) * (x[tok_r] . W_up[e]) )
- *   y[r,:] = bf16( h[r,:] . W_down[e] )           for rows r of expert e,
+ *   y[r,:] = h[r,:] . W_down[e]   (fp32)          for rows r of expert e,
  * bf16 MFMA with fp32 accumulation; token rows are gathered inside the GEMM.
  * Experts with 1..light_max_rows rows run the light-row loop, the others
  * the heavy tiles; both give bitwise identical rows.
@@ -131,16 +131,20 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t* counts
  *   w_gate_up        bf16 [E,2I,H]: rows 0..I-1 = W_gate^T, I..2I-1 = W_up^T
  *   w_down           bf16 [E,H,I]:  W_down^T
  *   h                bf16 [T*k,I] out, or NULL (then kept in the workspace)
- *   y                bf16 [T*k,H] out
+ *   y                fp32 [T*k,H] out (fp32 so that large |y| entering the
+ *                    weighted sum are not rounded to 8 significant bits)
  */
 int moe_grouped_ffn(const moe_shape* shape, const uint16_t* x,
                     const int32_t* sorted_token_ids, const int32_t* offsets,
                     const uint16_t* w_gate_up, const uint16_t* w_down, uint16_t* h,
-                    uint16_t* y, void* workspace, size_t ws_bytes, void* stream);
+                    float* y, void* workspace, size_t ws_bytes, void* stream);
 
 /* Shared expert (lumevalley.com Ling-2.6-1T article): one dense SwiGLU FFN
- * over all T tokens through the same GEMM kernels, written in fp32:
- *   out[t,:] = W_down_s^T-product of bf16(silu(x W_gate_s) * (x W_up_s))
+ * over all T tokens through the same heavy GEMM kernels, written in fp32:
+ *   h = silu(x W_gate_s) * (x W_up_s),  out[t,:] = h W_down_s
+ * Because this output enters the layer with weight 1, h is kept as a pair
+ * of bf16 values (hi + lo, ~16 significant bits) and the down GEMM runs
+ * over both halves against the same weights.
  *   ws_gate_up bf16 [2*I_shared,H], ws_down bf16 [H,I_shared], out fp32 [T,H]
  * Requires shape->I_shared > 0. */
 int moe_shared_ffn(const moe_shape* shape, const uint16_t* x, const uint16_t* ws_gate_up,
@@ -151,9 +155,9 @@ int moe_shared_ffn(const moe_shape* shape, const uint16_t* x, const uint16_t* ws
  *   s[t,c]   = sum_{j<k} topk_w[t,j] * y[inv_pos[t*k+j], c]   (ascending j,
  *              fp32; rows with inv_pos < 0 are skipped)
  *   out[t,c] = accumulate ? out[t,c] + s[t,c] : s[t,c]
- *   y bf16 [T*k,H], inv_pos int32 [T*k], topk_w fp32 [T,k], out fp32 [T,H].
+ *   y fp32 [T*k,H], inv_pos int32 [T*k], topk_w fp32 [T,k], out fp32 [T,H].
  * No workspace. */
-int moe_combine(const moe_shape* shape, const uint16_t* y, const int32_t* inv_pos,
+int moe_combine(const moe_shape* shape, const float* y, const int32_t* inv_pos,
                 const float* topk_w, int32_t accumulate, float* out, void* stream);
 
 /* The whole layer: router, permute, grouped FFN, shared expert (when

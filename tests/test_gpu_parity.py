@@ -150,7 +150,8 @@ def test_router_stage(oracle_lib, cfg):
     torch.cuda.synchronize()
     ref = oracle_lib.route(oracle_lib.logits(lay.x, lay.wg, lay.bias), cfg.k, cfg.renorm)
     gh.check_routing(ids.cpu().numpy(), w.cpu().numpy(), ref)
-    assert np.abs(probs.cpu().numpy() - ref["probs"]).max() <= 1e-6
+    rp = ref["probs"]
+    assert np.all(np.abs(probs.cpu().numpy() - rp) <= gh.W_ATOL + gh.W_RTOL * rp)
 
 
 def test_router_nonfinite(oracle_lib):
@@ -199,11 +200,11 @@ def test_light_heavy_bitwise():
         counts, offsets, srt, inv = t(cfg.E), t(cfg.E + 1), t(A), t(A)
         moe.permute(s, ids, counts, offsets, srt, inv, ws)
         h = torch.empty((A, cfg.I), dtype=torch.bfloat16, device=gh.DEV)
-        y = torch.empty((A, cfg.H), dtype=torch.bfloat16, device=gh.DEV)
+        y = torch.empty((A, cfg.H), dtype=torch.float32, device=gh.DEV)
         moe.grouped_ffn(s, lay.x, srt, offsets, lay.w_gu, lay.w_dn, h, y, ws)
         torch.cuda.synchronize()
         outs.append((counts.cpu().numpy(), h.view(torch.int16).cpu().numpy(),
-                     y.view(torch.int16).cpu().numpy()))
+                     y.view(torch.int32).cpu().numpy()))
     (c0, h0, y0), (c1, h1, y1) = outs
     assert np.array_equal(c0, c1)
     assert (c0 <= 16).sum() > 0 and (c0 > 0).sum() > 10
@@ -212,7 +213,7 @@ def test_light_heavy_bitwise():
 
 
 def test_ffn_stage_rows(oracle_lib):
-    """Grouped FFN rows (bf16 y) against the oracle's per-row expert FFN."""
+    """Grouped FFN rows (fp32 y from bf16 h) against the oracle's per-row expert FFN."""
     cfg = SMALL["mixed"]
     lay = layer_on_gpu(cfg)
     s = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I)
@@ -224,12 +225,12 @@ def test_ffn_stage_rows(oracle_lib):
     t = lambda n: torch.empty(n, dtype=torch.int32, device=gh.DEV)
     counts, offsets, srt, inv = t(cfg.E), t(cfg.E + 1), t(A), t(A)
     moe.permute(s, ids, counts, offsets, srt, inv, ws)
-    y = torch.empty((A, cfg.H), dtype=torch.bfloat16, device=gh.DEV)
+    y = torch.empty((A, cfg.H), dtype=torch.float32, device=gh.DEV)
     moe.grouped_ffn(s, lay.x, srt, offsets, lay.w_gu, lay.w_dn, None, y, ws)
     torch.cuda.synchronize()
     off = offsets.cpu().numpy()
     srt_np = srt.cpu().numpy()
-    y_np = y.float().cpu().numpy()
+    y_np = y.cpu().numpy()
     for e in range(cfg.E):
         rows = np.arange(off[e], off[e + 1])
         if rows.size == 0:
@@ -240,11 +241,11 @@ def test_ffn_stage_rows(oracle_lib):
 
 
 def test_combine_stage():
-    """Combine against a float64 numpy weighted sum of the same bf16 rows."""
+    """Combine against a float64 numpy weighted sum of the same fp32 rows."""
     rng = np.random.default_rng(9)
     T, H, k, E = 77, 320, 5, 20
     A = T * k
-    y = torch.randn((A, H), device=gh.DEV).to(torch.bfloat16)
+    y = torch.randn((A, H), device=gh.DEV)
     perm = rng.permutation(A).astype(np.int32)
     perm[3] = -1  # skipped row
     w = torch.rand((T, k), device=gh.DEV)
@@ -254,7 +255,7 @@ def test_combine_stage():
         prev = out.cpu().numpy().astype(np.float64)
         moe.combine(s, y, torch.as_tensor(perm, device=gh.DEV), w, acc, out)
         torch.cuda.synchronize()
-        yv = y.float().cpu().numpy().astype(np.float64)
+        yv = y.cpu().numpy().astype(np.float64)
         wv = w.cpu().numpy().astype(np.float64)
         ref = np.zeros((T, H))
         for t in range(T):
