@@ -114,15 +114,15 @@ def main():
     for name in moe.KERNELS:
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(2)]
+        launched = 0
         for a, b in ev:
             moe.profile_kernel(name, a, b)
             step()
+            launched += moe.profile_launches()
         moe.profile_kernel(None)
         torch.cuda.synchronize()
-        try:
+        if launched == len(ev):  # kernels this workload does not launch are left out
             per_kernel[name] = sum(a.elapsed_time(b) for a, b in ev) / len(ev) * 1e3  # us
-        except RuntimeError:
-            pass  # not launched for this workload
     dominant = max(per_kernel, key=per_kernel.get)
 
     # Timed region: K steps; the dominant kernel bracketed by events each step.
@@ -154,7 +154,7 @@ def main():
         alg = light_experts * 2 * I * H * 2 + x_bytes + light_rows * I * 2
         flops = 4 * light_rows * H * I
     elif dominant == "down_light":
-        alg = light_experts * H * I * 2 + light_rows * (I + H) * 2
+        alg = light_experts * H * I * 2 + light_rows * (I * 2 + H * 4)
         flops = 2 * light_rows * H * I
     elif dominant == "gateup_heavy":
         he = touched - light_experts
@@ -164,7 +164,7 @@ def main():
     elif dominant == "down_heavy":
         he = touched - light_experts
         hr = A - light_rows
-        alg = he * H * I * 2 + hr * (I + H) * 2
+        alg = he * H * I * 2 + hr * (I * 2 + H * 4)
         flops = 2 * hr * H * I
     elif dominant == "router_gemm":
         alg = x_bytes + H * cfg.E * 4

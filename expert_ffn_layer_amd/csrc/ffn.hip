@@ -13,9 +13,9 @@
 // Open on TPU v7 with SGLang-TorchTPU" (section on changing dependencies):
 // experts with few rows do not share a loop body with heavy experts, so the
 // light loop carries no heavy accumulators.
-//  * light: an expert with 1..16 rows is one 16-row MFMA tile; each wave
-//    streams 16 weight rows straight from HBM into registers and keeps one
-//    accumulator.  This is the decode path: it is bound by weight bytes.
+//  * light: an expert with 1..64 rows; each wave streams 16 weight rows
+//    straight from HBM into registers and keeps one accumulator per 16-row
+//    sub-tile.  This is the decode path: it is bound by weight bytes.
 //  * heavy: 128x128 output tiles, A and B staged through double-buffered LDS,
 //    row sub-tiles past the expert's count skipped.
 // Both paths give every output element the same chain of MFMAs over K in
@@ -87,148 +87,249 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restric
     }
 }
 
-// ------------------------------------------------------- light: gate|up
-// Work item = (light expert, 32 h-columns); 4 waves x 8 h-columns.
-// U = K steps (of 32) kept in flight per wave.
-template <int U>
-__global__ __launch_bounds__(kThreads) void gateup_light_kernel(FfnArgs a) {
-    const int nlight = a.plan[0];
-    const int nblk = a.I / 32;
-    const long long nwork = (long long)nlight * nblk;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int l16 = lane & 15, g = lane >> 4;
-    const int nk = a.H / 32;
-    for (long long wi = blockIdx.x; wi < nwork; wi += gridDim.x) {
-        const int slot = (int)(wi / nblk), nb = (int)(wi % nblk);
-        const int e = a.plan[kPlanHeader + slot];
-        const int r0 = a.offsets[e];
-        const int n = a.offsets[e + 1] - r0;
-        const int i0 = nb * 32 + wave * 8;
-        const int wrow = (l16 < 8) ? (i0 + l16) : (a.I + i0 + l16 - 8);
-        const uint16_t* Bp = a.w_gu + ((size_t)e * 2 * a.I + wrow) * a.H + 8 * g;
-        const bool has_a = l16 < n;
-        const int tok = has_a ? (a.sorted_ids ? a.sorted_ids[r0 + l16] : r0 + l16) : 0;
-        const uint16_t* Ap = a.x + (size_t)tok * a.H + 8 * g;
+// Tunables of the light loops (compile-time; the defaults are the measured best).
+#ifndef MOE_LIGHT_GU_U
+#define MOE_LIGHT_GU_U 8        // K steps of 32 in flight per wave (gate|up)
+#endif
+#ifndef MOE_LIGHT_GU_TILES
+#define MOE_LIGHT_GU_TILES 1    // 16-column MFMA tiles per wave (8 h-columns each)
+#endif
+#ifndef MOE_LIGHT_GU_BPC
+#define MOE_LIGHT_GU_BPC 8      // blocks per CU in the grid
+#endif
+#ifndef MOE_LIGHT_DN_U
+#define MOE_LIGHT_DN_U 4
+#endif
+#ifndef MOE_LIGHT_DN_TILES
+#define MOE_LIGHT_DN_TILES 2
+#endif
+#ifndef MOE_LIGHT_DN_BPC
+#define MOE_LIGHT_DN_BPC 8
+#endif
+#ifndef MOE_LIGHT_NT_LOADS
+#define MOE_LIGHT_NT_LOADS 0    // 1: weights streamed with non-temporal loads
+#endif
 
-        floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-        bf16x8_t ca[U], cb[U];
+// Expert weights are read once per step: optionally bypass cache retention.
+template <bool kNonTemporal>
+__device__ __forceinline__ bf16x8_t load_weights(const uint16_t* p) {
+    if constexpr (kNonTemporal)
+        return __builtin_bit_cast(bf16x8_t,
+                                  __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+    else
+        return load_bf16x8(p);
+}
+
+// Row sub-tiles of the light loop: experts with up to 16 rows run one 16-row
+// MFMA tile with deep weight prefetch; experts with 17..64 rows run four
+// sub-tiles (those past the row count skipped) with shallower prefetch, so
+// both branches fit the same register budget.
+constexpr int kLightSubTiles = kLightRowsMax / 16;  // 4
+constexpr int kLightWideU = 2;                      // K steps in flight, wide branch
+
+// ------------------------------------------------------- light: gate|up
+// One wave: MT row sub-tiles x NTILE column tiles of one expert, K = H.
+// Tile t pairs gate rows i0+8t.. and the matching up rows, so lanes
+// l16 < 8 end with g and lanes l16 >= 8 with u of the same h column.
+template <int MT, int U, int NTILE, bool NTL>
+__device__ __forceinline__ void gateup_light_rows(const FfnArgs& a, int e, int r0, int n, int i0,
+                                                  int l16, int g) {
+    const int nk = a.H / 32;
+    const int wrow = (l16 < 8) ? (i0 + l16) : (a.I + i0 + l16 - 8);
+    const uint16_t* Bp = a.w_gu + ((size_t)e * 2 * a.I + wrow) * a.H + 8 * g;
+    const size_t bstride = (size_t)8 * a.H;  // next column tile: 8 rows further
+    const uint16_t* Ap[MT];
+    bool has_a[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int row = m * 16 + l16;
+        has_a[m] = row < n;
+        const int tok = has_a[m] ? (a.sorted_ids ? a.sorted_ids[r0 + row] : r0 + row) : 0;
+        Ap[m] = a.x + (size_t)tok * a.H + 8 * g;
+    }
+    const int mt_live = (n + 15) / 16;  // wave-uniform
+
+    floatx4_t acc[MT][NTILE];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) acc[m][t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    bf16x8_t ca[U][MT], cb[U][NTILE];
+    auto load_step = [&](int kb, bf16x8_t (&aa)[MT], bf16x8_t (&bb)[NTILE]) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) aa[m] = zero_bf16x8();
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) bb[t] = zero_bf16x8();
+        if (kb < nk) {
+#pragma unroll
+            for (int t = 0; t < NTILE; ++t) bb[t] = load_weights<NTL>(Bp + t * bstride + kb * 32);
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                if (has_a[m]) aa[m] = load_bf16x8(Ap[m] + kb * 32);
+        }
+    };
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_step(u, ca[u], cb[u]);
+    for (int k0 = 0; k0 < nk; k0 += U) {
+        bf16x8_t na[U][MT], nb_[U][NTILE];
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_step(k0 + U + u, na[u], nb_[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (k0 + u < nk) {
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+                    if (m < mt_live) {
+#pragma unroll
+                        for (int t = 0; t < NTILE; ++t)
+                            acc[m][t] = mfma_16x16x32(ca[u][m], cb[u][t], acc[m][t]);
+                    }
+            }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            ca[u] = zero_bf16x8();
-            cb[u] = zero_bf16x8();
-            if (u < nk) {
-                cb[u] = load_bf16x8(Bp + u * 32);
-                if (has_a) ca[u] = load_bf16x8(Ap + u * 32);
-            }
+#pragma unroll
+            for (int m = 0; m < MT; ++m) ca[u][m] = na[u][m];
+#pragma unroll
+            for (int t = 0; t < NTILE; ++t) cb[u][t] = nb_[u][t];
         }
-        for (int k0 = 0; k0 < nk; k0 += U) {
-            bf16x8_t na[U], nb_[U];
+    }
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int kb = k0 + U + u;
-                na[u] = zero_bf16x8();
-                nb_[u] = zero_bf16x8();
-                if (kb < nk) {
-                    nb_[u] = load_bf16x8(Bp + kb * 32);
-                    if (has_a) na[u] = load_bf16x8(Ap + kb * 32);
-                }
+    for (int m = 0; m < MT; ++m) {
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float up = __shfl_down(acc[m][t][r], 8, 64);
+                const int row = m * 16 + 4 * g + r;
+                if (l16 < 8 && row < n)
+                    a.h[(size_t)(r0 + row) * a.I + i0 + 8 * t + l16] =
+                        (uint16_t)f32_to_bf16_bits(swiglu(acc[m][t][r], up));
             }
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (k0 + u < nk) acc = mfma_16x16x32(ca[u], cb[u], acc);
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                ca[u] = na[u];
-                cb[u] = nb_[u];
-            }
-        }
-        // lanes l16 < 8 hold g, lanes l16 >= 8 hold u of the same column.
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float up = __shfl_down(acc[r], 8, 64);
-            const int row = 4 * g + r;
-            if (l16 < 8 && row < n)
-                a.h[(size_t)(r0 + row) * a.I + i0 + l16] =
-                    (uint16_t)f32_to_bf16_bits(swiglu(acc[r], up));
         }
     }
 }
 
+// Work item = (light expert, 4 waves x NTILE x 8 h-columns).
+template <int U, int NTILE, bool NTL>
+__global__ __launch_bounds__(kThreads) void gateup_light_kernel(FfnArgs a) {
+    static_assert(32 % (NTILE * 8) == 0, "a wave's columns must divide I's multiple of 32");
+    constexpr int kCols = 4 * NTILE * 8;
+    const int nlight = a.plan[0];
+    const int nblk = (a.I + kCols - 1) / kCols;
+    const long long nwork = (long long)nlight * nblk;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l16 = lane & 15, g = lane >> 4;
+    for (long long wi = blockIdx.x; wi < nwork; wi += gridDim.x) {
+        const int slot = (int)(wi / nblk), nb = (int)(wi % nblk);
+        const int i0 = nb * kCols + wave * NTILE * 8;
+        if (i0 >= a.I) continue;  // I % 32 == 0: a wave is all in or all out
+        const int e = a.plan[kPlanHeader + slot];
+        const int r0 = a.offsets[e];
+        const int n = a.offsets[e + 1] - r0;
+        if (n <= 16)
+            gateup_light_rows<1, U, NTILE, NTL>(a, e, r0, n, i0, l16, g);
+        else
+            gateup_light_rows<kLightSubTiles, kLightWideU, NTILE, NTL>(a, e, r0, n, i0, l16, g);
+    }
+}
+
 // --------------------------------------------------------- light: down
-// Work item = (light expert, 256 output columns); each wave NT x 16 columns.
-template <int NT, int U>
+// One wave: MT row sub-tiles x NT column tiles (16 output columns each), K = I.
+template <int MT, int U, int NT, bool NTL>
+__device__ __forceinline__ void down_light_rows(const FfnArgs& a, int e, int r0, int n, int c0,
+                                                int l16, int g) {
+    const int nk = a.I / 32;
+    const uint16_t* Bp = a.w_dn + ((size_t)e * a.H + c0 + l16) * a.I + 8 * g;
+    const size_t bstride = (size_t)16 * a.I;
+    const uint16_t* Ap[MT];
+    bool has_a[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int row = m * 16 + l16;
+        has_a[m] = row < n;
+        Ap[m] = a.h + (size_t)(r0 + (has_a[m] ? row : 0)) * a.I + 8 * g;
+    }
+    const int mt_live = (n + 15) / 16;
+
+    floatx4_t acc[MT][NT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[m][t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    bf16x8_t ca[U][MT], cb[U][NT];
+    auto load_step = [&](int kb, bf16x8_t (&aa)[MT], bf16x8_t (&bb)[NT]) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) aa[m] = zero_bf16x8();
+#pragma unroll
+        for (int t = 0; t < NT; ++t) bb[t] = zero_bf16x8();
+        if (kb < nk) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                if (has_a[m]) aa[m] = load_bf16x8(Ap[m] + kb * 32);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) bb[t] = load_weights<NTL>(Bp + t * bstride + kb * 32);
+        }
+    };
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_step(u, ca[u], cb[u]);
+    for (int k0 = 0; k0 < nk; k0 += U) {
+        bf16x8_t na[U][MT], nb_[U][NT];
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_step(k0 + U + u, na[u], nb_[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (k0 + u < nk) {
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+                    if (m < mt_live) {
+#pragma unroll
+                        for (int t = 0; t < NT; ++t)
+                            acc[m][t] = mfma_16x16x32(ca[u][m], cb[u][t], acc[m][t]);
+                    }
+            }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) ca[u][m] = na[u][m];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) cb[u][t] = nb_[u][t];
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int c = c0 + t * 16 + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = m * 16 + 4 * g + r;
+                if (row < n) a.y[(size_t)(r0 + row) * a.H + c] = acc[m][t][r];
+            }
+        }
+    }
+}
+
+// Work item = (light expert, 4 waves x NT x 16 output columns).
+template <int NT, int U, bool NTL>
 __global__ __launch_bounds__(kThreads) void down_light_kernel(FfnArgs a) {
+    static_assert(64 % (NT * 16) == 0, "a wave's columns must divide H's multiple of 64");
     constexpr int kCols = 4 * NT * 16;
     const int nlight = a.plan[0];
     const int nblk = (a.H + kCols - 1) / kCols;
     const long long nwork = (long long)nlight * nblk;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l16 = lane & 15, g = lane >> 4;
-    const int nk = a.I / 32;
     for (long long wi = blockIdx.x; wi < nwork; wi += gridDim.x) {
         const int slot = (int)(wi / nblk), nb = (int)(wi % nblk);
         const int c0 = nb * kCols + wave * NT * 16;
-        if (c0 >= a.H) continue;  // H % 64 == 0: a wave is all in or all out
+        if (c0 >= a.H) continue;  // H % 64 == 0 and NT*16 divides 64: all in or all out
         const int e = a.plan[kPlanHeader + slot];
         const int r0 = a.offsets[e];
         const int n = a.offsets[e + 1] - r0;
-        const bool has_a = l16 < n;
-        const uint16_t* Ap = a.h + (size_t)(r0 + (has_a ? l16 : 0)) * a.I + 8 * g;
-        const uint16_t* Bp = a.w_dn + ((size_t)e * a.H + c0 + l16) * a.I + 8 * g;
-        const size_t bstride = (size_t)16 * a.I;
-
-        floatx4_t acc[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-        bf16x8_t ca[U], cb[U][NT];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            ca[u] = zero_bf16x8();
-#pragma unroll
-            for (int t = 0; t < NT; ++t) cb[u][t] = zero_bf16x8();
-            if (u < nk) {
-                if (has_a) ca[u] = load_bf16x8(Ap + u * 32);
-#pragma unroll
-                for (int t = 0; t < NT; ++t) cb[u][t] = load_bf16x8(Bp + t * bstride + u * 32);
-            }
-        }
-        for (int k0 = 0; k0 < nk; k0 += U) {
-            bf16x8_t na[U], nb_[U][NT];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int kb = k0 + U + u;
-                na[u] = zero_bf16x8();
-#pragma unroll
-                for (int t = 0; t < NT; ++t) nb_[u][t] = zero_bf16x8();
-                if (kb < nk) {
-                    if (has_a) na[u] = load_bf16x8(Ap + kb * 32);
-#pragma unroll
-                    for (int t = 0; t < NT; ++t)
-                        nb_[u][t] = load_bf16x8(Bp + t * bstride + kb * 32);
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (k0 + u < nk) {
-#pragma unroll
-                    for (int t = 0; t < NT; ++t) acc[t] = mfma_16x16x32(ca[u], cb[u][t], acc[t]);
-                }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                ca[u] = na[u];
-#pragma unroll
-                for (int t = 0; t < NT; ++t) cb[u][t] = nb_[u][t];
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int c = c0 + t * 16 + l16;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 4 * g + r;
-                if (row < n) a.y[(size_t)(r0 + row) * a.H + c] = acc[t][r];
-            }
-        }
+        if (n <= 16)
+            down_light_rows<1, U, NT, NTL>(a, e, r0, n, c0, l16, g);
+        else
+            down_light_rows<kLightSubTiles, kLightWideU, NT, NTL>(a, e, r0, n, c0, l16, g);
     }
 }
 
@@ -406,9 +507,11 @@ hipError_t launch_ffn_plan(const int32_t* offsets, int E, int light_max, int32_t
 
 hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t st) {
     if (a.plan && a.max_light > 0) {
-        const long long work = (long long)a.max_light * (a.I / 32);
+        constexpr int kCols = 4 * MOE_LIGHT_GU_TILES * 8;
+        const long long work = (long long)a.max_light * ((a.I + kCols - 1) / kCols);
         prof_begin(K_GATEUP_LIGHT, st);
-        gateup_light_kernel<8><<<grid_for(work, 8, a.num_cu), kThreads, 0, st>>>(a);
+        gateup_light_kernel<MOE_LIGHT_GU_U, MOE_LIGHT_GU_TILES, MOE_LIGHT_NT_LOADS != 0>
+            <<<grid_for(work, MOE_LIGHT_GU_BPC, a.num_cu), kThreads, 0, st>>>(a);
         prof_end(K_GATEUP_LIGHT, st);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
@@ -426,9 +529,11 @@ hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t st) {
 
 hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st) {
     if (a.plan && a.max_light > 0) {
-        const long long work = (long long)a.max_light * ((a.H + 255) / 256);
+        constexpr int kCols = 4 * MOE_LIGHT_DN_TILES * 16;
+        const long long work = (long long)a.max_light * ((a.H + kCols - 1) / kCols);
         prof_begin(K_DOWN_LIGHT, st);
-        down_light_kernel<4, 4><<<grid_for(work, 8, a.num_cu), kThreads, 0, st>>>(a);
+        down_light_kernel<MOE_LIGHT_DN_TILES, MOE_LIGHT_DN_U, MOE_LIGHT_NT_LOADS != 0>
+            <<<grid_for(work, MOE_LIGHT_DN_BPC, a.num_cu), kThreads, 0, st>>>(a);
         prof_end(K_DOWN_LIGHT, st);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;

@@ -10,11 +10,15 @@ namespace moe {
 struct ProfileHook {
     int kernel = -1;
     hipEvent_t start = nullptr, stop = nullptr;
+    long long launches = 0;
 };
 extern ProfileHook g_profile;
 
 inline void prof_begin(int kernel, hipStream_t st) {
-    if (g_profile.kernel == kernel) (void)hipEventRecord(g_profile.start, st);
+    if (g_profile.kernel == kernel) {
+        (void)hipEventRecord(g_profile.start, st);
+        ++g_profile.launches;
+    }
 }
 inline void prof_end(int kernel, hipStream_t st) {
     if (g_profile.kernel == kernel) (void)hipEventRecord(g_profile.stop, st);
@@ -23,7 +27,7 @@ inline void prof_end(int kernel, hipStream_t st) {
 // Kernel ids (same values as enum moe_kernel in moe.h).
 enum KernelId {
     K_ROUTER_GEMM = 0, K_ROUTER_SELECT, K_PERM_COUNT, K_PERM_SCAN, K_PERM_SCATTER, K_FFN_PLAN,
-    K_GATEUP_LIGHT, K_GATEUP_HEAVY, K_DOWN_LIGHT, K_DOWN_HEAVY, K_COMBINE, K_COUNT
+    K_GATEUP_LIGHT, K_GATEUP_HEAVY, K_DOWN_LIGHT, K_DOWN_HEAVY, K_COMBINE, K_PERM_SMALL, K_COUNT
 };
 
 // ---- router -------------------------------------------------------------
@@ -42,12 +46,14 @@ hipError_t launch_router_select(const float* part, int splits, const float* bias
 // ---- permute ------------------------------------------------------------
 constexpr int kPermChunk = 4096;  // assignments per permute block
 
+// A <= kPermChunk runs as one fused block; then `plan` (may be nullptr)
+// also receives the grouped-FFN plan for `light_max`.
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* chunk_counts,
                           int nchunks, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
-                          int32_t* inv_pos, hipStream_t st);
+                          int32_t* inv_pos, int32_t* plan, int light_max, hipStream_t st);
 
 // ---- grouped FFN --------------------------------------------------------
-constexpr int kLightRowsMax = 16;  // one 16-row MFMA tile
+constexpr int kLightRowsMax = 64;  // up to four 16-row MFMA sub-tiles
 constexpr int kHeavyBM = 128;      // rows per heavy tile
 // Plan layout (int32): [0] n_light, [1] n_tiles, [16 ..16+E) light expert
 // ids, [16+E ..) heavy tiles as (expert, first row) pairs.

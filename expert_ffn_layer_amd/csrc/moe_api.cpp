@@ -14,6 +14,7 @@
 static_assert((int)moe::K_COUNT == (int)MOE_K_COUNT, "kernel ids out of sync");
 static_assert((int)moe::K_GATEUP_LIGHT == (int)MOE_K_GATEUP_LIGHT, "kernel ids out of sync");
 static_assert((int)moe::K_COMBINE == (int)MOE_K_COMBINE, "kernel ids out of sync");
+static_assert((int)moe::K_PERM_SMALL == (int)MOE_K_PERM_SMALL, "kernel ids out of sync");
 
 namespace moe {
 ProfileHook g_profile;
@@ -60,7 +61,7 @@ int check_shape(const moe_shape* s) {
     if (s->k > 32) return fail(MOE_ERR_UNSUPPORTED, "k must be <= 32");
     if (s->renorm != 0 && s->renorm != 1) return fail(MOE_ERR_UNSUPPORTED, "renorm must be 0 or 1");
     if (s->light_max_rows < -1 || s->light_max_rows > moe::kLightRowsMax)
-        return fail(MOE_ERR_UNSUPPORTED, "light_max_rows must be -1 or in [0, 16]");
+        return fail(MOE_ERR_UNSUPPORTED, "light_max_rows must be -1 or in [0, 64]");
     return MOE_OK;
 }
 
@@ -70,7 +71,9 @@ Layout layout(const moe_shape* s) {
     L.splits = router_splits(s->T, s->H, s->E);
     L.nchunks = (int)std::max<long long>(1, (A + moe::kPermChunk - 1) / moe::kPermChunk);
     L.light_max = s->light_max_rows < 0 ? moe::kLightRowsMax : s->light_max_rows;
-    L.max_tiles = moe::max_heavy_tiles(A, s->E, L.light_max);
+    // Each token picks k distinct experts, so no expert gets more than T rows:
+    // with T <= light_max every expert is light and no heavy tile can exist.
+    L.max_tiles = (T <= L.light_max) ? 0 : moe::max_heavy_tiles(A, s->E, L.light_max);
     L.max_light = L.light_max > 0 ? (int)std::min<long long>(E, A) : 0;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -155,21 +158,28 @@ int run_router(const moe_shape* s, const Layout& L, const uint16_t* x, const flo
     return MOE_OK;
 }
 
+// Returns through *plan_ready whether the permute also wrote the FFN plan
+// (single-block path); then run_ffn skips its plan kernel.
 int run_permute(const moe_shape* s, const Layout& L, const int32_t* ids, int32_t* counts,
-                int32_t* offsets, int32_t* sorted, int32_t* inv, void* ws, hipStream_t st) {
+                int32_t* offsets, int32_t* sorted, int32_t* inv, void* ws, hipStream_t st,
+                bool* plan_ready = nullptr) {
+    const bool small = (long long)s->T * s->k <= moe::kPermChunk;
+    int32_t* plan = (plan_ready && small) ? at<int32_t>(ws, L.plan) : nullptr;
     HIP_TRY(moe::launch_permute(ids, s->T, s->k, s->E, at<int32_t>(ws, L.chunk), L.nchunks,
-                                counts, offsets, sorted, inv, st),
+                                counts, offsets, sorted, inv, plan, L.light_max, st),
             "permute");
+    if (plan_ready) *plan_ready = plan != nullptr;
     return MOE_OK;
 }
 
 int run_ffn(const moe_shape* s, const Layout& L, const uint16_t* x, const int32_t* sorted,
             const int32_t* offsets, const uint16_t* wgu, const uint16_t* wdn, uint16_t* h,
-            float* y, void* ws, hipStream_t st) {
+            float* y, void* ws, hipStream_t st, bool plan_ready = false) {
     int ncu = 0;
     if (int rc = device_cu_count(&ncu)) return rc;
     int32_t* plan = at<int32_t>(ws, L.plan);
-    HIP_TRY(moe::launch_ffn_plan(offsets, s->E, L.light_max, plan, st), "ffn plan");
+    if (!plan_ready)
+        HIP_TRY(moe::launch_ffn_plan(offsets, s->E, L.light_max, plan, st), "ffn plan");
     moe::FfnArgs a{};
     a.x = x;
     a.sorted_ids = sorted;
@@ -257,8 +267,11 @@ int moe_profile_kernel(int kernel, void* start, void* stop) {
     moe::g_profile.kernel = kernel;
     moe::g_profile.start = (hipEvent_t)start;
     moe::g_profile.stop = (hipEvent_t)stop;
+    moe::g_profile.launches = 0;
     return MOE_OK;
 }
+
+long long moe_profile_launches(void) { return moe::g_profile.launches; }
 
 int moe_router(const moe_shape* shape, const uint16_t* x, const float* w_router,
                const float* bias, int32_t* topk_ids, float* topk_w, float* probs,
@@ -383,8 +396,11 @@ int moe_forward(const moe_shape* shape, const uint16_t* x, const float* w_router
     int32_t* inv = at<int32_t>(workspace, L.inv);
     float* y = at<float>(workspace, L.y);
     if (int rc = run_router(shape, L, x, w_router, bias, ids, w, nullptr, workspace, st)) return rc;
-    if (int rc = run_permute(shape, L, ids, counts, offsets, sorted, inv, workspace, st)) return rc;
-    if (int rc = run_ffn(shape, L, x, sorted, offsets, w_gate_up, w_down, nullptr, y, workspace, st))
+    bool plan_ready = false;
+    if (int rc = run_permute(shape, L, ids, counts, offsets, sorted, inv, workspace, st, &plan_ready))
+        return rc;
+    if (int rc = run_ffn(shape, L, x, sorted, offsets, w_gate_up, w_down, nullptr, y, workspace, st,
+                         plan_ready))
         return rc;
     if (shape->I_shared > 0)
         if (int rc = run_shared(shape, L, x, ws_gate_up, ws_down, out, workspace, st)) return rc;

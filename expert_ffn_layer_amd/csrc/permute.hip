@@ -25,6 +25,48 @@ constexpr int kWavesPerBlock = kThreads / 64;
 
 __device__ __forceinline__ bool valid_id(int e, int E) { return e >= 0 && e < E; }
 
+// 64 consecutive assignments, one per lane: the lane's rank among this
+// wave's assignments to the same expert so far (earlier steps and lower
+// lanes).  Lanes holding equal ids are matched with one ballot per id bit;
+// the group's last lane advances my[e].  A wave's own LDS accesses complete
+// in program order, so the next step sees the update.
+__device__ __forceinline__ int wave_stable_rank(int e, bool ok, int nbits, uint64_t lt,
+                                                int32_t* my) {
+    uint64_t match = __ballot(ok);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t bal = __ballot(bit);
+        match &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(match & lt);
+    const int n = __popcll(match);
+    int loc = 0;
+    if (ok) {
+        loc = my[e] + rank;
+        if (rank == n - 1) my[e] = loc + 1;
+    }
+    return loc;
+}
+
+// Exclusive scan over a 256-thread block of one int per thread; returns the
+// thread's exclusive prefix and writes the block total to *total.
+__device__ __forceinline__ int block256_exclusive_scan(int v, int32_t* wsum, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += u;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    *total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+    return before + incl - v;
+}
+
 __global__ __launch_bounds__(kThreads) void perm_count_kernel(const int32_t* __restrict__ ids,
                                                              long long A, int E,
                                                              int32_t* __restrict__ chunk_counts) {
@@ -119,20 +161,7 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(
         const long long a = base + (long long)q * 64 + lane;
         const int e = (a < A) ? ids[a] : -1;
         const bool ok = valid_id(e, E);
-        uint64_t match = __ballot(ok);
-        for (int b = 0; b < nbits; ++b) {
-            const bool bit = (e >> b) & 1;
-            const uint64_t bal = __ballot(bit);
-            match &= bit ? bal : ~bal;
-        }
-        const int rank = __popcll(match & lt);
-        const int n = __popcll(match);
-        int loc = 0;
-        if (ok) {
-            loc = my[e] + rank;
-            if (rank == n - 1) my[e] = loc + 1;
-        }
-        local[q] = loc;
+        local[q] = wave_stable_rank(e, ok, nbits, lt, my);
         eid[q] = ok ? e : -1;
     }
     __syncthreads();
@@ -152,14 +181,120 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(
     }
 }
 
+// The whole permute in one block when all assignments fit one chunk
+// (A <= kPermChunk): per-wave stable ranks give the counts, a block scan
+// gives the offsets, then every assignment is written to its slot.  With a
+// plan pointer it also emits the grouped-FFN plan (same layout as
+// ffn_plan_kernel: light experts with 1..light_max rows, heavy row tiles).
+__global__ __launch_bounds__(kThreads) void perm_small_kernel(
+    const int32_t* __restrict__ ids, int A, int k, int E, int nbits,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_ids,
+    int32_t* __restrict__ inv_pos, int32_t* __restrict__ plan, int light_max, int tile_rows) {
+    extern __shared__ int32_t sm[];  // wcnt[4][E], off[E]
+    __shared__ int32_t wsum[4];
+    int32_t* wcnt = sm;
+    int32_t* off = sm + kWavesPerBlock * E;
+    for (int i = threadIdx.x; i < (kWavesPerBlock + 1) * E; i += kThreads) sm[i] = 0;
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int base = wave * (kPermChunk / kWavesPerBlock);
+    const uint64_t lt = lanemask_lt(lane);
+    int local[kPerThread];
+    int eid[kPerThread];
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+        const int a = base + q * 64 + lane;
+        const int e = (a < A) ? ids[a] : -1;
+        const bool ok = valid_id(e, E);
+        local[q] = wave_stable_rank(e, ok, nbits, lt, wcnt + wave * E);
+        eid[q] = ok ? e : -1;
+    }
+    __syncthreads();
+
+    // counts and exclusive offsets; each thread owns experts 4t..4t+3
+    int c[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = 4 * threadIdx.x + j;
+        c[j] = 0;
+        if (e < E) c[j] = wcnt[e] + wcnt[E + e] + wcnt[2 * E + e] + wcnt[3 * E + e];
+        sum += c[j];
+    }
+    int total = 0;
+    int run = block256_exclusive_scan(sum, wsum, &total);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = 4 * threadIdx.x + j;
+        if (e < E) {
+            off[e] = run;
+            counts[e] = c[j];
+            offsets[e] = run;
+        }
+        run += c[j];
+    }
+    if (threadIdx.x == 0) offsets[E] = total;
+    __syncthreads();
+
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+        const int a = base + q * 64 + lane;
+        if (a >= A) continue;
+        const int e = eid[q];
+        if (e < 0) {
+            inv_pos[a] = -1;
+            continue;
+        }
+        int pos = off[e] + local[q];
+        for (int w = 0; w < wave; ++w) pos += wcnt[w * E + e];
+        sorted_ids[pos] = a / k;
+        inv_pos[a] = pos;
+    }
+
+    if (!plan) return;
+    int lj[4], tj[4], lsum = 0, tsum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        lj[j] = (c[j] >= 1 && c[j] <= light_max) ? 1 : 0;
+        tj[j] = (c[j] > light_max) ? (c[j] + tile_rows - 1) / tile_rows : 0;
+        lsum += lj[j];
+        tsum += tj[j];
+    }
+    int ltot = 0, ttot = 0;
+    int lrun = block256_exclusive_scan(lsum, wsum, &ltot);
+    int trun = block256_exclusive_scan(tsum, wsum, &ttot);
+    int32_t* tiles = plan + kPlanHeader + E;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = 4 * threadIdx.x + j;
+        if (lj[j]) plan[kPlanHeader + lrun++] = e;
+        for (int i = 0; i < tj[j]; ++i, ++trun) {
+            tiles[2 * trun] = e;
+            tiles[2 * trun + 1] = i * tile_rows;
+        }
+    }
+    if (threadIdx.x == 0) {
+        plan[0] = ltot;
+        plan[1] = ttot;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* chunk_counts,
                           int nchunks, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
-                          int32_t* inv_pos, hipStream_t st) {
+                          int32_t* inv_pos, int32_t* plan, int light_max, hipStream_t st) {
     const long long A = (long long)T * k;
     int nbits = 1;
     while ((1 << nbits) < E) ++nbits;
+    if (A <= kPermChunk) {
+        prof_begin(K_PERM_SMALL, st);
+        perm_small_kernel<<<1, kThreads, (kWavesPerBlock + 1) * E * sizeof(int32_t), st>>>(
+            ids, (int)A, k, E, nbits, counts, offsets, sorted_ids, inv_pos, plan, light_max,
+            kHeavyBM);
+        prof_end(K_PERM_SMALL, st);
+        return hipGetLastError();
+    }
     prof_begin(K_PERM_COUNT, st);
     perm_count_kernel<<<nchunks, kThreads, E * sizeof(int32_t), st>>>(ids, A, E, chunk_counts);
     prof_end(K_PERM_COUNT, st);

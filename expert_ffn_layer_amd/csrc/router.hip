@@ -149,20 +149,34 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     __shared__ float lg[64 * kMaxPerLane];
     const int t = blockIdx.x;
     const size_t plane = (size_t)T * E;
-    for (int e = threadIdx.x; e < E; e += 256) {
-        const float* src = part + (size_t)t * E + e;
-        float acc = 0.f;
-        int s = 0;
-        for (; s + 8 <= splits; s += 8) {
-            float v[8];
+    // Each thread owns experts tid + 256q (q < 4, E <= 1024); 8 splits of
+    // each are loaded together, then added in ascending split order.
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < splits; s0 += 8) {
+        float v[4][8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(s + u) * plane];
+        for (int q = 0; q < 4; ++q) {
+            const int e = threadIdx.x + 256 * q;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) acc += v[u];
+            for (int u = 0; u < 8; ++u)
+                v[q][u] = (e < E && s0 + u < splits)
+                              ? part[(size_t)(s0 + u) * plane + (size_t)t * E + e]
+                              : 0.f;
         }
-        for (; s < splits; ++s) acc += src[(size_t)s * plane];
-        if (bias) acc += bias[e];
-        lg[e] = __builtin_isnan(acc) ? -INFINITY : acc;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s0 + u < splits) acc[q] += v[q][u];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = threadIdx.x + 256 * q;
+        if (e < E) {
+            float l = acc[q];
+            if (bias) l += bias[e];
+            lg[e] = __builtin_isnan(l) ? -INFINITY : l;
+        }
     }
     __syncthreads();
     if (threadIdx.x >= 64) return;

@@ -28,11 +28,11 @@ MOE_ERR_HIP = 6
 
 EXPORTED = ("moe_workspace_bytes", "moe_status_string", "moe_last_error", "moe_router",
             "moe_permute", "moe_grouped_ffn", "moe_shared_ffn", "moe_combine", "moe_forward",
-            "moe_profile_kernel")
+            "moe_profile_kernel", "moe_profile_launches")
 
 # enum moe_kernel
 KERNELS = ("router_gemm", "router_select", "perm_count", "perm_scan", "perm_scatter", "ffn_plan",
-           "gateup_light", "gateup_heavy", "down_light", "down_heavy", "combine")
+           "gateup_light", "gateup_heavy", "down_light", "down_heavy", "combine", "perm_small")
 KERNEL_ID = {n: i for i, n in enumerate(KERNELS)}
 
 
@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [_sp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp]
         L.moe_forward.argtypes = [_sp] + [_vp] * 12 + [ctypes.c_size_t, _vp]
         L.moe_profile_kernel.argtypes = [ctypes.c_int, _vp, _vp]
+        L.moe_profile_launches.argtypes = []
+        L.moe_profile_launches.restype = ctypes.c_longlong
         for name in ("moe_router", "moe_permute", "moe_grouped_ffn", "moe_shared_ffn",
                      "moe_combine", "moe_forward", "moe_profile_kernel"):
             getattr(L, name).restype = ctypes.c_int
@@ -216,6 +218,11 @@ def profile_kernel(name: Optional[str], start=None, stop=None) -> None:
         if not ev.cuda_event:  # torch creates the HIP event on first record
             ev.record()
     _check(lib().moe_profile_kernel(KERNEL_ID[name], start.cuda_event, stop.cuda_event))
+
+
+def profile_launches() -> int:
+    """Launches of the hooked kernel since profile_kernel() set the hook."""
+    return int(lib().moe_profile_launches())
 
 
 class MoELayer:

@@ -76,8 +76,9 @@ typedef struct moe_shape {
     int32_t I_shared;       /* shared expert intermediate size; 0 = no shared expert */
     int32_t renorm;         /* 1: selected weights renormalised to sum to 1; 0: raw probabilities */
     int32_t light_max_rows; /* experts with 1..light_max_rows rows take the light-row loop;
-                               -1 = library default (16); 0 = every expert takes the
-                               heavy tiles; at most 16 */
+                               -1 = library default (64); 0 = every expert takes the
+                               heavy tiles; at most 64.  An expert never gets more than T
+                               rows, so with T <= light_max_rows no heavy kernel runs. */
 } moe_shape;
 
 /* Bytes of workspace every call below needs for `shape` (host-only, pure;
@@ -185,7 +186,8 @@ enum moe_kernel {
     MOE_K_DOWN_LIGHT = 8,
     MOE_K_DOWN_HEAVY = 9,
     MOE_K_COMBINE = 10,
-    MOE_K_COUNT = 11
+    MOE_K_PERM_SMALL = 11, /* whole permute in one block when T*k <= 4096 */
+    MOE_K_COUNT = 12
 };
 
 /* Measurement hook (process-wide, not thread-safe): from now on every launch
@@ -197,6 +199,9 @@ enum moe_kernel {
  * the last launch.  Returns MOE_OK, or MOE_ERR_SHAPE for an unknown kernel,
  * MOE_ERR_NULL for a NULL event while turning the hook on. */
 int moe_profile_kernel(int kernel, void* start, void* stop);
+
+/* Launches of the hooked kernel since the last moe_profile_kernel call. */
+long long moe_profile_launches(void);
 
 #ifdef __cplusplus
 }

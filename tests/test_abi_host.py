@@ -64,7 +64,7 @@ def test_workspace_no_padding(L):
     (dict(k=0), moe.MOE_ERR_SHAPE), (dict(T=-1), moe.MOE_ERR_SHAPE), (dict(k=600), moe.MOE_ERR_SHAPE),
     (dict(H=100), moe.MOE_ERR_UNSUPPORTED), (dict(I=48), moe.MOE_ERR_UNSUPPORTED),
     (dict(E=2048, k=4), moe.MOE_ERR_UNSUPPORTED), (dict(k=33), moe.MOE_ERR_UNSUPPORTED),
-    (dict(renorm=2), moe.MOE_ERR_UNSUPPORTED), (dict(light_max_rows=17), moe.MOE_ERR_UNSUPPORTED),
+    (dict(renorm=2), moe.MOE_ERR_UNSUPPORTED), (dict(light_max_rows=65), moe.MOE_ERR_UNSUPPORTED),
     (dict(I_shared=40), moe.MOE_ERR_UNSUPPORTED), (dict(T=300000000, k=10), moe.MOE_ERR_SHAPE),
 ])
 def test_bad_shapes(L, kw, code):
