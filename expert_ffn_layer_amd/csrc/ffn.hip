@@ -16,8 +16,9 @@
 //  * light: an expert with 1..64 rows; each wave streams 16 weight rows
 //    straight from HBM into registers and keeps one accumulator per 16-row
 //    sub-tile.  This is the decode path: it is bound by weight bytes.
-//  * heavy: 128x128 output tiles, A and B staged through double-buffered LDS,
-//    row sub-tiles past the expert's count skipped.
+//  * heavy: 256x256 output tiles, A and B staged through a ring of LDS
+//    buffers by direct-to-LDS loads, row sub-tiles past the expert's count
+//    skipped, tiles of one expert scheduled together on one XCD.
 // Both paths give every output element the same chain of MFMAs over K in
 // ascending 32-wide steps with the same K-slot assignment, and the same
 // epilogue, so a row's h and y are bitwise identical whichever loop ran it.
@@ -334,34 +335,93 @@ __global__ __launch_bounds__(kThreads) void down_light_kernel(FfnArgs a) {
 }
 
 // ---------------------------------------------------------------- heavy
+// 256x256 output tiles computed by 8 waves (2 per SIMD) in a 2 (rows) x 4
+// (columns) grid; each wave owns a 128x64 block of 16x16 MFMA tiles (32
+// accumulators per lane).  Operands are staged with direct-to-LDS 16-byte
+// loads (global_load_lds_dwordx4) into a ring of kStages buffers, one 32-wide
+// K step per buffer.  Inside a buffer every 16-row x 32-K operand block is
+// stored in MFMA lane order (lane l's 16 bytes at l*16: row l%16, K slots
+// 8*(l/16)..+7), so a fragment read is one contiguous 1 KB access and the
+// load that fills it reads 64 contiguous bytes from each of 16 rows.
 enum class Mode { GateUp, Down };
 
-constexpr int HBM_ = kHeavyBM;  // 128 rows
-constexpr int HBN = 128;        // B rows (output columns, or gate+up rows)
-constexpr int HBK = 64;         // K per LDS stage
-constexpr int HLDK = HBK + 8;   // padded LDS row (bf16)
+constexpr int kHeavyThreads = 512;
+constexpr int kHeavyWaves = kHeavyThreads / 64;
+constexpr int kTM = kHeavyBM;  // 256 rows per tile
+constexpr int kTN = 256;       // B rows per tile (output columns, or 128 gate + 128 up rows)
+constexpr int kWTN = kTN / 4;  // 64 columns per wave
+#ifndef MOE_HEAVY_STAGES
+#define MOE_HEAVY_STAGES 4
+#endif
+#ifndef MOE_HEAVY_XCD_SLICES
+#define MOE_HEAVY_XCD_SLICES 8
+#endif
+constexpr int kStages = MOE_HEAVY_STAGES;  // LDS ring depth; kStages - 1 K steps in flight
+constexpr int kFrag = 1024;    // bytes of one 16 x 32 bf16 operand block
+constexpr int kFragsA = kTM / 16, kFragsB = kTN / 16;
+constexpr int kStageBytes = (kFragsA + kFragsB) * kFrag;       // 32 KB
+constexpr int kDmaPerWave = (kFragsA + kFragsB) / kHeavyWaves;  // 4 loads per wave per K step
+// The gate|up epilogue parks each wave's up accumulators (8 x 2 tiles x 64
+// lanes x 16 B) in its share of the idle ring.
+static_assert(kStages * kStageBytes / kHeavyWaves >= 8 * 2 * 64 * 16, "stash does not fit the ring");
+constexpr int kXcds = MOE_HEAVY_XCD_SLICES;  // MI355X: 8 XCDs, workgroups dispatched round-robin
+
+typedef __attribute__((address_space(1))) const void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+__device__ __forceinline__ void lds_dma16(const uint16_t* src, char* dst) {
+    __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, 0);
+}
+
+// Wait until at most n of this wave's vector-memory instructions are
+// outstanding (vmcnt; expcnt and lgkmcnt left unconstrained).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+
+// Workgroup barrier without the memory fences __syncthreads() adds: those
+// wait for every outstanding load (vmcnt(0)) and would drain the LDS ring.
+// Each wave first waits for its own part of the stage (wait_vmcnt); the empty
+// asm statements keep the compiler from moving LDS accesses across.
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 template <Mode M>
-__global__ __launch_bounds__(kThreads) void ffn_heavy_kernel(FfnArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][HBM_][HLDK];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][HBN][HLDK];
+__global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
+    __shared__ __attribute__((aligned(1024))) char lds[kStages][kStageBytes];
 
     const int N = (M == Mode::GateUp) ? 2 * a.I : a.H;
     // split_h: the down GEMM's K runs over [hi | lo] (2I) against W_down twice.
     const int K = (M == Mode::GateUp) ? a.H : (a.split_h ? 2 * a.I : a.I);
     const int hstride = a.split_h ? 2 * a.I : a.I;  // row pitch of h
-    const int nblk = (N + HBN - 1) / HBN;
-    const int ntiles = a.plan ? a.plan[1] : (a.dense_rows + HBM_ - 1) / HBM_;
+    const int nblk = (N + kTN - 1) / kTN;
+    const int ntiles = a.plan ? a.plan[1] : (a.dense_rows + kTM - 1) / kTM;
     const long long nwork = (long long)ntiles * nblk;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: LDS offsets in SGPRs
+    const int wm = wave >> 2, wn = wave & 3;
     const int l16 = lane & 15, g = lane >> 4;
-    const int nst = (K + HBK - 1) / HBK;
-    // global->LDS copy: thread covers rows (tid/8) + 32q, 16 bytes at (tid%8)*8
-    const int ld_row = tid >> 3, ld_k = (tid & 7) * 8;
+    const int nst = K / 32;  // K % 32 == 0
 
-    for (long long wi = blockIdx.x; wi < nwork; wi += gridDim.x) {
+    // XCD-aware static schedule.  The work list is tile-major (tiles of one
+    // expert are adjacent) with the N block fastest; it is cut into nslice
+    // contiguous slices and slice x is served, round-robin, by the blocks that
+    // share XCD x (blockIdx % nslice), so the M and N tiles of one expert run
+    // at the same time on one XCD and share weights and rows through its L2.
+    const int nslice = min(kXcds, (int)gridDim.x);
+    const int xs = blockIdx.x % nslice;
+    const int nb_x = ((int)gridDim.x - xs + nslice - 1) / nslice;
+    const int jx = blockIdx.x / nslice;
+    const long long per = (nwork + nslice - 1) / nslice;
+    const long long wbeg = xs * per;
+    const long long wend = min(nwork, wbeg + per);
+
+    for (long long wi = wbeg + jx; wi < wend; wi += nb_x) {
         const int tile = (int)(wi / nblk), nb = (int)(wi % nblk);
         int e, r0, m0, rows;
         if (a.plan) {
@@ -369,125 +429,171 @@ __global__ __launch_bounds__(kThreads) void ffn_heavy_kernel(FfnArgs a) {
             e = tl[2 * tile];
             m0 = tl[2 * tile + 1];
             r0 = a.offsets[e];
-            rows = min(HBM_, a.offsets[e + 1] - r0 - m0);
+            rows = min(kTM, a.offsets[e + 1] - r0 - m0);
         } else {
             e = 0;
             r0 = 0;
-            m0 = tile * HBM_;
-            rows = min(HBM_, a.dense_rows - m0);
+            m0 = tile * kTM;
+            rows = min(kTM, a.dense_rows - m0);
         }
 
-        const uint16_t* arow[4];
-        const uint16_t* brow[4];
-        bool aok[4], bok[4];
+        // This wave loads A row blocks 2*wave, 2*wave+1 and the same B blocks.
+        const uint16_t* asrc[2];
+        const uint16_t* bsrc[2];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r = ld_row + 32 * q;
-            aok[q] = r < rows;
-            const int rr = aok[q] ? r : 0;
+        for (int i = 0; i < 2; ++i) {
+            const int r = (2 * wave + i) * 16 + l16;  // row within the tile
+            const int rr = r < rows ? r : 0;          // rows past the count: any valid row
             if (M == Mode::GateUp) {
                 const int tok = a.sorted_ids ? a.sorted_ids[r0 + m0 + rr] : r0 + m0 + rr;
-                arow[q] = a.x + (size_t)tok * a.H + ld_k;
-                const int hc = nb * (HBN / 2) + (r >> 4) * 8 + (r & 7);
-                bok[q] = hc < a.I;
-                const int wr = ((r & 15) < 8) ? hc : a.I + hc;
-                brow[q] = a.w_gu + ((size_t)e * 2 * a.I + (bok[q] ? wr : 0)) * a.H + ld_k;
+                asrc[i] = a.x + (size_t)tok * a.H + 8 * g;
+                // 16-row blocks alternate: block 2p = gate rows, 2p+1 = the
+                // matching up rows, so g and u of an element share a lane.
+                const int hc = nb * (kTN / 2) + (r >> 5) * 16 + (r & 15);
+                const int wr = (hc < a.I) ? (((r & 16) == 0) ? hc : a.I + hc) : 0;
+                bsrc[i] = a.w_gu + ((size_t)e * 2 * a.I + wr) * a.H + 8 * g;
             } else {
-                arow[q] = a.h + (size_t)(r0 + m0 + rr) * hstride + ld_k;
-                const int c = nb * HBN + r;
-                bok[q] = c < a.H;
-                brow[q] = a.w_dn + ((size_t)e * a.H + (bok[q] ? c : 0)) * a.I + ld_k;
+                asrc[i] = a.h + (size_t)(r0 + m0 + rr) * hstride + 8 * g;
+                const int c = nb * kTN + r;
+                bsrc[i] = a.w_dn + ((size_t)e * a.H + (c < a.H ? c : 0)) * a.I + 8 * g;
             }
         }
-
-        u32x4_t ra[4], rb[4];
-        auto gload = [&](int st) {
-            const int kk = st * HBK;
-            const bool kin = kk + ld_k < K;
+        auto issue = [&](int st) {
+            char* buf = lds[st % kStages];
+            const int kk = st * 32;
             // down with split_h: K columns past I wrap back onto W_down
-            const int kb = (M == Mode::Down && kk + ld_k >= a.I) ? kk - a.I : kk;
+            const int kb = (M == Mode::Down && kk >= a.I) ? kk - a.I : kk;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                ra[q] = (aok[q] && kin) ? *reinterpret_cast<const u32x4_t*>(arow[q] + kk)
-                                        : u32x4_t{0u, 0u, 0u, 0u};
-                rb[q] = (bok[q] && kin) ? *reinterpret_cast<const u32x4_t*>(brow[q] + kb)
-                                        : u32x4_t{0u, 0u, 0u, 0u};
-            }
-        };
-        auto sstore = [&](int buf) {
+            for (int i = 0; i < 2; ++i) lds_dma16(asrc[i] + kk, buf + (2 * wave + i) * kFrag);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                *reinterpret_cast<u32x4_t*>(&As[buf][ld_row + 32 * q][ld_k]) = ra[q];
-                *reinterpret_cast<u32x4_t*>(&Bs[buf][ld_row + 32 * q][ld_k]) = rb[q];
-            }
+            for (int i = 0; i < 2; ++i)
+                lds_dma16(bsrc[i] + kb, buf + (kFragsA + 2 * wave + i) * kFrag);
         };
 
-        floatx4_t acc[4][4];
+        floatx4_t acc[8][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-        // row sub-tiles of this wave that hold any of the tile's rows
-        const int mt_live = max(0, min(4, (rows - wm * 64 + 15) / 16));
 
-        gload(0);
-        sstore(0);
-        __syncthreads();
-        for (int st = 0; st < nst; ++st) {
-            const int buf = st & 1;
-            if (st + 1 < nst) gload(st + 1);
+        // This wave's operand fragments of one K step.
+        auto read_frags = [&](int st, bf16x8_t (&af)[8], bf16x8_t (&bf)[4]) {
+            const char* buf = lds[st % kStages];
 #pragma unroll
-            for (int kk = 0; kk < HBK / 32; ++kk) {
-                if (st * HBK + kk * 32 < K) {
-                    bf16x8_t af[4], bfr[4];
+            for (int j = 0; j < 4; ++j)
+                bf[j] = *reinterpret_cast<const bf16x8_t*>(buf + (kFragsA + wn * 4 + j) * kFrag +
+                                                           lane * 16);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        bfr[j] = __builtin_bit_cast(
-                            bf16x8_t, *reinterpret_cast<const u32x4_t*>(
-                                          &Bs[buf][wn * 64 + j * 16 + l16][kk * 32 + 8 * g]));
+            for (int i = 0; i < 8; ++i)
+                af[i] = *reinterpret_cast<const bf16x8_t*>(buf + (wm * 8 + i) * kFrag + lane * 16);
+        };
+        // Wait for stage st (at most the stages after it still loading), then
+        // barrier: every wave's share of st is in, and every wave has
+        // finished reading the buffer that the next issue() refills.
+        auto stage_ready = [&](int st) {
+            const int later = min(kStages - 2, nst - 1 - st);
+            static_assert(kStages >= 2 && kStages <= 5, "ring depth");
+            if (later >= 3)
+                wait_vmcnt<3 * kDmaPerWave>();
+            else if (later == 2)
+                wait_vmcnt<2 * kDmaPerWave>();
+            else if (later == 1)
+                wait_vmcnt<kDmaPerWave>();
+            else
+                wait_vmcnt<0>();
+            ring_barrier();
+        };
+        // Every wave runs all its row sub-tiles: a block takes as long as its
+        // slowest wave, so skipping rows past the count in one wave would not
+        // shorten the tile.
+        auto mfma_rows = [&](int i0, const bf16x8_t (&af)[8], const bf16x8_t (&bf)[4]) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        if (i < mt_live) {
-                            af[i] = __builtin_bit_cast(
-                                bf16x8_t, *reinterpret_cast<const u32x4_t*>(
-                                              &As[buf][wm * 64 + i * 16 + l16][kk * 32 + 8 * g]));
+            for (int i = i0; i < i0 + 4; ++i)
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(af[i], bfr[j], acc[i][j]);
-                        }
-                    }
-                }
+                for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(af[i], bf[j], acc[i][j]);
+        };
+        // One K step: half of the MFMAs on (ca, cb); then, once this wave's
+        // reads of stage st are complete, the barrier that admits stage st+1
+        // (and lets stage st's buffer be refilled), the next issue and the
+        // reads of stage st+1 into (na, nb); then the other half, which hides
+        // those reads.  Unrolled by two so the fragment sets swap roles
+        // without copies.
+        auto kstep = [&](int st, const bf16x8_t (&ca)[8], const bf16x8_t (&cb)[4],
+                         bf16x8_t (&na)[8], bf16x8_t (&nb)[4]) {
+            mfma_rows(0, ca, cb);
+            if (st + 1 < nst) {
+                __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+                stage_ready(st + 1);
+                if (st + kStages < nst) issue(st + kStages);
+                read_frags(st + 1, na, nb);
             }
-            if (st + 1 < nst) sstore(buf ^ 1);
-            __syncthreads();
+            mfma_rows(4, ca, cb);
+        };
+
+#pragma unroll
+        for (int s = 0; s < kStages - 1; ++s)
+            if (s < nst) issue(s);
+        stage_ready(0);
+        if (kStages - 1 < nst) issue(kStages - 1);
+        bf16x8_t fa0[8], fb0[4], fa1[8], fb1[4];
+        read_frags(0, fa0, fb0);
+        for (int st = 0; st < nst; st += 2) {
+            kstep(st, fa0, fb0, fa1, fb1);
+            if (st + 1 < nst) kstep(st + 1, fa1, fb1, fa0, fb0);
         }
+        wait_vmcnt<0>();
+        ring_barrier();  // the ring is idle: the epilogue may use it
 
         // epilogue
+        if (M == Mode::GateUp) {
+            // Park the up accumulators in this wave's 16 KB of the idle ring
+            // (lane-private slots), then read each back beside its gate value.
+            char* stash = &lds[0][0] + wave * (kStages * kStageBytes / kHeavyWaves);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+                for (int jp = 0; jp < 2; ++jp)
+                    *reinterpret_cast<floatx4_t*>(stash + ((i * 2 + jp) * 64 + lane) * 16) =
+                        acc[i][2 * jp + 1];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = wm * 64 + i * 16 + 4 * g + r;
-                    const float v = acc[i][j][r];
-                    if (M == Mode::GateUp) {
-                        const float up = __shfl_down(v, 8, 64);
-                        const int hc = nb * (HBN / 2) + (wn * 4 + j) * 8 + l16;
-                        if (l16 < 8 && row < rows && hc < a.I) {
-                            const float hv = swiglu(v, up);
+            for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                for (int jp = 0; jp < 2; ++jp) {
+                    const floatx4_t up =
+                        *reinterpret_cast<const floatx4_t*>(stash + ((i * 2 + jp) * 64 + lane) * 16);
+                    const int hc = nb * (kTN / 2) + (wn * 2 + jp) * 16 + l16;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = wm * 128 + i * 16 + 4 * g + r;
+                        if (row < rows && hc < a.I) {
+                            const float hv = swiglu(acc[i][2 * jp][r], up[r]);
                             const uint32_t hi = f32_to_bf16_bits(hv);
                             uint16_t* hr = a.h + (size_t)(r0 + m0 + row) * hstride;
                             hr[hc] = (uint16_t)hi;
                             if (a.split_h)
                                 hr[a.I + hc] = (uint16_t)f32_to_bf16_bits(hv - bf16_bits_to_f32(hi));
                         }
-                    } else {
-                        const int c = nb * HBN + wn * 64 + j * 16 + l16;
-                        if (row < rows && c < a.H) a.y[(size_t)(r0 + m0 + row) * a.H + c] = v;
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int c = nb * kTN + wn * kWTN + j * 16 + l16;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = wm * 128 + i * 16 + 4 * g + r;
+                        if (row < rows && c < a.H) a.y[(size_t)(r0 + m0 + row) * a.H + c] = acc[i][j][r];
                     }
                 }
             }
         }
+        // Drain this tile's stores too: the next tile's stage waits count
+        // outstanding vector-memory operations and must see only its loads.
+        wait_vmcnt<0>();
+        ring_barrier();  // epilogue reads of the stash done before the ring is refilled
     }
 }
 
@@ -516,11 +622,11 @@ hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t st) {
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    const long long tiles = a.plan ? a.max_tiles : (a.dense_rows + HBM_ - 1) / HBM_;
-    const long long work = tiles * ((2 * a.I + HBN - 1) / HBN);
+    const long long tiles = a.plan ? a.max_tiles : (a.dense_rows + kTM - 1) / kTM;
+    const long long work = tiles * ((2 * a.I + kTN - 1) / kTN);
     if (work > 0) {
         prof_begin(K_GATEUP_HEAVY, st);
-        ffn_heavy_kernel<Mode::GateUp><<<grid_for(work, 2, a.num_cu), kThreads, 0, st>>>(a);
+        ffn_heavy_kernel<Mode::GateUp><<<grid_for(work, 1, a.num_cu), kHeavyThreads, 0, st>>>(a);
         prof_end(K_GATEUP_HEAVY, st);
         return hipGetLastError();
     }
@@ -538,11 +644,11 @@ hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st) {
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    const long long tiles = a.plan ? a.max_tiles : (a.dense_rows + HBM_ - 1) / HBM_;
-    const long long work = tiles * ((a.H + HBN - 1) / HBN);
+    const long long tiles = a.plan ? a.max_tiles : (a.dense_rows + kTM - 1) / kTM;
+    const long long work = tiles * ((a.H + kTN - 1) / kTN);
     if (work > 0) {
         prof_begin(K_DOWN_HEAVY, st);
-        ffn_heavy_kernel<Mode::Down><<<grid_for(work, 2, a.num_cu), kThreads, 0, st>>>(a);
+        ffn_heavy_kernel<Mode::Down><<<grid_for(work, 1, a.num_cu), kHeavyThreads, 0, st>>>(a);
         prof_end(K_DOWN_HEAVY, st);
         return hipGetLastError();
     }

@@ -54,7 +54,7 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* chun
 
 // ---- grouped FFN --------------------------------------------------------
 constexpr int kLightRowsMax = 64;  // up to four 16-row MFMA sub-tiles
-constexpr int kHeavyBM = 128;      // rows per heavy tile
+constexpr int kHeavyBM = 256;      // rows per heavy tile
 // Plan layout (int32): [0] n_light, [1] n_tiles, [16 ..16+E) light expert
 // ids, [16+E ..) heavy tiles as (expert, first row) pairs.
 constexpr int kPlanHeader = 16;
