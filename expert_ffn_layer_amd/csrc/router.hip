@@ -1,5 +1,5 @@
-// Router: fp32 gate GEMM on MFMA, then a wave-per-token softmax and
-// register top-k.
+// Router: fp32 gate GEMM (on bf16 MFMA with exact three-term weights), then
+// a block-per-token softmax and register top-k.
 //
 // The pages compute the router logits on the matrix unit and hand them to
 // the vector unit for top_k, and name the hand-off as a serialisation point
@@ -16,17 +16,30 @@ namespace {
 constexpr int BT = kRouterBT;
 constexpr int BE = kRouterBE;
 constexpr int BK = kRouterBK;
-constexpr int PAD = 16;  // floats; spreads consecutive K rows over the LDS banks
+constexpr int LDK = BK + 8;  // bf16 row pitch in LDS (80 bytes): spreads rows over the banks
+
+// fp32 -> three bf16 terms with hi + mid + lo == v up to 2^-24 relative
+// (each term rounds the exact fp32 remainder of the previous ones).
+__device__ __forceinline__ void split3(float v, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+    hi = f32_to_bf16_bits(v);
+    const float r1 = v - bf16_bits_to_f32(hi);
+    mid = f32_to_bf16_bits(r1);
+    const float r2 = r1 - bf16_bits_to_f32(mid);
+    lo = f32_to_bf16_bits(r2);
+}
 
 // part[s][t][e] for one 128x128 (token x expert) tile and one hidden slice.
-// 256 threads = 4 waves in a 2x2 grid, each a 64x64 block of 16x16 MFMA
-// tiles (v_mfma_f32_16x16x4_f32: lane l gives A[l%16][l/16], B[l/16][l%16]).
+// The fp32 router product runs on bf16 MFMA: x is bf16 already, and every
+// router weight enters as three bf16 terms (split3), so each product
+// x*w_term is exact and the MFMA accumulates in fp32.  256 threads = 4 waves
+// in a 2x2 grid, each a 64x64 block of 16x16 tiles
+// (v_mfma_f32_16x16x32_bf16, 3 MFMAs per tile and K step).
 __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ wg,
                                                           float* __restrict__ part, int T,
                                                           int H, int E, int k_per_split) {
-    __shared__ __attribute__((aligned(16))) float xs[BK][BT + PAD];
-    __shared__ __attribute__((aligned(16))) float ws[BK][BE + PAD];
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][BT][LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t ws[2][3][BE][LDK];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -38,53 +51,47 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
     const int s = blockIdx.z;
     const int kbeg = s * k_per_split;
     const int kend = kbeg + k_per_split;
-    const bool e_vec = (E % 4) == 0;
+    // router-weight staging: this thread owns expert e0+el, 16 consecutive k
+    const int el = tid & (BE - 1), kh = tid >> 7;
+    const bool e_ok = e0 + el < E;
 
-    // Register staging of one K stage: 2 x-chunks (8 bf16) and 4 wg float4.
     u32x4_t xr[2];
-    float4 wr[4];
-
+    float wr[16];
     auto load_stage = [&](int k0) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int c = tid + 256 * q;
             const int t = c >> 2, kc = (c & 3) * 8;
-            if (t0 + t < T)
-                xr[q] = *reinterpret_cast<const u32x4_t*>(x + (size_t)(t0 + t) * H + k0 + kc);
-            else
-                xr[q] = u32x4_t{0u, 0u, 0u, 0u};
+            xr[q] = (t0 + t < T) ? *reinterpret_cast<const u32x4_t*>(x + (size_t)(t0 + t) * H + k0 + kc)
+                                 : u32x4_t{0u, 0u, 0u, 0u};
         }
+        const float* src = wg + (size_t)(k0 + 16 * kh) * E + e0 + el;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int c = tid + 256 * q;
-            const int kk = c >> 5, e4 = (c & 31) * 4;
-            const float* src = wg + (size_t)(k0 + kk) * E + e0 + e4;
-            if (e_vec && e0 + e4 + 3 < E) {
-                wr[q] = *reinterpret_cast<const float4*>(src);
-            } else {
-                wr[q].x = (e0 + e4 + 0 < E) ? src[0] : 0.f;
-                wr[q].y = (e0 + e4 + 1 < E) ? src[1] : 0.f;
-                wr[q].z = (e0 + e4 + 2 < E) ? src[2] : 0.f;
-                wr[q].w = (e0 + e4 + 3 < E) ? src[3] : 0.f;
-            }
-        }
+        for (int j = 0; j < 16; ++j) wr[j] = e_ok ? src[(size_t)j * E] : 0.f;
     };
-    auto store_stage = [&]() {
+    auto store_stage = [&](int buf) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int c = tid + 256 * q;
             const int t = c >> 2, kc = (c & 3) * 8;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                xs[kc + 2 * j][t] = bf16_bits_to_f32(xr[q][j] & 0xffffu);
-                xs[kc + 2 * j + 1][t] = bf16_bits_to_f32(xr[q][j] >> 16);
-            }
+            *reinterpret_cast<u32x4_t*>(&xs[buf][t][kc]) = xr[q];
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int c = tid + 256 * q;
-            const int kk = c >> 5, e4 = (c & 31) * 4;
-            *reinterpret_cast<float4*>(&ws[kk][e4]) = wr[q];
+        for (int h8 = 0; h8 < 2; ++h8) {
+            uint32_t p[3][4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t a0, a1, a2, b0, b1, b2;
+                split3(wr[8 * h8 + 2 * j], a0, a1, a2);
+                split3(wr[8 * h8 + 2 * j + 1], b0, b1, b2);
+                p[0][j] = a0 | (b0 << 16);
+                p[1][j] = a1 | (b1 << 16);
+                p[2][j] = a2 | (b2 << 16);
+            }
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl)
+                *reinterpret_cast<u32x4_t*>(&ws[buf][pl][el][16 * kh + 8 * h8]) =
+                    u32x4_t{p[pl][0], p[pl][1], p[pl][2], p[pl][3]};
         }
     };
 
@@ -95,29 +102,31 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
         for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
     load_stage(kbeg);
-    store_stage();
+    store_stage(0);
     __syncthreads();
+    int buf = 0;
     for (int k0 = kbeg; k0 < kend; k0 += BK) {
         const bool more = k0 + BK < kend;
         if (more) load_stage(k0 + BK);
+        bf16x8_t af[4], bf[3][4];
 #pragma unroll
-        for (int kk = 0; kk < BK; kk += 4) {
-            float a[4], b[4];
+        for (int i = 0; i < 4; ++i)
+            af[i] = *reinterpret_cast<const bf16x8_t*>(&xs[buf][wm * 64 + i * 16 + l16][8 * g]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = xs[kk + g][wm * 64 + i * 16 + l16];
+        for (int pl = 0; pl < 3; ++pl)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = ws[kk + g][wn * 64 + j * 16 + l16];
+            for (int j = 0; j < 4; ++j)
+                bf[pl][j] =
+                    *reinterpret_cast<const bf16x8_t*>(&ws[buf][pl][wn * 64 + j * 16 + l16][8 * g]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int pl = 0; pl < 3; ++pl) acc[i][j] = mfma_16x16x32(af[i], bf[pl][j], acc[i][j]);
+        if (more) store_stage(buf ^ 1);
         __syncthreads();
-        if (more) {
-            store_stage();
-            __syncthreads();
-        }
+        buf ^= 1;
     }
 
     float* out = part + (size_t)s * T * E;
