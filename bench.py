@@ -48,7 +48,138 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=64, help="tokens in the oracle's sample")
     p.add_argument("--no-copy-calibration", action="store_true",
                    help="skip the untimed 1 GiB reference copy used to scale rocprof counters")
+    p.add_argument("--summarize", nargs=4, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR", "LOG"),
+                   help="no GPU: turn the rocprofv3 output of the three profiling runs of "
+                        "--config (and the kernel-trace run's stdout LOG) into the summaries "
+                        "under profiles/")
     return p.parse_args()
+
+
+# The profiling runs that profiles/<kernel>__<workload>.{md,traffic.json}
+# summarise; $R is the repository root, run from /tmp with TMPDIR=/tmp.
+PROFILE_COMMANDS = (
+    "rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/kt_{cfg} -o bench -- "
+    "python3 $R/bench.py --config {cfg} --steps 10 --warmup 2 --no-cpu-baseline "
+    "> $R/gpurun_out/kt_{cfg}.log",
+    "timeout -s KILL 150 rocprofv3 --pmc FETCH_SIZE -f csv -d $R/gpurun_out/fetch_{cfg} -o bench -- "
+    "python3 $R/bench.py --config {cfg} --steps 3 --warmup 1 --no-cpu-baseline",
+    "timeout -s KILL 150 rocprofv3 --pmc WRITE_SIZE -f csv -d $R/gpurun_out/write_{cfg} -o bench -- "
+    "python3 $R/bench.py --config {cfg} --steps 3 --warmup 1 --no-cpu-baseline",
+    "python3 $R/bench.py --config {cfg} --summarize $R/gpurun_out/kt_{cfg} "
+    "$R/gpurun_out/fetch_{cfg} $R/gpurun_out/write_{cfg} $R/gpurun_out/kt_{cfg}.log",
+)
+# bench.py's own untimed reference copy (torch.neg over 2^28 fp32 values):
+# it reads and writes exactly 1 GiB.
+COPY_BYTES = 1 << 30
+
+
+def kernel_label(name: str):
+    """The KERNELS name of a rocprof kernel name, or None if it is not ours."""
+    import re
+    m = re.search(r"moe::\(anonymous namespace\)::(\w+)", name)
+    if not m:
+        return None
+    base = m.group(1)
+    if base == "ffn_heavy_kernel":
+        return "gateup_heavy" if "Mode)0" in name else "down_heavy"
+    return base[:-len("_kernel")] if base.endswith("_kernel") else base
+
+
+def summarize(args):
+    """Per-kernel duration (kernel trace) and HBM traffic (FETCH_SIZE and
+    WRITE_SIZE in KiB per dispatch, each scaled by what the counter reads for
+    the 1 GiB reference copy) -> profiles/<dominant>__<workload>.md and
+    .traffic.json."""
+    import csv
+    from expert_ffn_layer_amd import synth
+
+    kt_dir, fetch_dir, write_dir, log = args.summarize
+    cfg = synth.CONFIGS[args.config]
+    workload = synth.workload_name(cfg)
+
+    def one_csv(d, suffix):
+        names = [f for f in os.listdir(d) if f.endswith(suffix)]
+        assert len(names) == 1, (d, names)
+        with open(os.path.join(d, names[0])) as f:
+            return list(csv.DictReader(f))
+
+    stats = {}
+    for r in one_csv(kt_dir, "kernel_stats.csv"):
+        lab = kernel_label(r["Name"])
+        if lab:
+            stats[lab] = dict(calls=int(r["Calls"]), avg_us=float(r["AverageNs"]) / 1e3,
+                              min_us=float(r["MinNs"]) / 1e3, max_us=float(r["MaxNs"]) / 1e3,
+                              total_us=float(r["TotalDurationNs"]) / 1e3)
+
+    def counter(d):
+        per, copy = {}, None
+        for r in one_csv(d, "counter_collection.csv"):
+            v = float(r["Counter_Value"])
+            if "neg_kernel_cuda" in r["Kernel_Name"]:
+                copy = v
+                continue
+            lab = kernel_label(r["Kernel_Name"])
+            if lab:
+                per.setdefault(lab, []).append(v)
+        assert copy, f"no reference copy kernel in {d}"
+        scale = COPY_BYTES / (copy * 1024.0)
+        return {k: sum(v) / len(v) * 1024.0 * scale for k, v in per.items()}, scale
+
+    fetch, f_scale = counter(fetch_dir)
+    write, w_scale = counter(write_dir)
+    rec = None
+    with open(log) as f:
+        for line in f:
+            if line.startswith('{"metric"'):
+                rec = json.loads(line)
+    assert rec and rec["config"]["workload"] == workload, "log is not this workload's bench line"
+    dom = max(stats, key=lambda k: stats[k]["total_us"])
+    src_hash = rec["kernel_source_hash"]
+    assert src_hash == kernel_source_hash(), "kernel sources changed since the profiled run"
+
+    traffic = fetch[dom] + write[dom]
+    roof = rec["roofline"]
+    out = {"kernel": dom, "workload": workload, "kernel_source_hash": src_hash,
+           "hbm_bytes_per_launch": int(round(traffic)),
+           "fetch_bytes_per_launch": int(round(fetch[dom])),
+           "write_bytes_per_launch": int(round(write[dom])),
+           "fetch_size_scale": round(f_scale, 4), "write_size_scale": round(w_scale, 4),
+           "algorithmic_bytes_per_launch": roof["algorithmic_bytes"] if roof["kernel"] == dom
+           else None,
+           "avg_duration_us": round(stats[dom]["avg_us"], 2)}
+    base = os.path.join(PROFILES, f"{dom}__{workload}")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(base + ".traffic.json", "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+
+    cmds = "\n".join(c.format(cfg=args.config) for c in PROFILE_COMMANDS)
+    lines = [f"# {dom} on {workload}", "",
+             "rocprofv3 summary of bench.py on one MI355X (gfx950).  Commands, from /tmp with",
+             "TMPDIR=/tmp, $R the repository root:", "", "```", cmds, "```", "",
+             f"Dominant kernel: **{dom}**, average {stats[dom]['avg_us']:.1f} us over "
+             f"{stats[dom]['calls']} launches (kernel trace); bench.py's own HIP-event timing "
+             f"of it in the same run: {roof['kernel_us']:.1f} us.",
+             "", f"bench line: {rec['value']:.1f} {rec['unit']}, {rec['ms_per_step']:.4f} ms/step; "
+             f"roofline {roof['bound']} {roof['achieved']} {roof['unit']} "
+             f"(frac {roof['frac']}) for {roof['kernel']}.", "",
+             f"Counter scale: FETCH_SIZE x {f_scale:.4f}, WRITE_SIZE x {w_scale:.4f} (the "
+             "counters' readings for bench.py's untimed 1 GiB read + 1 GiB write reference "
+             "copy).", "",
+             "| kernel | calls | avg us | min us | max us | HBM read MB/launch | "
+             "HBM write MB/launch |", "|---|---|---|---|---|---|---|"]
+    for k in sorted(stats, key=lambda k: -stats[k]["total_us"]):
+        st = stats[k]
+        lines.append(f"| {k} | {st['calls']} | {st['avg_us']:.1f} | {st['min_us']:.1f} | "
+                     f"{st['max_us']:.1f} | {fetch.get(k, 0) / 1e6:.2f} | "
+                     f"{write.get(k, 0) / 1e6:.2f} |")
+    alg = out["algorithmic_bytes_per_launch"]
+    if alg:
+        lines += ["", f"{dom}: measured HBM traffic {traffic / 1e6:.1f} MB per launch against "
+                      f"{alg / 1e6:.1f} MB algorithmic ({traffic / alg:.2f}x)."]
+    with open(base + ".md", "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {base}.md and .traffic.json")
 
 
 def kernel_source_hash() -> str:
@@ -75,6 +206,9 @@ def committed_traffic(kernel: str, workload: str, src_hash: str):
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -145,8 +279,9 @@ def main():
     # Algorithmic work, from this run's own routing.
     cnt = counts.cpu().numpy().astype(np.int64)
     touched = int((cnt > 0).sum())
-    light_rows = int(cnt[(cnt > 0) & (cnt <= 16)].sum())
-    light_experts = int(((cnt > 0) & (cnt <= 16)).sum())
+    light = (cnt > 0) & (cnt <= moe.LIGHT_MAX_ROWS)
+    light_rows = int(cnt[light].sum())
+    light_experts = int(light.sum())
     A = cfg.T * cfg.k
     H, I = cfg.H, cfg.I
     x_bytes = cfg.T * H * 2

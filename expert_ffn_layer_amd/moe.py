@@ -34,6 +34,9 @@ EXPORTED = ("moe_workspace_bytes", "moe_status_string", "moe_last_error", "moe_r
 KERNELS = ("router_gemm", "router_select", "perm_count", "perm_scan", "perm_scatter", "ffn_plan",
            "gateup_light", "gateup_heavy", "down_light", "down_heavy", "combine", "perm_small")
 KERNEL_ID = {n: i for i, n in enumerate(KERNELS)}
+# Experts with 1..LIGHT_MAX_ROWS rows take the light loop when
+# light_max_rows is left at -1 (the C ABI's default).
+LIGHT_MAX_ROWS = 64
 
 
 class MoeShape(ctypes.Structure):
