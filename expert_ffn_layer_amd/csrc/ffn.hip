@@ -338,11 +338,17 @@ __global__ __launch_bounds__(kThreads) void down_light_kernel(FfnArgs a) {
 // 256x256 output tiles computed by 8 waves (2 per SIMD) in a 2 (rows) x 4
 // (columns) grid; each wave owns a 128x64 block of 16x16 MFMA tiles (32
 // accumulators per lane).  Operands are staged with direct-to-LDS 16-byte
-// loads (global_load_lds_dwordx4) into a ring of kStages buffers, one 32-wide
-// K step per buffer.  Inside a buffer every 16-row x 32-K operand block is
-// stored in MFMA lane order (lane l's 16 bytes at l*16: row l%16, K slots
-// 8*(l/16)..+7), so a fragment read is one contiguous 1 KB access and the
-// load that fills it reads 64 contiguous bytes from each of 16 rows.
+// loads (global_load_lds_dwordx4) into a two-buffer ring, one 64-wide K step
+// per buffer, so that every load instruction reads 8 whole rows of 128
+// contiguous bytes (full cache lines).
+//
+// LDS layout of a stage: A then B, each a run of 1 KB blocks, block b holding
+// tile rows 8b..8b+7 x the stage's 64 K values.  Inside a block, 16-byte slot
+// p holds row p/8, K chunk (p%8) ^ (p/8) ^ (b%2) (chunk c = K values
+// 8c..8c+7).  The load that fills a block therefore reads one 128-byte line
+// per 8 lanes, and the MFMA fragment read (lane l: row l%16, chunk
+// l/16 + 4*half) lands its 8 lanes of a row group on 8 different 16-byte bank
+// groups, and its two row groups on the two complementary sets.
 enum class Mode { GateUp, Down };
 
 constexpr int kHeavyThreads = 512;
@@ -350,17 +356,17 @@ constexpr int kHeavyWaves = kHeavyThreads / 64;
 constexpr int kTM = kHeavyBM;  // 256 rows per tile
 constexpr int kTN = 256;       // B rows per tile (output columns, or 128 gate + 128 up rows)
 constexpr int kWTN = kTN / 4;  // 64 columns per wave
-#ifndef MOE_HEAVY_STAGES
-#define MOE_HEAVY_STAGES 4
-#endif
 #ifndef MOE_HEAVY_XCD_SLICES
 #define MOE_HEAVY_XCD_SLICES 8
 #endif
-constexpr int kStages = MOE_HEAVY_STAGES;  // LDS ring depth; kStages - 1 K steps in flight
-constexpr int kFrag = 1024;    // bytes of one 16 x 32 bf16 operand block
-constexpr int kFragsA = kTM / 16, kFragsB = kTN / 16;
-constexpr int kStageBytes = (kFragsA + kFragsB) * kFrag;       // 32 KB
-constexpr int kDmaPerWave = (kFragsA + kFragsB) / kHeavyWaves;  // 4 loads per wave per K step
+constexpr int kStages = 2;         // LDS ring depth: one K step computing, one loading
+constexpr int kKS = 64;            // K values per stage
+constexpr int kBlk = 1024;         // bytes of one 8-row x 64-K block
+constexpr int kBlocksA = kTM / 8, kBlocksB = kTN / 8;
+constexpr int kStageBytes = (kBlocksA + kBlocksB) * kBlk;         // 64 KB
+constexpr int kDmaPerWave = (kBlocksA + kBlocksB) / kHeavyWaves;  // 8 loads per wave per stage
+constexpr int kBlkPerWave = kBlocksA / kHeavyWaves;               // 4 A (and 4 B) blocks per wave
+static_assert(kBlocksA % kHeavyWaves == 0 && kBlocksB == kBlocksA, "block split");
 // The gate|up epilogue parks each wave's up accumulators (8 x 2 tiles x 64
 // lanes x 16 B) in its share of the idle ring.
 static_assert(kStages * kStageBytes / kHeavyWaves >= 8 * 2 * 64 * 16, "stash does not fit the ring");
@@ -371,6 +377,20 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 
 __device__ __forceinline__ void lds_dma16(const uint16_t* src, char* dst) {
     __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, 0);
+}
+
+// Raw buffer resource over [base, base + bytes): loads past the end read 0
+// instead of touching memory.  Word 3 = 0x00020000: 32-bit data format, no
+// swizzle (the CDNA raw-buffer setting).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from rsrc + voff + soff into LDS at dst + 16*lane
+// (buffer_load_dwordx4 ... lds).
+__device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                              char* dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)dst, 16, (int)voff, (int)soff, 0, 0);
 }
 
 // Wait until at most n of this wave's vector-memory instructions are
@@ -406,7 +426,16 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: LDS offsets in SGPRs
     const int wm = wave >> 2, wn = wave & 3;
     const int l16 = lane & 15, g = lane >> 4;
-    const int nst = K / 32;  // K % 32 == 0
+    const int nh = K / 32;              // 32-wide MFMA K steps (K % 32 == 0)
+    const int nst = (nh + 1) / 2;       // 64-wide stages; the last one is half full if nh is odd
+    // DMA side: lane L fills slot L of a block: row L/8, chunk (L%8)^(L/8)^(b%2).
+    const int drow = lane >> 3;
+    const int dchunk = (lane & 7) ^ drow;  // for even blocks; odd blocks use dchunk ^ 1
+    // Fragment side: lane l reads row l%16 (block 2f + (l%16)/8), chunk g + 4*half.
+    const int fpar = (lane >> 3) & 1;
+    const int frow = lane & 7;
+    const int foff0 = fpar * kBlk + frow * 128 + ((g ^ frow ^ fpar) << 4);
+    const int foff1 = fpar * kBlk + frow * 128 + (((g + 4) ^ frow ^ fpar) << 4);
 
     // XCD-aware static schedule.  The work list is tile-major (tiles of one
     // expert are adjacent) with the N block fastest; it is cut into nslice
@@ -437,37 +466,64 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
             rows = min(kTM, a.dense_rows - m0);
         }
 
-        // This wave loads A row blocks 2*wave, 2*wave+1 and the same B blocks.
-        const uint16_t* asrc[2];
-        const uint16_t* bsrc[2];
+        // This wave fills A blocks and B blocks kBlkPerWave*wave .. +3.  Each
+        // source is a buffer resource (SGPRs) plus a 32-bit per-lane byte
+        // offset that holds the lane's row and K chunk; the stage's K offset
+        // is the scalar offset, so a steady-state load needs no VALU work.
+        __amdgpu_buffer_rsrc_t ar, br;
+        if (M == Mode::GateUp) {
+            ar = make_rsrc(a.x, (uint32_t)((size_t)a.T * a.H * 2));
+            br = make_rsrc(a.w_gu + (size_t)e * 2 * a.I * a.H, (uint32_t)((size_t)2 * a.I * a.H * 2));
+        } else {
+            ar = make_rsrc(a.h + (size_t)(r0 + m0) * hstride, (uint32_t)((size_t)kTM * hstride * 2));
+            br = make_rsrc(a.w_dn + (size_t)e * a.H * a.I, (uint32_t)((size_t)a.H * a.I * 2));
+        }
+        uint32_t aoff[kBlkPerWave], boff[kBlkPerWave];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = (2 * wave + i) * 16 + l16;  // row within the tile
-            const int rr = r < rows ? r : 0;          // rows past the count: any valid row
+        for (int i = 0; i < kBlkPerWave; ++i) {
+            const int r = (kBlkPerWave * wave + i) * 8 + drow;  // row within the tile
+            const int rr = r < rows ? r : 0;                   // rows past the count: any valid row
+            const uint32_t cb = (uint32_t)(dchunk ^ (i & 1)) * 16u;
             if (M == Mode::GateUp) {
                 const int tok = a.sorted_ids ? a.sorted_ids[r0 + m0 + rr] : r0 + m0 + rr;
-                asrc[i] = a.x + (size_t)tok * a.H + 8 * g;
+                aoff[i] = (uint32_t)tok * (uint32_t)a.H * 2u + cb;
                 // 16-row blocks alternate: block 2p = gate rows, 2p+1 = the
                 // matching up rows, so g and u of an element share a lane.
                 const int hc = nb * (kTN / 2) + (r >> 5) * 16 + (r & 15);
                 const int wr = (hc < a.I) ? (((r & 16) == 0) ? hc : a.I + hc) : 0;
-                bsrc[i] = a.w_gu + ((size_t)e * 2 * a.I + wr) * a.H + 8 * g;
+                boff[i] = (uint32_t)wr * (uint32_t)a.H * 2u + cb;
             } else {
-                asrc[i] = a.h + (size_t)(r0 + m0 + rr) * hstride + 8 * g;
+                aoff[i] = (uint32_t)rr * (uint32_t)hstride * 2u + cb;
                 const int c = nb * kTN + r;
-                bsrc[i] = a.w_dn + ((size_t)e * a.H + (c < a.H ? c : 0)) * a.I + 8 * g;
+                boff[i] = (uint32_t)(c < a.H ? c : 0) * (uint32_t)a.I * 2u + cb;
             }
         }
+        // Lanes whose chunk is in the upper half of the stage (K values
+        // 32..63): bit 2 of the chunk, which the odd-block swizzle keeps.
+        const bool upper = (dchunk & 4) != 0;
         auto issue = [&](int st) {
             char* buf = lds[st % kStages];
-            const int kk = st * 32;
+            const int kk = st * kKS;
             // down with split_h: K columns past I wrap back onto W_down
             const int kb = (M == Mode::Down && kk >= a.I) ? kk - a.I : kk;
+            // Upper-half lanes in two rare stages: in the half-full last
+            // stage they reload an in-row chunk that is never used; in the
+            // stage that straddles I (split_h with I % 64 == 32) their B
+            // columns wrap back onto W_down.  The adjustment is made opaque so
+            // that no adjusted copy of the offsets is hoisted out of the loop.
+            const bool tail = kk + kKS > K;
+            const bool straddle = M == Mode::Down && kk < a.I && kk + kKS > a.I && K > a.I;
+            uint32_t adj_a = (tail && upper) ? 64u : 0u;
+            uint32_t adj_b = (tail && upper) ? 64u : ((straddle && upper) ? (uint32_t)a.I * 2u : 0u);
+            asm volatile("" : "+v"(adj_a), "+v"(adj_b));
+            // The whole offset goes in the lane's VGPR; the 32-bit sum is
+            // exact because the true offset is never negative.
+            const uint32_t sa = (uint32_t)kk * 2u - adj_a, sb = (uint32_t)kb * 2u - adj_b;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) lds_dma16(asrc[i] + kk, buf + (2 * wave + i) * kFrag);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                lds_dma16(bsrc[i] + kb, buf + (kFragsA + 2 * wave + i) * kFrag);
+            for (int i = 0; i < kBlkPerWave; ++i) {
+                lds_dma16_buf(ar, aoff[i] + sa, 0u, buf + (kBlkPerWave * wave + i) * kBlk);
+                lds_dma16_buf(br, boff[i] + sb, 0u, buf + (kBlocksA + kBlkPerWave * wave + i) * kBlk);
+            }
         };
 
         floatx4_t acc[8][4];
@@ -476,75 +532,80 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-        // This wave's operand fragments of one K step.
-        auto read_frags = [&](int st, bf16x8_t (&af)[8], bf16x8_t (&bf)[4]) {
-            const char* buf = lds[st % kStages];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bf[j] = *reinterpret_cast<const bf16x8_t*>(buf + (kFragsA + wn * 4 + j) * kFrag +
-                                                           lane * 16);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                af[i] = *reinterpret_cast<const bf16x8_t*>(buf + (wm * 8 + i) * kFrag + lane * 16);
+        // Fragment reads of one 32-wide K half of a stage.  A fragment i of
+        // this wave is tile rows wm*128 + 16i.., B fragment j is B rows
+        // (wn*4 + j)*16..
+        auto rd = [&](int st, int half, int blk) -> bf16x8_t {
+            const char* p = lds[st % kStages] + blk * kBlk + (half ? foff1 : foff0);
+            return *reinterpret_cast<const bf16x8_t*>(p);
         };
-        // Wait for stage st (at most the stages after it still loading), then
-        // barrier: every wave's share of st is in, and every wave has
-        // finished reading the buffer that the next issue() refills.
-        auto stage_ready = [&](int st) {
-            const int later = min(kStages - 2, nst - 1 - st);
-            static_assert(kStages >= 2 && kStages <= 5, "ring depth");
-            if (later >= 3)
-                wait_vmcnt<3 * kDmaPerWave>();
-            else if (later == 2)
-                wait_vmcnt<2 * kDmaPerWave>();
-            else if (later == 1)
-                wait_vmcnt<kDmaPerWave>();
-            else
-                wait_vmcnt<0>();
-            ring_barrier();
+        auto read_b = [&](int st, int half, bf16x8_t (&bf)[4]) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bf[j] = rd(st, half, kBlocksA + (wn * 4 + j) * 2);
         };
-        // Every wave runs all its row sub-tiles: a block takes as long as its
-        // slowest wave, so skipping rows past the count in one wave would not
-        // shorten the tile.
+        auto read_a = [&](int st, int half, int i0, bf16x8_t (&af)[8]) {
+#pragma unroll
+            for (int i = i0; i < i0 + 4; ++i) af[i] = rd(st, half, (wm * 8 + i) * 2);
+        };
         auto mfma_rows = [&](int i0, const bf16x8_t (&af)[8], const bf16x8_t (&bf)[4]) {
 #pragma unroll
             for (int i = i0; i < i0 + 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(af[i], bf[j], acc[i][j]);
         };
-        // One K step: half of the MFMAs on (ca, cb); then, once this wave's
-        // reads of stage st are complete, the barrier that admits stage st+1
-        // (and lets stage st's buffer be refilled), the next issue and the
-        // reads of stage st+1 into (na, nb); then the other half, which hides
-        // those reads.  Unrolled by two so the fragment sets swap roles
-        // without copies.
-        auto kstep = [&](int st, const bf16x8_t (&ca)[8], const bf16x8_t (&cb)[4],
-                         bf16x8_t (&na)[8], bf16x8_t (&nb)[4]) {
-            mfma_rows(0, ca, cb);
-            if (st + 1 < nst) {
-                __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-                stage_ready(st + 1);
-                if (st + kStages < nst) issue(st + kStages);
-                read_frags(st + 1, na, nb);
-            }
-            mfma_rows(4, ca, cb);
-        };
 
-#pragma unroll
-        for (int s = 0; s < kStages - 1; ++s)
-            if (s < nst) issue(s);
-        stage_ready(0);
-        if (kStages - 1 < nst) issue(kStages - 1);
-        bf16x8_t fa0[8], fb0[4], fa1[8], fb1[4];
-        read_frags(0, fa0, fb0);
-        for (int st = 0; st < nst; st += 2) {
-            kstep(st, fa0, fb0, fa1, fb1);
-            if (st + 1 < nst) kstep(st + 1, fa1, fb1, fa0, fb0);
+        // Prologue: stages 0 and 1 loading; wait for stage 0.
+        issue(0);
+        if (nst > 1) {
+            issue(1);
+            wait_vmcnt<kDmaPerWave>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        ring_barrier();
+        bf16x8_t af[8], bf0[4], bf1[4];
+        read_b(0, 0, bf0);
+        read_a(0, 0, 0, af);
+        read_a(0, 0, 4, af);
+        // Each 32-wide half step runs its MFMAs in two halves of 16; the
+        // fragments of the next half step are read behind them: B and A rows
+        // 0..3 after the first 16 (rows 0..3 are done with), A rows 4..7 after
+        // the second.  At a stage boundary the first 16 MFMAs also cover the
+        // wait for the next stage and the barrier that frees this stage's
+        // buffer for the load two stages ahead.  One loop with uniform
+        // branches (no peeled copies): peeling made the register allocator
+        // stop keeping each accumulator in place and spill.
+        for (int st = 0; st < nst; ++st) {
+            const bool h1 = 2 * st + 1 < nh;  // false only in a half-full last stage
+            const bool more = st + 1 < nst;
+            mfma_rows(0, af, bf0);
+            if (h1) {
+                read_b(st, 1, bf1);
+                read_a(st, 1, 0, af);
+            }
+            mfma_rows(4, af, bf0);
+            if (h1) {
+                read_a(st, 1, 4, af);
+                mfma_rows(0, af, bf1);
+                if (more) {
+                    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of st done
+                    wait_vmcnt<0>();                     // stage st+1 in (st+2 not yet issued)
+                    ring_barrier();
+                    if (st + 2 < nst) issue(st + 2);
+                    read_b(st + 1, 0, bf0);
+                    read_a(st + 1, 0, 0, af);
+                }
+                mfma_rows(4, af, bf1);
+                if (more) read_a(st + 1, 0, 4, af);
+            }
         }
         wait_vmcnt<0>();
         ring_barrier();  // the ring is idle: the epilogue may use it
 
-        // epilogue
+        // Epilogue.  Lane (l16, g) of wave (wm, wn) holds rows
+        // wm*128 + 16i + 4g + r of its MFMA tiles; the row offsets 16i + r are
+        // compile-time constants times a uniform pitch.
+        const int row0 = wm * 128 + 4 * g;
         if (M == Mode::GateUp) {
             // Park the up accumulators in this wave's 16 KB of the idle ring
             // (lane-private slots), then read each back beside its gate value.
@@ -555,37 +616,44 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
                 for (int jp = 0; jp < 2; ++jp)
                     *reinterpret_cast<floatx4_t*>(stash + ((i * 2 + jp) * 64 + lane) * 16) =
                         acc[i][2 * jp + 1];
+            const int hc0 = nb * (kTN / 2) + wn * 32 + l16;
+            uint16_t* hp = a.h + (size_t)(r0 + m0 + row0) * hstride + hc0;
+            const bool full = rows == kTM && nb * (kTN / 2) + kTN / 2 <= a.I;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
 #pragma unroll
                 for (int jp = 0; jp < 2; ++jp) {
                     const floatx4_t up =
                         *reinterpret_cast<const floatx4_t*>(stash + ((i * 2 + jp) * 64 + lane) * 16);
-                    const int hc = nb * (kTN / 2) + (wn * 2 + jp) * 16 + l16;
+                    const bool col_ok = hc0 + jp * 16 < a.I;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int row = wm * 128 + i * 16 + 4 * g + r;
-                        if (row < rows && hc < a.I) {
+                        const int dr = i * 16 + r;
+                        if (full || (row0 + dr < rows && col_ok)) {
                             const float hv = swiglu(acc[i][2 * jp][r], up[r]);
                             const uint32_t hi = f32_to_bf16_bits(hv);
-                            uint16_t* hr = a.h + (size_t)(r0 + m0 + row) * hstride;
-                            hr[hc] = (uint16_t)hi;
+                            uint16_t* q = hp + (size_t)dr * hstride + jp * 16;
+                            q[0] = (uint16_t)hi;
                             if (a.split_h)
-                                hr[a.I + hc] = (uint16_t)f32_to_bf16_bits(hv - bf16_bits_to_f32(hi));
+                                q[a.I] = (uint16_t)f32_to_bf16_bits(hv - bf16_bits_to_f32(hi));
                         }
                     }
                 }
             }
         } else {
+            const int c0 = nb * kTN + wn * kWTN + l16;
+            float* yp = a.y + (size_t)(r0 + m0 + row0) * a.H + c0;
+            const bool full = rows == kTM && nb * kTN + kTN <= a.H;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int c = nb * kTN + wn * kWTN + j * 16 + l16;
+                    const bool col_ok = c0 + j * 16 < a.H;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int row = wm * 128 + i * 16 + 4 * g + r;
-                        if (row < rows && c < a.H) a.y[(size_t)(r0 + m0 + row) * a.H + c] = acc[i][j][r];
+                        const int dr = i * 16 + r;
+                        if (full || (row0 + dr < rows && col_ok))
+                            yp[(size_t)dr * a.H + j * 16] = acc[i][j][r];
                     }
                 }
             }

@@ -53,7 +53,9 @@ int check_shape(const moe_shape* s) {
         return fail(MOE_ERR_SHAPE, "sizes must be T >= 0 and H, E, k, I > 0, I_shared >= 0");
     if (s->k > s->E) return fail(MOE_ERR_SHAPE, "k > E");
     if ((long long)s->T * s->k >= (1LL << 31)) return fail(MOE_ERR_SHAPE, "T*k >= 2^31");
-    if ((long long)s->T * s->H >= (1LL << 40)) return fail(MOE_ERR_SHAPE, "T*H too large");
+    if ((long long)s->T * s->H >= (1LL << 31)) return fail(MOE_ERR_UNSUPPORTED, "T*H must be < 2^31");
+    if ((long long)s->I * s->H >= (1LL << 30) || (long long)s->I_shared * s->H >= (1LL << 30))
+        return fail(MOE_ERR_UNSUPPORTED, "I*H and I_shared*H must be < 2^30");
     if (s->H % 64) return fail(MOE_ERR_UNSUPPORTED, "H must be a multiple of 64");
     if (s->I % 32) return fail(MOE_ERR_UNSUPPORTED, "I must be a multiple of 32");
     if (s->I_shared % 32) return fail(MOE_ERR_UNSUPPORTED, "I_shared must be a multiple of 32");

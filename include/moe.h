@@ -43,7 +43,8 @@
  *    and build: no floating-point atomics are used anywhere.
  *  - Supported sizes: T >= 0 (T == 0 is a no-op), H % 64 == 0,
  *    I % 32 == 0, 1 <= k <= min(E, 32), E <= 1024, T*k < 2^31,
- *    I_shared % 32 == 0 (or 0).  With T == 0 the activation and output
+ *    T*H < 2^31, I*H < 2^30 and I_shared*H < 2^30 (byte offsets into x and
+ *    into one expert's weights fit 32 bits), I_shared % 32 == 0 (or 0).  With T == 0 the activation and output
  *    pointers may be NULL; only moe_permute (and moe_forward's counts_out)
  *    write anything: all-zero counts and offsets.
  */

@@ -66,6 +66,8 @@ def test_workspace_no_padding(L):
     (dict(E=2048, k=4), moe.MOE_ERR_UNSUPPORTED), (dict(k=33), moe.MOE_ERR_UNSUPPORTED),
     (dict(renorm=2), moe.MOE_ERR_UNSUPPORTED), (dict(light_max_rows=65), moe.MOE_ERR_UNSUPPORTED),
     (dict(I_shared=40), moe.MOE_ERR_UNSUPPORTED), (dict(T=300000000, k=10), moe.MOE_ERR_SHAPE),
+    (dict(T=1 << 19, k=1), moe.MOE_ERR_UNSUPPORTED), (dict(I=1 << 18), moe.MOE_ERR_UNSUPPORTED),
+    (dict(I_shared=1 << 18), moe.MOE_ERR_UNSUPPORTED),
 ])
 def test_bad_shapes(L, kw, code):
     s = shp(**kw)
