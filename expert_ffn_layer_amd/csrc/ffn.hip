@@ -367,10 +367,8 @@ constexpr int kStageBytes = (kBlocksA + kBlocksB) * kBlk;         // 64 KB
 constexpr int kDmaPerWave = (kBlocksA + kBlocksB) / kHeavyWaves;  // 8 loads per wave per stage
 constexpr int kBlkPerWave = kBlocksA / kHeavyWaves;               // 4 A (and 4 B) blocks per wave
 static_assert(kBlocksA % kHeavyWaves == 0 && kBlocksB == kBlocksA, "block split");
-// The gate|up epilogue parks each wave's up accumulators (8 x 2 tiles x 64
-// lanes x 16 B) in its share of the idle ring.
-static_assert(kStages * kStageBytes / kHeavyWaves >= 8 * 2 * 64 * 16, "stash does not fit the ring");
-constexpr int kXcds = MOE_HEAVY_XCD_SLICES;  // MI355X: 8 XCDs, workgroups dispatched round-robin
+constexpr int kXcds = MOE_HEAVY_XCD_SLICES;
+  // MI355X: 8 XCDs, workgroups dispatched round-robin
 
 typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
@@ -426,11 +424,14 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: LDS offsets in SGPRs
     const int wm = wave >> 2, wn = wave & 3;
     const int l16 = lane & 15, g = lane >> 4;
-    const int nh = K / 32;              // 32-wide MFMA K steps (K % 32 == 0)
-    const int nst = (nh + 1) / 2;       // 64-wide stages; the last one is half full if nh is odd
+    const int nh = K / 32;         // 32-wide MFMA K steps (K % 32 == 0)
+    const int nst = (nh + 1) / 2;  // 64-wide stages; the last one is half full if nh is odd
     // DMA side: lane L fills slot L of a block: row L/8, chunk (L%8)^(L/8)^(b%2).
     const int drow = lane >> 3;
     const int dchunk = (lane & 7) ^ drow;  // for even blocks; odd blocks use dchunk ^ 1
+    // Lanes whose chunk is in the upper half of the stage (K values 32..63):
+    // bit 2 of the chunk, which the odd-block swizzle keeps.
+    const bool upper = (dchunk & 4) != 0;
     // Fragment side: lane l reads row l%16 (block 2f + (l%16)/8), chunk g + 4*half.
     const int fpar = (lane >> 3) & 1;
     const int frow = lane & 7;
@@ -450,9 +451,14 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
     const long long wbeg = xs * per;
     const long long wend = min(nwork, wbeg + per);
 
-    for (long long wi = wbeg + jx; wi < wend; wi += nb_x) {
-        const int tile = (int)(wi / nblk), nb = (int)(wi % nblk);
-        int e, r0, m0, rows;
+    // Per-tile state: output block nb of row tile (e, m0); rows of the tile
+    // that exist; buffer resources and per-lane byte offsets of the loads.
+    int nb = 0, e = 0, r0 = 0, m0 = 0, rows = 0;
+    __amdgpu_buffer_rsrc_t ar, br;
+    uint32_t aoff[kBlkPerWave], boff[kBlkPerWave];
+    auto setup = [&](long long wi) {
+        const int tile = (int)(wi / nblk);
+        nb = (int)(wi % nblk);
         if (a.plan) {
             const int32_t* tl = a.plan + kPlanHeader + a.E;
             e = tl[2 * tile];
@@ -465,12 +471,10 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
             m0 = tile * kTM;
             rows = min(kTM, a.dense_rows - m0);
         }
-
         // This wave fills A blocks and B blocks kBlkPerWave*wave .. +3.  Each
         // source is a buffer resource (SGPRs) plus a 32-bit per-lane byte
         // offset that holds the lane's row and K chunk; the stage's K offset
-        // is the scalar offset, so a steady-state load needs no VALU work.
-        __amdgpu_buffer_rsrc_t ar, br;
+        // is added once per stage.
         if (M == Mode::GateUp) {
             ar = make_rsrc(a.x, (uint32_t)((size_t)a.T * a.H * 2));
             br = make_rsrc(a.w_gu + (size_t)e * 2 * a.I * a.H, (uint32_t)((size_t)2 * a.I * a.H * 2));
@@ -478,7 +482,6 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
             ar = make_rsrc(a.h + (size_t)(r0 + m0) * hstride, (uint32_t)((size_t)kTM * hstride * 2));
             br = make_rsrc(a.w_dn + (size_t)e * a.H * a.I, (uint32_t)((size_t)a.H * a.I * 2));
         }
-        uint32_t aoff[kBlkPerWave], boff[kBlkPerWave];
 #pragma unroll
         for (int i = 0; i < kBlkPerWave; ++i) {
             const int r = (kBlkPerWave * wave + i) * 8 + drow;  // row within the tile
@@ -498,55 +501,58 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
                 boff[i] = (uint32_t)(c < a.H ? c : 0) * (uint32_t)a.I * 2u + cb;
             }
         }
-        // Lanes whose chunk is in the upper half of the stage (K values
-        // 32..63): bit 2 of the chunk, which the odd-block swizzle keeps.
-        const bool upper = (dchunk & 4) != 0;
-        auto issue = [&](int st) {
-            char* buf = lds[st % kStages];
-            const int kk = st * kKS;
-            // down with split_h: K columns past I wrap back onto W_down
-            const int kb = (M == Mode::Down && kk >= a.I) ? kk - a.I : kk;
-            // Upper-half lanes in two rare stages: in the half-full last
-            // stage they reload an in-row chunk that is never used; in the
-            // stage that straddles I (split_h with I % 64 == 32) their B
-            // columns wrap back onto W_down.  The adjustment is made opaque so
-            // that no adjusted copy of the offsets is hoisted out of the loop.
-            const bool tail = kk + kKS > K;
-            const bool straddle = M == Mode::Down && kk < a.I && kk + kKS > a.I && K > a.I;
-            uint32_t adj_a = (tail && upper) ? 64u : 0u;
-            uint32_t adj_b = (tail && upper) ? 64u : ((straddle && upper) ? (uint32_t)a.I * 2u : 0u);
-            asm volatile("" : "+v"(adj_a), "+v"(adj_b));
-            // The whole offset goes in the lane's VGPR; the 32-bit sum is
-            // exact because the true offset is never negative.
-            const uint32_t sa = (uint32_t)kk * 2u - adj_a, sb = (uint32_t)kb * 2u - adj_b;
+    };
+    auto issue = [&](int st) {
+        char* buf = lds[st % kStages];
+        const int kk = st * kKS;
+        // down with split_h: K columns past I wrap back onto W_down
+        const int kb = (M == Mode::Down && kk >= a.I) ? kk - a.I : kk;
+        // Upper-half lanes in two rare stages: in the half-full last stage
+        // they reload an in-row chunk that is never used; in the stage that
+        // straddles I (split_h with I % 64 == 32) their B columns wrap back
+        // onto W_down.  The adjustment is made opaque so that no adjusted copy
+        // of the offsets is hoisted out of the loop.
+        const bool tail = kk + kKS > K;
+        const bool straddle = M == Mode::Down && kk < a.I && kk + kKS > a.I && K > a.I;
+        uint32_t adj_a = (tail && upper) ? 64u : 0u;
+        uint32_t adj_b = (tail && upper) ? 64u : ((straddle && upper) ? (uint32_t)a.I * 2u : 0u);
+        asm volatile("" : "+v"(adj_a), "+v"(adj_b));
+        // The whole offset goes in the lane's VGPR; the 32-bit sum is exact
+        // because the true offset is never negative.
+        const uint32_t sa = (uint32_t)kk * 2u - adj_a, sb = (uint32_t)kb * 2u - adj_b;
 #pragma unroll
-            for (int i = 0; i < kBlkPerWave; ++i) {
-                lds_dma16_buf(ar, aoff[i] + sa, 0u, buf + (kBlkPerWave * wave + i) * kBlk);
-                lds_dma16_buf(br, boff[i] + sb, 0u, buf + (kBlocksA + kBlkPerWave * wave + i) * kBlk);
-            }
-        };
+        for (int i = 0; i < kBlkPerWave; ++i) {
+            lds_dma16_buf(ar, aoff[i] + sa, 0u, buf + (kBlkPerWave * wave + i) * kBlk);
+            lds_dma16_buf(br, boff[i] + sb, 0u, buf + (kBlocksA + kBlkPerWave * wave + i) * kBlk);
+        }
+    };
+    // Fragment reads of one 32-wide K half of a stage.  A fragment i of this
+    // wave is tile rows wm*128 + 16i.., B fragment j is B rows (wn*4 + j)*16..
+    auto rd = [&](int st, int half, int blk) -> bf16x8_t {
+        const char* p = lds[st % kStages] + blk * kBlk + (half ? foff1 : foff0);
+        return *reinterpret_cast<const bf16x8_t*>(p);
+    };
+    auto read_b = [&](int st, int half, bf16x8_t (&bf)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bf[j] = rd(st, half, kBlocksA + (wn * 4 + j) * 2);
+    };
+    auto read_a = [&](int st, int half, int i0, bf16x8_t (&af)[8]) {
+#pragma unroll
+        for (int i = i0; i < i0 + 4; ++i) af[i] = rd(st, half, (wm * 8 + i) * 2);
+    };
 
+    long long wi = wbeg + jx;
+    if (wi < wend) {
+        setup(wi);
+        issue(0);
+        if (nst > 1) issue(1);
+    }
+    while (wi < wend) {
         floatx4_t acc[8][4];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-
-        // Fragment reads of one 32-wide K half of a stage.  A fragment i of
-        // this wave is tile rows wm*128 + 16i.., B fragment j is B rows
-        // (wn*4 + j)*16..
-        auto rd = [&](int st, int half, int blk) -> bf16x8_t {
-            const char* p = lds[st % kStages] + blk * kBlk + (half ? foff1 : foff0);
-            return *reinterpret_cast<const bf16x8_t*>(p);
-        };
-        auto read_b = [&](int st, int half, bf16x8_t (&bf)[4]) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) bf[j] = rd(st, half, kBlocksA + (wn * 4 + j) * 2);
-        };
-        auto read_a = [&](int st, int half, int i0, bf16x8_t (&af)[8]) {
-#pragma unroll
-            for (int i = i0; i < i0 + 4; ++i) af[i] = rd(st, half, (wm * 8 + i) * 2);
-        };
         auto mfma_rows = [&](int i0, const bf16x8_t (&af)[8], const bf16x8_t (&bf)[4]) {
 #pragma unroll
             for (int i = i0; i < i0 + 4; ++i)
@@ -554,14 +560,13 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
                 for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(af[i], bf[j], acc[i][j]);
         };
 
-        // Prologue: stages 0 and 1 loading; wait for stage 0.
-        issue(0);
-        if (nst > 1) {
-            issue(1);
+        // Stages 0 and 1 were requested after the previous tile's epilogue
+        // stores (or above, for the first tile); vector-memory operations
+        // retire in order, so at most stage 1's loads may still be pending.
+        if (nst > 1)
             wait_vmcnt<kDmaPerWave>();
-        } else {
+        else
             wait_vmcnt<0>();
-        }
         ring_barrier();
         bf16x8_t af[8], bf0[4], bf1[4];
         read_b(0, 0, bf0);
@@ -572,64 +577,63 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
         // 0..3 after the first 16 (rows 0..3 are done with), A rows 4..7 after
         // the second.  At a stage boundary the first 16 MFMAs also cover the
         // wait for the next stage and the barrier that frees this stage's
-        // buffer for the load two stages ahead.  One loop with uniform
-        // branches (no peeled copies): peeling made the register allocator
-        // stop keeping each accumulator in place and spill.
-        for (int st = 0; st < nst; ++st) {
-            const bool h1 = 2 * st + 1 < nh;  // false only in a half-full last stage
-            const bool more = st + 1 < nst;
+        // buffer for the load two stages ahead.  One loop with a branch-free
+        // body (no peeled copies): peeling made the register allocator stop
+        // keeping each accumulator in place and spill.
+        const int nfull = nh / 2;  // stages with both halves
+        for (int st = 0; st < nfull; ++st) {
             mfma_rows(0, af, bf0);
-            if (h1) {
-                read_b(st, 1, bf1);
-                read_a(st, 1, 0, af);
-            }
+            read_b(st, 1, bf1);
+            read_a(st, 1, 0, af);
             mfma_rows(4, af, bf0);
-            if (h1) {
-                read_a(st, 1, 4, af);
-                mfma_rows(0, af, bf1);
-                if (more) {
-                    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of st done
-                    wait_vmcnt<0>();                     // stage st+1 in (st+2 not yet issued)
-                    ring_barrier();
-                    if (st + 2 < nst) issue(st + 2);
-                    read_b(st + 1, 0, bf0);
-                    read_a(st + 1, 0, 0, af);
-                }
-                mfma_rows(4, af, bf1);
-                if (more) read_a(st + 1, 0, 4, af);
-            }
+            read_a(st, 1, 4, af);
+            mfma_rows(0, af, bf1);
+            // After the last stage this wait, barrier and the reads of the
+            // (absent) next stage are harmless: no load is outstanding and
+            // the ring addresses are valid.
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of st done
+            wait_vmcnt<0>();                     // stage st+1 in (st+2 not yet issued)
+            ring_barrier();
+            if (st + 2 < nst) issue(st + 2);
+            read_b(st + 1, 0, bf0);
+            read_a(st + 1, 0, 0, af);
+            mfma_rows(4, af, bf1);
+            read_a(st + 1, 0, 4, af);
         }
-        wait_vmcnt<0>();
-        ring_barrier();  // the ring is idle: the epilogue may use it
+        if (nh & 1) {  // half-full last stage (down with I % 64 == 32)
+            mfma_rows(0, af, bf0);
+            mfma_rows(4, af, bf0);
+        }
+        // Every wave's reads of the ring are complete before the next tile's
+        // loads are requested into it (after the epilogue below).
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        ring_barrier();
 
         // Epilogue.  Lane (l16, g) of wave (wm, wn) holds rows
         // wm*128 + 16i + 4g + r of its MFMA tiles; the row offsets 16i + r are
-        // compile-time constants times a uniform pitch.
+        // compile-time constants times a uniform pitch.  The next tile's setup
+        // (its row indices are loads) runs first, so that waiting for those
+        // loads does not also wait for this tile's stores to drain.
         const int row0 = wm * 128 + 4 * g;
+        const int t_nb = nb, t_base = r0 + m0, t_rows = rows;
+        const long long wnext = wi + nb_x;
+        if (wnext < wend) setup(wnext);
         if (M == Mode::GateUp) {
-            // Park the up accumulators in this wave's 16 KB of the idle ring
-            // (lane-private slots), then read each back beside its gate value.
-            char* stash = &lds[0][0] + wave * (kStages * kStageBytes / kHeavyWaves);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int jp = 0; jp < 2; ++jp)
-                    *reinterpret_cast<floatx4_t*>(stash + ((i * 2 + jp) * 64 + lane) * 16) =
-                        acc[i][2 * jp + 1];
-            const int hc0 = nb * (kTN / 2) + wn * 32 + l16;
-            uint16_t* hp = a.h + (size_t)(r0 + m0 + row0) * hstride + hc0;
-            const bool full = rows == kTM && nb * (kTN / 2) + kTN / 2 <= a.I;
+            const int hc0 = t_nb * (kTN / 2) + wn * 32 + l16;
+            uint16_t* hp = a.h + (size_t)(t_base + row0) * hstride + hc0;
+            const bool full = t_rows == kTM && t_nb * (kTN / 2) + kTN / 2 <= a.I;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
 #pragma unroll
                 for (int jp = 0; jp < 2; ++jp) {
-                    const floatx4_t up =
-                        *reinterpret_cast<const floatx4_t*>(stash + ((i * 2 + jp) * 64 + lane) * 16);
+                    // gate tile 2jp and up tile 2jp+1 hold the same (row, i)
+                    // in the same lane
+                    const floatx4_t up = acc[i][2 * jp + 1];
                     const bool col_ok = hc0 + jp * 16 < a.I;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int dr = i * 16 + r;
-                        if (full || (row0 + dr < rows && col_ok)) {
+                        if (full || (row0 + dr < t_rows && col_ok)) {
                             const float hv = swiglu(acc[i][2 * jp][r], up[r]);
                             const uint32_t hi = f32_to_bf16_bits(hv);
                             uint16_t* q = hp + (size_t)dr * hstride + jp * 16;
@@ -641,9 +645,9 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
                 }
             }
         } else {
-            const int c0 = nb * kTN + wn * kWTN + l16;
-            float* yp = a.y + (size_t)(r0 + m0 + row0) * a.H + c0;
-            const bool full = rows == kTM && nb * kTN + kTN <= a.H;
+            const int c0 = t_nb * kTN + wn * kWTN + l16;
+            float* yp = a.y + (size_t)(t_base + row0) * a.H + c0;
+            const bool full = t_rows == kTM && t_nb * kTN + kTN <= a.H;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
 #pragma unroll
@@ -652,16 +656,18 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int dr = i * 16 + r;
-                        if (full || (row0 + dr < rows && col_ok))
+                        if (full || (row0 + dr < t_rows && col_ok))
                             yp[(size_t)dr * a.H + j * 16] = acc[i][j][r];
                     }
                 }
             }
         }
-        // Drain this tile's stores too: the next tile's stage waits count
-        // outstanding vector-memory operations and must see only its loads.
-        wait_vmcnt<0>();
-        ring_barrier();  // epilogue reads of the stash done before the ring is refilled
+
+        wi = wnext;
+        if (wi < wend) {
+            issue(0);
+            if (nst > 1) issue(1);
+        }
     }
 }
 
