@@ -34,9 +34,16 @@
 namespace moe {
 
 int max_heavy_tiles(long long A, int E, int light_max) {
-    // sum over heavy experts of ceil(n_e / BM) <= A / BM + (#heavy experts)
+    // sum over heavy experts of ceil(n_e / BM) <= A / BM + (#heavy experts),
+    // at the smallest tile height
     const long long heavy = std::min<long long>(E, A / (light_max + 1));
-    return (int)std::min<long long>(A / kHeavyBM + heavy + 1, A + 1);
+    return (int)std::min<long long>(A / kHeavyBMMin + heavy + 1, A + 1);
+}
+
+int dense_tile_height(int rows) {
+    const long long t0 = (rows + kTileTM0 - 1) / kTileTM0, t1 = (rows + kTileTM1 - 1) / kTileTM1,
+                    t2 = (rows + kTileTM2 - 1) / kTileTM2;
+    return tile_height(pick_tile_height(t0, t1, t2));
 }
 
 namespace {
@@ -44,17 +51,36 @@ namespace {
 constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------- plan
-// One block, one thread per expert: compact the light experts (ascending id)
-// and the heavy experts' row tiles (ascending id, then first row).
+// One block, one thread per expert: pick the heavy tile height from the
+// experts' row counts, then compact the light experts (ascending id) and the
+// heavy experts' row tiles (ascending id, then first row).
 __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restrict__ offsets,
-                                                        int E, int light_max,
+                                                        int E, int light_max, int force_tm,
                                                         int32_t* __restrict__ plan) {
-    __shared__ int wl[16], wt[16];
+    __shared__ int wl[16], wt[16], wc[3][16];
     const int e = threadIdx.x;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
     const int n = (e < E) ? offsets[e + 1] - offsets[e] : 0;
+    const bool heavy = n > light_max;
+    int c[3] = {heavy ? (n + kTileTM0 - 1) / kTileTM0 : 0, heavy ? (n + kTileTM1 - 1) / kTileTM1 : 0,
+                heavy ? (n + kTileTM2 - 1) / kTileTM2 : 0};
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) c[q] += __shfl_xor(c[q], o, 64);
+        if (lane == 0) wc[q][wave] = c[q];
+    }
+    __syncthreads();
+    long long tot[3] = {0, 0, 0};
+    for (int w = 0; w < nwave; ++w) {
+        tot[0] += wc[0][w];
+        tot[1] += wc[1][w];
+        tot[2] += wc[2][w];
+    }
+    const int tm = force_tm ? force_tm : tile_height(pick_tile_height(tot[0], tot[1], tot[2]));
+
     const int is_light = (n >= 1 && n <= light_max) ? 1 : 0;
-    const int nt = (n > light_max) ? (n + kHeavyBM - 1) / kHeavyBM : 0;
+    const int nt = heavy ? (n + tm - 1) / tm : 0;
     int il = is_light, it = nt;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -80,11 +106,12 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restric
     int32_t* tiles = plan + kPlanHeader + E;
     for (int i = 0; i < nt; ++i) {
         tiles[2 * (et + i)] = e;
-        tiles[2 * (et + i) + 1] = i * kHeavyBM;
+        tiles[2 * (et + i) + 1] = i * tm;
     }
     if (threadIdx.x == blockDim.x - 1) {
         plan[0] = el + is_light;
         plan[1] = et + nt;
+        plan[2] = tm;
     }
 }
 
@@ -353,20 +380,34 @@ enum class Mode { GateUp, Down };
 
 constexpr int kHeavyThreads = 512;
 constexpr int kHeavyWaves = kHeavyThreads / 64;
-constexpr int kTM = kHeavyBM;  // 256 rows per tile
 constexpr int kTN = 256;       // B rows per tile (output columns, or 128 gate + 128 up rows)
 constexpr int kWTN = kTN / 4;  // 64 columns per wave
 #ifndef MOE_HEAVY_XCD_SLICES
 #define MOE_HEAVY_XCD_SLICES 8
 #endif
-constexpr int kStages = 2;         // LDS ring depth: one K step computing, one loading
+// LDS rings: A (rows of x or h) two stages deep; B (expert weights) two
+// deep with 256-row tiles and three deep with 192- and 128-row tiles.  The
+// smaller heights are chosen when experts have few rows, so each expert's
+// weights feed few row tiles and stream from HBM with a longer latency to
+// cover; 256-row tiles are chosen for large experts whose weights the row
+// tiles share through L2 (measured: the third buffer costs 3% there and gains
+// 7% on streamed weights).
+constexpr int kAStages = 2;
 constexpr int kKS = 64;            // K values per stage
 constexpr int kBlk = 1024;         // bytes of one 8-row x 64-K block
-constexpr int kBlocksA = kTM / 8, kBlocksB = kTN / 8;
-constexpr int kStageBytes = (kBlocksA + kBlocksB) * kBlk;         // 64 KB
-constexpr int kDmaPerWave = (kBlocksA + kBlocksB) / kHeavyWaves;  // 8 loads per wave per stage
-constexpr int kBlkPerWave = kBlocksA / kHeavyWaves;               // 4 A (and 4 B) blocks per wave
-static_assert(kBlocksA % kHeavyWaves == 0 && kBlocksB == kBlocksA, "block split");
+constexpr int kBlocksB = kTN / 8;  // 32
+constexpr int kBBlkPerWave = kBlocksB / kHeavyWaves;  // 4
+// Per tile height TM (256, 192, 128): each wave row group holds TM/2 rows
+// = TM/32 MFMA row tiles; a stage holds TM/8 A blocks and 32 B blocks.
+template <int TM>
+struct HeavyGeom {
+    static_assert(TM % 64 == 0 && TM >= 128 && TM <= 256, "tile height");
+    static constexpr int kRF = TM / 32;                   // row tiles per wave (8, 6, 4)
+    static constexpr int kBlocksA = TM / 8;               // 32, 24, 16
+    static constexpr int kABlkPerWave = kBlocksA / kHeavyWaves;  // 4, 3, 2
+    static constexpr int kABytes = kBlocksA * kBlk;       // 32, 24, 16 KB per stage
+    static constexpr int kBStages = TM == 256 ? 2 : 3;    // LDS 128, 144, 128 KB
+};
 constexpr int kXcds = MOE_HEAVY_XCD_SLICES;
   // MI355X: 8 XCDs, workgroups dispatched round-robin
 
@@ -409,16 +450,29 @@ __device__ __forceinline__ void ring_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <Mode M>
+template <Mode M, int TM>
 __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
-    __shared__ __attribute__((aligned(1024))) char lds[kStages][kStageBytes];
+    using G = HeavyGeom<TM>;
+    constexpr int kRF = G::kRF, kBlocksA = G::kBlocksA, kABlk = G::kABlkPerWave;
+    constexpr int kABytes = G::kABytes;
+    // One height per launch: the plan (or the host, for a dense group) names it.
+    if ((a.plan ? a.plan[2] : a.dense_tm) != TM) return;
+    // One LDS object for both rings (A stages, then B stages): with two
+    // objects the compiler waits for every LDS DMA before any LDS read.
+    constexpr int kBBytes = kBlocksB * kBlk;
+    constexpr int bst = G::kBStages;
+    __shared__ __attribute__((aligned(1024))) char lds[kAStages * kABytes + bst * kBBytes];
+    // Stage st's A lives in slot st % 2, its B in slot st % bst; the B slot
+    // index is carried along.
+    auto a_slot = [&](int st) -> char* { return lds + (st & 1) * kABytes; };
+    auto b_slot = [&](int slot) -> char* { return lds + kAStages * kABytes + slot * kBBytes; };
 
     const int N = (M == Mode::GateUp) ? 2 * a.I : a.H;
     // split_h: the down GEMM's K runs over [hi | lo] (2I) against W_down twice.
     const int K = (M == Mode::GateUp) ? a.H : (a.split_h ? 2 * a.I : a.I);
     const int hstride = a.split_h ? 2 * a.I : a.I;  // row pitch of h
     const int nblk = (N + kTN - 1) / kTN;
-    const int ntiles = a.plan ? a.plan[1] : (a.dense_rows + kTM - 1) / kTM;
+    const int ntiles = a.plan ? a.plan[1] : (a.dense_rows + TM - 1) / TM;
     const long long nwork = (long long)ntiles * nblk;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: LDS offsets in SGPRs
@@ -455,7 +509,7 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
     // that exist; buffer resources and per-lane byte offsets of the loads.
     int nb = 0, e = 0, r0 = 0, m0 = 0, rows = 0;
     __amdgpu_buffer_rsrc_t ar, br;
-    uint32_t aoff[kBlkPerWave], boff[kBlkPerWave];
+    uint32_t aoff[kABlk], boff[kBBlkPerWave];
     auto setup = [&](long long wi) {
         const int tile = (int)(wi / nblk);
         nb = (int)(wi % nblk);
@@ -464,14 +518,14 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
             e = tl[2 * tile];
             m0 = tl[2 * tile + 1];
             r0 = a.offsets[e];
-            rows = min(kTM, a.offsets[e + 1] - r0 - m0);
+            rows = min(TM, a.offsets[e + 1] - r0 - m0);
         } else {
             e = 0;
             r0 = 0;
-            m0 = tile * kTM;
-            rows = min(kTM, a.dense_rows - m0);
+            m0 = tile * TM;
+            rows = min(TM, a.dense_rows - m0);
         }
-        // This wave fills A blocks and B blocks kBlkPerWave*wave .. +3.  Each
+        // This wave fills A blocks kABlk*wave.. and B blocks 4*wave..+3.  Each
         // source is a buffer resource (SGPRs) plus a 32-bit per-lane byte
         // offset that holds the lane's row and K chunk; the stage's K offset
         // is added once per stage.
@@ -479,34 +533,42 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
             ar = make_rsrc(a.x, (uint32_t)((size_t)a.T * a.H * 2));
             br = make_rsrc(a.w_gu + (size_t)e * 2 * a.I * a.H, (uint32_t)((size_t)2 * a.I * a.H * 2));
         } else {
-            ar = make_rsrc(a.h + (size_t)(r0 + m0) * hstride, (uint32_t)((size_t)kTM * hstride * 2));
+            ar = make_rsrc(a.h + (size_t)(r0 + m0) * hstride, (uint32_t)((size_t)TM * hstride * 2));
             br = make_rsrc(a.w_dn + (size_t)e * a.H * a.I, (uint32_t)((size_t)a.H * a.I * 2));
         }
 #pragma unroll
-        for (int i = 0; i < kBlkPerWave; ++i) {
-            const int r = (kBlkPerWave * wave + i) * 8 + drow;  // row within the tile
-            const int rr = r < rows ? r : 0;                   // rows past the count: any valid row
-            const uint32_t cb = (uint32_t)(dchunk ^ (i & 1)) * 16u;
+        for (int i = 0; i < kABlk; ++i) {
+            const int b = kABlk * wave + i;
+            const int r = b * 8 + drow;         // row within the tile
+            const int rr = r < rows ? r : 0;    // rows past the count: any valid row
+            const uint32_t cb = (uint32_t)(dchunk ^ (b & 1)) * 16u;
             if (M == Mode::GateUp) {
                 const int tok = a.sorted_ids ? a.sorted_ids[r0 + m0 + rr] : r0 + m0 + rr;
                 aoff[i] = (uint32_t)tok * (uint32_t)a.H * 2u + cb;
+            } else {
+                aoff[i] = (uint32_t)rr * (uint32_t)hstride * 2u + cb;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kBBlkPerWave; ++i) {
+            const int b = kBBlkPerWave * wave + i;
+            const int r = b * 8 + drow;  // B row within the tile
+            const uint32_t cb = (uint32_t)(dchunk ^ (b & 1)) * 16u;
+            if (M == Mode::GateUp) {
                 // 16-row blocks alternate: block 2p = gate rows, 2p+1 = the
                 // matching up rows, so g and u of an element share a lane.
                 const int hc = nb * (kTN / 2) + (r >> 5) * 16 + (r & 15);
                 const int wr = (hc < a.I) ? (((r & 16) == 0) ? hc : a.I + hc) : 0;
                 boff[i] = (uint32_t)wr * (uint32_t)a.H * 2u + cb;
             } else {
-                aoff[i] = (uint32_t)rr * (uint32_t)hstride * 2u + cb;
                 const int c = nb * kTN + r;
                 boff[i] = (uint32_t)(c < a.H ? c : 0) * (uint32_t)a.I * 2u + cb;
             }
         }
     };
-    auto issue = [&](int st) {
-        char* buf = lds[st % kStages];
-        const int kk = st * kKS;
-        // down with split_h: K columns past I wrap back onto W_down
-        const int kb = (M == Mode::Down && kk >= a.I) ? kk - a.I : kk;
+    // Stage st's loads of this wave: A blocks into A slot st % 2, B blocks
+    // into B slot st % bst.
+    auto adjust = [&](int kk, uint32_t& adj_a, uint32_t& adj_b) {
         // Upper-half lanes in two rare stages: in the half-full last stage
         // they reload an in-row chunk that is never used; in the stage that
         // straddles I (split_h with I % 64 == 32) their B columns wrap back
@@ -514,95 +576,141 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
         // of the offsets is hoisted out of the loop.
         const bool tail = kk + kKS > K;
         const bool straddle = M == Mode::Down && kk < a.I && kk + kKS > a.I && K > a.I;
-        uint32_t adj_a = (tail && upper) ? 64u : 0u;
-        uint32_t adj_b = (tail && upper) ? 64u : ((straddle && upper) ? (uint32_t)a.I * 2u : 0u);
+        adj_a = (tail && upper) ? 64u : 0u;
+        adj_b = (tail && upper) ? 64u : ((straddle && upper) ? (uint32_t)a.I * 2u : 0u);
         asm volatile("" : "+v"(adj_a), "+v"(adj_b));
-        // The whole offset goes in the lane's VGPR; the 32-bit sum is exact
-        // because the true offset is never negative.
-        const uint32_t sa = (uint32_t)kk * 2u - adj_a, sb = (uint32_t)kb * 2u - adj_b;
+    };
+    // The whole offset goes in the lane's VGPR; the 32-bit sum is exact
+    // because the true offset is never negative.
+    auto issue_a = [&](int st) {
+        char* buf = a_slot(st);
+        const int kk = st * kKS;
+        uint32_t adj_a, adj_b;
+        adjust(kk, adj_a, adj_b);
+        const uint32_t sa = (uint32_t)kk * 2u - adj_a;
 #pragma unroll
-        for (int i = 0; i < kBlkPerWave; ++i) {
-            lds_dma16_buf(ar, aoff[i] + sa, 0u, buf + (kBlkPerWave * wave + i) * kBlk);
-            lds_dma16_buf(br, boff[i] + sb, 0u, buf + (kBlocksA + kBlkPerWave * wave + i) * kBlk);
+        for (int i = 0; i < kABlk; ++i)
+            lds_dma16_buf(ar, aoff[i] + sa, 0u, buf + (kABlk * wave + i) * kBlk);
+    };
+    auto issue_b = [&](int st, int slot) {
+        char* buf = b_slot(slot);
+        const int kk = st * kKS;
+        // down with split_h: K columns past I wrap back onto W_down
+        const int kb = (M == Mode::Down && kk >= a.I) ? kk - a.I : kk;
+        uint32_t adj_a, adj_b;
+        adjust(kk, adj_a, adj_b);
+        const uint32_t sb = (uint32_t)kb * 2u - adj_b;
+#pragma unroll
+        for (int i = 0; i < kBBlkPerWave; ++i)
+            lds_dma16_buf(br, boff[i] + sb, 0u, buf + (kBBlkPerWave * wave + i) * kBlk);
+    };
+    // A tile's first loads, in the order the waits below count on: A0 B0
+    // [A1 B1] [B2].
+    auto issue_first = [&]() {
+        issue_a(0);
+        issue_b(0, 0);
+        if (nst > 1) {
+            issue_a(1);
+            issue_b(1, 1);
         }
+        if (bst == 3 && nst > 2) issue_b(2, 2);
     };
     // Fragment reads of one 32-wide K half of a stage.  A fragment i of this
-    // wave is tile rows wm*128 + 16i.., B fragment j is B rows (wn*4 + j)*16..
-    auto rd = [&](int st, int half, int blk) -> bf16x8_t {
-        const char* p = lds[st % kStages] + blk * kBlk + (half ? foff1 : foff0);
+    // wave is tile rows wm*TM/2 + 16i.., B fragment j is B rows (wn*4 + j)*16..
+    auto rd_a = [&](int st, int half, int blk) -> bf16x8_t {
+        const char* p = a_slot(st) + blk * kBlk + (half ? foff1 : foff0);
         return *reinterpret_cast<const bf16x8_t*>(p);
     };
-    auto read_b = [&](int st, int half, bf16x8_t (&bf)[4]) {
+    auto read_b = [&](int slot, int half, bf16x8_t (&bf)[4]) {
+        const char* base = b_slot(slot) + (half ? foff1 : foff0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bf[j] = rd(st, half, kBlocksA + (wn * 4 + j) * 2);
+        for (int j = 0; j < 4; ++j)
+            bf[j] = *reinterpret_cast<const bf16x8_t*>(base + (wn * 4 + j) * 2 * kBlk);
     };
-    auto read_a = [&](int st, int half, int i0, bf16x8_t (&af)[8]) {
+    // A fragments in two groups: rows [0, kRF/2) and [kRF/2, kRF).
+    constexpr int kG0 = kRF / 2;
+    auto read_a = [&](int st, int half, int grp, bf16x8_t (&af)[kRF]) {
+        const int i0 = grp ? kG0 : 0, i1 = grp ? kRF : kG0;
 #pragma unroll
-        for (int i = i0; i < i0 + 4; ++i) af[i] = rd(st, half, (wm * 8 + i) * 2);
+        for (int i = i0; i < i1; ++i) af[i] = rd_a(st, half, (wm * kRF + i) * 2);
     };
 
     long long wi = wbeg + jx;
     if (wi < wend) {
         setup(wi);
-        issue(0);
-        if (nst > 1) issue(1);
+        issue_first();
     }
     while (wi < wend) {
-        floatx4_t acc[8][4];
+        floatx4_t acc[kRF][4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < kRF; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-        auto mfma_rows = [&](int i0, const bf16x8_t (&af)[8], const bf16x8_t (&bf)[4]) {
+        auto mfma_rows = [&](int grp, const bf16x8_t (&af)[kRF], const bf16x8_t (&bf)[4]) {
+            const int i0 = grp ? kG0 : 0, i1 = grp ? kRF : kG0;
 #pragma unroll
-            for (int i = i0; i < i0 + 4; ++i)
+            for (int i = i0; i < i1; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(af[i], bf[j], acc[i][j]);
         };
 
-        // Stages 0 and 1 were requested after the previous tile's epilogue
+        // The first loads were requested after the previous tile's epilogue
         // stores (or above, for the first tile); vector-memory operations
-        // retire in order, so at most stage 1's loads may still be pending.
-        if (nst > 1)
-            wait_vmcnt<kDmaPerWave>();
+        // retire in order, so stage 0 is in once at most the loads after it
+        // (A1 B1, and B2 with a three-deep B ring) are pending.
+        if (nst > 2 && bst == 3)
+            wait_vmcnt<kABlk + 2 * kBBlkPerWave>();
+        else if (nst > 1)
+            wait_vmcnt<kABlk + kBBlkPerWave>();
         else
             wait_vmcnt<0>();
         ring_barrier();
-        bf16x8_t af[8], bf0[4], bf1[4];
+        bf16x8_t af[kRF], bf0[4], bf1[4];
         read_b(0, 0, bf0);
         read_a(0, 0, 0, af);
-        read_a(0, 0, 4, af);
-        // Each 32-wide half step runs its MFMAs in two halves of 16; the
-        // fragments of the next half step are read behind them: B and A rows
-        // 0..3 after the first 16 (rows 0..3 are done with), A rows 4..7 after
-        // the second.  At a stage boundary the first 16 MFMAs also cover the
-        // wait for the next stage and the barrier that frees this stage's
-        // buffer for the load two stages ahead.  One loop with a branch-free
-        // body (no peeled copies): peeling made the register allocator stop
-        // keeping each accumulator in place and spill.
+        read_a(0, 0, 1, af);
+        // Each 32-wide half step runs its MFMAs in two groups of rows; the
+        // fragments of the next half step are read behind them: B and the
+        // first half of the A rows after the first group (those rows are done
+        // with), the second half of the A rows after the second group.  At a
+        // stage boundary the first group also covers the wait for the next
+        // stage and the barrier that frees this stage's buffer for the load
+        // two stages ahead.  One loop with a branch-free body (no peeled
+        // copies): peeling made the register allocator stop keeping each
+        // accumulator in place and spill.
         const int nfull = nh / 2;  // stages with both halves
+        int bs = 0;                // B slot of stage st
         for (int st = 0; st < nfull; ++st) {
+            const int bn = (bs + 1 == bst) ? 0 : bs + 1;  // B slot of stage st+1
             mfma_rows(0, af, bf0);
-            read_b(st, 1, bf1);
+            read_b(bs, 1, bf1);
             read_a(st, 1, 0, af);
-            mfma_rows(4, af, bf0);
-            read_a(st, 1, 4, af);
+            mfma_rows(1, af, bf0);
+            read_a(st, 1, 1, af);
             mfma_rows(0, af, bf1);
             // After the last stage this wait, barrier and the reads of the
             // (absent) next stage are harmless: no load is outstanding and
             // the ring addresses are valid.
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of st done
-            wait_vmcnt<0>();                     // stage st+1 in (st+2 not yet issued)
+            // Stage st+1 in: only B(st+2) (three-deep B ring) may be pending.
+            if (bst == 3 && st + 2 < nst)
+                wait_vmcnt<kBBlkPerWave>();
+            else
+                wait_vmcnt<0>();
             ring_barrier();
-            if (st + 2 < nst) issue(st + 2);
-            read_b(st + 1, 0, bf0);
+            // Refill the buffers stage st used: A two stages ahead, then B
+            // bst ahead (this order is what the wait above counts on).
+            if (st + 2 < nst) issue_a(st + 2);
+            if (st + bst < nst) issue_b(st + bst, bs);  // (st + bst) % bst == bs
+            read_b(bn, 0, bf0);
             read_a(st + 1, 0, 0, af);
-            mfma_rows(4, af, bf1);
-            read_a(st + 1, 0, 4, af);
+            mfma_rows(1, af, bf1);
+            read_a(st + 1, 0, 1, af);
+            bs = bn;
         }
         if (nh & 1) {  // half-full last stage (down with I % 64 == 32)
             mfma_rows(0, af, bf0);
-            mfma_rows(4, af, bf0);
+            mfma_rows(1, af, bf0);
         }
         // Every wave's reads of the ring are complete before the next tile's
         // loads are requested into it (after the epilogue below).
@@ -610,20 +718,20 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
         ring_barrier();
 
         // Epilogue.  Lane (l16, g) of wave (wm, wn) holds rows
-        // wm*128 + 16i + 4g + r of its MFMA tiles; the row offsets 16i + r are
+        // wm*TM/2 + 16i + 4g + r of its MFMA tiles; the row offsets 16i + r are
         // compile-time constants times a uniform pitch.  The next tile's setup
         // (its row indices are loads) runs first, so that waiting for those
         // loads does not also wait for this tile's stores to drain.
-        const int row0 = wm * 128 + 4 * g;
+        const int row0 = wm * (TM / 2) + 4 * g;
         const int t_nb = nb, t_base = r0 + m0, t_rows = rows;
         const long long wnext = wi + nb_x;
         if (wnext < wend) setup(wnext);
         if (M == Mode::GateUp) {
             const int hc0 = t_nb * (kTN / 2) + wn * 32 + l16;
             uint16_t* hp = a.h + (size_t)(t_base + row0) * hstride + hc0;
-            const bool full = t_rows == kTM && t_nb * (kTN / 2) + kTN / 2 <= a.I;
+            const bool full = t_rows == TM && t_nb * (kTN / 2) + kTN / 2 <= a.I;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < kRF; ++i) {
 #pragma unroll
                 for (int jp = 0; jp < 2; ++jp) {
                     // gate tile 2jp and up tile 2jp+1 hold the same (row, i)
@@ -647,9 +755,9 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
         } else {
             const int c0 = t_nb * kTN + wn * kWTN + l16;
             float* yp = a.y + (size_t)(t_base + row0) * a.H + c0;
-            const bool full = t_rows == kTM && t_nb * kTN + kTN <= a.H;
+            const bool full = t_rows == TM && t_nb * kTN + kTN <= a.H;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < kRF; ++i) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const bool col_ok = c0 + j * 16 < a.H;
@@ -664,10 +772,7 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
         }
 
         wi = wnext;
-        if (wi < wend) {
-            issue(0);
-            if (nst > 1) issue(1);
-        }
+        if (wi < wend) issue_first();
     }
 }
 
@@ -675,12 +780,38 @@ int grid_for(long long work, int per_cu, int num_cu) {
     return (int)std::max<long long>(1, std::min<long long>(work, (long long)per_cu * num_cu));
 }
 
+// Heavy tiles of one GEMM.  With a plan the tile height is decided on the
+// device, so every height's kernel is launched and all but one return at
+// once; a dense group's height is known here.
+template <Mode M>
+hipError_t launch_heavy(const FfnArgs& a, int ncols, hipStream_t st) {
+    const long long nblk = (ncols + kTN - 1) / kTN;
+    if (a.plan) {
+        if (a.max_tiles <= 0) return hipSuccess;
+        const int grid = grid_for((long long)a.max_tiles * nblk, 1, a.num_cu);
+        ffn_heavy_kernel<M, kTileTM0><<<grid, kHeavyThreads, 0, st>>>(a);
+        ffn_heavy_kernel<M, kTileTM1><<<grid, kHeavyThreads, 0, st>>>(a);
+        ffn_heavy_kernel<M, kTileTM2><<<grid, kHeavyThreads, 0, st>>>(a);
+        return hipGetLastError();
+    }
+    if (a.dense_rows <= 0) return hipSuccess;
+    const long long tiles = (a.dense_rows + a.dense_tm - 1) / a.dense_tm;
+    const int grid = grid_for(tiles * nblk, 1, a.num_cu);
+    switch (a.dense_tm) {
+        case kTileTM0: ffn_heavy_kernel<M, kTileTM0><<<grid, kHeavyThreads, 0, st>>>(a); break;
+        case kTileTM1: ffn_heavy_kernel<M, kTileTM1><<<grid, kHeavyThreads, 0, st>>>(a); break;
+        case kTileTM2: ffn_heavy_kernel<M, kTileTM2><<<grid, kHeavyThreads, 0, st>>>(a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_ffn_plan(const int32_t* offsets, int E, int light_max, int32_t* plan,
-                           hipStream_t st) {
+hipError_t launch_ffn_plan(const int32_t* offsets, int E, int light_max, int force_tm,
+                           int32_t* plan, hipStream_t st) {
     prof_begin(K_FFN_PLAN, st);
-    ffn_plan_kernel<<<1, 1024, 0, st>>>(offsets, E, light_max, plan);
+    ffn_plan_kernel<<<1, 1024, 0, st>>>(offsets, E, light_max, force_tm, plan);
     prof_end(K_FFN_PLAN, st);
     return hipGetLastError();
 }
@@ -696,13 +827,11 @@ hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t st) {
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    const long long tiles = a.plan ? a.max_tiles : (a.dense_rows + kTM - 1) / kTM;
-    const long long work = tiles * ((2 * a.I + kTN - 1) / kTN);
-    if (work > 0) {
+    if ((a.plan && a.max_tiles > 0) || (!a.plan && a.dense_rows > 0)) {
         prof_begin(K_GATEUP_HEAVY, st);
-        ffn_heavy_kernel<Mode::GateUp><<<grid_for(work, 1, a.num_cu), kHeavyThreads, 0, st>>>(a);
+        hipError_t err = launch_heavy<Mode::GateUp>(a, 2 * a.I, st);
         prof_end(K_GATEUP_HEAVY, st);
-        return hipGetLastError();
+        return err;
     }
     return hipSuccess;
 }
@@ -718,13 +847,11 @@ hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st) {
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    const long long tiles = a.plan ? a.max_tiles : (a.dense_rows + kTM - 1) / kTM;
-    const long long work = tiles * ((a.H + kTN - 1) / kTN);
-    if (work > 0) {
+    if ((a.plan && a.max_tiles > 0) || (!a.plan && a.dense_rows > 0)) {
         prof_begin(K_DOWN_HEAVY, st);
-        ffn_heavy_kernel<Mode::Down><<<grid_for(work, 1, a.num_cu), kHeavyThreads, 0, st>>>(a);
+        hipError_t err = launch_heavy<Mode::Down>(a, a.H, st);
         prof_end(K_DOWN_HEAVY, st);
-        return hipGetLastError();
+        return err;
     }
     return hipSuccess;
 }

@@ -50,19 +50,43 @@ constexpr int kPermChunk = 4096;  // assignments per permute block
 // also receives the grouped-FFN plan for `light_max`.
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* chunk_counts,
                           int nchunks, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
-                          int32_t* inv_pos, int32_t* plan, int light_max, hipStream_t st);
+                          int32_t* inv_pos, int32_t* plan, int light_max, int force_tm,
+                          hipStream_t st);
 
 // ---- grouped FFN --------------------------------------------------------
 constexpr int kLightRowsMax = 64;  // up to four 16-row MFMA sub-tiles
-constexpr int kHeavyBM = 256;      // rows per heavy tile
-// Plan layout (int32): [0] n_light, [1] n_tiles, [16 ..16+E) light expert
-// ids, [16+E ..) heavy tiles as (expert, first row) pairs.
+// Heavy tiles are 256 columns wide and 256, 192 or 128 rows high; one height
+// per launch, the one with the least estimated time for the actual expert
+// row counts: sum_e ceil(n_e / tm) * tm * cost(tm), cost = relative time per
+// tile row (x1000, measured: smaller tiles re-read more weights per row).
+#ifndef MOE_TILE_COST_192
+#define MOE_TILE_COST_192 1060
+#endif
+#ifndef MOE_TILE_COST_128
+#define MOE_TILE_COST_128 1250
+#endif
+constexpr int kTileTM0 = 256, kTileTM1 = 192, kTileTM2 = 128;
+constexpr int kTileCost0 = 1000, kTileCost1 = MOE_TILE_COST_192, kTileCost2 = MOE_TILE_COST_128;
+constexpr int kHeavyBMMin = kTileTM2;  // sizes the plan's tile list
+// Index (0, 1, 2) of the cheapest height given the tile counts at each.
+inline __host__ __device__ int pick_tile_height(long long t0, long long t1, long long t2) {
+    const long long c0 = t0 * kTileTM0 * kTileCost0, c1 = t1 * kTileTM1 * kTileCost1,
+                    c2 = t2 * kTileTM2 * kTileCost2;
+    return (c0 <= c1 && c0 <= c2) ? 0 : (c1 <= c2 ? 1 : 2);
+}
+inline __host__ __device__ int tile_height(int idx) {
+    return idx == 0 ? kTileTM0 : (idx == 1 ? kTileTM1 : kTileTM2);
+}
+// Plan layout (int32): [0] n_light, [1] n_tiles, [2] tile height, [16 ..16+E)
+// light expert ids, [16+E ..) heavy tiles as (expert, first row) pairs.
 constexpr int kPlanHeader = 16;
 
 int max_heavy_tiles(long long A, int E, int light_max);
+int dense_tile_height(int rows);  // tile height for a dense group of `rows` rows
 
-hipError_t launch_ffn_plan(const int32_t* offsets, int E, int light_max, int32_t* plan,
-                           hipStream_t st);
+// force_tm: 0 = pick the heavy tile height from the counts, else that height.
+hipError_t launch_ffn_plan(const int32_t* offsets, int E, int light_max, int force_tm,
+                           int32_t* plan, hipStream_t st);
 
 struct FfnArgs {
     const uint16_t* x;           // [T,H]
@@ -75,6 +99,7 @@ struct FfnArgs {
     const int32_t* plan;         // device plan, or nullptr for a dense group
     int T, H, I, E;
     int dense_rows;              // rows of a dense group (plan == nullptr)
+    int dense_tm;                // tile height of a dense group (plan == nullptr)
     int split_h;                 // 1: h rows hold [hi | lo] bf16 halves (2I wide) and the
                                  //    down GEMM runs over both against the same weights
     int max_tiles;               // grid bound for heavy tiles

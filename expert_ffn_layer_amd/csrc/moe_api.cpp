@@ -64,6 +64,9 @@ int check_shape(const moe_shape* s) {
     if (s->renorm != 0 && s->renorm != 1) return fail(MOE_ERR_UNSUPPORTED, "renorm must be 0 or 1");
     if (s->light_max_rows < -1 || s->light_max_rows > moe::kLightRowsMax)
         return fail(MOE_ERR_UNSUPPORTED, "light_max_rows must be -1 or in [0, 64]");
+    if (s->heavy_tile_rows != 0 && s->heavy_tile_rows != moe::kTileTM0 &&
+        s->heavy_tile_rows != moe::kTileTM1 && s->heavy_tile_rows != moe::kTileTM2)
+        return fail(MOE_ERR_UNSUPPORTED, "heavy_tile_rows must be 0, 128, 192 or 256");
     return MOE_OK;
 }
 
@@ -168,7 +171,8 @@ int run_permute(const moe_shape* s, const Layout& L, const int32_t* ids, int32_t
     const bool small = (long long)s->T * s->k <= moe::kPermChunk;
     int32_t* plan = (plan_ready && small) ? at<int32_t>(ws, L.plan) : nullptr;
     HIP_TRY(moe::launch_permute(ids, s->T, s->k, s->E, at<int32_t>(ws, L.chunk), L.nchunks,
-                                counts, offsets, sorted, inv, plan, L.light_max, st),
+                                counts, offsets, sorted, inv, plan, L.light_max,
+                                s->heavy_tile_rows, st),
             "permute");
     if (plan_ready) *plan_ready = plan != nullptr;
     return MOE_OK;
@@ -181,7 +185,8 @@ int run_ffn(const moe_shape* s, const Layout& L, const uint16_t* x, const int32_
     if (int rc = device_cu_count(&ncu)) return rc;
     int32_t* plan = at<int32_t>(ws, L.plan);
     if (!plan_ready)
-        HIP_TRY(moe::launch_ffn_plan(offsets, s->E, L.light_max, plan, st), "ffn plan");
+        HIP_TRY(moe::launch_ffn_plan(offsets, s->E, L.light_max, s->heavy_tile_rows, plan, st),
+                "ffn plan");
     moe::FfnArgs a{};
     a.x = x;
     a.sorted_ids = sorted;
@@ -196,6 +201,7 @@ int run_ffn(const moe_shape* s, const Layout& L, const uint16_t* x, const int32_
     a.I = s->I;
     a.E = s->E;
     a.dense_rows = 0;
+    a.dense_tm = 0;
     a.split_h = 0;
     a.max_tiles = L.max_tiles;
     a.max_light = L.max_light;
@@ -223,6 +229,7 @@ int run_shared(const moe_shape* s, const Layout& L, const uint16_t* x, const uin
     a.I = s->I_shared;
     a.E = 1;
     a.dense_rows = s->T;
+    a.dense_tm = s->heavy_tile_rows ? s->heavy_tile_rows : moe::dense_tile_height(s->T);
     // The shared expert's output enters the sum with weight 1, so its h
     // carries a bf16 hi/lo pair: h = hi + lo to ~16 bits.
     a.split_h = 1;

@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(
 __global__ __launch_bounds__(kThreads) void perm_small_kernel(
     const int32_t* __restrict__ ids, int A, int k, int E, int nbits,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_ids,
-    int32_t* __restrict__ inv_pos, int32_t* __restrict__ plan, int light_max, int tile_rows) {
+    int32_t* __restrict__ inv_pos, int32_t* __restrict__ plan, int light_max, int force_tm) {
     extern __shared__ int32_t sm[];  // wcnt[4][E], off[E]
     __shared__ int32_t wsum[4];
     int32_t* wcnt = sm;
@@ -252,6 +252,22 @@ __global__ __launch_bounds__(kThreads) void perm_small_kernel(
     }
 
     if (!plan) return;
+    // Heavy tile height: the cheapest for these counts (same rule as
+    // ffn_plan_kernel).
+    int t0 = 0, t1 = 0, t2 = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (c[j] > light_max) {
+            t0 += (c[j] + kTileTM0 - 1) / kTileTM0;
+            t1 += (c[j] + kTileTM1 - 1) / kTileTM1;
+            t2 += (c[j] + kTileTM2 - 1) / kTileTM2;
+        }
+    }
+    int tot0 = 0, tot1 = 0, tot2 = 0;
+    (void)block256_exclusive_scan(t0, wsum, &tot0);
+    (void)block256_exclusive_scan(t1, wsum, &tot1);
+    (void)block256_exclusive_scan(t2, wsum, &tot2);
+    const int tile_rows = force_tm ? force_tm : tile_height(pick_tile_height(tot0, tot1, tot2));
     int lj[4], tj[4], lsum = 0, tsum = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -276,6 +292,7 @@ __global__ __launch_bounds__(kThreads) void perm_small_kernel(
     if (threadIdx.x == 0) {
         plan[0] = ltot;
         plan[1] = ttot;
+        plan[2] = tile_rows;
     }
 }
 
@@ -283,7 +300,8 @@ __global__ __launch_bounds__(kThreads) void perm_small_kernel(
 
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* chunk_counts,
                           int nchunks, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
-                          int32_t* inv_pos, int32_t* plan, int light_max, hipStream_t st) {
+                          int32_t* inv_pos, int32_t* plan, int light_max, int force_tm,
+                          hipStream_t st) {
     const long long A = (long long)T * k;
     int nbits = 1;
     while ((1 << nbits) < E) ++nbits;
@@ -291,7 +309,7 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* chun
         prof_begin(K_PERM_SMALL, st);
         perm_small_kernel<<<1, kThreads, (kWavesPerBlock + 1) * E * sizeof(int32_t), st>>>(
             ids, (int)A, k, E, nbits, counts, offsets, sorted_ids, inv_pos, plan, light_max,
-            kHeavyBM);
+            force_tm);
         prof_end(K_PERM_SMALL, st);
         return hipGetLastError();
     }

@@ -42,7 +42,8 @@ LIGHT_MAX_ROWS = 64
 class MoeShape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("I", ctypes.c_int32), ("I_shared", ctypes.c_int32),
-                ("renorm", ctypes.c_int32), ("light_max_rows", ctypes.c_int32)]
+                ("renorm", ctypes.c_int32), ("light_max_rows", ctypes.c_int32),
+                ("heavy_tile_rows", ctypes.c_int32)]
 
     def __repr__(self):
         return ("MoeShape(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")")
@@ -100,8 +101,9 @@ def _check(rc: int) -> None:
         raise MoeError(rc, f"{status_string(rc)}: {last_error()}")
 
 
-def make_shape(T, H, E, k, I, I_shared=0, renorm=1, light_max_rows=-1) -> MoeShape:
-    return MoeShape(T, H, E, k, I, I_shared, renorm, light_max_rows)
+def make_shape(T, H, E, k, I, I_shared=0, renorm=1, light_max_rows=-1,
+               heavy_tile_rows=0) -> MoeShape:
+    return MoeShape(T, H, E, k, I, I_shared, renorm, light_max_rows, heavy_tile_rows)
 
 
 def workspace_bytes(shape: MoeShape) -> int:
@@ -232,10 +234,11 @@ class MoELayer:
     """Convenience holder: weights + one workspace; ``__call__`` runs
     moe_forward and returns (out, topk_ids, topk_w, counts)."""
 
-    def __init__(self, layer, light_max_rows: int = -1):
+    def __init__(self, layer, light_max_rows: int = -1, heavy_tile_rows: int = 0):
         c = layer.cfg
         self.layer = layer
-        self.shape = make_shape(c.T, c.H, c.E, c.k, c.I, c.I_shared, c.renorm, light_max_rows)
+        self.shape = make_shape(c.T, c.H, c.E, c.k, c.I, c.I_shared, c.renorm, light_max_rows,
+                                heavy_tile_rows)
         self.workspace = alloc_workspace(self.shape, layer.x.device)
 
     def __call__(self, x=None, out=None, want_routing=True):

@@ -80,6 +80,9 @@ typedef struct moe_shape {
                                -1 = library default (64); 0 = every expert takes the
                                heavy tiles; at most 64.  An expert never gets more than T
                                rows, so with T <= light_max_rows no heavy kernel runs. */
+    int32_t heavy_tile_rows; /* rows per heavy tile: 0 = chosen per call from the expert
+                               row counts (the least padded-row time); 128, 192 or 256
+                               = that height.  Results do not depend on it. */
 } moe_shape;
 
 /* Bytes of workspace every call below needs for `shape` (host-only, pure;

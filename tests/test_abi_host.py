@@ -41,7 +41,8 @@ def test_library_has_gfx950_code():
 
 
 def shp(**kw):
-    base = dict(T=64, H=4096, E=512, k=10, I=1024, I_shared=0, renorm=1, light_max_rows=-1)
+    base = dict(T=64, H=4096, E=512, k=10, I=1024, I_shared=0, renorm=1, light_max_rows=-1,
+                heavy_tile_rows=0)
     base.update(kw)
     return moe.MoeShape(*[base[n] for n, _ in moe.MoeShape._fields_])
 
@@ -65,6 +66,7 @@ def test_workspace_no_padding(L):
     (dict(H=100), moe.MOE_ERR_UNSUPPORTED), (dict(I=48), moe.MOE_ERR_UNSUPPORTED),
     (dict(E=2048, k=4), moe.MOE_ERR_UNSUPPORTED), (dict(k=33), moe.MOE_ERR_UNSUPPORTED),
     (dict(renorm=2), moe.MOE_ERR_UNSUPPORTED), (dict(light_max_rows=65), moe.MOE_ERR_UNSUPPORTED),
+    (dict(heavy_tile_rows=100), moe.MOE_ERR_UNSUPPORTED), (dict(heavy_tile_rows=64), moe.MOE_ERR_UNSUPPORTED),
     (dict(I_shared=40), moe.MOE_ERR_UNSUPPORTED), (dict(T=300000000, k=10), moe.MOE_ERR_SHAPE),
     (dict(T=1 << 19, k=1), moe.MOE_ERR_UNSUPPORTED), (dict(I=1 << 18), moe.MOE_ERR_UNSUPPORTED),
     (dict(I_shared=1 << 18), moe.MOE_ERR_UNSUPPORTED),

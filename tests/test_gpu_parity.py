@@ -63,6 +63,35 @@ def test_forward_heavy_only(oracle_lib, name):
     log(name + "/heavy", rep)
 
 
+# ------------------------------------------------------------ tile heights
+# ~225 rows per expert: 1 tile of 256, 2 ragged tiles of 192 or 128; I % 64 ==
+# 32 gives the down GEMM a half-full last K stage, and the shared expert's
+# [hi | lo] K run straddles I inside one 64-wide stage.
+TILES = custom("tiles", T=600, H=320, E=8, k=3, I=96, I_shared=96)
+
+
+def test_tile_heights_bitwise(oracle_lib):
+    """Every heavy tile height gives the same output bits (each element's
+    MFMA chain over K is the same), and matches the oracle."""
+    print("[case] tile heights", flush=True)
+    lay = layer_on_gpu(TILES)
+    outs = {}
+    for tm in (0, 256, 192, 128):
+        g = gh.gpu_forward(lay, light_max_rows=0, heavy_tile_rows=tm)
+        outs[tm] = g["out"].view(np.int32)
+    for tm in (256, 192, 128):
+        assert np.array_equal(outs[tm], outs[0]), f"tile height {tm} differs"
+    rep = gh.check_layer(oracle_lib, lay, light_max_rows=0, heavy_tile_rows=192)
+    log("tiles/192", rep)
+
+
+@pytest.mark.parametrize("tm", [128, 192, 256])
+def test_forward_heavy_ragged_heights(oracle_lib, tm):
+    print(f"[case] heavy_ragged tm={tm}", flush=True)
+    rep = gh.check_layer(oracle_lib, layer_on_gpu(SMALL["heavy_ragged"]), heavy_tile_rows=tm)
+    log(f"heavy_ragged/{tm}", rep)
+
+
 # ------------------------------------------------------------ full size
 @pytest.mark.parametrize("name,sample", [("decode", None), ("prefill", 64), ("skew", 64),
                                          ("ling", 48)])
