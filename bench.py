@@ -103,13 +103,23 @@ def summarize(args):
         with open(os.path.join(d, names[0])) as f:
             return list(csv.DictReader(f))
 
+    # A heavy GEMM call launches one kernel per tile height (all but the chosen
+    # one return at once): per call, durations and bytes add over heights.
     stats = {}
     for r in one_csv(kt_dir, "kernel_stats.csv"):
         lab = kernel_label(r["Name"])
-        if lab:
-            stats[lab] = dict(calls=int(r["Calls"]), avg_us=float(r["AverageNs"]) / 1e3,
-                              min_us=float(r["MinNs"]) / 1e3, max_us=float(r["MaxNs"]) / 1e3,
-                              total_us=float(r["TotalDurationNs"]) / 1e3)
+        if not lab:
+            continue
+        cur = dict(calls=int(r["Calls"]), min_us=float(r["MinNs"]) / 1e3,
+                   max_us=float(r["MaxNs"]) / 1e3, total_us=float(r["TotalDurationNs"]) / 1e3)
+        if lab in stats:
+            prev = stats[lab]
+            big = prev if prev["total_us"] >= cur["total_us"] else cur
+            cur = dict(calls=max(prev["calls"], cur["calls"]), min_us=big["min_us"],
+                       max_us=big["max_us"], total_us=prev["total_us"] + cur["total_us"])
+        stats[lab] = cur
+    for st_ in stats.values():
+        st_["avg_us"] = st_["total_us"] / st_["calls"]
 
     def counter(d):
         per, copy = {}, None
@@ -120,10 +130,11 @@ def summarize(args):
                 continue
             lab = kernel_label(r["Kernel_Name"])
             if lab:
-                per.setdefault(lab, []).append(v)
+                per.setdefault(lab, {}).setdefault(r["Kernel_Name"], []).append(v)
         assert copy, f"no reference copy kernel in {d}"
         scale = COPY_BYTES / (copy * 1024.0)
-        return {k: sum(v) / len(v) * 1024.0 * scale for k, v in per.items()}, scale
+        return {k: sum(sum(v) / len(v) for v in inst.values()) * 1024.0 * scale
+                for k, inst in per.items()}, scale
 
     fetch, f_scale = counter(fetch_dir)
     write, w_scale = counter(write_dir)
@@ -158,8 +169,9 @@ def summarize(args):
              "rocprofv3 summary of bench.py on one MI355X (gfx950).  Commands, from /tmp with",
              "TMPDIR=/tmp, $R the repository root:", "", "```", cmds, "```", "",
              f"Dominant kernel: **{dom}**, average {stats[dom]['avg_us']:.1f} us over "
-             f"{stats[dom]['calls']} launches (kernel trace); bench.py's own HIP-event timing "
-             f"of it in the same run: {roof['kernel_us']:.1f} us.",
+             f"{stats[dom]['calls']} calls (kernel trace; a heavy GEMM call is one launch per "
+             f"tile height, summed); bench.py's own HIP-event timing of it in the same run: "
+             f"{roof['kernel_us']:.1f} us.",
              "", f"bench line: {rec['value']:.1f} {rec['unit']}, {rec['ms_per_step']:.4f} ms/step; "
              f"roofline {roof['bound']} {roof['achieved']} {roof['unit']} "
              f"(frac {roof['frac']}) for {roof['kernel']}.", "",
