@@ -5,7 +5,9 @@ One step = one moe_forward call (router GEMM, softmax/top-k, permute,
 grouped gate|up+SwiGLU and down FFN, combine) over one batch of seeded
 synthetic input already resident in HBM.  W untimed warm-up steps, then
 exactly K timed steps bracketed by torch.cuda.synchronize().  Prints one JSON
-line.
+line.  The routed expert weights are re-laid out once for the heavy tiles
+(moe_pack_weights) before anything is timed, as a serving engine does at load
+time; --no-packed keeps the plain layout.
 
 Default workload: one decode step of a Qwen-3.5-like layer (T=64 tokens,
 H=4096, E=512 experts, top-10, I=1024, bf16 experts, fp32 router).
@@ -46,6 +48,9 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=64, help="tokens in the oracle's sample")
+    p.add_argument("--no-packed", action="store_true",
+                   help="heavy tiles read the plain weight layout instead of the packed copy "
+                        "made once before timing (moe_pack_weights)")
     p.add_argument("--no-copy-calibration", action="store_true",
                    help="skip the untimed 1 GiB reference copy used to scale rocprof counters")
     p.add_argument("--summarize", nargs=4, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR", "LOG"),
@@ -239,7 +244,7 @@ def main():
     layer = synth.make_layer(cfg, seed=args.seed, device=dev)
     if cfg.fp32_values:
         layer = layer.rounded_to_bf16()
-    m = moe.MoELayer(layer)
+    m = moe.MoELayer(layer, packed=not args.no_packed)
     s = m.shape
     out = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=dev)
     ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
@@ -249,7 +254,8 @@ def main():
 
     def step():
         moe.forward(s, layer.x, layer.wg, layer.bias, layer.w_gu, layer.w_dn, layer.ws_gu,
-                    layer.ws_dn, out, m.workspace, ids, w, counts, stream=stream)
+                    layer.ws_dn, out, m.workspace, ids, w, counts, stream=stream,
+                    packed_weights=m.packed)
 
     for _ in range(max(args.warmup, 1)):
         step()
@@ -375,7 +381,7 @@ def main():
         "data": "synthetic (seeded normal draws, random-init weights)",
         "config": {"workload": workload, "tokens": cfg.T, "hidden": H, "experts": cfg.E,
                    "top_k": cfg.k, "intermediate": I, "shared_intermediate": cfg.I_shared,
-                   "seed": args.seed},
+                   "seed": args.seed, "packed_weights": m.packed is not None},
         "roofline": roof,
         "layer_roofline": layer,
         "kernels_us": {k: round(v, 2) for k, v in per_kernel.items()},

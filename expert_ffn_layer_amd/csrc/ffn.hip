@@ -365,17 +365,18 @@ __global__ __launch_bounds__(kThreads) void down_light_kernel(FfnArgs a) {
 // 256x256 output tiles computed by 8 waves (2 per SIMD) in a 2 (rows) x 4
 // (columns) grid; each wave owns a 128x64 block of 16x16 MFMA tiles (32
 // accumulators per lane).  Operands are staged with direct-to-LDS 16-byte
-// loads (global_load_lds_dwordx4) into a two-buffer ring, one 64-wide K step
+// loads (buffer_load_dwordx4 ... lds) into LDS rings, one 64-wide K step
 // per buffer, so that every load instruction reads 8 whole rows of 128
 // contiguous bytes (full cache lines).
 //
 // LDS layout of a stage: A then B, each a run of 1 KB blocks, block b holding
 // tile rows 8b..8b+7 x the stage's 64 K values.  Inside a block, 16-byte slot
-// p holds row p/8, K chunk (p%8) ^ (p/8) ^ (b%2) (chunk c = K values
-// 8c..8c+7).  The load that fills a block therefore reads one 128-byte line
-// per 8 lanes, and the MFMA fragment read (lane l: row l%16, chunk
-// l/16 + 4*half) lands its 8 lanes of a row group on 8 different 16-byte bank
-// groups, and its two row groups on the two complementary sets.
+// p holds row p/8, K chunk (p%8) ^ (p/8) (chunk c = K values 8c..8c+7).  The
+// load that fills a block therefore reads one 128-byte line per 8 lanes, and
+// the MFMA fragment read (lane l: row l%16, chunk l/16 + 4*half) puts the 8
+// lanes of each row group on 8 different 16-byte bank groups.  (Measured on
+// MI355X: this read runs at the speed of a contiguous 1 KB read; also
+// xor-ing the block parity into the chunk costs a third of it.)
 enum class Mode { GateUp, Down };
 
 constexpr int kHeavyThreads = 512;
@@ -480,17 +481,19 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
     const int l16 = lane & 15, g = lane >> 4;
     const int nh = K / 32;         // 32-wide MFMA K steps (K % 32 == 0)
     const int nst = (nh + 1) / 2;  // 64-wide stages; the last one is half full if nh is odd
-    // DMA side: lane L fills slot L of a block: row L/8, chunk (L%8)^(L/8)^(b%2).
+    // Packed weights (routed experts only; a split_h group reads W_down twice
+    // and uses the plain layout).
+    const char* pk = a.split_h ? nullptr : (M == Mode::GateUp ? a.pk_gu : a.pk_dn);
+    // DMA side: lane L fills slot L of a block: row L/8, chunk (L%8)^(L/8).
     const int drow = lane >> 3;
-    const int dchunk = (lane & 7) ^ drow;  // for even blocks; odd blocks use dchunk ^ 1
-    // Lanes whose chunk is in the upper half of the stage (K values 32..63):
-    // bit 2 of the chunk, which the odd-block swizzle keeps.
+    const int dchunk = (lane & 7) ^ drow;
+    // Lanes whose chunk is in the upper half of the stage (K values 32..63).
     const bool upper = (dchunk & 4) != 0;
     // Fragment side: lane l reads row l%16 (block 2f + (l%16)/8), chunk g + 4*half.
-    const int fpar = (lane >> 3) & 1;
+    const int fblk = (lane >> 3) & 1;
     const int frow = lane & 7;
-    const int foff0 = fpar * kBlk + frow * 128 + ((g ^ frow ^ fpar) << 4);
-    const int foff1 = fpar * kBlk + frow * 128 + (((g + 4) ^ frow ^ fpar) << 4);
+    const int foff0 = fblk * kBlk + frow * 128 + ((g ^ frow) << 4);
+    const int foff1 = fblk * kBlk + frow * 128 + (((g + 4) ^ frow) << 4);
 
     // XCD-aware static schedule.  The work list is tile-major (tiles of one
     // expert are adjacent) with the N block fastest; it is cut into nslice
@@ -531,17 +534,21 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
         // is added once per stage.
         if (M == Mode::GateUp) {
             ar = make_rsrc(a.x, (uint32_t)((size_t)a.T * a.H * 2));
-            br = make_rsrc(a.w_gu + (size_t)e * 2 * a.I * a.H, (uint32_t)((size_t)2 * a.I * a.H * 2));
+            br = pk ? make_rsrc(pk + ((size_t)e * nblk + nb) * nst * kPackStage,
+                                (uint32_t)(nst * kPackStage))
+                    : make_rsrc(a.w_gu + (size_t)e * 2 * a.I * a.H, (uint32_t)((size_t)2 * a.I * a.H * 2));
         } else {
             ar = make_rsrc(a.h + (size_t)(r0 + m0) * hstride, (uint32_t)((size_t)TM * hstride * 2));
-            br = make_rsrc(a.w_dn + (size_t)e * a.H * a.I, (uint32_t)((size_t)a.H * a.I * 2));
+            br = pk ? make_rsrc(pk + ((size_t)e * nblk + nb) * nst * kPackStage,
+                                (uint32_t)(nst * kPackStage))
+                    : make_rsrc(a.w_dn + (size_t)e * a.H * a.I, (uint32_t)((size_t)a.H * a.I * 2));
         }
 #pragma unroll
         for (int i = 0; i < kABlk; ++i) {
             const int b = kABlk * wave + i;
             const int r = b * 8 + drow;         // row within the tile
             const int rr = r < rows ? r : 0;    // rows past the count: any valid row
-            const uint32_t cb = (uint32_t)(dchunk ^ (b & 1)) * 16u;
+            const uint32_t cb = (uint32_t)dchunk * 16u;
             if (M == Mode::GateUp) {
                 const int tok = a.sorted_ids ? a.sorted_ids[r0 + m0 + rr] : r0 + m0 + rr;
                 aoff[i] = (uint32_t)tok * (uint32_t)a.H * 2u + cb;
@@ -553,8 +560,11 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
         for (int i = 0; i < kBBlkPerWave; ++i) {
             const int b = kBBlkPerWave * wave + i;
             const int r = b * 8 + drow;  // B row within the tile
-            const uint32_t cb = (uint32_t)(dchunk ^ (b & 1)) * 16u;
-            if (M == Mode::GateUp) {
+            const uint32_t cb = (uint32_t)dchunk * 16u;
+            if (pk) {
+                // packed: the stage image is the LDS image, block b at b KB
+                boff[i] = (uint32_t)b * kBlk + (uint32_t)lane * 16u;
+            } else if (M == Mode::GateUp) {
                 // 16-row blocks alternate: block 2p = gate rows, 2p+1 = the
                 // matching up rows, so g and u of an element share a lane.
                 const int hc = nb * (kTN / 2) + (r >> 5) * 16 + (r & 15);
@@ -599,7 +609,9 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
         const int kb = (M == Mode::Down && kk >= a.I) ? kk - a.I : kk;
         uint32_t adj_a, adj_b;
         adjust(kk, adj_a, adj_b);
-        const uint32_t sb = (uint32_t)kb * 2u - adj_b;
+        // packed weights: stage st's image at st * 32 KB (the half-full last
+        // stage and the zero rows past I or H are stored as zeros)
+        const uint32_t sb = pk ? (uint32_t)(st * kPackStage) : (uint32_t)kb * 2u - adj_b;
 #pragma unroll
         for (int i = 0; i < kBBlkPerWave; ++i)
             lds_dma16_buf(br, boff[i] + sb, 0u, buf + (kBBlkPerWave * wave + i) * kBlk);
@@ -776,6 +788,47 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
     }
 }
 
+// Packs one weight tensor into heavy-tile load order: slot q (16 bytes) of
+// the output is, for q = ((e * nblk + nb) * nst + st) * 2048 + b * 64 + p,
+// B row r = 8b + p/8 of output block nb, K chunk c = (p % 8) ^ (p / 8),
+// i.e. K values st*64 + 8c .. +7 (the same map as the heavy kernels'
+// direct-to-LDS loads).  gate|up: B rows alternate 16 gate / 16
+// up rows of h columns nb*128 ..; down: B row r is W_down row nb*256 + r.
+// Rows past I (or H) and K past the end are zeros.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __restrict__ w, int E,
+                                                           int rows, int K, int nblk, int nst,
+                                                           int gate_up, int I,
+                                                           uint16_t* __restrict__ out) {
+    const long long total = (long long)E * nblk * nst * (kPackStage / 16);
+    for (long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x; q < total;
+         q += (long long)gridDim.x * blockDim.x) {
+        const int slot = (int)(q & 2047);
+        long long t = q >> 11;
+        const int st = (int)(t % nst);
+        t /= nst;
+        const int nb = (int)(t % nblk);
+        const int e = (int)(t / nblk);
+        const int b = slot >> 6, p = slot & 63;
+        const int r = 8 * b + (p >> 3);
+        const int c = (p & 7) ^ (p >> 3);
+        const int k = st * 64 + 8 * c;
+        int row;
+        bool ok;
+        if (gate_up) {
+            const int hc = nb * 128 + (r >> 5) * 16 + (r & 15);
+            ok = hc < I;
+            row = (r & 16) ? I + hc : hc;
+        } else {
+            row = nb * 256 + r;
+            ok = row < rows;
+        }
+        ok = ok && k < K;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (ok) v = *reinterpret_cast<const u32x4_t*>(w + ((size_t)e * rows + row) * K + k);
+        *reinterpret_cast<u32x4_t*>(out + q * 8) = v;
+    }
+}
+
 int grid_for(long long work, int per_cu, int num_cu) {
     return (int)std::max<long long>(1, std::min<long long>(work, (long long)per_cu * num_cu));
 }
@@ -807,6 +860,30 @@ hipError_t launch_heavy(const FfnArgs& a, int ncols, hipStream_t st) {
 }
 
 }  // namespace
+
+size_t packed_gu_bytes(int E, int H, int I) {
+    return (size_t)E * ((I + 127) / 128) * (H / 64) * kPackStage;
+}
+
+size_t packed_dn_bytes(int E, int H, int I) {
+    return (size_t)E * ((H + 255) / 256) * ((I + 63) / 64) * kPackStage;
+}
+
+hipError_t launch_pack_weights(const uint16_t* w_gu, const uint16_t* w_dn, int E, int H, int I,
+                               char* packed, hipStream_t st) {
+    const int nbg = (I + 127) / 128, nstg = H / 64;
+    const int nbd = (H + 255) / 256, nstd = (I + 63) / 64;
+    const long long sg = (long long)E * nbg * nstg * (kPackStage / 16);
+    const long long sd = (long long)E * nbd * nstd * (kPackStage / 16);
+    pack_weights_kernel<<<(int)std::min<long long>((sg + 255) / 256, 65536), 256, 0, st>>>(
+        w_gu, E, 2 * I, H, nbg, nstg, 1, I, reinterpret_cast<uint16_t*>(packed));
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    pack_weights_kernel<<<(int)std::min<long long>((sd + 255) / 256, 65536), 256, 0, st>>>(
+        w_dn, E, H, I, nbd, nstd, 0, I,
+        reinterpret_cast<uint16_t*>(packed + packed_gu_bytes(E, H, I)));
+    return hipGetLastError();
+}
 
 hipError_t launch_ffn_plan(const int32_t* offsets, int E, int light_max, int force_tm,
                            int32_t* plan, hipStream_t st) {

@@ -103,9 +103,21 @@ struct FfnArgs {
     int split_h;                 // 1: h rows hold [hi | lo] bf16 halves (2I wide) and the
                                  //    down GEMM runs over both against the same weights
     int max_tiles;               // grid bound for heavy tiles
+    const char* pk_gu;           // packed W_gate|up (heavy-tile load order) or nullptr
+    const char* pk_dn;           // packed W_down or nullptr (not with split_h)
     int max_light;               // grid bound for light experts
     int num_cu;
 };
+
+// Packed expert weights: for each expert and 256-row output block, every
+// 64-wide K stage of the heavy tiles' weight operand as one contiguous 32 KB
+// image in the LDS order the heavy kernels use, so the weights stream as
+// long contiguous runs.  gate|up first, then down.
+constexpr size_t kPackStage = 32768;
+size_t packed_gu_bytes(int E, int H, int I);
+size_t packed_dn_bytes(int E, int H, int I);
+hipError_t launch_pack_weights(const uint16_t* w_gu, const uint16_t* w_dn, int E, int H, int I,
+                               char* packed, hipStream_t st);
 
 hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st);

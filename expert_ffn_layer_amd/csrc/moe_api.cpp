@@ -179,8 +179,9 @@ int run_permute(const moe_shape* s, const Layout& L, const int32_t* ids, int32_t
 }
 
 int run_ffn(const moe_shape* s, const Layout& L, const uint16_t* x, const int32_t* sorted,
-            const int32_t* offsets, const uint16_t* wgu, const uint16_t* wdn, uint16_t* h,
-            float* y, void* ws, hipStream_t st, bool plan_ready = false) {
+            const int32_t* offsets, const uint16_t* wgu, const uint16_t* wdn,
+            const void* packed, uint16_t* h, float* y, void* ws, hipStream_t st,
+            bool plan_ready = false) {
     int ncu = 0;
     if (int rc = device_cu_count(&ncu)) return rc;
     int32_t* plan = at<int32_t>(ws, L.plan);
@@ -206,6 +207,10 @@ int run_ffn(const moe_shape* s, const Layout& L, const uint16_t* x, const int32_
     a.max_tiles = L.max_tiles;
     a.max_light = L.max_light;
     a.num_cu = ncu;
+    if (packed) {
+        a.pk_gu = static_cast<const char*>(packed);
+        a.pk_dn = a.pk_gu + moe::packed_gu_bytes(s->E, s->H, s->I);
+    }
     HIP_TRY(moe::launch_ffn_gateup(a, st), "ffn gate|up");
     HIP_TRY(moe::launch_ffn_down(a, st), "ffn down");
     return MOE_OK;
@@ -248,6 +253,26 @@ extern "C" {
 size_t moe_workspace_bytes(const moe_shape* shape) {
     if (check_shape(shape) != MOE_OK) return 0;
     return layout(shape).total;
+}
+
+size_t moe_packed_weight_bytes(const moe_shape* shape) {
+    if (check_shape(shape) != MOE_OK) return 0;
+    return moe::packed_gu_bytes(shape->E, shape->H, shape->I) +
+           moe::packed_dn_bytes(shape->E, shape->H, shape->I);
+}
+
+int moe_pack_weights(const moe_shape* shape, const uint16_t* w_gate_up, const uint16_t* w_down,
+                     void* packed, void* stream) {
+    g_last_error.clear();
+    if (int rc = check_shape(shape)) return rc;
+    REQUIRE_PTR(w_gate_up);
+    REQUIRE_PTR(w_down);
+    if (!packed) return fail(MOE_ERR_NULL, "packed is NULL");
+    if (!aligned(packed, kAlign)) return fail(MOE_ERR_ALIGN, "packed must be 256-byte aligned");
+    HIP_TRY(moe::launch_pack_weights(w_gate_up, w_down, shape->E, shape->H, shape->I,
+                                     static_cast<char*>(packed), (hipStream_t)stream),
+            "pack weights");
+    return MOE_OK;
 }
 
 const char* moe_status_string(int status) {
@@ -318,7 +343,8 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t* counts
 
 int moe_grouped_ffn(const moe_shape* shape, const uint16_t* x, const int32_t* sorted_token_ids,
                     const int32_t* offsets, const uint16_t* w_gate_up, const uint16_t* w_down,
-                    uint16_t* h, float* y, void* workspace, size_t ws_bytes, void* stream) {
+                    const void* packed_weights, uint16_t* h, float* y, void* workspace,
+                    size_t ws_bytes, void* stream) {
     g_last_error.clear();
     if (int rc = check_shape(shape)) return rc;
     if (shape->T == 0) return MOE_OK;
@@ -329,9 +355,11 @@ int moe_grouped_ffn(const moe_shape* shape, const uint16_t* x, const int32_t* so
     REQUIRE_PTR(w_down);
     REQUIRE_PTR(y);
     OPTIONAL_PTR(h);
+    if (packed_weights && !aligned(packed_weights, kAlign))
+        return fail(MOE_ERR_ALIGN, "packed_weights must be 256-byte aligned");
     if (int rc = check_ws(shape, workspace, ws_bytes)) return rc;
-    return run_ffn(shape, layout(shape), x, sorted_token_ids, offsets, w_gate_up, w_down, h, y,
-                   workspace, (hipStream_t)stream);
+    return run_ffn(shape, layout(shape), x, sorted_token_ids, offsets, w_gate_up, w_down,
+                   packed_weights, h, y, workspace, (hipStream_t)stream);
 }
 
 int moe_shared_ffn(const moe_shape* shape, const uint16_t* x, const uint16_t* ws_gate_up,
@@ -367,7 +395,8 @@ int moe_combine(const moe_shape* shape, const float* y, const int32_t* inv_pos,
 
 int moe_forward(const moe_shape* shape, const uint16_t* x, const float* w_router,
                 const float* bias, const uint16_t* w_gate_up, const uint16_t* w_down,
-                const uint16_t* ws_gate_up, const uint16_t* ws_down, float* out,
+                const void* packed_weights, const uint16_t* ws_gate_up, const uint16_t* ws_down,
+                float* out,
                 int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, void* workspace,
                 size_t ws_bytes, void* stream) {
     g_last_error.clear();
@@ -395,6 +424,8 @@ int moe_forward(const moe_shape* shape, const uint16_t* x, const float* w_router
         REQUIRE_PTR(ws_gate_up);
         REQUIRE_PTR(ws_down);
     }
+    if (packed_weights && !aligned(packed_weights, kAlign))
+        return fail(MOE_ERR_ALIGN, "packed_weights must be 256-byte aligned");
     if (int rc = check_ws(shape, workspace, ws_bytes)) return rc;
     const Layout L = layout(shape);
     int32_t* counts = counts_out ? counts_out : at<int32_t>(workspace, L.counts);
@@ -408,8 +439,8 @@ int moe_forward(const moe_shape* shape, const uint16_t* x, const float* w_router
     bool plan_ready = false;
     if (int rc = run_permute(shape, L, ids, counts, offsets, sorted, inv, workspace, st, &plan_ready))
         return rc;
-    if (int rc = run_ffn(shape, L, x, sorted, offsets, w_gate_up, w_down, nullptr, y, workspace, st,
-                         plan_ready))
+    if (int rc = run_ffn(shape, L, x, sorted, offsets, w_gate_up, w_down, packed_weights, nullptr,
+                         y, workspace, st, plan_ready))
         return rc;
     if (shape->I_shared > 0)
         if (int rc = run_shared(shape, L, x, ws_gate_up, ws_down, out, workspace, st)) return rc;

@@ -26,9 +26,10 @@ MOE_ERR_ALIGN = 4
 MOE_ERR_WORKSPACE = 5
 MOE_ERR_HIP = 6
 
-EXPORTED = ("moe_workspace_bytes", "moe_status_string", "moe_last_error", "moe_router",
-            "moe_permute", "moe_grouped_ffn", "moe_shared_ffn", "moe_combine", "moe_forward",
-            "moe_profile_kernel", "moe_profile_launches")
+EXPORTED = ("moe_workspace_bytes", "moe_packed_weight_bytes", "moe_status_string",
+            "moe_last_error", "moe_router", "moe_permute", "moe_pack_weights", "moe_grouped_ffn",
+            "moe_shared_ffn", "moe_combine", "moe_forward", "moe_profile_kernel",
+            "moe_profile_launches")
 
 # enum moe_kernel
 KERNELS = ("router_gemm", "router_select", "perm_count", "perm_scan", "perm_scatter", "ffn_plan",
@@ -68,21 +69,24 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         L.moe_workspace_bytes.argtypes = [_sp]
         L.moe_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_packed_weight_bytes.argtypes = [_sp]
+        L.moe_packed_weight_bytes.restype = ctypes.c_size_t
+        L.moe_pack_weights.argtypes = [_sp] + [_vp] * 4
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_last_error.argtypes = []
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_router.argtypes = [_sp] + [_vp] * 7 + [ctypes.c_size_t, _vp]
         L.moe_permute.argtypes = [_sp] + [_vp] * 6 + [ctypes.c_size_t, _vp]
-        L.moe_grouped_ffn.argtypes = [_sp] + [_vp] * 8 + [ctypes.c_size_t, _vp]
+        L.moe_grouped_ffn.argtypes = [_sp] + [_vp] * 9 + [ctypes.c_size_t, _vp]
         L.moe_shared_ffn.argtypes = [_sp] + [_vp] * 5 + [ctypes.c_size_t, _vp]
         L.moe_combine.argtypes = [_sp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp]
-        L.moe_forward.argtypes = [_sp] + [_vp] * 12 + [ctypes.c_size_t, _vp]
+        L.moe_forward.argtypes = [_sp] + [_vp] * 13 + [ctypes.c_size_t, _vp]
         L.moe_profile_kernel.argtypes = [ctypes.c_int, _vp, _vp]
         L.moe_profile_launches.argtypes = []
         L.moe_profile_launches.restype = ctypes.c_longlong
-        for name in ("moe_router", "moe_permute", "moe_grouped_ffn", "moe_shared_ffn",
-                     "moe_combine", "moe_forward", "moe_profile_kernel"):
+        for name in ("moe_router", "moe_permute", "moe_pack_weights", "moe_grouped_ffn",
+                     "moe_shared_ffn", "moe_combine", "moe_forward", "moe_profile_kernel"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -115,6 +119,34 @@ def alloc_workspace(shape: MoeShape, device=None) -> torch.Tensor:
     if n == 0:
         raise MoeError(MOE_ERR_SHAPE, f"invalid shape {shape}")
     return torch.empty(n, dtype=torch.uint8, device=device or torch.device("cuda"))
+
+
+def packed_weight_bytes(shape: MoeShape) -> int:
+    return int(lib().moe_packed_weight_bytes(ctypes.byref(shape)))
+
+
+def pack_weights(shape: MoeShape, w_gate_up, w_down, stream=None) -> torch.Tensor:
+    """One-time re-layout of the routed expert weights for the heavy tiles
+    (moe_pack_weights); returns the packed uint8 device buffer."""
+    n = packed_weight_bytes(shape)
+    if n == 0:
+        raise MoeError(MOE_ERR_SHAPE, f"invalid shape {shape}")
+    E, H, I = shape.E, shape.H, shape.I
+    out = torch.empty(n, dtype=torch.uint8, device=w_gate_up.device)
+    _check(lib().moe_pack_weights(ctypes.byref(shape),
+                                  _ptr(w_gate_up, "w_gate_up", BF16, E * 2 * I * H),
+                                  _ptr(w_down, "w_down", BF16, E * H * I), out.data_ptr(),
+                                  _stream(stream)))
+    return out
+
+
+def _packed(p: Optional[torch.Tensor], shape: MoeShape):
+    if p is None:
+        return None
+    n = packed_weight_bytes(shape)
+    if not p.is_cuda or p.dtype != torch.uint8 or p.numel() < n:
+        raise ValueError(f"packed_weights must be a uint8 device tensor of >= {n} bytes")
+    return p.data_ptr()
 
 
 def _ptr(t: Optional[torch.Tensor], name: str, dtype, numel: Optional[int] = None,
@@ -170,11 +202,12 @@ def permute(shape, topk_ids, counts, offsets, sorted_token_ids, inv_pos, workspa
 
 
 def grouped_ffn(shape, x, sorted_token_ids, offsets, w_gate_up, w_down, h, y, workspace,
-                stream=None):
+                stream=None, packed_weights=None):
     T, H, E, I, A = shape.T, shape.H, shape.E, shape.I, shape.T * shape.k
     args = [_ptr(x, "x", BF16, T * H), _ptr(sorted_token_ids, "sorted_token_ids", I32, A),
             _ptr(offsets, "offsets", I32, E + 1), _ptr(w_gate_up, "w_gate_up", BF16, E * 2 * I * H),
-            _ptr(w_down, "w_down", BF16, E * H * I), _ptr(h, "h", BF16, A * I, optional=True),
+            _ptr(w_down, "w_down", BF16, E * H * I), _packed(packed_weights, shape),
+            _ptr(h, "h", BF16, A * I, optional=True),
             _ptr(y, "y", F32, A * H)]
     wp, wn = _ws(workspace, shape)
     _check(lib().moe_grouped_ffn(ctypes.byref(shape), *args, wp, wn, _stream(stream)))
@@ -197,12 +230,12 @@ def combine(shape, y, inv_pos, topk_w, accumulate, out, stream=None):
 
 
 def forward(shape, x, w_router, bias, w_gate_up, w_down, ws_gate_up, ws_down, out, workspace,
-            topk_ids_out=None, topk_w_out=None, counts_out=None, stream=None):
+            topk_ids_out=None, topk_w_out=None, counts_out=None, stream=None, packed_weights=None):
     T, H, E, k, I, Is = shape.T, shape.H, shape.E, shape.k, shape.I, shape.I_shared
     args = [_ptr(x, "x", BF16, T * H), _ptr(w_router, "w_router", F32, H * E),
             _ptr(bias, "bias", F32, E, optional=True),
             _ptr(w_gate_up, "w_gate_up", BF16, E * 2 * I * H),
-            _ptr(w_down, "w_down", BF16, E * H * I),
+            _ptr(w_down, "w_down", BF16, E * H * I), _packed(packed_weights, shape),
             _ptr(ws_gate_up, "ws_gate_up", BF16, 2 * Is * H, optional=True),
             _ptr(ws_down, "ws_down", BF16, H * Is, optional=True),
             _ptr(out, "out", F32, T * H),
@@ -234,12 +267,14 @@ class MoELayer:
     """Convenience holder: weights + one workspace; ``__call__`` runs
     moe_forward and returns (out, topk_ids, topk_w, counts)."""
 
-    def __init__(self, layer, light_max_rows: int = -1, heavy_tile_rows: int = 0):
+    def __init__(self, layer, light_max_rows: int = -1, heavy_tile_rows: int = 0,
+                 packed: bool = False):
         c = layer.cfg
         self.layer = layer
         self.shape = make_shape(c.T, c.H, c.E, c.k, c.I, c.I_shared, c.renorm, light_max_rows,
                                 heavy_tile_rows)
         self.workspace = alloc_workspace(self.shape, layer.x.device)
+        self.packed = pack_weights(self.shape, layer.w_gu, layer.w_dn) if packed else None
 
     def __call__(self, x=None, out=None, want_routing=True):
         L, s = self.layer, self.shape
@@ -250,5 +285,5 @@ class MoELayer:
         w = torch.empty((s.T, s.k), dtype=F32, device=dev) if want_routing else None
         counts = torch.empty((s.E,), dtype=I32, device=dev) if want_routing else None
         forward(s, x, L.wg, L.bias, L.w_gu, L.w_dn, L.ws_gu, L.ws_dn, out, self.workspace,
-                ids, w, counts)
+                ids, w, counts, packed_weights=self.packed)
         return out, ids, w, counts

@@ -89,6 +89,12 @@ typedef struct moe_shape {
  * returns 0 for an invalid shape). */
 size_t moe_workspace_bytes(const moe_shape* shape);
 
+/* Bytes of the packed expert-weight buffer for `shape` (host-only, pure;
+ * 0 for an invalid shape): ceil(I/128)*(H/64) + ceil(H/256)*ceil(I/64)
+ * images of 32 KB per expert, i.e. the size of W_gate|up plus W_down when
+ * I % 128 == 0 and H % 256 == 0. */
+size_t moe_packed_weight_bytes(const moe_shape* shape);
+
 /* Static text for a status code. */
 const char* moe_status_string(int status);
 
@@ -125,6 +131,23 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t* counts
                 int32_t* offsets, int32_t* sorted_token_ids, int32_t* inv_pos,
                 void* workspace, size_t ws_bytes, void* stream);
 
+/* Optional one-time re-layout of the routed expert weights for the heavy
+ * GEMM tiles (the expert weights are constant across calls, as a serving
+ * engine loads them once).  For each expert and 256-row output block, every
+ * 64-wide K stage of the weight operand becomes one contiguous 32 KB image
+ * in the order the heavy kernels stage it in LDS, so prefill-sized calls
+ * stream weights as long contiguous runs (on MI355X, reads of 128-byte
+ * pieces of 8 KB-strided rows reach ~4.8 TB/s, contiguous reads ~6.1 TB/s).
+ * Rows past I (or H) and K past the end are stored as zeros.
+ *   w_gate_up, w_down  bf16, layouts as for moe_grouped_ffn (read)
+ *   packed             device buffer of moe_packed_weight_bytes(shape)
+ *                      bytes, 256-byte aligned (written; caller-owned)
+ * Enqueued on `stream`; the packed buffer may be passed to moe_grouped_ffn
+ * and moe_forward once that work has completed.  Results are bitwise
+ * identical with and without it. */
+int moe_pack_weights(const moe_shape* shape, const uint16_t* w_gate_up, const uint16_t* w_down,
+                     void* packed, void* stream);
+
 /* Grouped expert FFN over the expert-major rows (pwwt.cn section 4.2):
  *   h[r,:] = bf16( silu(x[tok_r] . W_gate[e]) * (x[tok_r] . W_up[e]) )
  *   y[r,:] = h[r,:] . W_down[e]   (fp32)          for rows r of expert e,
@@ -135,14 +158,18 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t* counts
  *   sorted_token_ids int32 [T*k], offsets int32 [E+1]  (from moe_permute)
  *   w_gate_up        bf16 [E,2I,H]: rows 0..I-1 = W_gate^T, I..2I-1 = W_up^T
  *   w_down           bf16 [E,H,I]:  W_down^T
+ *   packed_weights   the same weights from moe_pack_weights, or NULL; when
+ *                    given, the heavy tiles read it instead (the light loop
+ *                    always reads w_gate_up / w_down)
  *   h                bf16 [T*k,I] out, or NULL (then kept in the workspace)
  *   y                fp32 [T*k,H] out (fp32 so that large |y| entering the
  *                    weighted sum are not rounded to 8 significant bits)
  */
 int moe_grouped_ffn(const moe_shape* shape, const uint16_t* x,
                     const int32_t* sorted_token_ids, const int32_t* offsets,
-                    const uint16_t* w_gate_up, const uint16_t* w_down, uint16_t* h,
-                    float* y, void* workspace, size_t ws_bytes, void* stream);
+                    const uint16_t* w_gate_up, const uint16_t* w_down,
+                    const void* packed_weights, uint16_t* h, float* y, void* workspace,
+                    size_t ws_bytes, void* stream);
 
 /* Shared expert (lumevalley.com Ling-2.6-1T article): one dense SwiGLU FFN
  * over all T tokens through the same heavy GEMM kernels, written in fp32:
@@ -168,12 +195,14 @@ int moe_combine(const moe_shape* shape, const float* y, const int32_t* inv_pos,
 /* The whole layer: router, permute, grouped FFN, shared expert (when
  * shape->I_shared > 0), combine.  out fp32 [T,H]:
  *   out[t] = sum_j w[t,j] FFN_{ids[t,j]}(x[t])  (+ FFN_shared(x[t]))
- * ws_gate_up / ws_down are required iff I_shared > 0.  topk_ids_out [T,k],
+ * ws_gate_up / ws_down are required iff I_shared > 0; packed_weights is
+ * optional, as for moe_grouped_ffn.  topk_ids_out [T,k],
  * topk_w_out [T,k] and counts_out [E] are optional copies of the routing
  * (NULL = not written). */
 int moe_forward(const moe_shape* shape, const uint16_t* x, const float* w_router,
                 const float* bias, const uint16_t* w_gate_up, const uint16_t* w_down,
-                const uint16_t* ws_gate_up, const uint16_t* ws_down, float* out,
+                const void* packed_weights, const uint16_t* ws_gate_up, const uint16_t* ws_down,
+                float* out,
                 int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out,
                 void* workspace, size_t ws_bytes, void* stream);
 

@@ -92,13 +92,14 @@ def test_argument_errors(L):
     assert L.moe_router(ctypes.byref(s), P, P, None, P, P, None, ctypes.c_void_p(0x10010), need,
                         None) == moe.MOE_ERR_ALIGN
     assert L.moe_router(None, P, P, None, P, P, None, P, need, None) == moe.MOE_ERR_NULL
-    assert L.moe_grouped_ffn(ctypes.byref(s), P, P, P, P, P, None, None, P, need, None) == moe.MOE_ERR_NULL
+    assert L.moe_grouped_ffn(ctypes.byref(s), P, P, P, P, P, None, None, None, P, need,
+                             None) == moe.MOE_ERR_NULL
     assert L.moe_combine(ctypes.byref(s), P, P, None, 0, P, None) == moe.MOE_ERR_NULL
     assert L.moe_shared_ffn(ctypes.byref(s), P, P, P, P, P, need, None) == moe.MOE_ERR_SHAPE
     s2 = shp(I_shared=1024)
     need2 = moe.workspace_bytes(s2)
     # shared expert requested but its down weights missing
-    assert L.moe_forward(ctypes.byref(s2), P, P, None, P, P, P, None, P, None, None, None, P, need2,
+    assert L.moe_forward(ctypes.byref(s2), P, P, None, P, P, None, P, None, P, None, None, None, P, need2,
                          None) == moe.MOE_ERR_NULL
     assert "ws_down" in moe.last_error()
 
@@ -109,10 +110,35 @@ def test_empty_batch_is_noop(L):
     need = moe.workspace_bytes(s)
     P = ctypes.c_void_p(0x10000)
     assert L.moe_router(ctypes.byref(s), P, P, None, P, P, None, P, need, None) == moe.MOE_OK
-    assert L.moe_grouped_ffn(ctypes.byref(s), P, P, P, P, P, None, P, P, need, None) == moe.MOE_OK
+    assert L.moe_grouped_ffn(ctypes.byref(s), P, P, P, P, P, None, None, P, P, need, None) == moe.MOE_OK
     assert L.moe_combine(ctypes.byref(s), P, P, P, 0, P, None) == moe.MOE_OK
 
 
 def test_status_strings(L):
     for code in range(7):
         assert moe.status_string(code)
+
+
+def test_packed_weight_bytes(L):
+    """One 32 KB image per (expert, 256-row output block, 64-wide K stage)
+    of each GEMM's weight operand; equal to the weights' own size when the
+    blocks divide evenly, padded with zero rows otherwise."""
+    s = shp()
+    assert moe.packed_weight_bytes(s) == 512 * 3 * 1024 * 4096 * 2
+    s = shp(E=3, k=2, H=320, I=96)
+    gu = 3 * 1 * (320 // 64) * 32768          # ceil(96/128) = 1 block, 5 stages
+    dn = 3 * 2 * 2 * 32768                    # ceil(320/256) = 2 blocks, ceil(96/64) = 2 stages
+    assert moe.packed_weight_bytes(s) == gu + dn
+    assert moe.packed_weight_bytes(shp(H=100)) == 0
+
+
+def test_pack_weights_argument_errors(L):
+    s = shp()
+    P = ctypes.c_void_p(0x10000)
+    assert L.moe_pack_weights(ctypes.byref(s), P, P, None, None) == moe.MOE_ERR_NULL
+    assert L.moe_pack_weights(ctypes.byref(s), None, P, P, None) == moe.MOE_ERR_NULL
+    assert L.moe_pack_weights(ctypes.byref(s), P, P, ctypes.c_void_p(0x10010), None) == moe.MOE_ERR_ALIGN
+    need = moe.workspace_bytes(s)
+    # a misaligned packed buffer is refused before anything is enqueued
+    assert L.moe_grouped_ffn(ctypes.byref(s), P, P, P, P, P, ctypes.c_void_p(0x10010), None, P, P,
+                             need, None) == moe.MOE_ERR_ALIGN

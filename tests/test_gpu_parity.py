@@ -352,3 +352,63 @@ def test_empty_batch():
     moe.forward(s, x, lay.wg, None, lay.w_gu, lay.w_dn, None, None, out, ws, counts_out=counts)
     torch.cuda.synchronize()
     assert cfg.T == 0 and np.all(counts.cpu().numpy() == 0)
+
+
+# ------------------------------------------------------------ packed weights
+@pytest.mark.parametrize("cfg,tm", [(TILES, 0), (TILES, 128), (TILES, 192), (TILES, 256),
+                                    (SMALL["mixed"], 0), (SMALL["heavy_ragged"], 0)],
+                         ids=lambda v: getattr(v, "name", str(v)))
+def test_packed_weights_bitwise(cfg, tm):
+    """The heavy tiles reading the packed weight copy give the same output
+    bits as reading the plain layout (same data, same MFMA chains), at every
+    tile height, with ragged N blocks (I % 128 != 0) and a half-full last
+    K stage (I % 64 == 32)."""
+    print(f"[case] packed {cfg.name} tm={tm}", flush=True)
+    lay = layer_on_gpu(cfg)
+    outs = []
+    for packed in (False, True):
+        m = moe.MoELayer(lay, light_max_rows=0, heavy_tile_rows=tm, packed=packed)
+        out, ids, w, counts = m()
+        torch.cuda.synchronize()
+        outs.append(out.view(torch.int32).cpu().numpy())
+    assert np.array_equal(outs[0], outs[1]), "packed weights change the output"
+
+
+def test_packed_weights_layout():
+    """Spot-check the packed image against its definition: slot p of block b
+    of stage st holds B row 8b + p//8, K chunk (p%8) ^ (p//8)."""
+    cfg = custom("pk", T=8, H=192, E=2, k=1, I=160)
+    lay = layer_on_gpu(cfg)
+    s = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I)
+    pk = moe.pack_weights(s, lay.w_gu, lay.w_dn)
+    torch.cuda.synchronize()
+    words = pk.view(torch.int16).cpu().numpy()
+    wgu = lay.w_gu.view(torch.int16).cpu().numpy()
+    wdn = lay.w_dn.view(torch.int16).cpu().numpy()
+    H, I, E = cfg.H, cfg.I, cfg.E
+    nbg, nstg = -(-I // 128), H // 64
+    nbd, nstd = -(-H // 256), -(-I // 64)
+    rng = np.random.default_rng(3)
+
+    def expect(gate_up, e, nb, st, b, p):
+        r = 8 * b + p // 8
+        c = (p % 8) ^ (p // 8)
+        k = st * 64 + 8 * c
+        if gate_up:
+            hc = nb * 128 + (r >> 5) * 16 + (r & 15)
+            row = I + hc if (r & 16) else hc
+            ok, src, K = hc < I and k < H, wgu[e], H
+        else:
+            row = nb * 256 + r
+            ok, src, K = row < H and k < I, wdn[e], I
+        return src[row, k:k + 8] if ok else np.zeros(8, np.int16)
+
+    base_dn = E * nbg * nstg * 2048 * 8
+    for _ in range(400):
+        gate_up = bool(rng.integers(2))
+        nb_n, st_n = (nbg, nstg) if gate_up else (nbd, nstd)
+        e, nb, st = rng.integers(E), rng.integers(nb_n), rng.integers(st_n)
+        b, p = rng.integers(32), rng.integers(64)
+        q = ((e * nb_n + nb) * st_n + st) * 2048 + b * 64 + p
+        off = (0 if gate_up else base_dn) + q * 8
+        assert np.array_equal(words[off:off + 8], expect(gate_up, e, nb, st, b, p)), (gate_up, e, nb, st, b, p)
