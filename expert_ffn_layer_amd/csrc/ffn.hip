@@ -159,13 +159,25 @@ constexpr int kLightWideU = 2;                      // K steps in flight, wide b
 // One wave: MT row sub-tiles x NTILE column tiles of one expert, K = H.
 // Tile t pairs gate rows i0+8t.. and the matching up rows, so lanes
 // l16 < 8 end with g and lanes l16 >= 8 with u of the same h column.
-template <int MT, int U, int NTILE, bool NTL>
+template <int MT, int U, int NTILE, bool NTL, bool PK>
 __device__ __forceinline__ void gateup_light_rows(const FfnArgs& a, int e, int r0, int n, int i0,
                                                   int l16, int g) {
     const int nk = a.H / 32;
-    const int wrow = (l16 < 8) ? (i0 + l16) : (a.I + i0 + l16 - 8);
-    const uint16_t* Bp = a.w_gu + ((size_t)e * 2 * a.I + wrow) * a.H + 8 * g;
-    const size_t bstride = (size_t)8 * a.H;  // next column tile: 8 rows further
+    const uint16_t* Bp;
+    size_t bstride, kstride;
+    if constexpr (PK) {
+        // packed: the tile's 16 rows x 32 K of each K step are one 1 KB chunk
+        // in lane order, and a column tile's chunks are consecutive
+        const int lane = g * 16 + l16;
+        Bp = a.pk_gu + ((size_t)e * packed_gu_groups(a.I) + i0 / 8) * nk * 512 + lane * 8;
+        bstride = (size_t)nk * 512;
+        kstride = 512;
+    } else {
+        const int wrow = (l16 < 8) ? (i0 + l16) : (a.I + i0 + l16 - 8);
+        Bp = a.w_gu + ((size_t)e * 2 * a.I + wrow) * a.H + 8 * g;
+        bstride = (size_t)8 * a.H;  // next column tile: 8 rows further
+        kstride = 32;
+    }
     const uint16_t* Ap[MT];
     bool has_a[MT];
 #pragma unroll
@@ -190,7 +202,7 @@ __device__ __forceinline__ void gateup_light_rows(const FfnArgs& a, int e, int r
         for (int t = 0; t < NTILE; ++t) bb[t] = zero_bf16x8();
         if (kb < nk) {
 #pragma unroll
-            for (int t = 0; t < NTILE; ++t) bb[t] = load_weights<NTL>(Bp + t * bstride + kb * 32);
+            for (int t = 0; t < NTILE; ++t) bb[t] = load_weights<NTL>(Bp + t * bstride + kb * kstride);
 #pragma unroll
             for (int m = 0; m < MT; ++m)
                 if (has_a[m]) aa[m] = load_bf16x8(Ap[m] + kb * 32);
@@ -238,7 +250,7 @@ __device__ __forceinline__ void gateup_light_rows(const FfnArgs& a, int e, int r
 }
 
 // Work item = (light expert, 4 waves x NTILE x 8 h-columns).
-template <int U, int NTILE, bool NTL>
+template <int U, int NTILE, bool NTL, bool PK>
 __global__ __launch_bounds__(kThreads) void gateup_light_kernel(FfnArgs a) {
     static_assert(32 % (NTILE * 8) == 0, "a wave's columns must divide I's multiple of 32");
     constexpr int kCols = 4 * NTILE * 8;
@@ -255,20 +267,31 @@ __global__ __launch_bounds__(kThreads) void gateup_light_kernel(FfnArgs a) {
         const int r0 = a.offsets[e];
         const int n = a.offsets[e + 1] - r0;
         if (n <= 16)
-            gateup_light_rows<1, U, NTILE, NTL>(a, e, r0, n, i0, l16, g);
+            gateup_light_rows<1, U, NTILE, NTL, PK>(a, e, r0, n, i0, l16, g);
         else
-            gateup_light_rows<kLightSubTiles, kLightWideU, NTILE, NTL>(a, e, r0, n, i0, l16, g);
+            gateup_light_rows<kLightSubTiles, kLightWideU, NTILE, NTL, PK>(a, e, r0, n, i0, l16, g);
     }
 }
 
 // --------------------------------------------------------- light: down
 // One wave: MT row sub-tiles x NT column tiles (16 output columns each), K = I.
-template <int MT, int U, int NT, bool NTL>
+template <int MT, int U, int NT, bool NTL, bool PK>
 __device__ __forceinline__ void down_light_rows(const FfnArgs& a, int e, int r0, int n, int c0,
                                                 int l16, int g) {
     const int nk = a.I / 32;
-    const uint16_t* Bp = a.w_dn + ((size_t)e * a.H + c0 + l16) * a.I + 8 * g;
-    const size_t bstride = (size_t)16 * a.I;
+    const uint16_t* Bp;
+    size_t bstride, kstride;
+    if constexpr (PK) {
+        const int lane = g * 16 + l16;
+        const int ks = packed_dn_ksteps(a.I);
+        Bp = a.pk_dn + ((size_t)e * packed_dn_groups(a.H) + c0 / 16) * ks * 512 + lane * 8;
+        bstride = (size_t)ks * 512;
+        kstride = 512;
+    } else {
+        Bp = a.w_dn + ((size_t)e * a.H + c0 + l16) * a.I + 8 * g;
+        bstride = (size_t)16 * a.I;
+        kstride = 32;
+    }
     const uint16_t* Ap[MT];
     bool has_a[MT];
 #pragma unroll
@@ -295,7 +318,7 @@ __device__ __forceinline__ void down_light_rows(const FfnArgs& a, int e, int r0,
             for (int m = 0; m < MT; ++m)
                 if (has_a[m]) aa[m] = load_bf16x8(Ap[m] + kb * 32);
 #pragma unroll
-            for (int t = 0; t < NT; ++t) bb[t] = load_weights<NTL>(Bp + t * bstride + kb * 32);
+            for (int t = 0; t < NT; ++t) bb[t] = load_weights<NTL>(Bp + t * bstride + kb * kstride);
         }
     };
 #pragma unroll
@@ -338,7 +361,7 @@ __device__ __forceinline__ void down_light_rows(const FfnArgs& a, int e, int r0,
 }
 
 // Work item = (light expert, 4 waves x NT x 16 output columns).
-template <int NT, int U, bool NTL>
+template <int NT, int U, bool NTL, bool PK>
 __global__ __launch_bounds__(kThreads) void down_light_kernel(FfnArgs a) {
     static_assert(64 % (NT * 16) == 0, "a wave's columns must divide H's multiple of 64");
     constexpr int kCols = 4 * NT * 16;
@@ -355,9 +378,9 @@ __global__ __launch_bounds__(kThreads) void down_light_kernel(FfnArgs a) {
         const int r0 = a.offsets[e];
         const int n = a.offsets[e + 1] - r0;
         if (n <= 16)
-            down_light_rows<1, U, NT, NTL>(a, e, r0, n, c0, l16, g);
+            down_light_rows<1, U, NT, NTL, PK>(a, e, r0, n, c0, l16, g);
         else
-            down_light_rows<kLightSubTiles, kLightWideU, NT, NTL>(a, e, r0, n, c0, l16, g);
+            down_light_rows<kLightSubTiles, kLightWideU, NT, NTL, PK>(a, e, r0, n, c0, l16, g);
     }
 }
 
@@ -481,9 +504,6 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
     const int l16 = lane & 15, g = lane >> 4;
     const int nh = K / 32;         // 32-wide MFMA K steps (K % 32 == 0)
     const int nst = (nh + 1) / 2;  // 64-wide stages; the last one is half full if nh is odd
-    // Packed weights (routed experts only; a split_h group reads W_down twice
-    // and uses the plain layout).
-    const char* pk = a.split_h ? nullptr : (M == Mode::GateUp ? a.pk_gu : a.pk_dn);
     // DMA side: lane L fills slot L of a block: row L/8, chunk (L%8)^(L/8).
     const int drow = lane >> 3;
     const int dchunk = (lane & 7) ^ drow;
@@ -532,16 +552,14 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
         // source is a buffer resource (SGPRs) plus a 32-bit per-lane byte
         // offset that holds the lane's row and K chunk; the stage's K offset
         // is added once per stage.
-        if (M == Mode::GateUp) {
+        if (M == Mode::GateUp)
             ar = make_rsrc(a.x, (uint32_t)((size_t)a.T * a.H * 2));
-            br = pk ? make_rsrc(pk + ((size_t)e * nblk + nb) * nst * kPackStage,
-                                (uint32_t)(nst * kPackStage))
-                    : make_rsrc(a.w_gu + (size_t)e * 2 * a.I * a.H, (uint32_t)((size_t)2 * a.I * a.H * 2));
-        } else {
+        else
             ar = make_rsrc(a.h + (size_t)(r0 + m0) * hstride, (uint32_t)((size_t)TM * hstride * 2));
-            br = pk ? make_rsrc(pk + ((size_t)e * nblk + nb) * nst * kPackStage,
-                                (uint32_t)(nst * kPackStage))
-                    : make_rsrc(a.w_dn + (size_t)e * a.H * a.I, (uint32_t)((size_t)a.H * a.I * 2));
+        if (M == Mode::GateUp) {
+            br = make_rsrc(a.w_gu + (size_t)e * 2 * a.I * a.H, (uint32_t)((size_t)2 * a.I * a.H * 2));
+        } else {
+            br = make_rsrc(a.w_dn + (size_t)e * a.H * a.I, (uint32_t)((size_t)a.H * a.I * 2));
         }
 #pragma unroll
         for (int i = 0; i < kABlk; ++i) {
@@ -561,10 +579,7 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
             const int b = kBBlkPerWave * wave + i;
             const int r = b * 8 + drow;  // B row within the tile
             const uint32_t cb = (uint32_t)dchunk * 16u;
-            if (pk) {
-                // packed: the stage image is the LDS image, block b at b KB
-                boff[i] = (uint32_t)b * kBlk + (uint32_t)lane * 16u;
-            } else if (M == Mode::GateUp) {
+            if (M == Mode::GateUp) {
                 // 16-row blocks alternate: block 2p = gate rows, 2p+1 = the
                 // matching up rows, so g and u of an element share a lane.
                 const int hc = nb * (kTN / 2) + (r >> 5) * 16 + (r & 15);
@@ -611,7 +626,7 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
         adjust(kk, adj_a, adj_b);
         // packed weights: stage st's image at st * 32 KB (the half-full last
         // stage and the zero rows past I or H are stored as zeros)
-        const uint32_t sb = pk ? (uint32_t)(st * kPackStage) : (uint32_t)kb * 2u - adj_b;
+        const uint32_t sb = (uint32_t)kb * 2u - adj_b;
 #pragma unroll
         for (int i = 0; i < kBBlkPerWave; ++i)
             lds_dma16_buf(br, boff[i] + sb, 0u, buf + (kBBlkPerWave * wave + i) * kBlk);
@@ -788,38 +803,33 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
     }
 }
 
-// Packs one weight tensor into heavy-tile load order: slot q (16 bytes) of
-// the output is, for q = ((e * nblk + nb) * nst + st) * 2048 + b * 64 + p,
-// B row r = 8b + p/8 of output block nb, K chunk c = (p % 8) ^ (p / 8),
-// i.e. K values st*64 + 8c .. +7 (the same map as the heavy kernels'
-// direct-to-LDS loads).  gate|up: B rows alternate 16 gate / 16
-// up rows of h columns nb*128 ..; down: B row r is W_down row nb*256 + r.
-// Rows past I (or H) and K past the end are zeros.
+// Packs one weight tensor into 1 KB lane-order chunks: output slot q (16
+// bytes) is lane L = q % 64 of chunk q / 64 = (e * groups + grp) * ksteps +
+// kb, i.e. K values 32kb + 8(L/16) .. +7 of weight row
+//   gate|up: h column c = 8grp + L%8, gate row c (L%16 < 8) or up row I + c;
+//   down:    row 16grp + L%16.
 __global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __restrict__ w, int E,
-                                                           int rows, int K, int nblk, int nst,
+                                                           int rows, int K, int groups, int ksteps,
                                                            int gate_up, int I,
                                                            uint16_t* __restrict__ out) {
-    const long long total = (long long)E * nblk * nst * (kPackStage / 16);
+    const long long total = (long long)E * groups * ksteps * 64;
     for (long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x; q < total;
          q += (long long)gridDim.x * blockDim.x) {
-        const int slot = (int)(q & 2047);
-        long long t = q >> 11;
-        const int st = (int)(t % nst);
-        t /= nst;
-        const int nb = (int)(t % nblk);
-        const int e = (int)(t / nblk);
-        const int b = slot >> 6, p = slot & 63;
-        const int r = 8 * b + (p >> 3);
-        const int c = (p & 7) ^ (p >> 3);
-        const int k = st * 64 + 8 * c;
+        const int L = (int)(q & 63);
+        long long t = q >> 6;
+        const int kb = (int)(t % ksteps);
+        t /= ksteps;
+        const int grp = (int)(t % groups);
+        const int e = (int)(t / groups);
+        const int l16 = L & 15, k = kb * 32 + 8 * (L >> 4);
         int row;
         bool ok;
         if (gate_up) {
-            const int hc = nb * 128 + (r >> 5) * 16 + (r & 15);
-            ok = hc < I;
-            row = (r & 16) ? I + hc : hc;
+            const int c = grp * 8 + (l16 & 7);
+            ok = c < I;
+            row = l16 < 8 ? c : I + c;
         } else {
-            row = nb * 256 + r;
+            row = grp * 16 + l16;
             ok = row < rows;
         }
         ok = ok && k < K;
@@ -862,26 +872,24 @@ hipError_t launch_heavy(const FfnArgs& a, int ncols, hipStream_t st) {
 }  // namespace
 
 size_t packed_gu_bytes(int E, int H, int I) {
-    return (size_t)E * ((I + 127) / 128) * (H / 64) * kPackStage;
+    return (size_t)E * packed_gu_groups(I) * (H / 32) * 1024;
 }
 
 size_t packed_dn_bytes(int E, int H, int I) {
-    return (size_t)E * ((H + 255) / 256) * ((I + 63) / 64) * kPackStage;
+    return (size_t)E * packed_dn_groups(H) * packed_dn_ksteps(I) * 1024;
 }
 
 hipError_t launch_pack_weights(const uint16_t* w_gu, const uint16_t* w_dn, int E, int H, int I,
                                char* packed, hipStream_t st) {
-    const int nbg = (I + 127) / 128, nstg = H / 64;
-    const int nbd = (H + 255) / 256, nstd = (I + 63) / 64;
-    const long long sg = (long long)E * nbg * nstg * (kPackStage / 16);
-    const long long sd = (long long)E * nbd * nstd * (kPackStage / 16);
+    const int gg = packed_gu_groups(I), kg = H / 32;
+    const int gd = packed_dn_groups(H), kd = packed_dn_ksteps(I);
+    const long long sg = (long long)E * gg * kg * 64, sd = (long long)E * gd * kd * 64;
     pack_weights_kernel<<<(int)std::min<long long>((sg + 255) / 256, 65536), 256, 0, st>>>(
-        w_gu, E, 2 * I, H, nbg, nstg, 1, I, reinterpret_cast<uint16_t*>(packed));
+        w_gu, E, 2 * I, H, gg, kg, 1, I, reinterpret_cast<uint16_t*>(packed));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     pack_weights_kernel<<<(int)std::min<long long>((sd + 255) / 256, 65536), 256, 0, st>>>(
-        w_dn, E, H, I, nbd, nstd, 0, I,
-        reinterpret_cast<uint16_t*>(packed + packed_gu_bytes(E, H, I)));
+        w_dn, E, H, I, gd, kd, 0, I, reinterpret_cast<uint16_t*>(packed + packed_gu_bytes(E, H, I)));
     return hipGetLastError();
 }
 
@@ -898,8 +906,13 @@ hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t st) {
         constexpr int kCols = 4 * MOE_LIGHT_GU_TILES * 8;
         const long long work = (long long)a.max_light * ((a.I + kCols - 1) / kCols);
         prof_begin(K_GATEUP_LIGHT, st);
-        gateup_light_kernel<MOE_LIGHT_GU_U, MOE_LIGHT_GU_TILES, MOE_LIGHT_NT_LOADS != 0>
-            <<<grid_for(work, MOE_LIGHT_GU_BPC, a.num_cu), kThreads, 0, st>>>(a);
+        const int grid = grid_for(work, MOE_LIGHT_GU_BPC, a.num_cu);
+        if (a.pk_gu)
+            gateup_light_kernel<MOE_LIGHT_GU_U, MOE_LIGHT_GU_TILES, MOE_LIGHT_NT_LOADS != 0, true>
+                <<<grid, kThreads, 0, st>>>(a);
+        else
+            gateup_light_kernel<MOE_LIGHT_GU_U, MOE_LIGHT_GU_TILES, MOE_LIGHT_NT_LOADS != 0, false>
+                <<<grid, kThreads, 0, st>>>(a);
         prof_end(K_GATEUP_LIGHT, st);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
@@ -918,8 +931,13 @@ hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st) {
         constexpr int kCols = 4 * MOE_LIGHT_DN_TILES * 16;
         const long long work = (long long)a.max_light * ((a.H + kCols - 1) / kCols);
         prof_begin(K_DOWN_LIGHT, st);
-        down_light_kernel<MOE_LIGHT_DN_TILES, MOE_LIGHT_DN_U, MOE_LIGHT_NT_LOADS != 0>
-            <<<grid_for(work, MOE_LIGHT_DN_BPC, a.num_cu), kThreads, 0, st>>>(a);
+        const int grid = grid_for(work, MOE_LIGHT_DN_BPC, a.num_cu);
+        if (a.pk_dn)
+            down_light_kernel<MOE_LIGHT_DN_TILES, MOE_LIGHT_DN_U, MOE_LIGHT_NT_LOADS != 0, true>
+                <<<grid, kThreads, 0, st>>>(a);
+        else
+            down_light_kernel<MOE_LIGHT_DN_TILES, MOE_LIGHT_DN_U, MOE_LIGHT_NT_LOADS != 0, false>
+                <<<grid, kThreads, 0, st>>>(a);
         prof_end(K_DOWN_LIGHT, st);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;

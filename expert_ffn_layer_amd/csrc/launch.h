@@ -103,17 +103,26 @@ struct FfnArgs {
     int split_h;                 // 1: h rows hold [hi | lo] bf16 halves (2I wide) and the
                                  //    down GEMM runs over both against the same weights
     int max_tiles;               // grid bound for heavy tiles
-    const char* pk_gu;           // packed W_gate|up (heavy-tile load order) or nullptr
-    const char* pk_dn;           // packed W_down or nullptr (not with split_h)
+    const uint16_t* pk_gu;       // packed W_gate|up for the light loop, or nullptr
+    const uint16_t* pk_dn;       // packed W_down for the light loop, or nullptr
     int max_light;               // grid bound for light experts
     int num_cu;
 };
 
-// Packed expert weights: for each expert and 256-row output block, every
-// 64-wide K stage of the heavy tiles' weight operand as one contiguous 32 KB
-// image in the LDS order the heavy kernels use, so the weights stream as
-// long contiguous runs.  gate|up first, then down.
-constexpr size_t kPackStage = 32768;
+// Packed expert weights: 1 KB chunks, each the 16 weight rows x 32 K of one
+// MFMA B operand in lane order (lane l: row l % 16, K values 8(l/16)..+7).
+//  gate|up: chunk (e, g, kb) holds gate rows 8g..8g+7 then the matching up
+//    rows (h columns 8g..8g+7), K step kb; I/8 groups, H/32 K steps.
+//  down: chunk (e, g, kb) holds W_down rows 16g..16g+15, K step kb; H/16
+//    groups, I/32 K steps.
+// The packed copy is exactly as large as the weights.
+// Chunks are ordered (e, g, kb): a light wave streams one group's chunks
+// contiguously.  gate|up first, then down.  Only the light loop reads them:
+// the heavy tiles stream the row-major weights faster (measured: a 64-wide
+// K stage of 16 groups is 16 runs of 2 KB at a power-of-two stride).
+inline __host__ __device__ int packed_gu_groups(int I) { return I / 8; }
+inline __host__ __device__ int packed_dn_groups(int H) { return H / 16; }
+inline __host__ __device__ int packed_dn_ksteps(int I) { return I / 32; }
 size_t packed_gu_bytes(int E, int H, int I);
 size_t packed_dn_bytes(int E, int H, int I);
 hipError_t launch_pack_weights(const uint16_t* w_gu, const uint16_t* w_dn, int E, int H, int I,

@@ -208,8 +208,9 @@ int run_ffn(const moe_shape* s, const Layout& L, const uint16_t* x, const int32_
     a.max_light = L.max_light;
     a.num_cu = ncu;
     if (packed) {
-        a.pk_gu = static_cast<const char*>(packed);
-        a.pk_dn = a.pk_gu + moe::packed_gu_bytes(s->E, s->H, s->I);
+        const char* p = static_cast<const char*>(packed);
+        a.pk_gu = reinterpret_cast<const uint16_t*>(p);
+        a.pk_dn = reinterpret_cast<const uint16_t*>(p + moe::packed_gu_bytes(s->E, s->H, s->I));
     }
     HIP_TRY(moe::launch_ffn_gateup(a, st), "ffn gate|up");
     HIP_TRY(moe::launch_ffn_down(a, st), "ffn down");

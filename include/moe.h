@@ -90,9 +90,8 @@ typedef struct moe_shape {
 size_t moe_workspace_bytes(const moe_shape* shape);
 
 /* Bytes of the packed expert-weight buffer for `shape` (host-only, pure;
- * 0 for an invalid shape): ceil(I/128)*(H/64) + ceil(H/256)*ceil(I/64)
- * images of 32 KB per expert, i.e. the size of W_gate|up plus W_down when
- * I % 128 == 0 and H % 256 == 0. */
+ * 0 for an invalid shape): the size of W_gate|up plus W_down,
+ * E * 3 * I * H * 2. */
 size_t moe_packed_weight_bytes(const moe_shape* shape);
 
 /* Static text for a status code. */
@@ -131,14 +130,21 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t* counts
                 int32_t* offsets, int32_t* sorted_token_ids, int32_t* inv_pos,
                 void* workspace, size_t ws_bytes, void* stream);
 
-/* Optional one-time re-layout of the routed expert weights for the heavy
- * GEMM tiles (the expert weights are constant across calls, as a serving
- * engine loads them once).  For each expert and 256-row output block, every
- * 64-wide K stage of the weight operand becomes one contiguous 32 KB image
- * in the order the heavy kernels stage it in LDS, so prefill-sized calls
- * stream weights as long contiguous runs (on MI355X, reads of 128-byte
- * pieces of 8 KB-strided rows reach ~4.8 TB/s, contiguous reads ~6.1 TB/s).
- * Rows past I (or H) and K past the end are stored as zeros.
+/* Optional one-time re-layout of the routed expert weights (the expert
+ * weights are constant across calls, as a serving engine loads them once).
+ * The weights become 1 KB chunks, each the 16 weight rows x 32 K values of
+ * one bf16 MFMA operand in lane order (lane l: row l%16, K 8(l/16)..+7):
+ *   gate|up chunk (e, g, kb): gate rows 8g..8g+7 then up rows I+8g..+7,
+ *     K 32kb..32kb+31; I/8 groups g per expert, H/32 steps kb;
+ *   down chunk (e, g, kb): W_down rows 16g..16g+15, K 32kb..; H/16 groups,
+ *     I/32 steps;
+ * ordered (e, g, kb).  The
+ * light loop (experts with few rows: every expert of a decode step) then
+ * streams each group's weights as one contiguous run: on MI355X the gate|up
+ * weights of a decode step stream at ~6.1 TB/s instead of ~5.7 TB/s from the
+ * row-major layout, whose 16-row tiles read 64 bytes from rows 8 KB apart.
+ * The heavy tiles keep reading w_gate_up / w_down (row-major is faster for
+ * them), so the packed buffer is a second copy of the routed weights.
  *   w_gate_up, w_down  bf16, layouts as for moe_grouped_ffn (read)
  *   packed             device buffer of moe_packed_weight_bytes(shape)
  *                      bytes, 256-byte aligned (written; caller-owned)
@@ -159,8 +165,8 @@ int moe_pack_weights(const moe_shape* shape, const uint16_t* w_gate_up, const ui
  *   w_gate_up        bf16 [E,2I,H]: rows 0..I-1 = W_gate^T, I..2I-1 = W_up^T
  *   w_down           bf16 [E,H,I]:  W_down^T
  *   packed_weights   the same weights from moe_pack_weights, or NULL; when
- *                    given, the heavy tiles read it instead (the light loop
- *                    always reads w_gate_up / w_down)
+ *                    given, the light loop reads it instead of w_gate_up /
+ *                    w_down (the heavy tiles always read those)
  *   h                bf16 [T*k,I] out, or NULL (then kept in the workspace)
  *   y                fp32 [T*k,H] out (fp32 so that large |y| entering the
  *                    weighted sum are not rounded to 8 significant bits)

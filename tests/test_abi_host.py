@@ -120,15 +120,11 @@ def test_status_strings(L):
 
 
 def test_packed_weight_bytes(L):
-    """One 32 KB image per (expert, 256-row output block, 64-wide K stage)
-    of each GEMM's weight operand; equal to the weights' own size when the
-    blocks divide evenly, padded with zero rows otherwise."""
+    """1 KB chunks of 16 rows x 32 K: exactly the weights' own size."""
     s = shp()
     assert moe.packed_weight_bytes(s) == 512 * 3 * 1024 * 4096 * 2
     s = shp(E=3, k=2, H=320, I=96)
-    gu = 3 * 1 * (320 // 64) * 32768          # ceil(96/128) = 1 block, 5 stages
-    dn = 3 * 2 * 2 * 32768                    # ceil(320/256) = 2 blocks, ceil(96/64) = 2 stages
-    assert moe.packed_weight_bytes(s) == gu + dn
+    assert moe.packed_weight_bytes(s) == 3 * 3 * 96 * 320 * 2
     assert moe.packed_weight_bytes(shp(H=100)) == 0
 
 

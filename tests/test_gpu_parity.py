@@ -355,19 +355,21 @@ def test_empty_batch():
 
 
 # ------------------------------------------------------------ packed weights
-@pytest.mark.parametrize("cfg,tm", [(TILES, 0), (TILES, 128), (TILES, 192), (TILES, 256),
-                                    (SMALL["mixed"], 0), (SMALL["heavy_ragged"], 0)],
+@pytest.mark.parametrize("cfg,tm,lm", [(TILES, 0, 0), (TILES, 128, 0), (TILES, 192, 0),
+                                       (TILES, 256, 0), (TILES, 0, -1), (SMALL["mixed"], 0, 0),
+                                       (SMALL["mixed"], 0, -1), (SMALL["heavy_ragged"], 0, 0),
+                                       (SMALL["light"], 0, -1), (SMALL["max_e_k"], 0, -1)],
                          ids=lambda v: getattr(v, "name", str(v)))
-def test_packed_weights_bitwise(cfg, tm):
-    """The heavy tiles reading the packed weight copy give the same output
-    bits as reading the plain layout (same data, same MFMA chains), at every
-    tile height, with ragged N blocks (I % 128 != 0) and a half-full last
-    K stage (I % 64 == 32)."""
-    print(f"[case] packed {cfg.name} tm={tm}", flush=True)
+def test_packed_weights_bitwise(cfg, tm, lm):
+    """The light loop reading the packed weight copy gives the same output
+    bits as reading the plain layout (same data, same MFMA chains); with the
+    light loop off (light_max_rows 0) the packed copy is unused and the
+    heavy tiles are unchanged at every height."""
+    print(f"[case] packed {cfg.name} tm={tm} light_max={lm}", flush=True)
     lay = layer_on_gpu(cfg)
     outs = []
     for packed in (False, True):
-        m = moe.MoELayer(lay, light_max_rows=0, heavy_tile_rows=tm, packed=packed)
+        m = moe.MoELayer(lay, light_max_rows=lm, heavy_tile_rows=tm, packed=packed)
         out, ids, w, counts = m()
         torch.cuda.synchronize()
         outs.append(out.view(torch.int32).cpu().numpy())
@@ -375,8 +377,10 @@ def test_packed_weights_bitwise(cfg, tm):
 
 
 def test_packed_weights_layout():
-    """Spot-check the packed image against its definition: slot p of block b
-    of stage st holds B row 8b + p//8, K chunk (p%8) ^ (p//8)."""
+    """Spot-check the packed chunks against their definition: lane L of
+    chunk (e, g, kb) holds K values 32kb + 8(L//16).. of gate row 8g + L%8
+    (L%16 < 8) or up row I + 8g + L%8 (gate|up), or of W_down row
+    16g + L%16 (down)."""
     cfg = custom("pk", T=8, H=192, E=2, k=1, I=160)
     lay = layer_on_gpu(cfg)
     s = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I)
@@ -386,29 +390,27 @@ def test_packed_weights_layout():
     wgu = lay.w_gu.view(torch.int16).cpu().numpy()
     wdn = lay.w_dn.view(torch.int16).cpu().numpy()
     H, I, E = cfg.H, cfg.I, cfg.E
-    nbg, nstg = -(-I // 128), H // 64
-    nbd, nstd = -(-H // 256), -(-I // 64)
+    gg, kg = I // 8, H // 32
+    gd, kd = H // 16, I // 32
     rng = np.random.default_rng(3)
 
-    def expect(gate_up, e, nb, st, b, p):
-        r = 8 * b + p // 8
-        c = (p % 8) ^ (p // 8)
-        k = st * 64 + 8 * c
+    def expect(gate_up, e, grp, kb, L):
+        k = 32 * kb + 8 * (L // 16)
         if gate_up:
-            hc = nb * 128 + (r >> 5) * 16 + (r & 15)
-            row = I + hc if (r & 16) else hc
-            ok, src, K = hc < I and k < H, wgu[e], H
+            c = 8 * grp + L % 8
+            row = c if L % 16 < 8 else I + c
+            ok, src = c < I and k < H, wgu[e]
         else:
-            row = nb * 256 + r
-            ok, src, K = row < H and k < I, wdn[e], I
+            row = 16 * grp + L % 16
+            ok, src = row < H and k < I, wdn[e]
         return src[row, k:k + 8] if ok else np.zeros(8, np.int16)
 
-    base_dn = E * nbg * nstg * 2048 * 8
-    for _ in range(400):
+    assert words.size == (E * gg * kg + E * gd * kd) * 512
+    base_dn = E * gg * kg * 512
+    for _ in range(600):
         gate_up = bool(rng.integers(2))
-        nb_n, st_n = (nbg, nstg) if gate_up else (nbd, nstd)
-        e, nb, st = rng.integers(E), rng.integers(nb_n), rng.integers(st_n)
-        b, p = rng.integers(32), rng.integers(64)
-        q = ((e * nb_n + nb) * st_n + st) * 2048 + b * 64 + p
+        ng, nk = (gg, kg) if gate_up else (gd, kd)
+        e, grp, kb, L = rng.integers(E), rng.integers(ng), rng.integers(nk), rng.integers(64)
+        q = ((e * ng + grp) * nk + kb) * 64 + L
         off = (0 if gate_up else base_dn) + q * 8
-        assert np.array_equal(words[off:off + 8], expect(gate_up, e, nb, st, b, p)), (gate_up, e, nb, st, b, p)
+        assert np.array_equal(words[off:off + 8], expect(gate_up, e, grp, kb, L)), (gate_up, e, grp, kb, L)
