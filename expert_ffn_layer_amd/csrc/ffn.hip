@@ -14,18 +14,18 @@
 // experts with few rows do not share a loop body with heavy experts, so the
 // light loop carries no heavy accumulators.
 //  * light: an expert with 1..64 rows; each wave streams 16 weight rows
-//    straight from HBM into registers and keeps one accumulator per 16-row
-//    sub-tile.  This is the decode path: it is bound by weight bytes.
-//  * heavy: 256x256 output tiles, A and B staged through a ring of LDS
-//    buffers by direct-to-LDS loads, row sub-tiles past the expert's count
-//    skipped, tiles of one expert scheduled together on one XCD.
+//    straight from HBM into registers (from the packed lane-order chunks when
+//    given, one contiguous run per wave) and keeps one accumulator per
+//    16-row sub-tile.  This is the decode path: it is bound by weight bytes.
+//    Its gate|up tiles hold 8 gate rows and the 8 matching up rows, so lanes
+//    n and n+8 carry g and u of one h column (one lane shuffle).
+//  * heavy: TM x 256 output tiles (TM = 256, 192 or 128, chosen from the row
+//    counts), A and B staged through LDS rings by direct-to-LDS loads, tiles
+//    of one expert scheduled together on one XCD.  Gate and up rows alternate
+//    by 16-row blocks, so g and u of an h column meet in one lane.
 // Both paths give every output element the same chain of MFMAs over K in
 // ascending 32-wide steps with the same K-slot assignment, and the same
 // epilogue, so a row's h and y are bitwise identical whichever loop ran it.
-//
-// gate|up column pairing: every 16-column MFMA tile holds 8 gate rows and the
-// 8 matching up rows of W_gate_up, so lane n (n < 8) and lane n+8 carry g_i
-// and u_i of the same i and the SwiGLU epilogue is one lane shuffle.
 #include <algorithm>
 
 #include "common.h"
@@ -435,12 +435,7 @@ struct HeavyGeom {
 constexpr int kXcds = MOE_HEAVY_XCD_SLICES;
   // MI355X: 8 XCDs, workgroups dispatched round-robin
 
-typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
-
-__device__ __forceinline__ void lds_dma16(const uint16_t* src, char* dst) {
-    __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, 0);
-}
 
 // Raw buffer resource over [base, base + bytes): loads past the end read 0
 // instead of touching memory.  Word 3 = 0x00020000: 32-bit data format, no
@@ -451,7 +446,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 // 16 bytes per lane from rsrc + voff + soff into LDS at dst + 16*lane
 // (buffer_load_dwordx4 ... lds).
-__device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
                                               char* dst) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)dst, 16, (int)voff, (int)soff, 0, 0);
 }
@@ -615,7 +610,7 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
         const uint32_t sa = (uint32_t)kk * 2u - adj_a;
 #pragma unroll
         for (int i = 0; i < kABlk; ++i)
-            lds_dma16_buf(ar, aoff[i] + sa, 0u, buf + (kABlk * wave + i) * kBlk);
+            lds_dma16(ar, aoff[i] + sa, 0u, buf + (kABlk * wave + i) * kBlk);
     };
     auto issue_b = [&](int st, int slot) {
         char* buf = b_slot(slot);
@@ -629,7 +624,7 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
         const uint32_t sb = (uint32_t)kb * 2u - adj_b;
 #pragma unroll
         for (int i = 0; i < kBBlkPerWave; ++i)
-            lds_dma16_buf(br, boff[i] + sb, 0u, buf + (kBBlkPerWave * wave + i) * kBlk);
+            lds_dma16(br, boff[i] + sb, 0u, buf + (kBBlkPerWave * wave + i) * kBlk);
     };
     // A tile's first loads, in the order the waits below count on: A0 B0
     // [A1 B1] [B2].

@@ -39,11 +39,18 @@ struct Layout {
            plan = 0, h = 0, y = 0, hs = 0, total = 0;
 };
 
+#ifndef MOE_ROUTER_MIN_BLOCKS
+#define MOE_ROUTER_MIN_BLOCKS 512
+#endif
+
+// Split-K factor of the router GEMM: doubled while the grid has fewer than
+// MOE_ROUTER_MIN_BLOCKS blocks and each split keeps >= 64 of H.
 int router_splits(int T, int H, int E) {
     const long long base = (long long)((E + moe::kRouterBE - 1) / moe::kRouterBE) *
                            ((T + moe::kRouterBT - 1) / moe::kRouterBT);
     int s = 1;
-    while (base * s < 512 && H % (2 * s * moe::kRouterBK) == 0 && H / (2 * s) >= 64) s *= 2;
+    while (base * s < MOE_ROUTER_MIN_BLOCKS && H % (2 * s * moe::kRouterBK) == 0 && H / (2 * s) >= 64)
+        s *= 2;
     return s;
 }
 

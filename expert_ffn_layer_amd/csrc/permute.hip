@@ -198,17 +198,25 @@ __global__ __launch_bounds__(kThreads) void perm_small_kernel(
     __syncthreads();
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int base = wave * (kPermChunk / kWavesPerBlock);
+    // Each wave ranks a contiguous quarter of the assignments (rounded up to
+    // whole 64-lane steps), so the four waves share the serial rank chain.
+    const int per_wave = (A + kWavesPerBlock * 64 - 1) / (kWavesPerBlock * 64) * 64;
+    const int steps = per_wave / 64;  // <= kPerThread since A <= kPermChunk
+    const int base = wave * per_wave;
     const uint64_t lt = lanemask_lt(lane);
     int local[kPerThread];
     int eid[kPerThread];
 #pragma unroll
     for (int q = 0; q < kPerThread; ++q) {
-        const int a = base + q * 64 + lane;
-        const int e = (a < A) ? ids[a] : -1;
-        const bool ok = valid_id(e, E);
-        local[q] = wave_stable_rank(e, ok, nbits, lt, wcnt + wave * E);
-        eid[q] = ok ? e : -1;
+        local[q] = 0;
+        eid[q] = -1;
+        if (q < steps) {
+            const int a = base + q * 64 + lane;
+            const int e = (a < A) ? ids[a] : -1;
+            const bool ok = valid_id(e, E);
+            local[q] = wave_stable_rank(e, ok, nbits, lt, wcnt + wave * E);
+            eid[q] = ok ? e : -1;
+        }
     }
     __syncthreads();
 
@@ -239,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void perm_small_kernel(
 #pragma unroll
     for (int q = 0; q < kPerThread; ++q) {
         const int a = base + q * 64 + lane;
-        if (a >= A) continue;
+        if (q >= steps || a >= A) continue;
         const int e = eid[q];
         if (e < 0) {
             inv_pos[a] = -1;

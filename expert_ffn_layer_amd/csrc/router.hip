@@ -146,29 +146,36 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
 
 constexpr int kMaxPerLane = 16;  // E <= 1024 = 16 * 64
 
-// One 256-thread block per token.  All threads reduce the split partials
-// (ascending split order) and add the bias into LDS; wave 0 then runs the
-// softmax over E and k rounds of a wave-wide argmax over (probability,
-// -expert id) keys held in registers.  Any k <= 32 works without padding k
-// to a power of 2.
-__global__ __launch_bounds__(256) void router_select_kernel(
+// One block of 256*NG threads per token.  The threads reduce the split
+// partials and add the bias into LDS: group g of 256 threads sums splits
+// [g*S/NG, (g+1)*S/NG) in ascending order and the NG group sums are added in
+// ascending g (NG = 4 when there are few tokens, so each thread has fewer
+// dependent loads).  Wave 0 then runs the softmax over E and k rounds of a
+// wave-wide argmax over (probability, -expert id) keys held in registers.
+// Any k <= 32 works without padding k to a power of 2.
+template <int NG>
+__global__ __launch_bounds__(256 * NG) void router_select_kernel(
     const float* __restrict__ part, int splits, const float* __restrict__ bias, int T, int E,
     int k, int renorm, int32_t* __restrict__ ids, float* __restrict__ w_out,
     float* __restrict__ probs) {
     __shared__ float lg[64 * kMaxPerLane];
+    __shared__ float gsum[NG > 1 ? NG - 1 : 1][64 * kMaxPerLane];
     const int t = blockIdx.x;
     const size_t plane = (size_t)T * E;
-    // Each thread owns experts tid + 256q (q < 4, E <= 1024); 8 splits of
+    const int col = threadIdx.x & 255, grp = threadIdx.x >> 8;
+    const int per = (splits + NG - 1) / NG;
+    const int sb = min(splits, grp * per), se = min(splits, sb + per);
+    // Each thread owns experts col + 256q (q < 4, E <= 1024); 8 splits of
     // each are loaded together, then added in ascending split order.
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < splits; s0 += 8) {
+    for (int s0 = sb; s0 < se; s0 += 8) {
         float v[4][8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int e = threadIdx.x + 256 * q;
+            const int e = col + 256 * q;
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-                v[q][u] = (e < E && s0 + u < splits)
+                v[q][u] = (e < E && s0 + u < se)
                               ? part[(size_t)(s0 + u) * plane + (size_t)t * E + e]
                               : 0.f;
         }
@@ -176,18 +183,38 @@ __global__ __launch_bounds__(256) void router_select_kernel(
         for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-                if (s0 + u < splits) acc[q] += v[q][u];
+                if (s0 + u < se) acc[q] += v[q][u];
     }
+    if (NG > 1) {
+        if (grp > 0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int e = threadIdx.x + 256 * q;
-        if (e < E) {
-            float l = acc[q];
-            if (bias) l += bias[e];
-            lg[e] = __builtin_isnan(l) ? -INFINITY : l;
+            for (int q = 0; q < 4; ++q) {
+                const int e = col + 256 * q;
+                if (e < E) gsum[grp - 1][e] = acc[q];
+            }
+        }
+        __syncthreads();
+        if (grp == 0) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int e = col + 256 * q;
+                if (e < E)
+                    for (int gg = 0; gg < NG - 1; ++gg) acc[q] += gsum[gg][e];
+            }
         }
     }
-    __syncthreads();
+    if (grp == 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = col + 256 * q;
+            if (e < E) {
+                float l = acc[q];
+                if (bias) l += bias[e];
+                lg[e] = __builtin_isnan(l) ? -INFINITY : l;
+            }
+        }
+    }
+    __syncthreads();  // every thread of the block reaches both barriers
     if (threadIdx.x >= 64) return;
     const int lane = threadIdx.x;
     const int nv = (E + 63) >> 6;
@@ -285,7 +312,12 @@ hipError_t launch_router_select(const float* part, int splits, const float* bias
                                 int k, int renorm, int32_t* ids, float* w, float* probs,
                                 hipStream_t st) {
     prof_begin(K_ROUTER_SELECT, st);
-    router_select_kernel<<<T, 256, 0, st>>>(part, splits, bias, T, E, k, renorm, ids, w, probs);
+    // Few tokens: four thread groups per token shorten each thread's chain
+    // of dependent partial loads.
+    if (T < 1024 && splits >= 16)
+        router_select_kernel<4><<<T, 1024, 0, st>>>(part, splits, bias, T, E, k, renorm, ids, w, probs);
+    else
+        router_select_kernel<1><<<T, 256, 0, st>>>(part, splits, bias, T, E, k, renorm, ids, w, probs);
     prof_end(K_ROUTER_SELECT, st);
     return hipGetLastError();
 }

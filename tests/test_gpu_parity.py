@@ -118,10 +118,12 @@ def _ids_tensor(rng, T, E, k):
                            device=gh.DEV)
 
 
-@pytest.mark.parametrize("T,E,k", [(1, 4, 1), (500, 64, 10), (1000, 512, 10), (4096, 8, 2),
+@pytest.mark.parametrize("T,E,k", [(1, 4, 1), (4, 16, 4), (64, 512, 10), (300, 128, 13),
+                                   (409, 64, 10), (500, 64, 10), (1000, 512, 10), (4096, 8, 2),
                                    (333, 1024, 32)])
 def test_permute_stage(oracle_lib, T, E, k):
-    """Bit-exact against the oracle's permutation (several chunks, ragged)."""
+    """Bit-exact against the oracle's permutation: one-block path (T*k <=
+    4096: 1, 16, 640, 3900, 4090 assignments) and several chunks, ragged."""
     print(f"[case] permute T={T} E={E} k={k}", flush=True)
     rng = np.random.default_rng(T + E)
     ids = _ids_tensor(rng, T, E, k)
