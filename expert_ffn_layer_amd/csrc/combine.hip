@@ -9,62 +9,70 @@ namespace moe {
 namespace {
 
 constexpr int kMaxK = 32;
+#ifndef MOE_COMBINE_V
+#define MOE_COMBINE_V 4
+#endif
+constexpr int kV = MOE_COMBINE_V;  // float4 column groups per thread (1024 columns apart)
 
-// grid (T, ceil(H / 1024)); each thread owns 4 consecutive columns.  The
-// token's k (row, weight) pairs are uniform across the block.
+// grid (T, ceil(H / (1024 kV))); each thread owns kV groups of 4 consecutive
+// columns.  The token's k (row, weight) pairs are uniform across the block.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                      const int32_t* __restrict__ inv_pos,
                                                      const float* __restrict__ w, int H, int k,
                                                      int accumulate, float* __restrict__ out) {
     const int t = blockIdx.x;
-    const int c0 = (blockIdx.y * 256 + threadIdx.x) * 4;
-    if (c0 >= H) return;
+    const int cb = blockIdx.y * 1024 * kV + threadIdx.x * 4;
     const int32_t* ip = inv_pos + (size_t)t * k;
     const float* wt = w + (size_t)t * k;
     bool all_valid = true;
     for (int j = 0; j < k; ++j) all_valid &= ip[j] >= 0;
-    float4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (all_valid) {
-        // every row present: issue the k row loads back to back
-        float4 v[kMaxK];
 #pragma unroll
-        for (int j = 0; j < kMaxK; ++j)
-            if (j < k) v[j] = *reinterpret_cast<const float4*>(y + (size_t)ip[j] * H + c0);
+    for (int q = 0; q < kV; ++q) {
+        const int c0 = cb + q * 1024;
+        if (c0 >= H) break;
+        float4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (all_valid) {
+            // every row present: issue the k row loads back to back
+            float4 v[kMaxK];
 #pragma unroll
-        for (int j = 0; j < kMaxK; ++j) {
-            if (j < k) {
+            for (int j = 0; j < kMaxK; ++j)
+                if (j < k) v[j] = *reinterpret_cast<const float4*>(y + (size_t)ip[j] * H + c0);
+#pragma unroll
+            for (int j = 0; j < kMaxK; ++j) {
+                if (j < k) {
+                    const float wj = wt[j];
+                    acc.x += wj * v[j].x;
+                    acc.y += wj * v[j].y;
+                    acc.z += wj * v[j].z;
+                    acc.w += wj * v[j].w;
+                }
+            }
+        } else {
+            for (int j = 0; j < k; ++j) {
+                const int p = ip[j];
+                if (p < 0) continue;
                 const float wj = wt[j];
-                acc.x += wj * v[j].x;
-                acc.y += wj * v[j].y;
-                acc.z += wj * v[j].z;
-                acc.w += wj * v[j].w;
+                const float4 v = *reinterpret_cast<const float4*>(y + (size_t)p * H + c0);
+                acc.x += wj * v.x;
+                acc.y += wj * v.y;
+                acc.z += wj * v.z;
+                acc.w += wj * v.w;
             }
         }
-    } else {
-        for (int j = 0; j < k; ++j) {
-            const int p = ip[j];
-            if (p < 0) continue;
-            const float wj = wt[j];
-            const float4 v = *reinterpret_cast<const float4*>(y + (size_t)p * H + c0);
-            acc.x += wj * v.x;
-            acc.y += wj * v.y;
-            acc.z += wj * v.z;
-            acc.w += wj * v.w;
+        float4* o = reinterpret_cast<float4*>(out + (size_t)t * H + c0);
+        if (accumulate) {
+            const float4 prev = *o;
+            acc = {prev.x + acc.x, prev.y + acc.y, prev.z + acc.z, prev.w + acc.w};
         }
+        *o = acc;
     }
-    float4* o = reinterpret_cast<float4*>(out + (size_t)t * H + c0);
-    if (accumulate) {
-        const float4 prev = *o;
-        acc = {prev.x + acc.x, prev.y + acc.y, prev.z + acc.z, prev.w + acc.w};
-    }
-    *o = acc;
 }
 
 }  // namespace
 
 hipError_t launch_combine(const float* y, const int32_t* inv_pos, const float* w, int T,
                           int H, int k, int accumulate, float* out, hipStream_t st) {
-    dim3 grid(T, (H + 1023) / 1024);
+    dim3 grid(T, (H + 1024 * kV - 1) / (1024 * kV));
     prof_begin(K_COMBINE, st);
     combine_kernel<<<grid, 256, 0, st>>>(y, inv_pos, w, H, k, accumulate, out);
     prof_end(K_COMBINE, st);
