@@ -18,19 +18,28 @@ constexpr int BE = kRouterBE;
 constexpr int BK = kRouterBK;
 constexpr int LDK = BK + 8;  // bf16 row pitch in LDS (80 bytes): spreads rows over the banks
 
-// fp32 -> three bf16 terms with hi + mid + lo == v up to 2^-24 relative
-// (each term rounds the exact fp32 remainder of the previous ones).
-__device__ __forceinline__ void split3(float v, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
-    hi = f32_to_bf16_bits(v);
-    const float r1 = v - bf16_bits_to_f32(hi);
-    mid = f32_to_bf16_bits(r1);
-    const float r2 = r1 - bf16_bits_to_f32(mid);
-    lo = f32_to_bf16_bits(r2);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float floatx2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> three packed bf16 pairs with hi + mid + lo == v exactly
+// for normal v (each term is the round-to-nearest-even bf16 of the exact fp32
+// remainder of the previous ones; 8 + 8 + 8 significand bits cover fp32's 24).
+__device__ __forceinline__ void split3_pair(float a, float b, uint32_t& hi, uint32_t& mid,
+                                            uint32_t& lo) {
+    const floatx2_t v = {a, b};
+    const bf16x2_t h = __builtin_convertvector(v, bf16x2_t);
+    const floatx2_t r1 = v - __builtin_convertvector(h, floatx2_t);
+    const bf16x2_t m = __builtin_convertvector(r1, bf16x2_t);
+    const floatx2_t r2 = r1 - __builtin_convertvector(m, floatx2_t);
+    const bf16x2_t l = __builtin_convertvector(r2, bf16x2_t);
+    hi = __builtin_bit_cast(uint32_t, h);
+    mid = __builtin_bit_cast(uint32_t, m);
+    lo = __builtin_bit_cast(uint32_t, l);
 }
 
 // part[s][t][e] for one 128x128 (token x expert) tile and one hidden slice.
 // The fp32 router product runs on bf16 MFMA: x is bf16 already, and every
-// router weight enters as three bf16 terms (split3), so each product
+// router weight enters as three bf16 terms (split3_pair), so each product
 // x*w_term is exact and the MFMA accumulates in fp32.  256 threads = 4 waves
 // in a 2x2 grid, each a 64x64 block of 16x16 tiles
 // (v_mfma_f32_16x16x32_bf16, 3 MFMAs per tile and K step).
@@ -46,9 +55,14 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int l16 = lane & 15, g = lane >> 4;
-    const int e0 = blockIdx.x * BE;
-    const int t0 = blockIdx.y * BT;
-    const int s = blockIdx.z;
+    // Blocks go round-robin to the 8 XCDs; each XCD takes a contiguous run of
+    // tiles, expert tile fastest, so the tiles sharing an x slice share an L2.
+    const int nb = gridDim.x, b = blockIdx.x;
+    const int tile = (nb & 7) ? b : (b & 7) * (nb >> 3) + (b >> 3);
+    const int ne = (E + BE - 1) / BE, nt = (T + BT - 1) / BT;
+    const int e0 = (tile % ne) * BE;
+    const int t0 = ((tile / ne) % nt) * BT;
+    const int s = tile / (ne * nt);
     const int kbeg = s * k_per_split;
     const int kend = kbeg + k_per_split;
     // router-weight staging: this thread owns expert e0+el, 16 consecutive k
@@ -80,14 +94,8 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
         for (int h8 = 0; h8 < 2; ++h8) {
             uint32_t p[3][4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint32_t a0, a1, a2, b0, b1, b2;
-                split3(wr[8 * h8 + 2 * j], a0, a1, a2);
-                split3(wr[8 * h8 + 2 * j + 1], b0, b1, b2);
-                p[0][j] = a0 | (b0 << 16);
-                p[1][j] = a1 | (b1 << 16);
-                p[2][j] = a2 | (b2 << 16);
-            }
+            for (int j = 0; j < 4; ++j)
+                split3_pair(wr[8 * h8 + 2 * j], wr[8 * h8 + 2 * j + 1], p[0][j], p[1][j], p[2][j]);
 #pragma unroll
             for (int pl = 0; pl < 3; ++pl)
                 *reinterpret_cast<u32x4_t*>(&ws[buf][pl][el][16 * kh + 8 * h8]) =
@@ -146,13 +154,94 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
 
 constexpr int kMaxPerLane = 16;  // E <= 1024 = 16 * 64
 
+// Softmax over the E logits held by one wave (lane holds experts lane + 64i,
+// i < NV; -inf marks a masked logit) and k rounds of a wave-wide argmax over
+// (probability, -expert id) keys held in registers.  Any k <= 32 works
+// without padding k to a power of 2.  Each lane sums its own slots in
+// ascending i and the lane sums are combined by a butterfly, so the result
+// does not depend on NV (slots past E hold 0).
+template <int NV>
+__device__ __forceinline__ void softmax_topk(float (&p)[NV], int lane, int t, int E, int k,
+                                             int renorm, int32_t* __restrict__ ids,
+                                             float* __restrict__ w_out,
+                                             float* __restrict__ probs) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) mx = fmaxf(mx, p[i]);
+    mx = wave_max(mx);
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = lane + 64 * i;
+        float z = 0.f;
+        if (e < E) {
+            if (mx == INFINITY)
+                z = (p[i] == INFINITY) ? 1.f : 0.f;
+            else if (mx == -INFINITY)
+                z = 1.f;
+            else
+                z = expf(p[i] - mx);
+        }
+        p[i] = z;
+        sum += z;
+    }
+    sum = wave_sum(sum);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E) {
+            p[i] = p[i] / sum;
+            if (probs) probs[(size_t)t * E + e] = p[i];
+        } else {
+            p[i] = -1.f;  // never selected: every real probability is >= 0
+        }
+    }
+
+    // k rounds of wave argmax.  Lane j keeps the j-th winner.
+    float my_p = 0.f;
+    int my_e = 0;
+    for (int j = 0; j < k; ++j) {
+        float bp = -2.f;
+        int be = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int e = lane + 64 * i;
+            if (p[i] > bp) {  // ascending e within a lane: the first max wins ties
+                bp = p[i];
+                be = e;
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const float op = __shfl_xor(bp, o, 64);
+            const int oe = __shfl_xor(be, o, 64);
+            if (op > bp || (op == bp && oe < be)) {
+                bp = op;
+                be = oe;
+            }
+        }
+        if (lane == j) {
+            my_p = bp;
+            my_e = be;
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            if (lane + 64 * i == be) p[i] = -2.f;
+    }
+    // Renormalise over the selected, summing in ascending j.
+    float ssum = 0.f;
+    for (int j = 0; j < k; ++j) ssum += __shfl(my_p, j, 64);
+    if (lane < k) {
+        ids[(size_t)t * k + lane] = my_e;
+        w_out[(size_t)t * k + lane] = renorm ? my_p / ssum : my_p;
+    }
+}
+
 // One block of 256*NG threads per token.  The threads reduce the split
 // partials and add the bias into LDS: group g of 256 threads sums splits
 // [g*S/NG, (g+1)*S/NG) in ascending order and the NG group sums are added in
 // ascending g (NG = 4 when there are few tokens, so each thread has fewer
-// dependent loads).  Wave 0 then runs the softmax over E and k rounds of a
-// wave-wide argmax over (probability, -expert id) keys held in registers.
-// Any k <= 32 works without padding k to a power of 2.
+// dependent loads).  Wave 0 then selects (softmax_topk).
 template <int NG>
 __global__ __launch_bounds__(256 * NG) void router_select_kernel(
     const float* __restrict__ part, int splits, const float* __restrict__ bias, int T, int E,
@@ -217,91 +306,57 @@ __global__ __launch_bounds__(256 * NG) void router_select_kernel(
     __syncthreads();  // every thread of the block reaches both barriers
     if (threadIdx.x >= 64) return;
     const int lane = threadIdx.x;
-    const int nv = (E + 63) >> 6;
-
     float p[kMaxPerLane];
-    float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < kMaxPerLane; ++i) {
         const int e = lane + 64 * i;
-        const float l = (i < nv && e < E) ? lg[e] : -INFINITY;
-        p[i] = l;
-        mx = fmaxf(mx, l);
+        p[i] = e < E ? lg[e] : -INFINITY;
     }
-    mx = wave_max(mx);
-    float sum = 0.f;
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-        const int e = lane + 64 * i;
-        float z = 0.f;
-        if (i < nv && e < E) {
-            if (mx == INFINITY)
-                z = (p[i] == INFINITY) ? 1.f : 0.f;
-            else if (mx == -INFINITY)
-                z = 1.f;
-            else
-                z = expf(p[i] - mx);
-        }
-        p[i] = z;
-        sum += z;
-    }
-    sum = wave_sum(sum);
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-        const int e = lane + 64 * i;
-        if (i < nv && e < E) {
-            p[i] = p[i] / sum;
-            if (probs) probs[(size_t)t * E + e] = p[i];
-        } else {
-            p[i] = -1.f;  // never selected: every real probability is >= 0
-        }
-    }
+    softmax_topk<kMaxPerLane>(p, lane, t, E, k, renorm, ids, w_out, probs);
+}
 
-    // k rounds of wave argmax.  Lane j keeps the j-th winner.
-    float my_p = 0.f;
-    int my_e = 0;
-    for (int j = 0; j < k; ++j) {
-        float bp = -2.f;
-        int be = 0x7fffffff;
+// One wave per token, four tokens per block: lane l sums the split partials
+// of experts l + 64i (i < NV) in ascending split order, adds the bias and
+// selects.  The logits equal router_select_kernel<1>'s bit for bit.
+template <int NV>
+__global__ __launch_bounds__(256) void router_select_wave_kernel(
+    const float* __restrict__ part, int splits, const float* __restrict__ bias, int T, int E,
+    int k, int renorm, int32_t* __restrict__ ids, float* __restrict__ w_out,
+    float* __restrict__ probs) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;  // no block barrier below
+    const size_t plane = (size_t)T * E;
+    const float* src = part + (size_t)t * E + lane;
+    float p[NV];
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i) {
-            const int e = lane + 64 * i;
-            if (p[i] > bp) {  // ascending e within a lane: the first max wins ties
-                bp = p[i];
-                be = e;
-            }
-        }
+    for (int i = 0; i < NV; ++i) p[i] = 0.f;
+    for (int s = 0; s < splits; ++s) {
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const float op = __shfl_xor(bp, o, 64);
-            const int oe = __shfl_xor(be, o, 64);
-            if (op > bp || (op == bp && oe < be)) {
-                bp = op;
-                be = oe;
-            }
-        }
-        if (lane == j) {
-            my_p = bp;
-            my_e = be;
-        }
-#pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i)
-            if (lane + 64 * i == be) p[i] = -2.f;
+        for (int i = 0; i < NV; ++i)
+            if (lane + 64 * i < E) p[i] += src[(size_t)s * plane + 64 * i];
     }
-    // Renormalise over the selected, summing in ascending j.
-    float ssum = 0.f;
-    for (int j = 0; j < k; ++j) ssum += __shfl(my_p, j, 64);
-    if (lane < k) {
-        ids[(size_t)t * k + lane] = my_e;
-        w_out[(size_t)t * k + lane] = renorm ? my_p / ssum : my_p;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E) {
+            float l = p[i];
+            if (bias) l += bias[e];
+            p[i] = __builtin_isnan(l) ? -INFINITY : l;
+        } else {
+            p[i] = -INFINITY;
+        }
     }
+    softmax_topk<NV>(p, lane, t, E, k, renorm, ids, w_out, probs);
 }
 
 }  // namespace
 
 hipError_t launch_router_gemm(const uint16_t* x, const float* wg, float* part, int T, int H,
                               int E, int splits, hipStream_t st) {
-    dim3 grid((E + BE - 1) / BE, (T + BT - 1) / BT, splits);
+    const long long nblk = (long long)((E + BE - 1) / BE) * ((T + BT - 1) / BT) * splits;
+    if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)nblk);
     prof_begin(K_ROUTER_GEMM, st);
     router_gemm_kernel<<<grid, 256, 0, st>>>(x, wg, part, T, H, E, H / splits);
     prof_end(K_ROUTER_GEMM, st);
@@ -316,8 +371,12 @@ hipError_t launch_router_select(const float* part, int splits, const float* bias
     // of dependent partial loads.
     if (T < 1024 && splits >= 16)
         router_select_kernel<4><<<T, 1024, 0, st>>>(part, splits, bias, T, E, k, renorm, ids, w, probs);
+    else if (E <= 512)
+        router_select_wave_kernel<8><<<(T + 3) / 4, 256, 0, st>>>(part, splits, bias, T, E, k,
+                                                                  renorm, ids, w, probs);
     else
-        router_select_kernel<1><<<T, 256, 0, st>>>(part, splits, bias, T, E, k, renorm, ids, w, probs);
+        router_select_wave_kernel<16><<<(T + 3) / 4, 256, 0, st>>>(part, splits, bias, T, E, k,
+                                                                   renorm, ids, w, probs);
     prof_end(K_ROUTER_SELECT, st);
     return hipGetLastError();
 }

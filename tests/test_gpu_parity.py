@@ -167,7 +167,11 @@ def test_permute_skips_invalid_ids():
     assert np.array_equal(inv_np[order], np.arange(n))
 
 
-@pytest.mark.parametrize("cfg", [SMALL["light"], SMALL["mixed"], SMALL["max_e_k"]],
+# many tokens (one wave per token in the select), E not a multiple of 64
+ROUTER_WIDE = custom("router_wide", T=1037, H=256, E=200, k=7, I=32)
+
+
+@pytest.mark.parametrize("cfg", [SMALL["light"], SMALL["mixed"], SMALL["max_e_k"], ROUTER_WIDE],
                          ids=lambda c: c.name)
 def test_router_stage(oracle_lib, cfg):
     print(f"[case] router {cfg.name}", flush=True)
