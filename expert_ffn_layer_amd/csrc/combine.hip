@@ -9,13 +9,15 @@ namespace moe {
 namespace {
 
 constexpr int kMaxK = 32;
-#ifndef MOE_COMBINE_V
-#define MOE_COMBINE_V 4
+#ifndef MOE_COMBINE_SMALL_T
+#define MOE_COMBINE_SMALL_T 512
 #endif
-constexpr int kV = MOE_COMBINE_V;  // float4 column groups per thread (1024 columns apart)
 
 // grid (T, ceil(H / (1024 kV))); each thread owns kV groups of 4 consecutive
-// columns.  The token's k (row, weight) pairs are uniform across the block.
+// columns, 1024 columns apart.  The token's k (row, weight) pairs are uniform
+// across the block.  y is read once and out written once, so both go through
+// non-temporal accesses (measured 9-14% faster at T = 4096..8192).
+template <int kV>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                      const int32_t* __restrict__ inv_pos,
                                                      const float* __restrict__ w, int H, int k,
@@ -36,7 +38,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
             float4 v[kMaxK];
 #pragma unroll
             for (int j = 0; j < kMaxK; ++j)
-                if (j < k) v[j] = *reinterpret_cast<const float4*>(y + (size_t)ip[j] * H + c0);
+                if (j < k) {
+                    const floatx4_t u = __builtin_nontemporal_load(
+                        reinterpret_cast<const floatx4_t*>(y + (size_t)ip[j] * H + c0));
+                    v[j] = float4{u[0], u[1], u[2], u[3]};
+                }
 #pragma unroll
             for (int j = 0; j < kMaxK; ++j) {
                 if (j < k) {
@@ -64,7 +70,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
             const float4 prev = *o;
             acc = {prev.x + acc.x, prev.y + acc.y, prev.z + acc.z, prev.w + acc.w};
         }
-        *o = acc;
+        __builtin_nontemporal_store(floatx4_t{acc.x, acc.y, acc.z, acc.w},
+                                    reinterpret_cast<floatx4_t*>(o));
     }
 }
 
@@ -72,9 +79,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 hipError_t launch_combine(const float* y, const int32_t* inv_pos, const float* w, int T,
                           int H, int k, int accumulate, float* out, hipStream_t st) {
-    dim3 grid(T, (H + 1024 * kV - 1) / (1024 * kV));
     prof_begin(K_COMBINE, st);
-    combine_kernel<<<grid, 256, 0, st>>>(y, inv_pos, w, H, k, accumulate, out);
+    // Few tokens: one column group per thread, so that T * H / 1024 blocks
+    // spread the gather over the whole chip (decode: 256 blocks, not 64).
+    if (T < MOE_COMBINE_SMALL_T)
+        combine_kernel<1><<<dim3(T, (H + 1023) / 1024), 256, 0, st>>>(y, inv_pos, w, H, k,
+                                                                     accumulate, out);
+    else
+        combine_kernel<4><<<dim3(T, (H + 4095) / 4096), 256, 0, st>>>(y, inv_pos, w, H, k,
+                                                                     accumulate, out);
     prof_end(K_COMBINE, st);
     return hipGetLastError();
 }

@@ -409,28 +409,31 @@ constexpr int kWTN = kTN / 4;  // 64 columns per wave
 #ifndef MOE_HEAVY_XCD_SLICES
 #define MOE_HEAVY_XCD_SLICES 8
 #endif
-// LDS rings: A (rows of x or h) two stages deep; B (expert weights) two
-// deep with 256-row tiles and three deep with 192- and 128-row tiles.  The
-// smaller heights are chosen when experts have few rows, so each expert's
-// weights feed few row tiles and stream from HBM with a longer latency to
-// cover; 256-row tiles are chosen for large experts whose weights the row
-// tiles share through L2 (measured: the third buffer costs 3% there and gains
-// 7% on streamed weights).
-constexpr int kAStages = 2;
+// LDS rings: A (rows of x or h) two stages deep, except three for the down
+// GEMM's 256-row tiles (measured 1.7% faster; 3% slower for gate|up); B
+// (expert weights) two deep with 256-row tiles and three deep with 192- and
+// 128-row tiles.  The smaller heights are chosen when experts have few rows,
+// so each expert's weights feed few row tiles and stream from HBM with a
+// longer latency to cover; 256-row tiles are chosen for large experts whose
+// weights the row tiles share through L2 (measured: the third B buffer costs
+// 3% there and gains 7% on streamed weights).  At most one of the two rings
+// is three deep: 160 KB of LDS.
 constexpr int kKS = 64;            // K values per stage
 constexpr int kBlk = 1024;         // bytes of one 8-row x 64-K block
 constexpr int kBlocksB = kTN / 8;  // 32
 constexpr int kBBlkPerWave = kBlocksB / kHeavyWaves;  // 4
 // Per tile height TM (256, 192, 128): each wave row group holds TM/2 rows
 // = TM/32 MFMA row tiles; a stage holds TM/8 A blocks and 32 B blocks.
-template <int TM>
+template <Mode M, int TM>
 struct HeavyGeom {
     static_assert(TM % 64 == 0 && TM >= 128 && TM <= 256, "tile height");
     static constexpr int kRF = TM / 32;                   // row tiles per wave (8, 6, 4)
     static constexpr int kBlocksA = TM / 8;               // 32, 24, 16
     static constexpr int kABlkPerWave = kBlocksA / kHeavyWaves;  // 4, 3, 2
     static constexpr int kABytes = kBlocksA * kBlk;       // 32, 24, 16 KB per stage
-    static constexpr int kBStages = TM == 256 ? 2 : 3;    // LDS 128, 144, 128 KB
+    static constexpr int kBStages = TM == 256 ? 2 : 3;
+    static constexpr int kAStages = (TM == 256 && M == Mode::Down) ? 3 : 2;
+    // LDS 128 (gate|up) or 160 (down), 144, 128 KB
 };
 constexpr int kXcds = MOE_HEAVY_XCD_SLICES;
   // MI355X: 8 XCDs, workgroups dispatched round-robin
@@ -471,7 +474,7 @@ __device__ __forceinline__ void ring_barrier() {
 
 template <Mode M, int TM>
 __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
-    using G = HeavyGeom<TM>;
+    using G = HeavyGeom<M, TM>;
     constexpr int kRF = G::kRF, kBlocksA = G::kBlocksA, kABlk = G::kABlkPerWave;
     constexpr int kABytes = G::kABytes;
     // One height per launch: the plan (or the host, for a dense group) names it.
@@ -479,12 +482,15 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
     // One LDS object for both rings (A stages, then B stages): with two
     // objects the compiler waits for every LDS DMA before any LDS read.
     constexpr int kBBytes = kBlocksB * kBlk;
-    constexpr int bst = G::kBStages;
-    __shared__ __attribute__((aligned(1024))) char lds[kAStages * kABytes + bst * kBBytes];
-    // Stage st's A lives in slot st % 2, its B in slot st % bst; the B slot
-    // index is carried along.
-    auto a_slot = [&](int st) -> char* { return lds + (st & 1) * kABytes; };
-    auto b_slot = [&](int slot) -> char* { return lds + kAStages * kABytes + slot * kBBytes; };
+    constexpr int bst = G::kBStages, ast = G::kAStages;
+    static_assert(ast == 2 || bst == 2, "one ring at most is three deep");
+    // Instructions per wave of the deeper ring's stage (0: both two deep).
+    constexpr int kDeepBlk = ast > 2 ? kABlk : (bst > 2 ? kBBlkPerWave : 0);
+    __shared__ __attribute__((aligned(1024))) char lds[ast * kABytes + bst * kBBytes];
+    // Stage st's A lives in slot st % ast, its B in slot st % bst; both slot
+    // indices are carried along (no division in the loop).
+    auto a_slot = [&](int slot) -> char* { return lds + slot * kABytes; };
+    auto b_slot = [&](int slot) -> char* { return lds + ast * kABytes + slot * kBBytes; };
 
     const int N = (M == Mode::GateUp) ? 2 * a.I : a.H;
     // split_h: the down GEMM's K runs over [hi | lo] (2I) against W_down twice.
@@ -586,7 +592,7 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
             }
         }
     };
-    // Stage st's loads of this wave: A blocks into A slot st % 2, B blocks
+    // Stage st's loads of this wave: A blocks into A slot st % ast, B blocks
     // into B slot st % bst.
     auto adjust = [&](int kk, uint32_t& adj_a, uint32_t& adj_b) {
         // Upper-half lanes in two rare stages: in the half-full last stage
@@ -602,8 +608,8 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
     };
     // The whole offset goes in the lane's VGPR; the 32-bit sum is exact
     // because the true offset is never negative.
-    auto issue_a = [&](int st) {
-        char* buf = a_slot(st);
+    auto issue_a = [&](int st, int slot) {
+        char* buf = a_slot(slot);
         const int kk = st * kKS;
         uint32_t adj_a, adj_b;
         adjust(kk, adj_a, adj_b);
@@ -619,28 +625,27 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
         const int kb = (M == Mode::Down && kk >= a.I) ? kk - a.I : kk;
         uint32_t adj_a, adj_b;
         adjust(kk, adj_a, adj_b);
-        // packed weights: stage st's image at st * 32 KB (the half-full last
-        // stage and the zero rows past I or H are stored as zeros)
         const uint32_t sb = (uint32_t)kb * 2u - adj_b;
 #pragma unroll
         for (int i = 0; i < kBBlkPerWave; ++i)
             lds_dma16(br, boff[i] + sb, 0u, buf + (kBBlkPerWave * wave + i) * kBlk);
     };
     // A tile's first loads, in the order the waits below count on: A0 B0
-    // [A1 B1] [B2].
+    // [A1 B1] [A2 or B2 of the three-deep ring].
     auto issue_first = [&]() {
-        issue_a(0);
+        issue_a(0, 0);
         issue_b(0, 0);
         if (nst > 1) {
-            issue_a(1);
+            issue_a(1, 1);
             issue_b(1, 1);
         }
+        if (ast == 3 && nst > 2) issue_a(2, 2);
         if (bst == 3 && nst > 2) issue_b(2, 2);
     };
     // Fragment reads of one 32-wide K half of a stage.  A fragment i of this
     // wave is tile rows wm*TM/2 + 16i.., B fragment j is B rows (wn*4 + j)*16..
-    auto rd_a = [&](int st, int half, int blk) -> bf16x8_t {
-        const char* p = a_slot(st) + blk * kBlk + (half ? foff1 : foff0);
+    auto rd_a = [&](int slot, int half, int blk) -> bf16x8_t {
+        const char* p = a_slot(slot) + blk * kBlk + (half ? foff1 : foff0);
         return *reinterpret_cast<const bf16x8_t*>(p);
     };
     auto read_b = [&](int slot, int half, bf16x8_t (&bf)[4]) {
@@ -651,10 +656,10 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
     };
     // A fragments in two groups: rows [0, kRF/2) and [kRF/2, kRF).
     constexpr int kG0 = kRF / 2;
-    auto read_a = [&](int st, int half, int grp, bf16x8_t (&af)[kRF]) {
+    auto read_a = [&](int slot, int half, int grp, bf16x8_t (&af)[kRF]) {
         const int i0 = grp ? kG0 : 0, i1 = grp ? kRF : kG0;
 #pragma unroll
-        for (int i = i0; i < i1; ++i) af[i] = rd_a(st, half, (wm * kRF + i) * 2);
+        for (int i = i0; i < i1; ++i) af[i] = rd_a(slot, half, (wm * kRF + i) * 2);
     };
 
     long long wi = wbeg + jx;
@@ -679,9 +684,9 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
         // The first loads were requested after the previous tile's epilogue
         // stores (or above, for the first tile); vector-memory operations
         // retire in order, so stage 0 is in once at most the loads after it
-        // (A1 B1, and B2 with a three-deep B ring) are pending.
-        if (nst > 2 && bst == 3)
-            wait_vmcnt<kABlk + 2 * kBBlkPerWave>();
+        // (A1 B1, and stage 2 of a three-deep ring) are pending.
+        if (nst > 2 && kDeepBlk > 0)
+            wait_vmcnt<kABlk + kBBlkPerWave + kDeepBlk>();
         else if (nst > 1)
             wait_vmcnt<kABlk + kBBlkPerWave>();
         else
@@ -696,39 +701,48 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
         // first half of the A rows after the first group (those rows are done
         // with), the second half of the A rows after the second group.  At a
         // stage boundary the first group also covers the wait for the next
-        // stage and the barrier that frees this stage's buffer for the load
-        // two stages ahead.  One loop with a branch-free body (no peeled
+        // stage and the barrier that frees this stage's buffers for the loads
+        // two or three stages ahead.  One loop with a branch-free body (no peeled
         // copies): peeling made the register allocator stop keeping each
         // accumulator in place and spill.
         const int nfull = nh / 2;  // stages with both halves
-        int bs = 0;                // B slot of stage st
+        int bs = 0, as = 0;        // B and A slots of stage st
         for (int st = 0; st < nfull; ++st) {
             const int bn = (bs + 1 == bst) ? 0 : bs + 1;  // B slot of stage st+1
+            const int an = (as + 1 == ast) ? 0 : as + 1;  // A slot of stage st+1
             mfma_rows(0, af, bf0);
             read_b(bs, 1, bf1);
-            read_a(st, 1, 0, af);
+            read_a(as, 1, 0, af);
             mfma_rows(1, af, bf0);
-            read_a(st, 1, 1, af);
+            read_a(as, 1, 1, af);
             mfma_rows(0, af, bf1);
             // After the last stage this wait, barrier and the reads of the
             // (absent) next stage are harmless: no load is outstanding and
             // the ring addresses are valid.
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of st done
-            // Stage st+1 in: only B(st+2) (three-deep B ring) may be pending.
-            if (bst == 3 && st + 2 < nst)
-                wait_vmcnt<kBBlkPerWave>();
+            // Stage st+1 in: only the three-deep ring's load of stage st+2
+            // may be pending.
+            if (kDeepBlk > 0 && st + 2 < nst)
+                wait_vmcnt<kDeepBlk>();
             else
                 wait_vmcnt<0>();
             ring_barrier();
-            // Refill the buffers stage st used: A two stages ahead, then B
-            // bst ahead (this order is what the wait above counts on).
-            if (st + 2 < nst) issue_a(st + 2);
-            if (st + bst < nst) issue_b(st + bst, bs);  // (st + bst) % bst == bs
+            // Refill the buffers stage st used, each ring its depth ahead and
+            // the two-deep ring first (this order is what the wait above
+            // counts on); stage st + depth lands in stage st's slot.
+            if (ast <= bst) {
+                if (st + ast < nst) issue_a(st + ast, as);
+                if (st + bst < nst) issue_b(st + bst, bs);
+            } else {
+                if (st + bst < nst) issue_b(st + bst, bs);
+                if (st + ast < nst) issue_a(st + ast, as);
+            }
             read_b(bn, 0, bf0);
-            read_a(st + 1, 0, 0, af);
+            read_a(an, 0, 0, af);
             mfma_rows(1, af, bf1);
-            read_a(st + 1, 0, 1, af);
+            read_a(an, 0, 1, af);
             bs = bn;
+            as = an;
         }
         if (nh & 1) {  // half-full last stage (down with I % 64 == 32)
             mfma_rows(0, af, bf0);
