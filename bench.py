@@ -87,6 +87,8 @@ def kernel_label(name: str):
     base = m.group(1)
     if base == "ffn_heavy_kernel":
         return "gateup_heavy" if "Mode)0" in name else "down_heavy"
+    if base.startswith("router_select"):  # block- and wave-per-token variants
+        return "router_select"
     return base[:-len("_kernel")] if base.endswith("_kernel") else base
 
 
