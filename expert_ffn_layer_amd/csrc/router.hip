@@ -242,7 +242,7 @@ __device__ __forceinline__ void softmax_topk(float (&p)[NV], int lane, int t, in
 // [g*S/NG, (g+1)*S/NG) in ascending order and the NG group sums are added in
 // ascending g (NG = 4 when there are few tokens, so each thread has fewer
 // dependent loads).  Wave 0 then selects (softmax_topk).
-template <int NG>
+template <int NG, int QN, int UB>
 __global__ __launch_bounds__(256 * NG) void router_select_kernel(
     const float* __restrict__ part, int splits, const float* __restrict__ bias, int T, int E,
     int k, int renorm, int32_t* __restrict__ ids, float* __restrict__ w_out,
@@ -254,30 +254,32 @@ __global__ __launch_bounds__(256 * NG) void router_select_kernel(
     const int col = threadIdx.x & 255, grp = threadIdx.x >> 8;
     const int per = (splits + NG - 1) / NG;
     const int sb = min(splits, grp * per), se = min(splits, sb + per);
-    // Each thread owns experts col + 256q (q < 4, E <= 1024); 8 splits of
-    // each are loaded together, then added in ascending split order.
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = sb; s0 < se; s0 += 8) {
-        float v[4][8];
+    // Each thread owns experts col + 256q (q < QN, E <= 256 QN); UB splits
+    // of each are loaded together, then added in ascending split order.
+    float acc[QN];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < QN; ++q) acc[q] = 0.f;
+    for (int s0 = sb; s0 < se; s0 += UB) {
+        float v[QN][UB];
+#pragma unroll
+        for (int q = 0; q < QN; ++q) {
             const int e = col + 256 * q;
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
+            for (int u = 0; u < UB; ++u)
                 v[q][u] = (e < E && s0 + u < se)
                               ? part[(size_t)(s0 + u) * plane + (size_t)t * E + e]
                               : 0.f;
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < QN; ++q)
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
+            for (int u = 0; u < UB; ++u)
                 if (s0 + u < se) acc[q] += v[q][u];
     }
     if (NG > 1) {
         if (grp > 0) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < QN; ++q) {
                 const int e = col + 256 * q;
                 if (e < E) gsum[grp - 1][e] = acc[q];
             }
@@ -285,7 +287,7 @@ __global__ __launch_bounds__(256 * NG) void router_select_kernel(
         __syncthreads();
         if (grp == 0) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < QN; ++q) {
                 const int e = col + 256 * q;
                 if (e < E)
                     for (int gg = 0; gg < NG - 1; ++gg) acc[q] += gsum[gg][e];
@@ -294,7 +296,7 @@ __global__ __launch_bounds__(256 * NG) void router_select_kernel(
     }
     if (grp == 0) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < QN; ++q) {
             const int e = col + 256 * q;
             if (e < E) {
                 float l = acc[q];
@@ -306,13 +308,14 @@ __global__ __launch_bounds__(256 * NG) void router_select_kernel(
     __syncthreads();  // every thread of the block reaches both barriers
     if (threadIdx.x >= 64) return;
     const int lane = threadIdx.x;
-    float p[kMaxPerLane];
+    constexpr int NV = 4 * QN;  // expert slots per lane
+    float p[NV];
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
+    for (int i = 0; i < NV; ++i) {
         const int e = lane + 64 * i;
         p[i] = e < E ? lg[e] : -INFINITY;
     }
-    softmax_topk<kMaxPerLane>(p, lane, t, E, k, renorm, ids, w_out, probs);
+    softmax_topk<NV>(p, lane, t, E, k, renorm, ids, w_out, probs);
 }
 
 // One wave per token, four tokens per block: lane l sums the split partials
@@ -369,8 +372,14 @@ hipError_t launch_router_select(const float* part, int splits, const float* bias
     prof_begin(K_ROUTER_SELECT, st);
     // Few tokens: four thread groups per token shorten each thread's chain
     // of dependent partial loads.
-    if (T < 1024 && splits >= 16)
-        router_select_kernel<4><<<T, 1024, 0, st>>>(part, splits, bias, T, E, k, renorm, ids, w, probs);
+    if (T < 1024 && splits >= 16) {
+        if (E <= 512)
+            router_select_kernel<4, 2, 16><<<T, 1024, 0, st>>>(part, splits, bias, T, E, k, renorm,
+                                                           ids, w, probs);
+        else
+            router_select_kernel<4, 4, 8><<<T, 1024, 0, st>>>(part, splits, bias, T, E, k, renorm, ids,
+                                                           w, probs);
+    }
     else if (E <= 512)
         router_select_wave_kernel<8><<<(T + 3) / 4, 256, 0, st>>>(part, splits, bias, T, E, k,
                                                                   renorm, ids, w, probs);

@@ -169,10 +169,13 @@ def test_permute_skips_invalid_ids():
 
 # many tokens (one wave per token in the select), E not a multiple of 64
 ROUTER_WIDE = custom("router_wide", T=1037, H=256, E=200, k=7, I=32)
+# few tokens and 16 split-K partials (the grouped select), E <= 512 and E > 512
+ROUTER_SPLIT = custom("router_split", T=10, H=1024, E=300, k=5, I=32)
+ROUTER_SPLIT_WIDE_E = custom("router_split_wide_e", T=20, H=1024, E=1000, k=12, I=32)
 
 
-@pytest.mark.parametrize("cfg", [SMALL["light"], SMALL["mixed"], SMALL["max_e_k"], ROUTER_WIDE],
-                         ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [SMALL["light"], SMALL["mixed"], SMALL["max_e_k"], ROUTER_WIDE,
+                                 ROUTER_SPLIT, ROUTER_SPLIT_WIDE_E], ids=lambda c: c.name)
 def test_router_stage(oracle_lib, cfg):
     print(f"[case] router {cfg.name}", flush=True)
     lay = layer_on_gpu(cfg)
