@@ -49,8 +49,12 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=64, help="tokens in the oracle's sample")
     p.add_argument("--no-packed", action="store_true",
-                   help="heavy tiles read the plain weight layout instead of the packed copy "
-                        "made once before timing (moe_pack_weights)")
+                   help="the light loop reads the plain weight layout instead of the packed "
+                        "copy made once before timing (moe_pack_weights)")
+    p.add_argument("--y-dtype", choices=("auto", "fp32", "bf16"), default="auto",
+                   help="storage of the routed expert outputs between the down GEMM and the "
+                        "combine; auto = bf16 except for a layer with a shared expert or "
+                        "fp32 values (their outputs need the fp32 margin)")
     p.add_argument("--no-copy-calibration", action="store_true",
                    help="skip the untimed 1 GiB reference copy used to scale rocprof counters")
     p.add_argument("--summarize", nargs=4, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR", "LOG"),
@@ -246,7 +250,9 @@ def main():
     layer = synth.make_layer(cfg, seed=args.seed, device=dev)
     if cfg.fp32_values:
         layer = layer.rounded_to_bf16()
-    m = moe.MoELayer(layer, packed=not args.no_packed)
+    y_bf16 = args.y_dtype == "bf16" or (args.y_dtype == "auto" and not cfg.I_shared
+                                        and not cfg.fp32_values)
+    m = moe.MoELayer(layer, packed=not args.no_packed, y_bf16=y_bf16)
     s = m.shape
     out = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=dev)
     ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
@@ -305,11 +311,12 @@ def main():
     A = cfg.T * cfg.k
     H, I = cfg.H, cfg.I
     x_bytes = cfg.T * H * 2
+    y_el = 2 if y_bf16 else 4  # bytes per stored y value
     if dominant == "gateup_light":
         alg = light_experts * 2 * I * H * 2 + x_bytes + light_rows * I * 2
         flops = 4 * light_rows * H * I
     elif dominant == "down_light":
-        alg = light_experts * H * I * 2 + light_rows * (I * 2 + H * 4)
+        alg = light_experts * H * I * 2 + light_rows * (I * 2 + H * y_el)
         flops = 2 * light_rows * H * I
     elif dominant == "gateup_heavy":
         he = touched - light_experts
@@ -319,7 +326,7 @@ def main():
     elif dominant == "down_heavy":
         he = touched - light_experts
         hr = A - light_rows
-        alg = he * H * I * 2 + hr * (I * 2 + H * 4)
+        alg = he * H * I * 2 + hr * (I * 2 + H * y_el)
         flops = 2 * hr * H * I
     elif dominant == "router_gemm":
         alg = x_bytes + H * cfg.E * 4
@@ -383,7 +390,8 @@ def main():
         "data": "synthetic (seeded normal draws, random-init weights)",
         "config": {"workload": workload, "tokens": cfg.T, "hidden": H, "experts": cfg.E,
                    "top_k": cfg.k, "intermediate": I, "shared_intermediate": cfg.I_shared,
-                   "seed": args.seed, "packed_weights": m.packed is not None},
+                   "seed": args.seed, "packed_weights": m.packed is not None,
+                   "y_dtype": "bf16" if y_bf16 else "fp32"},
         "roofline": roof,
         "layer_roofline": layer,
         "kernels_us": {k: round(v, 2) for k, v in per_kernel.items()},

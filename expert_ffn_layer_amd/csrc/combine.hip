@@ -13,44 +13,79 @@ constexpr int kMaxK = 32;
 #define MOE_COMBINE_SMALL_T 512
 #endif
 
-// grid (T, ceil(H / (1024 kV))); each thread owns kV groups of 4 consecutive
-// columns, 1024 columns apart.  The token's k (row, weight) pairs are uniform
-// across the block.  y is read once and out written once, so both go through
-// non-temporal accesses (measured 9-14% faster at T = 4096..8192).
-template <int kV>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// C consecutive y values (C = 4: fp32 or bf16; C = 8: bf16) as one raw
+// vector load, read non-temporally (each y row is read once); elem() widens
+// value c to fp32 exactly.
+template <int C, bool BF16>
+struct YLoad;
+template <>
+struct YLoad<4, false> {
+    typedef floatx4_t raw_t;
+    static __device__ __forceinline__ float elem(const raw_t& r, int c) { return r[c]; }
+};
+template <>
+struct YLoad<4, true> {
+    typedef u32x2_t raw_t;
+    static __device__ __forceinline__ float elem(const raw_t& r, int c) {
+        const uint32_t u = r[c >> 1];
+        return __uint_as_float((c & 1) ? (u & 0xffff0000u) : (u << 16));
+    }
+};
+template <>
+struct YLoad<8, true> {
+    typedef u32x4_t raw_t;
+    static __device__ __forceinline__ float elem(const raw_t& r, int c) {
+        const uint32_t u = r[c >> 1];
+        return __uint_as_float((c & 1) ? (u & 0xffff0000u) : (u << 16));
+    }
+};
+
+template <int C, bool BF16>
+__device__ __forceinline__ typename YLoad<C, BF16>::raw_t load_y(const void* y, size_t idx) {
+    typedef typename YLoad<C, BF16>::raw_t R;
+    const char* p = static_cast<const char*>(y) + idx * (BF16 ? 2 : 4);
+    return __builtin_nontemporal_load(reinterpret_cast<const R*>(p));
+}
+
+// grid (T, ceil(H / (256 C kV))); each thread owns kV groups of C
+// consecutive columns, 256 C columns apart.  The token's k (row, weight)
+// pairs are uniform across the block.  y is read once and out written once,
+// so both go through non-temporal accesses (measured 9-14% faster at
+// T = 4096..8192).  Every element sums its k rows in ascending j.
+template <int kV, int C, bool BF16>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y,
                                                      const int32_t* __restrict__ inv_pos,
                                                      const float* __restrict__ w, int H, int k,
                                                      int accumulate, float* __restrict__ out) {
+    typedef YLoad<C, BF16> L;
+    constexpr int kSpan = 256 * C;
     const int t = blockIdx.x;
-    const int cb = blockIdx.y * 1024 * kV + threadIdx.x * 4;
+    const int cb = blockIdx.y * kSpan * kV + threadIdx.x * C;
     const int32_t* ip = inv_pos + (size_t)t * k;
     const float* wt = w + (size_t)t * k;
     bool all_valid = true;
     for (int j = 0; j < k; ++j) all_valid &= ip[j] >= 0;
 #pragma unroll
     for (int q = 0; q < kV; ++q) {
-        const int c0 = cb + q * 1024;
+        const int c0 = cb + q * kSpan;
         if (c0 >= H) break;
-        float4 acc = {0.f, 0.f, 0.f, 0.f};
+        float acc[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) acc[c] = 0.f;
         if (all_valid) {
             // every row present: issue the k row loads back to back
-            float4 v[kMaxK];
+            typename L::raw_t v[kMaxK];
 #pragma unroll
             for (int j = 0; j < kMaxK; ++j)
-                if (j < k) {
-                    const floatx4_t u = __builtin_nontemporal_load(
-                        reinterpret_cast<const floatx4_t*>(y + (size_t)ip[j] * H + c0));
-                    v[j] = float4{u[0], u[1], u[2], u[3]};
-                }
+                if (j < k) v[j] = load_y<C, BF16>(y, (size_t)ip[j] * H + c0);
 #pragma unroll
             for (int j = 0; j < kMaxK; ++j) {
                 if (j < k) {
                     const float wj = wt[j];
-                    acc.x += wj * v[j].x;
-                    acc.y += wj * v[j].y;
-                    acc.z += wj * v[j].z;
-                    acc.w += wj * v[j].w;
+#pragma unroll
+                    for (int c = 0; c < C; ++c) acc[c] += wj * L::elem(v[j], c);
                 }
             }
         } else {
@@ -58,36 +93,45 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                 const int p = ip[j];
                 if (p < 0) continue;
                 const float wj = wt[j];
-                const float4 v = *reinterpret_cast<const float4*>(y + (size_t)p * H + c0);
-                acc.x += wj * v.x;
-                acc.y += wj * v.y;
-                acc.z += wj * v.z;
-                acc.w += wj * v.w;
+                const typename L::raw_t v = load_y<C, BF16>(y, (size_t)p * H + c0);
+#pragma unroll
+                for (int c = 0; c < C; ++c) acc[c] += wj * L::elem(v, c);
             }
         }
-        float4* o = reinterpret_cast<float4*>(out + (size_t)t * H + c0);
-        if (accumulate) {
-            const float4 prev = *o;
-            acc = {prev.x + acc.x, prev.y + acc.y, prev.z + acc.z, prev.w + acc.w};
+        floatx4_t* o = reinterpret_cast<floatx4_t*>(out + (size_t)t * H + c0);
+#pragma unroll
+        for (int c4 = 0; c4 < C / 4; ++c4) {
+            floatx4_t r = {acc[4 * c4], acc[4 * c4 + 1], acc[4 * c4 + 2], acc[4 * c4 + 3]};
+            if (accumulate) {
+                const floatx4_t prev = o[c4];
+                r = floatx4_t{prev[0] + r[0], prev[1] + r[1], prev[2] + r[2], prev[3] + r[3]};
+            }
+            __builtin_nontemporal_store(r, o + c4);
         }
-        __builtin_nontemporal_store(floatx4_t{acc.x, acc.y, acc.z, acc.w},
-                                    reinterpret_cast<floatx4_t*>(o));
     }
 }
 
 }  // namespace
 
-hipError_t launch_combine(const float* y, const int32_t* inv_pos, const float* w, int T,
-                          int H, int k, int accumulate, float* out, hipStream_t st) {
+hipError_t launch_combine(const void* y, int y_bf16, const int32_t* inv_pos, const float* w,
+                          int T, int H, int k, int accumulate, float* out, hipStream_t st) {
     prof_begin(K_COMBINE, st);
     // Few tokens: one column group per thread, so that T * H / 1024 blocks
     // spread the gather over the whole chip (decode: 256 blocks, not 64).
-    if (T < MOE_COMBINE_SMALL_T)
-        combine_kernel<1><<<dim3(T, (H + 1023) / 1024), 256, 0, st>>>(y, inv_pos, w, H, k,
-                                                                     accumulate, out);
-    else
-        combine_kernel<4><<<dim3(T, (H + 4095) / 4096), 256, 0, st>>>(y, inv_pos, w, H, k,
-                                                                     accumulate, out);
+    // From 512 tokens: 16-byte row loads (4 fp32 or 8 bf16 columns), 4096
+    // columns per block.
+    const dim3 g1(T, (H + 1023) / 1024), g4(T, (H + 4095) / 4096);
+    if (T < MOE_COMBINE_SMALL_T) {
+        if (y_bf16)
+            combine_kernel<1, 4, true><<<g1, 256, 0, st>>>(y, inv_pos, w, H, k, accumulate, out);
+        else
+            combine_kernel<1, 4, false><<<g1, 256, 0, st>>>(y, inv_pos, w, H, k, accumulate, out);
+    } else {
+        if (y_bf16)
+            combine_kernel<2, 8, true><<<g4, 256, 0, st>>>(y, inv_pos, w, H, k, accumulate, out);
+        else
+            combine_kernel<4, 4, false><<<g4, 256, 0, st>>>(y, inv_pos, w, H, k, accumulate, out);
+    }
     prof_end(K_COMBINE, st);
     return hipGetLastError();
 }

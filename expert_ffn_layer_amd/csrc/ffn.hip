@@ -155,6 +155,30 @@ __device__ __forceinline__ bf16x8_t load_weights(const uint16_t* p) {
 constexpr int kLightSubTiles = kLightRowsMax / 16;  // 4
 constexpr int kLightWideU = 2;                      // K steps in flight, wide branch
 
+// ------------------------------------------------------- y in bf16
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float floatx2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values as one word of two bf16 (round to nearest even), a in the
+// low half.
+__device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2_t{a, b}, bf16x2_t));
+}
+
+// A lane of a 16x16 MFMA result holds rows 4g..4g+3 of column c = l16.  For
+// 32-bit bf16 stores the lanes of columns c and c^1 swap halves: the even
+// column's lane then holds rows 4g, 4g+1 and the odd column's lane rows
+// 4g+2, 4g+3, each as the word (column c & ~1, column c | 1).  Every lane of
+// the wave must call this (a lane exchange).
+__device__ __forceinline__ void y_bf16_pairs(const floatx4_t v, int l16, uint32_t& w0,
+                                             uint32_t& w1) {
+    const bool odd = l16 & 1;
+    const float s0 = __shfl_xor(odd ? v[0] : v[2], 1, 64);
+    const float s1 = __shfl_xor(odd ? v[1] : v[3], 1, 64);
+    w0 = odd ? pack_bf16_rne(s0, v[2]) : pack_bf16_rne(v[0], s0);
+    w1 = odd ? pack_bf16_rne(s1, v[3]) : pack_bf16_rne(v[1], s1);
+}
+
 // ------------------------------------------------------- light: gate|up
 // One wave: MT row sub-tiles x NTILE column tiles of one expert, K = H.
 // Tile t pairs gate rows i0+8t.. and the matching up rows, so lanes
@@ -346,6 +370,26 @@ __device__ __forceinline__ void down_light_rows(const FfnArgs& a, int e, int r0,
             for (int t = 0; t < NT; ++t) cb[u][t] = nb_[u][t];
         }
     }
+    if (a.y_bf16) {
+        const int odd = l16 & 1;
+        uint32_t* y = static_cast<uint32_t*>(a.y);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                uint32_t w[2];
+                y_bf16_pairs(acc[m][t], l16, w[0], w[1]);
+                const int c = c0 + t * 16 + l16 - odd;  // even
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    const int row = m * 16 + 4 * g + 2 * odd + r;
+                    if (row < n) y[((size_t)(r0 + row) * a.H + c) / 2] = w[r];
+                }
+            }
+        }
+        return;
+    }
+    float* y = static_cast<float*>(a.y);
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
 #pragma unroll
@@ -354,7 +398,7 @@ __device__ __forceinline__ void down_light_rows(const FfnArgs& a, int e, int r0,
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = m * 16 + 4 * g + r;
-                if (row < n) a.y[(size_t)(r0 + row) * a.H + c] = acc[m][t][r];
+                if (row < n) y[(size_t)(r0 + row) * a.H + c] = acc[m][t][r];
             }
         }
     }
@@ -472,7 +516,8 @@ __device__ __forceinline__ void ring_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <Mode M, int TM>
+// YB (down only): y stored as bf16 instead of fp32 (a.y_bf16).
+template <Mode M, int TM, bool YB>
 __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
     using G = HeavyGeom<M, TM>;
     constexpr int kRF = G::kRF, kBlocksA = G::kBlocksA, kABlk = G::kABlkPerWave;
@@ -762,7 +807,7 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
         const int t_nb = nb, t_base = r0 + m0, t_rows = rows;
         const long long wnext = wi + nb_x;
         if (wnext < wend) setup(wnext);
-        if (M == Mode::GateUp) {
+        if constexpr (M == Mode::GateUp) {
             const int hc0 = t_nb * (kTN / 2) + wn * 32 + l16;
             uint16_t* hp = a.h + (size_t)(t_base + row0) * hstride + hc0;
             const bool full = t_rows == TM && t_nb * (kTN / 2) + kTN / 2 <= a.I;
@@ -788,9 +833,32 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
                     }
                 }
             }
+        } else if constexpr (YB) {
+            // bf16 y: lanes of adjacent columns pair up (y_bf16_pairs), so
+            // each lane writes 2 rows x 2 columns as two 32-bit words.
+            const int odd = l16 & 1;
+            const int c0 = t_nb * kTN + wn * kWTN + l16 - odd;  // even
+            uint32_t* yp = static_cast<uint32_t*>(a.y) +
+                           ((size_t)(t_base + row0 + 2 * odd) * a.H + c0) / 2;
+            const bool full = t_rows == TM && t_nb * kTN + kTN <= a.H;
+#pragma unroll
+            for (int i = 0; i < kRF; ++i) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    uint32_t w[2];
+                    y_bf16_pairs(acc[i][j], l16, w[0], w[1]);
+                    const bool col_ok = c0 + j * 16 < a.H;
+#pragma unroll
+                    for (int r = 0; r < 2; ++r) {
+                        const int dr = i * 16 + r;
+                        if (full || (row0 + 2 * odd + dr < t_rows && col_ok))
+                            yp[((size_t)dr * a.H + j * 16) / 2] = w[r];
+                    }
+                }
+            }
         } else {
             const int c0 = t_nb * kTN + wn * kWTN + l16;
-            float* yp = a.y + (size_t)(t_base + row0) * a.H + c0;
+            float* yp = static_cast<float*>(a.y) + (size_t)(t_base + row0) * a.H + c0;
             const bool full = t_rows == TM && t_nb * kTN + kTN <= a.H;
 #pragma unroll
             for (int i = 0; i < kRF; ++i) {
@@ -855,24 +923,24 @@ int grid_for(long long work, int per_cu, int num_cu) {
 // Heavy tiles of one GEMM.  With a plan the tile height is decided on the
 // device, so every height's kernel is launched and all but one return at
 // once; a dense group's height is known here.
-template <Mode M>
+template <Mode M, bool YB>
 hipError_t launch_heavy(const FfnArgs& a, int ncols, hipStream_t st) {
     const long long nblk = (ncols + kTN - 1) / kTN;
     if (a.plan) {
         if (a.max_tiles <= 0) return hipSuccess;
         const int grid = grid_for((long long)a.max_tiles * nblk, 1, a.num_cu);
-        ffn_heavy_kernel<M, kTileTM0><<<grid, kHeavyThreads, 0, st>>>(a);
-        ffn_heavy_kernel<M, kTileTM1><<<grid, kHeavyThreads, 0, st>>>(a);
-        ffn_heavy_kernel<M, kTileTM2><<<grid, kHeavyThreads, 0, st>>>(a);
+        ffn_heavy_kernel<M, kTileTM0, YB><<<grid, kHeavyThreads, 0, st>>>(a);
+        ffn_heavy_kernel<M, kTileTM1, YB><<<grid, kHeavyThreads, 0, st>>>(a);
+        ffn_heavy_kernel<M, kTileTM2, YB><<<grid, kHeavyThreads, 0, st>>>(a);
         return hipGetLastError();
     }
     if (a.dense_rows <= 0) return hipSuccess;
     const long long tiles = (a.dense_rows + a.dense_tm - 1) / a.dense_tm;
     const int grid = grid_for(tiles * nblk, 1, a.num_cu);
     switch (a.dense_tm) {
-        case kTileTM0: ffn_heavy_kernel<M, kTileTM0><<<grid, kHeavyThreads, 0, st>>>(a); break;
-        case kTileTM1: ffn_heavy_kernel<M, kTileTM1><<<grid, kHeavyThreads, 0, st>>>(a); break;
-        case kTileTM2: ffn_heavy_kernel<M, kTileTM2><<<grid, kHeavyThreads, 0, st>>>(a); break;
+        case kTileTM0: ffn_heavy_kernel<M, kTileTM0, YB><<<grid, kHeavyThreads, 0, st>>>(a); break;
+        case kTileTM1: ffn_heavy_kernel<M, kTileTM1, YB><<<grid, kHeavyThreads, 0, st>>>(a); break;
+        case kTileTM2: ffn_heavy_kernel<M, kTileTM2, YB><<<grid, kHeavyThreads, 0, st>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -928,7 +996,7 @@ hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t st) {
     }
     if ((a.plan && a.max_tiles > 0) || (!a.plan && a.dense_rows > 0)) {
         prof_begin(K_GATEUP_HEAVY, st);
-        hipError_t err = launch_heavy<Mode::GateUp>(a, 2 * a.I, st);
+        hipError_t err = launch_heavy<Mode::GateUp, false>(a, 2 * a.I, st);
         prof_end(K_GATEUP_HEAVY, st);
         return err;
     }
@@ -953,7 +1021,8 @@ hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st) {
     }
     if ((a.plan && a.max_tiles > 0) || (!a.plan && a.dense_rows > 0)) {
         prof_begin(K_DOWN_HEAVY, st);
-        hipError_t err = launch_heavy<Mode::Down>(a, a.H, st);
+        hipError_t err = a.y_bf16 ? launch_heavy<Mode::Down, true>(a, a.H, st)
+                                  : launch_heavy<Mode::Down, false>(a, a.H, st);
         prof_end(K_DOWN_HEAVY, st);
         return err;
     }

@@ -95,7 +95,7 @@ struct FfnArgs {
     const uint16_t* w_gu;        // [E,2I,H]
     const uint16_t* w_dn;        // [E,H,I]
     uint16_t* h;                 // [rows,I] bf16 ([rows,2I] when split_h)
-    float* y;                    // [rows,H] fp32
+    void* y;                     // [rows,H]: fp32, or bf16 when y_bf16
     const int32_t* plan;         // device plan, or nullptr for a dense group
     int T, H, I, E;
     int dense_rows;              // rows of a dense group (plan == nullptr)
@@ -107,6 +107,7 @@ struct FfnArgs {
     const uint16_t* pk_dn;       // packed W_down for the light loop, or nullptr
     int max_light;               // grid bound for light experts
     int num_cu;
+    int y_bf16;                  // 1: y stored as bf16 (round to nearest even)
 };
 
 // Packed expert weights: 1 KB chunks, each the 16 weight rows x 32 K of one
@@ -132,7 +133,8 @@ hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st);
 
 // ---- combine ------------------------------------------------------------
-hipError_t launch_combine(const float* y, const int32_t* inv_pos, const float* w, int T,
-                          int H, int k, int accumulate, float* out, hipStream_t st);
+// y: [A,H] fp32, or bf16 when y_bf16.
+hipError_t launch_combine(const void* y, int y_bf16, const int32_t* inv_pos, const float* w,
+                          int T, int H, int k, int accumulate, float* out, hipStream_t st);
 
 }  // namespace moe

@@ -74,6 +74,7 @@ int check_shape(const moe_shape* s) {
     if (s->heavy_tile_rows != 0 && s->heavy_tile_rows != moe::kTileTM0 &&
         s->heavy_tile_rows != moe::kTileTM1 && s->heavy_tile_rows != moe::kTileTM2)
         return fail(MOE_ERR_UNSUPPORTED, "heavy_tile_rows must be 0, 128, 192 or 256");
+    if (s->y_bf16 != 0 && s->y_bf16 != 1) return fail(MOE_ERR_UNSUPPORTED, "y_bf16 must be 0 or 1");
     return MOE_OK;
 }
 
@@ -103,7 +104,7 @@ Layout layout(const moe_shape* s) {
     L.inv = take((size_t)A * 4);
     L.plan = take((size_t)(moe::kPlanHeader + E + 2LL * L.max_tiles) * 4);
     L.h = take((size_t)A * I * 2);
-    L.y = take((size_t)A * H * 4);
+    L.y = take((size_t)A * H * (s->y_bf16 ? 2 : 4));
     L.hs = take((size_t)T * 2 * s->I_shared * 2);  // [hi | lo] rows
     L.total = off;
     return L;
@@ -187,7 +188,7 @@ int run_permute(const moe_shape* s, const Layout& L, const int32_t* ids, int32_t
 
 int run_ffn(const moe_shape* s, const Layout& L, const uint16_t* x, const int32_t* sorted,
             const int32_t* offsets, const uint16_t* wgu, const uint16_t* wdn,
-            const void* packed, uint16_t* h, float* y, void* ws, hipStream_t st,
+            const void* packed, uint16_t* h, void* y, void* ws, hipStream_t st,
             bool plan_ready = false) {
     int ncu = 0;
     if (int rc = device_cu_count(&ncu)) return rc;
@@ -214,6 +215,7 @@ int run_ffn(const moe_shape* s, const Layout& L, const uint16_t* x, const int32_
     a.max_tiles = L.max_tiles;
     a.max_light = L.max_light;
     a.num_cu = ncu;
+    a.y_bf16 = s->y_bf16;
     if (packed) {
         const char* p = static_cast<const char*>(packed);
         a.pk_gu = reinterpret_cast<const uint16_t*>(p);
@@ -249,6 +251,7 @@ int run_shared(const moe_shape* s, const Layout& L, const uint16_t* x, const uin
     a.max_tiles = 0;
     a.max_light = 0;
     a.num_cu = ncu;
+    a.y_bf16 = 0;  // written straight into the fp32 output
     HIP_TRY(moe::launch_ffn_gateup(a, st), "shared gate|up");
     HIP_TRY(moe::launch_ffn_down(a, st), "shared down");
     return MOE_OK;
@@ -351,7 +354,7 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t* counts
 
 int moe_grouped_ffn(const moe_shape* shape, const uint16_t* x, const int32_t* sorted_token_ids,
                     const int32_t* offsets, const uint16_t* w_gate_up, const uint16_t* w_down,
-                    const void* packed_weights, uint16_t* h, float* y, void* workspace,
+                    const void* packed_weights, uint16_t* h, void* y, void* workspace,
                     size_t ws_bytes, void* stream) {
     g_last_error.clear();
     if (int rc = check_shape(shape)) return rc;
@@ -386,7 +389,7 @@ int moe_shared_ffn(const moe_shape* shape, const uint16_t* x, const uint16_t* ws
                       (hipStream_t)stream);
 }
 
-int moe_combine(const moe_shape* shape, const float* y, const int32_t* inv_pos,
+int moe_combine(const moe_shape* shape, const void* y, const int32_t* inv_pos,
                 const float* topk_w, int32_t accumulate, float* out, void* stream) {
     g_last_error.clear();
     if (int rc = check_shape(shape)) return rc;
@@ -395,7 +398,7 @@ int moe_combine(const moe_shape* shape, const float* y, const int32_t* inv_pos,
     REQUIRE_PTR(inv_pos);
     REQUIRE_PTR(topk_w);
     REQUIRE_PTR(out);
-    HIP_TRY(moe::launch_combine(y, inv_pos, topk_w, shape->T, shape->H, shape->k,
+    HIP_TRY(moe::launch_combine(y, shape->y_bf16, inv_pos, topk_w, shape->T, shape->H, shape->k,
                                 accumulate ? 1 : 0, out, (hipStream_t)stream),
             "combine");
     return MOE_OK;
@@ -442,7 +445,7 @@ int moe_forward(const moe_shape* shape, const uint16_t* x, const float* w_router
     float* w = topk_w_out ? topk_w_out : at<float>(workspace, L.w);
     int32_t* sorted = at<int32_t>(workspace, L.sorted);
     int32_t* inv = at<int32_t>(workspace, L.inv);
-    float* y = at<float>(workspace, L.y);
+    void* y = at<char>(workspace, L.y);
     if (int rc = run_router(shape, L, x, w_router, bias, ids, w, nullptr, workspace, st)) return rc;
     bool plan_ready = false;
     if (int rc = run_permute(shape, L, ids, counts, offsets, sorted, inv, workspace, st, &plan_ready))
@@ -452,8 +455,8 @@ int moe_forward(const moe_shape* shape, const uint16_t* x, const float* w_router
         return rc;
     if (shape->I_shared > 0)
         if (int rc = run_shared(shape, L, x, ws_gate_up, ws_down, out, workspace, st)) return rc;
-    HIP_TRY(moe::launch_combine(y, inv, w, shape->T, shape->H, shape->k, shape->I_shared > 0 ? 1 : 0,
-                                out, st),
+    HIP_TRY(moe::launch_combine(y, shape->y_bf16, inv, w, shape->T, shape->H, shape->k,
+                                shape->I_shared > 0 ? 1 : 0, out, st),
             "combine");
     return MOE_OK;
 }

@@ -44,7 +44,7 @@ class MoeShape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("I", ctypes.c_int32), ("I_shared", ctypes.c_int32),
                 ("renorm", ctypes.c_int32), ("light_max_rows", ctypes.c_int32),
-                ("heavy_tile_rows", ctypes.c_int32)]
+                ("heavy_tile_rows", ctypes.c_int32), ("y_bf16", ctypes.c_int32)]
 
     def __repr__(self):
         return ("MoeShape(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")")
@@ -106,8 +106,9 @@ def _check(rc: int) -> None:
 
 
 def make_shape(T, H, E, k, I, I_shared=0, renorm=1, light_max_rows=-1,
-               heavy_tile_rows=0) -> MoeShape:
-    return MoeShape(T, H, E, k, I, I_shared, renorm, light_max_rows, heavy_tile_rows)
+               heavy_tile_rows=0, y_bf16=0) -> MoeShape:
+    return MoeShape(T, H, E, k, I, I_shared, renorm, light_max_rows, heavy_tile_rows,
+                    int(bool(y_bf16)))
 
 
 def workspace_bytes(shape: MoeShape) -> int:
@@ -126,8 +127,9 @@ def packed_weight_bytes(shape: MoeShape) -> int:
 
 
 def pack_weights(shape: MoeShape, w_gate_up, w_down, stream=None) -> torch.Tensor:
-    """One-time re-layout of the routed expert weights for the heavy tiles
-    (moe_pack_weights); returns the packed uint8 device buffer."""
+    """One-time re-layout of the routed expert weights into the lane-order
+    chunks the light loop streams (moe_pack_weights); returns the packed
+    uint8 device buffer."""
     n = packed_weight_bytes(shape)
     if n == 0:
         raise MoeError(MOE_ERR_SHAPE, f"invalid shape {shape}")
@@ -208,7 +210,7 @@ def grouped_ffn(shape, x, sorted_token_ids, offsets, w_gate_up, w_down, h, y, wo
             _ptr(offsets, "offsets", I32, E + 1), _ptr(w_gate_up, "w_gate_up", BF16, E * 2 * I * H),
             _ptr(w_down, "w_down", BF16, E * H * I), _packed(packed_weights, shape),
             _ptr(h, "h", BF16, A * I, optional=True),
-            _ptr(y, "y", F32, A * H)]
+            _ptr(y, "y", y_dtype(shape), A * H)]
     wp, wn = _ws(workspace, shape)
     _check(lib().moe_grouped_ffn(ctypes.byref(shape), *args, wp, wn, _stream(stream)))
 
@@ -221,9 +223,14 @@ def shared_ffn(shape, x, ws_gate_up, ws_down, out, workspace, stream=None):
     _check(lib().moe_shared_ffn(ctypes.byref(shape), *args, wp, wn, _stream(stream)))
 
 
+def y_dtype(shape) -> torch.dtype:
+    """Element type of the routed expert outputs y for ``shape``."""
+    return BF16 if shape.y_bf16 else F32
+
+
 def combine(shape, y, inv_pos, topk_w, accumulate, out, stream=None):
     T, H, A = shape.T, shape.H, shape.T * shape.k
-    args = [_ptr(y, "y", F32, A * H), _ptr(inv_pos, "inv_pos", I32, A),
+    args = [_ptr(y, "y", y_dtype(shape), A * H), _ptr(inv_pos, "inv_pos", I32, A),
             _ptr(topk_w, "topk_w", F32, A)]
     _check(lib().moe_combine(ctypes.byref(shape), *args, int(bool(accumulate)),
                              _ptr(out, "out", F32, T * H), _stream(stream)))
@@ -268,11 +275,11 @@ class MoELayer:
     moe_forward and returns (out, topk_ids, topk_w, counts)."""
 
     def __init__(self, layer, light_max_rows: int = -1, heavy_tile_rows: int = 0,
-                 packed: bool = False):
+                 packed: bool = False, y_bf16: bool = False):
         c = layer.cfg
         self.layer = layer
         self.shape = make_shape(c.T, c.H, c.E, c.k, c.I, c.I_shared, c.renorm, light_max_rows,
-                                heavy_tile_rows)
+                                heavy_tile_rows, y_bf16)
         self.workspace = alloc_workspace(self.shape, layer.x.device)
         self.packed = pack_weights(self.shape, layer.w_gu, layer.w_dn) if packed else None
 

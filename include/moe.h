@@ -83,6 +83,13 @@ typedef struct moe_shape {
     int32_t heavy_tile_rows; /* rows per heavy tile: 0 = chosen per call from the expert
                                row counts (the least padded-row time); 128, 192 or 256
                                = that height.  Results do not depend on it. */
+    int32_t y_bf16;         /* storage of the routed expert outputs y: 0 = fp32, 1 = bf16
+                               (round to nearest even).  bf16 halves the y round trip
+                               between the down GEMM and the combine (2*T*k*H bytes less
+                               written and read); it rounds each y to 8 significant bits
+                               before the fp32 weighted sum, so it suits layers whose
+                               |y| are small against the output tolerance.  The shared
+                               expert's output is always fp32. */
 } moe_shape;
 
 /* Bytes of workspace every call below needs for `shape` (host-only, pure;
@@ -156,7 +163,7 @@ int moe_pack_weights(const moe_shape* shape, const uint16_t* w_gate_up, const ui
 
 /* Grouped expert FFN over the expert-major rows (pwwt.cn section 4.2):
  *   h[r,:] = bf16( silu(x[tok_r] . W_gate[e]) * (x[tok_r] . W_up[e]) )
- *   y[r,:] = h[r,:] . W_down[e]   (fp32)          for rows r of expert e,
+ *   y[r,:] = h[r,:] . W_down[e]   (fp32 sum)      for rows r of expert e,
  * bf16 MFMA with fp32 accumulation; token rows are gathered inside the GEMM.
  * Experts with 1..light_max_rows rows run the light-row loop, the others
  * the heavy tiles; both give bitwise identical rows.
@@ -168,13 +175,14 @@ int moe_pack_weights(const moe_shape* shape, const uint16_t* w_gate_up, const ui
  *                    given, the light loop reads it instead of w_gate_up /
  *                    w_down (the heavy tiles always read those)
  *   h                bf16 [T*k,I] out, or NULL (then kept in the workspace)
- *   y                fp32 [T*k,H] out (fp32 so that large |y| entering the
- *                    weighted sum are not rounded to 8 significant bits)
+ *   y                [T*k,H] out: fp32 (shape->y_bf16 == 0; large |y| entering
+ *                    the weighted sum keep 24 significant bits) or bf16
+ *                    (shape->y_bf16 == 1, rounded to nearest even)
  */
 int moe_grouped_ffn(const moe_shape* shape, const uint16_t* x,
                     const int32_t* sorted_token_ids, const int32_t* offsets,
                     const uint16_t* w_gate_up, const uint16_t* w_down,
-                    const void* packed_weights, uint16_t* h, float* y, void* workspace,
+                    const void* packed_weights, uint16_t* h, void* y, void* workspace,
                     size_t ws_bytes, void* stream);
 
 /* Shared expert (lumevalley.com Ling-2.6-1T article): one dense SwiGLU FFN
@@ -193,9 +201,9 @@ int moe_shared_ffn(const moe_shape* shape, const uint16_t* x, const uint16_t* ws
  *   s[t,c]   = sum_{j<k} topk_w[t,j] * y[inv_pos[t*k+j], c]   (ascending j,
  *              fp32; rows with inv_pos < 0 are skipped)
  *   out[t,c] = accumulate ? out[t,c] + s[t,c] : s[t,c]
- *   y fp32 [T*k,H], inv_pos int32 [T*k], topk_w fp32 [T,k], out fp32 [T,H].
- * No workspace. */
-int moe_combine(const moe_shape* shape, const float* y, const int32_t* inv_pos,
+ *   y [T*k,H] fp32 or bf16 as shape->y_bf16 says, inv_pos int32 [T*k],
+ *   topk_w fp32 [T,k], out fp32 [T,H].  No workspace. */
+int moe_combine(const moe_shape* shape, const void* y, const int32_t* inv_pos,
                 const float* topk_w, int32_t accumulate, float* out, void* stream);
 
 /* The whole layer: router, permute, grouped FFN, shared expert (when

@@ -42,7 +42,7 @@ def test_library_has_gfx950_code():
 
 def shp(**kw):
     base = dict(T=64, H=4096, E=512, k=10, I=1024, I_shared=0, renorm=1, light_max_rows=-1,
-                heavy_tile_rows=0)
+                heavy_tile_rows=0, y_bf16=0)
     base.update(kw)
     return moe.MoeShape(*[base[n] for n, _ in moe.MoeShape._fields_])
 
@@ -61,6 +61,17 @@ def test_workspace_no_padding(L):
     assert small < need / 50
 
 
+def test_workspace_bf16_y(L):
+    """bf16 y takes exactly 2*A*H bytes less workspace (rounded to the
+    256-byte alignment of each buffer)."""
+    c = synth.CONFIGS["prefill"]
+    A = c.T * c.k
+    full = moe.workspace_bytes(shp(T=c.T))
+    half = moe.workspace_bytes(shp(T=c.T, y_bf16=1))
+    assert full - half == A * c.H * 2
+    assert moe.make_shape(4, 64, 8, 2, 32, y_bf16=True).y_bf16 == 1
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(k=0), moe.MOE_ERR_SHAPE), (dict(T=-1), moe.MOE_ERR_SHAPE), (dict(k=600), moe.MOE_ERR_SHAPE),
     (dict(H=100), moe.MOE_ERR_UNSUPPORTED), (dict(I=48), moe.MOE_ERR_UNSUPPORTED),
@@ -70,6 +81,7 @@ def test_workspace_no_padding(L):
     (dict(I_shared=40), moe.MOE_ERR_UNSUPPORTED), (dict(T=300000000, k=10), moe.MOE_ERR_SHAPE),
     (dict(T=1 << 19, k=1), moe.MOE_ERR_UNSUPPORTED), (dict(I=1 << 18), moe.MOE_ERR_UNSUPPORTED),
     (dict(I_shared=1 << 18), moe.MOE_ERR_UNSUPPORTED),
+    (dict(y_bf16=2), moe.MOE_ERR_UNSUPPORTED), (dict(y_bf16=-1), moe.MOE_ERR_UNSUPPORTED),
 ])
 def test_bad_shapes(L, kw, code):
     s = shp(**kw)

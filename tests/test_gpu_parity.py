@@ -55,6 +55,14 @@ def test_forward_small(oracle_lib, name):
     log(name, rep)
 
 
+@pytest.mark.parametrize("name", ["light", "heavy_ragged", "mixed", "shared", "max_e_k"])
+def test_forward_small_bf16_y(oracle_lib, name):
+    """Routed expert outputs stored as bf16 (the shared expert stays fp32)."""
+    print(f"[case] forward bf16 y {name}", flush=True)
+    rep = gh.check_layer(oracle_lib, layer_on_gpu(SMALL[name]), y_bf16=True)
+    log(name + "/bf16y", rep)
+
+
 @pytest.mark.parametrize("name", ["tiny", "light", "mixed"])
 def test_forward_heavy_only(oracle_lib, name):
     """Every expert through the heavy tiles (light loop off)."""
@@ -70,19 +78,20 @@ def test_forward_heavy_only(oracle_lib, name):
 TILES = custom("tiles", T=600, H=320, E=8, k=3, I=96, I_shared=96)
 
 
-def test_tile_heights_bitwise(oracle_lib):
+@pytest.mark.parametrize("y_bf16", [False, True])
+def test_tile_heights_bitwise(oracle_lib, y_bf16):
     """Every heavy tile height gives the same output bits (each element's
     MFMA chain over K is the same), and matches the oracle."""
-    print("[case] tile heights", flush=True)
+    print(f"[case] tile heights y_bf16={y_bf16}", flush=True)
     lay = layer_on_gpu(TILES)
     outs = {}
     for tm in (0, 256, 192, 128):
-        g = gh.gpu_forward(lay, light_max_rows=0, heavy_tile_rows=tm)
+        g = gh.gpu_forward(lay, light_max_rows=0, heavy_tile_rows=tm, y_bf16=y_bf16)
         outs[tm] = g["out"].view(np.int32)
     for tm in (256, 192, 128):
         assert np.array_equal(outs[tm], outs[0]), f"tile height {tm} differs"
-    rep = gh.check_layer(oracle_lib, lay, light_max_rows=0, heavy_tile_rows=192)
-    log("tiles/192", rep)
+    rep = gh.check_layer(oracle_lib, lay, light_max_rows=0, heavy_tile_rows=192, y_bf16=y_bf16)
+    log(f"tiles/192/bf16y={y_bf16}", rep)
 
 
 @pytest.mark.parametrize("tm", [128, 192, 256])
@@ -93,17 +102,19 @@ def test_forward_heavy_ragged_heights(oracle_lib, tm):
 
 
 # ------------------------------------------------------------ full size
-@pytest.mark.parametrize("name,sample", [("decode", None), ("prefill", 64), ("skew", 64),
-                                         ("ling", 48)])
-def test_forward_full_size(oracle_lib, name, sample):
-    print(f"[case] full-size {name}", flush=True)
+@pytest.mark.parametrize("name,sample,y_bf16", [
+    ("decode", None, False), ("prefill", 64, False), ("skew", 64, False), ("ling", 48, False),
+    # bf16 y, as the benchmark runs the layers without a shared expert
+    ("decode", None, True), ("prefill", 64, True), ("skew", 64, True)])
+def test_forward_full_size(oracle_lib, name, sample, y_bf16):
+    print(f"[case] full-size {name} y_bf16={y_bf16}", flush=True)
     cfg = synth.CONFIGS[name]
     lay = layer_on_gpu(cfg)
     tokens = None
     if sample:
         tokens = np.sort(np.random.default_rng(1).choice(cfg.T, sample, replace=False))
-    rep = gh.check_layer(oracle_lib, lay, tokens=tokens)
-    log(name, rep)
+    rep = gh.check_layer(oracle_lib, lay, tokens=tokens, y_bf16=y_bf16)
+    log(f"{name}/bf16y={y_bf16}", rep)
     counts = rep["gpu"]["counts"]
     assert counts.sum() == cfg.T * cfg.k
     if name == "prefill":
@@ -222,15 +233,16 @@ def test_router_nonfinite(oracle_lib):
 
 
 @pytest.mark.parametrize("light_max", [16, 64])
-def test_light_heavy_bitwise(light_max):
+@pytest.mark.parametrize("y_bf16", [False, True])
+def test_light_heavy_bitwise(light_max, y_bf16):
     """The same expert rows through the light loop (both its 16-row and its
     wide 17..64-row branch) and through the heavy tiles give bitwise
-    identical h and y."""
+    identical h and y (fp32 or bf16)."""
     cfg = custom("lh", T=160, H=512, E=64, k=8, I=256)
     lay = layer_on_gpu(cfg)
     outs = []
     for lm in (light_max, 0):
-        s = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, light_max_rows=lm)
+        s = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, light_max_rows=lm, y_bf16=y_bf16)
         ws = moe.alloc_workspace(s)
         A = cfg.T * cfg.k
         ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=gh.DEV)
@@ -240,11 +252,11 @@ def test_light_heavy_bitwise(light_max):
         counts, offsets, srt, inv = t(cfg.E), t(cfg.E + 1), t(A), t(A)
         moe.permute(s, ids, counts, offsets, srt, inv, ws)
         h = torch.empty((A, cfg.I), dtype=torch.bfloat16, device=gh.DEV)
-        y = torch.empty((A, cfg.H), dtype=torch.float32, device=gh.DEV)
+        y = torch.empty((A, cfg.H), dtype=moe.y_dtype(s), device=gh.DEV)
         moe.grouped_ffn(s, lay.x, srt, offsets, lay.w_gu, lay.w_dn, h, y, ws)
         torch.cuda.synchronize()
-        outs.append((counts.cpu().numpy(), h.view(torch.int16).cpu().numpy(),
-                     y.view(torch.int32).cpu().numpy()))
+        yi = y.view(torch.int16) if y_bf16 else y.view(torch.int32)
+        outs.append((counts.cpu().numpy(), h.view(torch.int16).cpu().numpy(), yi.cpu().numpy()))
     (c0, h0, y0), (c1, h1, y1) = outs
     assert np.array_equal(c0, c1)
     assert ((c0 >= 1) & (c0 <= 16)).sum() > 0
@@ -254,11 +266,13 @@ def test_light_heavy_bitwise(light_max):
     assert np.array_equal(y0, y1), "y differs between light and heavy loops"
 
 
-def test_ffn_stage_rows(oracle_lib):
-    """Grouped FFN rows (fp32 y from bf16 h) against the oracle's per-row expert FFN."""
+@pytest.mark.parametrize("y_bf16", [False, True])
+def test_ffn_stage_rows(oracle_lib, y_bf16):
+    """Grouped FFN rows (fp32 or bf16 y from bf16 h) against the oracle's
+    per-row expert FFN."""
     cfg = SMALL["mixed"]
     lay = layer_on_gpu(cfg)
-    s = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I)
+    s = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, y_bf16=y_bf16)
     ws = moe.alloc_workspace(s)
     A = cfg.T * cfg.k
     ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=gh.DEV)
@@ -267,12 +281,12 @@ def test_ffn_stage_rows(oracle_lib):
     t = lambda n: torch.empty(n, dtype=torch.int32, device=gh.DEV)
     counts, offsets, srt, inv = t(cfg.E), t(cfg.E + 1), t(A), t(A)
     moe.permute(s, ids, counts, offsets, srt, inv, ws)
-    y = torch.empty((A, cfg.H), dtype=torch.float32, device=gh.DEV)
+    y = torch.empty((A, cfg.H), dtype=moe.y_dtype(s), device=gh.DEV)
     moe.grouped_ffn(s, lay.x, srt, offsets, lay.w_gu, lay.w_dn, None, y, ws)
     torch.cuda.synchronize()
     off = offsets.cpu().numpy()
     srt_np = srt.cpu().numpy()
-    y_np = y.cpu().numpy()
+    y_np = y.float().cpu().numpy()
     for e in range(cfg.E):
         rows = np.arange(off[e], off[e + 1])
         if rows.size == 0:
@@ -282,22 +296,26 @@ def test_ffn_stage_rows(oracle_lib):
         gh.assert_close(y_np[rows], ref, f"expert {e}")
 
 
-def test_combine_stage():
-    """Combine against a float64 numpy weighted sum of the same fp32 rows."""
+@pytest.mark.parametrize("T,y_bf16", [(77, False), (77, True), (600, False), (600, True)])
+def test_combine_stage(T, y_bf16):
+    """Combine against a float64 numpy weighted sum of the same rows (fp32,
+    or bf16 widened exactly), below and above the 512-token grid switch."""
     rng = np.random.default_rng(9)
-    T, H, k, E = 77, 320, 5, 20
+    H, k, E = 320, 5, 20
     A = T * k
     y = torch.randn((A, H), device=gh.DEV)
+    if y_bf16:
+        y = y.to(torch.bfloat16)
     perm = rng.permutation(A).astype(np.int32)
     perm[3] = -1  # skipped row
     w = torch.rand((T, k), device=gh.DEV)
-    s = moe.make_shape(T, H, E, k, 32)
+    s = moe.make_shape(T, H, E, k, 32, y_bf16=y_bf16)
     for acc in (0, 1):
         out = torch.randn((T, H), device=gh.DEV)
         prev = out.cpu().numpy().astype(np.float64)
         moe.combine(s, y, torch.as_tensor(perm, device=gh.DEV), w, acc, out)
         torch.cuda.synchronize()
-        yv = y.cpu().numpy().astype(np.float64)
+        yv = y.float().cpu().numpy().astype(np.float64)
         wv = w.cpu().numpy().astype(np.float64)
         ref = np.zeros((T, H))
         for t in range(T):
