@@ -305,7 +305,7 @@ def main():
     # Algorithmic work, from this run's own routing.
     cnt = counts.cpu().numpy().astype(np.int64)
     touched = int((cnt > 0).sum())
-    light = (cnt > 0) & (cnt <= moe.LIGHT_MAX_ROWS)
+    light = moe.light_experts(cnt, s)
     light_rows = int(cnt[light].sum())
     light_experts = int(light.sum())
     A = cfg.T * cfg.k

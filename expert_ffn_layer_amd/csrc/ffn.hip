@@ -57,11 +57,22 @@ constexpr int kThreads = 256;
 __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restrict__ offsets,
                                                         int E, int light_max, int force_tm,
                                                         int32_t* __restrict__ plan) {
-    __shared__ int wl[16], wt[16], wc[3][16];
+    __shared__ int wl[16], wt[16], wc[3][16], wtouch[16];
     const int e = threadIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
     const int n = (e < E) ? offsets[e + 1] - offsets[e] : 0;
-    const bool heavy = n > light_max;
+    int lm = light_max;
+    if (lm == kLightAdaptive) {  // uniform: every thread takes this branch or none
+        int tch = n > 0 ? 1 : 0;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) tch += __shfl_xor(tch, o, 64);
+        if (lane == 0) wtouch[wave] = tch;
+        __syncthreads();
+        int touched = 0;
+        for (int w = 0; w < nwave; ++w) touched += wtouch[w];
+        lm = adaptive_light_max(offsets[E] - offsets[0], touched);
+    }
+    const bool heavy = n > lm;
     int c[3] = {heavy ? (n + kTileTM0 - 1) / kTileTM0 : 0, heavy ? (n + kTileTM1 - 1) / kTileTM1 : 0,
                 heavy ? (n + kTileTM2 - 1) / kTileTM2 : 0};
 #pragma unroll
@@ -79,7 +90,7 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restric
     }
     const int tm = force_tm ? force_tm : tile_height(pick_tile_height(tot[0], tot[1], tot[2]));
 
-    const int is_light = (n >= 1 && n <= light_max) ? 1 : 0;
+    const int is_light = (n >= 1 && n <= lm) ? 1 : 0;
     const int nt = heavy ? (n + tm - 1) / tm : 0;
     int il = is_light, it = nt;
 #pragma unroll

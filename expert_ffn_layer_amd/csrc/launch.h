@@ -55,6 +55,21 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* chun
 
 // ---- grouped FFN --------------------------------------------------------
 constexpr int kLightRowsMax = 64;  // up to four 16-row MFMA sub-tiles
+// light_max given to the plan kernels: >= 0 a fixed threshold (experts with
+// 1..light_max rows take the light loop); kLightAdaptive decides per call on
+// the device: when the routed rows average at most MOE_LIGHT_MEAN_ROWS per
+// touched expert, experts with up to kLightRowsMax rows take the light loop,
+// otherwise every expert takes the heavy tiles.  (Measured on MI355X: the
+// heavy tiles stream a small expert's weights about as fast as the light
+// loop, and splitting one call between the two loops, or light experts of
+// 17..64 rows, costs up to 40% at 10..80 rows per expert.)
+constexpr int kLightAdaptive = -1;
+#ifndef MOE_LIGHT_MEAN_ROWS
+#define MOE_LIGHT_MEAN_ROWS 8
+#endif
+inline __host__ __device__ int adaptive_light_max(long long rows, long long touched) {
+    return rows <= (long long)MOE_LIGHT_MEAN_ROWS * touched ? kLightRowsMax : 0;
+}
 // Heavy tiles are 256 columns wide and 256, 192 or 128 rows high; one height
 // per launch, the one with the least estimated time for the actual expert
 // row counts: sum_e ceil(n_e / tm) * tm * cost(tm), cost = relative time per

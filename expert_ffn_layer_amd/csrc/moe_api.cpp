@@ -83,11 +83,20 @@ Layout layout(const moe_shape* s) {
     const long long T = s->T, H = s->H, E = s->E, k = s->k, I = s->I, A = T * k;
     L.splits = router_splits(s->T, s->H, s->E);
     L.nchunks = (int)std::max<long long>(1, (A + moe::kPermChunk - 1) / moe::kPermChunk);
-    L.light_max = s->light_max_rows < 0 ? moe::kLightRowsMax : s->light_max_rows;
     // Each token picks k distinct experts, so no expert gets more than T rows:
     // with T <= light_max every expert is light and no heavy tile can exist.
-    L.max_tiles = (T <= L.light_max) ? 0 : moe::max_heavy_tiles(A, s->E, L.light_max);
-    L.max_light = L.light_max > 0 ? (int)std::min<long long>(E, A) : 0;
+    // The default is the per-call choice on the device (kLightAdaptive) from
+    // 65 tokens on, with grids sized for either outcome; up to 64 tokens
+    // every expert is light and no heavy kernel is launched.
+    if (s->light_max_rows < 0) {
+        L.light_max = T <= moe::kLightRowsMax ? moe::kLightRowsMax : moe::kLightAdaptive;
+        L.max_tiles = T <= moe::kLightRowsMax ? 0 : moe::max_heavy_tiles(A, s->E, 0);
+        L.max_light = (int)std::min<long long>(E, A);
+    } else {
+        L.light_max = s->light_max_rows;
+        L.max_tiles = (T <= L.light_max) ? 0 : moe::max_heavy_tiles(A, s->E, L.light_max);
+        L.max_light = L.light_max > 0 ? (int)std::min<long long>(E, A) : 0;
+    }
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;

@@ -260,12 +260,19 @@ __global__ __launch_bounds__(kThreads) void perm_small_kernel(
     }
 
     if (!plan) return;
+    int lm = light_max;
+    if (lm == kLightAdaptive) {  // uniform: every thread takes this branch or none
+        int touched = 0;
+        (void)block256_exclusive_scan((c[0] > 0) + (c[1] > 0) + (c[2] > 0) + (c[3] > 0), wsum,
+                                      &touched);
+        lm = adaptive_light_max(total, touched);
+    }
     // Heavy tile height: the cheapest for these counts (same rule as
     // ffn_plan_kernel).
     int t0 = 0, t1 = 0, t2 = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        if (c[j] > light_max) {
+        if (c[j] > lm) {
             t0 += (c[j] + kTileTM0 - 1) / kTileTM0;
             t1 += (c[j] + kTileTM1 - 1) / kTileTM1;
             t2 += (c[j] + kTileTM2 - 1) / kTileTM2;
@@ -279,8 +286,8 @@ __global__ __launch_bounds__(kThreads) void perm_small_kernel(
     int lj[4], tj[4], lsum = 0, tsum = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        lj[j] = (c[j] >= 1 && c[j] <= light_max) ? 1 : 0;
-        tj[j] = (c[j] > light_max) ? (c[j] + tile_rows - 1) / tile_rows : 0;
+        lj[j] = (c[j] >= 1 && c[j] <= lm) ? 1 : 0;
+        tj[j] = (c[j] > lm) ? (c[j] + tile_rows - 1) / tile_rows : 0;
         lsum += lj[j];
         tsum += tj[j];
     }

@@ -38,6 +38,22 @@ KERNEL_ID = {n: i for i, n in enumerate(KERNELS)}
 # Experts with 1..LIGHT_MAX_ROWS rows take the light loop when
 # light_max_rows is left at -1 (the C ABI's default).
 LIGHT_MAX_ROWS = 64
+LIGHT_MEAN_ROWS = 8  # the default's device-side rule (moe_shape.light_max_rows = -1)
+
+
+def light_experts(counts, shape):
+    """Boolean mask of the experts that take the light loop for these routing
+    counts (numpy int array [E]), the rule the library's plan applies."""
+    import numpy as np
+    counts = np.asarray(counts)
+    lm = shape.light_max_rows
+    if lm < 0:
+        if shape.T <= LIGHT_MAX_ROWS:
+            lm = LIGHT_MAX_ROWS
+        else:
+            touched = int((counts > 0).sum())
+            lm = LIGHT_MAX_ROWS if int(counts.sum()) <= LIGHT_MEAN_ROWS * touched else 0
+    return (counts >= 1) & (counts <= lm)
 
 
 class MoeShape(ctypes.Structure):

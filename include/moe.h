@@ -76,10 +76,17 @@ typedef struct moe_shape {
     int32_t I;              /* routed expert intermediate size */
     int32_t I_shared;       /* shared expert intermediate size; 0 = no shared expert */
     int32_t renorm;         /* 1: selected weights renormalised to sum to 1; 0: raw probabilities */
-    int32_t light_max_rows; /* experts with 1..light_max_rows rows take the light-row loop;
-                               -1 = library default (64); 0 = every expert takes the
-                               heavy tiles; at most 64.  An expert never gets more than T
-                               rows, so with T <= light_max_rows no heavy kernel runs. */
+    int32_t light_max_rows; /* experts with 1..light_max_rows rows take the light-row loop,
+                               the others the heavy tiles; 0 = every expert takes the heavy
+                               tiles; at most 64.  An expert never gets more than T rows,
+                               so with T <= light_max_rows no heavy kernel runs.
+                               -1 = library default: with T <= 64 every expert takes the
+                               light loop (no heavy kernel runs); with more tokens the
+                               device decides per call from the routing: experts with up
+                               to 64 rows take the light loop when the routed rows
+                               average at most 8 per touched expert, otherwise every
+                               expert takes the heavy tiles (faster on MI355X from about
+                               10 rows per expert on).  Results do not depend on it. */
     int32_t heavy_tile_rows; /* rows per heavy tile: 0 = chosen per call from the expert
                                row counts (the least padded-row time); 128, 192 or 256
                                = that height.  Results do not depend on it. */

@@ -94,6 +94,24 @@ def test_tile_heights_bitwise(oracle_lib, y_bf16):
     log(f"tiles/192/bf16y={y_bf16}", rep)
 
 
+@pytest.mark.parametrize("T,E,k,light", [(300, 512, 10, True), (300, 64, 10, False),
+                                         (1000, 512, 10, False), (500, 1024, 10, True)])
+def test_default_light_rule_bitwise(oracle_lib, T, E, k, light):
+    """The default's per-call light/heavy choice (decided on the device, in
+    the one-block permute for T*k <= 4096 and in the plan kernel above) gives
+    the bits of both fixed choices, and matches the oracle."""
+    print(f"[case] default light rule T={T} E={E} k={k}", flush=True)
+    cfg = custom(f"rule{T}_{E}", T=T, H=256, E=E, k=k, I=64)
+    lay = layer_on_gpu(cfg)
+    outs = {lm: gh.gpu_forward(lay, light_max_rows=lm) for lm in (-1, 0, 64)}
+    s = moe.make_shape(T, 256, E, k, 64)
+    assert bool(moe.light_experts(outs[-1]["counts"], s).any()) == light
+    for lm in (0, 64):
+        assert np.array_equal(outs[-1]["out"].view(np.int32), outs[lm]["out"].view(np.int32))
+    rep = gh.check_layer(oracle_lib, lay)
+    log(f"rule{T}_{E}", rep)
+
+
 @pytest.mark.parametrize("tm", [128, 192, 256])
 def test_forward_heavy_ragged_heights(oracle_lib, tm):
     print(f"[case] heavy_ragged tm={tm}", flush=True)
