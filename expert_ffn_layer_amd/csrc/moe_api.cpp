@@ -88,9 +88,20 @@ Layout layout(const moe_shape* s) {
     // The default is the per-call choice on the device (kLightAdaptive) from
     // 65 tokens on, with grids sized for either outcome; up to 64 tokens
     // every expert is light and no heavy kernel is launched.
-    if (s->light_max_rows < 0) {
-        L.light_max = T <= moe::kLightRowsMax ? moe::kLightRowsMax : moe::kLightAdaptive;
-        L.max_tiles = T <= moe::kLightRowsMax ? 0 : moe::max_heavy_tiles(A, s->E, 0);
+    if (s->light_max_rows < 0 && T <= moe::kLightRowsMax) {
+        L.light_max = moe::kLightRowsMax;
+        L.max_tiles = 0;
+        L.max_light = (int)std::min<long long>(E, A);
+    } else if (s->light_max_rows < 0 && moe::adaptive_light_max(A, E) == 0) {
+        // No more than E experts are touched, so beyond MOE_LIGHT_MEAN_ROWS * E
+        // routed rows the rule always picks the heavy tiles: fix that choice
+        // (light kernels not launched at all).
+        L.light_max = 0;
+        L.max_tiles = moe::max_heavy_tiles(A, s->E, 0);
+        L.max_light = 0;
+    } else if (s->light_max_rows < 0) {
+        L.light_max = moe::kLightAdaptive;
+        L.max_tiles = moe::max_heavy_tiles(A, s->E, 0);
         L.max_light = (int)std::min<long long>(E, A);
     } else {
         L.light_max = s->light_max_rows;

@@ -50,6 +50,8 @@ def light_experts(counts, shape):
     if lm < 0:
         if shape.T <= LIGHT_MAX_ROWS:
             lm = LIGHT_MAX_ROWS
+        elif shape.T * shape.k > LIGHT_MEAN_ROWS * shape.E:
+            lm = 0  # more rows than the rule can ever send to the light loop
         else:
             touched = int((counts > 0).sum())
             lm = LIGHT_MAX_ROWS if int(counts.sum()) <= LIGHT_MEAN_ROWS * touched else 0

@@ -86,7 +86,8 @@ typedef struct moe_shape {
                                to 64 rows take the light loop when the routed rows
                                average at most 8 per touched expert, otherwise every
                                expert takes the heavy tiles (faster on MI355X from about
-                               10 rows per expert on).  Results do not depend on it. */
+                               10 rows per expert on); with T*k > 8*E always the heavy
+                               tiles.  Results do not depend on it. */
     int32_t heavy_tile_rows; /* rows per heavy tile: 0 = chosen per call from the expert
                                row counts (the least padded-row time); 128, 192 or 256
                                = that height.  Results do not depend on it. */
