@@ -1,7 +1,7 @@
 // Grouped expert FFN on bf16 MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulate).
 //
 //   gate|up:  h[r, i] = bf16( silu(x[tok_r] . Wg[e,i]) * (x[tok_r] . Wu[e,i]) )
-//   down:     y[r, c] = h[r] . Wd[e,c]            (fp32)
+//   down:     y[r, c] = h[r] . Wd[e,c]            (fp32 sum; stored fp32 or bf16)
 //
 // for the expert-major rows r of expert e (pwwt.cn article on Qwen 3.5-397B
 // MoE on Ironwood, section 4.2: grouped GEMM with SwiGLU fused into the
@@ -17,6 +17,8 @@
 //    straight from HBM into registers (from the packed lane-order chunks when
 //    given, one contiguous run per wave) and keeps one accumulator per
 //    16-row sub-tile.  This is the decode path: it is bound by weight bytes.
+//    Which experts take it is the plan's choice (light_max; by default a
+//    per-call rule that sends every expert one way, see launch.h).
 //    Its gate|up tiles hold 8 gate rows and the 8 matching up rows, so lanes
 //    n and n+8 carry g and u of one h column (one lane shuffle).
 //  * heavy: TM x 256 output tiles (TM = 256, 192 or 128, chosen from the row

@@ -34,7 +34,7 @@ constexpr size_t kAlign = 256;
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    int splits = 1, nchunks = 1, light_max = 16, max_tiles = 0, max_light = 0;
+    int splits = 1, nchunks = 1, light_max = 0, max_tiles = 0, max_light = 0;
     size_t part = 0, ids = 0, w = 0, chunk = 0, counts = 0, offsets = 0, sorted = 0, inv = 0,
            plan = 0, h = 0, y = 0, hs = 0, total = 0;
 };
