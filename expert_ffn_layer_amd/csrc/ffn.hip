@@ -59,7 +59,7 @@ constexpr int kThreads = 256;
 __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restrict__ offsets,
                                                         int E, int light_max, int force_tm,
                                                         int32_t* __restrict__ plan) {
-    __shared__ int wl[16], wt[16], wc[3][16], wtouch[16];
+    __shared__ int wl[16], wt[16], wcs[16], wtouch[16];
     const int e = threadIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
     const int n = (e < E) ? offsets[e + 1] - offsets[e] : 0;
@@ -75,56 +75,54 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restric
         lm = adaptive_light_max(offsets[E] - offsets[0], touched);
     }
     const bool heavy = n > lm;
-    int c[3] = {heavy ? (n + kTileTM0 - 1) / kTileTM0 : 0, heavy ? (n + kTileTM1 - 1) / kTileTM1 : 0,
-                heavy ? (n + kTileTM2 - 1) / kTileTM2 : 0};
-#pragma unroll
-    for (int q = 0; q < 3; ++q) {
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) c[q] += __shfl_xor(c[q], o, 64);
-        if (lane == 0) wc[q][wave] = c[q];
-    }
-    __syncthreads();
-    long long tot[3] = {0, 0, 0};
-    for (int w = 0; w < nwave; ++w) {
-        tot[0] += wc[0][w];
-        tot[1] += wc[1][w];
-        tot[2] += wc[2][w];
-    }
-    const int tm = force_tm ? force_tm : tile_height(pick_tile_height(tot[0], tot[1], tot[2]));
-
+    int nt = 0, main_tmi = 0, last_tmi = 0;
+    if (heavy) tile_split(n, force_tm, nt, main_tmi, last_tmi);
     const int is_light = (n >= 1 && n <= lm) ? 1 : 0;
-    const int nt = heavy ? (n + tm - 1) / tm : 0;
-    int il = is_light, it = nt;
+    const int cost = tiles_cost_units(nt, main_tmi, last_tmi);
+    int il = is_light, it = nt, ic = cost;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
         const int vl = __shfl_up(il, o, 64);
         const int vt = __shfl_up(it, o, 64);
+        const int vc = __shfl_up(ic, o, 64);
         if (lane >= o) {
             il += vl;
             it += vt;
+            ic += vc;
         }
     }
     if (lane == 63) {
         wl[wave] = il;
         wt[wave] = it;
+        wcs[wave] = ic;
     }
     __syncthreads();
-    int bl = 0, bt = 0;
-    for (int w = 0; w < wave; ++w) {
-        bl += wl[w];
-        bt += wt[w];
+    int bl = 0, bt = 0, bc = 0, ctot = 0;
+    for (int w = 0; w < nwave; ++w) {
+        if (w < wave) {
+            bl += wl[w];
+            bt += wt[w];
+            bc += wcs[w];
+        }
+        ctot += wcs[w];
     }
     const int el = bl + il - is_light, et = bt + it - nt;
+    xcd_bounds(plan, et, nt, main_tmi, last_tmi, bc + ic - cost, ctot);
     if (is_light) plan[kPlanHeader + el] = e;
     int32_t* tiles = plan + kPlanHeader + E;
+    const int tm = tile_height(main_tmi);
     for (int i = 0; i < nt; ++i) {
         tiles[2 * (et + i)] = e;
-        tiles[2 * (et + i) + 1] = i * tm;
+        tiles[2 * (et + i) + 1] = (i * tm) | ((i + 1 < nt ? main_tmi : last_tmi) << kTileTmShift);
     }
     if (threadIdx.x == blockDim.x - 1) {
         plan[0] = el + is_light;
         plan[1] = et + nt;
-        plan[2] = tm;
+        plan[2] = force_tm;
+        plan[kPlanXcdBounds] = 0;
+        plan[kPlanXcdBounds + kXcds] = et + nt;
+        if (ctot == 0)
+            for (int x = 1; x < kXcds; ++x) plan[kPlanXcdBounds + x] = 0;
     }
 }
 
@@ -463,9 +461,6 @@ constexpr int kHeavyThreads = 512;
 constexpr int kHeavyWaves = kHeavyThreads / 64;
 constexpr int kTN = 256;       // B rows per tile (output columns, or 128 gate + 128 up rows)
 constexpr int kWTN = kTN / 4;  // 64 columns per wave
-#ifndef MOE_HEAVY_XCD_SLICES
-#define MOE_HEAVY_XCD_SLICES 8
-#endif
 // LDS rings: A (rows of x or h) two stages deep, except three for the down
 // GEMM's 256-row tiles (measured 1.7% faster; 3% slower for gate|up); B
 // (expert weights) two deep with 256-row tiles and three deep with 192- and
@@ -476,6 +471,7 @@ constexpr int kWTN = kTN / 4;  // 64 columns per wave
 // 3% there and gains 7% on streamed weights).  At most one of the two rings
 // is three deep: 160 KB of LDS.
 constexpr int kKS = 64;            // K values per stage
+constexpr int kHeavyLds = 160 * 1024;  // LDS of the heavy kernels: the largest ring below
 constexpr int kBlk = 1024;         // bytes of one 8-row x 64-K block
 constexpr int kBlocksB = kTN / 8;  // 32
 constexpr int kBBlkPerWave = kBlocksB / kHeavyWaves;  // 4
@@ -492,8 +488,6 @@ struct HeavyGeom {
     static constexpr int kAStages = (TM == 256 && M == Mode::Down) ? 3 : 2;
     // LDS 128 (gate|up) or 160 (down), 144, 128 KB
 };
-constexpr int kXcds = MOE_HEAVY_XCD_SLICES;
-  // MI355X: 8 XCDs, workgroups dispatched round-robin
 
 typedef __attribute__((address_space(3))) void* lptr_t;
 
@@ -529,14 +523,25 @@ __device__ __forceinline__ void ring_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Height index (0, 1, 2 for kTileTM0/1/2) of row tile `tile`: from the
+// plan's tile list, or the dense group's one height.
+__device__ __forceinline__ int tile_tmi(const FfnArgs& a, int tile) {
+    if (a.plan)
+        return (int)((uint32_t)a.plan[kPlanHeader + a.E + 2 * tile + 1] >> kTileTmShift);
+    return a.dense_tm == kTileTM0 ? 0 : (a.dense_tm == kTileTM1 ? 1 : 2);
+}
+
+// Runs this block's work items wi, wi + nb_x, ... (below wend) while their
+// row tiles are TM rows high, and returns the first item of another height
+// (or one at or past wend).
 // YB (down only): y stored as bf16 instead of fp32 (a.y_bf16).
 template <Mode M, int TM, bool YB>
-__global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
+__device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, long long wi,
+                                                 long long wend, int nb_x, int nblk) {
     using G = HeavyGeom<M, TM>;
     constexpr int kRF = G::kRF, kBlocksA = G::kBlocksA, kABlk = G::kABlkPerWave;
     constexpr int kABytes = G::kABytes;
-    // One height per launch: the plan (or the host, for a dense group) names it.
-    if ((a.plan ? a.plan[2] : a.dense_tm) != TM) return;
+    constexpr int kTmi = TM == kTileTM0 ? 0 : (TM == kTileTM1 ? 1 : 2);
     // One LDS object for both rings (A stages, then B stages): with two
     // objects the compiler waits for every LDS DMA before any LDS read.
     constexpr int kBBytes = kBlocksB * kBlk;
@@ -544,19 +549,15 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
     static_assert(ast == 2 || bst == 2, "one ring at most is three deep");
     // Instructions per wave of the deeper ring's stage (0: both two deep).
     constexpr int kDeepBlk = ast > 2 ? kABlk : (bst > 2 ? kBBlkPerWave : 0);
-    __shared__ __attribute__((aligned(1024))) char lds[ast * kABytes + bst * kBBytes];
+    static_assert(ast * kABytes + bst * kBBytes <= kHeavyLds, "LDS rings");
     // Stage st's A lives in slot st % ast, its B in slot st % bst; both slot
     // indices are carried along (no division in the loop).
     auto a_slot = [&](int slot) -> char* { return lds + slot * kABytes; };
     auto b_slot = [&](int slot) -> char* { return lds + ast * kABytes + slot * kBBytes; };
 
-    const int N = (M == Mode::GateUp) ? 2 * a.I : a.H;
     // split_h: the down GEMM's K runs over [hi | lo] (2I) against W_down twice.
     const int K = (M == Mode::GateUp) ? a.H : (a.split_h ? 2 * a.I : a.I);
     const int hstride = a.split_h ? 2 * a.I : a.I;  // row pitch of h
-    const int nblk = (N + kTN - 1) / kTN;
-    const int ntiles = a.plan ? a.plan[1] : (a.dense_rows + TM - 1) / TM;
-    const long long nwork = (long long)ntiles * nblk;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: LDS offsets in SGPRs
     const int wm = wave >> 2, wn = wave & 3;
@@ -574,19 +575,6 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
     const int foff0 = fblk * kBlk + frow * 128 + ((g ^ frow) << 4);
     const int foff1 = fblk * kBlk + frow * 128 + (((g + 4) ^ frow) << 4);
 
-    // XCD-aware static schedule.  The work list is tile-major (tiles of one
-    // expert are adjacent) with the N block fastest; it is cut into nslice
-    // contiguous slices and slice x is served, round-robin, by the blocks that
-    // share XCD x (blockIdx % nslice), so the M and N tiles of one expert run
-    // at the same time on one XCD and share weights and rows through its L2.
-    const int nslice = min(kXcds, (int)gridDim.x);
-    const int xs = blockIdx.x % nslice;
-    const int nb_x = ((int)gridDim.x - xs + nslice - 1) / nslice;
-    const int jx = blockIdx.x / nslice;
-    const long long per = (nwork + nslice - 1) / nslice;
-    const long long wbeg = xs * per;
-    const long long wend = min(nwork, wbeg + per);
-
     // Per-tile state: output block nb of row tile (e, m0); rows of the tile
     // that exist; buffer resources and per-lane byte offsets of the loads.
     int nb = 0, e = 0, r0 = 0, m0 = 0, rows = 0;
@@ -598,7 +586,7 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
         if (a.plan) {
             const int32_t* tl = a.plan + kPlanHeader + a.E;
             e = tl[2 * tile];
-            m0 = tl[2 * tile + 1];
+            m0 = tl[2 * tile + 1] & kTileRowMask;
             r0 = a.offsets[e];
             rows = min(TM, a.offsets[e + 1] - r0 - m0);
         } else {
@@ -720,12 +708,9 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
         for (int i = i0; i < i1; ++i) af[i] = rd_a(slot, half, (wm * kRF + i) * 2);
     };
 
-    long long wi = wbeg + jx;
-    if (wi < wend) {
-        setup(wi);
-        issue_first();
-    }
-    while (wi < wend) {
+    setup(wi);
+    issue_first();
+    while (true) {
         floatx4_t acc[kRF][4];
 #pragma unroll
         for (int i = 0; i < kRF; ++i)
@@ -819,7 +804,8 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
         const int row0 = wm * (TM / 2) + 4 * g;
         const int t_nb = nb, t_base = r0 + m0, t_rows = rows;
         const long long wnext = wi + nb_x;
-        if (wnext < wend) setup(wnext);
+        const bool more = wnext < wend && tile_tmi(a, (int)(wnext / nblk)) == kTmi;
+        if (more) setup(wnext);
         if constexpr (M == Mode::GateUp) {
             const int hc0 = t_nb * (kTN / 2) + wn * 32 + l16;
             uint16_t* hp = a.h + (size_t)(t_base + row0) * hstride + hc0;
@@ -889,7 +875,52 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
         }
 
         wi = wnext;
-        if (wi < wend) issue_first();
+        if (!more) break;
+        issue_first();
+    }
+    return wi;
+}
+
+// One launch per GEMM: every row tile runs with the body of its own height
+// (the plan mixes heights within an expert); the bodies share one LDS
+// allocation, the largest ring.
+template <Mode M, bool YB>
+__global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
+    __shared__ __attribute__((aligned(1024))) char lds[kHeavyLds];
+    const int N = (M == Mode::GateUp) ? 2 * a.I : a.H;
+    const int nblk = (N + kTN - 1) / kTN;
+    const int ntiles = a.plan ? a.plan[1] : (a.dense_rows + a.dense_tm - 1) / a.dense_tm;
+    const long long nwork = (long long)ntiles * nblk;
+
+    // XCD-aware static schedule.  The work list is tile-major (tiles of one
+    // expert are adjacent) with the N block fastest; it is cut into nslice
+    // contiguous slices and slice x is served, round-robin, by the blocks that
+    // share XCD x (blockIdx % nslice), so the M and N tiles of one expert run
+    // at the same time on one XCD and share weights and rows through its L2.
+    const int nslice = min(kXcds, (int)gridDim.x);
+    const int xs = blockIdx.x % nslice;
+    const int nb_x = ((int)gridDim.x - xs + nslice - 1) / nslice;
+    const int jx = blockIdx.x / nslice;
+    long long wbeg, wend;
+    if (a.plan && nslice == kXcds) {
+        // slices of about equal cost from the plan (tile heights differ)
+        wbeg = (long long)a.plan[kPlanXcdBounds + xs] * nblk;
+        wend = (long long)a.plan[kPlanXcdBounds + xs + 1] * nblk;
+    } else {
+        const long long per = (nwork + nslice - 1) / nslice;
+        wbeg = xs * per;
+        wend = min(nwork, wbeg + per);
+    }
+
+    long long wi = wbeg + jx;
+    while (wi < wend) {
+        const int tmi = tile_tmi(a, (int)(wi / nblk));
+        if (tmi == 0)
+            wi = ffn_heavy_run<M, kTileTM0, YB>(a, lds, wi, wend, nb_x, nblk);
+        else if (tmi == 1)
+            wi = ffn_heavy_run<M, kTileTM1, YB>(a, lds, wi, wend, nb_x, nblk);
+        else
+            wi = ffn_heavy_run<M, kTileTM2, YB>(a, lds, wi, wend, nb_x, nblk);
     }
 }
 
@@ -942,20 +973,15 @@ hipError_t launch_heavy(const FfnArgs& a, int ncols, hipStream_t st) {
     if (a.plan) {
         if (a.max_tiles <= 0) return hipSuccess;
         const int grid = grid_for((long long)a.max_tiles * nblk, 1, a.num_cu);
-        ffn_heavy_kernel<M, kTileTM0, YB><<<grid, kHeavyThreads, 0, st>>>(a);
-        ffn_heavy_kernel<M, kTileTM1, YB><<<grid, kHeavyThreads, 0, st>>>(a);
-        ffn_heavy_kernel<M, kTileTM2, YB><<<grid, kHeavyThreads, 0, st>>>(a);
+        ffn_heavy_kernel<M, YB><<<grid, kHeavyThreads, 0, st>>>(a);
         return hipGetLastError();
     }
     if (a.dense_rows <= 0) return hipSuccess;
     const long long tiles = (a.dense_rows + a.dense_tm - 1) / a.dense_tm;
     const int grid = grid_for(tiles * nblk, 1, a.num_cu);
-    switch (a.dense_tm) {
-        case kTileTM0: ffn_heavy_kernel<M, kTileTM0, YB><<<grid, kHeavyThreads, 0, st>>>(a); break;
-        case kTileTM1: ffn_heavy_kernel<M, kTileTM1, YB><<<grid, kHeavyThreads, 0, st>>>(a); break;
-        case kTileTM2: ffn_heavy_kernel<M, kTileTM2, YB><<<grid, kHeavyThreads, 0, st>>>(a); break;
-        default: return hipErrorInvalidValue;
-    }
+    if (a.dense_tm != kTileTM0 && a.dense_tm != kTileTM1 && a.dense_tm != kTileTM2)
+        return hipErrorInvalidValue;
+    ffn_heavy_kernel<M, YB><<<grid, kHeavyThreads, 0, st>>>(a);
     return hipGetLastError();
 }
 

@@ -70,10 +70,11 @@ constexpr int kLightAdaptive = -1;
 inline __host__ __device__ int adaptive_light_max(long long rows, long long touched) {
     return rows <= (long long)MOE_LIGHT_MEAN_ROWS * touched ? kLightRowsMax : 0;
 }
-// Heavy tiles are 256 columns wide and 256, 192 or 128 rows high; one height
-// per launch, the one with the least estimated time for the actual expert
-// row counts: sum_e ceil(n_e / tm) * tm * cost(tm), cost = relative time per
-// tile row (x1000, measured: smaller tiles re-read more weights per row).
+// Heavy tiles are 256 columns wide and 256, 192 or 128 rows high.  Each
+// expert's rows are cut into the tiles of least estimated time, sum over its
+// tiles of tm * cost(tm), cost = relative time per tile row (x1000, measured:
+// smaller tiles re-read more weights per row): all of one height, or 256-row
+// tiles and one smaller last tile for the remainder.
 #ifndef MOE_TILE_COST_192
 #define MOE_TILE_COST_192 1060
 #endif
@@ -92,9 +93,85 @@ inline __host__ __device__ int pick_tile_height(long long t0, long long t1, long
 inline __host__ __device__ int tile_height(int idx) {
     return idx == 0 ? kTileTM0 : (idx == 1 ? kTileTM1 : kTileTM2);
 }
-// Plan layout (int32): [0] n_light, [1] n_tiles, [2] tile height, [16 ..16+E)
-// light expert ids, [16+E ..) heavy tiles as (expert, first row) pairs.
+inline __host__ __device__ int tile_cost(int idx) {
+    return idx == 0 ? kTileCost0 : (idx == 1 ? kTileCost1 : kTileCost2);
+}
+// Plan layout (int32): [0] n_light, [1] n_tiles, [2] forced tile height or 0,
+// [16 ..16+E) light expert ids, [16+E ..) heavy tiles as (expert, first row
+// | height index << kTileTmShift) pairs; height index 0, 1, 2 = kTileTM0/1/2.
 constexpr int kPlanHeader = 16;
+// MI355X: 8 XCDs, workgroups dispatched round-robin.  The heavy work list is
+// cut into kXcds contiguous slices of about equal cost; plan[kPlanXcdBounds
+// + x] is the first tile of slice x (x = 0..kXcds, the last = n_tiles).
+#ifndef MOE_HEAVY_XCD_SLICES
+#define MOE_HEAVY_XCD_SLICES 8
+#endif
+constexpr int kXcds = MOE_HEAVY_XCD_SLICES;
+constexpr int kPlanXcdBounds = 3;
+static_assert(kPlanXcdBounds + kXcds + 1 <= kPlanHeader, "plan header");
+constexpr int kTileTmShift = 29;
+constexpr int kTileRowMask = (1 << kTileTmShift) - 1;
+inline __host__ __device__ int tile_tm_index(int tm) {
+    return tm == kTileTM0 ? 0 : (tm == kTileTM1 ? 1 : 2);
+}
+// Relative time of one tile of height index tmi (tm * cost(tm) / 16000).
+inline __host__ __device__ int tile_cost_units(int tmi) {
+    return tmi == 0 ? 16 : (tmi == 1 ? 13 : 10);
+}
+inline __host__ __device__ int tiles_cost_units(int nt, int main_tmi, int last_tmi) {
+    return nt > 0 ? (nt - 1) * tile_cost_units(main_tmi) + tile_cost_units(last_tmi) : 0;
+}
+// The XCD slice bounds that fall in one expert's tiles [t0, t0 + nt), whose
+// cost before them is cb out of a total C: slice x - 1 ends after the first
+// tile at which the cumulative cost reaches ceil(x C / kXcds).
+inline __host__ __device__ void xcd_bounds(int32_t* plan, int t0, int nt, int main_tmi,
+                                           int last_tmi, long long cb, long long C) {
+    const long long ce = cb + tiles_cost_units(nt, main_tmi, last_tmi);
+    for (int x = 1; x < kXcds; ++x) {
+        const long long target = (C * x + kXcds - 1) / kXcds;
+        if (target <= cb || target > ce) continue;
+        long long cum = cb;
+        int i = 0;
+        for (; i < nt; ++i) {
+            cum += tile_cost_units(i + 1 < nt ? main_tmi : last_tmi);
+            if (cum >= target) break;
+        }
+        plan[kPlanXcdBounds + x] = t0 + i + 1;
+    }
+}
+// Tiles of an expert with n heavy rows: ntiles tiles, all main_tmi high but
+// the last, last_tmi high (first rows 0, tm, 2 tm, ... with tm of main_tmi).
+// force_tm (128, 192, 256) puts every tile at that height.
+inline __host__ __device__ void tile_split(int n, int force_tm, int& ntiles, int& main_tmi,
+                                           int& last_tmi) {
+    if (force_tm) {
+        main_tmi = last_tmi = tile_tm_index(force_tm);
+        ntiles = (n + force_tm - 1) / force_tm;
+        return;
+    }
+    long long best = -1;
+    for (int i = 0; i < 3; ++i) {
+        const int tm = tile_height(i);
+        const int k = (n + tm - 1) / tm;
+        const long long c = (long long)k * tm * tile_cost(i);
+        if (best < 0 || c < best) {
+            best = c;
+            ntiles = k;
+            main_tmi = last_tmi = i;
+        }
+    }
+    const int q = n / kTileTM0, rem = n - q * kTileTM0;
+    if (q > 0 && rem > 0) {
+        const int r = rem <= kTileTM2 ? 2 : (rem <= kTileTM1 ? 1 : 0);
+        const long long c =
+            (long long)q * kTileTM0 * kTileCost0 + (long long)tile_height(r) * tile_cost(r);
+        if (c < best) {
+            ntiles = q + 1;
+            main_tmi = 0;
+            last_tmi = r;
+        }
+    }
+}
 
 int max_heavy_tiles(long long A, int E, int light_max);
 int dense_tile_height(int rows);  // tile height for a dense group of `rows` rows

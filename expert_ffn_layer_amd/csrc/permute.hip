@@ -267,47 +267,43 @@ __global__ __launch_bounds__(kThreads) void perm_small_kernel(
                                       &touched);
         lm = adaptive_light_max(total, touched);
     }
-    // Heavy tile height: the cheapest for these counts (same rule as
-    // ffn_plan_kernel).
-    int t0 = 0, t1 = 0, t2 = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        if (c[j] > lm) {
-            t0 += (c[j] + kTileTM0 - 1) / kTileTM0;
-            t1 += (c[j] + kTileTM1 - 1) / kTileTM1;
-            t2 += (c[j] + kTileTM2 - 1) / kTileTM2;
-        }
-    }
-    int tot0 = 0, tot1 = 0, tot2 = 0;
-    (void)block256_exclusive_scan(t0, wsum, &tot0);
-    (void)block256_exclusive_scan(t1, wsum, &tot1);
-    (void)block256_exclusive_scan(t2, wsum, &tot2);
-    const int tile_rows = force_tm ? force_tm : tile_height(pick_tile_height(tot0, tot1, tot2));
-    int lj[4], tj[4], lsum = 0, tsum = 0;
+    // Heavy tiles per expert (tile_split, the rule of ffn_plan_kernel).
+    int lj[4], tj[4], tmain[4], tlast[4], lsum = 0, tsum = 0, csum = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         lj[j] = (c[j] >= 1 && c[j] <= lm) ? 1 : 0;
-        tj[j] = (c[j] > lm) ? (c[j] + tile_rows - 1) / tile_rows : 0;
+        tj[j] = 0;
+        tmain[j] = tlast[j] = 0;
+        if (c[j] > lm) tile_split(c[j], force_tm, tj[j], tmain[j], tlast[j]);
         lsum += lj[j];
         tsum += tj[j];
+        csum += tiles_cost_units(tj[j], tmain[j], tlast[j]);
     }
-    int ltot = 0, ttot = 0;
+    int ltot = 0, ttot = 0, ctot = 0;
     int lrun = block256_exclusive_scan(lsum, wsum, &ltot);
     int trun = block256_exclusive_scan(tsum, wsum, &ttot);
+    int crun = block256_exclusive_scan(csum, wsum, &ctot);
     int32_t* tiles = plan + kPlanHeader + E;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int e = 4 * threadIdx.x + j;
         if (lj[j]) plan[kPlanHeader + lrun++] = e;
+        xcd_bounds(plan, trun, tj[j], tmain[j], tlast[j], crun, ctot);
+        crun += tiles_cost_units(tj[j], tmain[j], tlast[j]);
+        const int tm = tile_height(tmain[j]);
         for (int i = 0; i < tj[j]; ++i, ++trun) {
             tiles[2 * trun] = e;
-            tiles[2 * trun + 1] = i * tile_rows;
+            tiles[2 * trun + 1] = (i * tm) | ((i + 1 < tj[j] ? tmain[j] : tlast[j]) << kTileTmShift);
         }
     }
     if (threadIdx.x == 0) {
         plan[0] = ltot;
         plan[1] = ttot;
-        plan[2] = tile_rows;
+        plan[2] = force_tm;
+        plan[kPlanXcdBounds] = 0;
+        plan[kPlanXcdBounds + kXcds] = ttot;
+        if (ctot == 0)
+            for (int x = 1; x < kXcds; ++x) plan[kPlanXcdBounds + x] = 0;
     }
 }
 
