@@ -88,9 +88,10 @@ typedef struct moe_shape {
                                expert takes the heavy tiles (faster on MI355X from about
                                10 rows per expert on); with T*k > 8*E always the heavy
                                tiles.  Results do not depend on it. */
-    int32_t heavy_tile_rows; /* rows per heavy tile: 0 = chosen per call from the expert
-                               row counts (the least padded-row time); 128, 192 or 256
-                               = that height.  Results do not depend on it. */
+    int32_t heavy_tile_rows; /* rows per heavy tile: 0 = chosen per expert from its row
+                               count (the least estimated time: one height, or 256-row
+                               tiles and a smaller last tile); 128, 192 or 256 = every
+                               tile that height.  Results do not depend on it. */
     int32_t y_bf16;         /* storage of the routed expert outputs y: 0 = fp32, 1 = bf16
                                (round to nearest even).  bf16 halves the y round trip
                                between the down GEMM and the combine (2*T*k*H bytes less
