@@ -13,8 +13,10 @@ Default workload: one decode step of a Qwen-3.5-like layer (T=64 tokens,
 H=4096, E=512 experts, top-10, I=1024, bf16 experts, fp32 router).
 
 Also reported:
-  roofline      the dominant kernel (largest summed duration), timed with HIP
-                events on its own launch stream over the timed region, against
+  roofline      the dominant kernel launch (largest duration; a kernel run twice
+                per step, as the heavy GEMMs with a shared expert, is timed per
+                launch), timed with HIP events on its own launch stream over
+                the timed region, against
                 the HBM (or bf16 MFMA) peak; traffic from committed rocprofv3
                 counter summaries when they match the current kernel source.
   cpu_baseline  the CPU oracle timed on this host on a bounded sample.
@@ -114,8 +116,7 @@ def summarize(args):
         with open(os.path.join(d, names[0])) as f:
             return list(csv.DictReader(f))
 
-    # A heavy GEMM call launches one kernel per tile height (all but the chosen
-    # one return at once): per call, durations and bytes add over heights.
+    # Instances of one kernel (template arguments) add up per call.
     stats = {}
     for r in one_csv(kt_dir, "kernel_stats.csv"):
         lab = kernel_label(r["Name"])
@@ -180,8 +181,8 @@ def summarize(args):
              "rocprofv3 summary of bench.py on one MI355X (gfx950).  Commands, from /tmp with",
              "TMPDIR=/tmp, $R the repository root:", "", "```", cmds, "```", "",
              f"Dominant kernel: **{dom}**, average {stats[dom]['avg_us']:.1f} us over "
-             f"{stats[dom]['calls']} calls (kernel trace; a heavy GEMM call is one launch per "
-             f"tile height, summed); bench.py's own HIP-event timing of it in the same run: "
+             f"{stats[dom]['calls']} calls (kernel trace); bench.py's own HIP-event timing of "
+             f"it in the same run: "
              f"{roof['kernel_us']:.1f} us.",
              "", f"bench line: {rec['value']:.1f} {rec['unit']}, {rec['ms_per_step']:.4f} ms/step; "
              f"roofline {roof['bound']} {roof['achieved']} {roof['unit']} "
@@ -269,21 +270,31 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # Untimed pass: per-kernel durations, to name the dominant kernel.
-    per_kernel = {}
+    # Untimed pass: per-kernel durations, to name the dominant launch.  A
+    # kernel launched more than once per step (the heavy GEMMs of a layer with
+    # a shared expert: routed experts, then the shared one) is timed launch by
+    # launch; its per-step time is the sum.
+    per_kernel, per_launch = {}, {}
     for name in moe.KERNELS:
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(2)]
-        launched = 0
-        for a, b in ev:
-            moe.profile_kernel(name, a, b)
-            step()
-            launched += moe.profile_launches()
+        a0, b0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        moe.profile_kernel(name, a0, b0)
+        step()
+        n_launch = moe.profile_launches()
         moe.profile_kernel(None)
         torch.cuda.synchronize()
-        if launched == len(ev):  # kernels this workload does not launch are left out
-            per_kernel[name] = sum(a.elapsed_time(b) for a, b in ev) / len(ev) * 1e3  # us
-    dominant = max(per_kernel, key=per_kernel.get)
+        if n_launch == 0:  # kernels this workload does not launch are left out
+            continue
+        for i in range(n_launch):
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(2)]
+            for a, b in ev:
+                moe.profile_kernel(name, a, b, launch=i)
+                step()
+            moe.profile_kernel(None)
+            torch.cuda.synchronize()
+            per_launch[(name, i)] = sum(a.elapsed_time(b) for a, b in ev) / len(ev) * 1e3  # us
+        per_kernel[name] = sum(v for (k, _), v in per_launch.items() if k == name)
+    dominant, dom_launch = max(per_launch, key=per_launch.get)
 
     # Timed region: K steps; the dominant kernel bracketed by events each step.
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -293,7 +304,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for a, b in evs:
-        moe.profile_kernel(dominant, a, b)
+        moe.profile_kernel(dominant, a, b, launch=dom_launch)
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -312,7 +323,14 @@ def main():
     H, I = cfg.H, cfg.I
     x_bytes = cfg.T * H * 2
     y_el = 2 if y_bf16 else 4  # bytes per stored y value
-    if dominant == "gateup_light":
+    Is = cfg.I_shared
+    if dominant == "gateup_heavy" and dom_launch == 1:  # the shared expert, dense over T
+        alg = 2 * Is * H * 2 + x_bytes + cfg.T * 2 * Is * 2  # h kept as a bf16 hi|lo pair
+        flops = 4 * cfg.T * H * Is
+    elif dominant == "down_heavy" and dom_launch == 1:
+        alg = H * Is * 2 + cfg.T * 2 * Is * 2 + cfg.T * H * 4
+        flops = 2 * cfg.T * H * Is
+    elif dominant == "gateup_light":
         alg = light_experts * 2 * I * H * 2 + x_bytes + light_rows * I * 2
         flops = 4 * light_rows * H * I
     elif dominant == "down_light":
@@ -331,6 +349,9 @@ def main():
     elif dominant == "router_gemm":
         alg = x_bytes + H * cfg.E * 4
         flops = 2 * cfg.T * H * cfg.E
+    elif dominant == "combine":
+        alg = A * H * y_el + cfg.T * H * 4 * (2 if Is else 1)  # out also read when accumulating
+        flops = 0
     else:
         alg, flops = 0, 0
     t_k = kern_us * 1e-6
@@ -339,7 +360,8 @@ def main():
     t_mfma = flops / (peak_flops * 1e12)
     src_hash = kernel_source_hash()
     workload = synth.workload_name(cfg)
-    traffic = committed_traffic(dominant, workload, src_hash)
+    # (committed counter summaries cover a kernel's first launch of a step)
+    traffic = committed_traffic(dominant, workload, src_hash) if dom_launch == 0 else None
     if t_mfma > t_hbm:
         achieved = flops / t_k / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_flops,
@@ -348,7 +370,8 @@ def main():
         achieved = alg / t_k / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof.update({"traffic": traffic, "kernel": dominant, "kernel_us": round(kern_us, 2),
+    roof.update({"traffic": traffic, "kernel": dominant, "launch": dom_launch,
+                 "kernel_us": round(kern_us, 2),
                  "algorithmic_bytes": int(alg), "flops": int(flops)})
 
     # Whole-layer roofline (weights of touched experts + x + router + out).

@@ -9,6 +9,7 @@ namespace moe {
 // ---- measurement hook (moe_profile_kernel) --------------------------------
 struct ProfileHook {
     int kernel = -1;
+    int which = -1;  // bracket only this launch (counted from the hook's setting), -1 = each
     hipEvent_t start = nullptr, stop = nullptr;
     long long launches = 0;
 };
@@ -16,12 +17,15 @@ extern ProfileHook g_profile;
 
 inline void prof_begin(int kernel, hipStream_t st) {
     if (g_profile.kernel == kernel) {
-        (void)hipEventRecord(g_profile.start, st);
+        if (g_profile.which < 0 || g_profile.launches == g_profile.which)
+            (void)hipEventRecord(g_profile.start, st);
         ++g_profile.launches;
     }
 }
 inline void prof_end(int kernel, hipStream_t st) {
-    if (g_profile.kernel == kernel) (void)hipEventRecord(g_profile.stop, st);
+    if (g_profile.kernel == kernel &&
+        (g_profile.which < 0 || g_profile.launches - 1 == g_profile.which))
+        (void)hipEventRecord(g_profile.stop, st);
 }
 
 // Kernel ids (same values as enum moe_kernel in moe.h).

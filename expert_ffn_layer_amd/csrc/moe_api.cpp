@@ -321,19 +321,25 @@ const char* moe_status_string(int status) {
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
-int moe_profile_kernel(int kernel, void* start, void* stop) {
+int moe_profile_kernel_launch(int kernel, int launch, void* start, void* stop) {
     g_last_error.clear();
     if (kernel == -1) {
         moe::g_profile = moe::ProfileHook{};
         return MOE_OK;
     }
     if (kernel < 0 || kernel >= MOE_K_COUNT) return fail(MOE_ERR_SHAPE, "unknown kernel id");
+    if (launch < -1) return fail(MOE_ERR_SHAPE, "launch must be -1 or >= 0");
     if (!start || !stop) return fail(MOE_ERR_NULL, "profile events are NULL");
     moe::g_profile.kernel = kernel;
+    moe::g_profile.which = launch;
     moe::g_profile.start = (hipEvent_t)start;
     moe::g_profile.stop = (hipEvent_t)stop;
     moe::g_profile.launches = 0;
     return MOE_OK;
+}
+
+int moe_profile_kernel(int kernel, void* start, void* stop) {
+    return moe_profile_kernel_launch(kernel, -1, start, stop);
 }
 
 long long moe_profile_launches(void) { return moe::g_profile.launches; }

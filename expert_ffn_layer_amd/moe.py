@@ -29,7 +29,7 @@ MOE_ERR_HIP = 6
 EXPORTED = ("moe_workspace_bytes", "moe_packed_weight_bytes", "moe_status_string",
             "moe_last_error", "moe_router", "moe_permute", "moe_pack_weights", "moe_grouped_ffn",
             "moe_shared_ffn", "moe_combine", "moe_forward", "moe_profile_kernel",
-            "moe_profile_launches")
+            "moe_profile_kernel_launch", "moe_profile_launches")
 
 # enum moe_kernel
 KERNELS = ("router_gemm", "router_select", "perm_count", "perm_scan", "perm_scatter", "ffn_plan",
@@ -101,10 +101,12 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [_sp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp]
         L.moe_forward.argtypes = [_sp] + [_vp] * 13 + [ctypes.c_size_t, _vp]
         L.moe_profile_kernel.argtypes = [ctypes.c_int, _vp, _vp]
+        L.moe_profile_kernel_launch.argtypes = [ctypes.c_int, ctypes.c_int, _vp, _vp]
         L.moe_profile_launches.argtypes = []
         L.moe_profile_launches.restype = ctypes.c_longlong
         for name in ("moe_router", "moe_permute", "moe_pack_weights", "moe_grouped_ffn",
-                     "moe_shared_ffn", "moe_combine", "moe_forward", "moe_profile_kernel"):
+                     "moe_shared_ffn", "moe_combine", "moe_forward", "moe_profile_kernel",
+                     "moe_profile_kernel_launch"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -271,16 +273,17 @@ def forward(shape, x, w_router, bias, w_gate_up, w_down, ws_gate_up, ws_down, ou
     _check(lib().moe_forward(ctypes.byref(shape), *args, wp, wn, _stream(stream)))
 
 
-def profile_kernel(name: Optional[str], start=None, stop=None) -> None:
-    """Bracket every launch of kernel ``name`` with the two torch.cuda.Event
-    (or None to turn the hook off)."""
+def profile_kernel(name: Optional[str], start=None, stop=None, launch: int = -1) -> None:
+    """Bracket every launch of kernel ``name`` (or only its ``launch``-th one
+    from now on) with the two torch.cuda.Event, or None to turn the hook off."""
     if name is None:
         _check(lib().moe_profile_kernel(-1, None, None))
         return
     for ev in (start, stop):
         if not ev.cuda_event:  # torch creates the HIP event on first record
             ev.record()
-    _check(lib().moe_profile_kernel(KERNEL_ID[name], start.cuda_event, stop.cuda_event))
+    _check(lib().moe_profile_kernel_launch(KERNEL_ID[name], int(launch), start.cuda_event,
+                                           stop.cuda_event))
 
 
 def profile_launches() -> int:

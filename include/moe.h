@@ -256,6 +256,13 @@ enum moe_kernel {
  * MOE_ERR_NULL for a NULL event while turning the hook on. */
 int moe_profile_kernel(int kernel, void* start, void* stop);
 
+/* As moe_profile_kernel, but only the launch-th launch (0-based, counted from
+ * this call) of the kernel is bracketed; launch = -1 brackets every launch.
+ * moe_forward launches the heavy GEMM kernels twice when the layer has a
+ * shared expert: launch 0 runs the routed experts, launch 1 the shared one.
+ * MOE_ERR_SHAPE for launch < -1, otherwise as moe_profile_kernel. */
+int moe_profile_kernel_launch(int kernel, int launch, void* start, void* stop);
+
 /* Launches of the hooked kernel since the last moe_profile_kernel call. */
 long long moe_profile_launches(void);
 

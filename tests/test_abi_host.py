@@ -116,6 +116,18 @@ def test_argument_errors(L):
     assert "ws_down" in moe.last_error()
 
 
+def test_profile_hook_arguments(L):
+    """The measurement hook validates its arguments without touching the GPU
+    (it only stores the event handles)."""
+    P = ctypes.c_void_p(0x10000)
+    assert L.moe_profile_kernel(99, P, P) == moe.MOE_ERR_SHAPE
+    assert L.moe_profile_kernel_launch(moe.KERNEL_ID["combine"], -2, P, P) == moe.MOE_ERR_SHAPE
+    assert L.moe_profile_kernel_launch(moe.KERNEL_ID["combine"], 0, None, P) == moe.MOE_ERR_NULL
+    assert L.moe_profile_kernel_launch(moe.KERNEL_ID["combine"], 1, P, P) == moe.MOE_OK
+    assert moe.profile_launches() == 0
+    assert L.moe_profile_kernel(-1, None, None) == moe.MOE_OK
+
+
 def test_empty_batch_is_noop(L):
     """T == 0 validates and returns OK without launching anything."""
     s = shp(T=0)

@@ -350,6 +350,27 @@ def test_combine_stage(T, y_bf16):
         assert np.abs(out.cpu().numpy() - ref).max() <= 1e-5 * max(1.0, np.abs(ref).max())
 
 
+def test_profile_hook_per_launch():
+    """With a shared expert the heavy GEMM kernels run twice per forward;
+    the hook brackets either launch on its own, or every launch."""
+    lay = layer_on_gpu(SMALL["shared"])
+    m = moe.MoELayer(lay, light_max_rows=0)
+    m()
+    torch.cuda.synchronize()
+    durs = []
+    for launch in (-1, 0, 1, 2):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        moe.profile_kernel("gateup_heavy", a, b, launch=launch)
+        m()
+        n = moe.profile_launches()
+        moe.profile_kernel(None)
+        torch.cuda.synchronize()
+        assert n == 2
+        if launch != 2:  # a launch index past the last one records nothing
+            durs.append(a.elapsed_time(b))
+    assert all(d > 0 for d in durs)
+
+
 def test_shared_stage(oracle_lib):
     cfg = SMALL["shared"]
     lay = layer_on_gpu(cfg)
