@@ -523,11 +523,19 @@ __device__ __forceinline__ void ring_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Read of a plan or offsets entry at a wave-uniform index through the
+// constant address space: a scalar load, so it does not count against the
+// vector-memory counter that the LDS ring's waits are written for.  The
+// heavy kernels never write these arrays.
+__device__ __forceinline__ int32_t sload(const int32_t* p, int i) {
+    return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
 // Height index (0, 1, 2 for kTileTM0/1/2) of row tile `tile`: from the
 // plan's tile list, or the dense group's one height.
 __device__ __forceinline__ int tile_tmi(const FfnArgs& a, int tile) {
     if (a.plan)
-        return (int)((uint32_t)a.plan[kPlanHeader + a.E + 2 * tile + 1] >> kTileTmShift);
+        return (int)((uint32_t)sload(a.plan, kPlanHeader + a.E + 2 * tile + 1) >> kTileTmShift);
     return a.dense_tm == kTileTM0 ? 0 : (a.dense_tm == kTileTM1 ? 1 : 2);
 }
 
@@ -577,24 +585,38 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
 
     // Per-tile state: output block nb of row tile (e, m0); rows of the tile
     // that exist; buffer resources and per-lane byte offsets of the loads.
+    struct Tile {
+        int nb, e, r0, m0, rows;
+    };
+    // Where work item w sits (scalar reads only).
+    auto locate = [&](long long w) -> Tile {
+        Tile t;
+        const int tile = (int)(w / nblk);
+        t.nb = (int)(w % nblk);
+        if (a.plan) {
+            const int base = kPlanHeader + a.E + 2 * tile;
+            t.e = sload(a.plan, base);
+            t.m0 = sload(a.plan, base + 1) & kTileRowMask;
+            t.r0 = sload(a.offsets, t.e);
+            t.rows = min(TM, sload(a.offsets, t.e + 1) - t.r0 - t.m0);
+        } else {
+            t.e = 0;
+            t.r0 = 0;
+            t.m0 = tile * TM;
+            t.rows = min(TM, a.dense_rows - t.m0);
+        }
+        return t;
+    };
     int nb = 0, e = 0, r0 = 0, m0 = 0, rows = 0;
     __amdgpu_buffer_rsrc_t ar, br;
     uint32_t aoff[kABlk], boff[kBBlkPerWave];
-    auto setup = [&](long long wi) {
-        const int tile = (int)(wi / nblk);
-        nb = (int)(wi % nblk);
-        if (a.plan) {
-            const int32_t* tl = a.plan + kPlanHeader + a.E;
-            e = tl[2 * tile];
-            m0 = tl[2 * tile + 1] & kTileRowMask;
-            r0 = a.offsets[e];
-            rows = min(TM, a.offsets[e + 1] - r0 - m0);
-        } else {
-            e = 0;
-            r0 = 0;
-            m0 = tile * TM;
-            rows = min(TM, a.dense_rows - m0);
-        }
+    // Load sources of tile t: buffer resources and per-lane offsets.
+    auto use_tile = [&](const Tile& t) {
+        nb = t.nb;
+        e = t.e;
+        r0 = t.r0;
+        m0 = t.m0;
+        rows = t.rows;
         // This wave fills A blocks kABlk*wave.. and B blocks 4*wave..+3.  Each
         // source is a buffer resource (SGPRs) plus a 32-bit per-lane byte
         // offset that holds the lane's row and K chunk; the stage's K offset
@@ -638,6 +660,7 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
             }
         }
     };
+    auto setup = [&](long long w) { use_tile(locate(w)); };
     // Stage st's loads of this wave: A blocks into A slot st % ast, B blocks
     // into B slot st % bst.
     auto adjust = [&](int kk, uint32_t& adj_a, uint32_t& adj_b) {
@@ -708,8 +731,24 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
         for (int i = i0; i < i1; ++i) af[i] = rd_a(slot, half, (wm * kRF + i) * 2);
     };
 
+    // Cross-tile prefetch (down only): while a tile runs its last stages, the
+    // stages freed in the rings take the next tile's first stages, as if the
+    // two tiles' K loops were one stream, so the next tile starts with its
+    // first stage in LDS and its first fragments in registers.  The next
+    // tile's sources are set up between the shallow ring's last load of this
+    // tile and the deep ring's first load of the next one.  Down only: its
+    // setup needs scalar reads alone, while gate|up gathers row ids with
+    // vector loads, which the ring's vmcnt waits do not count.  Needs whole
+    // stages (nh even) and at least as many stages as the deeper ring.
+    constexpr int kDeepest = ast > bst ? ast : bst;
+    const bool pf_ok = M == Mode::Down && TM != 256 && (nh & 1) == 0 && nst >= kDeepest;
+    static_assert(M != Mode::Down || ast != bst, "cross-tile prefetch wants rings of different depth");
+
     setup(wi);
     issue_first();
+    int bs = 0, as = 0;     // B and A slots of the current stage
+    bool primed = false;    // stage 0 already in, its first fragments in af / bf0
+    bf16x8_t af[kRF], bf0[4], bf1[4];
     while (true) {
         floatx4_t acc[kRF][4];
 #pragma unroll
@@ -724,21 +763,30 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
                 for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(af[i], bf[j], acc[i][j]);
         };
 
-        // The first loads were requested after the previous tile's epilogue
-        // stores (or above, for the first tile); vector-memory operations
-        // retire in order, so stage 0 is in once at most the loads after it
-        // (A1 B1, and stage 2 of a three-deep ring) are pending.
-        if (nst > 2 && kDeepBlk > 0)
-            wait_vmcnt<kABlk + kBBlkPerWave + kDeepBlk>();
-        else if (nst > 1)
-            wait_vmcnt<kABlk + kBBlkPerWave>();
-        else
-            wait_vmcnt<0>();
-        ring_barrier();
-        bf16x8_t af[kRF], bf0[4], bf1[4];
-        read_b(0, 0, bf0);
-        read_a(0, 0, 0, af);
-        read_a(0, 0, 1, af);
+        const int t_nb = nb, t_base = r0 + m0, t_rows = rows;
+        const long long wnext = wi + nb_x;
+        const bool more = wnext < wend && tile_tmi(a, (int)(wnext / nblk)) == kTmi;
+        const bool pf = pf_ok && more;
+        Tile nx{};
+        if (pf) nx = locate(wnext);
+
+        if (!primed) {
+            // The first loads were requested after the previous tile's
+            // epilogue stores (or above, for the first tile); vector-memory
+            // operations retire in order, so stage 0 is in once at most the
+            // loads after it (A1 B1, and stage 2 of a three-deep ring) are
+            // pending.
+            if (nst > 2 && kDeepBlk > 0)
+                wait_vmcnt<kABlk + kBBlkPerWave + kDeepBlk>();
+            else if (nst > 1)
+                wait_vmcnt<kABlk + kBBlkPerWave>();
+            else
+                wait_vmcnt<0>();
+            ring_barrier();
+            read_b(0, 0, bf0);
+            read_a(0, 0, 0, af);
+            read_a(0, 0, 1, af);
+        }
         // Each 32-wide half step runs its MFMAs in two groups of rows; the
         // fragments of the next half step are read behind them: B and the
         // first half of the A rows after the first group (those rows are done
@@ -749,7 +797,6 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
         // copies): peeling made the register allocator stop keeping each
         // accumulator in place and spill.
         const int nfull = nh / 2;  // stages with both halves
-        int bs = 0, as = 0;        // B and A slots of stage st
         for (int st = 0; st < nfull; ++st) {
             const int bn = (bs + 1 == bst) ? 0 : bs + 1;  // B slot of stage st+1
             const int an = (as + 1 == ast) ? 0 : as + 1;  // A slot of stage st+1
@@ -759,26 +806,36 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
             mfma_rows(1, af, bf0);
             read_a(as, 1, 1, af);
             mfma_rows(0, af, bf1);
-            // After the last stage this wait, barrier and the reads of the
-            // (absent) next stage are harmless: no load is outstanding and
-            // the ring addresses are valid.
+            // After the last stage without a prefetch this wait, barrier and
+            // the reads of the (absent) next stage are harmless: no load is
+            // outstanding and the ring addresses are valid.  With one, the
+            // next stage is the next tile's stage 0.
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of st done
             // Stage st+1 in: only the three-deep ring's load of stage st+2
-            // may be pending.
-            if (kDeepBlk > 0 && st + 2 < nst)
+            // may be pending.  After the previous tile's epilogue the stores
+            // are pending too, behind that load; counting them out is exact
+            // enough (it only waits for them as well).
+            if (kDeepBlk > 0 && (st + 2 < nst || pf))
                 wait_vmcnt<kDeepBlk>();
             else
                 wait_vmcnt<0>();
             ring_barrier();
             // Refill the buffers stage st used, each ring its depth ahead and
             // the two-deep ring first (this order is what the wait above
-            // counts on); stage st + depth lands in stage st's slot.
+            // counts on); stage st + depth lands in stage st's slot.  Stages
+            // past this tile's last are the next tile's.
             if (ast <= bst) {
                 if (st + ast < nst) issue_a(st + ast, as);
+                else if (pf) issue_a(st + ast - nst, as);
+                if (pf && st + bst == nst) use_tile(nx);
                 if (st + bst < nst) issue_b(st + bst, bs);
+                else if (pf) issue_b(st + bst - nst, bs);
             } else {
                 if (st + bst < nst) issue_b(st + bst, bs);
+                else if (pf) issue_b(st + bst - nst, bs);
+                if (pf && st + ast == nst) use_tile(nx);
                 if (st + ast < nst) issue_a(st + ast, as);
+                else if (pf) issue_a(st + ast - nst, as);
             }
             read_b(bn, 0, bf0);
             read_a(an, 0, 0, af);
@@ -791,21 +848,21 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
             mfma_rows(0, af, bf0);
             mfma_rows(1, af, bf0);
         }
-        // Every wave's reads of the ring are complete before the next tile's
-        // loads are requested into it (after the epilogue below).
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        ring_barrier();
+        if (!pf) {
+            // Every wave's reads of the ring are complete before the next
+            // tile's loads are requested into it (after the epilogue below).
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            ring_barrier();
+        }
 
         // Epilogue.  Lane (l16, g) of wave (wm, wn) holds rows
         // wm*TM/2 + 16i + 4g + r of its MFMA tiles; the row offsets 16i + r are
-        // compile-time constants times a uniform pitch.  The next tile's setup
-        // (its row indices are loads) runs first, so that waiting for those
-        // loads does not also wait for this tile's stores to drain.
+        // compile-time constants times a uniform pitch.  Without a prefetch
+        // the next tile's setup (gate|up's row ids are loads) runs first, so
+        // that waiting for those loads does not also wait for this tile's
+        // stores to drain.
         const int row0 = wm * (TM / 2) + 4 * g;
-        const int t_nb = nb, t_base = r0 + m0, t_rows = rows;
-        const long long wnext = wi + nb_x;
-        const bool more = wnext < wend && tile_tmi(a, (int)(wnext / nblk)) == kTmi;
-        if (more) setup(wnext);
+        if (more && !pf) setup(wnext);
         if constexpr (M == Mode::GateUp) {
             const int hc0 = t_nb * (kTN / 2) + wn * 32 + l16;
             uint16_t* hp = a.h + (size_t)(t_base + row0) * hstride + hc0;
@@ -876,7 +933,11 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
 
         wi = wnext;
         if (!more) break;
-        issue_first();
+        primed = pf;
+        if (!pf) {
+            bs = as = 0;
+            issue_first();
+        }
     }
     return wi;
 }
