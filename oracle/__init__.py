@@ -34,6 +34,7 @@ CFLAGS = ["-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
 
 _f32p = ctypes.POINTER(ctypes.c_float)
 _i32p = ctypes.POINTER(ctypes.c_int32)
+_u8p = ctypes.POINTER(ctypes.c_uint8)
 
 
 def build(out: str = LIB, src: str = SRC) -> str:
@@ -85,6 +86,9 @@ class Oracle:
         lib.oref_permute.restype = ctypes.c_int
         lib.oref_expert_ffn.argtypes = [ctypes.c_int] * 3 + [_f32p] * 4
         lib.oref_combine.argtypes = [ctypes.c_int] * 3 + [_f32p] * 4
+        lib.oref_mxfp8_quantize.argtypes = [ctypes.c_long, ctypes.c_int, _f32p, _u8p, _u8p]
+        lib.oref_mxfp8_quantize.restype = ctypes.c_int
+        lib.oref_mxfp8_dequantize.argtypes = [ctypes.c_long, ctypes.c_int, _u8p, _u8p, _f32p]
         self.lib = lib
 
     # -- threads ----------------------------------------------------------
@@ -167,6 +171,31 @@ class Oracle:
         s = None if shared is None else _np32(shared)
         out = np.empty((T, H), np.float32)
         self.lib.oref_combine(T, H, k, _p(w), _p(y), None if s is None else _p(s), _p(out))
+        return out
+
+    # -- MXFP8 expert weights (OCP MX v1.0, E4M3 elements, 32-value blocks) --
+    def mxfp8_quantize(self, w):
+        """w [..., K] (K % 32 == 0) -> (codes uint8 [..., K], scales uint8
+        [..., K/32]); see oref_mxfp8_quantize for the rule."""
+        w = _np32(w)
+        K = w.shape[-1]
+        rows = w.size // K if K else 0
+        codes = np.empty(w.shape, np.uint8)
+        scales = np.empty(w.shape[:-1] + (K // 32,), np.uint8)
+        rc = self.lib.oref_mxfp8_quantize(rows, K, _p(w), _p(codes, _u8p), _p(scales, _u8p))
+        if rc != 0:
+            raise ValueError(f"oref_mxfp8_quantize failed ({rc})")
+        return codes, scales
+
+    def mxfp8_dequantize(self, codes, scales) -> np.ndarray:
+        """codes uint8 [..., K], scales uint8 [..., K/32] -> fp32 [..., K]."""
+        codes = np.ascontiguousarray(codes, dtype=np.uint8)
+        scales = np.ascontiguousarray(scales, dtype=np.uint8)
+        K = codes.shape[-1]
+        assert K % 32 == 0 and scales.shape == codes.shape[:-1] + (K // 32,)
+        out = np.empty(codes.shape, np.float32)
+        rows = codes.size // K if K else 0
+        self.lib.oref_mxfp8_dequantize(rows, K, _p(codes, _u8p), _p(scales, _u8p), _p(out))
         return out
 
     # -- composition ------------------------------------------------------

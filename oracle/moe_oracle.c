@@ -299,3 +299,104 @@ OREF_EXPORT void oref_combine(int T, int H, int k, const float* w, const float* 
         }
     }
 }
+
+/* ---------------------------------------------------------------------------
+ * MXFP8 expert weights (a variant of the layer with 8-bit routed expert
+ * weights).  The pages mention FP8 scaling blocks (pwwt.cn article, section 6:
+ * the gating kernels' accumulation is audited across FP8 scaling blocks) and
+ * MX formats (first page, section 3: MXFP6 units), but fix no format for
+ * expert weights.  Reading: the OCP Microscaling Formats (MX) specification
+ * v1.0, format MXFP8 with E4M3 elements:
+ *  - a block is 32 consecutive values of one weight row (along the reduction
+ *    dimension: H for W_gate|up, I for W_down) and shares one E8M0 scale,
+ *    code s8 meaning X = 2^(s8 - 127);
+ *  - an element is an FP8 E4M3 number: sign, 4 exponent bits (bias 7),
+ *    3 mantissa bits; exponent field 0 holds subnormals m/8 * 2^-6; the
+ *    largest finite magnitude is 1.75 * 2^8 = 448; S.1111.111 is NaN; there
+ *    are no infinities.
+ * Quantising a block (the specification's conversion rule, restated):
+ *  - shared exponent s = floor(log2(max_i |v_i|)) - 8 (8 = exponent of the
+ *    largest normal E4M3 value), clamped to [-127, 127]; an all-zero block
+ *    takes -127;
+ *  - element i = v_i / 2^s rounded to the nearest E4M3 value, ties to the
+ *    even mantissa; magnitudes past 448 become 448 (saturation); the sign bit
+ *    is the sign of v_i, so -0 and negative values rounding to 0 give 0x80.
+ * Dequantised weight: value(code) * 2^s (exact in fp32).
+ * Plain double arithmetic: frexp/ldexp are exact, nearbyint rounds half to
+ * even in the default rounding mode.
+ */
+static double oref_e4m3_value(uint8_t c) {
+    const int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double mag;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        mag = ldexp((double)m, -9);          /* m/8 * 2^-6 */
+    else
+        mag = ldexp(8.0 + m, e - 7 - 3);     /* (1 + m/8) * 2^(e-7) */
+    return s ? -mag : mag;
+}
+
+static uint8_t oref_e4m3_encode(double v) {
+    const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    const double a = fabs(v);
+    int ex = 0;
+    /* exponent of the binade holding a; below 2^-6 the spacing stays that of
+     * the subnormals, 2^-9 */
+    int E = -6;
+    if (a > 0.0) {
+        frexp(a, &ex);                       /* a = f * 2^ex, f in [0.5, 1) */
+        E = ex - 1;
+        if (E < -6) E = -6;
+    }
+    /* round to a multiple of the spacing 2^(E-3) (3 mantissa bits) */
+    double r = ldexp(nearbyint(ldexp(a, 3 - E)), E - 3);
+    if (r > 448.0) r = 448.0;
+    if (r == 0.0) return sign;
+    frexp(r, &ex);
+    const int Er = ex - 1;
+    if (Er < -6) return (uint8_t)(sign | (uint8_t)ldexp(r, 9)); /* subnormal: m = r / 2^-9 */
+    return (uint8_t)(sign | ((Er + 7) << 3) | (int)(ldexp(r, 3 - Er) - 8.0));
+}
+
+/* w [rows,K] fp32 (finite) -> codes [rows,K], scales [rows,K/32].
+ * Returns 0, or 1 if K % 32 != 0, 2 on a non-finite input. */
+OREF_EXPORT int oref_mxfp8_quantize(long rows, int K, const float* w, uint8_t* codes,
+                                    uint8_t* scales) {
+    if (K % 32 != 0) return 1;
+    const int nb = K / 32;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (long r = 0; r < rows; ++r) {
+        for (int b = 0; b < nb; ++b) {
+            const float* v = w + r * K + b * 32;
+            double amax = 0.0;
+            for (int i = 0; i < 32; ++i) {
+                if (!isfinite(v[i])) bad = 1;
+                if (fabs((double)v[i]) > amax) amax = fabs((double)v[i]);
+            }
+            int s = -127;
+            if (amax > 0.0) {
+                int ex = 0;
+                frexp(amax, &ex);
+                s = ex - 1 - 8;
+            }
+            if (s < -127) s = -127;
+            if (s > 127) s = 127;
+            scales[r * nb + b] = (uint8_t)(s + 127);
+            for (int i = 0; i < 32; ++i)
+                codes[r * K + b * 32 + i] = oref_e4m3_encode(ldexp((double)v[i], -s));
+        }
+    }
+    return bad ? 2 : 0;
+}
+
+/* codes [rows,K], scales [rows,K/32] -> out [rows,K] fp32. */
+OREF_EXPORT void oref_mxfp8_dequantize(long rows, int K, const uint8_t* codes,
+                                       const uint8_t* scales, float* out) {
+    const int nb = K / 32;
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < rows; ++r)
+        for (int i = 0; i < K; ++i)
+            out[r * K + i] =
+                (float)ldexp(oref_e4m3_value(codes[r * K + i]), (int)scales[r * nb + i / 32] - 127);
+}

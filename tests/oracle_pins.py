@@ -307,11 +307,141 @@ def pin_ffn_closed_form(o):
         assert abs(got - ref) <= 1e-6 * max(1.0, abs(ref))
 
 
+# ------------------------------------------------------- MXFP8 weights
+def _e4m3_library_table():
+    """Values of the 256 FP8 E4M3 codes from torch's float8_e4m3fn (a
+    library's decoding of the same OCP format), float64."""
+    import torch
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy() \
+        .astype(np.float64)
+
+
+def _e4m3_library_round(v):
+    """torch's round-to-nearest-even cast of fp32 values to E4M3 codes (it is
+    not saturating: only |v| < 464 is meaningful)."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(torch.float8_e4m3fn) \
+        .view(torch.uint8).numpy()
+
+
+def pin_mxfp8_decode_table(o):
+    """Every code, at scale 2^0, decodes to the library's E4M3 value (NaN
+    codes included); a scale code c multiplies by 2^(c-127)."""
+    tab = _e4m3_library_table()
+    codes = np.arange(256, dtype=np.uint8).reshape(8, 32)
+    got = o.mxfp8_dequantize(codes, np.full((8, 1), 127, np.uint8)).astype(np.float64)
+    assert np.array_equal(got.reshape(-1), tab, equal_nan=True)
+    for sc in (100, 127 - 9, 131, 140):
+        got = o.mxfp8_dequantize(codes, np.full((8, 1), sc, np.uint8)).astype(np.float64)
+        assert np.array_equal(got.reshape(-1), tab * 2.0 ** (sc - 127), equal_nan=True)
+
+
+def pin_mxfp8_rounding_vs_library(o):
+    """With the block scale at 2^0 (an anchor of 300 in every block), element
+    codes equal the library's nearest-even cast: random magnitudes over the
+    subnormal and normal ranges, every representable value, every midpoint
+    between neighbours (ties), both signs, signed zeros."""
+    tab = _e4m3_library_table()[:127]           # codes 0..126: 0 .. 448 ascending
+    mids = (tab[:-1] + tab[1:]) / 2
+    rng = np.random.default_rng(21)
+    mags = 2.0 ** rng.uniform(-12.0, np.log2(463.0), size=31 * 40)
+    vals = np.concatenate([mags * rng.choice([-1.0, 1.0], mags.size), mids, -mids, tab, -tab,
+                           [0.0, -0.0, 463.0, -463.0]])
+    vals = np.concatenate([vals, np.zeros((-vals.size) % 31)])
+    blocks = np.concatenate([vals.reshape(-1, 31), np.full((vals.size // 31, 1), 300.0)], 1)
+    blocks = blocks.astype(np.float32)
+    codes, scales = o.mxfp8_quantize(blocks)
+    assert np.all(scales == 127)
+    assert np.array_equal(codes, _e4m3_library_round(blocks))
+
+
+def pin_mxfp8_saturation(o):
+    """Past 448 (after scaling) elements saturate to +-448 (codes 0x7E/0xFE);
+    a block maximum of 512 moves the scale up one binade instead."""
+    b = np.zeros((2, 32), np.float32)
+    b[0, :6] = [511.0, 500.0, -470.0, 449.0, -448.5, 1.0]
+    b[1, :3] = [512.0, -300.0, 1.0]
+    codes, scales = o.mxfp8_quantize(b)
+    assert scales[0, 0] == 127 and scales[1, 0] == 128
+    assert list(codes[0, :6]) == [0x7E, 0x7E, 0xFE, 0x7E, 0xFE, 0x38]
+    d = o.mxfp8_dequantize(codes, scales)
+    assert list(d[0, :5]) == [448.0, 448.0, -448.0, 448.0, -448.0]
+    assert list(d[1, :3]) == [512.0, -288.0, 1.0]      # -150 -> -144 (spacing 16), x 2
+
+
+def pin_mxfp8_scale_rule(o):
+    """Block scale = floor(log2 max|v|) - 8 (numpy's log2), clamped at -127
+    (zero blocks and tiny blocks): max |v| / X then lies in [256, 512)."""
+    rng = np.random.default_rng(22)
+    nb = 400
+    e = rng.integers(-40, 40, size=nb)
+    b = rng.standard_normal((nb, 32)) * 2.0 ** e[:, None]
+    b[::7, 5] = 2.0 ** e[::7]                              # exact powers of two as maxima
+    b[::7] = np.where(np.arange(32) == 5, b[::7], b[::7] * 1e-3)
+    b[3] = 0.0
+    b[4] = 0.0
+    b[4, 9] = -(2.0 ** -140)
+    b = b.astype(np.float32)
+    codes, scales = o.mxfp8_quantize(b)
+    amax = np.abs(b.astype(np.float64)).max(1)
+    with np.errstate(divide="ignore"):
+        want = np.where(amax > 0, np.floor(np.log2(amax)) - 8, -127)
+    want = np.clip(want, -127, 127)
+    assert np.array_equal(scales[:, 0].astype(np.int64) - 127, want.astype(np.int64))
+    ok = want > -127
+    ratio = amax[ok] / 2.0 ** want[ok]
+    assert np.all((ratio >= 256) & (ratio < 512))
+    assert np.all(codes[3] == 0)
+
+
+def pin_mxfp8_nearest_bruteforce(o):
+    """Each element is the finite E4M3 value nearest to v / X by exhaustive
+    search over the library's table (ties to the even code), or +-448 past
+    the range; bf16-valued weights as the layer uses them."""
+    tab = _e4m3_library_table()[:127]
+    rng = np.random.default_rng(23)
+    w = (rng.standard_normal((24, 64)) * 0.02).astype(np.float32)
+    w[5, :32] *= 1e-3
+    w[6, 32:] = np.round(w[6, 32:] * 4096) / 4096          # many exact ties after scaling
+    w = (w.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)  # bf16 values
+    codes, scales = o.mxfp8_quantize(w)
+    X = 2.0 ** (scales.astype(np.float64) - 127)
+    t = w.astype(np.float64) / np.repeat(X, 32, axis=1)
+    for (r, c), tv in np.ndenumerate(t):
+        a = abs(tv)
+        dist = np.abs(tab - a)
+        best = np.flatnonzero(dist == dist.min())
+        code = int(best[0]) if best.size == 1 else int(best[best % 2 == 0][0])
+        if a > 448.0:
+            code = 0x7E
+        if np.signbit(tv):
+            code |= 0x80
+        assert codes[r, c] == code, (r, c, tv, codes[r, c], code)
+
+
+def pin_mxfp8_golden_block(o):
+    """A block worked by hand from the MX conversion rule
+    (tests/golden/mxfp8_block.json)."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                           "mxfp8_block.json")) as f:
+        g = json.load(f)
+    codes, scales = o.mxfp8_quantize(np.array([g["values"]], np.float32))
+    assert int(scales[0, 0]) == g["scale_code"]
+    assert codes[0].tolist() == g["codes"]
+    d = o.mxfp8_dequantize(codes, scales)[0]
+    assert np.array_equal(d, np.array(g["dequantized"], np.float32))
+    assert np.array_equal(np.signbit(d), np.signbit(np.array(g["dequantized"])))
+
+
 ALL_PINS = [pin_logits_vs_library, pin_topk_full_sort, pin_tie_rule, pin_bias_only,
             pin_nonfinite, pin_large_logits, pin_renorm_off, pin_permute,
             pin_k1_single_expert, pin_identical_experts, pin_zero_weights,
             pin_identity_weights, pin_dense_bruteforce, pin_shared_expert,
-            pin_exact_scaling, pin_token_permutation, pin_ffn_closed_form]
+            pin_exact_scaling, pin_token_permutation, pin_ffn_closed_form,
+            pin_mxfp8_decode_table, pin_mxfp8_rounding_vs_library, pin_mxfp8_saturation,
+            pin_mxfp8_scale_rule, pin_mxfp8_nearest_bruteforce, pin_mxfp8_golden_block]
 
 
 def run_all(o) -> dict:

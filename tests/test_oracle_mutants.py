@@ -45,6 +45,18 @@ MUTANTS = {
                               "s = s + w[(size_t)t * k] * y["),
     "combine_drops_shared": ("out[(size_t)t * H + c] = shared ? shared[(size_t)t * H + c] + s : s;",
                              "out[(size_t)t * H + c] = s;"),
+    "mx_emax_7": ("s = ex - 1 - 8;", "s = ex - 1 - 7;"),
+    "mx_round_half_up": ("ldexp(nearbyint(ldexp(a, 3 - E)), E - 3)",
+                         "ldexp(floor(ldexp(a, 3 - E) + 0.5), E - 3)"),
+    "mx_no_saturation": ("if (r > 448.0) r = 448.0;", "if (r > 480.0) r = 480.0;"),
+    "mx_scale_bias": ("scales[r * nb + b] = (uint8_t)(s + 127);",
+                      "scales[r * nb + b] = (uint8_t)(s + 128);"),
+    "mx_subnormal_spacing": ("if (E < -6) E = -6;\n    }", "if (E < -7) E = -7;\n    }"),
+    "mx_sign_dropped": ("const uint8_t sign = signbit(v) ? 0x80 : 0x00;",
+                        "const uint8_t sign = 0x00;"),
+    "mx_dequant_scale_off": ("(int)scales[r * nb + i / 32] - 127", "(int)scales[r * nb + i / 32] - 126"),
+    "mx_subnormal_decode": ("mag = ldexp((double)m, -9);", "mag = ldexp(8.0 + m, -10);"),
+    "mx_zero_block_scale": ("int s = -127;\n            if (amax > 0.0)", "int s = 0;\n            if (amax > 0.0)"),
     "permute_unstable": ("for (int t = 0; t < T; ++t) {\n        for (int j = 0; j < k; ++j) {\n            const long a",
                          "for (int t = T - 1; t >= 0; --t) {\n        for (int j = 0; j < k; ++j) {\n            const long a"),
 }
