@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["router.hip", "permute.hip", "ffn.hip", "combine.hip", "moe_api.cpp"]
+SOURCES = ["router.hip", "permute.hip", "ffn.hip", "combine.hip", "mxfp8.hip", "moe_api.cpp"]
 
 # -packed-fp32-ops off: packed fp32 VALU forms are not emitted.
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -439,6 +439,327 @@ __global__ __launch_bounds__(kThreads) void down_light_kernel(FfnArgs a) {
     }
 }
 
+// ------------------------------------------------ light: MXFP8 weights
+// The same loops over packed MXFP8 weights: a lane's 16-byte load carries
+// the codes of two 32-wide K steps (see the packed layout in launch.h) and
+// each is turned into the bf16 operand of the bf16 loop by the hardware's
+// scaled conversion, code * 2^(scale - 127): exact, since an E4M3 value has
+// 4 significant bits.  Each accumulator then takes the same chain of MFMAs
+// over the same operands as the bf16 loop given the dequantised weights, so
+// the two give bitwise identical results.  Experts with more than 64 rows run
+// in passes of 64 rows (the weights are then read once per pass).
+#ifndef MOE_LIGHT_MX_GU_U
+#define MOE_LIGHT_MX_GU_U 8     // 64-wide K chunks in flight per wave (gate|up)
+#endif
+#ifndef MOE_LIGHT_MX_DN_U
+#define MOE_LIGHT_MX_DN_U 4
+#endif
+constexpr int kLightMxWideU = 1;  // chunks in flight, 17..64-row branch
+
+// Eight E4M3 codes (words w0, w1 in K order) times 2^(sb - 127) as an MFMA
+// operand.
+__device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t w0, uint32_t w1, uint32_t sb) {
+    const float sc = __uint_as_float(sb << 23);
+    const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, false);
+    const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, true);
+    const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, false);
+    const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, true);
+    return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+__device__ __forceinline__ uint32_t load_u16(const uint8_t* p) {
+    return *reinterpret_cast<const uint16_t*>(p);
+}
+
+// gate|up over MXFP8 weights: one wave, MT row sub-tiles x NTILE column
+// tiles (h columns 8*grp0 ..), K = H in 64-wide chunks.
+template <int MT, int U, int NTILE>
+__device__ __forceinline__ void gateup_light_rows_mx(const FfnArgs& a, int e, int r0, int n,
+                                                     int grp0, int l16, int g) {
+    const int nc = a.H / 64;
+    const int nk = a.H / 32;
+    const int lane = g * 16 + l16;
+    const size_t grp = (size_t)e * packed_gu_groups(a.I) + grp0;
+    const uint8_t* Bp = a.q_gu + grp * nc * 1024 + lane * 16;
+    const uint8_t* Sp = a.qs_gu + grp * nc * 32 + l16 * 2;
+    const size_t bstride = (size_t)nc * 1024, sstride = (size_t)nc * 32;
+    const uint16_t* Ap[MT];
+    bool has_a[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int row = m * 16 + l16;
+        has_a[m] = row < n;
+        const int tok = has_a[m] ? (a.sorted_ids ? a.sorted_ids[r0 + row] : r0 + row) : 0;
+        Ap[m] = a.x + (size_t)tok * a.H + 8 * g;
+    }
+    const int mt_live = (n + 15) / 16;
+
+    floatx4_t acc[MT][NTILE];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) acc[m][t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    bf16x8_t ca[U][MT][2];
+    u32x4_t cb[U][NTILE];
+    uint32_t cs[U][NTILE];
+    auto load_chunk = [&](int c, bf16x8_t (&aa)[MT][2], u32x4_t (&bb)[NTILE],
+                          uint32_t (&ss)[NTILE]) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) aa[m][0] = aa[m][1] = zero_bf16x8();
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) {
+            bb[t] = u32x4_t{0u, 0u, 0u, 0u};
+            ss[t] = 0u;
+        }
+        if (c < nc) {
+#pragma unroll
+            for (int t = 0; t < NTILE; ++t) {
+                bb[t] = *reinterpret_cast<const u32x4_t*>(Bp + t * bstride + (size_t)c * 1024);
+                ss[t] = load_u16(Sp + t * sstride + (size_t)c * 32);
+            }
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                if (has_a[m]) {
+                    aa[m][0] = load_bf16x8(Ap[m] + c * 64);
+                    aa[m][1] = load_bf16x8(Ap[m] + c * 64 + 32);
+                }
+        }
+    };
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_chunk(u, ca[u], cb[u], cs[u]);
+    for (int c0 = 0; c0 < nc; c0 += U) {
+        bf16x8_t na[U][MT][2];
+        u32x4_t nb_[U][NTILE];
+        uint32_t ns[U][NTILE];
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_chunk(c0 + U + u, na[u], nb_[u], ns[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (c0 + u < nc) {
+#pragma unroll
+                for (int t = 0; t < NTILE; ++t) {
+                    const bf16x8_t b0 = e4m3x8_to_bf16(cb[u][t][0], cb[u][t][1], cs[u][t] & 0xffu);
+                    const bf16x8_t b1 = e4m3x8_to_bf16(cb[u][t][2], cb[u][t][3], cs[u][t] >> 8);
+#pragma unroll
+                    for (int m = 0; m < MT; ++m)
+                        if (m < mt_live) {
+                            acc[m][t] = mfma_16x16x32(ca[u][m][0], b0, acc[m][t]);
+                            if (2 * (c0 + u) + 1 < nk)
+                                acc[m][t] = mfma_16x16x32(ca[u][m][1], b1, acc[m][t]);
+                        }
+                }
+            }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                ca[u][m][0] = na[u][m][0];
+                ca[u][m][1] = na[u][m][1];
+            }
+#pragma unroll
+            for (int t = 0; t < NTILE; ++t) {
+                cb[u][t] = nb_[u][t];
+                cs[u][t] = ns[u][t];
+            }
+        }
+    }
+    const int i0 = grp0 * 8;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float up = __shfl_down(acc[m][t][r], 8, 64);
+                const int row = m * 16 + 4 * g + r;
+                if (l16 < 8 && row < n)
+                    a.h[(size_t)(r0 + row) * a.I + i0 + 8 * t + l16] =
+                        (uint16_t)f32_to_bf16_bits(swiglu(acc[m][t][r], up));
+            }
+        }
+    }
+}
+
+template <int U, int NTILE>
+__global__ __launch_bounds__(kThreads) void gateup_light_mx_kernel(FfnArgs a) {
+    static_assert(32 % (NTILE * 8) == 0, "a wave's columns must divide I's multiple of 32");
+    constexpr int kCols = 4 * NTILE * 8;
+    const int nlight = a.plan[0];
+    const int nblk = (a.I + kCols - 1) / kCols;
+    const long long nwork = (long long)nlight * nblk;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l16 = lane & 15, g = lane >> 4;
+    for (long long wi = blockIdx.x; wi < nwork; wi += gridDim.x) {
+        const int slot = (int)(wi / nblk), nb = (int)(wi % nblk);
+        const int i0 = nb * kCols + wave * NTILE * 8;
+        if (i0 >= a.I) continue;  // I % 32 == 0: a wave is all in or all out
+        const int e = a.plan[kPlanHeader + slot];
+        const int r0 = a.offsets[e];
+        const int n = a.offsets[e + 1] - r0;
+        for (int p = 0; p < n; p += kLightRowsMax) {
+            const int np = min(kLightRowsMax, n - p);
+            if (np <= 16)
+                gateup_light_rows_mx<1, U, NTILE>(a, e, r0 + p, np, i0 / 8, l16, g);
+            else
+                gateup_light_rows_mx<kLightSubTiles, kLightMxWideU, NTILE>(a, e, r0 + p, np,
+                                                                           i0 / 8, l16, g);
+        }
+    }
+}
+
+// down over MXFP8 weights: MT row sub-tiles x NT column tiles (16 output
+// columns each, c0 ..), K = I in 64-wide chunks; a chunk's second K step
+// past I (I % 64 == 32) is padding and is skipped.
+template <int MT, int U, int NT>
+__device__ __forceinline__ void down_light_rows_mx(const FfnArgs& a, int e, int r0, int n, int c0,
+                                                   int l16, int g) {
+    const int nc = mx_chunks(a.I);
+    const int nk = a.I / 32;
+    const int lane = g * 16 + l16;
+    const size_t grp = (size_t)e * packed_dn_groups(a.H) + c0 / 16;
+    const uint8_t* Bp = a.q_dn + grp * nc * 1024 + lane * 16;
+    const uint8_t* Sp = a.qs_dn + grp * nc * 32 + l16 * 2;
+    const size_t bstride = (size_t)nc * 1024, sstride = (size_t)nc * 32;
+    const uint16_t* Ap[MT];
+    bool has_a[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int row = m * 16 + l16;
+        has_a[m] = row < n;
+        Ap[m] = a.h + (size_t)(r0 + (has_a[m] ? row : 0)) * a.I + 8 * g;
+    }
+    const int mt_live = (n + 15) / 16;
+
+    floatx4_t acc[MT][NT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[m][t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    bf16x8_t ca[U][MT][2];
+    u32x4_t cb[U][NT];
+    uint32_t cs[U][NT];
+    auto load_chunk = [&](int c, bf16x8_t (&aa)[MT][2], u32x4_t (&bb)[NT], uint32_t (&ss)[NT]) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) aa[m][0] = aa[m][1] = zero_bf16x8();
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            bb[t] = u32x4_t{0u, 0u, 0u, 0u};
+            ss[t] = 0u;
+        }
+        if (c < nc) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                bb[t] = *reinterpret_cast<const u32x4_t*>(Bp + t * bstride + (size_t)c * 1024);
+                ss[t] = load_u16(Sp + t * sstride + (size_t)c * 32);
+            }
+            const bool second = 2 * c + 1 < nk;
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                if (has_a[m]) {
+                    aa[m][0] = load_bf16x8(Ap[m] + c * 64);
+                    if (second) aa[m][1] = load_bf16x8(Ap[m] + c * 64 + 32);
+                }
+        }
+    };
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_chunk(u, ca[u], cb[u], cs[u]);
+    for (int k0 = 0; k0 < nc; k0 += U) {
+        bf16x8_t na[U][MT][2];
+        u32x4_t nb_[U][NT];
+        uint32_t ns[U][NT];
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_chunk(k0 + U + u, na[u], nb_[u], ns[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (k0 + u < nc) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const bf16x8_t b0 = e4m3x8_to_bf16(cb[u][t][0], cb[u][t][1], cs[u][t] & 0xffu);
+                    const bf16x8_t b1 = e4m3x8_to_bf16(cb[u][t][2], cb[u][t][3], cs[u][t] >> 8);
+#pragma unroll
+                    for (int m = 0; m < MT; ++m)
+                        if (m < mt_live) {
+                            acc[m][t] = mfma_16x16x32(ca[u][m][0], b0, acc[m][t]);
+                            if (2 * (k0 + u) + 1 < nk)
+                                acc[m][t] = mfma_16x16x32(ca[u][m][1], b1, acc[m][t]);
+                        }
+                }
+            }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                ca[u][m][0] = na[u][m][0];
+                ca[u][m][1] = na[u][m][1];
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                cb[u][t] = nb_[u][t];
+                cs[u][t] = ns[u][t];
+            }
+        }
+    }
+    if (a.y_bf16) {
+        const int odd = l16 & 1;
+        uint32_t* y = static_cast<uint32_t*>(a.y);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                uint32_t w[2];
+                y_bf16_pairs(acc[m][t], l16, w[0], w[1]);
+                const int c = c0 + t * 16 + l16 - odd;  // even
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    const int row = m * 16 + 4 * g + 2 * odd + r;
+                    if (row < n) y[((size_t)(r0 + row) * a.H + c) / 2] = w[r];
+                }
+            }
+        }
+        return;
+    }
+    float* y = static_cast<float*>(a.y);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int c = c0 + t * 16 + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = m * 16 + 4 * g + r;
+                if (row < n) y[(size_t)(r0 + row) * a.H + c] = acc[m][t][r];
+            }
+        }
+    }
+}
+
+template <int NT, int U>
+__global__ __launch_bounds__(kThreads) void down_light_mx_kernel(FfnArgs a) {
+    static_assert(64 % (NT * 16) == 0, "a wave's columns must divide H's multiple of 64");
+    constexpr int kCols = 4 * NT * 16;
+    const int nlight = a.plan[0];
+    const int nblk = (a.H + kCols - 1) / kCols;
+    const long long nwork = (long long)nlight * nblk;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l16 = lane & 15, g = lane >> 4;
+    for (long long wi = blockIdx.x; wi < nwork; wi += gridDim.x) {
+        const int slot = (int)(wi / nblk), nb = (int)(wi % nblk);
+        const int c0 = nb * kCols + wave * NT * 16;
+        if (c0 >= a.H) continue;
+        const int e = a.plan[kPlanHeader + slot];
+        const int r0 = a.offsets[e];
+        const int n = a.offsets[e + 1] - r0;
+        for (int p = 0; p < n; p += kLightRowsMax) {
+            const int np = min(kLightRowsMax, n - p);
+            if (np <= 16)
+                down_light_rows_mx<1, U, NT>(a, e, r0 + p, np, c0, l16, g);
+            else
+                down_light_rows_mx<kLightSubTiles, kLightMxWideU, NT>(a, e, r0 + p, np, c0, l16,
+                                                                      g);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- heavy
 // 256x256 output tiles computed by 8 waves (2 per SIMD) in a 2 (rows) x 4
 // (columns) grid; each wave owns a 128x64 block of 16x16 MFMA tiles (32
@@ -1084,7 +1405,9 @@ hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t st) {
         const long long work = (long long)a.max_light * ((a.I + kCols - 1) / kCols);
         prof_begin(K_GATEUP_LIGHT, st);
         const int grid = grid_for(work, MOE_LIGHT_GU_BPC, a.num_cu);
-        if (a.pk_gu)
+        if (a.w_mxfp8)
+            gateup_light_mx_kernel<MOE_LIGHT_MX_GU_U, MOE_LIGHT_GU_TILES><<<grid, kThreads, 0, st>>>(a);
+        else if (a.pk_gu)
             gateup_light_kernel<MOE_LIGHT_GU_U, MOE_LIGHT_GU_TILES, MOE_LIGHT_NT_LOADS != 0, true>
                 <<<grid, kThreads, 0, st>>>(a);
         else
@@ -1109,7 +1432,9 @@ hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st) {
         const long long work = (long long)a.max_light * ((a.H + kCols - 1) / kCols);
         prof_begin(K_DOWN_LIGHT, st);
         const int grid = grid_for(work, MOE_LIGHT_DN_BPC, a.num_cu);
-        if (a.pk_dn)
+        if (a.w_mxfp8)
+            down_light_mx_kernel<MOE_LIGHT_DN_TILES, MOE_LIGHT_MX_DN_U><<<grid, kThreads, 0, st>>>(a);
+        else if (a.pk_dn)
             down_light_kernel<MOE_LIGHT_DN_TILES, MOE_LIGHT_DN_U, MOE_LIGHT_NT_LOADS != 0, true>
                 <<<grid, kThreads, 0, st>>>(a);
         else

@@ -204,6 +204,13 @@ struct FfnArgs {
     int max_light;               // grid bound for light experts
     int num_cu;
     int y_bf16;                  // 1: y stored as bf16 (round to nearest even)
+    // MXFP8 routed weights (w_mxfp8 = 1): the light loop reads these instead
+    // of pk_gu / pk_dn and every expert takes it (no heavy tiles).
+    int w_mxfp8;
+    const uint8_t* q_gu;         // packed E4M3 codes of W_gate|up
+    const uint8_t* q_dn;         // packed E4M3 codes of W_down
+    const uint8_t* qs_gu;        // per-chunk E8M0 scales of W_gate|up
+    const uint8_t* qs_dn;        // per-chunk E8M0 scales of W_down
 };
 
 // Packed expert weights: 1 KB chunks, each the 16 weight rows x 32 K of one
@@ -224,6 +231,31 @@ size_t packed_gu_bytes(int E, int H, int I);
 size_t packed_dn_bytes(int E, int H, int I);
 hipError_t launch_pack_weights(const uint16_t* w_gu, const uint16_t* w_dn, int E, int H, int I,
                                char* packed, hipStream_t st);
+
+// Packed MXFP8 expert weights (OCP MX: E4M3 codes, one E8M0 scale per 32
+// values along K).  Codes: 1 KB chunks of 16 weight rows x 64 K in lane order
+// -- lane l holds row l % 16, its 16 bytes the codes of K 8(l/16)..+7 of the
+// chunk's first 32-wide K step, then those of its second; rows grouped as in
+// the bf16 packing (gate|up: gate rows 8g..8g+7 then up rows I+8g..; down:
+// W_down rows 16g..16g+15); chunks ordered (e, g, c) with c over ceil(K/64)
+// (down pads K past I with code 0).  Scales: 32 bytes per chunk, byte
+// 2*row + s the scale of the chunk's K step s for that row (127 = 2^0 for
+// padded steps), in the same (e, g, c) order.  Sections: gate|up codes, down
+// codes, gate|up scales, down scales.
+inline __host__ __device__ int mx_chunks(int K) { return (K + 63) / 64; }
+size_t mx_codes_gu_bytes(int E, int H, int I);
+size_t mx_codes_dn_bytes(int E, int H, int I);
+size_t mx_scales_gu_bytes(int E, int H, int I);
+size_t mx_scales_dn_bytes(int E, int H, int I);
+// Row-major MXFP8 of bf16 rows: codes [rows,K], scales [rows,K/32].
+hipError_t launch_mxfp8_quantize(const uint16_t* w, long long rows, int K, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t st);
+// Row-major codes/scales of both expert weights -> the packed layout above.
+hipError_t launch_pack_mxfp8(const uint8_t* c_gu, const uint8_t* s_gu, const uint8_t* c_dn,
+                             const uint8_t* s_dn, int E, int H, int I, char* packed,
+                             hipStream_t st);
+// light_max for layers whose every expert takes the light loop (MXFP8).
+constexpr int kLightAll = 1 << 30;
 
 hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st);

@@ -75,6 +75,8 @@ int check_shape(const moe_shape* s) {
         s->heavy_tile_rows != moe::kTileTM1 && s->heavy_tile_rows != moe::kTileTM2)
         return fail(MOE_ERR_UNSUPPORTED, "heavy_tile_rows must be 0, 128, 192 or 256");
     if (s->y_bf16 != 0 && s->y_bf16 != 1) return fail(MOE_ERR_UNSUPPORTED, "y_bf16 must be 0 or 1");
+    if (s->w_mxfp8 != 0 && s->w_mxfp8 != 1)
+        return fail(MOE_ERR_UNSUPPORTED, "w_mxfp8 must be 0 or 1");
     return MOE_OK;
 }
 
@@ -88,7 +90,13 @@ Layout layout(const moe_shape* s) {
     // The default is the per-call choice on the device (kLightAdaptive) from
     // 65 tokens on, with grids sized for either outcome; up to 64 tokens
     // every expert is light and no heavy kernel is launched.
-    if (s->light_max_rows < 0 && T <= moe::kLightRowsMax) {
+    if (s->w_mxfp8) {
+        // MXFP8 weights: every expert takes the light loop (in passes of 64
+        // rows), no heavy tile.
+        L.light_max = moe::kLightAll;
+        L.max_tiles = 0;
+        L.max_light = (int)std::min<long long>(E, A);
+    } else if (s->light_max_rows < 0 && T <= moe::kLightRowsMax) {
         L.light_max = moe::kLightRowsMax;
         L.max_tiles = 0;
         L.max_light = (int)std::min<long long>(E, A);
@@ -236,7 +244,14 @@ int run_ffn(const moe_shape* s, const Layout& L, const uint16_t* x, const int32_
     a.max_light = L.max_light;
     a.num_cu = ncu;
     a.y_bf16 = s->y_bf16;
-    if (packed) {
+    a.w_mxfp8 = s->w_mxfp8;
+    if (packed && s->w_mxfp8) {
+        const uint8_t* p = static_cast<const uint8_t*>(packed);
+        a.q_gu = p;
+        a.q_dn = a.q_gu + moe::mx_codes_gu_bytes(s->E, s->H, s->I);
+        a.qs_gu = a.q_dn + moe::mx_codes_dn_bytes(s->E, s->H, s->I);
+        a.qs_dn = a.qs_gu + moe::mx_scales_gu_bytes(s->E, s->H, s->I);
+    } else if (packed) {
         const char* p = static_cast<const char*>(packed);
         a.pk_gu = reinterpret_cast<const uint16_t*>(p);
         a.pk_dn = reinterpret_cast<const uint16_t*>(p + moe::packed_gu_bytes(s->E, s->H, s->I));
@@ -288,8 +303,43 @@ size_t moe_workspace_bytes(const moe_shape* shape) {
 
 size_t moe_packed_weight_bytes(const moe_shape* shape) {
     if (check_shape(shape) != MOE_OK) return 0;
-    return moe::packed_gu_bytes(shape->E, shape->H, shape->I) +
-           moe::packed_dn_bytes(shape->E, shape->H, shape->I);
+    const int E = shape->E, H = shape->H, I = shape->I;
+    if (shape->w_mxfp8)
+        return moe::mx_codes_gu_bytes(E, H, I) + moe::mx_codes_dn_bytes(E, H, I) +
+               moe::mx_scales_gu_bytes(E, H, I) + moe::mx_scales_dn_bytes(E, H, I);
+    return moe::packed_gu_bytes(E, H, I) + moe::packed_dn_bytes(E, H, I);
+}
+
+int moe_quantize_mxfp8(const uint16_t* w, int64_t rows, int32_t K, uint8_t* codes,
+                       uint8_t* scales, void* stream) {
+    g_last_error.clear();
+    if (rows < 0 || K <= 0) return fail(MOE_ERR_SHAPE, "rows must be >= 0 and K > 0");
+    if (K % 32) return fail(MOE_ERR_UNSUPPORTED, "K must be a multiple of 32");
+    if (rows == 0) return MOE_OK;
+    REQUIRE_PTR(w);
+    REQUIRE_PTR(codes);
+    if (!scales) return fail(MOE_ERR_NULL, "scales is NULL");
+    HIP_TRY(moe::launch_mxfp8_quantize(w, rows, K, codes, scales, (hipStream_t)stream),
+            "quantize mxfp8");
+    return MOE_OK;
+}
+
+int moe_pack_weights_mxfp8(const moe_shape* shape, const uint8_t* codes_gate_up,
+                           const uint8_t* scales_gate_up, const uint8_t* codes_down,
+                           const uint8_t* scales_down, void* packed, void* stream) {
+    g_last_error.clear();
+    if (int rc = check_shape(shape)) return rc;
+    if (!shape->w_mxfp8) return fail(MOE_ERR_SHAPE, "moe_pack_weights_mxfp8 needs w_mxfp8 = 1");
+    REQUIRE_PTR(codes_gate_up);
+    REQUIRE_PTR(codes_down);
+    if (!scales_gate_up || !scales_down) return fail(MOE_ERR_NULL, "a scales array is NULL");
+    if (!packed) return fail(MOE_ERR_NULL, "packed is NULL");
+    if (!aligned(packed, kAlign)) return fail(MOE_ERR_ALIGN, "packed must be 256-byte aligned");
+    HIP_TRY(moe::launch_pack_mxfp8(codes_gate_up, scales_gate_up, codes_down, scales_down,
+                                   shape->E, shape->H, shape->I, static_cast<char*>(packed),
+                                   (hipStream_t)stream),
+            "pack mxfp8 weights");
+    return MOE_OK;
 }
 
 int moe_pack_weights(const moe_shape* shape, const uint16_t* w_gate_up, const uint16_t* w_down,
@@ -388,8 +438,12 @@ int moe_grouped_ffn(const moe_shape* shape, const uint16_t* x, const int32_t* so
     REQUIRE_PTR(x);
     REQUIRE_PTR(sorted_token_ids);
     REQUIRE_PTR(offsets);
-    REQUIRE_PTR(w_gate_up);
-    REQUIRE_PTR(w_down);
+    if (shape->w_mxfp8) {
+        if (!packed_weights) return fail(MOE_ERR_NULL, "w_mxfp8 = 1 needs packed_weights");
+    } else {
+        REQUIRE_PTR(w_gate_up);
+        REQUIRE_PTR(w_down);
+    }
     REQUIRE_PTR(y);
     OPTIONAL_PTR(h);
     if (packed_weights && !aligned(packed_weights, kAlign))
@@ -450,8 +504,12 @@ int moe_forward(const moe_shape* shape, const uint16_t* x, const float* w_router
     }
     REQUIRE_PTR(x);
     REQUIRE_PTR(w_router);
-    REQUIRE_PTR(w_gate_up);
-    REQUIRE_PTR(w_down);
+    if (shape->w_mxfp8) {
+        if (!packed_weights) return fail(MOE_ERR_NULL, "w_mxfp8 = 1 needs packed_weights");
+    } else {
+        REQUIRE_PTR(w_gate_up);
+        REQUIRE_PTR(w_down);
+    }
     REQUIRE_PTR(out);
     OPTIONAL_PTR(bias);
     OPTIONAL_PTR(topk_ids_out);

@@ -29,7 +29,8 @@ MOE_ERR_HIP = 6
 EXPORTED = ("moe_workspace_bytes", "moe_packed_weight_bytes", "moe_status_string",
             "moe_last_error", "moe_router", "moe_permute", "moe_pack_weights", "moe_grouped_ffn",
             "moe_shared_ffn", "moe_combine", "moe_forward", "moe_profile_kernel",
-            "moe_profile_kernel_launch", "moe_profile_launches")
+            "moe_profile_kernel_launch", "moe_profile_launches", "moe_quantize_mxfp8",
+            "moe_pack_weights_mxfp8")
 
 # enum moe_kernel
 KERNELS = ("router_gemm", "router_select", "perm_count", "perm_scan", "perm_scatter", "ffn_plan",
@@ -47,6 +48,8 @@ def light_experts(counts, shape):
     import numpy as np
     counts = np.asarray(counts)
     lm = shape.light_max_rows
+    if shape.w_mxfp8:
+        return counts >= 1  # MXFP8 weights: every expert takes the light loop
     if lm < 0:
         if shape.T <= LIGHT_MAX_ROWS:
             lm = LIGHT_MAX_ROWS
@@ -62,7 +65,8 @@ class MoeShape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("I", ctypes.c_int32), ("I_shared", ctypes.c_int32),
                 ("renorm", ctypes.c_int32), ("light_max_rows", ctypes.c_int32),
-                ("heavy_tile_rows", ctypes.c_int32), ("y_bf16", ctypes.c_int32)]
+                ("heavy_tile_rows", ctypes.c_int32), ("y_bf16", ctypes.c_int32),
+                ("w_mxfp8", ctypes.c_int32)]
 
     def __repr__(self):
         return ("MoeShape(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")")
@@ -90,6 +94,8 @@ def lib() -> ctypes.CDLL:
         L.moe_packed_weight_bytes.argtypes = [_sp]
         L.moe_packed_weight_bytes.restype = ctypes.c_size_t
         L.moe_pack_weights.argtypes = [_sp] + [_vp] * 4
+        L.moe_quantize_mxfp8.argtypes = [_vp, ctypes.c_int64, ctypes.c_int32, _vp, _vp, _vp]
+        L.moe_pack_weights_mxfp8.argtypes = [_sp] + [_vp] * 6
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_last_error.argtypes = []
@@ -126,9 +132,9 @@ def _check(rc: int) -> None:
 
 
 def make_shape(T, H, E, k, I, I_shared=0, renorm=1, light_max_rows=-1,
-               heavy_tile_rows=0, y_bf16=0) -> MoeShape:
+               heavy_tile_rows=0, y_bf16=0, w_mxfp8=0) -> MoeShape:
     return MoeShape(T, H, E, k, I, I_shared, renorm, light_max_rows, heavy_tile_rows,
-                    int(bool(y_bf16)))
+                    int(bool(y_bf16)), int(bool(w_mxfp8)))
 
 
 def workspace_bytes(shape: MoeShape) -> int:
@@ -159,6 +165,41 @@ def pack_weights(shape: MoeShape, w_gate_up, w_down, stream=None) -> torch.Tenso
                                   _ptr(w_gate_up, "w_gate_up", BF16, E * 2 * I * H),
                                   _ptr(w_down, "w_down", BF16, E * H * I), out.data_ptr(),
                                   _stream(stream)))
+    return out
+
+
+def quantize_mxfp8(w, stream=None):
+    """MXFP8 (OCP MX, E4M3 codes, one E8M0 scale per 32 values along the last
+    dimension) of a bf16 device tensor [..., K]: returns (codes uint8
+    [..., K], scales uint8 [..., K/32]) (moe_quantize_mxfp8)."""
+    if w.dtype != BF16 or not w.is_cuda or not w.is_contiguous():
+        raise ValueError("w must be a contiguous bf16 device tensor")
+    K = w.shape[-1]
+    rows = w.numel() // K if K else 0
+    codes = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    scales = torch.empty(w.shape[:-1] + (K // 32,), dtype=torch.uint8, device=w.device)
+    _check(lib().moe_quantize_mxfp8(w.data_ptr(), rows, K, codes.data_ptr(), scales.data_ptr(),
+                                    _stream(stream)))
+    return codes, scales
+
+
+def pack_weights_mxfp8(shape: MoeShape, codes_gate_up, scales_gate_up, codes_down, scales_down,
+                       stream=None) -> torch.Tensor:
+    """Packed MXFP8 expert weights for a shape with w_mxfp8 = 1
+    (moe_pack_weights_mxfp8); returns the uint8 device buffer."""
+    if not shape.w_mxfp8:
+        raise ValueError("shape.w_mxfp8 must be 1")
+    n = packed_weight_bytes(shape)
+    if n == 0:
+        raise MoeError(MOE_ERR_SHAPE, f"invalid shape {shape}")
+    E, H, I = shape.E, shape.H, shape.I
+    U8 = torch.uint8
+    out = torch.empty(n, dtype=U8, device=codes_gate_up.device)
+    _check(lib().moe_pack_weights_mxfp8(
+        ctypes.byref(shape), _ptr(codes_gate_up, "codes_gate_up", U8, E * 2 * I * H),
+        _ptr(scales_gate_up, "scales_gate_up", U8, E * 2 * I * H // 32),
+        _ptr(codes_down, "codes_down", U8, E * H * I),
+        _ptr(scales_down, "scales_down", U8, E * H * I // 32), out.data_ptr(), _stream(stream)))
     return out
 
 
@@ -227,8 +268,10 @@ def grouped_ffn(shape, x, sorted_token_ids, offsets, w_gate_up, w_down, h, y, wo
                 stream=None, packed_weights=None):
     T, H, E, I, A = shape.T, shape.H, shape.E, shape.I, shape.T * shape.k
     args = [_ptr(x, "x", BF16, T * H), _ptr(sorted_token_ids, "sorted_token_ids", I32, A),
-            _ptr(offsets, "offsets", I32, E + 1), _ptr(w_gate_up, "w_gate_up", BF16, E * 2 * I * H),
-            _ptr(w_down, "w_down", BF16, E * H * I), _packed(packed_weights, shape),
+            _ptr(offsets, "offsets", I32, E + 1),
+            _ptr(w_gate_up, "w_gate_up", BF16, E * 2 * I * H, optional=bool(shape.w_mxfp8)),
+            _ptr(w_down, "w_down", BF16, E * H * I, optional=bool(shape.w_mxfp8)),
+            _packed(packed_weights, shape),
             _ptr(h, "h", BF16, A * I, optional=True),
             _ptr(y, "y", y_dtype(shape), A * H)]
     wp, wn = _ws(workspace, shape)
@@ -261,8 +304,9 @@ def forward(shape, x, w_router, bias, w_gate_up, w_down, ws_gate_up, ws_down, ou
     T, H, E, k, I, Is = shape.T, shape.H, shape.E, shape.k, shape.I, shape.I_shared
     args = [_ptr(x, "x", BF16, T * H), _ptr(w_router, "w_router", F32, H * E),
             _ptr(bias, "bias", F32, E, optional=True),
-            _ptr(w_gate_up, "w_gate_up", BF16, E * 2 * I * H),
-            _ptr(w_down, "w_down", BF16, E * H * I), _packed(packed_weights, shape),
+            _ptr(w_gate_up, "w_gate_up", BF16, E * 2 * I * H, optional=bool(shape.w_mxfp8)),
+            _ptr(w_down, "w_down", BF16, E * H * I, optional=bool(shape.w_mxfp8)),
+            _packed(packed_weights, shape),
             _ptr(ws_gate_up, "ws_gate_up", BF16, 2 * Is * H, optional=True),
             _ptr(ws_down, "ws_down", BF16, H * Is, optional=True),
             _ptr(out, "out", F32, T * H),
@@ -296,13 +340,24 @@ class MoELayer:
     moe_forward and returns (out, topk_ids, topk_w, counts)."""
 
     def __init__(self, layer, light_max_rows: int = -1, heavy_tile_rows: int = 0,
-                 packed: bool = False, y_bf16: bool = False):
+                 packed: bool = False, y_bf16: bool = False, weights: str = "bf16"):
+        """weights="mxfp8" quantises the routed expert weights to MXFP8 on the
+        device and runs the layer on them (packed implied)."""
+        if weights not in ("bf16", "mxfp8"):
+            raise ValueError("weights must be 'bf16' or 'mxfp8'")
         c = layer.cfg
         self.layer = layer
+        mx = weights == "mxfp8"
         self.shape = make_shape(c.T, c.H, c.E, c.k, c.I, c.I_shared, c.renorm, light_max_rows,
-                                heavy_tile_rows, y_bf16)
+                                heavy_tile_rows, y_bf16, mx)
         self.workspace = alloc_workspace(self.shape, layer.x.device)
-        self.packed = pack_weights(self.shape, layer.w_gu, layer.w_dn) if packed else None
+        if mx:
+            q_gu, s_gu = quantize_mxfp8(layer.w_gu)
+            q_dn, s_dn = quantize_mxfp8(layer.w_dn)
+            self.packed = pack_weights_mxfp8(self.shape, q_gu, s_gu, q_dn, s_dn)
+            del q_gu, s_gu, q_dn, s_dn
+        else:
+            self.packed = pack_weights(self.shape, layer.w_gu, layer.w_dn) if packed else None
 
     def __call__(self, x=None, out=None, want_routing=True):
         L, s = self.layer, self.shape
@@ -312,6 +367,6 @@ class MoELayer:
         ids = torch.empty((s.T, s.k), dtype=I32, device=dev) if want_routing else None
         w = torch.empty((s.T, s.k), dtype=F32, device=dev) if want_routing else None
         counts = torch.empty((s.E,), dtype=I32, device=dev) if want_routing else None
-        forward(s, x, L.wg, L.bias, L.w_gu, L.w_dn, L.ws_gu, L.ws_dn, out, self.workspace,
-                ids, w, counts, packed_weights=self.packed)
+        forward(s, x, L.wg, L.bias, None if s.w_mxfp8 else L.w_gu, None if s.w_mxfp8 else L.w_dn,
+                L.ws_gu, L.ws_dn, out, self.workspace, ids, w, counts, packed_weights=self.packed)
         return out, ids, w, counts

@@ -99,6 +99,13 @@ typedef struct moe_shape {
                                before the fp32 weighted sum, so it suits layers whose
                                |y| are small against the output tolerance.  The shared
                                expert's output is always fp32. */
+    int32_t w_mxfp8;        /* routed expert weights: 0 = bf16 (w_gate_up / w_down, optionally
+                               packed); 1 = MXFP8, given only as the packed buffer of
+                               moe_pack_weights_mxfp8 (see there).  With 1 every expert takes
+                               the light loop (in passes of 64 rows; light_max_rows and
+                               heavy_tile_rows are ignored) and the results are those of the
+                               bf16 path on the dequantised weights, bit for bit.  The shared
+                               expert stays bf16. */
 } moe_shape;
 
 /* Bytes of workspace every call below needs for `shape` (host-only, pure;
@@ -106,8 +113,9 @@ typedef struct moe_shape {
 size_t moe_workspace_bytes(const moe_shape* shape);
 
 /* Bytes of the packed expert-weight buffer for `shape` (host-only, pure;
- * 0 for an invalid shape): the size of W_gate|up plus W_down,
- * E * 3 * I * H * 2. */
+ * 0 for an invalid shape).  bf16 (w_mxfp8 = 0): the size of W_gate|up plus
+ * W_down, E * 3 * I * H * 2.  MXFP8 (w_mxfp8 = 1): one byte per weight (K of
+ * W_down padded to a multiple of 64) plus one scale byte per 32 weights. */
 size_t moe_packed_weight_bytes(const moe_shape* shape);
 
 /* Static text for a status code. */
@@ -170,6 +178,38 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t* counts
 int moe_pack_weights(const moe_shape* shape, const uint16_t* w_gate_up, const uint16_t* w_down,
                      void* packed, void* stream);
 
+/* MXFP8 quantisation of bf16 weight rows (a variant with 8-bit routed expert
+ * weights; the pages name FP8 scaling blocks -- pwwt.cn article, section 6 --
+ * and MX formats -- first page, section 3 -- but fix no weight format).
+ * Format: OCP Microscaling Formats (MX) specification v1.0, MXFP8 with E4M3
+ * elements: each 32 consecutive values of a row share an E8M0 scale code s8
+ * (X = 2^(s8 - 127)); each value is an E4M3 code (bias 7, 3 mantissa bits,
+ * largest finite 448).  Per block, as the specification converts:
+ * shared exponent floor(log2 max|v|) - 8 clamped to [-127, 127] (an all-zero
+ * block: -127); value / X rounded to the nearest E4M3 value, ties to the
+ * even mantissa, saturated at +-448, sign kept (also for zero).
+ *   w       bf16 [rows,K], finite (codes of non-finite values are unspecified)
+ *   codes   uint8 [rows,K] out (16-byte aligned)
+ *   scales  uint8 [rows,K/32] out (any alignment)
+ * K % 32 == 0 (else MOE_ERR_UNSUPPORTED); rows == 0 is a no-op.  For expert
+ * weights pass W_gate|up as rows = E*2I, K = H and W_down as rows = E*H,
+ * K = I (blocks run along the reduction dimension). */
+int moe_quantize_mxfp8(const uint16_t* w, int64_t rows, int32_t K, uint8_t* codes,
+                       uint8_t* scales, void* stream);
+
+/* Packs MXFP8 expert weights (codes and scales as moe_quantize_mxfp8 writes
+ * them for W_gate|up [E,2I,H] and W_down [E,H,I]) for the light loop, into
+ * `packed` (moe_packed_weight_bytes(shape) bytes, 256-byte aligned) with
+ * shape->w_mxfp8 = 1.  Codes become 1 KB chunks of 16 weight rows x 64 K in
+ * lane order (lane l: row l%16, the codes of K 8(l/16)..+7 of the chunk's
+ * first 32-wide K step, then of its second), rows grouped as for
+ * moe_pack_weights; each chunk's scales are 32 bytes (row r's two steps at
+ * 2r, 2r+1).  The result is passed to moe_grouped_ffn / moe_forward as
+ * packed_weights. */
+int moe_pack_weights_mxfp8(const moe_shape* shape, const uint8_t* codes_gate_up,
+                           const uint8_t* scales_gate_up, const uint8_t* codes_down,
+                           const uint8_t* scales_down, void* packed, void* stream);
+
 /* Grouped expert FFN over the expert-major rows (pwwt.cn section 4.2):
  *   h[r,:] = bf16( silu(x[tok_r] . W_gate[e]) * (x[tok_r] . W_up[e]) )
  *   y[r,:] = h[r,:] . W_down[e]   (fp32 sum)      for rows r of expert e,
@@ -182,7 +222,10 @@ int moe_pack_weights(const moe_shape* shape, const uint16_t* w_gate_up, const ui
  *   w_down           bf16 [E,H,I]:  W_down^T
  *   packed_weights   the same weights from moe_pack_weights, or NULL; when
  *                    given, the light loop reads it instead of w_gate_up /
- *                    w_down (the heavy tiles always read those)
+ *                    w_down (the heavy tiles always read those).  With
+ *                    shape->w_mxfp8 = 1 it is required (from
+ *                    moe_pack_weights_mxfp8) and w_gate_up / w_down are not
+ *                    read (may be NULL)
  *   h                bf16 [T*k,I] out, or NULL (then kept in the workspace)
  *   y                [T*k,H] out: fp32 (shape->y_bf16 == 0; large |y| entering
  *                    the weighted sum keep 24 significant bits) or bf16
@@ -219,7 +262,8 @@ int moe_combine(const moe_shape* shape, const void* y, const int32_t* inv_pos,
  * shape->I_shared > 0), combine.  out fp32 [T,H]:
  *   out[t] = sum_j w[t,j] FFN_{ids[t,j]}(x[t])  (+ FFN_shared(x[t]))
  * ws_gate_up / ws_down are required iff I_shared > 0; packed_weights is
- * optional, as for moe_grouped_ffn.  topk_ids_out [T,k],
+ * optional, as for moe_grouped_ffn (required, and w_gate_up / w_down unused,
+ * with shape->w_mxfp8 = 1).  topk_ids_out [T,k],
  * topk_w_out [T,k] and counts_out [E] are optional copies of the routing
  * (NULL = not written). */
 int moe_forward(const moe_shape* shape, const uint16_t* x, const float* w_router,

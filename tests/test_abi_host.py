@@ -42,7 +42,7 @@ def test_library_has_gfx950_code():
 
 def shp(**kw):
     base = dict(T=64, H=4096, E=512, k=10, I=1024, I_shared=0, renorm=1, light_max_rows=-1,
-                heavy_tile_rows=0, y_bf16=0)
+                heavy_tile_rows=0, y_bf16=0, w_mxfp8=0)
     base.update(kw)
     return moe.MoeShape(*[base[n] for n, _ in moe.MoeShape._fields_])
 
@@ -82,6 +82,7 @@ def test_workspace_bf16_y(L):
     (dict(T=1 << 19, k=1), moe.MOE_ERR_UNSUPPORTED), (dict(I=1 << 18), moe.MOE_ERR_UNSUPPORTED),
     (dict(I_shared=1 << 18), moe.MOE_ERR_UNSUPPORTED),
     (dict(y_bf16=2), moe.MOE_ERR_UNSUPPORTED), (dict(y_bf16=-1), moe.MOE_ERR_UNSUPPORTED),
+    (dict(w_mxfp8=2), moe.MOE_ERR_UNSUPPORTED), (dict(w_mxfp8=-1), moe.MOE_ERR_UNSUPPORTED),
 ])
 def test_bad_shapes(L, kw, code):
     s = shp(**kw)
@@ -162,3 +163,49 @@ def test_pack_weights_argument_errors(L):
     # a misaligned packed buffer is refused before anything is enqueued
     assert L.moe_grouped_ffn(ctypes.byref(s), P, P, P, P, P, ctypes.c_void_p(0x10010), None, P, P,
                              need, None) == moe.MOE_ERR_ALIGN
+
+
+def test_mxfp8_packed_bytes(L):
+    """MXFP8 packed weights: one byte per weight (W_down's K padded to 64)
+    plus a scale byte per 32 weights; bf16 packing stays 2 bytes per weight."""
+    for (H, I) in ((4096, 1024), (64, 96), (128, 32)):
+        E = 8
+        b16 = moe.packed_weight_bytes(shp(E=E, H=H, I=I, k=2))
+        mx = moe.packed_weight_bytes(shp(E=E, H=H, I=I, k=2, w_mxfp8=1))
+        assert b16 == E * 3 * I * H * 2
+        Ip = (I + 63) // 64 * 64
+        assert mx == E * (2 * I * H + H * Ip) * (1 + 1 / 32)
+
+
+def test_mxfp8_argument_errors(L):
+    """Quantiser and MXFP8 packer validate before any HIP call; with
+    w_mxfp8 = 1 the layer needs the packed weights and not the bf16 ones."""
+    P = ctypes.c_void_p(0x10000)
+    bad = ctypes.c_void_p(0x10008)
+    assert L.moe_quantize_mxfp8(P, 4, 48, P, P, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_quantize_mxfp8(P, -1, 64, P, P, None) == moe.MOE_ERR_SHAPE
+    assert L.moe_quantize_mxfp8(P, 0, 64, None, None, None) == moe.MOE_OK
+    assert L.moe_quantize_mxfp8(None, 4, 64, P, P, None) == moe.MOE_ERR_NULL
+    assert L.moe_quantize_mxfp8(bad, 4, 64, P, P, None) == moe.MOE_ERR_ALIGN
+    assert L.moe_quantize_mxfp8(P, 4, 64, P, None, None) == moe.MOE_ERR_NULL
+    s16, smx = shp(), shp(w_mxfp8=1)
+    assert L.moe_pack_weights_mxfp8(ctypes.byref(s16), P, P, P, P, P, None) == moe.MOE_ERR_SHAPE
+    assert L.moe_pack_weights_mxfp8(ctypes.byref(smx), P, None, P, P, P, None) == moe.MOE_ERR_NULL
+    assert L.moe_pack_weights_mxfp8(ctypes.byref(smx), P, P, P, P,
+                                    ctypes.c_void_p(0x10010), None) == moe.MOE_ERR_ALIGN
+    need = moe.workspace_bytes(smx)
+    # no packed weights with w_mxfp8 = 1
+    assert L.moe_grouped_ffn(ctypes.byref(smx), P, P, P, None, None, None, None, P, P, need,
+                             None) == moe.MOE_ERR_NULL
+    assert "packed" in moe.last_error()
+    assert L.moe_forward(ctypes.byref(smx), P, P, None, None, None, None, None, None, P, None, None,
+                         None, P, need, None) == moe.MOE_ERR_NULL
+    assert "packed" in moe.last_error()
+
+
+def test_mxfp8_light_rule():
+    """With MXFP8 weights every touched expert takes the light loop."""
+    import numpy as np
+    counts = np.array([0, 1, 64, 65, 500, 3000])
+    assert list(moe.light_experts(counts, shp(T=8192, w_mxfp8=1))) == [False] + [True] * 5
+    assert not moe.light_experts(counts, shp(T=8192)).any()
