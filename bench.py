@@ -57,6 +57,9 @@ def parse():
                    help="storage of the routed expert outputs between the down GEMM and the "
                         "combine; auto = bf16 except for a layer with a shared expert or "
                         "fp32 values (their outputs need the fp32 margin)")
+    p.add_argument("--weights", choices=("bf16", "mxfp8"), default="bf16",
+                   help="routed expert weights: bf16, or MXFP8 (OCP MX E4M3 codes with one "
+                        "E8M0 scale per 32 values, quantised on the GPU before timing)")
     p.add_argument("--no-copy-calibration", action="store_true",
                    help="skip the untimed 1 GiB reference copy used to scale rocprof counters")
     p.add_argument("--summarize", nargs=4, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR", "LOG"),
@@ -69,16 +72,22 @@ def parse():
 # The profiling runs that profiles/<kernel>__<workload>.{md,traffic.json}
 # summarise; $R is the repository root, run from /tmp with TMPDIR=/tmp.
 PROFILE_COMMANDS = (
-    "rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/kt_{cfg} -o bench -- "
-    "python3 $R/bench.py --config {cfg} --steps 10 --warmup 2 --no-cpu-baseline "
-    "> $R/gpurun_out/kt_{cfg}.log",
-    "timeout -s KILL 150 rocprofv3 --pmc FETCH_SIZE -f csv -d $R/gpurun_out/fetch_{cfg} -o bench -- "
-    "python3 $R/bench.py --config {cfg} --steps 3 --warmup 1 --no-cpu-baseline",
-    "timeout -s KILL 150 rocprofv3 --pmc WRITE_SIZE -f csv -d $R/gpurun_out/write_{cfg} -o bench -- "
-    "python3 $R/bench.py --config {cfg} --steps 3 --warmup 1 --no-cpu-baseline",
-    "python3 $R/bench.py --config {cfg} --summarize $R/gpurun_out/kt_{cfg} "
-    "$R/gpurun_out/fetch_{cfg} $R/gpurun_out/write_{cfg} $R/gpurun_out/kt_{cfg}.log",
+    "rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/kt_{cfg}{tag} -o bench -- "
+    "python3 $R/bench.py --config {cfg}{extra} --steps 10 --warmup 2 --no-cpu-baseline "
+    "> $R/gpurun_out/kt_{cfg}{tag}.log",
+    "timeout -s KILL 150 rocprofv3 --pmc FETCH_SIZE -f csv -d $R/gpurun_out/fetch_{cfg}{tag} -o bench -- "
+    "python3 $R/bench.py --config {cfg}{extra} --steps 3 --warmup 1 --no-cpu-baseline",
+    "timeout -s KILL 150 rocprofv3 --pmc WRITE_SIZE -f csv -d $R/gpurun_out/write_{cfg}{tag} -o bench -- "
+    "python3 $R/bench.py --config {cfg}{extra} --steps 3 --warmup 1 --no-cpu-baseline",
+    "python3 $R/bench.py --config {cfg}{extra} --summarize $R/gpurun_out/kt_{cfg}{tag} "
+    "$R/gpurun_out/fetch_{cfg}{tag} $R/gpurun_out/write_{cfg}{tag} $R/gpurun_out/kt_{cfg}{tag}.log",
 )
+
+
+def workload_of(cfg, weights: str) -> str:
+    """Workload name: the layer's shape, plus the weight format when not bf16."""
+    from expert_ffn_layer_amd import synth
+    return synth.workload_name(cfg) + ("" if weights == "bf16" else f"_{weights}")
 # bench.py's own untimed reference copy (torch.neg over 2^28 fp32 values):
 # it reads and writes exactly 1 GiB.
 COPY_BYTES = 1 << 30
@@ -91,6 +100,8 @@ def kernel_label(name: str):
     if not m:
         return None
     base = m.group(1)
+    if base.endswith("_mx_kernel"):  # MXFP8-weight variants of the light loops
+        base = base[:-len("_mx_kernel")] + "_kernel"
     if base == "ffn_heavy_kernel":
         return "gateup_heavy" if "Mode)0" in name else "down_heavy"
     if base.startswith("router_select"):  # block- and wave-per-token variants
@@ -108,7 +119,7 @@ def summarize(args):
 
     kt_dir, fetch_dir, write_dir, log = args.summarize
     cfg = synth.CONFIGS[args.config]
-    workload = synth.workload_name(cfg)
+    workload = workload_of(cfg, args.weights)
 
     def one_csv(d, suffix):
         names = [f for f in os.listdir(d) if f.endswith(suffix)]
@@ -176,7 +187,10 @@ def summarize(args):
         json.dump(out, f, indent=1)
         f.write("\n")
 
-    cmds = "\n".join(c.format(cfg=args.config) for c in PROFILE_COMMANDS)
+    mxw = args.weights != "bf16"
+    cmds = "\n".join(c.format(cfg=args.config, tag=f"_{args.weights}" if mxw else "",
+                              extra=f" --weights {args.weights}" if mxw else "")
+                     for c in PROFILE_COMMANDS)
     lines = [f"# {dom} on {workload}", "",
              "rocprofv3 summary of bench.py on one MI355X (gfx950).  Commands, from /tmp with",
              "TMPDIR=/tmp, $R the repository root:", "", "```", cmds, "```", "",
@@ -253,8 +267,10 @@ def main():
         layer = layer.rounded_to_bf16()
     y_bf16 = args.y_dtype == "bf16" or (args.y_dtype == "auto" and not cfg.I_shared
                                         and not cfg.fp32_values)
-    m = moe.MoELayer(layer, packed=not args.no_packed, y_bf16=y_bf16)
+    mx = args.weights == "mxfp8"
+    m = moe.MoELayer(layer, packed=not args.no_packed, y_bf16=y_bf16, weights=args.weights)
     s = m.shape
+    w_gu_arg, w_dn_arg = (None, None) if mx else (layer.w_gu, layer.w_dn)
     out = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=dev)
     ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
     w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
@@ -262,7 +278,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step():
-        moe.forward(s, layer.x, layer.wg, layer.bias, layer.w_gu, layer.w_dn, layer.ws_gu,
+        moe.forward(s, layer.x, layer.wg, layer.bias, w_gu_arg, w_dn_arg, layer.ws_gu,
                     layer.ws_dn, out, m.workspace, ids, w, counts, stream=stream,
                     packed_weights=m.packed)
 
@@ -324,6 +340,14 @@ def main():
     x_bytes = cfg.T * H * 2
     y_el = 2 if y_bf16 else 4  # bytes per stored y value
     Is = cfg.I_shared
+    # Bytes of one routed expert's weights as the kernels stream them: bf16,
+    # or MXFP8 codes (W_down's K padded to 64) plus a scale byte per 32.
+    if mx:
+        i_pad = (I + 63) // 64 * 64
+        gu_w = 2 * I * H * (1 + 1 / 32)
+        dn_w = H * i_pad * (1 + 1 / 32)
+    else:
+        gu_w, dn_w = 2 * I * H * 2, H * I * 2
     if dominant == "gateup_heavy" and dom_launch == 1:  # the shared expert, dense over T
         alg = 2 * Is * H * 2 + x_bytes + cfg.T * 2 * Is * 2  # h kept as a bf16 hi|lo pair
         flops = 4 * cfg.T * H * Is
@@ -331,10 +355,10 @@ def main():
         alg = H * Is * 2 + cfg.T * 2 * Is * 2 + cfg.T * H * 4
         flops = 2 * cfg.T * H * Is
     elif dominant == "gateup_light":
-        alg = light_experts * 2 * I * H * 2 + x_bytes + light_rows * I * 2
+        alg = light_experts * gu_w + x_bytes + light_rows * I * 2
         flops = 4 * light_rows * H * I
     elif dominant == "down_light":
-        alg = light_experts * H * I * 2 + light_rows * (I * 2 + H * y_el)
+        alg = light_experts * dn_w + light_rows * (I * 2 + H * y_el)
         flops = 2 * light_rows * H * I
     elif dominant == "gateup_heavy":
         he = touched - light_experts
@@ -359,7 +383,7 @@ def main():
     peak_flops = FP32_PEAK_TFLOPS if dominant == "router_gemm" else BF16_PEAK_TFLOPS
     t_mfma = flops / (peak_flops * 1e12)
     src_hash = kernel_source_hash()
-    workload = synth.workload_name(cfg)
+    workload = workload_of(cfg, args.weights)
     # (committed counter summaries cover a kernel's first launch of a step)
     traffic = committed_traffic(dominant, workload, src_hash) if dom_launch == 0 else None
     if t_mfma > t_hbm:
@@ -375,7 +399,7 @@ def main():
                  "algorithmic_bytes": int(alg), "flops": int(flops)})
 
     # Whole-layer roofline (weights of touched experts + x + router + out).
-    layer_bytes = touched * 3 * H * I * 2 + x_bytes + H * cfg.E * 4 + cfg.T * H * 4
+    layer_bytes = int(touched * (gu_w + dn_w)) + x_bytes + H * cfg.E * 4 + cfg.T * H * 4
     if cfg.I_shared:
         layer_bytes += 3 * H * cfg.I_shared * 2
     layer_flops = 6 * A * H * I + (6 * cfg.T * H * cfg.I_shared if cfg.I_shared else 0)
@@ -396,7 +420,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(layer_obj=m.layer, cfg=cfg, n=args.cpu_sample, gpu_out=out)
+        cpu = cpu_baseline(layer_obj=m.layer, cfg=cfg, n=args.cpu_sample, gpu_out=out, mx=mx)
 
     rec = {
         "metric": "MoE-layer tokens/s",
@@ -414,7 +438,8 @@ def main():
         "config": {"workload": workload, "tokens": cfg.T, "hidden": H, "experts": cfg.E,
                    "top_k": cfg.k, "intermediate": I, "shared_intermediate": cfg.I_shared,
                    "seed": args.seed, "packed_weights": m.packed is not None,
-                   "y_dtype": "bf16" if y_bf16 else "fp32"},
+                   "y_dtype": "bf16" if y_bf16 else "fp32",
+                   "weights": "mxfp8 (E4M3, E8M0 per 32)" if mx else "bf16"},
         "roofline": roof,
         "layer_roofline": layer,
         "kernels_us": {k: round(v, 2) for k, v in per_kernel.items()},
@@ -424,10 +449,12 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline(layer_obj, cfg, n, gpu_out):
+def cpu_baseline(layer_obj, cfg, n, gpu_out, mx=False):
     """The oracle (plain fp32 C loops, OpenMP over rows) on the first n tokens
     of the same layer, weights already on the host; also reports its
-    agreement with the GPU output on those tokens."""
+    agreement with the GPU output on those tokens.  With MXFP8 weights the
+    oracle first quantises and dequantises (untimed) the experts those tokens
+    reach, then runs the same forward on them."""
     import numpy as np
     import torch
 
@@ -443,6 +470,14 @@ def cpu_baseline(layer_obj, cfg, n, gpu_out):
     w_dn = layer_obj.w_dn.cpu()
     ws_gu = None if layer_obj.ws_gu is None else layer_obj.ws_gu.cpu()
     ws_dn = None if layer_obj.ws_dn is None else layer_obj.ws_dn.cpu()
+    if mx:
+        r = o.route(o.logits(x, wg, bias), cfg.k, cfg.renorm)
+        deq_gu, deq_dn = {}, {}
+        for e in np.unique(r["ids"]):
+            for src, dst in ((w_gu, deq_gu), (w_dn, deq_dn)):
+                c, sc = o.mxfp8_quantize(src[int(e)].float().numpy())
+                dst[int(e)] = o.mxfp8_dequantize(c, sc)
+        w_gu, w_dn = deq_gu, deq_dn
     print(f"[bench] cpu baseline: oracle on {n} tokens", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     ref = o.forward(x, wg, bias, w_gu, w_dn, cfg.k, cfg.renorm, ws_gu, ws_dn, permute=False)
@@ -454,7 +489,8 @@ def cpu_baseline(layer_obj, cfg, n, gpu_out):
     return {"value": round(n / wall, 3), "unit": "tokens/s", "cores": o.max_threads(),
             "kind": "oracle",
             "sample": f"first {n} of {cfg.T} tokens of the same layer (routing, all their expert "
-                      f"FFN rows, combine); fp32 C loops; expert weights pre-copied to host",
+                      f"FFN rows, combine); fp32 C loops; expert weights pre-copied to host"
+                      + (" (MXFP8-dequantised by the oracle, untimed)" if mx else ""),
             "wall_s": round(wall, 3),
             "gpu_vs_oracle": {"max_abs": float(np.abs(d).max()),
                               "rel_l2": float(np.linalg.norm(d) / np.linalg.norm(ref["out"]))}}

@@ -449,10 +449,16 @@ __global__ __launch_bounds__(kThreads) void down_light_kernel(FfnArgs a) {
 // the two give bitwise identical results.  Experts with more than 64 rows run
 // in passes of 64 rows (the weights are then read once per pass).
 #ifndef MOE_LIGHT_MX_GU_U
-#define MOE_LIGHT_MX_GU_U 8     // 64-wide K chunks in flight per wave (gate|up)
+#define MOE_LIGHT_MX_GU_U 2     // 64-wide K chunks in flight per wave (gate|up)
 #endif
 #ifndef MOE_LIGHT_MX_DN_U
-#define MOE_LIGHT_MX_DN_U 4
+#define MOE_LIGHT_MX_DN_U 2
+#endif
+#ifndef MOE_LIGHT_MX_GU_TILES
+#define MOE_LIGHT_MX_GU_TILES 2
+#endif
+#ifndef MOE_LIGHT_MX_DN_TILES
+#define MOE_LIGHT_MX_DN_TILES 2
 #endif
 constexpr int kLightMxWideU = 1;  // chunks in flight, 17..64-row branch
 
@@ -1401,12 +1407,13 @@ hipError_t launch_ffn_plan(const int32_t* offsets, int E, int light_max, int for
 
 hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t st) {
     if (a.plan && a.max_light > 0) {
-        constexpr int kCols = 4 * MOE_LIGHT_GU_TILES * 8;
+        const int kCols = 4 * (a.w_mxfp8 ? MOE_LIGHT_MX_GU_TILES : MOE_LIGHT_GU_TILES) * 8;
         const long long work = (long long)a.max_light * ((a.I + kCols - 1) / kCols);
         prof_begin(K_GATEUP_LIGHT, st);
         const int grid = grid_for(work, MOE_LIGHT_GU_BPC, a.num_cu);
         if (a.w_mxfp8)
-            gateup_light_mx_kernel<MOE_LIGHT_MX_GU_U, MOE_LIGHT_GU_TILES><<<grid, kThreads, 0, st>>>(a);
+            gateup_light_mx_kernel<MOE_LIGHT_MX_GU_U, MOE_LIGHT_MX_GU_TILES>
+                <<<grid, kThreads, 0, st>>>(a);
         else if (a.pk_gu)
             gateup_light_kernel<MOE_LIGHT_GU_U, MOE_LIGHT_GU_TILES, MOE_LIGHT_NT_LOADS != 0, true>
                 <<<grid, kThreads, 0, st>>>(a);
@@ -1428,12 +1435,13 @@ hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t st) {
 
 hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st) {
     if (a.plan && a.max_light > 0) {
-        constexpr int kCols = 4 * MOE_LIGHT_DN_TILES * 16;
+        const int kCols = 4 * (a.w_mxfp8 ? MOE_LIGHT_MX_DN_TILES : MOE_LIGHT_DN_TILES) * 16;
         const long long work = (long long)a.max_light * ((a.H + kCols - 1) / kCols);
         prof_begin(K_DOWN_LIGHT, st);
         const int grid = grid_for(work, MOE_LIGHT_DN_BPC, a.num_cu);
         if (a.w_mxfp8)
-            down_light_mx_kernel<MOE_LIGHT_DN_TILES, MOE_LIGHT_MX_DN_U><<<grid, kThreads, 0, st>>>(a);
+            down_light_mx_kernel<MOE_LIGHT_MX_DN_TILES, MOE_LIGHT_MX_DN_U>
+                <<<grid, kThreads, 0, st>>>(a);
         else if (a.pk_dn)
             down_light_kernel<MOE_LIGHT_DN_TILES, MOE_LIGHT_DN_U, MOE_LIGHT_NT_LOADS != 0, true>
                 <<<grid, kThreads, 0, st>>>(a);
