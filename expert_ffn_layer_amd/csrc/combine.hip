@@ -13,7 +13,6 @@ constexpr int kMaxK = 32;
 #define MOE_COMBINE_SMALL_T 512
 #endif
 
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // C consecutive y values (C = 4: fp32 or bf16; C = 8: bf16) as one raw
 // vector load, read non-temporally (each y row is read once); elem() widens

@@ -473,6 +473,12 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t w0, uint32_t w1, uin
     return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// Position swizzle of MXFP8 heavy B rows in LDS (64-byte rows of four
+// 16-byte units): unit u of row r sits at u ^ mx_swz(r), so that the 16
+// rows of one fragment read fall on distinct banks in groups of 8 or 16
+// lanes.
+__device__ __forceinline__ int mx_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
 __device__ __forceinline__ uint32_t load_u16(const uint8_t* p) {
     return *reinterpret_cast<const uint16_t*>(p);
 }
@@ -870,7 +876,13 @@ __device__ __forceinline__ int tile_tmi(const FfnArgs& a, int tile) {
 // row tiles are TM rows high, and returns the first item of another height
 // (or one at or past wend).
 // YB (down only): y stored as bf16 instead of fp32 (a.y_bf16).
-template <Mode M, int TM, bool YB>
+// W8: B (the weights) from the MXFP8 heavy-tile records (a.hq_gu / a.hq_dn):
+// a stage is 256 rows x 64 codes plus their scales, staged by the same LDS
+// DMA; each fragment read takes both 32-wide halves of a row's chunk (16
+// bytes) and its two scales, and the hardware's scaled conversion turns
+// them into the bf16 operands of the bf16 path -- the same MFMA chains on the
+// dequantised weights, so the results equal the bf16 path's bit for bit.
+template <Mode M, int TM, bool YB, bool W8>
 __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, long long wi,
                                                  long long wend, int nb_x, int nblk) {
     using G = HeavyGeom<M, TM>;
@@ -879,11 +891,15 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
     constexpr int kTmi = TM == kTileTM0 ? 0 : (TM == kTileTM1 ? 1 : 2);
     // One LDS object for both rings (A stages, then B stages): with two
     // objects the compiler waits for every LDS DMA before any LDS read.
-    constexpr int kBBytes = kBlocksB * kBlk;
+    constexpr int kBBytes = W8 ? kMxStageBytes : kBlocksB * kBlk;
+    // B load instructions per wave and stage: 4 x 1 KB of bf16, or 2 x 1 KB of
+    // codes plus 64 bytes of scales.
+    constexpr int kBInst = W8 ? 3 : kBBlkPerWave;
+    constexpr int kB8Blk = 2;  // code blocks (16 rows x 64 codes) per wave
     constexpr int bst = G::kBStages, ast = G::kAStages;
     static_assert(ast == 2 || bst == 2, "one ring at most is three deep");
     // Instructions per wave of the deeper ring's stage (0: both two deep).
-    constexpr int kDeepBlk = ast > 2 ? kABlk : (bst > 2 ? kBBlkPerWave : 0);
+    constexpr int kDeepBlk = ast > 2 ? kABlk : (bst > 2 ? kBInst : 0);
     static_assert(ast * kABytes + bst * kBBytes <= kHeavyLds, "LDS rings");
     // Stage st's A lives in slot st % ast, its B in slot st % bst; both slot
     // indices are carried along (no division in the loop).
@@ -936,7 +952,7 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
     };
     int nb = 0, e = 0, r0 = 0, m0 = 0, rows = 0;
     __amdgpu_buffer_rsrc_t ar, br;
-    uint32_t aoff[kABlk], boff[kBBlkPerWave];
+    uint32_t aoff[kABlk], boff[W8 ? kB8Blk + 1 : kBBlkPerWave];
     // Load sources of tile t: buffer resources and per-lane offsets.
     auto use_tile = [&](const Tile& t) {
         nb = t.nb;
@@ -952,7 +968,12 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
             ar = make_rsrc(a.x, (uint32_t)((size_t)a.T * a.H * 2));
         else
             ar = make_rsrc(a.h + (size_t)(r0 + m0) * hstride, (uint32_t)((size_t)TM * hstride * 2));
-        if (M == Mode::GateUp) {
+        if constexpr (W8) {
+            // the tile's records: one per K chunk, kMxStageBytes each
+            const uint8_t* base = M == Mode::GateUp ? a.hq_gu : a.hq_dn;
+            const size_t rec = (size_t)nst * kMxStageBytes;
+            br = make_rsrc(base + ((size_t)e * nblk + nb) * rec, (uint32_t)rec);
+        } else if (M == Mode::GateUp) {
             br = make_rsrc(a.w_gu + (size_t)e * 2 * a.I * a.H, (uint32_t)((size_t)2 * a.I * a.H * 2));
         } else {
             br = make_rsrc(a.w_dn + (size_t)e * a.H * a.I, (uint32_t)((size_t)a.H * a.I * 2));
@@ -969,6 +990,20 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
             } else {
                 aoff[i] = (uint32_t)rr * (uint32_t)hstride * 2u + cb;
             }
+        }
+        if constexpr (W8) {
+            // Code block b = 2*wave + i holds tile rows 16b..16b+15; lane L
+            // fills LDS slot L: row L/4, 16-byte unit L%4, which takes unit
+            // (L%4) ^ mx_swz(row) of the record's row (the swizzle spreads the
+            // fragment reads of 16 rows over all banks).
+#pragma unroll
+            for (int i = 0; i < kB8Blk; ++i) {
+                const int r = (kB8Blk * wave + i) * 16 + (lane >> 2);
+                boff[i] = (uint32_t)r * 64u + 16u * (uint32_t)((lane & 3) ^ mx_swz(r));
+            }
+            // scales: this wave's 64 bytes, lanes 0..3
+            boff[kB8Blk] = (uint32_t)kMxCodeBytes + 64u * (uint32_t)wave + 16u * (uint32_t)(lane & 3);
+            return;
         }
 #pragma unroll
         for (int i = 0; i < kBBlkPerWave; ++i) {
@@ -1016,6 +1051,14 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
     };
     auto issue_b = [&](int st, int slot) {
         char* buf = b_slot(slot);
+        if constexpr (W8) {
+            const uint32_t sb = (uint32_t)st * (uint32_t)kMxStageBytes;
+#pragma unroll
+            for (int i = 0; i < kB8Blk; ++i)
+                lds_dma16(br, boff[i] + sb, 0u, buf + (kB8Blk * wave + i) * kBlk);
+            if (lane < 4) lds_dma16(br, boff[kB8Blk] + sb, 0u, buf + kMxCodeBytes + 64 * wave);
+            return;
+        }
         const int kk = st * kKS;
         // down with split_h: K columns past I wrap back onto W_down
         const int kb = (M == Mode::Down && kk >= a.I) ? kk - a.I : kk;
@@ -1050,6 +1093,26 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
         for (int j = 0; j < 4; ++j)
             bf[j] = *reinterpret_cast<const bf16x8_t*>(base + (wn * 4 + j) * 2 * kBlk);
     };
+    // W8: raw codes of both halves of B fragment j (row (wn*4 + j)*16 + l16,
+    // unit g: K 8g.. then 32+8g..) and the lane's 8 scale bytes (2j: first
+    // half of fragment j, 2j+1: second half).
+    const int b8off = l16 * 64 + 16 * (g ^ mx_swz(l16));
+    auto read_b8 = [&](int slot, u32x4_t (&raw)[4], u32x2_t& sc) {
+        const char* base = b_slot(slot);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            raw[j] = *reinterpret_cast<const u32x4_t*>(base + (wn * 4 + j) * 16 * 64 + b8off);
+        sc = *reinterpret_cast<const u32x2_t*>(base + kMxCodeBytes + (wn * 16 + l16) * 8);
+    };
+    auto cvt_b8 = [&](const u32x4_t (&raw)[4], const u32x2_t& sc, bf16x8_t (&b0)[4],
+                      bf16x8_t (&b1)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t sw = sc[j >> 1] >> (16 * (j & 1));
+            b0[j] = e4m3x8_to_bf16(raw[j][0], raw[j][1], sw & 0xffu);
+            b1[j] = e4m3x8_to_bf16(raw[j][2], raw[j][3], (sw >> 8) & 0xffu);
+        }
+    };
     // A fragments in two groups: rows [0, kRF/2) and [kRF/2, kRF).
     constexpr int kG0 = kRF / 2;
     auto read_a = [&](int slot, int half, int grp, bf16x8_t (&af)[kRF]) {
@@ -1076,6 +1139,8 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
     int bs = 0, as = 0;     // B and A slots of the current stage
     bool primed = false;    // stage 0 already in, its first fragments in af / bf0
     bf16x8_t af[kRF], bf0[4], bf1[4];
+    u32x4_t raw[4];  // W8: next stage's B codes, converted behind the MFMAs
+    u32x2_t sc;
     while (true) {
         floatx4_t acc[kRF][4];
 #pragma unroll
@@ -1104,13 +1169,18 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
             // loads after it (A1 B1, and stage 2 of a three-deep ring) are
             // pending.
             if (nst > 2 && kDeepBlk > 0)
-                wait_vmcnt<kABlk + kBBlkPerWave + kDeepBlk>();
+                wait_vmcnt<kABlk + kBInst + kDeepBlk>();
             else if (nst > 1)
-                wait_vmcnt<kABlk + kBBlkPerWave>();
+                wait_vmcnt<kABlk + kBInst>();
             else
                 wait_vmcnt<0>();
             ring_barrier();
-            read_b(0, 0, bf0);
+            if constexpr (W8) {
+                read_b8(0, raw, sc);
+                cvt_b8(raw, sc, bf0, bf1);
+            } else {
+                read_b(0, 0, bf0);
+            }
             read_a(0, 0, 0, af);
             read_a(0, 0, 1, af);
         }
@@ -1128,7 +1198,7 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
             const int bn = (bs + 1 == bst) ? 0 : bs + 1;  // B slot of stage st+1
             const int an = (as + 1 == ast) ? 0 : as + 1;  // A slot of stage st+1
             mfma_rows(0, af, bf0);
-            read_b(bs, 1, bf1);
+            if constexpr (!W8) read_b(bs, 1, bf1);  // W8: both halves came with stage st
             read_a(as, 1, 0, af);
             mfma_rows(1, af, bf0);
             read_a(as, 1, 1, af);
@@ -1164,10 +1234,14 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
                 if (st + ast < nst) issue_a(st + ast, as);
                 else if (pf) issue_a(st + ast - nst, as);
             }
-            read_b(bn, 0, bf0);
+            if constexpr (W8)
+                read_b8(bn, raw, sc);
+            else
+                read_b(bn, 0, bf0);
             read_a(an, 0, 0, af);
             mfma_rows(1, af, bf1);
             read_a(an, 0, 1, af);
+            if constexpr (W8) cvt_b8(raw, sc, bf0, bf1);
             bs = bn;
             as = an;
         }
@@ -1272,7 +1346,7 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
 // One launch per GEMM: every row tile runs with the body of its own height
 // (the plan mixes heights within an expert); the bodies share one LDS
 // allocation, the largest ring.
-template <Mode M, bool YB>
+template <Mode M, bool YB, bool W8>
 __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
     __shared__ __attribute__((aligned(1024))) char lds[kHeavyLds];
     const int N = (M == Mode::GateUp) ? 2 * a.I : a.H;
@@ -1303,12 +1377,18 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
     long long wi = wbeg + jx;
     while (wi < wend) {
         const int tmi = tile_tmi(a, (int)(wi / nblk));
-        if (tmi == 0)
-            wi = ffn_heavy_run<M, kTileTM0, YB>(a, lds, wi, wend, nb_x, nblk);
+        if (tmi == 0) {
+            // MXFP8 plans never hold 256-row tiles (the body would spill);
+            // the host rejects a forced 256 with MXFP8 weights.
+            if constexpr (W8)
+                wi = wend;
+            else
+                wi = ffn_heavy_run<M, kTileTM0, YB, W8>(a, lds, wi, wend, nb_x, nblk);
+        }
         else if (tmi == 1)
-            wi = ffn_heavy_run<M, kTileTM1, YB>(a, lds, wi, wend, nb_x, nblk);
+            wi = ffn_heavy_run<M, kTileTM1, YB, W8>(a, lds, wi, wend, nb_x, nblk);
         else
-            wi = ffn_heavy_run<M, kTileTM2, YB>(a, lds, wi, wend, nb_x, nblk);
+            wi = ffn_heavy_run<M, kTileTM2, YB, W8>(a, lds, wi, wend, nb_x, nblk);
     }
 }
 
@@ -1361,7 +1441,10 @@ hipError_t launch_heavy(const FfnArgs& a, int ncols, hipStream_t st) {
     if (a.plan) {
         if (a.max_tiles <= 0) return hipSuccess;
         const int grid = grid_for((long long)a.max_tiles * nblk, 1, a.num_cu);
-        ffn_heavy_kernel<M, YB><<<grid, kHeavyThreads, 0, st>>>(a);
+        if (a.w_mxfp8)
+            ffn_heavy_kernel<M, YB, true><<<grid, kHeavyThreads, 0, st>>>(a);
+        else
+            ffn_heavy_kernel<M, YB, false><<<grid, kHeavyThreads, 0, st>>>(a);
         return hipGetLastError();
     }
     if (a.dense_rows <= 0) return hipSuccess;
@@ -1369,7 +1452,7 @@ hipError_t launch_heavy(const FfnArgs& a, int ncols, hipStream_t st) {
     const int grid = grid_for(tiles * nblk, 1, a.num_cu);
     if (a.dense_tm != kTileTM0 && a.dense_tm != kTileTM1 && a.dense_tm != kTileTM2)
         return hipErrorInvalidValue;
-    ffn_heavy_kernel<M, YB><<<grid, kHeavyThreads, 0, st>>>(a);
+    ffn_heavy_kernel<M, YB, false><<<grid, kHeavyThreads, 0, st>>>(a);  // dense groups: bf16
     return hipGetLastError();
 }
 

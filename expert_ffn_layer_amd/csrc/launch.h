@@ -145,16 +145,20 @@ inline __host__ __device__ void xcd_bounds(int32_t* plan, int t0, int nt, int ma
 }
 // Tiles of an expert with n heavy rows: ntiles tiles, all main_tmi high but
 // the last, last_tmi high (first rows 0, tm, 2 tm, ... with tm of main_tmi).
-// force_tm (128, 192, 256) puts every tile at that height.
+// force_tm (128, 192, 256) puts every tile at that height; a negative
+// force_tm = -m chooses as with 0 among the heights up to m (kTileMaxMx for
+// MXFP8 weights, whose 256-row tile body does not fit the register file).
+constexpr int kTileMaxMx = -192;
 inline __host__ __device__ void tile_split(int n, int force_tm, int& ntiles, int& main_tmi,
                                            int& last_tmi) {
-    if (force_tm) {
+    if (force_tm > 0) {
         main_tmi = last_tmi = tile_tm_index(force_tm);
         ntiles = (n + force_tm - 1) / force_tm;
         return;
     }
+    const int i0 = force_tm < 0 ? tile_tm_index(-force_tm) : 0;
     long long best = -1;
-    for (int i = 0; i < 3; ++i) {
+    for (int i = i0; i < 3; ++i) {
         const int tm = tile_height(i);
         const int k = (n + tm - 1) / tm;
         const long long c = (long long)k * tm * tile_cost(i);
@@ -165,7 +169,7 @@ inline __host__ __device__ void tile_split(int n, int force_tm, int& ntiles, int
         }
     }
     const int q = n / kTileTM0, rem = n - q * kTileTM0;
-    if (q > 0 && rem > 0) {
+    if (i0 == 0 && q > 0 && rem > 0) {
         const int r = rem <= kTileTM2 ? 2 : (rem <= kTileTM1 ? 1 : 0);
         const long long c =
             (long long)q * kTileTM0 * kTileCost0 + (long long)tile_height(r) * tile_cost(r);
@@ -204,13 +208,15 @@ struct FfnArgs {
     int max_light;               // grid bound for light experts
     int num_cu;
     int y_bf16;                  // 1: y stored as bf16 (round to nearest even)
-    // MXFP8 routed weights (w_mxfp8 = 1): the light loop reads these instead
-    // of pk_gu / pk_dn and every expert takes it (no heavy tiles).
+    // MXFP8 routed weights (w_mxfp8 = 1): the light loop and the heavy tiles
+    // read these instead of pk_gu / pk_dn and w_gu / w_dn.
     int w_mxfp8;
     const uint8_t* q_gu;         // packed E4M3 codes of W_gate|up
     const uint8_t* q_dn;         // packed E4M3 codes of W_down
     const uint8_t* qs_gu;        // per-chunk E8M0 scales of W_gate|up
     const uint8_t* qs_dn;        // per-chunk E8M0 scales of W_down
+    const uint8_t* hq_gu;        // heavy-tile records of W_gate|up (codes + scales)
+    const uint8_t* hq_dn;        // heavy-tile records of W_down
 };
 
 // Packed expert weights: 1 KB chunks, each the 16 weight rows x 32 K of one
@@ -241,8 +247,16 @@ hipError_t launch_pack_weights(const uint16_t* w_gu, const uint16_t* w_dn, int E
 // (down pads K past I with code 0).  Scales: 32 bytes per chunk, byte
 // 2*row + s the scale of the chunk's K step s for that row (127 = 2^0 for
 // padded steps), in the same (e, g, c) order.  Sections: gate|up codes, down
-// codes, gate|up scales, down scales.
+// codes, gate|up scales, down scales, then the heavy tiles' copies of gate|up
+// and down.
 inline __host__ __device__ int mx_chunks(int K) { return (K + 63) / 64; }
+// Heavy tiles read a second copy (sections 5 and 6 of the packed buffer): one
+// record per (expert, 256-row B tile, 64-wide K chunk) = the 256 rows' codes
+// (64 bytes each) then their 512 scale bytes; see pack_mxfp8_heavy_kernel.
+constexpr int kMxCodeBytes = 256 * 64;
+constexpr int kMxStageBytes = kMxCodeBytes + 512;
+size_t mx_heavy_gu_bytes(int E, int H, int I);
+size_t mx_heavy_dn_bytes(int E, int H, int I);
 size_t mx_codes_gu_bytes(int E, int H, int I);
 size_t mx_codes_dn_bytes(int E, int H, int I);
 size_t mx_scales_gu_bytes(int E, int H, int I);
@@ -254,8 +268,6 @@ hipError_t launch_mxfp8_quantize(const uint16_t* w, long long rows, int K, uint8
 hipError_t launch_pack_mxfp8(const uint8_t* c_gu, const uint8_t* s_gu, const uint8_t* c_dn,
                              const uint8_t* s_dn, int E, int H, int I, char* packed,
                              hipStream_t st);
-// light_max for layers whose every expert takes the light loop (MXFP8).
-constexpr int kLightAll = 1 << 30;
 
 hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st);

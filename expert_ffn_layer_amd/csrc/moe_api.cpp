@@ -77,6 +77,8 @@ int check_shape(const moe_shape* s) {
     if (s->y_bf16 != 0 && s->y_bf16 != 1) return fail(MOE_ERR_UNSUPPORTED, "y_bf16 must be 0 or 1");
     if (s->w_mxfp8 != 0 && s->w_mxfp8 != 1)
         return fail(MOE_ERR_UNSUPPORTED, "w_mxfp8 must be 0 or 1");
+    if (s->w_mxfp8 && s->heavy_tile_rows == moe::kTileTM0)
+        return fail(MOE_ERR_UNSUPPORTED, "MXFP8 heavy tiles are at most 192 rows");
     return MOE_OK;
 }
 
@@ -90,13 +92,7 @@ Layout layout(const moe_shape* s) {
     // The default is the per-call choice on the device (kLightAdaptive) from
     // 65 tokens on, with grids sized for either outcome; up to 64 tokens
     // every expert is light and no heavy kernel is launched.
-    if (s->w_mxfp8) {
-        // MXFP8 weights: every expert takes the light loop (in passes of 64
-        // rows), no heavy tile.
-        L.light_max = moe::kLightAll;
-        L.max_tiles = 0;
-        L.max_light = (int)std::min<long long>(E, A);
-    } else if (s->light_max_rows < 0 && T <= moe::kLightRowsMax) {
+    if (s->light_max_rows < 0 && T <= moe::kLightRowsMax) {
         L.light_max = moe::kLightRowsMax;
         L.max_tiles = 0;
         L.max_light = (int)std::min<long long>(E, A);
@@ -139,6 +135,12 @@ Layout layout(const moe_shape* s) {
 }
 
 bool aligned(const void* p, size_t a = 16) { return ((uintptr_t)p % a) == 0; }
+
+// Tile height rule handed to the plan kernels (see tile_split).
+int plan_force_tm(const moe_shape* s) {
+    if (s->w_mxfp8 && s->heavy_tile_rows == 0) return moe::kTileMaxMx;
+    return s->heavy_tile_rows;
+}
 
 int check_ws(const moe_shape* s, const void* ws, size_t ws_bytes) {
     if (!ws) return fail(MOE_ERR_NULL, "workspace is NULL");
@@ -208,7 +210,7 @@ int run_permute(const moe_shape* s, const Layout& L, const int32_t* ids, int32_t
     int32_t* plan = (plan_ready && small) ? at<int32_t>(ws, L.plan) : nullptr;
     HIP_TRY(moe::launch_permute(ids, s->T, s->k, s->E, at<int32_t>(ws, L.chunk), L.nchunks,
                                 counts, offsets, sorted, inv, plan, L.light_max,
-                                s->heavy_tile_rows, st),
+                                plan_force_tm(s), st),
             "permute");
     if (plan_ready) *plan_ready = plan != nullptr;
     return MOE_OK;
@@ -222,7 +224,7 @@ int run_ffn(const moe_shape* s, const Layout& L, const uint16_t* x, const int32_
     if (int rc = device_cu_count(&ncu)) return rc;
     int32_t* plan = at<int32_t>(ws, L.plan);
     if (!plan_ready)
-        HIP_TRY(moe::launch_ffn_plan(offsets, s->E, L.light_max, s->heavy_tile_rows, plan, st),
+        HIP_TRY(moe::launch_ffn_plan(offsets, s->E, L.light_max, plan_force_tm(s), plan, st),
                 "ffn plan");
     moe::FfnArgs a{};
     a.x = x;
@@ -251,6 +253,8 @@ int run_ffn(const moe_shape* s, const Layout& L, const uint16_t* x, const int32_
         a.q_dn = a.q_gu + moe::mx_codes_gu_bytes(s->E, s->H, s->I);
         a.qs_gu = a.q_dn + moe::mx_codes_dn_bytes(s->E, s->H, s->I);
         a.qs_dn = a.qs_gu + moe::mx_scales_gu_bytes(s->E, s->H, s->I);
+        a.hq_gu = a.qs_dn + moe::mx_scales_dn_bytes(s->E, s->H, s->I);
+        a.hq_dn = a.hq_gu + moe::mx_heavy_gu_bytes(s->E, s->H, s->I);
     } else if (packed) {
         const char* p = static_cast<const char*>(packed);
         a.pk_gu = reinterpret_cast<const uint16_t*>(p);
@@ -306,7 +310,8 @@ size_t moe_packed_weight_bytes(const moe_shape* shape) {
     const int E = shape->E, H = shape->H, I = shape->I;
     if (shape->w_mxfp8)
         return moe::mx_codes_gu_bytes(E, H, I) + moe::mx_codes_dn_bytes(E, H, I) +
-               moe::mx_scales_gu_bytes(E, H, I) + moe::mx_scales_dn_bytes(E, H, I);
+               moe::mx_scales_gu_bytes(E, H, I) + moe::mx_scales_dn_bytes(E, H, I) +
+               moe::mx_heavy_gu_bytes(E, H, I) + moe::mx_heavy_dn_bytes(E, H, I);
     return moe::packed_gu_bytes(E, H, I) + moe::packed_dn_bytes(E, H, I);
 }
 

@@ -162,6 +162,66 @@ __global__ __launch_bounds__(256) void pack_mxfp8_kernel(const uint8_t* __restri
     }
 }
 
+// Heavy-tile layout: one record of kMxStageBytes per (expert, 256-row B tile
+// nb, 64-wide K chunk c) -- the tile rows' codes (64 bytes each, the 16-byte
+// unit q holding K 8q..8q+7 then 32+8q..32+8q+7 of the chunk), then their
+// scales (two bytes per row: the chunk's two K steps) in the order the MFMA
+// fragment reads take them: row rr at byte 2 * (4 * (16 * (rr / 64) + rr % 16)
+// + (rr / 16) % 4).  Tile rows follow the heavy kernel's B tile: gate|up rows
+// alternate in 16-row blocks of gate and up rows of the same h columns
+// (column nb*128 + 16*(rr/32) + rr%16); down rows are W_down rows nb*256 + rr.
+// Rows past the weights and K past the end hold code 0 (scale 127).
+// One thread per 16-byte code unit; units 0..3 of a row also write its scales.
+template <bool kGateUp>
+__global__ __launch_bounds__(256) void pack_mxfp8_heavy_kernel(const uint8_t* __restrict__ codes,
+                                                               const uint8_t* __restrict__ scales,
+                                                               int E, int rows_per, int K, int I,
+                                                               int nblk, int nchunks,
+                                                               uint8_t* __restrict__ out) {
+    const long long nunits = (long long)E * nblk * nchunks * 256 * 4;
+    const int nks = K / 32;
+    for (long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x; u < nunits;
+         u += (long long)gridDim.x * blockDim.x) {
+        const int q = (int)(u & 3);
+        const int rr = (int)((u >> 2) & 255);
+        const long long rec = u >> 10;
+        const int c = (int)(rec % nchunks);
+        const long long enb = rec / nchunks;
+        const int nb = (int)(enb % nblk), e = (int)(enb / nblk);
+        int row;
+        bool valid;
+        if (kGateUp) {
+            const int hc = nb * 128 + (rr >> 5) * 16 + (rr & 15);
+            valid = hc < I;
+            row = ((rr & 16) == 0) ? hc : I + hc;
+        } else {
+            row = nb * 256 + rr;
+            valid = row < rows_per;
+        }
+        uint32_t word[4] = {0u, 0u, 0u, 0u};
+        if (valid) {
+            const uint8_t* src = codes + ((long long)e * rows_per + row) * K;
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int kk = 64 * c + 32 * half + 8 * q + i;
+                    if (kk < K) word[2 * half + i / 4] |= (uint32_t)src[kk] << (8 * (i % 4));
+                }
+        }
+        uint8_t* dst = out + rec * kMxStageBytes;
+        *reinterpret_cast<u32x4_t*>(dst + rr * 64 + 16 * q) =
+            u32x4_t{word[0], word[1], word[2], word[3]};
+        if (q < 2) {
+            const int ks = 2 * c + q;
+            uint8_t sv = 127;
+            if (valid && ks < nks) sv = scales[((long long)e * rows_per + row) * nks + ks];
+            const int slot = 4 * (16 * (rr >> 6) + (rr & 15)) + ((rr >> 4) & 3);
+            dst[kMxCodeBytes + 2 * slot + q] = sv;
+        }
+    }
+}
+
 int grid_of(long long items) {
     return (int)std::min<long long>((items + 255) / 256, 65536);
 }
@@ -179,6 +239,12 @@ size_t mx_scales_gu_bytes(int E, int H, int I) {
 }
 size_t mx_scales_dn_bytes(int E, int H, int I) {
     return (size_t)E * packed_dn_groups(H) * mx_chunks(I) * 32;
+}
+size_t mx_heavy_gu_bytes(int E, int H, int I) {
+    return (size_t)E * ((2 * I + 255) / 256) * mx_chunks(H) * kMxStageBytes;
+}
+size_t mx_heavy_dn_bytes(int E, int H, int I) {
+    return (size_t)E * ((H + 255) / 256) * mx_chunks(I) * kMxStageBytes;
 }
 
 hipError_t launch_mxfp8_quantize(const uint16_t* w, long long rows, int K, uint8_t* codes,
@@ -205,6 +271,17 @@ hipError_t launch_pack_mxfp8(const uint8_t* c_gu, const uint8_t* s_gu, const uin
     if (err != hipSuccess) return err;
     pack_mxfp8_kernel<false><<<grid_of((long long)E * gd * cd * 64), 256, 0, st>>>(
         c_dn, s_dn, E, H, I, I, gd, cd, q_dn, qs_dn);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    uint8_t* hq_gu = qs_dn + mx_scales_dn_bytes(E, H, I);
+    uint8_t* hq_dn = hq_gu + mx_heavy_gu_bytes(E, H, I);
+    const int nbg = (2 * I + 255) / 256, nbd = (H + 255) / 256;
+    pack_mxfp8_heavy_kernel<true><<<grid_of((long long)E * nbg * cg * 1024), 256, 0, st>>>(
+        c_gu, s_gu, E, 2 * I, H, I, nbg, cg, hq_gu);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    pack_mxfp8_heavy_kernel<false><<<grid_of((long long)E * nbd * cd * 1024), 256, 0, st>>>(
+        c_dn, s_dn, E, H, I, I, nbd, cd, hq_dn);
     return hipGetLastError();
 }
 

@@ -48,8 +48,6 @@ def light_experts(counts, shape):
     import numpy as np
     counts = np.asarray(counts)
     lm = shape.light_max_rows
-    if shape.w_mxfp8:
-        return counts >= 1  # MXFP8 weights: every expert takes the light loop
     if lm < 0:
         if shape.T <= LIGHT_MAX_ROWS:
             lm = LIGHT_MAX_ROWS

@@ -101,11 +101,11 @@ typedef struct moe_shape {
                                expert's output is always fp32. */
     int32_t w_mxfp8;        /* routed expert weights: 0 = bf16 (w_gate_up / w_down, optionally
                                packed); 1 = MXFP8, given only as the packed buffer of
-                               moe_pack_weights_mxfp8 (see there).  With 1 every expert takes
-                               the light loop (in passes of 64 rows; light_max_rows and
-                               heavy_tile_rows are ignored) and the results are those of the
-                               bf16 path on the dequantised weights, bit for bit.  The shared
-                               expert stays bf16. */
+                               moe_pack_weights_mxfp8 (see there).  With 1 the light/heavy
+                               choice is as for bf16 but heavy tiles are at most 192 rows
+                               (heavy_tile_rows = 256 is MOE_ERR_UNSUPPORTED), and the results
+                               are those of the bf16 path on the dequantised weights, bit for
+                               bit.  The shared expert stays bf16. */
 } moe_shape;
 
 /* Bytes of workspace every call below needs for `shape` (host-only, pure;
@@ -114,8 +114,10 @@ size_t moe_workspace_bytes(const moe_shape* shape);
 
 /* Bytes of the packed expert-weight buffer for `shape` (host-only, pure;
  * 0 for an invalid shape).  bf16 (w_mxfp8 = 0): the size of W_gate|up plus
- * W_down, E * 3 * I * H * 2.  MXFP8 (w_mxfp8 = 1): one byte per weight (K of
- * W_down padded to a multiple of 64) plus one scale byte per 32 weights. */
+ * W_down, E * 3 * I * H * 2.  MXFP8 (w_mxfp8 = 1): two copies (light loop,
+ * heavy tiles) of one byte per weight (K padded to a multiple of 64, the
+ * heavy copy's weight rows to a multiple of 256) plus one scale byte per 32
+ * weights. */
 size_t moe_packed_weight_bytes(const moe_shape* shape);
 
 /* Static text for a status code. */
@@ -200,11 +202,13 @@ int moe_quantize_mxfp8(const uint16_t* w, int64_t rows, int32_t K, uint8_t* code
 /* Packs MXFP8 expert weights (codes and scales as moe_quantize_mxfp8 writes
  * them for W_gate|up [E,2I,H] and W_down [E,H,I]) for the light loop, into
  * `packed` (moe_packed_weight_bytes(shape) bytes, 256-byte aligned) with
- * shape->w_mxfp8 = 1.  Codes become 1 KB chunks of 16 weight rows x 64 K in
- * lane order (lane l: row l%16, the codes of K 8(l/16)..+7 of the chunk's
- * first 32-wide K step, then of its second), rows grouped as for
- * moe_pack_weights; each chunk's scales are 32 bytes (row r's two steps at
- * 2r, 2r+1).  The result is passed to moe_grouped_ffn / moe_forward as
+ * shape->w_mxfp8 = 1.  Two copies: for the light loop, codes in 1 KB chunks
+ * of 16 weight rows x 64 K in lane order (lane l: row l%16, the codes of K
+ * 8(l/16)..+7 of the chunk's first 32-wide K step, then of its second), rows
+ * grouped as for moe_pack_weights, each chunk's scales 32 bytes (row r's two
+ * steps at 2r, 2r+1); for the heavy tiles, one record per (expert, 256-row
+ * weight tile, 64-wide K chunk): the tile rows' 64 codes each, then their
+ * 512 scale bytes.  The result is passed to moe_grouped_ffn / moe_forward as
  * packed_weights. */
 int moe_pack_weights_mxfp8(const moe_shape* shape, const uint8_t* codes_gate_up,
                            const uint8_t* scales_gate_up, const uint8_t* codes_down,

@@ -54,6 +54,12 @@ int main() {
         std::printf(" %lld", c);
     }
     std::printf("\n");
+    // heights limited to 192 (MXFP8 weights): prefix "mx"
+    for (int n = 1; n <= 1500; ++n) {
+        int nt = 0, mt = 0, lt = 0;
+        moe::tile_split(n, moe::kTileMaxMx, nt, mt, lt);
+        std::printf("mx %d %d %d %d\n", n, nt, moe::tile_height(mt), moe::tile_height(lt));
+    }
     std::printf("light %d %d %d\n", moe::adaptive_light_max(4000, 500), moe::adaptive_light_max(4001, 500),
                 moe::kLightRowsMax);
     return 0;

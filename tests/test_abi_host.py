@@ -166,15 +166,19 @@ def test_pack_weights_argument_errors(L):
 
 
 def test_mxfp8_packed_bytes(L):
-    """MXFP8 packed weights: one byte per weight (W_down's K padded to 64)
-    plus a scale byte per 32 weights; bf16 packing stays 2 bytes per weight."""
+    """MXFP8 packed weights: two copies (light loop, heavy tiles) of one byte
+    per weight (K padded to 64; the heavy copy's rows to 256) plus a scale
+    byte per 32 weights; bf16 packing stays 2 bytes per weight."""
     for (H, I) in ((4096, 1024), (64, 96), (128, 32)):
         E = 8
         b16 = moe.packed_weight_bytes(shp(E=E, H=H, I=I, k=2))
         mx = moe.packed_weight_bytes(shp(E=E, H=H, I=I, k=2, w_mxfp8=1))
         assert b16 == E * 3 * I * H * 2
         Ip = (I + 63) // 64 * 64
-        assert mx == E * (2 * I * H + H * Ip) * (1 + 1 / 32)
+        light = E * (2 * I * H + H * Ip) * (1 + 1 / 32)
+        r256 = lambda n: (n + 255) // 256 * 256
+        heavy = E * (r256(2 * I) * H + r256(H) * Ip) * (1 + 1 / 32)
+        assert mx == light + heavy
 
 
 def test_mxfp8_argument_errors(L):
@@ -203,9 +207,8 @@ def test_mxfp8_argument_errors(L):
     assert "packed" in moe.last_error()
 
 
-def test_mxfp8_light_rule():
-    """With MXFP8 weights every touched expert takes the light loop."""
-    import numpy as np
-    counts = np.array([0, 1, 64, 65, 500, 3000])
-    assert list(moe.light_experts(counts, shp(T=8192, w_mxfp8=1))) == [False] + [True] * 5
-    assert not moe.light_experts(counts, shp(T=8192)).any()
+def test_mxfp8_tile_limit(L):
+    """MXFP8 heavy tiles stop at 192 rows: a forced 256 is rejected."""
+    assert moe.workspace_bytes(shp(w_mxfp8=1, heavy_tile_rows=256)) == 0
+    assert moe.workspace_bytes(shp(w_mxfp8=1, heavy_tile_rows=192)) > 0
+    assert moe.workspace_bytes(shp(w_mxfp8=1, heavy_tile_rows=0)) > 0

@@ -4,8 +4,9 @@
   outputs): random bf16 weights, every finite bf16 bit pattern class
   (subnormals, huge values, signed zeros), ties and saturating blocks.
 - The packed layout matches its definition (spot checks).
-- The layer on MXFP8 weights gives the bits of the bf16 layer run on the
-  dequantised weights (same MFMA chains on the same operands).
+- The layer on MXFP8 weights -- light loop and heavy tiles -- gives the
+  bits of the bf16 layer run on the dequantised weights (same MFMA chains on
+  the same operands).
 - Against the oracle run on its own quantisation of the same weights: the
   bar of the bf16 path (max_abs 2e-2, relL2 5e-3).
 """
@@ -118,8 +119,43 @@ def test_pack_layout():
     off_cdn = E * gg * ncg * 1024
     off_sgu = off_cdn + E * gd * ncd * 1024
     off_sdn = off_sgu + E * gg * ncg * 32
-    assert pk.size == off_sdn + E * gd * ncd * 32
+    off_hgu = off_sdn + E * gd * ncd * 32
+    nbg, nbd = -(-2 * I // 256), -(-H // 256)
+    REC = 256 * 64 + 512
+    off_hdn = off_hgu + E * nbg * ncg * REC
+    assert pk.size == off_hdn + E * nbd * ncd * REC
     rng = np.random.default_rng(4)
+    # heavy-tile records (e, nb, c): row rr's 16-byte unit q = K 64c + 8q..+7
+    # then 64c + 32 + 8q..+7; scales after the 16 KB of codes, row rr's two K
+    # steps at 2 * (4 * (16 * (rr // 64) + rr % 16) + (rr // 16) % 4)
+    for _ in range(400):
+        gate_up = bool(rng.integers(0, 2))
+        e = int(rng.integers(0, E))
+        nb = int(rng.integers(0, nbg if gate_up else nbd))
+        c = int(rng.integers(0, ncg if gate_up else ncd))
+        rr, q = int(rng.integers(0, 256)), int(rng.integers(0, 4))
+        if gate_up:
+            hc = nb * 128 + (rr // 32) * 16 + rr % 16
+            valid, row = hc < I, (hc if rr % 32 < 16 else I + hc)
+            src, ssrc, K, nc, base = cgu[e], sgu[e], H, ncg, off_hgu
+        else:
+            row = nb * 256 + rr
+            valid = row < H
+            src, ssrc, K, nc, base = cdn[e], sdn[e], I, ncd, off_hdn
+        want = np.zeros(16, np.uint8)
+        if valid:
+            for half in range(2):
+                for i in range(8):
+                    kk = 64 * c + 32 * half + 8 * q + i
+                    if kk < K:
+                        want[8 * half + i] = src[row, kk]
+        rec = base + ((e * (nbg if gate_up else nbd) + nb) * nc + c) * REC
+        assert np.array_equal(pk[rec + rr * 64 + 16 * q: rec + rr * 64 + 16 * q + 16], want)
+        slot = 4 * (16 * (rr // 64) + rr % 16) + (rr // 16) % 4
+        for st in range(2):
+            ks = 2 * c + st
+            w = ssrc[row, ks] if valid and ks < K // 32 else 127
+            assert pk[rec + 256 * 64 + 2 * slot + st] == w, (gate_up, e, nb, c, rr, st)
     for _ in range(400):
         gate_up = bool(rng.integers(0, 2))
         e = int(rng.integers(0, E))
@@ -179,6 +215,8 @@ MX_CASES = {
 @pytest.mark.parametrize("name", list(MX_CASES))
 @pytest.mark.parametrize("y_bf16", [False, True])
 def test_layer_bitwise_vs_dequantised_bf16(oracle_lib, name, y_bf16):
+    """Default light/heavy rule: light loop, heavy tiles (128/192 rows) or
+    both, depending on the shape."""
     print(f"[case] mxfp8 bitwise {name} y_bf16={y_bf16}", flush=True)
     lay = layer_on_gpu(MX_CASES[name])
     ref = dequant_layer(oracle_lib, lay)
@@ -188,6 +226,22 @@ def test_layer_bitwise_vs_dequantised_bf16(oracle_lib, name, y_bf16):
     assert torch.equal(out_mx[1], out_16[1])
     assert torch.equal(out_mx[0].view(torch.int32), out_16[0].view(torch.int32)), \
         "MXFP8 layer differs from the bf16 layer on dequantised weights"
+
+
+@pytest.mark.parametrize("name", ["heavy_ragged", "mixed", "i_tail", "hot", "shared"])
+@pytest.mark.parametrize("lm,tm", [(0, 0), (0, 128), (0, 192), (64, 0), (16, 128)])
+def test_layer_bitwise_paths(oracle_lib, name, lm, tm):
+    """Every MXFP8 path -- heavy tiles of each height, the light loop (in
+    64-row passes past 64 rows), and splits between the two -- against the
+    bf16 layer on the dequantised weights (y bf16)."""
+    print(f"[case] mxfp8 paths {name} light_max={lm} tm={tm}", flush=True)
+    lay = layer_on_gpu(MX_CASES[name])
+    ref = dequant_layer(oracle_lib, lay)
+    out_mx = moe.MoELayer(lay, light_max_rows=lm, heavy_tile_rows=tm, y_bf16=True,
+                          weights="mxfp8")()
+    out_16 = moe.MoELayer(ref, y_bf16=True)()
+    torch.cuda.synchronize()
+    assert torch.equal(out_mx[0].view(torch.int32), out_16[0].view(torch.int32))
 
 
 class _LazyMx:
@@ -226,7 +280,7 @@ def test_layer_vs_oracle_small(oracle_lib, name):
 
 
 @pytest.mark.parametrize("name,sample,y_bf16", [("decode", 16, True), ("prefill", 12, True),
-                                                ("decode", 8, False)])
+                                                ("skew", 12, True), ("decode", 8, False)])
 def test_layer_vs_oracle_full_size(oracle_lib, name, sample, y_bf16):
     """Full-size layers on MXFP8 weights against the oracle on a token
     sample (the oracle quantises only the experts those tokens reach)."""
@@ -240,12 +294,13 @@ def test_layer_vs_oracle_full_size(oracle_lib, name, sample, y_bf16):
     torch.cuda.empty_cache()
 
 
-def test_full_size_decode_bitwise_and_quantisation_error():
-    """Decode layer: MXFP8 output equals the bf16 layer on weights
+@pytest.mark.parametrize("name", ["decode", "prefill", "skew"])
+def test_full_size_bitwise_and_quantisation_error(name):
+    """Full-size layers: MXFP8 output equals the bf16 layer on weights
     dequantised by torch's float8_e4m3fn (a library decoding) bit for bit;
     the quantisation's own effect on the output is reported."""
-    print("[case] mxfp8 decode bitwise", flush=True)
-    lay = layer_on_gpu(synth.CONFIGS["decode"])
+    print(f"[case] mxfp8 {name} bitwise", flush=True)
+    lay = layer_on_gpu(synth.CONFIGS[name])
 
     def dq(w):
         c, s = moe.quantize_mxfp8(w)
@@ -261,5 +316,7 @@ def test_full_size_decode_bitwise_and_quantisation_error():
     torch.cuda.synchronize()
     assert torch.equal(out_mx.view(torch.int32), out_16.view(torch.int32))
     ma, rel = gh.err_stats(out_mx.cpu().numpy(), out_orig.cpu().numpy())
-    print(f"[quant] mxfp8 vs bf16 weights at decode: max_abs={ma:.3e} relL2={rel:.3e}", flush=True)
+    print(f"[quant] mxfp8 vs bf16 weights ({name}): max_abs={ma:.3e} relL2={rel:.3e}", flush=True)
     assert rel < 0.1  # E4M3 keeps 4 significant bits: a few percent of the output
+    del lay, ref
+    torch.cuda.empty_cache()

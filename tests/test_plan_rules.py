@@ -49,6 +49,18 @@ def test_tile_split(output):
         assert cost == (nt - 1) * UNITS[mt] + UNITS[lt]
 
 
+def test_tile_split_max_192(output):
+    """With heights limited to 192 (MXFP8 weights): one height per expert,
+    the cheaper of all-192 and all-128, no 256-row tile, no tile to spare."""
+    rows = [list(map(int, l.split()[1:])) for l in output if l.startswith("mx ")]
+    assert len(rows) == 1500
+    for n, nt, mt, lt in rows:
+        assert mt == lt and mt in (128, 192)
+        assert nt * mt >= n > (nt - 1) * mt
+        best = min(-(-n // tm) * tm * COST[tm] for tm in (192, 128))
+        assert nt * mt * COST[mt] == best, n
+
+
 def test_xcd_bounds(output):
     line = [l for l in output if l.startswith("xcd ")][0].split()
     C, T = int(line[1]), int(line[2])
