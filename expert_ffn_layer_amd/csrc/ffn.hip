@@ -876,16 +876,21 @@ __device__ __forceinline__ int tile_tmi(const FfnArgs& a, int tile) {
 // row tiles are TM rows high, and returns the first item of another height
 // (or one at or past wend).
 // YB (down only): y stored as bf16 instead of fp32 (a.y_bf16).
-// W8: B (the weights) from the MXFP8 heavy-tile records (a.hq_gu / a.hq_dn):
+// BS: where B (the weights) comes from -- kBRowMajor: w_gu / w_dn; kBRec16:
+// the bf16 heavy-tile records of the packed copy (a.hr_gu / a.hr_dn: one
+// 32 KB run per (expert, 256-row tile, K stage), so a stage is one
+// contiguous read instead of 256 row pieces 2H bytes apart); kBRecMx (W8):
+// the MXFP8 heavy-tile records (a.hq_gu / a.hq_dn):
 // a stage is 256 rows x 64 codes plus their scales, staged by the same LDS
 // DMA; each fragment read takes both 32-wide halves of a row's chunk (16
 // bytes) and its two scales, and the hardware's scaled conversion turns
 // them into the bf16 operands of the bf16 path -- the same MFMA chains on the
 // dequantised weights, so the results equal the bf16 path's bit for bit.
-template <Mode M, int TM, bool YB, bool W8>
+template <Mode M, int TM, bool YB, int BS>
 __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, long long wi,
                                                  long long wend, int nb_x, int nblk) {
     using G = HeavyGeom<M, TM>;
+    constexpr bool W8 = BS == kBRecMx;
     constexpr int kRF = G::kRF, kBlocksA = G::kBlocksA, kABlk = G::kABlkPerWave;
     constexpr int kABytes = G::kABytes;
     constexpr int kTmi = TM == kTileTM0 ? 0 : (TM == kTileTM1 ? 1 : 2);
@@ -973,6 +978,11 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
             const uint8_t* base = M == Mode::GateUp ? a.hq_gu : a.hq_dn;
             const size_t rec = (size_t)nst * kMxStageBytes;
             br = make_rsrc(base + ((size_t)e * nblk + nb) * rec, (uint32_t)rec);
+        } else if (BS == kBRec16) {
+            const uint16_t* base = M == Mode::GateUp ? a.hr_gu : a.hr_dn;
+            const size_t rec = (size_t)nst * kRec16Bytes;
+            br = make_rsrc(reinterpret_cast<const char*>(base) + ((size_t)e * nblk + nb) * rec,
+                           (uint32_t)rec);
         } else if (M == Mode::GateUp) {
             br = make_rsrc(a.w_gu + (size_t)e * 2 * a.I * a.H, (uint32_t)((size_t)2 * a.I * a.H * 2));
         } else {
@@ -1003,6 +1013,15 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
             }
             // scales: this wave's 64 bytes, lanes 0..3
             boff[kB8Blk] = (uint32_t)kMxCodeBytes + 64u * (uint32_t)wave + 16u * (uint32_t)(lane & 3);
+            return;
+        }
+        if constexpr (BS == kBRec16) {
+            // record rows are already the tile's B rows (128 bytes each)
+#pragma unroll
+            for (int i = 0; i < kBBlkPerWave; ++i) {
+                const int r = (kBBlkPerWave * wave + i) * 8 + drow;
+                boff[i] = (uint32_t)r * 128u + (uint32_t)dchunk * 16u;
+            }
             return;
         }
 #pragma unroll
@@ -1057,6 +1076,14 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
             for (int i = 0; i < kB8Blk; ++i)
                 lds_dma16(br, boff[i] + sb, 0u, buf + (kB8Blk * wave + i) * kBlk);
             if (lane < 4) lds_dma16(br, boff[kB8Blk] + sb, 0u, buf + kMxCodeBytes + 64 * wave);
+            return;
+        }
+        if constexpr (BS == kBRec16) {
+            // padded records: no tail adjustment
+            const uint32_t sb = (uint32_t)st * (uint32_t)kRec16Bytes;
+#pragma unroll
+            for (int i = 0; i < kBBlkPerWave; ++i)
+                lds_dma16(br, boff[i] + sb, 0u, buf + (kBBlkPerWave * wave + i) * kBlk);
             return;
         }
         const int kk = st * kKS;
@@ -1346,7 +1373,7 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
 // One launch per GEMM: every row tile runs with the body of its own height
 // (the plan mixes heights within an expert); the bodies share one LDS
 // allocation, the largest ring.
-template <Mode M, bool YB, bool W8>
+template <Mode M, bool YB, int BS>
 __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
     __shared__ __attribute__((aligned(1024))) char lds[kHeavyLds];
     const int N = (M == Mode::GateUp) ? 2 * a.I : a.H;
@@ -1380,15 +1407,15 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
         if (tmi == 0) {
             // MXFP8 plans never hold 256-row tiles (the body would spill);
             // the host rejects a forced 256 with MXFP8 weights.
-            if constexpr (W8)
+            if constexpr (BS == kBRecMx)
                 wi = wend;
             else
-                wi = ffn_heavy_run<M, kTileTM0, YB, W8>(a, lds, wi, wend, nb_x, nblk);
+                wi = ffn_heavy_run<M, kTileTM0, YB, BS>(a, lds, wi, wend, nb_x, nblk);
         }
         else if (tmi == 1)
-            wi = ffn_heavy_run<M, kTileTM1, YB, W8>(a, lds, wi, wend, nb_x, nblk);
+            wi = ffn_heavy_run<M, kTileTM1, YB, BS>(a, lds, wi, wend, nb_x, nblk);
         else
-            wi = ffn_heavy_run<M, kTileTM2, YB, W8>(a, lds, wi, wend, nb_x, nblk);
+            wi = ffn_heavy_run<M, kTileTM2, YB, BS>(a, lds, wi, wend, nb_x, nblk);
     }
 }
 
@@ -1435,6 +1462,47 @@ int grid_for(long long work, int per_cu, int num_cu) {
 // Heavy tiles of one GEMM.  With a plan the tile height is decided on the
 // device, so every height's kernel is launched and all but one return at
 // once; a dense group's height is known here.
+// bf16 heavy-tile records: one kRec16Bytes run per (expert, 256-row B tile
+// nb, 64-wide K stage c), row rr of the tile (the heavy kernel's B row order:
+// gate|up rows alternate in 16-row blocks of gate and up rows of h columns
+// nb*128 + 16*(rr/32) + rr%16; down rows are W_down rows nb*256 + rr) holding
+// its 64 K values; rows past the weights and K past the end are 0.  One
+// thread per 16 bytes.
+template <bool kGateUp>
+__global__ __launch_bounds__(256) void pack_heavy_rec_kernel(const uint16_t* __restrict__ w, int E,
+                                                             int rows_per, int K, int I, int nblk,
+                                                             int nchunks, uint16_t* __restrict__ out) {
+    const long long nunits = (long long)E * nblk * nchunks * 256 * 8;
+    for (long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x; u < nunits;
+         u += (long long)gridDim.x * blockDim.x) {
+        const int q = (int)(u & 7);
+        const int rr = (int)((u >> 3) & 255);
+        const long long rec = u >> 11;
+        const int c = (int)(rec % nchunks);
+        const long long enb = rec / nchunks;
+        const int nb = (int)(enb % nblk), e = (int)(enb / nblk);
+        int row;
+        bool valid;
+        if (kGateUp) {
+            const int hc = nb * 128 + (rr >> 5) * 16 + (rr & 15);
+            valid = hc < I;
+            row = ((rr & 16) == 0) ? hc : I + hc;
+        } else {
+            row = nb * 256 + rr;
+            valid = row < rows_per;
+        }
+        uint32_t word[4] = {0u, 0u, 0u, 0u};
+        const int k0 = 64 * c + 8 * q;
+        if (valid && k0 < K) {  // K % 32 == 0: a unit is all in or all out
+            const u32x4_t v =
+                *reinterpret_cast<const u32x4_t*>(w + ((long long)e * rows_per + row) * K + k0);
+            word[0] = v[0], word[1] = v[1], word[2] = v[2], word[3] = v[3];
+        }
+        *reinterpret_cast<u32x4_t*>(out + rec * (kRec16Bytes / 2) + rr * 64 + 8 * q) =
+            u32x4_t{word[0], word[1], word[2], word[3]};
+    }
+}
+
 template <Mode M, bool YB>
 hipError_t launch_heavy(const FfnArgs& a, int ncols, hipStream_t st) {
     const long long nblk = (ncols + kTN - 1) / kTN;
@@ -1442,9 +1510,11 @@ hipError_t launch_heavy(const FfnArgs& a, int ncols, hipStream_t st) {
         if (a.max_tiles <= 0) return hipSuccess;
         const int grid = grid_for((long long)a.max_tiles * nblk, 1, a.num_cu);
         if (a.w_mxfp8)
-            ffn_heavy_kernel<M, YB, true><<<grid, kHeavyThreads, 0, st>>>(a);
+            ffn_heavy_kernel<M, YB, kBRecMx><<<grid, kHeavyThreads, 0, st>>>(a);
+        else if (a.hr_gu)
+            ffn_heavy_kernel<M, YB, kBRec16><<<grid, kHeavyThreads, 0, st>>>(a);
         else
-            ffn_heavy_kernel<M, YB, false><<<grid, kHeavyThreads, 0, st>>>(a);
+            ffn_heavy_kernel<M, YB, kBRowMajor><<<grid, kHeavyThreads, 0, st>>>(a);
         return hipGetLastError();
     }
     if (a.dense_rows <= 0) return hipSuccess;
@@ -1452,7 +1522,7 @@ hipError_t launch_heavy(const FfnArgs& a, int ncols, hipStream_t st) {
     const int grid = grid_for(tiles * nblk, 1, a.num_cu);
     if (a.dense_tm != kTileTM0 && a.dense_tm != kTileTM1 && a.dense_tm != kTileTM2)
         return hipErrorInvalidValue;
-    ffn_heavy_kernel<M, YB, false><<<grid, kHeavyThreads, 0, st>>>(a);  // dense groups: bf16
+    ffn_heavy_kernel<M, YB, kBRowMajor><<<grid, kHeavyThreads, 0, st>>>(a);  // dense groups
     return hipGetLastError();
 }
 
@@ -1466,6 +1536,14 @@ size_t packed_dn_bytes(int E, int H, int I) {
     return (size_t)E * packed_dn_groups(H) * packed_dn_ksteps(I) * 1024;
 }
 
+size_t rec16_gu_bytes(int E, int H, int I) {
+    return (size_t)E * ((2 * I + 255) / 256) * mx_chunks(H) * kRec16Bytes;
+}
+
+size_t rec16_dn_bytes(int E, int H, int I) {
+    return (size_t)E * ((H + 255) / 256) * mx_chunks(I) * kRec16Bytes;
+}
+
 hipError_t launch_pack_weights(const uint16_t* w_gu, const uint16_t* w_dn, int E, int H, int I,
                                char* packed, hipStream_t st) {
     const int gg = packed_gu_groups(I), kg = H / 32;
@@ -1477,6 +1555,20 @@ hipError_t launch_pack_weights(const uint16_t* w_gu, const uint16_t* w_dn, int E
     if (err != hipSuccess) return err;
     pack_weights_kernel<<<(int)std::min<long long>((sd + 255) / 256, 65536), 256, 0, st>>>(
         w_dn, E, H, I, gd, kd, 0, I, reinterpret_cast<uint16_t*>(packed + packed_gu_bytes(E, H, I)));
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    // the heavy tiles' records
+    char* rec = packed + packed_gu_bytes(E, H, I) + packed_dn_bytes(E, H, I);
+    const int nbg = (2 * I + 255) / 256, nbd = (H + 255) / 256;
+    const long long ug = (long long)E * nbg * mx_chunks(H) * 2048;
+    const long long ud = (long long)E * nbd * mx_chunks(I) * 2048;
+    pack_heavy_rec_kernel<true><<<(int)std::min<long long>((ug + 255) / 256, 65536), 256, 0, st>>>(
+        w_gu, E, 2 * I, H, I, nbg, mx_chunks(H), reinterpret_cast<uint16_t*>(rec));
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    pack_heavy_rec_kernel<false><<<(int)std::min<long long>((ud + 255) / 256, 65536), 256, 0, st>>>(
+        w_dn, E, H, I, I, nbd, mx_chunks(I),
+        reinterpret_cast<uint16_t*>(rec + rec16_gu_bytes(E, H, I)));
     return hipGetLastError();
 }
 

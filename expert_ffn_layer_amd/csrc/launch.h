@@ -217,6 +217,8 @@ struct FfnArgs {
     const uint8_t* qs_dn;        // per-chunk E8M0 scales of W_down
     const uint8_t* hq_gu;        // heavy-tile records of W_gate|up (codes + scales)
     const uint8_t* hq_dn;        // heavy-tile records of W_down
+    const uint16_t* hr_gu;       // bf16 heavy-tile records of W_gate|up, or nullptr
+    const uint16_t* hr_dn;       // bf16 heavy-tile records of W_down
 };
 
 // Packed expert weights: 1 KB chunks, each the 16 weight rows x 32 K of one
@@ -235,6 +237,16 @@ inline __host__ __device__ int packed_dn_groups(int H) { return H / 16; }
 inline __host__ __device__ int packed_dn_ksteps(int I) { return I / 32; }
 size_t packed_gu_bytes(int E, int H, int I);
 size_t packed_dn_bytes(int E, int H, int I);
+// The packed copy also holds the heavy tiles' records (after the light
+// chunks): one kRec16Bytes run per (expert, 256-row B tile, 64-wide K stage),
+// the tile rows in the heavy kernel's order, 64 bf16 K values each.
+constexpr int kRec16Bytes = 256 * 64 * 2;
+size_t rec16_gu_bytes(int E, int H, int I);
+size_t rec16_dn_bytes(int E, int H, int I);
+// Where the heavy tiles read B from.
+constexpr int kBRowMajor = 0;  // w_gu / w_dn
+constexpr int kBRec16 = 1;     // bf16 records of the packed copy
+constexpr int kBRecMx = 2;     // MXFP8 records
 hipError_t launch_pack_weights(const uint16_t* w_gu, const uint16_t* w_dn, int E, int H, int I,
                                char* packed, hipStream_t st);
 

@@ -257,8 +257,12 @@ int run_ffn(const moe_shape* s, const Layout& L, const uint16_t* x, const int32_
         a.hq_dn = a.hq_gu + moe::mx_heavy_gu_bytes(s->E, s->H, s->I);
     } else if (packed) {
         const char* p = static_cast<const char*>(packed);
+        const size_t gu = moe::packed_gu_bytes(s->E, s->H, s->I);
+        const size_t dn = moe::packed_dn_bytes(s->E, s->H, s->I);
         a.pk_gu = reinterpret_cast<const uint16_t*>(p);
-        a.pk_dn = reinterpret_cast<const uint16_t*>(p + moe::packed_gu_bytes(s->E, s->H, s->I));
+        a.pk_dn = reinterpret_cast<const uint16_t*>(p + gu);
+        a.hr_gu = reinterpret_cast<const uint16_t*>(p + gu + dn);
+        a.hr_dn = reinterpret_cast<const uint16_t*>(p + gu + dn + moe::rec16_gu_bytes(s->E, s->H, s->I));
     }
     HIP_TRY(moe::launch_ffn_gateup(a, st), "ffn gate|up");
     HIP_TRY(moe::launch_ffn_down(a, st), "ffn down");
@@ -312,7 +316,8 @@ size_t moe_packed_weight_bytes(const moe_shape* shape) {
         return moe::mx_codes_gu_bytes(E, H, I) + moe::mx_codes_dn_bytes(E, H, I) +
                moe::mx_scales_gu_bytes(E, H, I) + moe::mx_scales_dn_bytes(E, H, I) +
                moe::mx_heavy_gu_bytes(E, H, I) + moe::mx_heavy_dn_bytes(E, H, I);
-    return moe::packed_gu_bytes(E, H, I) + moe::packed_dn_bytes(E, H, I);
+    return moe::packed_gu_bytes(E, H, I) + moe::packed_dn_bytes(E, H, I) +
+           moe::rec16_gu_bytes(E, H, I) + moe::rec16_dn_bytes(E, H, I);
 }
 
 int moe_quantize_mxfp8(const uint16_t* w, int64_t rows, int32_t K, uint8_t* codes,

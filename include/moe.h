@@ -169,8 +169,13 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t* counts
  * streams each group's weights as one contiguous run: on MI355X the gate|up
  * weights of a decode step stream at ~6.1 TB/s instead of ~5.7 TB/s from the
  * row-major layout, whose 16-row tiles read 64 bytes from rows 8 KB apart.
- * The heavy tiles keep reading w_gate_up / w_down (row-major is faster for
- * them), so the packed buffer is a second copy of the routed weights.
+ * A second part holds the weights again for the heavy tiles: one 32 KB
+ * record per (expert e, 256-row weight tile nb, 64-wide K stage c), ordered
+ * (e, nb, c), each the tile's 256 rows x 64 K values -- gate|up tile rows
+ * alternate in 16-row blocks between gate and up rows of h columns
+ * nb*128 + 16*(r/32) + r%16; down tile rows are W_down rows nb*256 + r --
+ * with zeros past the weights (rows padded to 256, K to 64); a heavy stage
+ * is then one contiguous read.  The packed buffer thus holds two copies.
  *   w_gate_up, w_down  bf16, layouts as for moe_grouped_ffn (read)
  *   packed             device buffer of moe_packed_weight_bytes(shape)
  *                      bytes, 256-byte aligned (written; caller-owned)
@@ -225,8 +230,8 @@ int moe_pack_weights_mxfp8(const moe_shape* shape, const uint8_t* codes_gate_up,
  *   w_gate_up        bf16 [E,2I,H]: rows 0..I-1 = W_gate^T, I..2I-1 = W_up^T
  *   w_down           bf16 [E,H,I]:  W_down^T
  *   packed_weights   the same weights from moe_pack_weights, or NULL; when
- *                    given, the light loop reads it instead of w_gate_up /
- *                    w_down (the heavy tiles always read those).  With
+ *                    given, the light loop and the heavy tiles read it
+ *                    instead of w_gate_up / w_down.  With
  *                    shape->w_mxfp8 = 1 it is required (from
  *                    moe_pack_weights_mxfp8) and w_gate_up / w_down are not
  *                    read (may be NULL)

@@ -145,11 +145,12 @@ def test_status_strings(L):
 
 
 def test_packed_weight_bytes(L):
-    """1 KB chunks of 16 rows x 32 K: exactly the weights' own size."""
+    """The light loop's 1 KB chunks (exactly the weights' own size) plus the
+    heavy tiles' records (weight rows padded to 256, K to 64)."""
     s = shp()
-    assert moe.packed_weight_bytes(s) == 512 * 3 * 1024 * 4096 * 2
+    assert moe.packed_weight_bytes(s) == 2 * 512 * 3 * 1024 * 4096 * 2
     s = shp(E=3, k=2, H=320, I=96)
-    assert moe.packed_weight_bytes(s) == 3 * 3 * 96 * 320 * 2
+    assert moe.packed_weight_bytes(s) == 3 * 3 * 96 * 320 * 2 + 3 * (256 * 320 + 512 * 128) * 2
     assert moe.packed_weight_bytes(shp(H=100)) == 0
 
 
@@ -166,17 +167,18 @@ def test_pack_weights_argument_errors(L):
 
 
 def test_mxfp8_packed_bytes(L):
-    """MXFP8 packed weights: two copies (light loop, heavy tiles) of one byte
-    per weight (K padded to 64; the heavy copy's rows to 256) plus a scale
-    byte per 32 weights; bf16 packing stays 2 bytes per weight."""
+    """Packed weights hold two copies (light loop, heavy tiles; the heavy
+    copy's rows padded to 256 and K to 64): bf16 at 2 bytes per weight, MXFP8
+    at one byte per weight plus a scale byte per 32."""
     for (H, I) in ((4096, 1024), (64, 96), (128, 32)):
         E = 8
         b16 = moe.packed_weight_bytes(shp(E=E, H=H, I=I, k=2))
         mx = moe.packed_weight_bytes(shp(E=E, H=H, I=I, k=2, w_mxfp8=1))
-        assert b16 == E * 3 * I * H * 2
-        Ip = (I + 63) // 64 * 64
-        light = E * (2 * I * H + H * Ip) * (1 + 1 / 32)
         r256 = lambda n: (n + 255) // 256 * 256
+        Ip = (I + 63) // 64 * 64
+        # light chunks (E*3*I*H*2) + heavy records (rows to 256, K to 64)
+        assert b16 == E * 3 * I * H * 2 + E * (r256(2 * I) * H + r256(H) * Ip) * 2
+        light = E * (2 * I * H + H * Ip) * (1 + 1 / 32)
         heavy = E * (r256(2 * I) * H + r256(H) * Ip) * (1 + 1 / 32)
         assert mx == light + heavy
 

@@ -475,7 +475,11 @@ def test_packed_weights_layout():
             ok, src = row < H and k < I, wdn[e]
         return src[row, k:k + 8] if ok else np.zeros(8, np.int16)
 
-    assert words.size == (E * gg * kg + E * gd * kd) * 512
+    light = (E * gg * kg + E * gd * kd) * 512
+    nbg, nbd = -(-2 * I // 256), -(-H // 256)
+    ncg, ncd = -(-H // 64), -(-I // 64)
+    rec_gu = E * nbg * ncg * 256 * 64
+    assert words.size == light + rec_gu + E * nbd * ncd * 256 * 64
     base_dn = E * gg * kg * 512
     for _ in range(600):
         gate_up = bool(rng.integers(2))
@@ -484,3 +488,22 @@ def test_packed_weights_layout():
         q = ((e * ng + grp) * nk + kb) * 64 + L
         off = (0 if gate_up else base_dn) + q * 8
         assert np.array_equal(words[off:off + 8], expect(gate_up, e, grp, kb, L)), (gate_up, e, grp, kb, L)
+    # heavy-tile records (e, nb, c): tile row rr (gate|up: gate and up rows of
+    # h columns nb*128 + 16*(rr//32) + rr%16 alternating in 16-row blocks;
+    # down: W_down row nb*256 + rr) with K 64c..64c+63, zero past the weights
+    for _ in range(600):
+        gate_up = bool(rng.integers(2))
+        nbk, nc = (nbg, ncg) if gate_up else (nbd, ncd)
+        e, nb, c, rr = (int(rng.integers(n)) for n in (E, nbk, nc, 256))
+        if gate_up:
+            hc = nb * 128 + (rr // 32) * 16 + rr % 16
+            ok, row, src, K = hc < I, (hc if rr % 32 < 16 else I + hc), wgu[e], H
+        else:
+            row = nb * 256 + rr
+            ok, src, K = row < H, wdn[e], I
+        want = np.zeros(64, np.int16)
+        if ok:
+            seg = src[row, 64 * c: min(64 * c + 64, K)]
+            want[:seg.size] = seg
+        off = light + (0 if gate_up else rec_gu) + ((e * nbk + nb) * nc + c) * 256 * 64 + rr * 64
+        assert np.array_equal(words[off:off + 64], want), (gate_up, e, nb, c, rr)
