@@ -363,12 +363,12 @@ def main():
     elif dominant == "gateup_heavy":
         he = touched - light_experts
         hr = A - light_rows
-        alg = he * 2 * I * H * 2 + x_bytes + hr * I * 2
+        alg = he * gu_w + x_bytes + hr * I * 2
         flops = 4 * hr * H * I
     elif dominant == "down_heavy":
         he = touched - light_experts
         hr = A - light_rows
-        alg = he * H * I * 2 + hr * (I * 2 + H * y_el)
+        alg = he * dn_w + hr * (I * 2 + H * y_el)
         flops = 2 * hr * H * I
     elif dominant == "router_gemm":
         alg = x_bytes + H * cfg.E * 4
