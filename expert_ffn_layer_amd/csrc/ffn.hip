@@ -24,10 +24,15 @@
 //  * heavy: TM x 256 output tiles (TM = 256, 192 or 128, chosen from the row
 //    counts), A and B staged through LDS rings by direct-to-LDS loads, tiles
 //    of one expert scheduled together on one XCD.  Gate and up rows alternate
-//    by 16-row blocks, so g and u of an h column meet in one lane.
+//    by 16-row blocks, so g and u of an h column meet in one lane.  B comes
+//    from the row-major weights, or from the packed copy's per-stage records.
 // Both paths give every output element the same chain of MFMAs over K in
 // ascending 32-wide steps with the same K-slot assignment, and the same
 // epilogue, so a row's h and y are bitwise identical whichever loop ran it.
+// MXFP8 weights (OCP MX: E4M3 codes, an E8M0 scale per 32 values) run the
+// same loops: each 8 codes become the bf16 operand times the block scale by
+// the hardware's scaled conversion (exact), so the results are those of the
+// bf16 loops on the dequantised weights, bit for bit.
 #include <algorithm>
 
 #include "common.h"
@@ -446,8 +451,9 @@ __global__ __launch_bounds__(kThreads) void down_light_kernel(FfnArgs a) {
 // scaled conversion, code * 2^(scale - 127): exact, since an E4M3 value has
 // 4 significant bits.  Each accumulator then takes the same chain of MFMAs
 // over the same operands as the bf16 loop given the dequantised weights, so
-// the two give bitwise identical results.  Experts with more than 64 rows run
-// in passes of 64 rows (the weights are then read once per pass).
+// the two give bitwise identical results.  (The plan gives the light loop at
+// most 64 rows per expert; the kernels still step through larger counts in
+// passes of 64 rows, so no count can leave rows unwritten.)
 #ifndef MOE_LIGHT_MX_GU_U
 #define MOE_LIGHT_MX_GU_U 2     // 64-wide K chunks in flight per wave (gate|up)
 #endif

@@ -199,7 +199,7 @@ def dequant_layer(o, lay):
 
 MX_CASES = {
     "light": custom("light", T=40, H=256, E=64, k=4, I=192),
-    # 75 rows per expert: two passes of the light loop
+    # 75 rows per expert: heavy tiles, ragged
     "heavy_ragged": custom("heavy_ragged", T=300, H=320, E=16, k=4, I=96),
     "mixed": custom("mixed", T=203, H=256, E=48, k=10, I=128, zipf_s=1.2, zipf_alpha=0.6),
     "one_token": custom("one_token", T=1, H=512, E=128, k=10, I=256),
@@ -207,7 +207,7 @@ MX_CASES = {
     # I % 64 == 32: the last K chunk of W_down is half padding
     "i_tail": custom("i_tail", T=90, H=192, E=12, k=3, I=160),
     "max_e_k": custom("max_e_k", T=33, H=128, E=1024, k=32, I=64),
-    # 170 rows on one expert: three passes
+    # 170 rows on one expert (heavy tiles of 192 or 128 rows)
     "hot": custom("hot", T=170, H=128, E=4, k=1, I=64, zipf_s=3.0, zipf_alpha=1.0),
 }
 
@@ -231,9 +231,9 @@ def test_layer_bitwise_vs_dequantised_bf16(oracle_lib, name, y_bf16):
 @pytest.mark.parametrize("name", ["heavy_ragged", "mixed", "i_tail", "hot", "shared"])
 @pytest.mark.parametrize("lm,tm", [(0, 0), (0, 128), (0, 192), (64, 0), (16, 128)])
 def test_layer_bitwise_paths(oracle_lib, name, lm, tm):
-    """Every MXFP8 path -- heavy tiles of each height, the light loop (in
-    64-row passes past 64 rows), and splits between the two -- against the
-    bf16 layer on the dequantised weights (y bf16)."""
+    """Every MXFP8 path -- heavy tiles of each height, the light loop, and
+    splits between the two -- against the bf16 layer on the dequantised
+    weights (y bf16)."""
     print(f"[case] mxfp8 paths {name} light_max={lm} tm={tm}", flush=True)
     lay = layer_on_gpu(MX_CASES[name])
     ref = dequant_layer(oracle_lib, lay)
