@@ -1465,9 +1465,6 @@ int grid_for(long long work, int per_cu, int num_cu) {
     return (int)std::max<long long>(1, std::min<long long>(work, (long long)per_cu * num_cu));
 }
 
-// Heavy tiles of one GEMM.  With a plan the tile height is decided on the
-// device, so every height's kernel is launched and all but one return at
-// once; a dense group's height is known here.
 // bf16 heavy-tile records: one kRec16Bytes run per (expert, 256-row B tile
 // nb, 64-wide K stage c), row rr of the tile (the heavy kernel's B row order:
 // gate|up rows alternate in 16-row blocks of gate and up rows of h columns
@@ -1509,6 +1506,8 @@ __global__ __launch_bounds__(256) void pack_heavy_rec_kernel(const uint16_t* __r
     }
 }
 
+// Heavy tiles of one GEMM: one launch, one block per CU (the tile heights are
+// the plan's, read on the device); a dense group has one height.
 template <Mode M, bool YB>
 hipError_t launch_heavy(const FfnArgs& a, int ncols, hipStream_t st) {
     const long long nblk = (ncols + kTN - 1) / kTN;
