@@ -127,14 +127,19 @@ def summarize(args):
         with open(os.path.join(d, names[0])) as f:
             return list(csv.DictReader(f))
 
-    # Instances of one kernel (template arguments) add up per call.
-    stats = {}
+    # A kernel's instances (template arguments) are different launches: the
+    # heavy GEMMs of a layer with a shared expert run one instance for the
+    # routed experts and another for the shared one.  The table sums them per
+    # step; the dominant kernel's own line and traffic take its largest
+    # instance, the launch bench.py times (the routed one).
+    stats, inst = {}, {}
     for r in one_csv(kt_dir, "kernel_stats.csv"):
         lab = kernel_label(r["Name"])
         if not lab:
             continue
         cur = dict(calls=int(r["Calls"]), min_us=float(r["MinNs"]) / 1e3,
                    max_us=float(r["MaxNs"]) / 1e3, total_us=float(r["TotalDurationNs"]) / 1e3)
+        inst[r["Name"]] = dict(cur, label=lab, avg_us=cur["total_us"] / cur["calls"])
         if lab in stats:
             prev = stats[lab]
             big = prev if prev["total_us"] >= cur["total_us"] else cur
@@ -156,11 +161,14 @@ def summarize(args):
                 per.setdefault(lab, {}).setdefault(r["Kernel_Name"], []).append(v)
         assert copy, f"no reference copy kernel in {d}"
         scale = COPY_BYTES / (copy * 1024.0)
-        return {k: sum(sum(v) / len(v) for v in inst.values()) * 1024.0 * scale
-                for k, inst in per.items()}, scale
+        by_label = {k: sum(sum(v) / len(v) for v in ins.values()) * 1024.0 * scale
+                    for k, ins in per.items()}
+        by_inst = {n: sum(v) / len(v) * 1024.0 * scale
+                   for ins in per.values() for n, v in ins.items()}
+        return by_label, by_inst, scale
 
-    fetch, f_scale = counter(fetch_dir)
-    write, w_scale = counter(write_dir)
+    fetch, fetch_i, f_scale = counter(fetch_dir)
+    write, write_i, w_scale = counter(write_dir)
     rec = None
     with open(log) as f:
         for line in f:
@@ -171,16 +179,21 @@ def summarize(args):
     src_hash = rec["kernel_source_hash"]
     assert src_hash == kernel_source_hash(), "kernel sources changed since the profiled run"
 
-    traffic = fetch[dom] + write[dom]
+    dom_inst = max((n for n in inst if inst[n]["label"] == dom), key=lambda n: inst[n]["total_us"])
+    n_inst = sum(1 for n in inst if inst[n]["label"] == dom)
+    d_avg, d_calls = inst[dom_inst]["avg_us"], inst[dom_inst]["calls"]
+    f_dom = fetch_i.get(dom_inst, fetch[dom])
+    w_dom = write_i.get(dom_inst, write[dom])
+    traffic = f_dom + w_dom
     roof = rec["roofline"]
     out = {"kernel": dom, "workload": workload, "kernel_source_hash": src_hash,
            "hbm_bytes_per_launch": int(round(traffic)),
-           "fetch_bytes_per_launch": int(round(fetch[dom])),
-           "write_bytes_per_launch": int(round(write[dom])),
+           "fetch_bytes_per_launch": int(round(f_dom)),
+           "write_bytes_per_launch": int(round(w_dom)),
            "fetch_size_scale": round(f_scale, 4), "write_size_scale": round(w_scale, 4),
            "algorithmic_bytes_per_launch": roof["algorithmic_bytes"] if roof["kernel"] == dom
            else None,
-           "avg_duration_us": round(stats[dom]["avg_us"], 2)}
+           "avg_duration_us": round(d_avg, 2)}
     base = os.path.join(PROFILES, f"{dom}__{workload}")
     os.makedirs(PROFILES, exist_ok=True)
     with open(base + ".traffic.json", "w") as f:
@@ -194,9 +207,11 @@ def summarize(args):
     lines = [f"# {dom} on {workload}", "",
              "rocprofv3 summary of bench.py on one MI355X (gfx950).  Commands, from /tmp with",
              "TMPDIR=/tmp, $R the repository root:", "", "```", cmds, "```", "",
-             f"Dominant kernel: **{dom}**, average {stats[dom]['avg_us']:.1f} us over "
-             f"{stats[dom]['calls']} calls (kernel trace); bench.py's own HIP-event timing of "
-             f"it in the same run: "
+             f"Dominant kernel: **{dom}**, average {d_avg:.1f} us over "
+             f"{d_calls} calls (kernel trace"
+             + (f"; its largest of {n_inst} instances, the launch timed below; the table sums "
+                f"the instances per step" if n_inst > 1 else "")
+             + f"); bench.py's own HIP-event timing of it in the same run: "
              f"{roof['kernel_us']:.1f} us.",
              "", f"bench line: {rec['value']:.1f} {rec['unit']}, {rec['ms_per_step']:.4f} ms/step; "
              f"roofline {roof['bound']} {roof['achieved']} {roof['unit']} "
