@@ -53,10 +53,10 @@ def parse():
     p.add_argument("--no-packed", action="store_true",
                    help="the light loop reads the plain weight layout instead of the packed "
                         "copy made once before timing (moe_pack_weights)")
-    p.add_argument("--y-dtype", choices=("auto", "fp32", "bf16"), default="auto",
+    p.add_argument("--y-dtype", choices=("auto", "fp32", "bf16", "fp16"), default="auto",
                    help="storage of the routed expert outputs between the down GEMM and the "
-                        "combine; auto = bf16 except for a layer with a shared expert or "
-                        "fp32 values (their outputs need the fp32 margin)")
+                        "combine; auto = bf16, fp16 for a layer with a shared expert (its "
+                        "outputs need more than bf16's 8 bits), fp32 for fp32-valued layers")
     p.add_argument("--weights", choices=("bf16", "mxfp8"), default="bf16",
                    help="routed expert weights: bf16, or MXFP8 (OCP MX E4M3 codes with one "
                         "E8M0 scale per 32 values, quantised on the GPU before timing)")
@@ -280,10 +280,12 @@ def main():
     layer = synth.make_layer(cfg, seed=args.seed, device=dev)
     if cfg.fp32_values:
         layer = layer.rounded_to_bf16()
-    y_bf16 = args.y_dtype == "bf16" or (args.y_dtype == "auto" and not cfg.I_shared
-                                        and not cfg.fp32_values)
+    y_dt = args.y_dtype
+    if y_dt == "auto":
+        y_dt = "fp32" if cfg.fp32_values else ("fp16" if cfg.I_shared else "bf16")
     mx = args.weights == "mxfp8"
-    m = moe.MoELayer(layer, packed=not args.no_packed, y_bf16=y_bf16, weights=args.weights)
+    m = moe.MoELayer(layer, packed=not args.no_packed, y_bf16=y_dt == "bf16",
+                     weights=args.weights, y_fp16=y_dt == "fp16")
     s = m.shape
     w_gu_arg, w_dn_arg = (None, None) if mx else (layer.w_gu, layer.w_dn)
     out = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=dev)
@@ -353,7 +355,7 @@ def main():
     A = cfg.T * cfg.k
     H, I = cfg.H, cfg.I
     x_bytes = cfg.T * H * 2
-    y_el = 2 if y_bf16 else 4  # bytes per stored y value
+    y_el = 4 if y_dt == "fp32" else 2  # bytes per stored y value
     Is = cfg.I_shared
     # Bytes of one routed expert's weights as the kernels stream them: bf16,
     # or MXFP8 codes (W_down's K padded to 64) plus a scale byte per 32.
@@ -453,7 +455,7 @@ def main():
         "config": {"workload": workload, "tokens": cfg.T, "hidden": H, "experts": cfg.E,
                    "top_k": cfg.k, "intermediate": I, "shared_intermediate": cfg.I_shared,
                    "seed": args.seed, "packed_weights": m.packed is not None,
-                   "y_dtype": "bf16" if y_bf16 else "fp32",
+                   "y_dtype": y_dt,
                    "weights": "mxfp8 (E4M3, E8M0 per 32)" if mx else "bf16"},
         "roofline": roof,
         "layer_roofline": layer,

@@ -14,37 +14,48 @@ constexpr int kMaxK = 32;
 #endif
 
 
-// C consecutive y values (C = 4: fp32 or bf16; C = 8: bf16) as one raw
+// Storage of y: fp32, bf16 or fp16 (launch_combine's y_fmt).
+constexpr int kYF32 = 0, kYBF16 = 1, kYF16 = 2;
+
+// The 16-bit half of word u holding value c (c even: low half), widened to
+// fp32 exactly.
+template <int F>
+__device__ __forceinline__ float y16_elem(uint32_t u, int c) {
+    const uint32_t h = (c & 1) ? (u >> 16) : (u & 0xffffu);
+    if constexpr (F == kYBF16) return __uint_as_float(h << 16);
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// C consecutive y values (C = 4: any storage; C = 8: 16-bit) as one raw
 // vector load, read non-temporally (each y row is read once); elem() widens
 // value c to fp32 exactly.
-template <int C, bool BF16>
+template <int C, int F>
 struct YLoad;
 template <>
-struct YLoad<4, false> {
+struct YLoad<4, kYF32> {
     typedef floatx4_t raw_t;
     static __device__ __forceinline__ float elem(const raw_t& r, int c) { return r[c]; }
 };
-template <>
-struct YLoad<4, true> {
+template <int F>
+struct YLoad<4, F> {
     typedef u32x2_t raw_t;
     static __device__ __forceinline__ float elem(const raw_t& r, int c) {
-        const uint32_t u = r[c >> 1];
-        return __uint_as_float((c & 1) ? (u & 0xffff0000u) : (u << 16));
+        return y16_elem<F>(r[c >> 1], c);
     }
 };
-template <>
-struct YLoad<8, true> {
+template <int F>
+struct YLoad<8, F> {
+    static_assert(F != kYF32, "8 values per load: 16-bit y");
     typedef u32x4_t raw_t;
     static __device__ __forceinline__ float elem(const raw_t& r, int c) {
-        const uint32_t u = r[c >> 1];
-        return __uint_as_float((c & 1) ? (u & 0xffff0000u) : (u << 16));
+        return y16_elem<F>(r[c >> 1], c);
     }
 };
 
-template <int C, bool BF16>
-__device__ __forceinline__ typename YLoad<C, BF16>::raw_t load_y(const void* y, size_t idx) {
-    typedef typename YLoad<C, BF16>::raw_t R;
-    const char* p = static_cast<const char*>(y) + idx * (BF16 ? 2 : 4);
+template <int C, int F>
+__device__ __forceinline__ typename YLoad<C, F>::raw_t load_y(const void* y, size_t idx) {
+    typedef typename YLoad<C, F>::raw_t R;
+    const char* p = static_cast<const char*>(y) + idx * (F == kYF32 ? 4 : 2);
     return __builtin_nontemporal_load(reinterpret_cast<const R*>(p));
 }
 
@@ -53,12 +64,12 @@ __device__ __forceinline__ typename YLoad<C, BF16>::raw_t load_y(const void* y, 
 // pairs are uniform across the block.  y is read once and out written once,
 // so both go through non-temporal accesses (measured 9-14% faster at
 // T = 4096..8192).  Every element sums its k rows in ascending j.
-template <int kV, int C, bool BF16>
+template <int kV, int C, int F>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y,
                                                      const int32_t* __restrict__ inv_pos,
                                                      const float* __restrict__ w, int H, int k,
                                                      int accumulate, float* __restrict__ out) {
-    typedef YLoad<C, BF16> L;
+    typedef YLoad<C, F> L;
     constexpr int kSpan = 256 * C;
     const int t = blockIdx.x;
     const int cb = blockIdx.y * kSpan * kV + threadIdx.x * C;
@@ -78,7 +89,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
             typename L::raw_t v[kMaxK];
 #pragma unroll
             for (int j = 0; j < kMaxK; ++j)
-                if (j < k) v[j] = load_y<C, BF16>(y, (size_t)ip[j] * H + c0);
+                if (j < k) v[j] = load_y<C, F>(y, (size_t)ip[j] * H + c0);
 #pragma unroll
             for (int j = 0; j < kMaxK; ++j) {
                 if (j < k) {
@@ -92,7 +103,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
                 const int p = ip[j];
                 if (p < 0) continue;
                 const float wj = wt[j];
-                const typename L::raw_t v = load_y<C, BF16>(y, (size_t)p * H + c0);
+                const typename L::raw_t v = load_y<C, F>(y, (size_t)p * H + c0);
 #pragma unroll
                 for (int c = 0; c < C; ++c) acc[c] += wj * L::elem(v, c);
             }
@@ -112,24 +123,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
 
 }  // namespace
 
-hipError_t launch_combine(const void* y, int y_bf16, const int32_t* inv_pos, const float* w,
+hipError_t launch_combine(const void* y, int y_fmt, const int32_t* inv_pos, const float* w,
                           int T, int H, int k, int accumulate, float* out, hipStream_t st) {
     prof_begin(K_COMBINE, st);
     // Few tokens: one column group per thread, so that T * H / 1024 blocks
     // spread the gather over the whole chip (decode: 256 blocks, not 64).
-    // From 512 tokens: 16-byte row loads (4 fp32 or 8 bf16 columns), 4096
+    // From 512 tokens: 16-byte row loads (4 fp32 or 8 16-bit columns), 4096
     // columns per block.
     const dim3 g1(T, (H + 1023) / 1024), g4(T, (H + 4095) / 4096);
     if (T < MOE_COMBINE_SMALL_T) {
-        if (y_bf16)
-            combine_kernel<1, 4, true><<<g1, 256, 0, st>>>(y, inv_pos, w, H, k, accumulate, out);
+        if (y_fmt == kYBF16)
+            combine_kernel<1, 4, kYBF16><<<g1, 256, 0, st>>>(y, inv_pos, w, H, k, accumulate, out);
+        else if (y_fmt == kYF16)
+            combine_kernel<1, 4, kYF16><<<g1, 256, 0, st>>>(y, inv_pos, w, H, k, accumulate, out);
         else
-            combine_kernel<1, 4, false><<<g1, 256, 0, st>>>(y, inv_pos, w, H, k, accumulate, out);
+            combine_kernel<1, 4, kYF32><<<g1, 256, 0, st>>>(y, inv_pos, w, H, k, accumulate, out);
     } else {
-        if (y_bf16)
-            combine_kernel<2, 8, true><<<g4, 256, 0, st>>>(y, inv_pos, w, H, k, accumulate, out);
+        if (y_fmt == kYBF16)
+            combine_kernel<2, 8, kYBF16><<<g4, 256, 0, st>>>(y, inv_pos, w, H, k, accumulate, out);
+        else if (y_fmt == kYF16)
+            combine_kernel<2, 8, kYF16><<<g4, 256, 0, st>>>(y, inv_pos, w, H, k, accumulate, out);
         else
-            combine_kernel<4, 4, false><<<g4, 256, 0, st>>>(y, inv_pos, w, H, k, accumulate, out);
+            combine_kernel<4, 4, kYF32><<<g4, 256, 0, st>>>(y, inv_pos, w, H, k, accumulate, out);
     }
     prof_end(K_COMBINE, st);
     return hipGetLastError();

@@ -171,28 +171,64 @@ __device__ __forceinline__ bf16x8_t load_weights(const uint16_t* p) {
 constexpr int kLightSubTiles = kLightRowsMax / 16;  // 4
 constexpr int kLightWideU = 2;                      // K steps in flight, wide branch
 
-// ------------------------------------------------------- y in bf16
+// ------------------------------------------------------- y in 16 bits
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float floatx2_t __attribute__((ext_vector_type(2)));
+
+// Storage of y (FfnArgs::y_fmt): fp32, bf16 or fp16.
+constexpr int kYF32 = 0, kYBF16 = 1, kYF16 = 2;
 
 // Two fp32 values as one word of two bf16 (round to nearest even), a in the
 // low half.
 __device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2_t{a, b}, bf16x2_t));
 }
+// The same as two fp16 (round to nearest even; past 65504 rounds to inf).
+__device__ __forceinline__ uint32_t pack_f16_rne(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2_t{a, b}, f16x2_t));
+}
+template <int YF>
+__device__ __forceinline__ uint32_t pack_y16(float a, float b) {
+    static_assert(YF == kYBF16 || YF == kYF16, "16-bit y");
+    return YF == kYBF16 ? pack_bf16_rne(a, b) : pack_f16_rne(a, b);
+}
 
 // A lane of a 16x16 MFMA result holds rows 4g..4g+3 of column c = l16.  For
-// 32-bit bf16 stores the lanes of columns c and c^1 swap halves: the even
-// column's lane then holds rows 4g, 4g+1 and the odd column's lane rows
+// 32-bit stores of 16-bit y the lanes of columns c and c^1 swap halves: the
+// even column's lane then holds rows 4g, 4g+1 and the odd column's lane rows
 // 4g+2, 4g+3, each as the word (column c & ~1, column c | 1).  Every lane of
 // the wave must call this (a lane exchange).
-__device__ __forceinline__ void y_bf16_pairs(const floatx4_t v, int l16, uint32_t& w0,
-                                             uint32_t& w1) {
+template <int YF>
+__device__ __forceinline__ void y16_pairs(const floatx4_t v, int l16, uint32_t& w0, uint32_t& w1) {
     const bool odd = l16 & 1;
     const float s0 = __shfl_xor(odd ? v[0] : v[2], 1, 64);
     const float s1 = __shfl_xor(odd ? v[1] : v[3], 1, 64);
-    w0 = odd ? pack_bf16_rne(s0, v[2]) : pack_bf16_rne(v[0], s0);
-    w1 = odd ? pack_bf16_rne(s1, v[3]) : pack_bf16_rne(v[1], s1);
+    w0 = odd ? pack_y16<YF>(s0, v[2]) : pack_y16<YF>(v[0], s0);
+    w1 = odd ? pack_y16<YF>(s1, v[3]) : pack_y16<YF>(v[1], s1);
+}
+
+// The light loops' 16-bit y epilogue: rows r0.. of the wave's MT x NT tiles
+// at columns c0 + 16t ...
+template <int YF, int MT, int NT>
+__device__ __forceinline__ void light_store_y16(const FfnArgs& a, const floatx4_t (&acc)[MT][NT],
+                                                int r0, int n, int c0, int l16, int g) {
+    const int odd = l16 & 1;
+    uint32_t* y = static_cast<uint32_t*>(a.y);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            uint32_t w[2];
+            y16_pairs<YF>(acc[m][t], l16, w[0], w[1]);
+            const int c = c0 + t * 16 + l16 - odd;  // even
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int row = m * 16 + 4 * g + 2 * odd + r;
+                if (row < n) y[((size_t)(r0 + row) * a.H + c) / 2] = w[r];
+            }
+        }
+    }
 }
 
 // ------------------------------------------------------- light: gate|up
@@ -386,23 +422,12 @@ __device__ __forceinline__ void down_light_rows(const FfnArgs& a, int e, int r0,
             for (int t = 0; t < NT; ++t) cb[u][t] = nb_[u][t];
         }
     }
-    if (a.y_bf16) {
-        const int odd = l16 & 1;
-        uint32_t* y = static_cast<uint32_t*>(a.y);
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                uint32_t w[2];
-                y_bf16_pairs(acc[m][t], l16, w[0], w[1]);
-                const int c = c0 + t * 16 + l16 - odd;  // even
-#pragma unroll
-                for (int r = 0; r < 2; ++r) {
-                    const int row = m * 16 + 4 * g + 2 * odd + r;
-                    if (row < n) y[((size_t)(r0 + row) * a.H + c) / 2] = w[r];
-                }
-            }
-        }
+    if (a.y_fmt == kYBF16) {
+        light_store_y16<kYBF16>(a, acc, r0, n, c0, l16, g);
+        return;
+    }
+    if (a.y_fmt == kYF16) {
+        light_store_y16<kYF16>(a, acc, r0, n, c0, l16, g);
         return;
     }
     float* y = static_cast<float*>(a.y);
@@ -717,23 +742,12 @@ __device__ __forceinline__ void down_light_rows_mx(const FfnArgs& a, int e, int 
             }
         }
     }
-    if (a.y_bf16) {
-        const int odd = l16 & 1;
-        uint32_t* y = static_cast<uint32_t*>(a.y);
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                uint32_t w[2];
-                y_bf16_pairs(acc[m][t], l16, w[0], w[1]);
-                const int c = c0 + t * 16 + l16 - odd;  // even
-#pragma unroll
-                for (int r = 0; r < 2; ++r) {
-                    const int row = m * 16 + 4 * g + 2 * odd + r;
-                    if (row < n) y[((size_t)(r0 + row) * a.H + c) / 2] = w[r];
-                }
-            }
-        }
+    if (a.y_fmt == kYBF16) {
+        light_store_y16<kYBF16>(a, acc, r0, n, c0, l16, g);
+        return;
+    }
+    if (a.y_fmt == kYF16) {
+        light_store_y16<kYF16>(a, acc, r0, n, c0, l16, g);
         return;
     }
     float* y = static_cast<float*>(a.y);
@@ -885,7 +899,7 @@ __device__ __forceinline__ int tile_tmi(const FfnArgs& a, int tile) {
 // Runs this block's work items wi, wi + nb_x, ... (below wend) while their
 // row tiles are TM rows high, and returns the first item of another height
 // (or one at or past wend).
-// YB (down only): y stored as bf16 instead of fp32 (a.y_bf16).
+// YF (down only): y storage, fp32, bf16 or fp16 (a.y_fmt).
 // BS: where B (the weights) comes from -- kBRowMajor: w_gu / w_dn; kBRec16:
 // the bf16 heavy-tile records of the packed copy (a.hr_gu / a.hr_dn: one
 // 32 KB run per (expert, 256-row tile, K stage), so a stage is one
@@ -896,7 +910,7 @@ __device__ __forceinline__ int tile_tmi(const FfnArgs& a, int tile) {
 // bytes) and its two scales, and the hardware's scaled conversion turns
 // them into the bf16 operands of the bf16 path -- the same MFMA chains on the
 // dequantised weights, so the results equal the bf16 path's bit for bit.
-template <Mode M, int TM, bool YB, int BS>
+template <Mode M, int TM, int YF, int BS>
 __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, long long wi,
                                                  long long wend, int nb_x, int nblk) {
     using G = HeavyGeom<M, TM>;
@@ -1358,8 +1372,8 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
                     }
                 }
             }
-        } else if constexpr (YB) {
-            // bf16 y: lanes of adjacent columns pair up (y_bf16_pairs), so
+        } else if constexpr (YF != kYF32) {
+            // 16-bit y: lanes of adjacent columns pair up (y16_pairs), so
             // each lane writes 2 rows x 2 columns as two 32-bit words.
             const int odd = l16 & 1;
             const int c0 = t_nb * kTN + wn * kWTN + l16 - odd;  // even
@@ -1371,7 +1385,7 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     uint32_t w[2];
-                    y_bf16_pairs(acc[i][j], l16, w[0], w[1]);
+                    y16_pairs<YF>(acc[i][j], l16, w[0], w[1]);
                     const bool col_ok = c0 + j * 16 < a.H;
 #pragma unroll
                     for (int r = 0; r < 2; ++r) {
@@ -1414,7 +1428,7 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
 // One launch per GEMM: every row tile runs with the body of its own height
 // (the plan mixes heights within an expert); the bodies share one LDS
 // allocation, the largest ring.
-template <Mode M, bool YB, int BS>
+template <Mode M, int YF, int BS>
 __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
     __shared__ __attribute__((aligned(1024))) char lds[kHeavyLds];
     const int N = (M == Mode::GateUp) ? 2 * a.I : a.H;
@@ -1451,12 +1465,12 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
             if constexpr (BS == kBRecMx)
                 wi = wend;
             else
-                wi = ffn_heavy_run<M, kTileTM0, YB, BS>(a, lds, wi, wend, nb_x, nblk);
+                wi = ffn_heavy_run<M, kTileTM0, YF, BS>(a, lds, wi, wend, nb_x, nblk);
         }
         else if (tmi == 1)
-            wi = ffn_heavy_run<M, kTileTM1, YB, BS>(a, lds, wi, wend, nb_x, nblk);
+            wi = ffn_heavy_run<M, kTileTM1, YF, BS>(a, lds, wi, wend, nb_x, nblk);
         else
-            wi = ffn_heavy_run<M, kTileTM2, YB, BS>(a, lds, wi, wend, nb_x, nblk);
+            wi = ffn_heavy_run<M, kTileTM2, YF, BS>(a, lds, wi, wend, nb_x, nblk);
     }
 }
 
@@ -1543,18 +1557,18 @@ __global__ __launch_bounds__(256) void pack_heavy_rec_kernel(const uint16_t* __r
 
 // Heavy tiles of one GEMM: one launch, one block per CU (the tile heights are
 // the plan's, read on the device); a dense group has one height.
-template <Mode M, bool YB>
+template <Mode M, int YF>
 hipError_t launch_heavy(const FfnArgs& a, int ncols, hipStream_t st) {
     const long long nblk = (ncols + kTN - 1) / kTN;
     if (a.plan) {
         if (a.max_tiles <= 0) return hipSuccess;
         const int grid = grid_for((long long)a.max_tiles * nblk, 1, a.num_cu);
         if (a.w_mxfp8)
-            ffn_heavy_kernel<M, YB, kBRecMx><<<grid, kHeavyThreads, 0, st>>>(a);
+            ffn_heavy_kernel<M, YF, kBRecMx><<<grid, kHeavyThreads, 0, st>>>(a);
         else if (a.hr_gu)
-            ffn_heavy_kernel<M, YB, kBRec16><<<grid, kHeavyThreads, 0, st>>>(a);
+            ffn_heavy_kernel<M, YF, kBRec16><<<grid, kHeavyThreads, 0, st>>>(a);
         else
-            ffn_heavy_kernel<M, YB, kBRowMajor><<<grid, kHeavyThreads, 0, st>>>(a);
+            ffn_heavy_kernel<M, YF, kBRowMajor><<<grid, kHeavyThreads, 0, st>>>(a);
         return hipGetLastError();
     }
     if (a.dense_rows <= 0) return hipSuccess;
@@ -1562,7 +1576,7 @@ hipError_t launch_heavy(const FfnArgs& a, int ncols, hipStream_t st) {
     const int grid = grid_for(tiles * nblk, 1, a.num_cu);
     if (a.dense_tm != kTileTM0 && a.dense_tm != kTileTM1 && a.dense_tm != kTileTM2)
         return hipErrorInvalidValue;
-    ffn_heavy_kernel<M, YB, kBRowMajor><<<grid, kHeavyThreads, 0, st>>>(a);  // dense groups
+    ffn_heavy_kernel<M, YF, kBRowMajor><<<grid, kHeavyThreads, 0, st>>>(a);  // dense groups
     return hipGetLastError();
 }
 
@@ -1641,7 +1655,7 @@ hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t st) {
     }
     if ((a.plan && a.max_tiles > 0) || (!a.plan && a.dense_rows > 0)) {
         prof_begin(K_GATEUP_HEAVY, st);
-        hipError_t err = launch_heavy<Mode::GateUp, false>(a, 2 * a.I, st);
+        hipError_t err = launch_heavy<Mode::GateUp, kYF32>(a, 2 * a.I, st);
         prof_end(K_GATEUP_HEAVY, st);
         return err;
     }
@@ -1669,8 +1683,9 @@ hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st) {
     }
     if ((a.plan && a.max_tiles > 0) || (!a.plan && a.dense_rows > 0)) {
         prof_begin(K_DOWN_HEAVY, st);
-        hipError_t err = a.y_bf16 ? launch_heavy<Mode::Down, true>(a, a.H, st)
-                                  : launch_heavy<Mode::Down, false>(a, a.H, st);
+        hipError_t err = a.y_fmt == kYBF16  ? launch_heavy<Mode::Down, kYBF16>(a, a.H, st)
+                         : a.y_fmt == kYF16 ? launch_heavy<Mode::Down, kYF16>(a, a.H, st)
+                                            : launch_heavy<Mode::Down, kYF32>(a, a.H, st);
         prof_end(K_DOWN_HEAVY, st);
         return err;
     }

@@ -195,7 +195,7 @@ struct FfnArgs {
     const uint16_t* w_gu;        // [E,2I,H]
     const uint16_t* w_dn;        // [E,H,I]
     uint16_t* h;                 // [rows,I] bf16 ([rows,2I] when split_h)
-    void* y;                     // [rows,H]: fp32, or bf16 when y_bf16
+    void* y;                     // [rows,H]: fp32, bf16 or fp16 (y_fmt)
     const int32_t* plan;         // device plan, or nullptr for a dense group
     int T, H, I, E;
     int dense_rows;              // rows of a dense group (plan == nullptr)
@@ -207,7 +207,7 @@ struct FfnArgs {
     const uint16_t* pk_dn;       // packed W_down for the light loop, or nullptr
     int max_light;               // grid bound for light experts
     int num_cu;
-    int y_bf16;                  // 1: y stored as bf16 (round to nearest even)
+    int y_fmt;                   // y storage: 0 fp32, 1 bf16, 2 fp16 (round to nearest even)
     // MXFP8 routed weights (w_mxfp8 = 1): the light loop and the heavy tiles
     // read these instead of pk_gu / pk_dn and w_gu / w_dn.
     int w_mxfp8;
@@ -285,8 +285,8 @@ hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t st);
 hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st);
 
 // ---- combine ------------------------------------------------------------
-// y: [A,H] fp32, or bf16 when y_bf16.
-hipError_t launch_combine(const void* y, int y_bf16, const int32_t* inv_pos, const float* w,
+// y: [A,H] fp32 (y_fmt 0), bf16 (1) or fp16 (2).
+hipError_t launch_combine(const void* y, int y_fmt, const int32_t* inv_pos, const float* w,
                           int T, int H, int k, int accumulate, float* out, hipStream_t st);
 
 }  // namespace moe

@@ -54,6 +54,9 @@ int router_splits(int T, int H, int E) {
     return s;
 }
 
+// Storage of the routed outputs y: 0 fp32, 1 bf16, 2 fp16.
+int y_format(const moe_shape* s) { return s->y_fp16 ? 2 : (s->y_bf16 ? 1 : 0); }
+
 int check_shape(const moe_shape* s) {
     if (!s) return fail(MOE_ERR_NULL, "shape is NULL");
     if (s->T < 0 || s->H <= 0 || s->E <= 0 || s->k <= 0 || s->I <= 0 || s->I_shared < 0)
@@ -75,6 +78,8 @@ int check_shape(const moe_shape* s) {
         s->heavy_tile_rows != moe::kTileTM1 && s->heavy_tile_rows != moe::kTileTM2)
         return fail(MOE_ERR_UNSUPPORTED, "heavy_tile_rows must be 0, 128, 192 or 256");
     if (s->y_bf16 != 0 && s->y_bf16 != 1) return fail(MOE_ERR_UNSUPPORTED, "y_bf16 must be 0 or 1");
+    if (s->y_fp16 != 0 && s->y_fp16 != 1) return fail(MOE_ERR_UNSUPPORTED, "y_fp16 must be 0 or 1");
+    if (s->y_bf16 && s->y_fp16) return fail(MOE_ERR_UNSUPPORTED, "y_bf16 and y_fp16 are exclusive");
     if (s->w_mxfp8 != 0 && s->w_mxfp8 != 1)
         return fail(MOE_ERR_UNSUPPORTED, "w_mxfp8 must be 0 or 1");
     if (s->w_mxfp8 && s->heavy_tile_rows == moe::kTileTM0)
@@ -128,7 +133,7 @@ Layout layout(const moe_shape* s) {
     L.inv = take((size_t)A * 4);
     L.plan = take((size_t)(moe::kPlanHeader + E + 2LL * L.max_tiles) * 4);
     L.h = take((size_t)A * I * 2);
-    L.y = take((size_t)A * H * (s->y_bf16 ? 2 : 4));
+    L.y = take((size_t)A * H * (y_format(s) ? 2 : 4));
     L.hs = take((size_t)T * 2 * s->I_shared * 2);  // [hi | lo] rows
     L.total = off;
     return L;
@@ -245,7 +250,7 @@ int run_ffn(const moe_shape* s, const Layout& L, const uint16_t* x, const int32_
     a.max_tiles = L.max_tiles;
     a.max_light = L.max_light;
     a.num_cu = ncu;
-    a.y_bf16 = s->y_bf16;
+    a.y_fmt = y_format(s);
     a.w_mxfp8 = s->w_mxfp8;
     if (packed && s->w_mxfp8) {
         const uint8_t* p = static_cast<const uint8_t*>(packed);
@@ -294,7 +299,7 @@ int run_shared(const moe_shape* s, const Layout& L, const uint16_t* x, const uin
     a.max_tiles = 0;
     a.max_light = 0;
     a.num_cu = ncu;
-    a.y_bf16 = 0;  // written straight into the fp32 output
+    a.y_fmt = 0;  // written straight into the fp32 output
     HIP_TRY(moe::launch_ffn_gateup(a, st), "shared gate|up");
     HIP_TRY(moe::launch_ffn_down(a, st), "shared down");
     return MOE_OK;
@@ -488,7 +493,7 @@ int moe_combine(const moe_shape* shape, const void* y, const int32_t* inv_pos,
     REQUIRE_PTR(inv_pos);
     REQUIRE_PTR(topk_w);
     REQUIRE_PTR(out);
-    HIP_TRY(moe::launch_combine(y, shape->y_bf16, inv_pos, topk_w, shape->T, shape->H, shape->k,
+    HIP_TRY(moe::launch_combine(y, y_format(shape), inv_pos, topk_w, shape->T, shape->H, shape->k,
                                 accumulate ? 1 : 0, out, (hipStream_t)stream),
             "combine");
     return MOE_OK;
@@ -549,7 +554,7 @@ int moe_forward(const moe_shape* shape, const uint16_t* x, const float* w_router
         return rc;
     if (shape->I_shared > 0)
         if (int rc = run_shared(shape, L, x, ws_gate_up, ws_down, out, workspace, st)) return rc;
-    HIP_TRY(moe::launch_combine(y, shape->y_bf16, inv, w, shape->T, shape->H, shape->k,
+    HIP_TRY(moe::launch_combine(y, y_format(shape), inv, w, shape->T, shape->H, shape->k,
                                 shape->I_shared > 0 ? 1 : 0, out, st),
             "combine");
     return MOE_OK;

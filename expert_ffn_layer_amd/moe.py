@@ -64,7 +64,7 @@ class MoeShape(ctypes.Structure):
                 ("k", ctypes.c_int32), ("I", ctypes.c_int32), ("I_shared", ctypes.c_int32),
                 ("renorm", ctypes.c_int32), ("light_max_rows", ctypes.c_int32),
                 ("heavy_tile_rows", ctypes.c_int32), ("y_bf16", ctypes.c_int32),
-                ("w_mxfp8", ctypes.c_int32)]
+                ("w_mxfp8", ctypes.c_int32), ("y_fp16", ctypes.c_int32)]
 
     def __repr__(self):
         return ("MoeShape(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")")
@@ -130,9 +130,9 @@ def _check(rc: int) -> None:
 
 
 def make_shape(T, H, E, k, I, I_shared=0, renorm=1, light_max_rows=-1,
-               heavy_tile_rows=0, y_bf16=0, w_mxfp8=0) -> MoeShape:
+               heavy_tile_rows=0, y_bf16=0, w_mxfp8=0, y_fp16=0) -> MoeShape:
     return MoeShape(T, H, E, k, I, I_shared, renorm, light_max_rows, heavy_tile_rows,
-                    int(bool(y_bf16)), int(bool(w_mxfp8)))
+                    int(bool(y_bf16)), int(bool(w_mxfp8)), int(bool(y_fp16)))
 
 
 def workspace_bytes(shape: MoeShape) -> int:
@@ -286,7 +286,7 @@ def shared_ffn(shape, x, ws_gate_up, ws_down, out, workspace, stream=None):
 
 def y_dtype(shape) -> torch.dtype:
     """Element type of the routed expert outputs y for ``shape``."""
-    return BF16 if shape.y_bf16 else F32
+    return torch.float16 if shape.y_fp16 else (BF16 if shape.y_bf16 else F32)
 
 
 def combine(shape, y, inv_pos, topk_w, accumulate, out, stream=None):
@@ -338,7 +338,8 @@ class MoELayer:
     moe_forward and returns (out, topk_ids, topk_w, counts)."""
 
     def __init__(self, layer, light_max_rows: int = -1, heavy_tile_rows: int = 0,
-                 packed: bool = False, y_bf16: bool = False, weights: str = "bf16"):
+                 packed: bool = False, y_bf16: bool = False, weights: str = "bf16",
+                 y_fp16: bool = False):
         """weights="mxfp8" quantises the routed expert weights to MXFP8 on the
         device and runs the layer on them (packed implied)."""
         if weights not in ("bf16", "mxfp8"):
@@ -347,7 +348,7 @@ class MoELayer:
         self.layer = layer
         mx = weights == "mxfp8"
         self.shape = make_shape(c.T, c.H, c.E, c.k, c.I, c.I_shared, c.renorm, light_max_rows,
-                                heavy_tile_rows, y_bf16, mx)
+                                heavy_tile_rows, y_bf16, mx, y_fp16)
         self.workspace = alloc_workspace(self.shape, layer.x.device)
         if mx:
             q_gu, s_gu = quantize_mxfp8(layer.w_gu)

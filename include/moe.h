@@ -106,6 +106,11 @@ typedef struct moe_shape {
                                (heavy_tile_rows = 256 is MOE_ERR_UNSUPPORTED), and the results
                                are those of the bf16 path on the dequantised weights, bit for
                                bit.  The shared expert stays bf16. */
+    int32_t y_fp16;         /* 1: the routed expert outputs y are stored as fp16 (round to
+                               nearest even) instead: the same bytes as bf16 with 11
+                               significant bits, for layers whose |y| stay well below
+                               65504 (larger values round to infinity).  Exclusive with
+                               y_bf16 (both 1: MOE_ERR_UNSUPPORTED). */
 } moe_shape;
 
 /* Bytes of workspace every call below needs for `shape` (host-only, pure;
@@ -236,9 +241,10 @@ int moe_pack_weights_mxfp8(const moe_shape* shape, const uint8_t* codes_gate_up,
  *                    moe_pack_weights_mxfp8) and w_gate_up / w_down are not
  *                    read (may be NULL)
  *   h                bf16 [T*k,I] out, or NULL (then kept in the workspace)
- *   y                [T*k,H] out: fp32 (shape->y_bf16 == 0; large |y| entering
- *                    the weighted sum keep 24 significant bits) or bf16
- *                    (shape->y_bf16 == 1, rounded to nearest even)
+ *   y                [T*k,H] out: fp32 (shape->y_bf16 == y_fp16 == 0; large |y|
+ *                    entering the weighted sum keep 24 significant bits), bf16
+ *                    (shape->y_bf16 == 1) or fp16 (shape->y_fp16 == 1), rounded
+ *                    to nearest even
  */
 int moe_grouped_ffn(const moe_shape* shape, const uint16_t* x,
                     const int32_t* sorted_token_ids, const int32_t* offsets,
@@ -262,7 +268,7 @@ int moe_shared_ffn(const moe_shape* shape, const uint16_t* x, const uint16_t* ws
  *   s[t,c]   = sum_{j<k} topk_w[t,j] * y[inv_pos[t*k+j], c]   (ascending j,
  *              fp32; rows with inv_pos < 0 are skipped)
  *   out[t,c] = accumulate ? out[t,c] + s[t,c] : s[t,c]
- *   y [T*k,H] fp32 or bf16 as shape->y_bf16 says, inv_pos int32 [T*k],
+ *   y [T*k,H] fp32, bf16 or fp16 as shape->y_bf16 / y_fp16 say, inv_pos int32 [T*k],
  *   topk_w fp32 [T,k], out fp32 [T,H].  No workspace. */
 int moe_combine(const moe_shape* shape, const void* y, const int32_t* inv_pos,
                 const float* topk_w, int32_t accumulate, float* out, void* stream);

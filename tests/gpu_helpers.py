@@ -29,8 +29,9 @@ W_ATOL = 1e-6
 DEV = "cuda"
 
 
-def gpu_forward(layer, light_max_rows: int = -1, heavy_tile_rows: int = 0, y_bf16: bool = False):
-    m = moe.MoELayer(layer, light_max_rows, heavy_tile_rows, y_bf16=y_bf16)
+def gpu_forward(layer, light_max_rows: int = -1, heavy_tile_rows: int = 0, y_bf16: bool = False,
+                y_fp16: bool = False):
+    m = moe.MoELayer(layer, light_max_rows, heavy_tile_rows, y_bf16=y_bf16, y_fp16=y_fp16)
     out, ids, w, counts = m()
     torch.cuda.synchronize()
     return dict(out=out.cpu().numpy(), ids=ids.cpu().numpy(), w=w.cpu().numpy(),
@@ -73,12 +74,12 @@ def check_routing(gpu_ids, gpu_w, ref):
 
 
 def check_layer(o, layer, tokens=None, light_max_rows: int = -1, full_routing=True,
-                heavy_tile_rows: int = 0, y_bf16: bool = False):
+                heavy_tile_rows: int = 0, y_bf16: bool = False, y_fp16: bool = False):
     """Run the layer on the GPU and compare with the oracle.  ``tokens``
     restricts the FFN/combine comparison to a sample of token rows; routing
     is compared on every token when ``full_routing``."""
     c = layer.cfg
-    g = gpu_forward(layer, light_max_rows, heavy_tile_rows, y_bf16)
+    g = gpu_forward(layer, light_max_rows, heavy_tile_rows, y_bf16, y_fp16)
     report = {}
     if full_routing:
         r_all = o.route(o.logits(layer.x, layer.wg, layer.bias), c.k, c.renorm)

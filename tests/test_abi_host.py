@@ -42,7 +42,7 @@ def test_library_has_gfx950_code():
 
 def shp(**kw):
     base = dict(T=64, H=4096, E=512, k=10, I=1024, I_shared=0, renorm=1, light_max_rows=-1,
-                heavy_tile_rows=0, y_bf16=0, w_mxfp8=0)
+                heavy_tile_rows=0, y_bf16=0, w_mxfp8=0, y_fp16=0)
     base.update(kw)
     return moe.MoeShape(*[base[n] for n, _ in moe.MoeShape._fields_])
 
@@ -70,6 +70,9 @@ def test_workspace_bf16_y(L):
     half = moe.workspace_bytes(shp(T=c.T, y_bf16=1))
     assert full - half == A * c.H * 2
     assert moe.make_shape(4, 64, 8, 2, 32, y_bf16=True).y_bf16 == 1
+    # fp16 y: the same bytes as bf16
+    assert moe.workspace_bytes(shp(T=c.T, y_fp16=1)) == half
+    assert moe.make_shape(4, 64, 8, 2, 32, y_fp16=True).y_fp16 == 1
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -83,6 +86,7 @@ def test_workspace_bf16_y(L):
     (dict(I_shared=1 << 18), moe.MOE_ERR_UNSUPPORTED),
     (dict(y_bf16=2), moe.MOE_ERR_UNSUPPORTED), (dict(y_bf16=-1), moe.MOE_ERR_UNSUPPORTED),
     (dict(w_mxfp8=2), moe.MOE_ERR_UNSUPPORTED), (dict(w_mxfp8=-1), moe.MOE_ERR_UNSUPPORTED),
+    (dict(y_fp16=2), moe.MOE_ERR_UNSUPPORTED), (dict(y_fp16=1, y_bf16=1), moe.MOE_ERR_UNSUPPORTED),
 ])
 def test_bad_shapes(L, kw, code):
     s = shp(**kw)

@@ -55,12 +55,19 @@ def test_forward_small(oracle_lib, name):
     log(name, rep)
 
 
+# y storage as (y_bf16, y_fp16)
+YFMT = {"fp32": (False, False), "bf16": (True, False), "fp16": (False, True)}
+
+
 @pytest.mark.parametrize("name", ["light", "heavy_ragged", "mixed", "shared", "max_e_k"])
-def test_forward_small_bf16_y(oracle_lib, name):
-    """Routed expert outputs stored as bf16 (the shared expert stays fp32)."""
-    print(f"[case] forward bf16 y {name}", flush=True)
-    rep = gh.check_layer(oracle_lib, layer_on_gpu(SMALL[name]), y_bf16=True)
-    log(name + "/bf16y", rep)
+@pytest.mark.parametrize("yf", ["bf16", "fp16"])
+def test_forward_small_16bit_y(oracle_lib, name, yf):
+    """Routed expert outputs stored as bf16 or fp16 (the shared expert stays
+    fp32)."""
+    print(f"[case] forward {yf} y {name}", flush=True)
+    yb, yh = YFMT[yf]
+    rep = gh.check_layer(oracle_lib, layer_on_gpu(SMALL[name]), y_bf16=yb, y_fp16=yh)
+    log(f"{name}/{yf}y", rep)
 
 
 @pytest.mark.parametrize("name", ["tiny", "light", "mixed"])
@@ -124,19 +131,21 @@ def test_forward_heavy_ragged_heights(oracle_lib, tm):
 
 
 # ------------------------------------------------------------ full size
-@pytest.mark.parametrize("name,sample,y_bf16", [
-    ("decode", None, False), ("prefill", 64, False), ("skew", 64, False), ("ling", 48, False),
-    # bf16 y, as the benchmark runs the layers without a shared expert
-    ("decode", None, True), ("prefill", 64, True), ("skew", 64, True)])
-def test_forward_full_size(oracle_lib, name, sample, y_bf16):
-    print(f"[case] full-size {name} y_bf16={y_bf16}", flush=True)
+@pytest.mark.parametrize("name,sample,yf", [
+    ("decode", None, "fp32"), ("prefill", 64, "fp32"), ("skew", 64, "fp32"), ("ling", 48, "fp32"),
+    # 16-bit y, as the benchmark runs the layers: bf16 without a shared
+    # expert, fp16 with one
+    ("decode", None, "bf16"), ("prefill", 64, "bf16"), ("skew", 64, "bf16"), ("ling", 48, "fp16")])
+def test_forward_full_size(oracle_lib, name, sample, yf):
+    print(f"[case] full-size {name} y={yf}", flush=True)
+    y_bf16, y_fp16 = YFMT[yf]
     cfg = synth.CONFIGS[name]
     lay = layer_on_gpu(cfg)
     tokens = None
     if sample:
         tokens = np.sort(np.random.default_rng(1).choice(cfg.T, sample, replace=False))
-    rep = gh.check_layer(oracle_lib, lay, tokens=tokens, y_bf16=y_bf16)
-    log(f"{name}/bf16y={y_bf16}", rep)
+    rep = gh.check_layer(oracle_lib, lay, tokens=tokens, y_bf16=y_bf16, y_fp16=y_fp16)
+    log(f"{name}/y={yf}", rep)
     counts = rep["gpu"]["counts"]
     assert counts.sum() == cfg.T * cfg.k
     if name == "prefill":
@@ -255,16 +264,18 @@ def test_router_nonfinite(oracle_lib):
 
 
 @pytest.mark.parametrize("light_max", [16, 64])
-@pytest.mark.parametrize("y_bf16", [False, True])
-def test_light_heavy_bitwise(light_max, y_bf16):
+@pytest.mark.parametrize("yf", ["fp32", "bf16", "fp16"])
+def test_light_heavy_bitwise(light_max, yf):
     """The same expert rows through the light loop (both its 16-row and its
     wide 17..64-row branch) and through the heavy tiles give bitwise
-    identical h and y (fp32 or bf16)."""
+    identical h and y (fp32, bf16 or fp16)."""
+    y_bf16, y_fp16 = YFMT[yf]
     cfg = custom("lh", T=160, H=512, E=64, k=8, I=256)
     lay = layer_on_gpu(cfg)
     outs = []
     for lm in (light_max, 0):
-        s = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, light_max_rows=lm, y_bf16=y_bf16)
+        s = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, light_max_rows=lm, y_bf16=y_bf16,
+                           y_fp16=y_fp16)
         ws = moe.alloc_workspace(s)
         A = cfg.T * cfg.k
         ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=gh.DEV)
@@ -277,7 +288,7 @@ def test_light_heavy_bitwise(light_max, y_bf16):
         y = torch.empty((A, cfg.H), dtype=moe.y_dtype(s), device=gh.DEV)
         moe.grouped_ffn(s, lay.x, srt, offsets, lay.w_gu, lay.w_dn, h, y, ws)
         torch.cuda.synchronize()
-        yi = y.view(torch.int16) if y_bf16 else y.view(torch.int32)
+        yi = y.view(torch.int16) if (y_bf16 or y_fp16) else y.view(torch.int32)
         outs.append((counts.cpu().numpy(), h.view(torch.int16).cpu().numpy(), yi.cpu().numpy()))
     (c0, h0, y0), (c1, h1, y1) = outs
     assert np.array_equal(c0, c1)
@@ -288,13 +299,14 @@ def test_light_heavy_bitwise(light_max, y_bf16):
     assert np.array_equal(y0, y1), "y differs between light and heavy loops"
 
 
-@pytest.mark.parametrize("y_bf16", [False, True])
-def test_ffn_stage_rows(oracle_lib, y_bf16):
-    """Grouped FFN rows (fp32 or bf16 y from bf16 h) against the oracle's
-    per-row expert FFN."""
+@pytest.mark.parametrize("yf", ["fp32", "bf16", "fp16"])
+def test_ffn_stage_rows(oracle_lib, yf):
+    """Grouped FFN rows (fp32, bf16 or fp16 y from bf16 h) against the
+    oracle's per-row expert FFN."""
     cfg = SMALL["mixed"]
     lay = layer_on_gpu(cfg)
-    s = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, y_bf16=y_bf16)
+    y_bf16, y_fp16 = YFMT[yf]
+    s = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, y_bf16=y_bf16, y_fp16=y_fp16)
     ws = moe.alloc_workspace(s)
     A = cfg.T * cfg.k
     ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=gh.DEV)
@@ -318,20 +330,25 @@ def test_ffn_stage_rows(oracle_lib, y_bf16):
         gh.assert_close(y_np[rows], ref, f"expert {e}")
 
 
-@pytest.mark.parametrize("T,y_bf16", [(77, False), (77, True), (600, False), (600, True)])
-def test_combine_stage(T, y_bf16):
+@pytest.mark.parametrize("T", [77, 600])
+@pytest.mark.parametrize("yf", ["fp32", "bf16", "fp16"])
+def test_combine_stage(T, yf):
     """Combine against a float64 numpy weighted sum of the same rows (fp32,
-    or bf16 widened exactly), below and above the 512-token grid switch."""
+    or bf16 / fp16 widened exactly), below and above the 512-token grid
+    switch."""
     rng = np.random.default_rng(9)
     H, k, E = 320, 5, 20
     A = T * k
+    y_bf16, y_fp16 = YFMT[yf]
     y = torch.randn((A, H), device=gh.DEV)
     if y_bf16:
         y = y.to(torch.bfloat16)
+    if y_fp16:
+        y = y.to(torch.float16)
     perm = rng.permutation(A).astype(np.int32)
     perm[3] = -1  # skipped row
     w = torch.rand((T, k), device=gh.DEV)
-    s = moe.make_shape(T, H, E, k, 32, y_bf16=y_bf16)
+    s = moe.make_shape(T, H, E, k, 32, y_bf16=y_bf16, y_fp16=y_fp16)
     for acc in (0, 1):
         out = torch.randn((T, H), device=gh.DEV)
         prev = out.cpu().numpy().astype(np.float64)
