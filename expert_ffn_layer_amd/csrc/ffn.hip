@@ -151,10 +151,13 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restric
 #define MOE_LIGHT_DN_BPC 8
 #endif
 #ifndef MOE_LIGHT_NT_LOADS
-#define MOE_LIGHT_NT_LOADS 0    // 1: weights streamed with non-temporal loads
+#define MOE_LIGHT_NT_LOADS 1    // 0: weights read with the default cache policy
 #endif
 
-// Expert weights are read once per step: optionally bypass cache retention.
+// Expert weights are read once per step: with the non-temporal hint they are
+// not retained in the caches (measured on MI355X: a plain stream of 16-byte
+// loads over 4 GiB reads at 6.2 TB/s with the default policy and 7.0 TB/s
+// with the hint; decode step -8%, gate|up light loop at 6.8 TB/s).
 template <bool kNonTemporal>
 __device__ __forceinline__ bf16x8_t load_weights(const uint16_t* p) {
     if constexpr (kNonTemporal)
@@ -491,6 +494,13 @@ __global__ __launch_bounds__(kThreads) void down_light_kernel(FfnArgs a) {
 #ifndef MOE_LIGHT_MX_DN_TILES
 #define MOE_LIGHT_MX_DN_TILES 2
 #endif
+// 16 weight codes, streamed like the bf16 weights (load_weights).
+__device__ __forceinline__ u32x4_t load_codes(const uint8_t* p) {
+    if constexpr (MOE_LIGHT_NT_LOADS != 0)
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    else
+        return *reinterpret_cast<const u32x4_t*>(p);
+}
 constexpr int kLightMxWideU = 1;  // chunks in flight, 17..64-row branch
 
 // Eight E4M3 codes (words w0, w1 in K order) times 2^(sb - 127) as an MFMA
@@ -557,7 +567,7 @@ __device__ __forceinline__ void gateup_light_rows_mx(const FfnArgs& a, int e, in
         if (c < nc) {
 #pragma unroll
             for (int t = 0; t < NTILE; ++t) {
-                bb[t] = *reinterpret_cast<const u32x4_t*>(Bp + t * bstride + (size_t)c * 1024);
+                bb[t] = load_codes(Bp + t * bstride + (size_t)c * 1024);
                 ss[t] = load_u16(Sp + t * sstride + (size_t)c * 32);
             }
 #pragma unroll
@@ -692,7 +702,7 @@ __device__ __forceinline__ void down_light_rows_mx(const FfnArgs& a, int e, int 
         if (c < nc) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                bb[t] = *reinterpret_cast<const u32x4_t*>(Bp + t * bstride + (size_t)c * 1024);
+                bb[t] = load_codes(Bp + t * bstride + (size_t)c * 1024);
                 ss[t] = load_u16(Sp + t * sstride + (size_t)c * 32);
             }
             const bool second = 2 * c + 1 < nk;

@@ -101,13 +101,12 @@ Layout layout(const moe_shape* s) {
         L.light_max = moe::kLightRowsMax;
         L.max_tiles = 0;
         L.max_light = (int)std::min<long long>(E, A);
-    } else if (s->light_max_rows < 0 && moe::adaptive_light_max(A, E) == 0) {
+    } else if (s->light_max_rows < 0 && moe::adaptive_light_max(A, E) < moe::kLightRowsMax) {
         // No more than E experts are touched, so beyond MOE_LIGHT_MEAN_ROWS * E
-        // routed rows the rule always picks the heavy tiles: fix that choice
-        // (light kernels not launched at all).
-        L.light_max = 0;
-        L.max_tiles = moe::max_heavy_tiles(A, s->E, 0);
-        L.max_light = 0;
+        // routed rows the rule always picks the tail threshold: fix it.
+        L.light_max = moe::adaptive_light_max(A, E);
+        L.max_tiles = moe::max_heavy_tiles(A, s->E, L.light_max);
+        L.max_light = L.light_max > 0 ? (int)std::min<long long>(E, A) : 0;
     } else if (s->light_max_rows < 0) {
         L.light_max = moe::kLightAdaptive;
         L.max_tiles = moe::max_heavy_tiles(A, s->E, 0);

@@ -84,10 +84,11 @@ typedef struct moe_shape {
                                light loop (no heavy kernel runs); with more tokens the
                                device decides per call from the routing: experts with up
                                to 64 rows take the light loop when the routed rows
-                               average at most 8 per touched expert, otherwise every
-                               expert takes the heavy tiles (faster on MI355X from about
-                               10 rows per expert on); with T*k > 8*E always the heavy
-                               tiles.  Results do not depend on it. */
+                               average at most 8 per touched expert, otherwise only
+                               experts with up to 8 rows do and the others take the
+                               heavy tiles (faster on MI355X from about 10 rows per
+                               expert on); with T*k > 8*E always the latter.  Results
+                               do not depend on it. */
     int32_t heavy_tile_rows; /* rows per heavy tile: 0 = chosen per expert from its row
                                count (the least estimated time: one height, or 256-row
                                tiles and a smaller last tile); 128, 192 or 256 = every

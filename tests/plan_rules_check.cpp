@@ -60,7 +60,7 @@ int main() {
         moe::tile_split(n, moe::kTileMaxMx, nt, mt, lt);
         std::printf("mx %d %d %d %d\n", n, nt, moe::tile_height(mt), moe::tile_height(lt));
     }
-    std::printf("light %d %d %d\n", moe::adaptive_light_max(4000, 500), moe::adaptive_light_max(4001, 500),
-                moe::kLightRowsMax);
+    std::printf("light %d %d %d %d\n", moe::adaptive_light_max(4000, 500),
+                moe::adaptive_light_max(4001, 500), moe::kLightRowsMax, MOE_LIGHT_TAIL_ROWS);
     return 0;
 }

@@ -76,4 +76,5 @@ def test_xcd_bounds(output):
 def test_light_rule(output):
     line = [l for l in output if l.startswith("light ")][0].split()
     assert int(line[1]) == int(line[3])  # 4000 rows over 500 experts: mean 8 -> light
-    assert int(line[2]) == 0             # one row more: heavy
+    assert int(line[2]) == int(line[4])  # one row more: only the cold tail stays light
+    assert 0 <= int(line[4]) <= 16
