@@ -40,6 +40,7 @@ KERNEL_ID = {n: i for i, n in enumerate(KERNELS)}
 # light_max_rows is left at -1 (the C ABI's default).
 LIGHT_MAX_ROWS = 64
 LIGHT_MEAN_ROWS = 8  # the default's device-side rule (moe_shape.light_max_rows = -1)
+LIGHT_TAIL_ROWS = 8  # light threshold of that rule when the mean is above LIGHT_MEAN_ROWS
 
 
 def light_experts(counts, shape):
@@ -52,10 +53,10 @@ def light_experts(counts, shape):
         if shape.T <= LIGHT_MAX_ROWS:
             lm = LIGHT_MAX_ROWS
         elif shape.T * shape.k > LIGHT_MEAN_ROWS * shape.E:
-            lm = 0  # more rows than the rule can ever send to the light loop
+            lm = LIGHT_TAIL_ROWS  # the mean is above LIGHT_MEAN_ROWS whatever the routing
         else:
             touched = int((counts > 0).sum())
-            lm = LIGHT_MAX_ROWS if int(counts.sum()) <= LIGHT_MEAN_ROWS * touched else 0
+            lm = LIGHT_MAX_ROWS if int(counts.sum()) <= LIGHT_MEAN_ROWS * touched else LIGHT_TAIL_ROWS
     return (counts >= 1) & (counts <= lm)
 
 

@@ -101,22 +101,27 @@ def test_tile_heights_bitwise(oracle_lib, y_bf16):
     log(f"tiles/192/bf16y={y_bf16}", rep)
 
 
-@pytest.mark.parametrize("T,E,k,zipf,light", [
-    (300, 512, 10, 0.0, True), (400, 512, 10, 3.0, False),    # one-block permute decides
-    (500, 1024, 10, 0.0, True), (700, 1024, 10, 3.0, False),  # plan kernel decides
-    (1000, 512, 10, 0.0, False), (300, 64, 10, 0.0, False)])  # T*k > 8E: fixed on the host
-def test_default_light_rule_bitwise(oracle_lib, T, E, k, zipf, light):
+@pytest.mark.parametrize("T,E,k,zipf,lm", [
+    (300, 512, 10, 0.0, 64), (400, 512, 10, 3.0, 8),    # one-block permute decides
+    (500, 1024, 10, 0.0, 64), (700, 1024, 10, 3.0, 8),  # plan kernel decides
+    (1000, 512, 10, 0.0, 8), (300, 64, 10, 0.0, 8)])    # T*k > 8E: fixed on the host
+def test_default_light_rule_bitwise(oracle_lib, T, E, k, zipf, lm):
     """The default's per-call light/heavy choice (decided on the device, in
     the one-block permute for T*k <= 4096 and in the plan kernel above, or
-    on the host when T*k > 8E) gives the bits of both fixed choices, and
-    matches the oracle."""
+    on the host when T*k > 8E): experts with up to 64 rows take the light
+    loop when the rows average at most 8 per touched expert, else those with
+    up to 8 rows.  It gives the bits of both fixed choices and matches the
+    oracle."""
     print(f"[case] default light rule T={T} E={E} k={k} zipf={zipf}", flush=True)
     kw = dict(zipf_s=1.2, zipf_alpha=zipf) if zipf else {}
     cfg = custom(f"rule{T}_{E}", T=T, H=256, E=E, k=k, I=64, **kw)
     lay = layer_on_gpu(cfg)
     outs = {lm: gh.gpu_forward(lay, light_max_rows=lm) for lm in (-1, 0, 64)}
     s = moe.make_shape(T, 256, E, k, 64)
-    assert bool(moe.light_experts(outs[-1]["counts"], s).any()) == light
+    c = outs[-1]["counts"]
+    assert np.array_equal(moe.light_experts(c, s), (c >= 1) & (c <= lm))
+    mean = c.sum() / max(1, int((c > 0).sum()))
+    assert (mean <= moe.LIGHT_MEAN_ROWS) == (lm == moe.LIGHT_MAX_ROWS)
     for lm in (0, 64):
         assert np.array_equal(outs[-1]["out"].view(np.int32), outs[lm]["out"].view(np.int32))
     rep = gh.check_layer(oracle_lib, lay)
