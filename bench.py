@@ -66,7 +66,100 @@ def parse():
                    help="no GPU: turn the rocprofv3 output of the three profiling runs of "
                         "--config (and the kernel-trace run's stdout LOG) into the summaries "
                         "under profiles/")
+    p.add_argument("--summarize-mfma", nargs=3, metavar=("KT_DIR", "PMC_DIR", "LOG"),
+                   help="no GPU: MFMA pipe occupancy and clock of the heavy GEMMs from a "
+                        "kernel-trace run and a SQ_VALU_MFMA_BUSY_CYCLES + GRBM_GUI_ACTIVE run "
+                        "of --config -> profiles/mfma_busy__<workload>.md")
     return p.parse_args()
+
+
+# The runs that profiles/mfma_busy__<workload>.md summarises ($R as below).
+MFMA_COMMANDS = (
+    "rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/mkt_{cfg}{tag} -o bench -- "
+    "python3 $R/bench.py --config {cfg}{extra} --steps 5 --warmup 1 --no-cpu-baseline "
+    "> $R/gpurun_out/mkt_{cfg}{tag}.log",
+    "timeout -s KILL 150 rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE -f csv "
+    "-d $R/gpurun_out/mfma_{cfg}{tag} -o bench -- python3 $R/bench.py --config {cfg}{extra} "
+    "--steps 3 --warmup 1 --no-cpu-baseline",
+    "python3 $R/bench.py --config {cfg}{extra} --summarize-mfma $R/gpurun_out/mkt_{cfg}{tag} "
+    "$R/gpurun_out/mfma_{cfg}{tag} $R/gpurun_out/mkt_{cfg}{tag}.log",
+)
+N_CU, SIMD_PER_CU, N_XCD = 256, 4, 8
+
+
+def summarize_mfma(args):
+    """MFMA pipe occupancy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x
+    CUs x 4 SIMDs) per launch, averaged over a kernel's launches; the clock
+    the chip held = GRBM_GUI_ACTIVE / the kernel-trace average duration."""
+    import csv
+    import collections
+    from expert_ffn_layer_amd import synth
+
+    kt_dir, pmc_dir, log = args.summarize_mfma
+    cfg = synth.CONFIGS[args.config]
+    workload = workload_of(cfg, args.weights)
+
+    def one_csv(d, suffix):
+        names = [f for f in os.listdir(d) if f.endswith(suffix)]
+        assert len(names) == 1, (d, names)
+        with open(os.path.join(d, names[0])) as f:
+            return list(csv.DictReader(f))
+
+    dur = collections.defaultdict(list)
+    for r in one_csv(kt_dir, "kernel_stats.csv"):
+        lab = kernel_label(r["Name"])
+        if lab in ("gateup_heavy", "down_heavy", "gateup_light", "down_light", "router_gemm"):
+            dur[lab].append((float(r["TotalDurationNs"]), int(r["Calls"])))
+    # Per dispatch: the MFMA busy cycles summed over the chip, and
+    # GRBM_GUI_ACTIVE, which rocprofv3 reports as one value summed over the
+    # 8 XCDs (each XCD counts the cycles the GPU is busy): /8 gives the cycles.
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    span = {}
+    for r in one_csv(pmc_dir, "counter_collection.csv"):
+        lab = kernel_label(r["Kernel_Name"])
+        if lab in dur:
+            key = (lab, r["Dispatch_Id"])
+            per[key][r["Counter_Name"]] += float(r["Counter_Value"])
+            span[key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    rows = {}
+    for lab in dur:
+        ks = [k for k in per if k[0] == lab and per[k].get("GRBM_GUI_ACTIVE")]
+        tot_ns = sum(t for t, _ in dur[lab])
+        calls = sum(c for _, c in dur[lab])
+        avg_us = tot_ns / calls / 1e3
+        if not ks or avg_us < 50:  # empty or tiny launches: counts dominated by launch overhead
+            continue
+        cyc = [per[k]["GRBM_GUI_ACTIVE"] / N_XCD for k in ks]
+        busy = sum(per[k]["SQ_VALU_MFMA_BUSY_CYCLES"] / (c * N_CU * SIMD_PER_CU)
+                   for k, c in zip(ks, cyc)) / len(ks)
+        mhz = sum(c / span[k] for k, c in zip(ks, cyc)) / len(ks) / 1e6
+        rows[lab] = (busy, avg_us, mhz, len(ks))
+    with open(log) as f:
+        line = [l for l in f if l.startswith("{")][-1]
+    rec = json.loads(line)
+    rf = rec["roofline"]
+    tag = "" if args.weights == "bf16" else f"_{args.weights}"
+    extra = "" if args.weights == "bf16" else f" --weights {args.weights}"
+    cmds = [c.format(cfg=args.config, tag=tag, extra=extra) for c in MFMA_COMMANDS]
+    lines = [f"# MFMA pipe occupancy on {workload}", "",
+             "rocprofv3 counters of bench.py on one MI355X (gfx950).  Commands, from /tmp with",
+             "TMPDIR=/tmp, $R the repository root:", "", "```", *cmds, "```", "",
+             f"Occupancy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x {N_CU} CUs x "
+             f"{SIMD_PER_CU} SIMDs), per launch, averaged, with GRBM_GUI_ACTIVE (reported summed "
+             f"over the {N_XCD} XCDs) divided by {N_XCD}; clock = those cycles over the "
+             "launch's own start-to-end time in the counter run.  Kernels of 50 us and more.", "",
+             "| kernel | launches counted | avg us | MFMA pipes busy | clock MHz |",
+             "|---|---|---|---|---|"]
+    for lab, (busy, avg_us, mhz, n) in sorted(rows.items(), key=lambda kv: -kv[1][1]):
+        lines.append(f"| {lab} | {n} | {avg_us:.1f} | {100 * busy:.1f}% | {mhz:.0f} |")
+    lines += ["", f"bench line: {rec['value']:.1f} tokens/s, {rec['ms_per_step']:.4f} ms/step; "
+                  f"{rf['kernel']} at {rf['flops'] / (rf['kernel_us'] * 1e-6) / 1e12:.1f} TFLOP/s "
+                  f"of expert FLOPs = {100 * rf['flops'] / (rf['kernel_us'] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS:.1f}% "
+                  f"of the {BF16_PEAK_TFLOPS:.0f} TFLOP/s bf16 dense peak."]
+    path = os.path.join(PROFILES, f"mfma_busy__{workload}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {path}")
 
 
 # The profiling runs that profiles/<kernel>__<workload>.{md,traffic.json}
@@ -261,6 +354,9 @@ def main():
     args = parse()
     if args.summarize:
         summarize(args)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
