@@ -1,0 +1,51 @@
+"""Seeded random layers within the ABI's limits against the oracle.
+
+Each case draws its sizes from a fixed seed (so a failure names a
+reproducible case): T 1..400, H a multiple of 64 up to 512, E 1..96, k up to
+min(E, 12), I a multiple of 32 up to 320, an optional shared expert, optional
+Zipf routing skew, the light threshold (default rule, all heavy, 16, 64),
+the heavy tile height (chosen, 128, 192, 256) and the y storage.  Routing
+must match exactly (near-ties flagged) and the output meet the 2e-2 /
+5e-3 bar.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from expert_ffn_layer_amd import synth
+from tests import gpu_helpers as gh
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 24
+
+
+def draw_case(i):
+    r = np.random.default_rng(1000 + i)
+    E = int(r.integers(1, 97))
+    kw = dict(T=int(r.integers(1, 401)), H=64 * int(r.integers(1, 9)), E=E,
+              k=int(r.integers(1, min(E, 12) + 1)), I=32 * int(r.integers(1, 11)))
+    if r.random() < 0.25:
+        kw["I_shared"] = 32 * int(r.integers(1, 11))
+    if r.random() < 0.35:
+        kw.update(zipf_s=1.2, zipf_alpha=float(r.choice([0.6, 1.5, 3.0])))
+    if r.random() < 0.15:
+        kw["renorm"] = 0
+    lm = int(r.choice([-1, -1, 0, 16, 64]))
+    tm = int(r.choice([0, 0, 128, 192, 256]))
+    yf = str(r.choice(["fp32", "bf16", "fp16"]))
+    return kw, lm, tm, yf
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_layer(oracle_lib, i):
+    kw, lm, tm, yf = draw_case(i)
+    print(f"[case] random {i}: {kw} light_max={lm} tm={tm} y={yf}", flush=True)
+    cfg = synth.custom_config(f"rand{i}", **kw)
+    layer = synth.make_layer(cfg, seed=i, device=gh.DEV)
+    rep = gh.check_layer(oracle_lib, layer, light_max_rows=lm, heavy_tile_rows=tm,
+                         y_bf16=yf == "bf16", y_fp16=yf == "fp16")
+    ma, rel = rep["err"]
+    print(f"[parity] random {i}: near_ties={rep['near_ties']} max_abs={ma:.3e} relL2={rel:.3e}",
+          flush=True)
