@@ -49,3 +49,36 @@ def test_random_layer(oracle_lib, i):
     ma, rel = rep["err"]
     print(f"[parity] random {i}: near_ties={rep['near_ties']} max_abs={ma:.3e} relL2={rel:.3e}",
           flush=True)
+
+
+N_MX_CASES = 8
+
+
+@pytest.mark.parametrize("i", range(N_MX_CASES))
+def test_random_layer_mxfp8(oracle_lib, i):
+    """MXFP8 expert weights on random layers: the layer equals, bit for bit,
+    the bf16 layer on the oracle's dequantisation of the same weights, and
+    that layer meets the bar against the oracle."""
+    import torch
+
+    from expert_ffn_layer_amd import moe
+    from tests.test_gpu_mxfp8 import dequant_layer
+
+    kw, lm, tm, yf = draw_case(500 + i)
+    tm = 0 if tm == 256 else tm  # MXFP8 tiles are at most 192 rows high
+    print(f"[case] random mxfp8 {i}: {kw} light_max={lm} tm={tm} y={yf}", flush=True)
+    cfg = synth.custom_config(f"randmx{i}", **kw)
+    layer = synth.make_layer(cfg, seed=500 + i, device=gh.DEV)
+    ref = dequant_layer(oracle_lib, layer)
+    yb, yh = yf == "bf16", yf == "fp16"
+    out_mx = moe.MoELayer(layer, lm, tm, y_bf16=yb, y_fp16=yh, weights="mxfp8")()
+    out_16 = moe.MoELayer(ref, lm, tm, y_bf16=yb, y_fp16=yh)()
+    torch.cuda.synchronize()
+    assert torch.equal(out_mx[1], out_16[1])
+    assert torch.equal(out_mx[0].view(torch.int32), out_16[0].view(torch.int32)), \
+        "MXFP8 layer differs from the bf16 layer on dequantised weights"
+    rep = gh.check_layer(oracle_lib, ref, light_max_rows=lm, heavy_tile_rows=tm, y_bf16=yb,
+                         y_fp16=yh)
+    ma, rel = rep["err"]
+    print(f"[parity] random mxfp8 {i}: near_ties={rep['near_ties']} max_abs={ma:.3e} "
+          f"relL2={rel:.3e}", flush=True)
