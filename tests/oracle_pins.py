@@ -168,6 +168,33 @@ def pin_renorm_off(o):
     assert np.array_equal(r["w"], np.take_along_axis(r["probs"], r["ids"].astype(np.int64), 1))
 
 
+def pin_weights_for_ids(o):
+    """Routing weights of ids that are not the oracle's own top-k (the k-th
+    and (k+1)-th ranks swapped, the order reversed, random distinct ids):
+    the float64 softmax probabilities of exactly those ids, renormalised over
+    them (renorm 1) or raw (renorm 0)."""
+    rng = np.random.default_rng(24)
+    for T, E, k in [(30, 64, 10), (12, 512, 10), (10, 16, 4), (6, 9, 8)]:
+        l = (rng.standard_normal((T, E)) * 2.0).astype(np.float32)
+        p64 = softmax64(l)
+        top = topk_by_sort(p64, k + 1)
+        swapped = top[:, :k].copy()
+        swapped[:, k - 1] = top[:, k]
+        variants = {
+            "swapped": swapped,
+            "reversed": top[:, :k][:, ::-1],
+            "random": np.stack([rng.permutation(E)[:k] for _ in range(T)]),
+        }
+        for name, ids in variants.items():
+            ids = np.ascontiguousarray(ids, dtype=np.int32)
+            psel = np.take_along_axis(p64, ids.astype(np.int64), axis=1)
+            w1 = o.weights_for_ids(l, ids, 1)
+            want1 = psel / psel.sum(axis=1, keepdims=True)
+            assert np.abs(w1 - want1).max() < 2e-6, f"renormalised weights of {name} ids"
+            w0 = o.weights_for_ids(l, ids, 0)
+            assert rel_max(w0, psel) < 1e-6, f"raw probabilities of {name} ids"
+
+
 def pin_permute(o):
     """Counts sum to T*k, every token appears exactly k times, each expert's
     segment lists its tokens in increasing order, inv_pos is a bijection that
@@ -436,7 +463,7 @@ def pin_mxfp8_golden_block(o):
 
 
 ALL_PINS = [pin_logits_vs_library, pin_topk_full_sort, pin_tie_rule, pin_bias_only,
-            pin_nonfinite, pin_large_logits, pin_renorm_off, pin_permute,
+            pin_nonfinite, pin_large_logits, pin_renorm_off, pin_weights_for_ids, pin_permute,
             pin_k1_single_expert, pin_identical_experts, pin_zero_weights,
             pin_identity_weights, pin_dense_bruteforce, pin_shared_expert,
             pin_exact_scaling, pin_token_permutation, pin_ffn_closed_form,

@@ -57,6 +57,11 @@ MUTANTS = {
     "mx_dequant_scale_off": ("(int)scales[r * nb + i / 32] - 127", "(int)scales[r * nb + i / 32] - 126"),
     "mx_subnormal_decode": ("mag = ldexp((double)m, -9);", "mag = ldexp(8.0 + m, -10);"),
     "mx_zero_block_scale": ("int s = -127;\n            if (amax > 0.0)", "int s = 0;\n            if (amax > 0.0)"),
+    "wfi_sum_short": ("if (e < 0 || e >= E) { bad = 1; break; }\n                s = s + z[e] / S;",
+                      "if (e < 0 || e >= E) { bad = 1; break; }\n                if (j + 1 < k) s = s + z[e] / S;"),
+    "wfi_renorm_dropped": ("w[(size_t)t * k + j] = renorm ? p / s : p;",
+                           "w[(size_t)t * k + j] = p;"),
+    "wfi_first_id_only": ("const float p = z[e] / S;", "const float p = z[ids[(size_t)t * k]] / S;"),
     "permute_unstable": ("for (int t = 0; t < T; ++t) {\n        for (int j = 0; j < k; ++j) {\n            const long a",
                          "for (int t = T - 1; t >= 0; --t) {\n        for (int j = 0; j < k; ++j) {\n            const long a"),
 }
