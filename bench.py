@@ -4,10 +4,14 @@
 One step = one moe_forward call (router GEMM, softmax/top-k, permute,
 grouped gate|up+SwiGLU and down FFN, combine) over one batch of seeded
 synthetic input already resident in HBM.  W untimed warm-up steps, then
-exactly K timed steps bracketed by torch.cuda.synchronize().  Prints one JSON
-line.  The routed expert weights are re-laid out once for the heavy tiles
-(moe_pack_weights) before anything is timed, as a serving engine does at load
-time; --no-packed keeps the plain layout.
+exactly K timed steps bracketed by torch.cuda.synchronize(); before each
+step an untimed 1 GiB fill evicts the L2 caches and the 256 MiB MALL, and a
+HIP event pair on the launch stream times the step itself.  `value` is the
+token count over the median step time; the minimum and mean are reported
+beside it.  Prints one JSON line.  The routed expert weights are re-laid out
+once (moe_pack_weights) before anything is timed, as a serving engine does at
+load time, and the plain layout is then freed: only the packed copy stays
+resident.  --no-packed keeps the plain layout instead.
 
 Default workload: one decode step of a Qwen-3.5-like layer (T=64 tokens,
 H=4096, E=512 experts, top-10, I=1024, bf16 experts, fp32 router).
@@ -35,6 +39,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FLUSH_BYTES = 1 << 30          # untimed fill before each timed step (> L2 + 256 MiB MALL)
+NEAR_TIE = 1e-6                # k-th vs (k+1)-th probability gap flagged as a near-tie
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3
 PROFILES = os.path.join(ROOT, "profiles")
@@ -383,7 +389,14 @@ def main():
     m = moe.MoELayer(layer, packed=not args.no_packed, y_bf16=y_dt == "bf16",
                      weights=args.weights, y_fp16=y_dt == "fp16")
     s = m.shape
-    w_gu_arg, w_dn_arg = (None, None) if mx else (layer.w_gu, layer.w_dn)
+    # The oracle's inputs for the CPU baseline (its sample's tokens and the
+    # experts they reach) are copied to the host before the plain weights
+    # are freed; then only the packed copy of the expert weights is resident.
+    cpu_in = None if args.no_cpu_baseline else cpu_baseline_inputs(layer, cfg, args.cpu_sample)
+    if m.packed is not None:
+        layer.w_gu = layer.w_dn = None
+        torch.cuda.empty_cache()
+    w_gu_arg, w_dn_arg = layer.w_gu, layer.w_dn
     out = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=dev)
     ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
     w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
@@ -425,26 +438,37 @@ def main():
         per_kernel[name] = sum(v for (k, _), v in per_launch.items() if k == name)
     dominant, dom_launch = max(per_launch, key=per_launch.get)
 
-    # Timed region: K steps; the dominant kernel bracketed by events each step.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # Timed region: K steps, each after an untimed 1 GiB fill that evicts the
+    # caches, timed by its own event pair on the launch stream; the dominant
+    # kernel's launch is bracketed by events each step too.
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    evs = [mk() for _ in range(args.steps)]
+    step_evs = [mk() for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps (dominant kernel {dominant})", file=sys.stderr,
           flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for a, b in evs:
+    for i, ((a, b), (sa, sb)) in enumerate(zip(evs, step_evs)):
+        flush.fill_(float(i))
+        sa.record(stream)
         moe.profile_kernel(dominant, a, b, launch=dom_launch)
         step()
+        sb.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     moe.profile_kernel(None)
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    del flush
+    step_ms = sorted(sa.elapsed_time(sb) for sa, sb in step_evs)
+    ms_per_step = float(np.median(step_ms))
+    wall_ms_per_step = (t1 - t0) * 1e3 / args.steps
     kern_us = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3
     value = cfg.T / (ms_per_step / 1e3)
 
     # Algorithmic work, from this run's own routing.
     cnt = counts.cpu().numpy().astype(np.int64)
     touched = int((cnt > 0).sum())
+    routing = routing_stats(s, layer, cnt, cfg, m.workspace)
     light = moe.light_experts(cnt, s)
     light_rows = int(cnt[light].sum())
     light_experts = int(light.sum())
@@ -532,8 +556,8 @@ def main():
         del src, dst
 
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(layer_obj=m.layer, cfg=cfg, n=args.cpu_sample, gpu_out=out, mx=mx)
+    if cpu_in is not None:
+        cpu = cpu_baseline(cpu_in, cfg=cfg, gpu_out=out, mx=mx)
 
     rec = {
         "metric": "MoE-layer tokens/s",
@@ -543,10 +567,17 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "step_ms": {"median": round(ms_per_step, 4), "min": round(step_ms[0], 4),
+                    "mean": round(float(np.mean(step_ms)), 4),
+                    "wall_incl_flush": round(wall_ms_per_step, 4),
+                    "timing": "HIP events around each moe_forward, after an untimed "
+                              f"{FLUSH_BYTES >> 20} MiB fill that evicts L2 and MALL"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        # the MFMAs multiply bf16 operands (MXFP8 codes are converted to bf16
+        # operands exactly, before the MFMA)
+        "dtype": "mxfp8-weights/bf16" if mx else "bf16",
         "data": "synthetic (seeded normal draws, random-init weights)",
         "config": {"workload": workload, "tokens": cfg.T, "hidden": H, "experts": cfg.E,
                    "top_k": cfg.k, "intermediate": I, "shared_intermediate": cfg.I_shared,
@@ -555,6 +586,7 @@ def main():
                    "weights": "mxfp8 (E4M3, E8M0 per 32)" if mx else "bf16"},
         "roofline": roof,
         "layer_roofline": layer,
+        "routing": routing,
         "kernels_us": {k: round(v, 2) for k, v in per_kernel.items()},
         "kernel_source_hash": src_hash,
         "cpu_baseline": cpu,
@@ -562,7 +594,76 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline(layer_obj, cfg, n, gpu_out, mx=False):
+def routing_stats(shape, layer_obj, cnt, cfg, ws):
+    """The routing this step saw: rows per expert (max, min, experts with at
+    most 3 rows, the top 10% of experts' share of all rows) and near-ties
+    (tokens whose k-th and (k+1)-th softmax probabilities, as the GPU router
+    computes them, are within 1e-6; and tokens with two adjacent ranks among
+    the first k+1 that close).  One untimed moe_router call with probs."""
+    import numpy as np
+    import torch
+
+    from expert_ffn_layer_amd import moe
+
+    A = cfg.T * cfg.k
+    srt = np.sort(cnt)[::-1]
+    top = max(1, cfg.E // 10)
+    st = {"max_rows": int(cnt.max()), "min_rows": int(cnt.min()),
+          "experts_le3_rows": int((cnt <= 3).sum()), "touched_experts": int((cnt > 0).sum()),
+          "top10pct_share": round(float(srt[:top].sum()) / A, 4)}
+    dev = layer_obj.x.device
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
+    w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
+    probs = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev)
+    moe.router(shape, layer_obj.x, layer_obj.wg, layer_obj.bias, ids, w, probs, ws)
+    kk = min(cfg.k + 1, cfg.E)
+    p = torch.topk(probs, kk, dim=1).values.cpu().numpy().astype(np.float64)
+    gaps = p[:, :-1] - p[:, 1:]
+    set_doubt = (gaps[:, cfg.k - 1] < NEAR_TIE) if kk > cfg.k else np.zeros(cfg.T, bool)
+    order_doubt = (gaps < NEAR_TIE).any(axis=1) & ~set_doubt
+    st["near_ties"] = {"kth_vs_next": int(set_doubt.sum()), "order_within_topk": int(order_doubt.sum()),
+                       "threshold": NEAR_TIE, "from": "GPU router probabilities"}
+    del probs
+    return st
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline_inputs(layer_obj, cfg, n):
+    """Host copies of what the oracle reads for the first n tokens: their
+    activations, the router, the shared expert, and the routed experts the
+    oracle's own routing of those tokens reaches (untimed)."""
+    import numpy as np
+
+    import oracle
+
+    n = min(n, cfg.T)
+    o = oracle.Oracle()
+    x = layer_obj.x[:n].cpu()
+    wg = layer_obj.wg.cpu()
+    bias = None if layer_obj.bias is None else layer_obj.bias.cpu()
+    r = o.route(o.logits(x, wg, bias), cfg.k, cfg.renorm)
+    experts = [int(e) for e in np.unique(r["ids"])]
+    print(f"[bench] cpu baseline: copying {len(experts)} experts to host", file=sys.stderr,
+          flush=True)
+    return dict(n=n, x=x, wg=wg, bias=bias,
+                w_gu={e: layer_obj.w_gu[e].cpu() for e in experts},
+                w_dn={e: layer_obj.w_dn[e].cpu() for e in experts},
+                ws_gu=None if layer_obj.ws_gu is None else layer_obj.ws_gu.cpu(),
+                ws_dn=None if layer_obj.ws_dn is None else layer_obj.ws_dn.cpu())
+
+
+def cpu_baseline(inp, cfg, gpu_out, mx=False):
     """The oracle (plain fp32 C loops, OpenMP over rows) on the first n tokens
     of the same layer, weights already on the host; also reports its
     agreement with the GPU output on those tokens.  With MXFP8 weights the
@@ -573,33 +674,26 @@ def cpu_baseline(layer_obj, cfg, n, gpu_out, mx=False):
 
     import oracle
 
-    n = min(n, cfg.T)
+    n = inp["n"]
     o = oracle.Oracle()
-    x = layer_obj.x[:n].cpu()
-    wg = layer_obj.wg.cpu()
-    bias = None if layer_obj.bias is None else layer_obj.bias.cpu()
-    print(f"[bench] cpu baseline: copying weights to host", file=sys.stderr, flush=True)
-    w_gu = layer_obj.w_gu.cpu()
-    w_dn = layer_obj.w_dn.cpu()
-    ws_gu = None if layer_obj.ws_gu is None else layer_obj.ws_gu.cpu()
-    ws_dn = None if layer_obj.ws_dn is None else layer_obj.ws_dn.cpu()
+    w_gu, w_dn = inp["w_gu"], inp["w_dn"]
     if mx:
-        r = o.route(o.logits(x, wg, bias), cfg.k, cfg.renorm)
         deq_gu, deq_dn = {}, {}
-        for e in np.unique(r["ids"]):
+        for e in w_gu:
             for src, dst in ((w_gu, deq_gu), (w_dn, deq_dn)):
-                c, sc = o.mxfp8_quantize(src[int(e)].float().numpy())
-                dst[int(e)] = o.mxfp8_dequantize(c, sc)
+                c, sc = o.mxfp8_quantize(src[e].float().numpy())
+                dst[e] = o.mxfp8_dequantize(c, sc)
         w_gu, w_dn = deq_gu, deq_dn
     print(f"[bench] cpu baseline: oracle on {n} tokens", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
-    ref = o.forward(x, wg, bias, w_gu, w_dn, cfg.k, cfg.renorm, ws_gu, ws_dn, permute=False)
+    ref = o.forward(inp["x"], inp["wg"], inp["bias"], w_gu, w_dn, cfg.k, cfg.renorm,
+                    inp["ws_gu"], inp["ws_dn"], permute=False)
     wall = time.perf_counter() - t0
     g = gpu_out[:n].cpu().numpy().astype(np.float64)
     d = g - ref["out"].astype(np.float64)
-    del w_gu, w_dn
     torch.cuda.synchronize()
     return {"value": round(n / wall, 3), "unit": "tokens/s", "cores": o.max_threads(),
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "kind": "oracle",
             "sample": f"first {n} of {cfg.T} tokens of the same layer (routing, all their expert "
                       f"FFN rows, combine); fp32 C loops; expert weights pre-copied to host"

@@ -20,6 +20,12 @@ ARCH = "gfx950"
 
 SOURCES = ["router.hip", "permute.hip", "ffn.hip", "combine.hip", "mxfp8.hip", "moe_api.cpp"]
 
+# A second build of the same sources with the heavy kernels' grid capped at 16
+# blocks, so each block runs many work items in a row: the tests compare its
+# bits with the default build's to cover the cross-tile paths on small shapes.
+GRID16_LIB = os.path.join(PKG, "libmoe_grid16.so")
+GRID16_FLAGS = ["-DMOE_HEAVY_MAX_GRID=16"]
+
 # -packed-fp32-ops off: packed fp32 VALU forms are not emitted.
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC,
@@ -54,5 +60,12 @@ def build(verbose: bool = False, out: str = LIB, objdir: str = OBJDIR, extra=())
     return out
 
 
+def build_all(verbose: bool = False) -> None:
+    """The library and its grid-capped test variant."""
+    build(verbose=verbose)
+    build(verbose=verbose, out=GRID16_LIB, objdir=os.path.join(OBJDIR, "grid16"),
+          extra=GRID16_FLAGS)
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    build_all(verbose=True)

@@ -1565,6 +1565,18 @@ __global__ __launch_bounds__(256) void pack_heavy_rec_kernel(const uint16_t* __r
     }
 }
 
+// Upper bound on the heavy kernels' grid (0: none).  A small cap makes every
+// block run many work items in a row, which is how the cross-tile paths
+// (same-height chaining, the down GEMM's prefetch of the next tile) are put
+// under test on small shapes; the default build leaves it off.
+#ifndef MOE_HEAVY_MAX_GRID
+#define MOE_HEAVY_MAX_GRID 0
+#endif
+int heavy_grid(long long work, int num_cu) {
+    const int g = grid_for(work, 1, num_cu);
+    return MOE_HEAVY_MAX_GRID > 0 ? std::min(g, MOE_HEAVY_MAX_GRID) : g;
+}
+
 // Heavy tiles of one GEMM: one launch, one block per CU (the tile heights are
 // the plan's, read on the device); a dense group has one height.
 template <Mode M, int YF>
@@ -1572,7 +1584,7 @@ hipError_t launch_heavy(const FfnArgs& a, int ncols, hipStream_t st) {
     const long long nblk = (ncols + kTN - 1) / kTN;
     if (a.plan) {
         if (a.max_tiles <= 0) return hipSuccess;
-        const int grid = grid_for((long long)a.max_tiles * nblk, 1, a.num_cu);
+        const int grid = heavy_grid((long long)a.max_tiles * nblk, a.num_cu);
         if (a.w_mxfp8)
             ffn_heavy_kernel<M, YF, kBRecMx><<<grid, kHeavyThreads, 0, st>>>(a);
         else if (a.hr_gu)
@@ -1583,7 +1595,7 @@ hipError_t launch_heavy(const FfnArgs& a, int ncols, hipStream_t st) {
     }
     if (a.dense_rows <= 0) return hipSuccess;
     const long long tiles = (a.dense_rows + a.dense_tm - 1) / a.dense_tm;
-    const int grid = grid_for(tiles * nblk, 1, a.num_cu);
+    const int grid = heavy_grid(tiles * nblk, a.num_cu);
     if (a.dense_tm != kTileTM0 && a.dense_tm != kTileTM1 && a.dense_tm != kTileTM2)
         return hipErrorInvalidValue;
     ffn_heavy_kernel<M, YF, kBRowMajor><<<grid, kHeavyThreads, 0, st>>>(a);  // dense groups

@@ -29,12 +29,17 @@ int fail(int code, const std::string& msg) {
     return code;
 }
 
+
 constexpr size_t kAlign = 256;
 
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    int splits = 1, nchunks = 1, light_max = 0, max_tiles = 0, max_light = 0;
+    // max_tiles: heavy-grid bound when every token's ids are distinct (the
+    // router's output); plan_tiles: tile capacity of the plan region, which
+    // also holds the tiles of ids that repeat within a token (moe_permute
+    // accepts them, so an expert can then get more than T rows).
+    int splits = 1, nchunks = 1, light_max = 0, max_tiles = 0, max_light = 0, plan_tiles = 0;
     size_t part = 0, ids = 0, w = 0, chunk = 0, counts = 0, offsets = 0, sorted = 0, inv = 0,
            plan = 0, h = 0, y = 0, hs = 0, total = 0;
 };
@@ -116,6 +121,7 @@ Layout layout(const moe_shape* s) {
         L.max_tiles = (T <= L.light_max) ? 0 : moe::max_heavy_tiles(A, s->E, L.light_max);
         L.max_light = L.light_max > 0 ? (int)std::min<long long>(E, A) : 0;
     }
+    L.plan_tiles = moe::max_heavy_tiles(A, s->E, L.light_max > 0 ? L.light_max : 0);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
@@ -130,7 +136,7 @@ Layout layout(const moe_shape* s) {
     L.offsets = take((size_t)(E + 1) * 4);
     L.sorted = take((size_t)A * 4);
     L.inv = take((size_t)A * 4);
-    L.plan = take((size_t)(moe::kPlanHeader + E + 2LL * L.max_tiles) * 4);
+    L.plan = take((size_t)(moe::kPlanHeader + E + 2LL * L.plan_tiles) * 4);
     L.h = take((size_t)A * I * 2);
     L.y = take((size_t)A * H * (y_format(s) ? 2 : 4));
     L.hs = take((size_t)T * 2 * s->I_shared * 2);  // [hi | lo] rows
@@ -220,10 +226,13 @@ int run_permute(const moe_shape* s, const Layout& L, const int32_t* ids, int32_t
     return MOE_OK;
 }
 
+// distinct_ids: the rows come from the router (each token's k ids distinct,
+// so no expert has more than T rows); otherwise (moe_grouped_ffn on any
+// moe_permute output) the heavy grid covers every tile the plan can hold.
 int run_ffn(const moe_shape* s, const Layout& L, const uint16_t* x, const int32_t* sorted,
             const int32_t* offsets, const uint16_t* wgu, const uint16_t* wdn,
             const void* packed, uint16_t* h, void* y, void* ws, hipStream_t st,
-            bool plan_ready = false) {
+            bool plan_ready, bool distinct_ids) {
     int ncu = 0;
     if (int rc = device_cu_count(&ncu)) return rc;
     int32_t* plan = at<int32_t>(ws, L.plan);
@@ -246,7 +255,7 @@ int run_ffn(const moe_shape* s, const Layout& L, const uint16_t* x, const int32_
     a.dense_rows = 0;
     a.dense_tm = 0;
     a.split_h = 0;
-    a.max_tiles = L.max_tiles;
+    a.max_tiles = distinct_ids ? L.max_tiles : L.plan_tiles;
     a.max_light = L.max_light;
     a.num_cu = ncu;
     a.y_fmt = y_format(s);
@@ -452,11 +461,14 @@ int moe_grouped_ffn(const moe_shape* shape, const uint16_t* x, const int32_t* so
     REQUIRE_PTR(x);
     REQUIRE_PTR(sorted_token_ids);
     REQUIRE_PTR(offsets);
-    if (shape->w_mxfp8) {
-        if (!packed_weights) return fail(MOE_ERR_NULL, "w_mxfp8 = 1 needs packed_weights");
-    } else {
+    if (shape->w_mxfp8 && !packed_weights)
+        return fail(MOE_ERR_NULL, "w_mxfp8 = 1 needs packed_weights");
+    if (!packed_weights) {
         REQUIRE_PTR(w_gate_up);
         REQUIRE_PTR(w_down);
+    } else {
+        OPTIONAL_PTR(w_gate_up);
+        OPTIONAL_PTR(w_down);
     }
     REQUIRE_PTR(y);
     OPTIONAL_PTR(h);
@@ -464,7 +476,7 @@ int moe_grouped_ffn(const moe_shape* shape, const uint16_t* x, const int32_t* so
         return fail(MOE_ERR_ALIGN, "packed_weights must be 256-byte aligned");
     if (int rc = check_ws(shape, workspace, ws_bytes)) return rc;
     return run_ffn(shape, layout(shape), x, sorted_token_ids, offsets, w_gate_up, w_down,
-                   packed_weights, h, y, workspace, (hipStream_t)stream);
+                   packed_weights, h, y, workspace, (hipStream_t)stream, false, false);
 }
 
 int moe_shared_ffn(const moe_shape* shape, const uint16_t* x, const uint16_t* ws_gate_up,
@@ -518,11 +530,14 @@ int moe_forward(const moe_shape* shape, const uint16_t* x, const float* w_router
     }
     REQUIRE_PTR(x);
     REQUIRE_PTR(w_router);
-    if (shape->w_mxfp8) {
-        if (!packed_weights) return fail(MOE_ERR_NULL, "w_mxfp8 = 1 needs packed_weights");
-    } else {
+    if (shape->w_mxfp8 && !packed_weights)
+        return fail(MOE_ERR_NULL, "w_mxfp8 = 1 needs packed_weights");
+    if (!packed_weights) {
         REQUIRE_PTR(w_gate_up);
         REQUIRE_PTR(w_down);
+    } else {
+        OPTIONAL_PTR(w_gate_up);
+        OPTIONAL_PTR(w_down);
     }
     REQUIRE_PTR(out);
     OPTIONAL_PTR(bias);
@@ -549,7 +564,7 @@ int moe_forward(const moe_shape* shape, const uint16_t* x, const float* w_router
     if (int rc = run_permute(shape, L, ids, counts, offsets, sorted, inv, workspace, st, &plan_ready))
         return rc;
     if (int rc = run_ffn(shape, L, x, sorted, offsets, w_gate_up, w_down, packed_weights, nullptr,
-                         y, workspace, st, plan_ready))
+                         y, workspace, st, plan_ready, true))
         return rc;
     if (shape->I_shared > 0)
         if (int rc = run_shared(shape, L, x, ws_gate_up, ws_down, out, workspace, st)) return rc;

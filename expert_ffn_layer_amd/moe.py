@@ -10,13 +10,17 @@ raises if ``libmoe.so`` has not been built.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+# MOE_LIB_PATH names another build of the same C ABI (e.g. a sanitizer build
+# of the host code for the host-side tests).
+LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK = 0
 MOE_ERR_NULL = 1
@@ -77,17 +81,32 @@ class MoeError(RuntimeError):
         self.status = status
 
 
-_lib = None
+_libs = {}
+_active_path = LIB_PATH
 _vp = ctypes.c_void_p
 _sp = ctypes.POINTER(MoeShape)
 
 
+@contextlib.contextmanager
+def using_library(path: str):
+    """Route every call in the block to another build of the same C ABI
+    (e.g. a build with other compile-time tunables), then back."""
+    global _active_path
+    prev = _active_path
+    _active_path = path
+    try:
+        yield lib()
+    finally:
+        _active_path = prev
+
+
 def lib() -> ctypes.CDLL:
-    global _lib
-    if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m expert_ffn_layer_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
+    path = _active_path
+    L = _libs.get(path)
+    if L is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built: run `python -m expert_ffn_layer_amd.build`")
+        L = ctypes.CDLL(path)
         L.moe_workspace_bytes.argtypes = [_sp]
         L.moe_workspace_bytes.restype = ctypes.c_size_t
         L.moe_packed_weight_bytes.argtypes = [_sp]
@@ -110,11 +129,11 @@ def lib() -> ctypes.CDLL:
         L.moe_profile_launches.argtypes = []
         L.moe_profile_launches.restype = ctypes.c_longlong
         for name in ("moe_router", "moe_permute", "moe_pack_weights", "moe_grouped_ffn",
-                     "moe_shared_ffn", "moe_combine", "moe_forward", "moe_profile_kernel",
-                     "moe_profile_kernel_launch"):
+                     "moe_shared_ffn", "moe_combine", "moe_forward",
+                     "moe_profile_kernel", "moe_profile_kernel_launch"):
             getattr(L, name).restype = ctypes.c_int
-        _lib = L
-    return _lib
+        _libs[path] = L
+    return L
 
 
 def status_string(status: int) -> str:
@@ -268,8 +287,8 @@ def grouped_ffn(shape, x, sorted_token_ids, offsets, w_gate_up, w_down, h, y, wo
     T, H, E, I, A = shape.T, shape.H, shape.E, shape.I, shape.T * shape.k
     args = [_ptr(x, "x", BF16, T * H), _ptr(sorted_token_ids, "sorted_token_ids", I32, A),
             _ptr(offsets, "offsets", I32, E + 1),
-            _ptr(w_gate_up, "w_gate_up", BF16, E * 2 * I * H, optional=bool(shape.w_mxfp8)),
-            _ptr(w_down, "w_down", BF16, E * H * I, optional=bool(shape.w_mxfp8)),
+            _ptr(w_gate_up, "w_gate_up", BF16, E * 2 * I * H, optional=packed_weights is not None),
+            _ptr(w_down, "w_down", BF16, E * H * I, optional=packed_weights is not None),
             _packed(packed_weights, shape),
             _ptr(h, "h", BF16, A * I, optional=True),
             _ptr(y, "y", y_dtype(shape), A * H)]
@@ -300,11 +319,19 @@ def combine(shape, y, inv_pos, topk_w, accumulate, out, stream=None):
 
 def forward(shape, x, w_router, bias, w_gate_up, w_down, ws_gate_up, ws_down, out, workspace,
             topk_ids_out=None, topk_w_out=None, counts_out=None, stream=None, packed_weights=None):
+    args = _forward_args(shape, x, w_router, bias, w_gate_up, w_down, ws_gate_up, ws_down, out,
+                         topk_ids_out, topk_w_out, counts_out, packed_weights)
+    wp, wn = _ws(workspace, shape)
+    _check(lib().moe_forward(ctypes.byref(shape), *args, wp, wn, _stream(stream)))
+
+
+def _forward_args(shape, x, w_router, bias, w_gate_up, w_down, ws_gate_up, ws_down, out,
+                  topk_ids_out, topk_w_out, counts_out, packed_weights):
     T, H, E, k, I, Is = shape.T, shape.H, shape.E, shape.k, shape.I, shape.I_shared
-    args = [_ptr(x, "x", BF16, T * H), _ptr(w_router, "w_router", F32, H * E),
+    return [_ptr(x, "x", BF16, T * H), _ptr(w_router, "w_router", F32, H * E),
             _ptr(bias, "bias", F32, E, optional=True),
-            _ptr(w_gate_up, "w_gate_up", BF16, E * 2 * I * H, optional=bool(shape.w_mxfp8)),
-            _ptr(w_down, "w_down", BF16, E * H * I, optional=bool(shape.w_mxfp8)),
+            _ptr(w_gate_up, "w_gate_up", BF16, E * 2 * I * H, optional=packed_weights is not None),
+            _ptr(w_down, "w_down", BF16, E * H * I, optional=packed_weights is not None),
             _packed(packed_weights, shape),
             _ptr(ws_gate_up, "ws_gate_up", BF16, 2 * Is * H, optional=True),
             _ptr(ws_down, "ws_down", BF16, H * Is, optional=True),
@@ -312,8 +339,6 @@ def forward(shape, x, w_router, bias, w_gate_up, w_down, ws_gate_up, ws_down, ou
             _ptr(topk_ids_out, "topk_ids_out", I32, T * k, optional=True),
             _ptr(topk_w_out, "topk_w_out", F32, T * k, optional=True),
             _ptr(counts_out, "counts_out", I32, E, optional=True)]
-    wp, wn = _ws(workspace, shape)
-    _check(lib().moe_forward(ctypes.byref(shape), *args, wp, wn, _stream(stream)))
 
 
 def profile_kernel(name: Optional[str], start=None, stop=None, launch: int = -1) -> None:
@@ -367,6 +392,7 @@ class MoELayer:
         ids = torch.empty((s.T, s.k), dtype=I32, device=dev) if want_routing else None
         w = torch.empty((s.T, s.k), dtype=F32, device=dev) if want_routing else None
         counts = torch.empty((s.E,), dtype=I32, device=dev) if want_routing else None
-        forward(s, x, L.wg, L.bias, None if s.w_mxfp8 else L.w_gu, None if s.w_mxfp8 else L.w_dn,
+        plain = self.packed is None
+        forward(s, x, L.wg, L.bias, L.w_gu if plain else None, L.w_dn if plain else None,
                 L.ws_gu, L.ws_dn, out, self.workspace, ids, w, counts, packed_weights=self.packed)
         return out, ids, w, counts

@@ -78,8 +78,9 @@ typedef struct moe_shape {
     int32_t renorm;         /* 1: selected weights renormalised to sum to 1; 0: raw probabilities */
     int32_t light_max_rows; /* experts with 1..light_max_rows rows take the light-row loop,
                                the others the heavy tiles; 0 = every expert takes the heavy
-                               tiles; at most 64.  An expert never gets more than T rows,
-                               so with T <= light_max_rows no heavy kernel runs.
+                               tiles; at most 64.  When each token's ids are distinct
+                               (always so in moe_forward) an expert gets at most T
+                               rows, so with T <= light_max_rows no heavy kernel runs.
                                -1 = library default: with T <= 64 every expert takes the
                                light loop (no heavy kernel runs); with more tokens the
                                device decides per call from the routing: experts with up
@@ -230,17 +231,19 @@ int moe_pack_weights_mxfp8(const moe_shape* shape, const uint8_t* codes_gate_up,
  *   y[r,:] = h[r,:] . W_down[e]   (fp32 sum)      for rows r of expert e,
  * bf16 MFMA with fp32 accumulation; token rows are gathered inside the GEMM.
  * Experts with 1..light_max_rows rows run the light-row loop, the others
- * the heavy tiles; both give bitwise identical rows.
+ * the heavy tiles; both give bitwise identical rows.  Any moe_permute output
+ * is accepted, including ids repeated within a token (an expert may then
+ * hold more than T rows).
  *   x                bf16 [T,H]
  *   sorted_token_ids int32 [T*k], offsets int32 [E+1]  (from moe_permute)
  *   w_gate_up        bf16 [E,2I,H]: rows 0..I-1 = W_gate^T, I..2I-1 = W_up^T
  *   w_down           bf16 [E,H,I]:  W_down^T
  *   packed_weights   the same weights from moe_pack_weights, or NULL; when
  *                    given, the light loop and the heavy tiles read it
- *                    instead of w_gate_up / w_down.  With
- *                    shape->w_mxfp8 = 1 it is required (from
- *                    moe_pack_weights_mxfp8) and w_gate_up / w_down are not
- *                    read (may be NULL)
+ *                    instead of w_gate_up / w_down, which are then not read
+ *                    and may be NULL (a caller may keep only the packed
+ *                    copy resident).  With shape->w_mxfp8 = 1 it is
+ *                    required (from moe_pack_weights_mxfp8)
  *   h                bf16 [T*k,I] out, or NULL (then kept in the workspace)
  *   y                [T*k,H] out: fp32 (shape->y_bf16 == y_fp16 == 0; large |y|
  *                    entering the weighted sum keep 24 significant bits), bf16
@@ -278,8 +281,8 @@ int moe_combine(const moe_shape* shape, const void* y, const int32_t* inv_pos,
  * shape->I_shared > 0), combine.  out fp32 [T,H]:
  *   out[t] = sum_j w[t,j] FFN_{ids[t,j]}(x[t])  (+ FFN_shared(x[t]))
  * ws_gate_up / ws_down are required iff I_shared > 0; packed_weights is
- * optional, as for moe_grouped_ffn (required, and w_gate_up / w_down unused,
- * with shape->w_mxfp8 = 1).  topk_ids_out [T,k],
+ * optional, as for moe_grouped_ffn (required with shape->w_mxfp8 = 1); when
+ * it is given, w_gate_up / w_down are not read and may be NULL.  topk_ids_out [T,k],
  * topk_w_out [T,k] and counts_out [E] are optional copies of the routing
  * (NULL = not written). */
 int moe_forward(const moe_shape* shape, const uint16_t* x, const float* w_router,

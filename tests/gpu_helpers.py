@@ -30,9 +30,13 @@ DEV = "cuda"
 
 
 def gpu_forward(layer, light_max_rows: int = -1, heavy_tile_rows: int = 0, y_bf16: bool = False,
-                y_fp16: bool = False):
-    m = moe.MoELayer(layer, light_max_rows, heavy_tile_rows, y_bf16=y_bf16, y_fp16=y_fp16)
+                y_fp16: bool = False, packed: bool = False):
+    """moe_forward on the layer; with ``packed`` the weights are handed over
+    only as the packed copy (the plain layout is not passed)."""
+    m = moe.MoELayer(layer, light_max_rows, heavy_tile_rows, y_bf16=y_bf16, y_fp16=y_fp16,
+                     packed=packed)
     out, ids, w, counts = m()
+    del m
     torch.cuda.synchronize()
     return dict(out=out.cpu().numpy(), ids=ids.cpu().numpy(), w=w.cpu().numpy(),
                 counts=counts.cpu().numpy())
@@ -73,17 +77,30 @@ def check_routing(gpu_ids, gpu_w, ref):
     return int(set_doubt.sum()), int(order_doubt.sum())
 
 
+def weight_error(gpu_w, ref):
+    """Largest |dw| - W_ATOL over |w| on the tokens whose routing is clear:
+    the relative weight error the W_RTOL bound has to cover."""
+    set_doubt, order_doubt = routing_flags(ref)
+    clean = ~(set_doubt | order_doubt)
+    if not clean.any():
+        return 0.0
+    d = np.abs(gpu_w[clean].astype(np.float64) - ref["w"][clean])
+    return float(np.max(np.maximum(d - W_ATOL, 0.0) / np.maximum(np.abs(ref["w"][clean]), 1e-30)))
+
+
 def check_layer(o, layer, tokens=None, light_max_rows: int = -1, full_routing=True,
-                heavy_tile_rows: int = 0, y_bf16: bool = False, y_fp16: bool = False):
+                heavy_tile_rows: int = 0, y_bf16: bool = False, y_fp16: bool = False,
+                packed: bool = False):
     """Run the layer on the GPU and compare with the oracle.  ``tokens``
     restricts the FFN/combine comparison to a sample of token rows; routing
     is compared on every token when ``full_routing``."""
     c = layer.cfg
-    g = gpu_forward(layer, light_max_rows, heavy_tile_rows, y_bf16, y_fp16)
+    g = gpu_forward(layer, light_max_rows, heavy_tile_rows, y_bf16, y_fp16, packed)
     report = {}
     if full_routing:
         r_all = o.route(o.logits(layer.x, layer.wg, layer.bias), c.k, c.renorm)
         report["near_ties"] = check_routing(g["ids"], g["w"], r_all)
+        report["w_rel"] = weight_error(g["w"], r_all)
         perm = o.permute(g["ids"], c.E)
         assert np.array_equal(g["counts"], perm["counts"]), "counts differ from oracle permute"
         assert int(g["counts"].sum()) == c.T * c.k
@@ -93,6 +110,7 @@ def check_layer(o, layer, tokens=None, light_max_rows: int = -1, full_routing=Tr
                     layer.ws_gu, layer.ws_dn, tokens=tok_t, permute=False)
     if not full_routing:
         report["near_ties"] = check_routing(g["ids"][tok], g["w"][tok], ref)
+        report["w_rel"] = weight_error(g["w"][tok], ref)
     set_doubt, order_doubt = routing_flags(ref)
     flagged = set_doubt | order_doubt
     clean = ~flagged

@@ -218,3 +218,32 @@ def test_mxfp8_tile_limit(L):
     assert moe.workspace_bytes(shp(w_mxfp8=1, heavy_tile_rows=256)) == 0
     assert moe.workspace_bytes(shp(w_mxfp8=1, heavy_tile_rows=192)) > 0
     assert moe.workspace_bytes(shp(w_mxfp8=1, heavy_tile_rows=0)) > 0
+
+
+def test_plain_weights_optional_with_packed(L):
+    """With packed weights the plain layout is not read: NULL w_gate_up /
+    w_down pass validation (the call then stops at the misaligned y)."""
+    s = shp()
+    need = moe.workspace_bytes(s)
+    P = ctypes.c_void_p(0x10000)
+    bad = ctypes.c_void_p(0x10008)
+    rc = L.moe_grouped_ffn(ctypes.byref(s), P, P, P, None, None, P, None, bad, P, need, None)
+    assert rc == moe.MOE_ERR_ALIGN and "y" in moe.last_error()
+    # without packed weights they are required
+    rc = L.moe_grouped_ffn(ctypes.byref(s), P, P, P, None, None, None, None, P, P, need, None)
+    assert rc == moe.MOE_ERR_NULL and "w_gate_up" in moe.last_error()
+    rc = L.moe_forward(ctypes.byref(s), P, P, None, None, None, P, None, None, bad, None, None,
+                       None, P, need, None)
+    assert rc == moe.MOE_ERR_ALIGN and "out" in moe.last_error()
+
+
+def test_workspace_holds_plan_of_repeated_ids(L):
+    """moe_permute accepts ids repeated within a token, so the plan region is
+    sized for the tiles of an expert holding every routed row: at T <= 64 the
+    workspace still grows with the rows, by two ints per possible tile."""
+    a = moe.workspace_bytes(shp(T=64))
+    b = moe.workspace_bytes(shp(T=64, light_max_rows=0))
+    assert a > 0 and b > 0
+    # the all-heavy layout can hold at least A/128 + 1 tiles as well
+    assert abs(a - b) < 64 * 1024
+
