@@ -18,7 +18,8 @@ LIB = os.path.join(PKG, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["router.hip", "permute.hip", "ffn.hip", "combine.hip", "mxfp8.hip", "moe_api.cpp"]
+SOURCES = ["router.hip", "permute.hip", "ffn.hip", "combine.hip", "mxfp8.hip", "noalloc.hip",
+           "moe_api.cpp"]
 
 # A second build of the same sources with the heavy kernels' grid capped at 16
 # blocks, so each block runs many work items in a row: the tests compare its

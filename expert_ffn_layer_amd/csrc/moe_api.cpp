@@ -29,6 +29,13 @@ int fail(int code, const std::string& msg) {
     return code;
 }
 
+}  // namespace
+
+namespace moe {
+int report_error(int code, const char* msg) { return fail(code, msg); }
+}  // namespace moe
+
+namespace {
 
 constexpr size_t kAlign = 256;
 

@@ -34,7 +34,9 @@ EXPORTED = ("moe_workspace_bytes", "moe_packed_weight_bytes", "moe_status_string
             "moe_last_error", "moe_router", "moe_permute", "moe_pack_weights", "moe_grouped_ffn",
             "moe_shared_ffn", "moe_combine", "moe_forward", "moe_profile_kernel",
             "moe_profile_kernel_launch", "moe_profile_launches", "moe_quantize_mxfp8",
-            "moe_pack_weights_mxfp8")
+            "moe_pack_weights_mxfp8", "moe_forward_noalloc")
+# Fixed scratch of moe_forward_noalloc (MOE_NOALLOC_SCRATCH_BYTES in moe.h).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # enum moe_kernel
 KERNELS = ("router_gemm", "router_select", "perm_count", "perm_scan", "perm_scatter", "ffn_plan",
@@ -124,12 +126,13 @@ def lib() -> ctypes.CDLL:
         L.moe_shared_ffn.argtypes = [_sp] + [_vp] * 5 + [ctypes.c_size_t, _vp]
         L.moe_combine.argtypes = [_sp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp]
         L.moe_forward.argtypes = [_sp] + [_vp] * 13 + [ctypes.c_size_t, _vp]
+        L.moe_forward_noalloc.argtypes = [_sp] + [_vp] * 12 + [_vp]
         L.moe_profile_kernel.argtypes = [ctypes.c_int, _vp, _vp]
         L.moe_profile_kernel_launch.argtypes = [ctypes.c_int, ctypes.c_int, _vp, _vp]
         L.moe_profile_launches.argtypes = []
         L.moe_profile_launches.restype = ctypes.c_longlong
         for name in ("moe_router", "moe_permute", "moe_pack_weights", "moe_grouped_ffn",
-                     "moe_shared_ffn", "moe_combine", "moe_forward",
+                     "moe_shared_ffn", "moe_combine", "moe_forward", "moe_forward_noalloc",
                      "moe_profile_kernel", "moe_profile_kernel_launch"):
             getattr(L, name).restype = ctypes.c_int
         _libs[path] = L
@@ -323,6 +326,17 @@ def forward(shape, x, w_router, bias, w_gate_up, w_down, ws_gate_up, ws_down, ou
                          topk_ids_out, topk_w_out, counts_out, packed_weights)
     wp, wn = _ws(workspace, shape)
     _check(lib().moe_forward(ctypes.byref(shape), *args, wp, wn, _stream(stream)))
+
+
+def forward_noalloc(shape, x, w_router, bias, w_gate_up, w_down, ws_gate_up, ws_down, out,
+                    topk_ids_out=None, topk_w_out=None, counts_out=None, stream=None,
+                    packed_weights=None):
+    """moe_forward_noalloc: the layer on the library's fixed per-GPU scratch
+    array (no workspace argument; shapes needing more than
+    NOALLOC_SCRATCH_BYTES of scratch are rejected)."""
+    args = _forward_args(shape, x, w_router, bias, w_gate_up, w_down, ws_gate_up, ws_down, out,
+                         topk_ids_out, topk_w_out, counts_out, packed_weights)
+    _check(lib().moe_forward_noalloc(ctypes.byref(shape), *args, _stream(stream)))
 
 
 def _forward_args(shape, x, w_router, bias, w_gate_up, w_down, ws_gate_up, ws_down, out,

@@ -292,6 +292,30 @@ int moe_forward(const moe_shape* shape, const uint16_t* x, const float* w_router
                 int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out,
                 void* workspace, size_t ws_bytes, void* stream);
 
+/* Size of the fixed scratch array behind moe_forward_noalloc (per GPU). */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* moe_forward for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * layer, arguments and results as moe_forward, with no workspace argument:
+ * the scratch memory is a file-scope device array of
+ * MOE_NOALLOC_SCRATCH_BYTES (64 MiB) that each GPU the library runs on holds
+ * until the process ends.  Its device address is looked up once per device
+ * (hipGetSymbolAddress, on the first call made with that device current);
+ * no call allocates or frees memory.  Shapes whose moe_workspace_bytes
+ * exceeds the array are rejected with MOE_ERR_WORKSPACE before anything is
+ * enqueued (64 MiB covers, e.g., a decode step of 64 tokens at H = 4096,
+ * E = 512, k = 10, I = 1024 with fp32 y).  Every call on one GPU uses that
+ * GPU's one array and leaves its contents behind (no step relies on them
+ * being zero): calls that may overlap on one GPU -- on different streams,
+ * or from different host threads -- race on it and must be serialised by
+ * the caller. */
+int moe_forward_noalloc(const moe_shape* shape, const uint16_t* x, const float* w_router,
+                        const float* bias, const uint16_t* w_gate_up, const uint16_t* w_down,
+                        const void* packed_weights, const uint16_t* ws_gate_up,
+                        const uint16_t* ws_down, float* out, int32_t* topk_ids_out,
+                        float* topk_w_out, int32_t* counts_out, void* stream);
+
 /* Kernels of the layer, for moe_profile_kernel. */
 enum moe_kernel {
     MOE_K_ROUTER_GEMM = 0,

@@ -247,3 +247,22 @@ def test_workspace_holds_plan_of_repeated_ids(L):
     # the all-heavy layout can hold at least A/128 + 1 tiles as well
     assert abs(a - b) < 64 * 1024
 
+
+def test_noalloc_limits(L):
+    """moe_forward_noalloc checks the shape and its scratch size on the host:
+    an invalid shape gives moe_forward's code, an oversized one
+    MOE_ERR_WORKSPACE naming the limit, both before any HIP call."""
+    P = ctypes.c_void_p(0x10000)
+    big = shp(T=4096)
+    assert moe.workspace_bytes(big) > moe.NOALLOC_SCRATCH_BYTES
+    rc = L.moe_forward_noalloc(ctypes.byref(big), P, P, None, P, P, None, None, None, P, None,
+                               None, None, None)
+    assert rc == moe.MOE_ERR_WORKSPACE and "MOE_NOALLOC_SCRATCH_BYTES" in moe.last_error()
+    rc = L.moe_forward_noalloc(ctypes.byref(shp(k=0)), P, P, None, P, P, None, None, None, P,
+                               None, None, None, None)
+    assert rc == moe.MOE_ERR_SHAPE
+    assert moe.workspace_bytes(shp(T=64)) <= moe.NOALLOC_SCRATCH_BYTES
+    # the header's limit is the binding's
+    text = open(HEADER).read()
+    assert "#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)" in text
+    assert moe.NOALLOC_SCRATCH_BYTES == 64 << 20

@@ -1,7 +1,7 @@
 """The host side of the C ABI under AddressSanitizer and
 UndefinedBehaviorSanitizer (CPU only).
 
-moe_api.cpp holds all the host code of libmoe.so: argument
+moe_api.cpp and noalloc.hip hold all the host code of libmoe.so: argument
 validation, the workspace layout and carving, the plan sizing, the error
 texts.  They are rebuilt with the sanitizers on their host pass only (the
 GPU code is built as usual and never runs here), linked with the kernels'
@@ -22,7 +22,7 @@ from expert_ffn_layer_amd import build
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 OBJDIR = os.path.join(build.OBJDIR, "sanitized")
 LIB = os.path.join(OBJDIR, "libmoe_sanitized.so")
-HOST_SOURCES = ("moe_api.cpp",)
+HOST_SOURCES = ("moe_api.cpp", "noalloc.hip")
 # sanitizers on the host compilation only (-Xarch_host before each)
 SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
        "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
