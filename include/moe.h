@@ -280,6 +280,10 @@ int moe_combine(const moe_shape* shape, const void* y, const int32_t* inv_pos,
 /* The whole layer: router, permute, grouped FFN, shared expert (when
  * shape->I_shared > 0), combine.  out fp32 [T,H]:
  *   out[t] = sum_j w[t,j] FFN_{ids[t,j]}(x[t])  (+ FFN_shared(x[t]))
+ * (pwwt.cn article on Qwen 3.5-397B MoE on Ironwood: section 8.2 routing,
+ * section 4.2 permute and grouped SwiGLU FFN, section 7.2 un-permute and
+ * gather-reduce; lumevalley.com Ling-2.6-1T article, opening paragraph: the
+ * shared expert added to the routed sum.)
  * ws_gate_up / ws_down are required iff I_shared > 0; packed_weights is
  * optional, as for moe_grouped_ffn (required with shape->w_mxfp8 = 1); when
  * it is given, w_gate_up / w_down are not read and may be NULL.  topk_ids_out [T,k],

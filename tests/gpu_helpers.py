@@ -17,6 +17,10 @@ import torch
 
 from expert_ffn_layer_amd import moe
 
+# (case, max_abs, relL2, largest relative routing-weight error, near-ties)
+# of the parity checks run in this session; printed at the end of the run.
+RESULTS = []
+
 MAX_ABS = 2e-2
 REL_L2 = 5e-3
 NEAR_TIE = 1e-6
@@ -115,6 +119,10 @@ def check_layer(o, layer, tokens=None, light_max_rows: int = -1, full_routing=Tr
     flagged = set_doubt | order_doubt
     clean = ~flagged
     report["err"] = assert_close(g["out"][tok][clean], ref["out"][clean], "layer output")
+    tag = (f"{c.name}[T={c.T} tokens={tok.size} light={light_max_rows} tm={heavy_tile_rows} "
+           f"y={'bf16' if y_bf16 else ('fp16' if y_fp16 else 'fp32')}"
+           f"{' packed' if packed else ''}]")
+    RESULTS.append((tag, *report["err"], report.get("w_rel", 0.0), report["near_ties"]))
     if flagged.any():
         ft = torch.as_tensor(tok[flagged], device=layer.x.device)
         ref2 = o.forward(layer.x, layer.wg, layer.bias, layer.w_gu, layer.w_dn, c.k, c.renorm,
