@@ -66,6 +66,9 @@ def parse():
     p.add_argument("--weights", choices=("bf16", "mxfp8"), default="bf16",
                    help="routed expert weights: bf16, or MXFP8 (OCP MX E4M3 codes with one "
                         "E8M0 scale per 32 values, quantised on the GPU before timing)")
+    p.add_argument("--heavy-tile-rows", type=int, default=0, choices=(0, 128, 192, 256),
+                   help="heavy tile height: 0 = the library's per-expert choice (results do "
+                        "not depend on it)")
     p.add_argument("--no-copy-calibration", action="store_true",
                    help="skip the untimed 1 GiB reference copy used to scale rocprof counters")
     p.add_argument("--summarize", nargs=4, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR", "LOG"),
@@ -387,7 +390,8 @@ def main():
         y_dt = "fp32" if cfg.fp32_values else ("fp16" if cfg.I_shared else "bf16")
     mx = args.weights == "mxfp8"
     m = moe.MoELayer(layer, packed=not args.no_packed, y_bf16=y_dt == "bf16",
-                     weights=args.weights, y_fp16=y_dt == "fp16")
+                     weights=args.weights, y_fp16=y_dt == "fp16",
+                     heavy_tile_rows=args.heavy_tile_rows)
     s = m.shape
     # The oracle's inputs for the CPU baseline (its sample's tokens and the
     # experts they reach) are copied to the host before the plain weights

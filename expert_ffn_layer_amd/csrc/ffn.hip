@@ -48,9 +48,9 @@ int max_heavy_tiles(long long A, int E, int light_max) {
 }
 
 int dense_tile_height(int rows) {
-    const long long t0 = (rows + kTileTM0 - 1) / kTileTM0, t1 = (rows + kTileTM1 - 1) / kTileTM1,
-                    t2 = (rows + kTileTM2 - 1) / kTileTM2;
-    return tile_height(pick_tile_height(t0, t1, t2));
+    int nt, main_tmi, last_tmi;
+    tile_split(rows, 0, nt, main_tmi, last_tmi);
+    return tile_height(main_tmi);
 }
 
 namespace {
@@ -824,32 +824,106 @@ constexpr int kHeavyThreads = 512;
 constexpr int kHeavyWaves = kHeavyThreads / 64;
 constexpr int kTN = 256;       // B rows per tile (output columns, or 128 gate + 128 up rows)
 constexpr int kWTN = kTN / 4;  // 64 columns per wave
-// LDS rings: A (rows of x or h) two stages deep, except three for the down
-// GEMM's 256-row tiles (measured 1.7% faster; 3% slower for gate|up); B
-// (expert weights) two deep with 256-row tiles and three deep with 192- and
-// 128-row tiles.  The smaller heights are chosen when experts have few rows,
-// so each expert's weights feed few row tiles and stream from HBM with a
-// longer latency to cover; 256-row tiles are chosen for large experts whose
-// weights the row tiles share through L2 (measured: the third B buffer costs
-// 3% there and gains 7% on streamed weights).  At most one of the two rings
-// is three deep: 160 KB of LDS.
+// LDS rings, one per operand: A (rows of x or h, TM x 64 K per stage) and B
+// (the expert weights, 256 x 64 per stage; MXFP8: 16 KB of codes + 512 B of
+// scales), each as deep as the 160 KB allow for the tile height.  The loads
+// are split by role: waves 0..3 fill the A ring, waves 4..7 the B ring, so
+// every wave keeps one ring's loads in flight and waits for its own stage
+// with one vmcnt count, whatever the tile height.  A stage is issued `depth
+// - 1` stages before it is read: a deeper ring covers a longer load latency
+// (the weights come from HBM; on MI355X the latency under load is about the
+// MFMA time of one 64-wide stage of a 256-row tile).
 constexpr int kKS = 64;            // K values per stage
-constexpr int kHeavyLds = 160 * 1024;  // LDS of the heavy kernels: the largest ring below
+constexpr int kHeavyLds = 160 * 1024;  // LDS of the heavy kernels: the largest ring pair below
 constexpr int kBlk = 1024;         // bytes of one 8-row x 64-K block
 constexpr int kBlocksB = kTN / 8;  // 32
-constexpr int kBBlkPerWave = kBlocksB / kHeavyWaves;  // 4
-// Per tile height TM (256, 192, 128): each wave row group holds TM/2 rows
-// = TM/32 MFMA row tiles; a stage holds TM/8 A blocks and 32 B blocks.
-template <Mode M, int TM>
+constexpr int kRoleWaves = 4;      // waves per DMA role (A: 0..3, B: 4..7)
+constexpr int kBInst16 = kBlocksB / kRoleWaves;  // 8 bf16 B blocks per B wave and stage
+constexpr int kB8Blk = 4;          // MXFP8 code blocks (16 rows x 64 codes) per B wave and stage
+constexpr int kBInst8 = kB8Blk + 1;  // ... plus one load of 128 scale bytes
+
+// Ring depths (A, B) per tile height (compile-time tunables).
+#ifndef MOE_RING_256
+#define MOE_RING_256 2, 3
+#endif
+#ifndef MOE_RING_256_DOWN
+#define MOE_RING_256_DOWN 3, 2
+#endif
+#ifndef MOE_RING_224
+#define MOE_RING_224 2, 3
+#endif
+#ifndef MOE_RING_192
+#define MOE_RING_192 2, 3
+#endif
+#ifndef MOE_RING_160
+#define MOE_RING_160 3, 3
+#endif
+#ifndef MOE_RING_128
+#define MOE_RING_128 3, 3
+#endif
+#ifndef MOE_RING_MX
+#define MOE_RING_MX 3, 3
+#endif
+struct RingDepth {
+    int a, b;
+};
+template <Mode M, int TM, bool W8>
+constexpr RingDepth ring_depth() {
+    if (W8) return RingDepth{MOE_RING_MX};
+    if (TM == 256) return M == Mode::Down ? RingDepth{MOE_RING_256_DOWN} : RingDepth{MOE_RING_256};
+    if (TM == 224) return RingDepth{MOE_RING_224};
+    if (TM == 192) return RingDepth{MOE_RING_192};
+    if (TM == 160) return RingDepth{MOE_RING_160};
+    return RingDepth{MOE_RING_128};
+}
+
+// Per tile height TM (a multiple of 32 in [128, 256]): each wave row group
+// holds TM/2 rows = TM/32 MFMA row tiles; a stage holds TM/8 A blocks, TM/32
+// per A wave, and 32 B blocks, 8 per B wave.
+template <Mode M, int TM, bool W8>
 struct HeavyGeom {
-    static_assert(TM % 64 == 0 && TM >= 128 && TM <= 256, "tile height");
-    static constexpr int kRF = TM / 32;                   // row tiles per wave (8, 6, 4)
-    static constexpr int kBlocksA = TM / 8;               // 32, 24, 16
-    static constexpr int kABlkPerWave = kBlocksA / kHeavyWaves;  // 4, 3, 2
-    static constexpr int kABytes = kBlocksA * kBlk;       // 32, 24, 16 KB per stage
-    static constexpr int kBStages = TM == 256 ? 2 : 3;
-    static constexpr int kAStages = (TM == 256 && M == Mode::Down) ? 3 : 2;
-    // LDS 128 (gate|up) or 160 (down), 144, 128 KB
+    static_assert(TM % 32 == 0 && TM >= 128 && TM <= 256, "tile height");
+    static constexpr int kRF = TM / 32;                   // row tiles per wave
+    static constexpr int kBlocksA = TM / 8;
+    static constexpr int kAInst = kBlocksA / kRoleWaves;  // A loads per A wave and stage
+    static constexpr int kABytes = kBlocksA * kBlk;       // A bytes per stage
+    static constexpr int kBBytes = W8 ? kMxStageBytes : kBlocksB * kBlk;
+    static constexpr int kBInst = W8 ? kBInst8 : kBInst16;
+    static constexpr int kAStages = ring_depth<M, TM, W8>().a;
+    static constexpr int kBStages = ring_depth<M, TM, W8>().b;
+    static_assert(kAStages >= 2 && kBStages >= 2 && kAStages <= 4 && kBStages <= 4, "ring depth");
+    static_assert(kAStages * kABytes + kBStages * kBBytes <= kHeavyLds, "LDS rings");
+    static_assert(kAInst * 3 < 64 && kBInst * 3 < 64, "vmcnt range");
+};
+
+// Epilogue staging of the down GEMM's y.  A finished tile is written to LDS
+// (the ring is idle by then) in row-major order, rows padded by 16 bytes,
+// then read back in 16-byte chunks of whole rows and stored with 16-byte
+// lane stores: each store instruction writes 1 KB of whole cache lines.
+// Stored straight from the MFMA layout a lane holds 4 rows of one column, so
+// every store instruction wrote 2- or 4-byte pieces of 4 or 8 rows (measured
+// on MI355X: down -10% at prefill, -3% at the Ling-like layer with staging).
+// gate|up keeps the direct stores: its h tile is half as wide, and staging
+// it cost more than it saved (+4%).  fp32 y is staged in two passes of half
+// the rows (one wave row each) to fit the 160 KB.
+#ifndef MOE_HEAVY_STAGED_EPI
+#define MOE_HEAVY_STAGED_EPI 1
+#endif
+constexpr int kStgPad = 16;
+template <Mode M, int TM, int YF>
+struct Staging {
+    static constexpr int kCols = M == Mode::GateUp ? kTN / 2 : kTN;  // output columns of a tile
+    static constexpr int kElt = (M == Mode::Down && YF == kYF32) ? 4 : 2;
+    static constexpr int kRowBytes = kCols * kElt;  // 256 (h), 512 (16-bit y), 1024 (fp32 y)
+    static constexpr int kPitch = kRowBytes + kStgPad;
+    static constexpr int kPasses = (M == Mode::Down && YF == kYF32) ? 2 : 1;
+    static constexpr int kPassRows = TM / kPasses;
+    static constexpr int kChunks = kRowBytes / 16;        // 16-byte chunks per row
+    static constexpr int kIters = kPassRows * kChunks / kHeavyThreads;  // chunks per lane and pass
+    static_assert(kPassRows * kChunks % kHeavyThreads == 0, "staging split");
+    // gate|up with split h stages two planes (hi, lo)
+    static_assert(2 * kPassRows * kPitch <= kHeavyLds || M == Mode::Down, "staging size");
+    static_assert(kPassRows * kPitch <= kHeavyLds, "staging size");
 };
 
 typedef __attribute__((address_space(3))) void* lptr_t;
@@ -898,12 +972,47 @@ __device__ __forceinline__ int32_t sload(const int32_t* p, int i) {
     return ((const __attribute__((address_space(4))) int32_t*)p)[i];
 }
 
-// Height index (0, 1, 2 for kTileTM0/1/2) of row tile `tile`: from the
+// Height index (height 256 - 32 * index) of row tile `tile`: from the
 // plan's tile list, or the dense group's one height.
 __device__ __forceinline__ int tile_tmi(const FfnArgs& a, int tile) {
     if (a.plan)
         return (int)((uint32_t)sload(a.plan, kPlanHeader + a.E + 2 * tile + 1) >> kTileTmShift);
-    return a.dense_tm == kTileTM0 ? 0 : (a.dense_tm == kTileTM1 ? 1 : 2);
+    return tile_tm_index(a.dense_tm);
+}
+
+// Order of the work items of one expert (its row tiles x N blocks, a
+// contiguous range of the work list): 0 = the N block runs fastest, 1 = the
+// row tile runs fastest (the row tiles that read one N block's weights are
+// then neighbours in the list, and so run at the same time).
+#ifndef MOE_HEAVY_ORDER
+#define MOE_HEAVY_ORDER 0
+#endif
+
+// Row tile and N block of work item w.
+__device__ __forceinline__ int item_tile(const FfnArgs& a, long long w, int nblk, int& nb) {
+    const int tg = (int)(w / nblk);
+    if (MOE_HEAVY_ORDER == 0) {
+        nb = (int)(w % nblk);
+        return tg;
+    }
+    // The expert of tile tg, its tile count and tg's index among its tiles
+    // (the split rule the plan applied); a dense group is one expert.
+    int t0, nt;
+    if (a.plan) {
+        const int base = kPlanHeader + a.E + 2 * tg;
+        const int e = sload(a.plan, base);
+        const int m0 = sload(a.plan, base + 1) & kTileRowMask;
+        const int n = sload(a.offsets, e + 1) - sload(a.offsets, e);
+        int main_tmi, last_tmi;
+        tile_split(n, sload(a.plan, 2), nt, main_tmi, last_tmi);
+        t0 = tg - m0 / tile_height(main_tmi);
+    } else {
+        t0 = 0;
+        nt = (a.dense_rows + a.dense_tm - 1) / a.dense_tm;
+    }
+    const long long q = w - (long long)t0 * nblk;
+    nb = (int)(q / nt);
+    return t0 + (int)(q % nt);
 }
 
 // Runs this block's work items wi, wi + nb_x, ... (below wend) while their
@@ -920,28 +1029,31 @@ __device__ __forceinline__ int tile_tmi(const FfnArgs& a, int tile) {
 // bytes) and its two scales, and the hardware's scaled conversion turns
 // them into the bf16 operands of the bf16 path -- the same MFMA chains on the
 // dequantised weights, so the results equal the bf16 path's bit for bit.
+// Wait until at most `stages` whole stages of this wave's ring (kInst loads
+// each) are outstanding; `stages` is 0..3 (wave-uniform).
+template <int kInst>
+__device__ __forceinline__ void wait_stages(int stages) {
+    if (stages <= 0)
+        wait_vmcnt<0>();
+    else if (stages == 1)
+        wait_vmcnt<kInst>();
+    else if (stages == 2)
+        wait_vmcnt<2 * kInst>();
+    else
+        wait_vmcnt<3 * kInst>();
+}
+
 template <Mode M, int TM, int YF, int BS>
 __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, long long wi,
                                                  long long wend, int nb_x, int nblk) {
-    using G = HeavyGeom<M, TM>;
     constexpr bool W8 = BS == kBRecMx;
-    constexpr int kRF = G::kRF, kBlocksA = G::kBlocksA, kABlk = G::kABlkPerWave;
-    constexpr int kABytes = G::kABytes;
-    constexpr int kTmi = TM == kTileTM0 ? 0 : (TM == kTileTM1 ? 1 : 2);
+    using G = HeavyGeom<M, TM, W8>;
+    constexpr int kRF = G::kRF, kAInst = G::kAInst, kBInst = G::kBInst;
+    constexpr int kABytes = G::kABytes, kBBytes = G::kBBytes;
+    constexpr int ast = G::kAStages, bst = G::kBStages;
+    constexpr int kTmi = (kTileTMMax - TM) / kTileTMStep;
     // One LDS object for both rings (A stages, then B stages): with two
     // objects the compiler waits for every LDS DMA before any LDS read.
-    constexpr int kBBytes = W8 ? kMxStageBytes : kBlocksB * kBlk;
-    // B load instructions per wave and stage: 4 x 1 KB of bf16, or 2 x 1 KB of
-    // codes plus 64 bytes of scales.
-    constexpr int kBInst = W8 ? 3 : kBBlkPerWave;
-    constexpr int kB8Blk = 2;  // code blocks (16 rows x 64 codes) per wave
-    constexpr int bst = G::kBStages, ast = G::kAStages;
-    static_assert(ast == 2 || bst == 2, "one ring at most is three deep");
-    // Instructions per wave of the deeper ring's stage (0: both two deep).
-    constexpr int kDeepBlk = ast > 2 ? kABlk : (bst > 2 ? kBInst : 0);
-    static_assert(ast * kABytes + bst * kBBytes <= kHeavyLds, "LDS rings");
-    // Stage st's A lives in slot st % ast, its B in slot st % bst; both slot
-    // indices are carried along (no division in the loop).
     auto a_slot = [&](int slot) -> char* { return lds + slot * kABytes; };
     auto b_slot = [&](int slot) -> char* { return lds + ast * kABytes + slot * kBBytes; };
 
@@ -951,6 +1063,11 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: LDS offsets in SGPRs
     const int wm = wave >> 2, wn = wave & 3;
+    // DMA role (wave-uniform): waves 0..3 load A, waves 4..7 load B; rw is
+    // the wave's index within its role.
+    const bool a_role = wave < kRoleWaves;
+    const int rw = wave & (kRoleWaves - 1);
+    const int depth = a_role ? ast : bst;
     const int l16 = lane & 15, g = lane >> 4;
     const int nh = K / 32;         // 32-wide MFMA K steps (K % 32 == 0)
     const int nst = (nh + 1) / 2;  // 64-wide stages; the last one is half full if nh is odd
@@ -974,8 +1091,7 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
     // Where work item w sits (scalar reads only).
     auto locate = [&](long long w) -> Tile {
         Tile t;
-        const int tile = (int)(w / nblk);
-        t.nb = (int)(w % nblk);
+        const int tile = item_tile(a, w, nblk, t.nb);
         if (a.plan) {
             const int base = kPlanHeader + a.E + 2 * tile;
             t.e = sload(a.plan, base);
@@ -993,85 +1109,80 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
         }
         return t;
     };
-    int nb = 0, e = 0, r0 = 0, m0 = 0, rows = 0;
+    int nb = 0, r0 = 0, m0 = 0, rows = 0;
     // Weights of a tile that is its expert's only one are streamed past the
     // caches' retention (nt): they are read once, and keeping them would
     // push out the A rows the tile's N blocks share.  Weights that several
     // row tiles read stay cached.  (Measured: Ling-like step -6%, prefill
     // -2.5%; long prefill, three row tiles per expert, +8% if all were nt.)
     bool b_once = false;
-    __amdgpu_buffer_rsrc_t ar, br;
-    uint32_t aoff[kABlk], boff[W8 ? kB8Blk + 1 : kBBlkPerWave];
-    // Load sources of tile t: buffer resources and per-lane offsets.
+    __amdgpu_buffer_rsrc_t src;  // this wave's ring source
+    // Per-lane byte offsets of this wave's loads within `src` (A waves: row
+    // and K chunk of each A block; B waves: of each B block, or for the
+    // records the first block's, the others following 1 KB apart).
+    constexpr int kDOff = kAInst > kBInst16 ? kAInst : kBInst16;
+    uint32_t doff[kDOff];
+    // Load sources of tile t for this wave's role.
     auto use_tile = [&](const Tile& t) {
         nb = t.nb;
-        e = t.e;
         r0 = t.r0;
         m0 = t.m0;
         rows = t.rows;
         b_once = t.once;
-        // This wave fills A blocks kABlk*wave.. and B blocks 4*wave..+3.  Each
-        // source is a buffer resource (SGPRs) plus a 32-bit per-lane byte
-        // offset that holds the lane's row and K chunk; the stage's K offset
-        // is added once per stage.
-        if (M == Mode::GateUp)
-            ar = make_rsrc(a.x, (uint32_t)((size_t)a.T * a.H * 2));
-        else
-            ar = make_rsrc(a.h + (size_t)(r0 + m0) * hstride, (uint32_t)((size_t)TM * hstride * 2));
+        if (a_role) {
+            if (M == Mode::GateUp)
+                src = make_rsrc(a.x, (uint32_t)((size_t)a.T * a.H * 2));
+            else
+                src = make_rsrc(a.h + (size_t)(r0 + m0) * hstride, (uint32_t)((size_t)TM * hstride * 2));
+#pragma unroll
+            for (int i = 0; i < kAInst; ++i) {
+                const int b = kAInst * rw + i;
+                const int r = b * 8 + drow;         // row within the tile
+                const int rr = r < rows ? r : 0;    // rows past the count: any valid row
+                const uint32_t cb = (uint32_t)dchunk * 16u;
+                if (M == Mode::GateUp) {
+                    const int tok = a.sorted_ids ? a.sorted_ids[r0 + m0 + rr] : r0 + m0 + rr;
+                    doff[i] = (uint32_t)tok * (uint32_t)a.H * 2u + cb;
+                } else {
+                    doff[i] = (uint32_t)rr * (uint32_t)hstride * 2u + cb;
+                }
+            }
+            return;
+        }
         if constexpr (W8) {
-            // the tile's records: one per K chunk, kMxStageBytes each
+            // the tile's records: one per K chunk, kMxStageBytes each.  Code
+            // block b = 4*rw + i holds tile rows 16b..16b+15; lane L fills
+            // LDS slot L: row L/4, 16-byte unit L%4, which takes unit
+            // (L%4) ^ mx_swz(row) of the record's row (the swizzle spreads
+            // the fragment reads of 16 rows over all banks).
             const uint8_t* base = M == Mode::GateUp ? a.hq_gu : a.hq_dn;
             const size_t rec = (size_t)nst * kMxStageBytes;
-            br = make_rsrc(base + ((size_t)e * nblk + nb) * rec, (uint32_t)rec);
-        } else if (BS == kBRec16) {
-            const uint16_t* base = M == Mode::GateUp ? a.hr_gu : a.hr_dn;
-            const size_t rec = (size_t)nst * kRec16Bytes;
-            br = make_rsrc(reinterpret_cast<const char*>(base) + ((size_t)e * nblk + nb) * rec,
-                           (uint32_t)rec);
-        } else if (M == Mode::GateUp) {
-            br = make_rsrc(a.w_gu + (size_t)e * 2 * a.I * a.H, (uint32_t)((size_t)2 * a.I * a.H * 2));
-        } else {
-            br = make_rsrc(a.w_dn + (size_t)e * a.H * a.I, (uint32_t)((size_t)a.H * a.I * 2));
-        }
-#pragma unroll
-        for (int i = 0; i < kABlk; ++i) {
-            const int b = kABlk * wave + i;
-            const int r = b * 8 + drow;         // row within the tile
-            const int rr = r < rows ? r : 0;    // rows past the count: any valid row
-            const uint32_t cb = (uint32_t)dchunk * 16u;
-            if (M == Mode::GateUp) {
-                const int tok = a.sorted_ids ? a.sorted_ids[r0 + m0 + rr] : r0 + m0 + rr;
-                aoff[i] = (uint32_t)tok * (uint32_t)a.H * 2u + cb;
-            } else {
-                aoff[i] = (uint32_t)rr * (uint32_t)hstride * 2u + cb;
-            }
-        }
-        if constexpr (W8) {
-            // Code block b = 2*wave + i holds tile rows 16b..16b+15; lane L
-            // fills LDS slot L: row L/4, 16-byte unit L%4, which takes unit
-            // (L%4) ^ mx_swz(row) of the record's row (the swizzle spreads the
-            // fragment reads of 16 rows over all banks).
+            src = make_rsrc(base + ((size_t)t.e * nblk + nb) * rec, (uint32_t)rec);
 #pragma unroll
             for (int i = 0; i < kB8Blk; ++i) {
-                const int r = (kB8Blk * wave + i) * 16 + (lane >> 2);
-                boff[i] = (uint32_t)r * 64u + 16u * (uint32_t)((lane & 3) ^ mx_swz(r));
+                const int r = (kB8Blk * rw + i) * 16 + (lane >> 2);
+                doff[i] = (uint32_t)r * 64u + 16u * (uint32_t)((lane & 3) ^ mx_swz(r));
             }
-            // scales: this wave's 64 bytes, lanes 0..3
-            boff[kB8Blk] = (uint32_t)kMxCodeBytes + 64u * (uint32_t)wave + 16u * (uint32_t)(lane & 3);
+            // scales: this wave's 128 bytes, lanes 0..7
+            doff[kB8Blk] = (uint32_t)kMxCodeBytes + 128u * (uint32_t)rw + 16u * (uint32_t)(lane & 7);
             return;
         }
         if constexpr (BS == kBRec16) {
             // record rows are already the tile's B rows (128 bytes each)
-#pragma unroll
-            for (int i = 0; i < kBBlkPerWave; ++i) {
-                const int r = (kBBlkPerWave * wave + i) * 8 + drow;
-                boff[i] = (uint32_t)r * 128u + (uint32_t)dchunk * 16u;
-            }
+            const uint16_t* base = M == Mode::GateUp ? a.hr_gu : a.hr_dn;
+            const size_t rec = (size_t)nst * kRec16Bytes;
+            src = make_rsrc(reinterpret_cast<const char*>(base) + ((size_t)t.e * nblk + nb) * rec,
+                            (uint32_t)rec);
+            doff[0] = (uint32_t)((kBInst16 * rw) * 8 + drow) * 128u + (uint32_t)dchunk * 16u;
             return;
         }
+        if (M == Mode::GateUp)
+            src = make_rsrc(a.w_gu + (size_t)t.e * 2 * a.I * a.H, (uint32_t)((size_t)2 * a.I * a.H * 2));
+        else
+            src = make_rsrc(a.w_dn + (size_t)t.e * a.H * a.I, (uint32_t)((size_t)a.H * a.I * 2));
 #pragma unroll
-        for (int i = 0; i < kBBlkPerWave; ++i) {
-            const int b = kBBlkPerWave * wave + i;
+        for (int i = 0; i < kBInst16; ++i) {
+            const int b = kBInst16 * rw + i;
             const int r = b * 8 + drow;  // B row within the tile
             const uint32_t cb = (uint32_t)dchunk * 16u;
             if (M == Mode::GateUp) {
@@ -1079,16 +1190,14 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
                 // matching up rows, so g and u of an element share a lane.
                 const int hc = nb * (kTN / 2) + (r >> 5) * 16 + (r & 15);
                 const int wr = (hc < a.I) ? (((r & 16) == 0) ? hc : a.I + hc) : 0;
-                boff[i] = (uint32_t)wr * (uint32_t)a.H * 2u + cb;
+                doff[i] = (uint32_t)wr * (uint32_t)a.H * 2u + cb;
             } else {
                 const int c = nb * kTN + r;
-                boff[i] = (uint32_t)(c < a.H ? c : 0) * (uint32_t)a.I * 2u + cb;
+                doff[i] = (uint32_t)(c < a.H ? c : 0) * (uint32_t)a.I * 2u + cb;
             }
         }
     };
     auto setup = [&](long long w) { use_tile(locate(w)); };
-    // Stage st's loads of this wave: A blocks into A slot st % ast, B blocks
-    // into B slot st % bst.
     auto adjust = [&](int kk, uint32_t& adj_a, uint32_t& adj_b) {
         // Upper-half lanes in two rare stages: in the half-full last stage
         // they reload an in-row chunk that is never used; in the stage that
@@ -1101,47 +1210,50 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
         adj_b = (tail && upper) ? 64u : ((straddle && upper) ? (uint32_t)a.I * 2u : 0u);
         asm volatile("" : "+v"(adj_a), "+v"(adj_b));
     };
-    // The whole offset goes in the lane's VGPR; the 32-bit sum is exact
-    // because the true offset is never negative.
-    auto issue_a = [&](int st, int slot) {
-        char* buf = a_slot(slot);
-        const int kk = st * kKS;
-        uint32_t adj_a, adj_b;
-        adjust(kk, adj_a, adj_b);
-        const uint32_t sa = (uint32_t)kk * 2u - adj_a;
+    // This wave's loads of stage st (of the current source) into ring slot
+    // `slot`: A blocks kAInst*rw.. or B blocks of the wave's share.  The
+    // whole offset goes in the lane's VGPR; the 32-bit sum is exact because
+    // the true offset is never negative.
+    auto issue = [&](int st, int slot) {
+        if (a_role) {
+            char* buf = a_slot(slot) + kAInst * rw * kBlk;
+            const int kk = st * kKS;
+            uint32_t adj_a, adj_b;
+            adjust(kk, adj_a, adj_b);
+            const uint32_t sa = (uint32_t)kk * 2u - adj_a;
 #pragma unroll
-        for (int i = 0; i < kABlk; ++i)
-            lds_dma16(ar, aoff[i] + sa, 0u, buf + (kABlk * wave + i) * kBlk);
-    };
-    auto issue_b = [&](int st, int slot) {
+            for (int i = 0; i < kAInst; ++i) lds_dma16(src, doff[i] + sa, 0u, buf + i * kBlk);
+            return;
+        }
         char* buf = b_slot(slot);
         if constexpr (W8) {
             const uint32_t sb = (uint32_t)st * (uint32_t)kMxStageBytes;
+            char* cbuf = buf + kB8Blk * rw * kBlk;
+            char* sbuf = buf + kMxCodeBytes + 128 * rw;
             if (b_once) {
 #pragma unroll
-                for (int i = 0; i < kB8Blk; ++i)
-                    lds_dma16<true>(br, boff[i] + sb, 0u, buf + (kB8Blk * wave + i) * kBlk);
-                if (lane < 4)
-                    lds_dma16<true>(br, boff[kB8Blk] + sb, 0u, buf + kMxCodeBytes + 64 * wave);
+                for (int i = 0; i < kB8Blk; ++i) lds_dma16<true>(src, doff[i] + sb, 0u, cbuf + i * kBlk);
+                if (lane < 8) lds_dma16<true>(src, doff[kB8Blk] + sb, 0u, sbuf);
             } else {
 #pragma unroll
-                for (int i = 0; i < kB8Blk; ++i)
-                    lds_dma16(br, boff[i] + sb, 0u, buf + (kB8Blk * wave + i) * kBlk);
-                if (lane < 4) lds_dma16(br, boff[kB8Blk] + sb, 0u, buf + kMxCodeBytes + 64 * wave);
+                for (int i = 0; i < kB8Blk; ++i) lds_dma16(src, doff[i] + sb, 0u, cbuf + i * kBlk);
+                if (lane < 8) lds_dma16(src, doff[kB8Blk] + sb, 0u, sbuf);
             }
             return;
         }
+        buf += kBInst16 * rw * kBlk;
         if constexpr (BS == kBRec16) {
-            // padded records: no tail adjustment
-            const uint32_t sb = (uint32_t)st * (uint32_t)kRec16Bytes;
+            // padded records: no tail adjustment; the wave's 8 blocks are
+            // 8 KB contiguous in the record
+            const uint32_t sb = (uint32_t)st * (uint32_t)kRec16Bytes + doff[0];
             if (b_once) {
 #pragma unroll
-                for (int i = 0; i < kBBlkPerWave; ++i)
-                    lds_dma16<true>(br, boff[i] + sb, 0u, buf + (kBBlkPerWave * wave + i) * kBlk);
+                for (int i = 0; i < kBInst16; ++i)
+                    lds_dma16<true>(src, sb + (uint32_t)(i * kBlk), 0u, buf + i * kBlk);
             } else {
 #pragma unroll
-                for (int i = 0; i < kBBlkPerWave; ++i)
-                    lds_dma16(br, boff[i] + sb, 0u, buf + (kBBlkPerWave * wave + i) * kBlk);
+                for (int i = 0; i < kBInst16; ++i)
+                    lds_dma16(src, sb + (uint32_t)(i * kBlk), 0u, buf + i * kBlk);
             }
             return;
         }
@@ -1153,25 +1265,23 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
         const uint32_t sb = (uint32_t)kb * 2u - adj_b;
         if (b_once) {
 #pragma unroll
-            for (int i = 0; i < kBBlkPerWave; ++i)
-                lds_dma16<true>(br, boff[i] + sb, 0u, buf + (kBBlkPerWave * wave + i) * kBlk);
+            for (int i = 0; i < kBInst16; ++i) lds_dma16<true>(src, doff[i] + sb, 0u, buf + i * kBlk);
         } else {
 #pragma unroll
-            for (int i = 0; i < kBBlkPerWave; ++i)
-                lds_dma16(br, boff[i] + sb, 0u, buf + (kBBlkPerWave * wave + i) * kBlk);
+            for (int i = 0; i < kBInst16; ++i) lds_dma16(src, doff[i] + sb, 0u, buf + i * kBlk);
         }
     };
-    // A tile's first loads, in the order the waits below count on: A0 B0
-    // [A1 B1] [A2 or B2 of the three-deep ring].
+    // A tile's first loads: this wave's ring, stages 0 .. depth-1 (those
+    // that exist) into slots 0 .. depth-1.
     auto issue_first = [&]() {
-        issue_a(0, 0);
-        issue_b(0, 0);
-        if (nst > 1) {
-            issue_a(1, 1);
-            issue_b(1, 1);
-        }
-        if (ast == 3 && nst > 2) issue_a(2, 2);
-        if (bst == 3 && nst > 2) issue_b(2, 2);
+        for (int st = 0; st < depth && st < nst; ++st) issue(st, st);
+    };
+    // Wait until this wave's loads leave at most `stages` stages outstanding.
+    auto wait_own = [&](int stages) {
+        if (a_role)
+            wait_stages<kAInst>(stages);
+        else
+            wait_stages<kBInst>(stages);
     };
     // Fragment reads of one 32-wide K half of a stage.  A fragment i of this
     // wave is tile rows wm*TM/2 + 16i.., B fragment j is B rows (wn*4 + j)*16..
@@ -1205,7 +1315,7 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
             b1[j] = e4m3x8_to_bf16(raw[j][2], raw[j][3], (sw >> 8) & 0xffu);
         }
     };
-    // A fragments in two groups: rows [0, kRF/2) and [kRF/2, kRF).
+    // A fragments in two groups: rows [0, kG0) and [kG0, kRF).
     constexpr int kG0 = kRF / 2;
     auto read_a = [&](int slot, int half, int grp, bf16x8_t (&af)[kRF]) {
         const int i0 = grp ? kG0 : 0, i1 = grp ? kRF : kG0;
@@ -1214,21 +1324,24 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
     };
 
     // Cross-tile prefetch (down only): while a tile runs its last stages, the
-    // stages freed in the rings take the next tile's first stages, as if the
-    // two tiles' K loops were one stream, so the next tile starts with its
-    // first stage in LDS and its first fragments in registers.  The next
-    // tile's sources are set up between the shallow ring's last load of this
-    // tile and the deep ring's first load of the next one.  Down only: its
-    // setup needs scalar reads alone, while gate|up gathers row ids with
-    // vector loads, which the ring's vmcnt waits do not count.  Needs whole
-    // stages (nh even) and at least as many stages as the deeper ring.
+    // ring slots it frees take the next tile's first stages, as if the two
+    // tiles' K loops were one stream, so the next tile starts with its first
+    // stage in LDS and its first fragments in registers.  Each wave switches
+    // its source to the next tile just before its ring's first load of it.
+    // Down only: its setup needs scalar reads alone, while gate|up gathers
+    // row ids with vector loads, which the ring's vmcnt waits do not count.
+    // Needs whole stages (nh even) and at least as many stages as a ring is
+    // deep; not for 256-row tiles (the extra state spills).
     constexpr int kDeepest = ast > bst ? ast : bst;
-    const bool pf_ok = M == Mode::Down && TM != 256 && (nh & 1) == 0 && nst >= kDeepest;
-    static_assert(M != Mode::Down || ast != bst, "cross-tile prefetch wants rings of different depth");
+    // (The down GEMM's staged epilogue reuses the ring, so it leaves no room
+    // for a prefetch.)
+    const bool pf_ok = !MOE_HEAVY_STAGED_EPI && M == Mode::Down && TM != 256 && (nh & 1) == 0 &&
+                       nst >= kDeepest;
 
     setup(wi);
     issue_first();
-    int bs = 0, as = 0;     // B and A slots of the current stage
+    int rs = 0;             // this wave's ring slot of the current stage
+    int as = 0, bs = 0;     // A and B slots of the current stage (fragment reads)
     bool primed = false;    // stage 0 already in, its first fragments in af / bf0
     bf16x8_t af[kRF], bf0[4], bf1[4];
     u32x4_t raw[4];  // W8: next stage's B codes, converted behind the MFMAs
@@ -1249,7 +1362,8 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
 
         const int t_nb = nb, t_base = r0 + m0, t_rows = rows;
         const long long wnext = wi + nb_x;
-        const bool more = wnext < wend && tile_tmi(a, (int)(wnext / nblk)) == kTmi;
+        int nb_next;
+        const bool more = wnext < wend && tile_tmi(a, item_tile(a, wnext, nblk, nb_next)) == kTmi;
         const bool pf = pf_ok && more;
         Tile nx{};
         if (pf) nx = locate(wnext);
@@ -1258,14 +1372,8 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
             // The first loads were requested after the previous tile's
             // epilogue stores (or above, for the first tile); vector-memory
             // operations retire in order, so stage 0 is in once at most the
-            // loads after it (A1 B1, and stage 2 of a three-deep ring) are
-            // pending.
-            if (nst > 2 && kDeepBlk > 0)
-                wait_vmcnt<kABlk + kBInst + kDeepBlk>();
-            else if (nst > 1)
-                wait_vmcnt<kABlk + kBInst>();
-            else
-                wait_vmcnt<0>();
+            // wave's later stages are pending.
+            wait_own(min(depth, nst) - 1);
             ring_barrier();
             if constexpr (W8) {
                 read_b8(0, raw, sc);
@@ -1282,7 +1390,7 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
         // with), the second half of the A rows after the second group.  At a
         // stage boundary the first group also covers the wait for the next
         // stage and the barrier that frees this stage's buffers for the loads
-        // two or three stages ahead.  One loop with a branch-free body (no peeled
+        // `depth` stages ahead.  One loop with a branch-free body (no peeled
         // copies): peeling made the register allocator stop keeping each
         // accumulator in place and spill.
         const int nfull = nh / 2;  // stages with both halves
@@ -1300,32 +1408,22 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
             // outstanding and the ring addresses are valid.  With one, the
             // next stage is the next tile's stage 0.
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of st done
-            // Stage st+1 in: only the three-deep ring's load of stage st+2
-            // may be pending.  After the previous tile's epilogue the stores
-            // are pending too, behind that load; counting them out is exact
-            // enough (it only waits for them as well).
-            if (kDeepBlk > 0 && (st + 2 < nst || pf))
-                wait_vmcnt<kDeepBlk>();
-            else
-                wait_vmcnt<0>();
+            // Stage st+1 in: this wave has issued stages up to st+depth-1 (of
+            // this tile, then the next one's with a prefetch), so at most
+            // depth-2 later stages may be pending.  After the previous tile's
+            // epilogue the stores are pending too, behind those loads;
+            // counting them out only waits for them as well.
+            wait_own(pf ? depth - 2 : min(depth - 2, nst - st - 2));
             ring_barrier();
-            // Refill the buffers stage st used, each ring its depth ahead and
-            // the two-deep ring first (this order is what the wait above
-            // counts on); stage st + depth lands in stage st's slot.  Stages
+            // Refill the slot stage st used with stage st + depth; stages
             // past this tile's last are the next tile's.
-            if (ast <= bst) {
-                if (st + ast < nst) issue_a(st + ast, as);
-                else if (pf) issue_a(st + ast - nst, as);
-                if (pf && st + bst == nst) use_tile(nx);
-                if (st + bst < nst) issue_b(st + bst, bs);
-                else if (pf) issue_b(st + bst - nst, bs);
-            } else {
-                if (st + bst < nst) issue_b(st + bst, bs);
-                else if (pf) issue_b(st + bst - nst, bs);
-                if (pf && st + ast == nst) use_tile(nx);
-                if (st + ast < nst) issue_a(st + ast, as);
-                else if (pf) issue_a(st + ast - nst, as);
+            if (st + depth < nst) {
+                issue(st + depth, rs);
+            } else if (pf) {
+                if (st + depth == nst) use_tile(nx);
+                issue(st + depth - nst, rs);
             }
+            rs = (rs + 1 == depth) ? 0 : rs + 1;
             if constexpr (W8)
                 read_b8(bn, raw, sc);
             else
@@ -1356,7 +1454,87 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
         // stores to drain.
         const int row0 = wm * (TM / 2) + 4 * g;
         if (more && !pf) setup(wnext);
-        if constexpr (M == Mode::GateUp) {
+        if constexpr (MOE_HEAVY_STAGED_EPI != 0 && M == Mode::Down) {
+            using S = Staging<M, TM, YF>;
+            const int tid = threadIdx.x;
+            for (int pass = 0; pass < S::kPasses; ++pass) {
+                // 1. this wave's results into the staging rows
+                if constexpr (M == Mode::GateUp) {
+#pragma unroll
+                    for (int i = 0; i < kRF; ++i)
+#pragma unroll
+                        for (int jp = 0; jp < 2; ++jp)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const float hv = swiglu(acc[i][2 * jp][r], acc[i][2 * jp + 1][r]);
+                                const uint32_t hi = f32_to_bf16_bits(hv);
+                                char* q = lds + (row0 + i * 16 + r) * S::kPitch +
+                                          (wn * 32 + jp * 16 + l16) * 2;
+                                *reinterpret_cast<uint16_t*>(q) = (uint16_t)hi;
+                                if (a.split_h)
+                                    *reinterpret_cast<uint16_t*>(q + TM * S::kPitch) =
+                                        (uint16_t)f32_to_bf16_bits(hv - bf16_bits_to_f32(hi));
+                            }
+                } else if constexpr (YF != kYF32) {
+                    const int odd = l16 & 1;
+#pragma unroll
+                    for (int i = 0; i < kRF; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            uint32_t w[2];
+                            y16_pairs<YF>(acc[i][j], l16, w[0], w[1]);
+#pragma unroll
+                            for (int r = 0; r < 2; ++r)
+                                *reinterpret_cast<uint32_t*>(
+                                    lds + (row0 + 2 * odd + i * 16 + r) * S::kPitch +
+                                    (wn * kWTN + j * 16 + l16 - odd) * 2) = w[r];
+                        }
+                } else {
+                    if (wm == pass) {
+#pragma unroll
+                        for (int i = 0; i < kRF; ++i)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                                for (int r = 0; r < 4; ++r)
+                                    *reinterpret_cast<float*>(
+                                        lds + (4 * g + i * 16 + r) * S::kPitch +
+                                        (wn * kWTN + j * 16 + l16) * 4) = acc[i][j][r];
+                    }
+                }
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+                ring_barrier();
+                // 2. whole-row 16-byte chunks read back and stored with
+                // 16-byte lane stores (1 KB of whole lines per instruction)
+                const int planes = (M == Mode::GateUp && a.split_h) ? 2 : 1;
+                const int prow0 = pass * S::kPassRows;
+                for (int pl = 0; pl < planes; ++pl) {
+#pragma unroll 4
+                    for (int q = 0; q < S::kIters; ++q) {
+                        const int c = q * kHeavyThreads + tid;
+                        const int row = c / S::kChunks, ch = c % S::kChunks;
+                        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
+                            lds + pl * TM * S::kPitch + row * S::kPitch + ch * 16);
+                        if (prow0 + row >= t_rows) continue;
+                        if constexpr (M == Mode::GateUp) {
+                            const int col = t_nb * (kTN / 2) + ch * 8;
+                            if (col < a.I)
+                                *reinterpret_cast<u32x4_t*>(
+                                    a.h + (size_t)(t_base + row) * hstride + pl * a.I + col) = v;
+                        } else {
+                            const int col = t_nb * kTN + ch * (16 / S::kElt);
+                            if (col < a.H) {
+                                char* yb = static_cast<char*>(a.y) +
+                                           ((size_t)(t_base + prow0 + row) * a.H + col) * S::kElt;
+                                __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(yb));
+                            }
+                        }
+                    }
+                }
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+                ring_barrier();  // staging read: the LDS is free for the next pass / tile
+            }
+        } else if constexpr (M == Mode::GateUp) {
             const int hc0 = t_nb * (kTN / 2) + wn * 32 + l16;
             uint16_t* hp = a.h + (size_t)(t_base + row0) * hstride + hc0;
             const bool full = t_rows == TM && t_nb * (kTN / 2) + kTN / 2 <= a.I;
@@ -1428,7 +1606,7 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
         if (!more) break;
         primed = pf;
         if (!pf) {
-            bs = as = 0;
+            as = bs = rs = 0;
             issue_first();
         }
     }
@@ -1468,19 +1646,31 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
 
     long long wi = wbeg + jx;
     while (wi < wend) {
-        const int tmi = tile_tmi(a, (int)(wi / nblk));
-        if (tmi == 0) {
-            // MXFP8 plans never hold 256-row tiles (the body would spill);
-            // the host rejects a forced 256 with MXFP8 weights.
-            if constexpr (BS == kBRecMx)
-                wi = wend;
+        int nb_i;
+        const int tmi = tile_tmi(a, item_tile(a, wi, nblk, nb_i));
+        if constexpr (BS == kBRecMx) {
+            // MXFP8 plans hold tiles of at most 192 rows (the larger bodies
+            // spill); the host rejects a forced 224 or 256 with MXFP8 weights.
+            if (tmi == 2)
+                wi = ffn_heavy_run<M, 192, YF, BS>(a, lds, wi, wend, nb_x, nblk);
+            else if (tmi == 3)
+                wi = ffn_heavy_run<M, 160, YF, BS>(a, lds, wi, wend, nb_x, nblk);
+            else if (tmi == 4)
+                wi = ffn_heavy_run<M, 128, YF, BS>(a, lds, wi, wend, nb_x, nblk);
             else
-                wi = ffn_heavy_run<M, kTileTM0, YF, BS>(a, lds, wi, wend, nb_x, nblk);
+                wi = wend;
+        } else {
+            if (tmi == 0)
+                wi = ffn_heavy_run<M, 256, YF, BS>(a, lds, wi, wend, nb_x, nblk);
+            else if (tmi == 1)
+                wi = ffn_heavy_run<M, 224, YF, BS>(a, lds, wi, wend, nb_x, nblk);
+            else if (tmi == 2)
+                wi = ffn_heavy_run<M, 192, YF, BS>(a, lds, wi, wend, nb_x, nblk);
+            else if (tmi == 3)
+                wi = ffn_heavy_run<M, 160, YF, BS>(a, lds, wi, wend, nb_x, nblk);
+            else
+                wi = ffn_heavy_run<M, 128, YF, BS>(a, lds, wi, wend, nb_x, nblk);
         }
-        else if (tmi == 1)
-            wi = ffn_heavy_run<M, kTileTM1, YF, BS>(a, lds, wi, wend, nb_x, nblk);
-        else
-            wi = ffn_heavy_run<M, kTileTM2, YF, BS>(a, lds, wi, wend, nb_x, nblk);
     }
 }
 
@@ -1596,8 +1786,7 @@ hipError_t launch_heavy(const FfnArgs& a, int ncols, hipStream_t st) {
     if (a.dense_rows <= 0) return hipSuccess;
     const long long tiles = (a.dense_rows + a.dense_tm - 1) / a.dense_tm;
     const int grid = heavy_grid(tiles * nblk, a.num_cu);
-    if (a.dense_tm != kTileTM0 && a.dense_tm != kTileTM1 && a.dense_tm != kTileTM2)
-        return hipErrorInvalidValue;
+    if (!valid_tile_height(a.dense_tm)) return hipErrorInvalidValue;
     ffn_heavy_kernel<M, YF, kBRowMajor><<<grid, kHeavyThreads, 0, st>>>(a);  // dense groups
     return hipGetLastError();
 }

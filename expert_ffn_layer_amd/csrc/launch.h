@@ -79,35 +79,43 @@ constexpr int kLightAdaptive = -1;
 inline __host__ __device__ int adaptive_light_max(long long rows, long long touched) {
     return rows <= (long long)MOE_LIGHT_MEAN_ROWS * touched ? kLightRowsMax : MOE_LIGHT_TAIL_ROWS;
 }
-// Heavy tiles are 256 columns wide and 256, 192 or 128 rows high.  Each
-// expert's rows are cut into the tiles of least estimated time, sum over its
-// tiles of tm * cost(tm), cost = relative time per tile row (x1000, measured:
-// smaller tiles re-read more weights per row): all of one height, or 256-row
-// tiles and one smaller last tile for the remainder.
+// Heavy tiles are 256 columns wide and 128..256 rows high in steps of 32.
+// An expert's rows are cut into equal tiles of the height with the least
+// estimated time, ntiles * tm * cost(tm), cost = relative time per tile row
+// (x1000; smaller tiles re-read more weights per row).  Equal heights keep
+// the row tiles that share an expert's weights in step, so the weights are
+// fetched once (a short last tile would run ahead of the others and drift
+// out of the L2 window).
+#ifndef MOE_TILE_COST_224
+#define MOE_TILE_COST_224 1020
+#endif
 #ifndef MOE_TILE_COST_192
 #define MOE_TILE_COST_192 1060
+#endif
+#ifndef MOE_TILE_COST_160
+#define MOE_TILE_COST_160 1130
 #endif
 #ifndef MOE_TILE_COST_128
 #define MOE_TILE_COST_128 1250
 #endif
-constexpr int kTileTM0 = 256, kTileTM1 = 192, kTileTM2 = 128;
-constexpr int kTileCost0 = 1000, kTileCost1 = MOE_TILE_COST_192, kTileCost2 = MOE_TILE_COST_128;
-constexpr int kHeavyBMMin = kTileTM2;  // sizes the plan's tile list
-// Index (0, 1, 2) of the cheapest height given the tile counts at each.
-inline __host__ __device__ int pick_tile_height(long long t0, long long t1, long long t2) {
-    const long long c0 = t0 * kTileTM0 * kTileCost0, c1 = t1 * kTileTM1 * kTileCost1,
-                    c2 = t2 * kTileTM2 * kTileCost2;
-    return (c0 <= c1 && c0 <= c2) ? 0 : (c1 <= c2 ? 1 : 2);
-}
-inline __host__ __device__ int tile_height(int idx) {
-    return idx == 0 ? kTileTM0 : (idx == 1 ? kTileTM1 : kTileTM2);
+constexpr int kTileTMMax = 256, kTileTMStep = 32, kTileTMMin = 128;
+constexpr int kNumTileHeights = (kTileTMMax - kTileTMMin) / kTileTMStep + 1;  // 5
+constexpr int kHeavyBMMin = kTileTMMin;  // sizes the plan's tile list
+// Height index i: height 256 - 32 i.
+inline __host__ __device__ int tile_height(int idx) { return kTileTMMax - kTileTMStep * idx; }
+inline __host__ __device__ int tile_tm_index(int tm) { return (kTileTMMax - tm) / kTileTMStep; }
+inline __host__ __device__ bool valid_tile_height(int tm) {
+    return tm >= kTileTMMin && tm <= kTileTMMax && tm % kTileTMStep == 0;
 }
 inline __host__ __device__ int tile_cost(int idx) {
-    return idx == 0 ? kTileCost0 : (idx == 1 ? kTileCost1 : kTileCost2);
+    return idx == 0 ? 1000
+                    : (idx == 1 ? MOE_TILE_COST_224
+                                : (idx == 2 ? MOE_TILE_COST_192
+                                            : (idx == 3 ? MOE_TILE_COST_160 : MOE_TILE_COST_128)));
 }
 // Plan layout (int32): [0] n_light, [1] n_tiles, [2] forced tile height or 0,
 // [16 ..16+E) light expert ids, [16+E ..) heavy tiles as (expert, first row
-// | height index << kTileTmShift) pairs; height index 0, 1, 2 = kTileTM0/1/2.
+// | height index << kTileTmShift) pairs (height 256 - 32 * index).
 constexpr int kPlanHeader = 16;
 // MI355X: 8 XCDs, workgroups dispatched round-robin.  The heavy work list is
 // cut into kXcds contiguous slices of about equal cost; plan[kPlanXcdBounds
@@ -120,12 +128,9 @@ constexpr int kPlanXcdBounds = 3;
 static_assert(kPlanXcdBounds + kXcds + 1 <= kPlanHeader, "plan header");
 constexpr int kTileTmShift = 29;
 constexpr int kTileRowMask = (1 << kTileTmShift) - 1;
-inline __host__ __device__ int tile_tm_index(int tm) {
-    return tm == kTileTM0 ? 0 : (tm == kTileTM1 ? 1 : 2);
-}
-// Relative time of one tile of height index tmi (tm * cost(tm) / 16000).
+// Relative time of one tile of height index tmi (about tm * cost(tm) / 16000).
 inline __host__ __device__ int tile_cost_units(int tmi) {
-    return tmi == 0 ? 16 : (tmi == 1 ? 13 : 10);
+    return (tile_height(tmi) * tile_cost(tmi) + 8000) / 16000;
 }
 inline __host__ __device__ int tiles_cost_units(int nt, int main_tmi, int last_tmi) {
     return nt > 0 ? (nt - 1) * tile_cost_units(main_tmi) + tile_cost_units(last_tmi) : 0;
@@ -148,11 +153,12 @@ inline __host__ __device__ void xcd_bounds(int32_t* plan, int t0, int nt, int ma
         plan[kPlanXcdBounds + x] = t0 + i + 1;
     }
 }
-// Tiles of an expert with n heavy rows: ntiles tiles, all main_tmi high but
-// the last, last_tmi high (first rows 0, tm, 2 tm, ... with tm of main_tmi).
-// force_tm (128, 192, 256) puts every tile at that height; a negative
-// force_tm = -m chooses as with 0 among the heights up to m (kTileMaxMx for
-// MXFP8 weights, whose 256-row tile body does not fit the register file).
+// Tiles of an expert with n heavy rows: ntiles tiles of one height (index
+// main_tmi; last_tmi, the last tile's, is the same), first rows 0, tm, 2 tm,
+// ...; the height with the least ntiles * tm * cost(tm).  force_tm (128 ..
+// 256) puts every tile at that height; a negative force_tm = -m chooses as
+// with 0 among the heights up to m (kTileMaxMx for MXFP8 weights, whose
+// larger tile bodies do not fit the register file).
 constexpr int kTileMaxMx = -192;
 inline __host__ __device__ void tile_split(int n, int force_tm, int& ntiles, int& main_tmi,
                                            int& last_tmi) {
@@ -163,7 +169,9 @@ inline __host__ __device__ void tile_split(int n, int force_tm, int& ntiles, int
     }
     const int i0 = force_tm < 0 ? tile_tm_index(-force_tm) : 0;
     long long best = -1;
-    for (int i = i0; i < 3; ++i) {
+    ntiles = 0;
+    main_tmi = last_tmi = i0;
+    for (int i = i0; i < kNumTileHeights; ++i) {
         const int tm = tile_height(i);
         const int k = (n + tm - 1) / tm;
         const long long c = (long long)k * tm * tile_cost(i);
@@ -171,17 +179,6 @@ inline __host__ __device__ void tile_split(int n, int force_tm, int& ntiles, int
             best = c;
             ntiles = k;
             main_tmi = last_tmi = i;
-        }
-    }
-    const int q = n / kTileTM0, rem = n - q * kTileTM0;
-    if (i0 == 0 && q > 0 && rem > 0) {
-        const int r = rem <= kTileTM2 ? 2 : (rem <= kTileTM1 ? 1 : 0);
-        const long long c =
-            (long long)q * kTileTM0 * kTileCost0 + (long long)tile_height(r) * tile_cost(r);
-        if (c < best) {
-            ntiles = q + 1;
-            main_tmi = 0;
-            last_tmi = r;
         }
     }
 }

@@ -86,15 +86,14 @@ int check_shape(const moe_shape* s) {
     if (s->renorm != 0 && s->renorm != 1) return fail(MOE_ERR_UNSUPPORTED, "renorm must be 0 or 1");
     if (s->light_max_rows < -1 || s->light_max_rows > moe::kLightRowsMax)
         return fail(MOE_ERR_UNSUPPORTED, "light_max_rows must be -1 or in [0, 64]");
-    if (s->heavy_tile_rows != 0 && s->heavy_tile_rows != moe::kTileTM0 &&
-        s->heavy_tile_rows != moe::kTileTM1 && s->heavy_tile_rows != moe::kTileTM2)
-        return fail(MOE_ERR_UNSUPPORTED, "heavy_tile_rows must be 0, 128, 192 or 256");
+    if (s->heavy_tile_rows != 0 && !moe::valid_tile_height(s->heavy_tile_rows))
+        return fail(MOE_ERR_UNSUPPORTED, "heavy_tile_rows must be 0, 128, 160, 192, 224 or 256");
     if (s->y_bf16 != 0 && s->y_bf16 != 1) return fail(MOE_ERR_UNSUPPORTED, "y_bf16 must be 0 or 1");
     if (s->y_fp16 != 0 && s->y_fp16 != 1) return fail(MOE_ERR_UNSUPPORTED, "y_fp16 must be 0 or 1");
     if (s->y_bf16 && s->y_fp16) return fail(MOE_ERR_UNSUPPORTED, "y_bf16 and y_fp16 are exclusive");
     if (s->w_mxfp8 != 0 && s->w_mxfp8 != 1)
         return fail(MOE_ERR_UNSUPPORTED, "w_mxfp8 must be 0 or 1");
-    if (s->w_mxfp8 && s->heavy_tile_rows == moe::kTileTM0)
+    if (s->w_mxfp8 && s->heavy_tile_rows > -moe::kTileMaxMx)
         return fail(MOE_ERR_UNSUPPORTED, "MXFP8 heavy tiles are at most 192 rows");
     return MOE_OK;
 }

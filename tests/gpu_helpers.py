@@ -26,9 +26,12 @@ REL_L2 = 5e-3
 NEAR_TIE = 1e-6
 # Routing weights / probabilities: the GPU sums the H-term logits in another
 # fp32 order than the oracle (MFMA blocks, split-K partials), so logits
-# differ by up to a few 1e-5 at H = 4096..8192 and each renormalised weight
-# moves by about 2*w*|dlogit|.
-W_RTOL = 1e-4
+# differ by up to about 1e-5 at H = 4096..8192 and each renormalised weight
+# moves by about 2*w*|dlogit|.  Measured largest relative weight error on the
+# clear tokens of the full-size layers: 2.3e-5 (Ling-like, H = 8192), 1.4e-5
+# (prefill), 9e-6 (skew), 3.3e-6 (decode); 0 on the small layers.  The bound
+# is twice the largest.
+W_RTOL = 5e-5
 W_ATOL = 1e-6
 DEV = "cuda"
 

@@ -229,7 +229,7 @@ def test_layer_bitwise_vs_dequantised_bf16(oracle_lib, name, y_bf16):
 
 
 @pytest.mark.parametrize("name", ["heavy_ragged", "mixed", "i_tail", "hot", "shared"])
-@pytest.mark.parametrize("lm,tm", [(0, 0), (0, 128), (0, 192), (64, 0), (16, 128)])
+@pytest.mark.parametrize("lm,tm", [(0, 0), (0, 128), (0, 160), (0, 192), (64, 0), (16, 128)])
 def test_layer_bitwise_paths(oracle_lib, name, lm, tm):
     """Every MXFP8 path -- heavy tiles of each height, the light loop, and
     splits between the two -- against the bf16 layer on the dequantised

@@ -93,10 +93,10 @@ def test_tile_heights_bitwise(oracle_lib, y_bf16):
     print(f"[case] tile heights y_bf16={y_bf16}", flush=True)
     lay = layer_on_gpu(TILES)
     outs = {}
-    for tm in (0, 256, 192, 128):
+    for tm in (0, 256, 224, 192, 160, 128):
         g = gh.gpu_forward(lay, light_max_rows=0, heavy_tile_rows=tm, y_bf16=y_bf16)
         outs[tm] = g["out"].view(np.int32)
-    for tm in (256, 192, 128):
+    for tm in (256, 224, 192, 160, 128):
         assert np.array_equal(outs[tm], outs[0]), f"tile height {tm} differs"
     rep = gh.check_layer(oracle_lib, lay, light_max_rows=0, heavy_tile_rows=192, y_bf16=y_bf16)
     log(f"tiles/192/bf16y={y_bf16}", rep)
@@ -129,7 +129,7 @@ def test_default_light_rule_bitwise(oracle_lib, T, E, k, zipf, lm):
     log(f"rule{T}_{E}", rep)
 
 
-@pytest.mark.parametrize("tm", [128, 192, 256])
+@pytest.mark.parametrize("tm", [128, 160, 192, 224, 256])
 def test_forward_heavy_ragged_heights(oracle_lib, tm):
     print(f"[case] heavy_ragged tm={tm}", flush=True)
     rep = gh.check_layer(oracle_lib, layer_on_gpu(SMALL["heavy_ragged"]), heavy_tile_rows=tm)

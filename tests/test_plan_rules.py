@@ -12,8 +12,9 @@ import pytest
 from expert_ffn_layer_amd import build as B
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-COST = {256: 1000, 192: 1060, 128: 1250}
-UNITS = {256: 16, 192: 13, 128: 10}
+COST = {256: 1000, 224: 1020, 192: 1060, 160: 1130, 128: 1250}
+HEIGHTS = (256, 224, 192, 160, 128)
+UNITS = {tm: (tm * COST[tm] + 8000) // 16000 for tm in HEIGHTS}
 
 
 @pytest.fixture(scope="module")
@@ -26,38 +27,36 @@ def output(tmp_path_factory):
     return subprocess.run([exe], check=True, capture_output=True, text=True).stdout.splitlines()
 
 
-def candidates(n):
-    out = []
-    for tm in (256, 192, 128):
-        k = -(-n // tm)
-        out.append((k * tm * COST[tm], k, tm, tm))
-    q, rem = divmod(n, 256)
-    if q and rem:
-        r = 128 if rem <= 128 else (192 if rem <= 192 else 256)
-        out.append((q * 256 * COST[256] + r * COST[r], q + 1, 256, r))
-    return out
+def candidates(n, heights=HEIGHTS):
+    """(cost, ntiles, height) of cutting n rows into equal tiles of each height."""
+    return [(-(-n // tm) * tm * COST[tm], -(-n // tm), tm) for tm in heights]
 
 
 def test_tile_split(output):
+    """One height per expert (the tiles that share its weights stay in step),
+    the cheapest of the five, no tile to spare."""
     rows = [l.split() for l in output if l[0].isdigit()]
     assert len(rows) == 3000
     for n, nt, mt, lt, cost in (map(int, r) for r in rows):
-        covered = (nt - 1) * mt + lt
-        assert covered >= n > covered - lt, (n, nt, mt, lt)  # no tile to spare
-        best = min(c[0] for c in candidates(n))
-        assert (nt - 1) * mt * COST[mt] + lt * COST[lt] == best, n
-        assert cost == (nt - 1) * UNITS[mt] + UNITS[lt]
+        assert mt == lt and mt in HEIGHTS
+        assert nt * mt >= n > (nt - 1) * mt, (n, nt, mt)  # no tile to spare
+        assert nt * mt * COST[mt] == min(c[0] for c in candidates(n)), n
+        assert cost == nt * UNITS[mt]
+    # the rows of an expert of 640 rows (long prefill) and of 160 (prefill)
+    # go in equal tiles with little padding
+    by_n = {int(r[0]): (int(r[1]), int(r[2])) for r in rows}
+    assert by_n[640] == (3, 224) and by_n[160] == (1, 160)
 
 
 def test_tile_split_max_192(output):
     """With heights limited to 192 (MXFP8 weights): one height per expert,
-    the cheaper of all-192 and all-128, no 256-row tile, no tile to spare."""
+    the cheapest of 192, 160 and 128, no taller tile, no tile to spare."""
     rows = [list(map(int, l.split()[1:])) for l in output if l.startswith("mx ")]
     assert len(rows) == 1500
     for n, nt, mt, lt in rows:
-        assert mt == lt and mt in (128, 192)
+        assert mt == lt and mt in (128, 160, 192)
         assert nt * mt >= n > (nt - 1) * mt
-        best = min(-(-n // tm) * tm * COST[tm] for tm in (192, 128))
+        best = min(c[0] for c in candidates(n, (192, 160, 128)))
         assert nt * mt * COST[mt] == best, n
 
 
