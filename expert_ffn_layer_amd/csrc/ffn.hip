@@ -63,6 +63,7 @@ constexpr int kThreads = 256;
 // heavy experts' row tiles (ascending id, then first row).
 __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restrict__ offsets,
                                                         int E, int light_max, int force_tm,
+                                                        int round_tiles,
                                                         int32_t* __restrict__ plan) {
     __shared__ int wl[16], wt[16], wcs[16], wtouch[16];
     const int e = threadIdx.x;
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restric
         wcs[wave] = ic;
     }
     __syncthreads();
-    int bl = 0, bt = 0, bc = 0, ctot = 0;
+    int bl = 0, bt = 0, bc = 0, ctot = 0, ttot = 0;
     for (int w = 0; w < nwave; ++w) {
         if (w < wave) {
             bl += wl[w];
@@ -110,9 +111,10 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restric
             bc += wcs[w];
         }
         ctot += wcs[w];
+        ttot += wt[w];
     }
     const int el = bl + il - is_light, et = bt + it - nt;
-    xcd_bounds(plan, et, nt, main_tmi, last_tmi, bc + ic - cost, ctot);
+    xcd_bounds(plan, et, nt, main_tmi, last_tmi, bc + ic - cost, ctot, round_tiles, ttot);
     if (is_light) plan[kPlanHeader + el] = e;
     int32_t* tiles = plan + kPlanHeader + E;
     const int tm = tile_height(main_tmi);
@@ -1838,9 +1840,9 @@ hipError_t launch_pack_weights(const uint16_t* w_gu, const uint16_t* w_dn, int E
 }
 
 hipError_t launch_ffn_plan(const int32_t* offsets, int E, int light_max, int force_tm,
-                           int32_t* plan, hipStream_t st) {
+                           int round_tiles, int32_t* plan, hipStream_t st) {
     prof_begin(K_FFN_PLAN, st);
-    ffn_plan_kernel<<<1, 1024, 0, st>>>(offsets, E, light_max, force_tm, plan);
+    ffn_plan_kernel<<<1, 1024, 0, st>>>(offsets, E, light_max, force_tm, round_tiles, plan);
     prof_end(K_FFN_PLAN, st);
     return hipGetLastError();
 }

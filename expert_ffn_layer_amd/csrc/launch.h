@@ -55,7 +55,7 @@ constexpr int kPermChunk = 4096;  // assignments per permute block
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* chunk_counts,
                           int nchunks, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
                           int32_t* inv_pos, int32_t* plan, int light_max, int force_tm,
-                          hipStream_t st);
+                          int round_tiles, hipStream_t st);
 
 // ---- grouped FFN --------------------------------------------------------
 constexpr int kLightRowsMax = 64;  // up to four 16-row MFMA sub-tiles
@@ -99,6 +99,7 @@ inline __host__ __device__ int adaptive_light_max(long long rows, long long touc
 #define MOE_TILE_COST_128 1250
 #endif
 constexpr int kTileTMMax = 256, kTileTMStep = 32, kTileTMMin = 128;
+constexpr int kTileN = 256;  // heavy tile width (output columns; gate|up: 128 gate + 128 up rows)
 constexpr int kNumTileHeights = (kTileTMMax - kTileTMMin) / kTileTMStep + 1;  // 5
 constexpr int kHeavyBMMin = kTileTMMin;  // sizes the plan's tile list
 // Height index i: height 256 - 32 i.
@@ -137,9 +138,16 @@ inline __host__ __device__ int tiles_cost_units(int nt, int main_tmi, int last_t
 }
 // The XCD slice bounds that fall in one expert's tiles [t0, t0 + nt), whose
 // cost before them is cb out of a total C: slice x - 1 ends after the first
-// tile at which the cumulative cost reaches ceil(x C / kXcds).
+// tile at which the cumulative cost reaches ceil(x C / kXcds), rounded to the
+// nearest multiple of round_tiles (and at most the tile count ttot).  The
+// blocks of a slice take its work items round-robin, so a slice whose items
+// are a whole number of rounds of its blocks leaves none of them a short
+// extra round: round_tiles is the tiles per round of the GEMM with the fewest
+// N blocks (measured on the prefill layer: slices of 504..520 items gave
+// some blocks 17 rounds of 16; rounded, every block runs 16).
 inline __host__ __device__ void xcd_bounds(int32_t* plan, int t0, int nt, int main_tmi,
-                                           int last_tmi, long long cb, long long C) {
+                                           int last_tmi, long long cb, long long C,
+                                           int round_tiles, int ttot) {
     const long long ce = cb + tiles_cost_units(nt, main_tmi, last_tmi);
     for (int x = 1; x < kXcds; ++x) {
         const long long target = (C * x + kXcds - 1) / kXcds;
@@ -150,7 +158,9 @@ inline __host__ __device__ void xcd_bounds(int32_t* plan, int t0, int nt, int ma
             cum += tile_cost_units(i + 1 < nt ? main_tmi : last_tmi);
             if (cum >= target) break;
         }
-        plan[kPlanXcdBounds + x] = t0 + i + 1;
+        int b = t0 + i + 1;
+        if (round_tiles > 1) b = (b + round_tiles / 2) / round_tiles * round_tiles;
+        plan[kPlanXcdBounds + x] = b < ttot ? b : ttot;
     }
 }
 // Tiles of an expert with n heavy rows: ntiles tiles of one height (index
@@ -187,8 +197,18 @@ int max_heavy_tiles(long long A, int E, int light_max);
 int dense_tile_height(int rows);  // tile height for a dense group of `rows` rows
 
 // force_tm: 0 = pick the heavy tile height from the counts, else that height.
+// round_tiles: multiple of tiles the XCD slice bounds are rounded to (xcd_bounds).
 hipError_t launch_ffn_plan(const int32_t* offsets, int E, int light_max, int force_tm,
-                           int32_t* plan, hipStream_t st);
+                           int round_tiles, int32_t* plan, hipStream_t st);
+// Tiles per round of a heavy GEMM's XCD slice for `num_cu` CUs (one block per
+// CU, kXcds slices) with N blocks of nblk_gu (gate|up) and nblk_dn (down): the
+// rounding of the slice bounds; 1 when it does not divide evenly.
+inline int slice_round_tiles(int num_cu, int nblk_gu, int nblk_dn) {
+    const int per_slice = num_cu / kXcds;
+    const int nb = nblk_gu < nblk_dn ? nblk_gu : nblk_dn;
+    if (nb <= 0 || per_slice <= 0 || per_slice % nb) return 1;
+    return per_slice / nb;
+}
 
 struct FfnArgs {
     const uint16_t* x;           // [T,H]

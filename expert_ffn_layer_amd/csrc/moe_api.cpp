@@ -217,6 +217,17 @@ int run_router(const moe_shape* s, const Layout& L, const uint16_t* x, const flo
     return MOE_OK;
 }
 
+// Tiles per round of the heavy GEMMs' XCD slices on this device (see
+// moe::xcd_bounds).
+int plan_round_tiles(const moe_shape* s, int* out) {
+    int ncu = 0;
+    if (int rc = device_cu_count(&ncu)) return rc;
+    const int nblk_gu = (2 * s->I + moe::kTileN - 1) / moe::kTileN;
+    const int nblk_dn = (s->H + moe::kTileN - 1) / moe::kTileN;
+    *out = moe::slice_round_tiles(ncu, nblk_gu, nblk_dn);
+    return MOE_OK;
+}
+
 // Returns through *plan_ready whether the permute also wrote the FFN plan
 // (single-block path); then run_ffn skips its plan kernel.
 int run_permute(const moe_shape* s, const Layout& L, const int32_t* ids, int32_t* counts,
@@ -224,9 +235,12 @@ int run_permute(const moe_shape* s, const Layout& L, const int32_t* ids, int32_t
                 bool* plan_ready = nullptr) {
     const bool small = (long long)s->T * s->k <= moe::kPermChunk;
     int32_t* plan = (plan_ready && small) ? at<int32_t>(ws, L.plan) : nullptr;
+    int round_tiles = 1;
+    if (plan)
+        if (int rc = plan_round_tiles(s, &round_tiles)) return rc;
     HIP_TRY(moe::launch_permute(ids, s->T, s->k, s->E, at<int32_t>(ws, L.chunk), L.nchunks,
                                 counts, offsets, sorted, inv, plan, L.light_max,
-                                plan_force_tm(s), st),
+                                plan_force_tm(s), round_tiles, st),
             "permute");
     if (plan_ready) *plan_ready = plan != nullptr;
     return MOE_OK;
@@ -242,9 +256,13 @@ int run_ffn(const moe_shape* s, const Layout& L, const uint16_t* x, const int32_
     int ncu = 0;
     if (int rc = device_cu_count(&ncu)) return rc;
     int32_t* plan = at<int32_t>(ws, L.plan);
-    if (!plan_ready)
-        HIP_TRY(moe::launch_ffn_plan(offsets, s->E, L.light_max, plan_force_tm(s), plan, st),
+    if (!plan_ready) {
+        int round_tiles = 1;
+        if (int rc = plan_round_tiles(s, &round_tiles)) return rc;
+        HIP_TRY(moe::launch_ffn_plan(offsets, s->E, L.light_max, plan_force_tm(s), round_tiles,
+                                     plan, st),
                 "ffn plan");
+    }
     moe::FfnArgs a{};
     a.x = x;
     a.sorted_ids = sorted;

@@ -189,7 +189,8 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(
 __global__ __launch_bounds__(kThreads) void perm_small_kernel(
     const int32_t* __restrict__ ids, int A, int k, int E, int nbits,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_ids,
-    int32_t* __restrict__ inv_pos, int32_t* __restrict__ plan, int light_max, int force_tm) {
+    int32_t* __restrict__ inv_pos, int32_t* __restrict__ plan, int light_max, int force_tm,
+    int round_tiles) {
     extern __shared__ int32_t sm[];  // wcnt[4][E], off[E]
     __shared__ int32_t wsum[4];
     int32_t* wcnt = sm;
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void perm_small_kernel(
     for (int j = 0; j < 4; ++j) {
         const int e = 4 * threadIdx.x + j;
         if (lj[j]) plan[kPlanHeader + lrun++] = e;
-        xcd_bounds(plan, trun, tj[j], tmain[j], tlast[j], crun, ctot);
+        xcd_bounds(plan, trun, tj[j], tmain[j], tlast[j], crun, ctot, round_tiles, ttot);
         crun += tiles_cost_units(tj[j], tmain[j], tlast[j]);
         const int tm = tile_height(tmain[j]);
         for (int i = 0; i < tj[j]; ++i, ++trun) {
@@ -312,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void perm_small_kernel(
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* chunk_counts,
                           int nchunks, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
                           int32_t* inv_pos, int32_t* plan, int light_max, int force_tm,
-                          hipStream_t st) {
+                          int round_tiles, hipStream_t st) {
     const long long A = (long long)T * k;
     int nbits = 1;
     while ((1 << nbits) < E) ++nbits;
@@ -320,7 +321,7 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* chun
         prof_begin(K_PERM_SMALL, st);
         perm_small_kernel<<<1, kThreads, (kWavesPerBlock + 1) * E * sizeof(int32_t), st>>>(
             ids, (int)A, k, E, nbits, counts, offsets, sorted_ids, inv_pos, plan, light_max,
-            force_tm);
+            force_tm, round_tiles);
         prof_end(K_PERM_SMALL, st);
         return hipGetLastError();
     }

@@ -26,34 +26,42 @@ int main() {
         C += moe::tiles_cost_units(nt, mt, lt);
         T += nt;
     }
-    int32_t plan[moe::kPlanHeader] = {0};
-    long long cb = 0;
-    int t0 = 0;
-    for (int n : counts) {
-        int nt, mt, lt;
-        moe::tile_split(n, 0, nt, mt, lt);
-        moe::xcd_bounds(plan, t0, nt, mt, lt, cb, C);
-        cb += moe::tiles_cost_units(nt, mt, lt);
-        t0 += nt;
-    }
-    plan[moe::kPlanXcdBounds] = 0;
-    plan[moe::kPlanXcdBounds + moe::kXcds] = T;
     std::vector<int> tile_cost;
     for (int n : counts) {
         int nt, mt, lt;
         moe::tile_split(n, 0, nt, mt, lt);
         for (int i = 0; i < nt; ++i) tile_cost.push_back(moe::tile_cost_units(i + 1 < nt ? mt : lt));
     }
-    std::printf("xcd %lld %d", C, T);
-    for (int x = 0; x <= moe::kXcds; ++x) std::printf(" %d", plan[moe::kPlanXcdBounds + x]);
-    std::printf("\nslices");
-    for (int x = 0; x < moe::kXcds; ++x) {
-        long long c = 0;
-        for (int t = plan[moe::kPlanXcdBounds + x]; t < plan[moe::kPlanXcdBounds + x + 1]; ++t)
-            c += tile_cost[t];
-        std::printf(" %lld", c);
+    // slice bounds without rounding ("xcd"/"slices") and rounded to 4 tiles
+    // ("xcdr"/"slicesr")
+    for (int round_tiles : {1, 4}) {
+        int32_t plan[moe::kPlanHeader] = {0};
+        long long cb = 0;
+        int t0 = 0;
+        for (int n : counts) {
+            int nt, mt, lt;
+            moe::tile_split(n, 0, nt, mt, lt);
+            moe::xcd_bounds(plan, t0, nt, mt, lt, cb, C, round_tiles, T);
+            cb += moe::tiles_cost_units(nt, mt, lt);
+            t0 += nt;
+        }
+        plan[moe::kPlanXcdBounds] = 0;
+        plan[moe::kPlanXcdBounds + moe::kXcds] = T;
+        const char* tag = round_tiles > 1 ? "r" : "";
+        std::printf("xcd%s %lld %d", tag, C, T);
+        for (int x = 0; x <= moe::kXcds; ++x) std::printf(" %d", plan[moe::kPlanXcdBounds + x]);
+        std::printf("\nslices%s", tag);
+        for (int x = 0; x < moe::kXcds; ++x) {
+            long long c = 0;
+            for (int t = plan[moe::kPlanXcdBounds + x]; t < plan[moe::kPlanXcdBounds + x + 1]; ++t)
+                c += tile_cost[t];
+            std::printf(" %lld", c);
+        }
+        std::printf("\n");
     }
-    std::printf("\n");
+    std::printf("round %d %d %d %d\n", moe::slice_round_tiles(256, 8, 16),
+                moe::slice_round_tiles(256, 16, 32), moe::slice_round_tiles(256, 3, 16),
+                moe::slice_round_tiles(304, 8, 16));
     // heights limited to 192 (MXFP8 weights): prefix "mx"
     for (int n = 1; n <= 1500; ++n) {
         int nt = 0, mt = 0, lt = 0;

@@ -67,9 +67,27 @@ def test_xcd_bounds(output):
     assert len(b) == 9 and b[0] == 0 and b[-1] == T and b == sorted(b)
     # each slice ends at the first tile where the running cost reaches its
     # share, so every slice is within one tile (at most 16 units) of C/8
-    sl = list(map(int, [l for l in output if l.startswith("slices")][0].split()[1:]))
+    sl = list(map(int, [l for l in output if l.startswith("slices ")][0].split()[1:]))
     assert sum(sl) == C
     assert all(abs(c - C / 8) <= 16 for c in sl), sl
+
+
+def test_xcd_bounds_rounded(output):
+    """Bounds rounded to whole rounds of 4 tiles: monotone, multiples of 4
+    (but the last), each within 2 tiles of the unrounded one, so every slice
+    stays within 5 tiles (80 units) of C/8."""
+    un = list(map(int, [l for l in output if l.startswith("xcd ")][0].split()[3:]))
+    line = [l for l in output if l.startswith("xcdr ")][0].split()
+    C, T = int(line[1]), int(line[2])
+    b = list(map(int, line[3:]))
+    assert len(b) == 9 and b[0] == 0 and b[-1] == T and b == sorted(b)
+    assert all(x % 4 == 0 for x in b[:-1])
+    assert all(abs(x - y) <= 2 for x, y in zip(b, un))
+    sl = list(map(int, [l for l in output if l.startswith("slicesr ")][0].split()[1:]))
+    assert sum(sl) == C and all(abs(c - C / 8) <= 80 for c in sl), sl
+    # tiles per round: 256 CUs / 8 XCDs = 32 blocks per slice over the N blocks
+    # of the narrower GEMM (8 -> 4 tiles, 16 -> 2), 1 where it does not divide
+    assert [l for l in output if l.startswith("round ")][0].split()[1:] == ["4", "2", "1", "1"]
 
 
 def test_light_rule(output):
