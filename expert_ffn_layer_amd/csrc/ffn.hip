@@ -135,10 +135,7 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int32_t* __restric
 
 // Tunables of the light loops (compile-time; the defaults are the measured best).
 #ifndef MOE_LIGHT_GU_U
-#define MOE_LIGHT_GU_U 8        // K steps of 32 in flight per wave (gate|up)
-#endif
-#ifndef MOE_LIGHT_GU_TILES
-#define MOE_LIGHT_GU_TILES 1    // 16-column MFMA tiles per wave (8 h-columns each)
+#define MOE_LIGHT_GU_U 4        // K steps of 32 in flight per wave (gate|up: 2 loads each)
 #endif
 #ifndef MOE_LIGHT_GU_BPC
 #define MOE_LIGHT_GU_BPC 8      // blocks per CU in the grid
@@ -167,6 +164,17 @@ __device__ __forceinline__ bf16x8_t load_weights(const uint16_t* p) {
                                   __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
     else
         return load_bf16x8(p);
+}
+
+// Offset of 32-wide K step kb from a light lane's first weight: along the
+// weight row, or, in the packed records, chunk kb % 2 of the operand's
+// 16-row block in record kb / 2.
+template <bool kRecords>
+__device__ __forceinline__ size_t light_koff(int kb) {
+    if constexpr (kRecords)
+        return (size_t)(kb >> 1) * kRecElems + (size_t)(kb & 1) * kRecChunkElems;
+    else
+        return (size_t)kb * 32;
 }
 
 // Row sub-tiles of the light loop: experts with up to 16 rows run one 16-row
@@ -237,27 +245,25 @@ __device__ __forceinline__ void light_store_y16(const FfnArgs& a, const floatx4_
 }
 
 // ------------------------------------------------------- light: gate|up
-// One wave: MT row sub-tiles x NTILE column tiles of one expert, K = H.
-// Tile t pairs gate rows i0+8t.. and the matching up rows, so lanes
-// l16 < 8 end with g and lanes l16 >= 8 with u of the same h column.
-template <int MT, int U, int NTILE, bool NTL, bool PK>
+// One wave: MT row sub-tiles x 16 h columns i0..i0+15 of one expert, K = H:
+// one MFMA tile over the 16 gate rows and one over the matching 16 up rows,
+// so a lane ends with g and u of the same h column.
+template <int MT, int U, bool NTL, bool PK>
 __device__ __forceinline__ void gateup_light_rows(const FfnArgs& a, int e, int r0, int n, int i0,
                                                   int l16, int g) {
     const int nk = a.H / 32;
-    const uint16_t* Bp;
-    size_t bstride, kstride;
+    const uint16_t* Bg;  // gate operand; the up operand is `uoff` further
+    size_t uoff;
     if constexpr (PK) {
-        // packed: the tile's 16 rows x 32 K of each K step are one 1 KB chunk
-        // in lane order, and a column tile's chunks are consecutive
+        // record chunks: the gate rows of h columns i0.. are 16-row block
+        // 2 (i0 % 128) / 16 of tile i0 / 128, their up rows the next block
         const int lane = g * 16 + l16;
-        Bp = a.pk_gu + ((size_t)e * packed_gu_groups(a.I) + i0 / 8) * nk * 512 + lane * 8;
-        bstride = (size_t)nk * 512;
-        kstride = 512;
+        const size_t rec = ((size_t)e * rec_tiles(2 * a.I) + (i0 >> 7)) * mx_chunks(a.H);
+        Bg = a.hr_gu + rec * kRecElems + (size_t)(((i0 & 127) >> 4) * 2) * kRecBlockElems + lane * 8;
+        uoff = kRecBlockElems;
     } else {
-        const int wrow = (l16 < 8) ? (i0 + l16) : (a.I + i0 + l16 - 8);
-        Bp = a.w_gu + ((size_t)e * 2 * a.I + wrow) * a.H + 8 * g;
-        bstride = (size_t)8 * a.H;  // next column tile: 8 rows further
-        kstride = 32;
+        Bg = a.w_gu + ((size_t)e * 2 * a.I + i0 + l16) * a.H + 8 * g;
+        uoff = (size_t)a.I * a.H;
     }
     const uint16_t* Ap[MT];
     bool has_a[MT];
@@ -270,20 +276,18 @@ __device__ __forceinline__ void gateup_light_rows(const FfnArgs& a, int e, int r
     }
     const int mt_live = (n + 15) / 16;  // wave-uniform
 
-    floatx4_t acc[MT][NTILE];
+    floatx4_t acc[MT][2];  // [m][0] gate, [m][1] up
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int t = 0; t < NTILE; ++t) acc[m][t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    bf16x8_t ca[U][MT], cb[U][NTILE];
-    auto load_step = [&](int kb, bf16x8_t (&aa)[MT], bf16x8_t (&bb)[NTILE]) {
+    for (int m = 0; m < MT; ++m) acc[m][0] = acc[m][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    bf16x8_t ca[U][MT], cb[U][2];
+    auto load_step = [&](int kb, bf16x8_t (&aa)[MT], bf16x8_t (&bb)[2]) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) aa[m] = zero_bf16x8();
-#pragma unroll
-        for (int t = 0; t < NTILE; ++t) bb[t] = zero_bf16x8();
+        bb[0] = bb[1] = zero_bf16x8();
         if (kb < nk) {
-#pragma unroll
-            for (int t = 0; t < NTILE; ++t) bb[t] = load_weights<NTL>(Bp + t * bstride + kb * kstride);
+            const size_t ko = light_koff<PK>(kb);
+            bb[0] = load_weights<NTL>(Bg + ko);
+            bb[1] = load_weights<NTL>(Bg + uoff + ko);
 #pragma unroll
             for (int m = 0; m < MT; ++m)
                 if (has_a[m]) aa[m] = load_bf16x8(Ap[m] + kb * 32);
@@ -292,7 +296,7 @@ __device__ __forceinline__ void gateup_light_rows(const FfnArgs& a, int e, int r
 #pragma unroll
     for (int u = 0; u < U; ++u) load_step(u, ca[u], cb[u]);
     for (int k0 = 0; k0 < nk; k0 += U) {
-        bf16x8_t na[U][MT], nb_[U][NTILE];
+        bf16x8_t na[U][MT], nb_[U][2];
 #pragma unroll
         for (int u = 0; u < U; ++u) load_step(k0 + U + u, na[u], nb_[u]);
 #pragma unroll
@@ -301,40 +305,34 @@ __device__ __forceinline__ void gateup_light_rows(const FfnArgs& a, int e, int r
 #pragma unroll
                 for (int m = 0; m < MT; ++m)
                     if (m < mt_live) {
-#pragma unroll
-                        for (int t = 0; t < NTILE; ++t)
-                            acc[m][t] = mfma_16x16x32(ca[u][m], cb[u][t], acc[m][t]);
+                        acc[m][0] = mfma_16x16x32(ca[u][m], cb[u][0], acc[m][0]);
+                        acc[m][1] = mfma_16x16x32(ca[u][m], cb[u][1], acc[m][1]);
                     }
             }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
             for (int m = 0; m < MT; ++m) ca[u][m] = na[u][m];
-#pragma unroll
-            for (int t = 0; t < NTILE; ++t) cb[u][t] = nb_[u][t];
+            cb[u][0] = nb_[u][0];
+            cb[u][1] = nb_[u][1];
         }
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
 #pragma unroll
-        for (int t = 0; t < NTILE; ++t) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float up = __shfl_down(acc[m][t][r], 8, 64);
-                const int row = m * 16 + 4 * g + r;
-                if (l16 < 8 && row < n)
-                    a.h[(size_t)(r0 + row) * a.I + i0 + 8 * t + l16] =
-                        (uint16_t)f32_to_bf16_bits(swiglu(acc[m][t][r], up));
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int row = m * 16 + 4 * g + r;
+            if (row < n)
+                a.h[(size_t)(r0 + row) * a.I + i0 + l16] =
+                    (uint16_t)f32_to_bf16_bits(swiglu(acc[m][0][r], acc[m][1][r]));
         }
     }
 }
 
-// Work item = (light expert, 4 waves x NTILE x 8 h-columns).
-template <int U, int NTILE, bool NTL, bool PK>
+// Work item = (light expert, 4 waves x 16 h-columns).
+template <int U, bool NTL, bool PK>
 __global__ __launch_bounds__(kThreads) void gateup_light_kernel(FfnArgs a) {
-    static_assert(32 % (NTILE * 8) == 0, "a wave's columns must divide I's multiple of 32");
-    constexpr int kCols = 4 * NTILE * 8;
+    constexpr int kCols = 4 * 16;
     const int nlight = a.plan[0];
     const int nblk = (a.I + kCols - 1) / kCols;
     const long long nwork = (long long)nlight * nblk;
@@ -342,15 +340,15 @@ __global__ __launch_bounds__(kThreads) void gateup_light_kernel(FfnArgs a) {
     const int l16 = lane & 15, g = lane >> 4;
     for (long long wi = blockIdx.x; wi < nwork; wi += gridDim.x) {
         const int slot = (int)(wi / nblk), nb = (int)(wi % nblk);
-        const int i0 = nb * kCols + wave * NTILE * 8;
+        const int i0 = nb * kCols + wave * 16;
         if (i0 >= a.I) continue;  // I % 32 == 0: a wave is all in or all out
         const int e = a.plan[kPlanHeader + slot];
         const int r0 = a.offsets[e];
         const int n = a.offsets[e + 1] - r0;
         if (n <= 16)
-            gateup_light_rows<1, U, NTILE, NTL, PK>(a, e, r0, n, i0, l16, g);
+            gateup_light_rows<1, U, NTL, PK>(a, e, r0, n, i0, l16, g);
         else
-            gateup_light_rows<kLightSubTiles, kLightWideU, NTILE, NTL, PK>(a, e, r0, n, i0, l16, g);
+            gateup_light_rows<kLightSubTiles, kLightWideU, NTL, PK>(a, e, r0, n, i0, l16, g);
     }
 }
 
@@ -360,18 +358,19 @@ template <int MT, int U, int NT, bool NTL, bool PK>
 __device__ __forceinline__ void down_light_rows(const FfnArgs& a, int e, int r0, int n, int c0,
                                                 int l16, int g) {
     const int nk = a.I / 32;
-    const uint16_t* Bp;
-    size_t bstride, kstride;
-    if constexpr (PK) {
-        const int lane = g * 16 + l16;
-        const int ks = packed_dn_ksteps(a.I);
-        Bp = a.pk_dn + ((size_t)e * packed_dn_groups(a.H) + c0 / 16) * ks * 512 + lane * 8;
-        bstride = (size_t)ks * 512;
-        kstride = 512;
-    } else {
-        Bp = a.w_dn + ((size_t)e * a.H + c0 + l16) * a.I + 8 * g;
-        bstride = (size_t)16 * a.I;
-        kstride = 32;
+    // Lane l16 holds W_down row c0 + 16t + l16, K values 8g.. of each step.
+    const uint16_t* Bt[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int c = c0 + 16 * t + l16;
+        if constexpr (PK) {
+            // record chunks: 16-row block (c % 256) / 16 of tile c / 256
+            const int lane = g * 16 + l16;
+            const size_t rec = ((size_t)e * rec_tiles(a.H) + (c >> 8)) * mx_chunks(a.I);
+            Bt[t] = a.hr_dn + rec * kRecElems + (size_t)((c & 255) >> 4) * kRecBlockElems + lane * 8;
+        } else {
+            Bt[t] = a.w_dn + ((size_t)e * a.H + c) * a.I + 8 * g;
+        }
     }
     const uint16_t* Ap[MT];
     bool has_a[MT];
@@ -399,7 +398,7 @@ __device__ __forceinline__ void down_light_rows(const FfnArgs& a, int e, int r0,
             for (int m = 0; m < MT; ++m)
                 if (has_a[m]) aa[m] = load_bf16x8(Ap[m] + kb * 32);
 #pragma unroll
-            for (int t = 0; t < NT; ++t) bb[t] = load_weights<NTL>(Bp + t * bstride + kb * kstride);
+            for (int t = 0; t < NT; ++t) bb[t] = load_weights<NTL>(Bt[t] + light_koff<PK>(kb));
         }
     };
 #pragma unroll
@@ -841,6 +840,7 @@ constexpr int kBlk = 1024;         // bytes of one 8-row x 64-K block
 constexpr int kBlocksB = kTN / 8;  // 32
 constexpr int kRoleWaves = 4;      // waves per DMA role (A: 0..3, B: 4..7)
 constexpr int kBInst16 = kBlocksB / kRoleWaves;  // 8 bf16 B blocks per B wave and stage
+static_assert(kBInst16 % 2 == 0, "a B wave's blocks start a record row block");
 constexpr int kB8Blk = 4;          // MXFP8 code blocks (16 rows x 64 codes) per B wave and stage
 constexpr int kBInst8 = kB8Blk + 1;  // ... plus one load of 128 scale bytes
 
@@ -1170,12 +1170,14 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
             return;
         }
         if constexpr (BS == kBRec16) {
-            // record rows are already the tile's B rows (128 bytes each)
+            // the record's 1 KB chunks are copied as they are: LDS block
+            // 2jb + h holds chunk h of the tile's row block jb, lane L's
+            // operand at 16 L; this wave's 8 chunks are 8 KB contiguous
             const uint16_t* base = M == Mode::GateUp ? a.hr_gu : a.hr_dn;
             const size_t rec = (size_t)nst * kRec16Bytes;
             src = make_rsrc(reinterpret_cast<const char*>(base) + ((size_t)t.e * nblk + nb) * rec,
                             (uint32_t)rec);
-            doff[0] = (uint32_t)((kBInst16 * rw) * 8 + drow) * 128u + (uint32_t)dchunk * 16u;
+            doff[0] = (uint32_t)(kBInst16 * rw) * (uint32_t)kBlk + (uint32_t)lane * 16u;
             return;
         }
         if (M == Mode::GateUp)
@@ -1291,8 +1293,14 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
         const char* p = a_slot(slot) + blk * kBlk + (half ? foff1 : foff0);
         return *reinterpret_cast<const bf16x8_t*>(p);
     };
+    // (From the packed records the stage is in chunk order: fragment j's
+    // half is chunk 2 (wn*4 + j) + half, lane l's operand at 16 l.)
     auto read_b = [&](int slot, int half, bf16x8_t (&bf)[4]) {
-        const char* base = b_slot(slot) + (half ? foff1 : foff0);
+        const char* base = b_slot(slot);
+        if constexpr (BS == kBRec16)
+            base += half * kBlk + lane * 16;
+        else
+            base += half ? foff1 : foff0;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             bf[j] = *reinterpret_cast<const bf16x8_t*>(base + (wn * 4 + j) * 2 * kBlk);
@@ -1676,61 +1684,26 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
     }
 }
 
-// Packs one weight tensor into 1 KB lane-order chunks: output slot q (16
-// bytes) is lane L = q % 64 of chunk q / 64 = (e * groups + grp) * ksteps +
-// kb, i.e. K values 32kb + 8(L/16) .. +7 of weight row
-//   gate|up: h column c = 8grp + L%8, gate row c (L%16 < 8) or up row I + c;
-//   down:    row 16grp + L%16.
-__global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __restrict__ w, int E,
-                                                           int rows, int K, int groups, int ksteps,
-                                                           int gate_up, int I,
-                                                           uint16_t* __restrict__ out) {
-    const long long total = (long long)E * groups * ksteps * 64;
-    for (long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x; q < total;
-         q += (long long)gridDim.x * blockDim.x) {
-        const int L = (int)(q & 63);
-        long long t = q >> 6;
-        const int kb = (int)(t % ksteps);
-        t /= ksteps;
-        const int grp = (int)(t % groups);
-        const int e = (int)(t / groups);
-        const int l16 = L & 15, k = kb * 32 + 8 * (L >> 4);
-        int row;
-        bool ok;
-        if (gate_up) {
-            const int c = grp * 8 + (l16 & 7);
-            ok = c < I;
-            row = l16 < 8 ? c : I + c;
-        } else {
-            row = grp * 16 + l16;
-            ok = row < rows;
-        }
-        ok = ok && k < K;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (ok) v = *reinterpret_cast<const u32x4_t*>(w + ((size_t)e * rows + row) * K + k);
-        *reinterpret_cast<u32x4_t*>(out + q * 8) = v;
-    }
-}
-
 int grid_for(long long work, int per_cu, int num_cu) {
     return (int)std::max<long long>(1, std::min<long long>(work, (long long)per_cu * num_cu));
 }
 
-// bf16 heavy-tile records: one kRec16Bytes run per (expert, 256-row B tile
-// nb, 64-wide K stage c), row rr of the tile (the heavy kernel's B row order:
-// gate|up rows alternate in 16-row blocks of gate and up rows of h columns
-// nb*128 + 16*(rr/32) + rr%16; down rows are W_down rows nb*256 + rr) holding
-// its 64 K values; rows past the weights and K past the end are 0.  One
-// thread per 16 bytes.
+// Packed bf16 records (layout in launch.h): one thread per 16-byte unit u
+// of the output, unit u % 2048 of record u / 2048 = lane L of chunk h of
+// row block j (u % 2048 = 128 j + 64 h + L): tile row rr = 16 j + L % 16,
+// K values 64 c + 32 h + 8 (L / 16) .. +7 of the weight row it stands for
+// (gate|up: h column nb*128 + 16*(rr/32) + rr%16, gate row where rr % 32 <
+// 16, else the up row; down: W_down row nb*256 + rr), zero past the weights.
 template <bool kGateUp>
-__global__ __launch_bounds__(256) void pack_heavy_rec_kernel(const uint16_t* __restrict__ w, int E,
-                                                             int rows_per, int K, int I, int nblk,
-                                                             int nchunks, uint16_t* __restrict__ out) {
-    const long long nunits = (long long)E * nblk * nchunks * 256 * 8;
+__global__ __launch_bounds__(256) void pack_rec_kernel(const uint16_t* __restrict__ w, int E,
+                                                       int rows_per, int K, int I, int nblk,
+                                                       int nchunks, uint16_t* __restrict__ out) {
+    const long long nunits = (long long)E * nblk * nchunks * 2048;
     for (long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x; u < nunits;
          u += (long long)gridDim.x * blockDim.x) {
-        const int q = (int)(u & 7);
-        const int rr = (int)((u >> 3) & 255);
+        const int q = (int)(u & 2047);
+        const int L = q & 63, half = (q >> 6) & 1, j = q >> 7;
+        const int rr = 16 * j + (L & 15);
         const long long rec = u >> 11;
         const int c = (int)(rec % nchunks);
         const long long enb = rec / nchunks;
@@ -1745,15 +1718,11 @@ __global__ __launch_bounds__(256) void pack_heavy_rec_kernel(const uint16_t* __r
             row = nb * 256 + rr;
             valid = row < rows_per;
         }
-        uint32_t word[4] = {0u, 0u, 0u, 0u};
-        const int k0 = 64 * c + 8 * q;
-        if (valid && k0 < K) {  // K % 32 == 0: a unit is all in or all out
-            const u32x4_t v =
-                *reinterpret_cast<const u32x4_t*>(w + ((long long)e * rows_per + row) * K + k0);
-            word[0] = v[0], word[1] = v[1], word[2] = v[2], word[3] = v[3];
-        }
-        *reinterpret_cast<u32x4_t*>(out + rec * (kRec16Bytes / 2) + rr * 64 + 8 * q) =
-            u32x4_t{word[0], word[1], word[2], word[3]};
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        const int k0 = 64 * c + 32 * half + 8 * (L >> 4);
+        if (valid && k0 < K)  // K % 32 == 0: a unit is all in or all out
+            v = *reinterpret_cast<const u32x4_t*>(w + ((long long)e * rows_per + row) * K + k0);
+        *reinterpret_cast<u32x4_t*>(out + u * 8) = v;
     }
 }
 
@@ -1795,47 +1764,26 @@ hipError_t launch_heavy(const FfnArgs& a, int ncols, hipStream_t st) {
 
 }  // namespace
 
-size_t packed_gu_bytes(int E, int H, int I) {
-    return (size_t)E * packed_gu_groups(I) * (H / 32) * 1024;
-}
-
-size_t packed_dn_bytes(int E, int H, int I) {
-    return (size_t)E * packed_dn_groups(H) * packed_dn_ksteps(I) * 1024;
-}
-
 size_t rec16_gu_bytes(int E, int H, int I) {
-    return (size_t)E * ((2 * I + 255) / 256) * mx_chunks(H) * kRec16Bytes;
+    return (size_t)E * rec_tiles(2 * I) * mx_chunks(H) * kRec16Bytes;
 }
 
 size_t rec16_dn_bytes(int E, int H, int I) {
-    return (size_t)E * ((H + 255) / 256) * mx_chunks(I) * kRec16Bytes;
+    return (size_t)E * rec_tiles(H) * mx_chunks(I) * kRec16Bytes;
 }
 
 hipError_t launch_pack_weights(const uint16_t* w_gu, const uint16_t* w_dn, int E, int H, int I,
                                char* packed, hipStream_t st) {
-    const int gg = packed_gu_groups(I), kg = H / 32;
-    const int gd = packed_dn_groups(H), kd = packed_dn_ksteps(I);
-    const long long sg = (long long)E * gg * kg * 64, sd = (long long)E * gd * kd * 64;
-    pack_weights_kernel<<<(int)std::min<long long>((sg + 255) / 256, 65536), 256, 0, st>>>(
-        w_gu, E, 2 * I, H, gg, kg, 1, I, reinterpret_cast<uint16_t*>(packed));
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    pack_weights_kernel<<<(int)std::min<long long>((sd + 255) / 256, 65536), 256, 0, st>>>(
-        w_dn, E, H, I, gd, kd, 0, I, reinterpret_cast<uint16_t*>(packed + packed_gu_bytes(E, H, I)));
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    // the heavy tiles' records
-    char* rec = packed + packed_gu_bytes(E, H, I) + packed_dn_bytes(E, H, I);
-    const int nbg = (2 * I + 255) / 256, nbd = (H + 255) / 256;
+    const int nbg = rec_tiles(2 * I), nbd = rec_tiles(H);
     const long long ug = (long long)E * nbg * mx_chunks(H) * 2048;
     const long long ud = (long long)E * nbd * mx_chunks(I) * 2048;
-    pack_heavy_rec_kernel<true><<<(int)std::min<long long>((ug + 255) / 256, 65536), 256, 0, st>>>(
-        w_gu, E, 2 * I, H, I, nbg, mx_chunks(H), reinterpret_cast<uint16_t*>(rec));
-    err = hipGetLastError();
+    pack_rec_kernel<true><<<(int)std::min<long long>((ug + 255) / 256, 65536), 256, 0, st>>>(
+        w_gu, E, 2 * I, H, I, nbg, mx_chunks(H), reinterpret_cast<uint16_t*>(packed));
+    hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    pack_heavy_rec_kernel<false><<<(int)std::min<long long>((ud + 255) / 256, 65536), 256, 0, st>>>(
+    pack_rec_kernel<false><<<(int)std::min<long long>((ud + 255) / 256, 65536), 256, 0, st>>>(
         w_dn, E, H, I, I, nbd, mx_chunks(I),
-        reinterpret_cast<uint16_t*>(rec + rec16_gu_bytes(E, H, I)));
+        reinterpret_cast<uint16_t*>(packed + rec16_gu_bytes(E, H, I)));
     return hipGetLastError();
 }
 
@@ -1849,18 +1797,18 @@ hipError_t launch_ffn_plan(const int32_t* offsets, int E, int light_max, int for
 
 hipError_t launch_ffn_gateup(const FfnArgs& a, hipStream_t st) {
     if (a.plan && a.max_light > 0) {
-        const int kCols = 4 * (a.w_mxfp8 ? MOE_LIGHT_MX_GU_TILES : MOE_LIGHT_GU_TILES) * 8;
+        const int kCols = a.w_mxfp8 ? 4 * MOE_LIGHT_MX_GU_TILES * 8 : 4 * 16;
         const long long work = (long long)a.max_light * ((a.I + kCols - 1) / kCols);
         prof_begin(K_GATEUP_LIGHT, st);
         const int grid = grid_for(work, MOE_LIGHT_GU_BPC, a.num_cu);
         if (a.w_mxfp8)
             gateup_light_mx_kernel<MOE_LIGHT_MX_GU_U, MOE_LIGHT_MX_GU_TILES>
                 <<<grid, kThreads, 0, st>>>(a);
-        else if (a.pk_gu)
-            gateup_light_kernel<MOE_LIGHT_GU_U, MOE_LIGHT_GU_TILES, MOE_LIGHT_NT_LOADS != 0, true>
+        else if (a.hr_gu)
+            gateup_light_kernel<MOE_LIGHT_GU_U, MOE_LIGHT_NT_LOADS != 0, true>
                 <<<grid, kThreads, 0, st>>>(a);
         else
-            gateup_light_kernel<MOE_LIGHT_GU_U, MOE_LIGHT_GU_TILES, MOE_LIGHT_NT_LOADS != 0, false>
+            gateup_light_kernel<MOE_LIGHT_GU_U, MOE_LIGHT_NT_LOADS != 0, false>
                 <<<grid, kThreads, 0, st>>>(a);
         prof_end(K_GATEUP_LIGHT, st);
         hipError_t err = hipGetLastError();
@@ -1884,7 +1832,7 @@ hipError_t launch_ffn_down(const FfnArgs& a, hipStream_t st) {
         if (a.w_mxfp8)
             down_light_mx_kernel<MOE_LIGHT_MX_DN_TILES, MOE_LIGHT_MX_DN_U>
                 <<<grid, kThreads, 0, st>>>(a);
-        else if (a.pk_dn)
+        else if (a.hr_dn)
             down_light_kernel<MOE_LIGHT_DN_TILES, MOE_LIGHT_DN_U, MOE_LIGHT_NT_LOADS != 0, true>
                 <<<grid, kThreads, 0, st>>>(a);
         else

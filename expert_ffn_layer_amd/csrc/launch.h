@@ -225,13 +225,11 @@ struct FfnArgs {
     int split_h;                 // 1: h rows hold [hi | lo] bf16 halves (2I wide) and the
                                  //    down GEMM runs over both against the same weights
     int max_tiles;               // grid bound for heavy tiles
-    const uint16_t* pk_gu;       // packed W_gate|up for the light loop, or nullptr
-    const uint16_t* pk_dn;       // packed W_down for the light loop, or nullptr
     int max_light;               // grid bound for light experts
     int num_cu;
     int y_fmt;                   // y storage: 0 fp32, 1 bf16, 2 fp16 (round to nearest even)
     // MXFP8 routed weights (w_mxfp8 = 1): the light loop and the heavy tiles
-    // read these instead of pk_gu / pk_dn and w_gu / w_dn.
+    // read these instead of hr_gu / hr_dn and w_gu / w_dn.
     int w_mxfp8;
     const uint8_t* q_gu;         // packed E4M3 codes of W_gate|up
     const uint8_t* q_dn;         // packed E4M3 codes of W_down
@@ -239,30 +237,31 @@ struct FfnArgs {
     const uint8_t* qs_dn;        // per-chunk E8M0 scales of W_down
     const uint8_t* hq_gu;        // heavy-tile records of W_gate|up (codes + scales)
     const uint8_t* hq_dn;        // heavy-tile records of W_down
-    const uint16_t* hr_gu;       // bf16 heavy-tile records of W_gate|up, or nullptr
-    const uint16_t* hr_dn;       // bf16 heavy-tile records of W_down
+    const uint16_t* hr_gu;       // packed bf16 records of W_gate|up (both loops), or nullptr
+    const uint16_t* hr_dn;       // packed bf16 records of W_down
 };
 
-// Packed expert weights: 1 KB chunks, each the 16 weight rows x 32 K of one
-// MFMA B operand in lane order (lane l: row l % 16, K values 8(l/16)..+7).
-//  gate|up: chunk (e, g, kb) holds gate rows 8g..8g+7 then the matching up
-//    rows (h columns 8g..8g+7), K step kb; I/8 groups, H/32 K steps.
-//  down: chunk (e, g, kb) holds W_down rows 16g..16g+15, K step kb; H/16
-//    groups, I/32 K steps.
-// The packed copy is exactly as large as the weights.
-// Chunks are ordered (e, g, kb): a light wave streams one group's chunks
-// contiguously.  gate|up first, then down.  Only the light loop reads them:
-// the heavy tiles stream the row-major weights faster (measured: a 64-wide
-// K stage of 16 groups is 16 runs of 2 KB at a power-of-two stride).
+// Row groups of the MXFP8 light loop's packed chunks (mxfp8.hip): 8 h
+// columns (8 gate + the 8 matching up rows) or 16 W_down rows per group.
 inline __host__ __device__ int packed_gu_groups(int I) { return I / 8; }
 inline __host__ __device__ int packed_dn_groups(int H) { return H / 16; }
-inline __host__ __device__ int packed_dn_ksteps(int I) { return I / 32; }
-size_t packed_gu_bytes(int E, int H, int I);
-size_t packed_dn_bytes(int E, int H, int I);
-// The packed copy also holds the heavy tiles' records (after the light
-// chunks): one kRec16Bytes run per (expert, 256-row B tile, 64-wide K stage),
-// the tile rows in the heavy kernel's order, 64 bf16 K values each.
+// Packed bf16 expert weights: one kRec16Bytes record per (expert, 256-row
+// weight tile, 64-wide K stage), ordered (expert, tile, stage); W_gate|up's
+// records first, then W_down's.  The tile's rows (gate|up: 16-row blocks
+// alternate between the gate rows and the up rows of 16 h columns, block 2p
+// gate and 2p+1 up of columns tile*128 + 16p..; down: W_down rows in order)
+// are 16 blocks of 16 rows; block j holds two 1 KB chunks, K values 0..31
+// and 32..63 of the stage, each one bf16 MFMA B operand in lane order (lane
+// l: row 16j + l % 16, K values 8(l / 16)..+7 of the chunk).  Zero past the
+// weights (rows to a multiple of 256, K to 64).  A light wave's operand for
+// one K step is one chunk; a heavy tile's stage is the whole record, each
+// DMA load of 8 rows reading 8 whole 128-byte lines.
 constexpr int kRec16Bytes = 256 * 64 * 2;
+constexpr int kRecElems = kRec16Bytes / 2;  // bf16 values of a record
+constexpr int kRecChunkElems = 16 * 32;     // one chunk: 16 rows x 32 K
+constexpr int kRecBlockElems = 16 * 64;     // one 16-row block: two chunks
+// 256-row weight tiles of `rows` rows (the last one padded with zero rows).
+inline __host__ __device__ int rec_tiles(int rows) { return (rows + 255) / 256; }
 size_t rec16_gu_bytes(int E, int H, int I);
 size_t rec16_dn_bytes(int E, int H, int I);
 // Where the heavy tiles read B from.

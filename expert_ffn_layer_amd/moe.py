@@ -174,9 +174,9 @@ def packed_weight_bytes(shape: MoeShape) -> int:
 
 
 def pack_weights(shape: MoeShape, w_gate_up, w_down, stream=None) -> torch.Tensor:
-    """One-time re-layout of the routed expert weights into the lane-order
-    chunks the light loop streams (moe_pack_weights); returns the packed
-    uint8 device buffer."""
+    """One-time re-layout of the routed expert weights into the records both
+    FFN loops stream (moe_pack_weights); returns the packed uint8 device
+    buffer, one copy of the weights."""
     n = packed_weight_bytes(shape)
     if n == 0:
         raise MoeError(MOE_ERR_SHAPE, f"invalid shape {shape}")

@@ -120,10 +120,12 @@ typedef struct moe_shape {
 size_t moe_workspace_bytes(const moe_shape* shape);
 
 /* Bytes of the packed expert-weight buffer for `shape` (host-only, pure;
- * 0 for an invalid shape).  bf16 (w_mxfp8 = 0): the size of W_gate|up plus
- * W_down, E * 3 * I * H * 2.  MXFP8 (w_mxfp8 = 1): two copies (light loop,
- * heavy tiles) of one byte per weight (K padded to a multiple of 64, the
- * heavy copy's weight rows to a multiple of 256) plus one scale byte per 32
+ * 0 for an invalid shape).  bf16 (w_mxfp8 = 0): one copy of W_gate|up and
+ * W_down, 2 bytes per weight with weight rows padded to a multiple of 256
+ * and K to a multiple of 64 (E * 3 * I * H * 2 when 2I and H are multiples
+ * of 256 and I of 64).  MXFP8 (w_mxfp8 = 1): two copies (light loop, heavy
+ * tiles) of one byte per weight (K padded to a multiple of 64, the heavy
+ * copy's weight rows to a multiple of 256) plus one scale byte per 32
  * weights. */
 size_t moe_packed_weight_bytes(const moe_shape* shape);
 
@@ -164,31 +166,26 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t* counts
                 void* workspace, size_t ws_bytes, void* stream);
 
 /* Optional one-time re-layout of the routed expert weights (the expert
- * weights are constant across calls, as a serving engine loads them once).
- * The weights become 1 KB chunks, each the 16 weight rows x 32 K values of
- * one bf16 MFMA operand in lane order (lane l: row l%16, K 8(l/16)..+7):
- *   gate|up chunk (e, g, kb): gate rows 8g..8g+7 then up rows I+8g..+7,
- *     K 32kb..32kb+31; I/8 groups g per expert, H/32 steps kb;
- *   down chunk (e, g, kb): W_down rows 16g..16g+15, K 32kb..; H/16 groups,
- *     I/32 steps;
- * ordered (e, g, kb).  The
- * light loop (experts with few rows: every expert of a decode step) then
- * streams each group's weights as one contiguous run: on MI355X the gate|up
- * weights of a decode step stream at ~6.1 TB/s instead of ~5.7 TB/s from the
- * row-major layout, whose 16-row tiles read 64 bytes from rows 8 KB apart.
- * A second part holds the weights again for the heavy tiles: one 32 KB
- * record per (expert e, 256-row weight tile nb, 64-wide K stage c), ordered
- * (e, nb, c), each the tile's 256 rows x 64 K values -- gate|up tile rows
- * alternate in 16-row blocks between gate and up rows of h columns
- * nb*128 + 16*(r/32) + r%16; down tile rows are W_down rows nb*256 + r --
- * with zeros past the weights (rows padded to 256, K to 64); a heavy stage
- * is then one contiguous read.  The packed buffer thus holds two copies.
+ * weights are constant across calls, as a serving engine loads them once),
+ * read by both the light loop and the heavy tiles.  One 32 KB record per
+ * (expert e, 256-row weight tile nb, 64-wide K stage c), ordered (e, nb, c),
+ * W_gate|up's records first, then W_down's.  A record's 256 tile rows --
+ * gate|up: 16-row blocks alternating between the gate rows and the up rows
+ * of h columns nb*128 + 16p .. +15 (block 2p gate, 2p+1 up); down: W_down
+ * rows nb*256 + r -- form 16 row blocks j, each two 1 KB chunks (K values
+ * 64c..64c+31, then 64c+32..64c+63), each chunk one bf16 MFMA operand in
+ * lane order (lane l: row 16j + l%16, K values 8(l/16)..+7 of the chunk).
+ * Zeros past the weights (rows padded to 256, K to 64).  A heavy stage is
+ * then one contiguous 32 KB read and a light wave's operand one contiguous
+ * 1 KB read, where the row-major layout's 16-row operands read 64 bytes
+ * from each of 16 rows a whole weight row apart.
  *   w_gate_up, w_down  bf16, layouts as for moe_grouped_ffn (read)
  *   packed             device buffer of moe_packed_weight_bytes(shape)
  *                      bytes, 256-byte aligned (written; caller-owned)
  * Enqueued on `stream`; the packed buffer may be passed to moe_grouped_ffn
- * and moe_forward once that work has completed.  Results are bitwise
- * identical with and without it. */
+ * and moe_forward once that work has completed (the plain weights are then
+ * optional there and may be freed).  Results are bitwise identical with and
+ * without it. */
 int moe_pack_weights(const moe_shape* shape, const uint16_t* w_gate_up, const uint16_t* w_down,
                      void* packed, void* stream);
 

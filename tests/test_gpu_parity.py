@@ -495,10 +495,9 @@ def test_empty_batch():
                                        (SMALL["light"], 0, -1), (SMALL["max_e_k"], 0, -1)],
                          ids=lambda v: getattr(v, "name", str(v)))
 def test_packed_weights_bitwise(cfg, tm, lm):
-    """The light loop reading the packed weight copy gives the same output
-    bits as reading the plain layout (same data, same MFMA chains); with the
-    light loop off (light_max_rows 0) the packed copy is unused and the
-    heavy tiles are unchanged at every height."""
+    """Both loops reading the packed records give the same output bits as
+    reading the plain layout (same data, same MFMA chains), at every heavy
+    tile height and with the light loop on and off."""
     print(f"[case] packed {cfg.name} tm={tm} light_max={lm}", flush=True)
     lay = layer_on_gpu(cfg)
     outs = []
@@ -511,10 +510,13 @@ def test_packed_weights_bitwise(cfg, tm, lm):
 
 
 def test_packed_weights_layout():
-    """Spot-check the packed chunks against their definition: lane L of
-    chunk (e, g, kb) holds K values 32kb + 8(L//16).. of gate row 8g + L%8
-    (L%16 < 8) or up row I + 8g + L%8 (gate|up), or of W_down row
-    16g + L%16 (down)."""
+    """Spot-check the packed records against their definition: record
+    (e, nb, c) is 16 row blocks j of two 1 KB chunks h; lane L of chunk
+    (j, h) holds K values 64c + 32h + 8(L//16) .. +7 of tile row
+    rr = 16j + L%16, which is the gate|up row of h column
+    nb*128 + 16*(rr//32) + rr%16 (gate where rr%32 < 16, else up) or W_down
+    row nb*256 + rr, zero past the weights; W_gate|up's records first,
+    nothing else in the buffer."""
     cfg = custom("pk", T=8, H=192, E=2, k=1, I=160)
     lay = layer_on_gpu(cfg)
     s = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I)
@@ -524,50 +526,24 @@ def test_packed_weights_layout():
     wgu = lay.w_gu.view(torch.int16).cpu().numpy()
     wdn = lay.w_dn.view(torch.int16).cpu().numpy()
     H, I, E = cfg.H, cfg.I, cfg.E
-    gg, kg = I // 8, H // 32
-    gd, kd = H // 16, I // 32
     rng = np.random.default_rng(3)
-
-    def expect(gate_up, e, grp, kb, L):
-        k = 32 * kb + 8 * (L // 16)
-        if gate_up:
-            c = 8 * grp + L % 8
-            row = c if L % 16 < 8 else I + c
-            ok, src = c < I and k < H, wgu[e]
-        else:
-            row = 16 * grp + L % 16
-            ok, src = row < H and k < I, wdn[e]
-        return src[row, k:k + 8] if ok else np.zeros(8, np.int16)
-
-    light = (E * gg * kg + E * gd * kd) * 512
     nbg, nbd = -(-2 * I // 256), -(-H // 256)
     ncg, ncd = -(-H // 64), -(-I // 64)
     rec_gu = E * nbg * ncg * 256 * 64
-    assert words.size == light + rec_gu + E * nbd * ncd * 256 * 64
-    base_dn = E * gg * kg * 512
-    for _ in range(600):
-        gate_up = bool(rng.integers(2))
-        ng, nk = (gg, kg) if gate_up else (gd, kd)
-        e, grp, kb, L = rng.integers(E), rng.integers(ng), rng.integers(nk), rng.integers(64)
-        q = ((e * ng + grp) * nk + kb) * 64 + L
-        off = (0 if gate_up else base_dn) + q * 8
-        assert np.array_equal(words[off:off + 8], expect(gate_up, e, grp, kb, L)), (gate_up, e, grp, kb, L)
-    # heavy-tile records (e, nb, c): tile row rr (gate|up: gate and up rows of
-    # h columns nb*128 + 16*(rr//32) + rr%16 alternating in 16-row blocks;
-    # down: W_down row nb*256 + rr) with K 64c..64c+63, zero past the weights
-    for _ in range(600):
+    assert words.size == rec_gu + E * nbd * ncd * 256 * 64
+    for _ in range(3000):
         gate_up = bool(rng.integers(2))
         nbk, nc = (nbg, ncg) if gate_up else (nbd, ncd)
-        e, nb, c, rr = (int(rng.integers(n)) for n in (E, nbk, nc, 256))
+        e, nb, c, j, h, L = (int(rng.integers(n)) for n in (E, nbk, nc, 16, 2, 64))
+        rr = 16 * j + L % 16
+        k0 = 64 * c + 32 * h + 8 * (L // 16)
         if gate_up:
             hc = nb * 128 + (rr // 32) * 16 + rr % 16
             ok, row, src, K = hc < I, (hc if rr % 32 < 16 else I + hc), wgu[e], H
         else:
             row = nb * 256 + rr
             ok, src, K = row < H, wdn[e], I
-        want = np.zeros(64, np.int16)
-        if ok:
-            seg = src[row, 64 * c: min(64 * c + 64, K)]
-            want[:seg.size] = seg
-        off = light + (0 if gate_up else rec_gu) + ((e * nbk + nb) * nc + c) * 256 * 64 + rr * 64
-        assert np.array_equal(words[off:off + 64], want), (gate_up, e, nb, c, rr)
+        want = src[row, k0:k0 + 8] if ok and k0 < K else np.zeros(8, np.int16)
+        off = ((0 if gate_up else rec_gu) + ((e * nbk + nb) * nc + c) * 256 * 64
+               + (2 * j + h) * 512 + L * 8)
+        assert np.array_equal(words[off:off + 8], want), (gate_up, e, nb, c, j, h, L)

@@ -4,7 +4,8 @@ Each case draws its sizes from a fixed seed (so a failure names a
 reproducible case): T 1..400, H a multiple of 64 up to 512, E 1..96, k up to
 min(E, 12), I a multiple of 32 up to 320, an optional shared expert, optional
 Zipf routing skew, the light threshold (default rule, all heavy, 16, 64),
-the heavy tile height (chosen, 128, 192, 256) and the y storage.  Routing
+the heavy tile height (chosen, 128..256) and the y storage; odd cases read
+the packed weight records (and must equal the plain layout bit for bit).  Routing
 must match exactly (near-ties flagged) and the output meet the 2e-2 /
 5e-3 bar.
 """
@@ -41,11 +42,20 @@ def draw_case(i):
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_layer(oracle_lib, i):
     kw, lm, tm, yf = draw_case(i)
-    print(f"[case] random {i}: {kw} light_max={lm} tm={tm} y={yf}", flush=True)
+    packed = i % 2 == 1
+    print(f"[case] random {i}: {kw} light_max={lm} tm={tm} y={yf} packed={packed}", flush=True)
     cfg = synth.custom_config(f"rand{i}", **kw)
     layer = synth.make_layer(cfg, seed=i, device=gh.DEV)
     rep = gh.check_layer(oracle_lib, layer, light_max_rows=lm, heavy_tile_rows=tm,
-                         y_bf16=yf == "bf16", y_fp16=yf == "fp16")
+                         y_bf16=yf == "bf16", y_fp16=yf == "fp16", packed=packed)
+    if packed:  # the packed records give the plain layout's bits
+        import torch
+
+        from expert_ffn_layer_amd import moe
+        outs = [moe.MoELayer(layer, lm, tm, y_bf16=yf == "bf16", y_fp16=yf == "fp16",
+                             packed=pk)()[0] for pk in (False, True)]
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
     ma, rel = rep["err"]
     print(f"[parity] random {i}: near_ties={rep['near_ties']} max_abs={ma:.3e} relL2={rel:.3e}",
           flush=True)
