@@ -228,6 +228,45 @@ int plan_round_tiles(const moe_shape* s, int* out) {
     return MOE_OK;
 }
 
+// The shared expert depends on x alone, so moe_forward runs it on a second
+// stream of the device beside the routing and the routed FFN (which read x,
+// the router and expert weights and write only the workspace): the side
+// stream waits for an event recorded on the caller's stream before the
+// router, and the caller's stream waits for the side stream's last launch
+// before the combine, which adds the routed outputs to the shared expert's.
+// One side stream and one fork/join event pair per device, created at the
+// first call that needs them (default priority, non-blocking); g_side_mu is
+// held from the fork until the join is enqueued, so calls from several host
+// threads pair their own records and waits (and their shared experts queue
+// on the one side stream).  Built with MOE_SHARED_OVERLAP=0, everything is
+// enqueued on the caller's stream.
+#ifndef MOE_SHARED_OVERLAP
+#define MOE_SHARED_OVERLAP 1
+#endif
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxSideDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxSideDevices];
+
+// Call with g_side_mu held.
+int side_stream(SideStream** out) {
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= kMaxSideDevices)
+        return fail(MOE_ERR_UNSUPPORTED, "device index beyond the side-stream table");
+    SideStream& ss = g_side[dev];
+    if (!ss.s) {
+        HIP_TRY(hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming), "side fork event");
+        HIP_TRY(hipEventCreateWithFlags(&ss.join, hipEventDisableTiming), "side join event");
+        HIP_TRY(hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking), "side stream");
+    }
+    *out = &ss;
+    return MOE_OK;
+}
+
 // Returns through *plan_ready whether the permute also wrote the FFN plan
 // (single-block path); then run_ffn skips its plan kernel.
 int run_permute(const moe_shape* s, const Layout& L, const int32_t* ids, int32_t* counts,
@@ -529,12 +568,17 @@ int moe_combine(const moe_shape* shape, const void* y, const int32_t* inv_pos,
     return MOE_OK;
 }
 
-int moe_forward(const moe_shape* shape, const uint16_t* x, const float* w_router,
-                const float* bias, const uint16_t* w_gate_up, const uint16_t* w_down,
-                const void* packed_weights, const uint16_t* ws_gate_up, const uint16_t* ws_down,
-                float* out,
-                int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, void* workspace,
-                size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace moe {
+
+// moe_forward; overlap_shared: the shared expert on the device's side stream
+// (else on `stream` after the routed FFN).
+int forward(const moe_shape* shape, const uint16_t* x, const float* w_router, const float* bias,
+            const uint16_t* w_gate_up, const uint16_t* w_down, const void* packed_weights,
+            const uint16_t* ws_gate_up, const uint16_t* ws_down, float* out,
+            int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, void* workspace,
+            size_t ws_bytes, void* stream, bool overlap_shared) {
     g_last_error.clear();
     if (int rc = check_shape(shape)) return rc;
     hipStream_t st = (hipStream_t)stream;
@@ -578,6 +622,15 @@ int moe_forward(const moe_shape* shape, const uint16_t* x, const float* w_router
     int32_t* sorted = at<int32_t>(workspace, L.sorted);
     int32_t* inv = at<int32_t>(workspace, L.inv);
     void* y = at<char>(workspace, L.y);
+    std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
+    SideStream* side = nullptr;
+    if (shape->I_shared > 0 && overlap_shared) {
+        // fork point: the side stream starts from here once its work is
+        // enqueued (after the routed launches, which keeps their order)
+        side_lock.lock();
+        if (int rc = side_stream(&side)) return rc;
+        HIP_TRY(hipEventRecord(side->fork, st), "fork");
+    }
     if (int rc = run_router(shape, L, x, w_router, bias, ids, w, nullptr, workspace, st)) return rc;
     bool plan_ready = false;
     if (int rc = run_permute(shape, L, ids, counts, offsets, sorted, inv, workspace, st, &plan_ready))
@@ -585,12 +638,35 @@ int moe_forward(const moe_shape* shape, const uint16_t* x, const float* w_router
     if (int rc = run_ffn(shape, L, x, sorted, offsets, w_gate_up, w_down, packed_weights, nullptr,
                          y, workspace, st, plan_ready, true))
         return rc;
-    if (shape->I_shared > 0)
+    if (side) {
+        HIP_TRY(hipStreamWaitEvent(side->s, side->fork, 0), "fork wait");
+        if (int rc = run_shared(shape, L, x, ws_gate_up, ws_down, out, workspace, side->s))
+            return rc;
+        HIP_TRY(hipEventRecord(side->join, side->s), "join");
+        HIP_TRY(hipStreamWaitEvent(st, side->join, 0), "join wait");
+        side_lock.unlock();
+    } else if (shape->I_shared > 0) {
         if (int rc = run_shared(shape, L, x, ws_gate_up, ws_down, out, workspace, st)) return rc;
+    }
     HIP_TRY(moe::launch_combine(y, y_format(shape), inv, w, shape->T, shape->H, shape->k,
                                 shape->I_shared > 0 ? 1 : 0, out, st),
             "combine");
     return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" {
+
+int moe_forward(const moe_shape* shape, const uint16_t* x, const float* w_router,
+                const float* bias, const uint16_t* w_gate_up, const uint16_t* w_down,
+                const void* packed_weights, const uint16_t* ws_gate_up, const uint16_t* ws_down,
+                float* out,
+                int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, void* workspace,
+                size_t ws_bytes, void* stream) {
+    return moe::forward(shape, x, w_router, bias, w_gate_up, w_down, packed_weights, ws_gate_up,
+                        ws_down, out, topk_ids_out, topk_w_out, counts_out, workspace, ws_bytes,
+                        stream, MOE_SHARED_OVERLAP != 0);
 }
 
 }  // extern "C"

@@ -8,7 +8,8 @@
 // device (with that device current) and kept per device; host code only ever
 // passes that address on, never the array's own name, which in host code is
 // a stand-in rather than a device address.  Nothing here allocates: the
-// layer's kernels run as in moe_forward, on the address of the array.
+// layer's kernels run as in moe_forward, on the address of the array, all
+// on the caller's stream (the shared expert too: no side stream is made).
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -19,6 +20,13 @@
 namespace moe {
 // Sets the calling thread's moe_last_error() text and returns `code`.
 int report_error(int code, const char* msg);
+// moe_forward, with the shared expert on the caller's stream when
+// overlap_shared is false (no side stream or event is created).
+int forward(const moe_shape* shape, const uint16_t* x, const float* w_router, const float* bias,
+            const uint16_t* w_gate_up, const uint16_t* w_down, const void* packed_weights,
+            const uint16_t* ws_gate_up, const uint16_t* ws_down, float* out,
+            int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, void* workspace,
+            size_t ws_bytes, void* stream, bool overlap_shared);
 }  // namespace moe
 
 namespace {
@@ -77,7 +85,7 @@ extern "C" int moe_forward_noalloc(const moe_shape* shape, const uint16_t* x,
                 .c_str());
     void* ws = nullptr;
     if (int rc = scratch_address(&ws)) return rc;
-    return moe_forward(shape, x, w_router, bias, w_gate_up, w_down, packed_weights, ws_gate_up,
-                       ws_down, out, topk_ids_out, topk_w_out, counts_out, ws,
-                       MOE_NOALLOC_SCRATCH_BYTES, stream);
+    return moe::forward(shape, x, w_router, bias, w_gate_up, w_down, packed_weights, ws_gate_up,
+                        ws_down, out, topk_ids_out, topk_w_out, counts_out, ws,
+                        MOE_NOALLOC_SCRATCH_BYTES, stream, false);
 }

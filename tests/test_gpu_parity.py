@@ -447,6 +447,47 @@ def test_shared_stage(oracle_lib):
     gh.assert_close(out.cpu().numpy(), ref, "shared expert")
 
 
+def test_shared_overlap_back_to_back():
+    """moe_forward runs the shared expert on a side stream that forks from
+    the caller's stream before the router and joins before the combine.
+    Four calls enqueued back to back on a non-default stream, each writing
+    its own output (and the last two sharing one), with no host wait in
+    between, must each equal the serial composition of the stages bit for
+    bit: shared expert into `out`, routed FFN, then the combine adding to it."""
+    cfg = custom("ovl", T=700, H=512, E=16, k=4, I=256, I_shared=512)
+    lay = layer_on_gpu(cfg)
+    s = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_shared)
+    ws = moe.alloc_workspace(s)
+    T, H, k = cfg.T, cfg.H, cfg.k
+    # serial reference from the stage calls, on the default stream
+    ids = torch.empty((T, k), dtype=torch.int32, device=gh.DEV)
+    w = torch.empty((T, k), dtype=torch.float32, device=gh.DEV)
+    moe.router(s, lay.x, lay.wg, lay.bias, ids, w, None, ws)
+    counts = torch.empty((cfg.E,), dtype=torch.int32, device=gh.DEV)
+    offsets = torch.empty((cfg.E + 1,), dtype=torch.int32, device=gh.DEV)
+    sorted_ids = torch.empty((T * k,), dtype=torch.int32, device=gh.DEV)
+    inv = torch.empty((T * k,), dtype=torch.int32, device=gh.DEV)
+    moe.permute(s, ids, counts, offsets, sorted_ids, inv, ws)
+    y = torch.empty((T * k, H), dtype=torch.float32, device=gh.DEV)
+    moe.grouped_ffn(s, lay.x, sorted_ids, offsets, lay.w_gu, lay.w_dn, None, y, ws)
+    ref = torch.empty((T, H), dtype=torch.float32, device=gh.DEV)
+    moe.shared_ffn(s, lay.x, lay.ws_gu, lay.ws_dn, ref, ws)
+    moe.combine(s, y, inv, w, True, ref)
+    torch.cuda.synchronize()
+    ref = ref.view(torch.int32).cpu()
+    st = torch.cuda.Stream()
+    outs = [torch.full((T, H), float("nan"), device=gh.DEV) for _ in range(3)]
+    wss = [moe.alloc_workspace(s) for _ in range(2)]
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        for i, o in enumerate(outs + [outs[2]]):
+            moe.forward(s, lay.x, lay.wg, lay.bias, lay.w_gu, lay.w_dn, lay.ws_gu, lay.ws_dn,
+                        o, wss[i % 2], stream=st)
+    st.synchronize()
+    for i, o in enumerate(outs):
+        assert torch.equal(o.view(torch.int32).cpu(), ref), f"call {i} differs from the stages"
+
+
 # ------------------------------------------------------------ properties
 def test_determinism_and_equivariance():
     cfg = SMALL["mixed"]
