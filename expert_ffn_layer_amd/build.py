@@ -26,6 +26,10 @@ SOURCES = ["router.hip", "permute.hip", "ffn.hip", "combine.hip", "mxfp8.hip", "
 # bits with the default build's to cover the cross-tile paths on small shapes.
 GRID16_LIB = os.path.join(PKG, "libmoe_grid16.so")
 GRID16_FLAGS = ["-DMOE_HEAVY_MAX_GRID=16"]
+# Test variant: the light loop as one persistent gate|up -> down launch
+# (off in the default build; kept correct by tests/test_gpu_fused_light.py).
+FUSED_LIB = os.path.join(PKG, "libmoe_fusedlight.so")
+FUSED_FLAGS = ["-DMOE_FUSED_LIGHT=1"]
 
 # -packed-fp32-ops off: packed fp32 VALU forms are not emitted.
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -62,10 +66,13 @@ def build(verbose: bool = False, out: str = LIB, objdir: str = OBJDIR, extra=())
 
 
 def build_all(verbose: bool = False) -> None:
-    """The library and its grid-capped test variant."""
+    """The library and its test variants (grid-capped heavy kernels, fused
+    light loop)."""
     build(verbose=verbose)
     build(verbose=verbose, out=GRID16_LIB, objdir=os.path.join(OBJDIR, "grid16"),
           extra=GRID16_FLAGS)
+    build(verbose=verbose, out=FUSED_LIB, objdir=os.path.join(OBJDIR, "fused"),
+          extra=FUSED_FLAGS)
 
 
 if __name__ == "__main__":

@@ -55,7 +55,7 @@ constexpr int kPermChunk = 4096;  // assignments per permute block
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* chunk_counts,
                           int nchunks, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
                           int32_t* inv_pos, int32_t* plan, int light_max, int force_tm,
-                          int round_tiles, hipStream_t st);
+                          int round_tiles, int32_t* sync, hipStream_t st);
 
 // ---- grouped FFN --------------------------------------------------------
 constexpr int kLightRowsMax = 64;  // up to four 16-row MFMA sub-tiles
@@ -199,7 +199,13 @@ int dense_tile_height(int rows);  // tile height for a dense group of `rows` row
 // force_tm: 0 = pick the heavy tile height from the counts, else that height.
 // round_tiles: multiple of tiles the XCD slice bounds are rounded to (xcd_bounds).
 hipError_t launch_ffn_plan(const int32_t* offsets, int E, int light_max, int force_tm,
-                           int round_tiles, int32_t* plan, hipStream_t st);
+                           int round_tiles, int32_t* plan, int32_t* sync, hipStream_t st);
+// Counters of the fused light loop (FfnArgs::sync), zeroed by whichever
+// kernel writes the plan (when given): [kSyncTicket] the next work item,
+// [kSyncTimeouts] readiness waits that gave up (0 unless something is
+// broken), [kSyncReady + slot] gate|up items finished for light slot `slot`.
+constexpr int kSyncTicket = 0, kSyncTimeouts = 1, kSyncReady = 2;
+inline __host__ __device__ int sync_ints(int E) { return kSyncReady + E; }
 // Tiles per round of a heavy GEMM's XCD slice for `num_cu` CUs (one block per
 // CU, kXcds slices) with N blocks of nblk_gu (gate|up) and nblk_dn (down): the
 // rounding of the slice bounds; 1 when it does not divide evenly.
@@ -239,6 +245,8 @@ struct FfnArgs {
     const uint8_t* hq_dn;        // heavy-tile records of W_down
     const uint16_t* hr_gu;       // packed bf16 records of W_gate|up (both loops), or nullptr
     const uint16_t* hr_dn;       // packed bf16 records of W_down
+    int32_t* sync;               // fused light loop's counters (zeroed with the plan), or
+                                 // nullptr: the light loop runs as two launches
 };
 
 // Row groups of the MXFP8 light loop's packed chunks (mxfp8.hip): 8 h

@@ -48,7 +48,7 @@ struct Layout {
     // accepts them, so an expert can then get more than T rows).
     int splits = 1, nchunks = 1, light_max = 0, max_tiles = 0, max_light = 0, plan_tiles = 0;
     size_t part = 0, ids = 0, w = 0, chunk = 0, counts = 0, offsets = 0, sorted = 0, inv = 0,
-           plan = 0, h = 0, y = 0, hs = 0, total = 0;
+           plan = 0, sync = 0, h = 0, y = 0, hs = 0, total = 0;
 };
 
 #ifndef MOE_ROUTER_MIN_BLOCKS
@@ -143,6 +143,7 @@ Layout layout(const moe_shape* s) {
     L.sorted = take((size_t)A * 4);
     L.inv = take((size_t)A * 4);
     L.plan = take((size_t)(moe::kPlanHeader + E + 2LL * L.plan_tiles) * 4);
+    L.sync = take((size_t)moe::sync_ints(s->E) * 4);
     L.h = take((size_t)A * I * 2);
     L.y = take((size_t)A * H * (y_format(s) ? 2 : 4));
     L.hs = take((size_t)T * 2 * s->I_shared * 2);  // [hi | lo] rows
@@ -279,7 +280,7 @@ int run_permute(const moe_shape* s, const Layout& L, const int32_t* ids, int32_t
         if (int rc = plan_round_tiles(s, &round_tiles)) return rc;
     HIP_TRY(moe::launch_permute(ids, s->T, s->k, s->E, at<int32_t>(ws, L.chunk), L.nchunks,
                                 counts, offsets, sorted, inv, plan, L.light_max,
-                                plan_force_tm(s), round_tiles, st),
+                                plan_force_tm(s), round_tiles, at<int32_t>(ws, L.sync), st),
             "permute");
     if (plan_ready) *plan_ready = plan != nullptr;
     return MOE_OK;
@@ -299,7 +300,7 @@ int run_ffn(const moe_shape* s, const Layout& L, const uint16_t* x, const int32_
         int round_tiles = 1;
         if (int rc = plan_round_tiles(s, &round_tiles)) return rc;
         HIP_TRY(moe::launch_ffn_plan(offsets, s->E, L.light_max, plan_force_tm(s), round_tiles,
-                                     plan, st),
+                                     plan, at<int32_t>(ws, L.sync), st),
                 "ffn plan");
     }
     moe::FfnArgs a{};
@@ -311,6 +312,7 @@ int run_ffn(const moe_shape* s, const Layout& L, const uint16_t* x, const int32_
     a.h = h ? h : at<uint16_t>(ws, L.h);
     a.y = y;
     a.plan = plan;
+    a.sync = at<int32_t>(ws, L.sync);
     a.T = s->T;
     a.H = s->H;
     a.I = s->I;

@@ -190,12 +190,14 @@ __global__ __launch_bounds__(kThreads) void perm_small_kernel(
     const int32_t* __restrict__ ids, int A, int k, int E, int nbits,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_ids,
     int32_t* __restrict__ inv_pos, int32_t* __restrict__ plan, int light_max, int force_tm,
-    int round_tiles) {
+    int round_tiles, int32_t* __restrict__ sync) {
     extern __shared__ int32_t sm[];  // wcnt[4][E], off[E]
     __shared__ int32_t wsum[4];
     int32_t* wcnt = sm;
     int32_t* off = sm + kWavesPerBlock * E;
     for (int i = threadIdx.x; i < (kWavesPerBlock + 1) * E; i += kThreads) sm[i] = 0;
+    if (plan && sync)  // the fused light loop's counters start at zero
+        for (int i = threadIdx.x; i < sync_ints(E); i += kThreads) sync[i] = 0;
     __syncthreads();
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -313,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void perm_small_kernel(
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* chunk_counts,
                           int nchunks, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
                           int32_t* inv_pos, int32_t* plan, int light_max, int force_tm,
-                          int round_tiles, hipStream_t st) {
+                          int round_tiles, int32_t* sync, hipStream_t st) {
     const long long A = (long long)T * k;
     int nbits = 1;
     while ((1 << nbits) < E) ++nbits;
@@ -321,7 +323,7 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* chun
         prof_begin(K_PERM_SMALL, st);
         perm_small_kernel<<<1, kThreads, (kWavesPerBlock + 1) * E * sizeof(int32_t), st>>>(
             ids, (int)A, k, E, nbits, counts, offsets, sorted_ids, inv_pos, plan, light_max,
-            force_tm, round_tiles);
+            force_tm, round_tiles, sync);
         prof_end(K_PERM_SMALL, st);
         return hipGetLastError();
     }
