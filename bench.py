@@ -66,7 +66,7 @@ def parse():
     p.add_argument("--weights", choices=("bf16", "mxfp8"), default="bf16",
                    help="routed expert weights: bf16, or MXFP8 (OCP MX E4M3 codes with one "
                         "E8M0 scale per 32 values, quantised on the GPU before timing)")
-    p.add_argument("--heavy-tile-rows", type=int, default=0, choices=(0, 128, 192, 256),
+    p.add_argument("--heavy-tile-rows", type=int, default=0, choices=(0, 128, 160, 192, 224, 256),
                    help="heavy tile height: 0 = the library's per-expert choice (results do "
                         "not depend on it)")
     p.add_argument("--no-copy-calibration", action="store_true",

@@ -91,9 +91,10 @@ typedef struct moe_shape {
                                expert on); with T*k > 8*E always the latter.  Results
                                do not depend on it. */
     int32_t heavy_tile_rows; /* rows per heavy tile: 0 = chosen per expert from its row
-                               count (the least estimated time: one height, or 256-row
-                               tiles and a smaller last tile); 128, 192 or 256 = every
-                               tile that height.  Results do not depend on it. */
+                               count (equal tiles of the one height among 256, 224, 192,
+                               160 and 128 with the least estimated time); 128, 160, 192,
+                               224 or 256 = every tile that height.  Results do not
+                               depend on it. */
     int32_t y_bf16;         /* storage of the routed expert outputs y: 0 = fp32, 1 = bf16
                                (round to nearest even).  bf16 halves the y round trip
                                between the down GEMM and the combine (2*T*k*H bytes less
@@ -285,7 +286,19 @@ int moe_combine(const moe_shape* shape, const void* y, const int32_t* inv_pos,
  * optional, as for moe_grouped_ffn (required with shape->w_mxfp8 = 1); when
  * it is given, w_gate_up / w_down are not read and may be NULL.  topk_ids_out [T,k],
  * topk_w_out [T,k] and counts_out [E] are optional copies of the routing
- * (NULL = not written). */
+ * (NULL = not written).
+ * Streams: with a shared expert, its two GEMMs run on a side stream the
+ * library keeps per device (default priority, non-blocking, created at the
+ * first such call), which waits for an event recorded on `stream` before
+ * the router and which `stream` waits for before the combine: the shared
+ * expert, which needs only x, runs beside the routing and the routed FFN
+ * (after the yuxiaoba.github.io summary of "Optimizing Muse Spark Open on
+ * TPU v7 with SGLang-TorchTPU", section on chaining one verify pass's 62
+ * layers into a continuous data flow: weight traffic does not wait for
+ * work it does not depend on).
+ * All work is ordered after what `stream` held at the call and before what
+ * it is given next, also under HIP graph capture; calls from several host
+ * threads on one device are serialised between fork and join. */
 int moe_forward(const moe_shape* shape, const uint16_t* x, const float* w_router,
                 const float* bias, const uint16_t* w_gate_up, const uint16_t* w_down,
                 const void* packed_weights, const uint16_t* ws_gate_up, const uint16_t* ws_down,
@@ -310,7 +323,8 @@ int moe_forward(const moe_shape* shape, const uint16_t* x, const float* w_router
  * GPU's one array and leaves its contents behind (no step relies on them
  * being zero): calls that may overlap on one GPU -- on different streams,
  * or from different host threads -- race on it and must be serialised by
- * the caller. */
+ * the caller.  All its work, the shared expert's too, goes on `stream`: no
+ * stream or event is created. */
 int moe_forward_noalloc(const moe_shape* shape, const uint16_t* x, const float* w_router,
                         const float* bias, const uint16_t* w_gate_up, const uint16_t* w_down,
                         const void* packed_weights, const uint16_t* ws_gate_up,
