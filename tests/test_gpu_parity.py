@@ -447,14 +447,28 @@ def test_shared_stage(oracle_lib):
     gh.assert_close(out.cpu().numpy(), ref, "shared expert")
 
 
-def test_shared_overlap_back_to_back():
+OVERLAP = {
+    "shared": custom("ovl", T=700, H=512, E=16, k=4, I=256, I_shared=512),
+    # Zipf routing: the cold experts take the light loop, the rest heavy tiles
+    "light": custom("ovl_light", T=600, H=384, E=48, k=6, I=128, zipf_s=1.2, zipf_alpha=1.5),
+    "both": custom("ovl_both", T=600, H=384, E=48, k=6, I=128, I_shared=96, zipf_s=1.2,
+                   zipf_alpha=1.5),
+}
+
+
+@pytest.mark.parametrize("name", list(OVERLAP))
+def test_shared_overlap_back_to_back(name):
     """moe_forward runs the shared expert on a side stream that forks from
     the caller's stream before the router and joins before the combine.
     Four calls enqueued back to back on a non-default stream, each writing
     its own output (and the last two sharing one), with no host wait in
     between, must each equal the serial composition of the stages bit for
-    bit: shared expert into `out`, routed FFN, then the combine adding to it."""
-    cfg = custom("ovl", T=700, H=512, E=16, k=4, I=256, I_shared=512)
+    bit: shared expert into `out`, routed FFN, then the combine adding to it.
+    The layers: a shared expert with heavy experts only, and Zipf-routed
+    layers whose cold experts take the light loop, with and without a shared
+    expert."""
+    cfg = OVERLAP[name]
+    print(f"[case] overlap {name}", flush=True)
     lay = layer_on_gpu(cfg)
     s = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_shared)
     ws = moe.alloc_workspace(s)
@@ -468,11 +482,16 @@ def test_shared_overlap_back_to_back():
     sorted_ids = torch.empty((T * k,), dtype=torch.int32, device=gh.DEV)
     inv = torch.empty((T * k,), dtype=torch.int32, device=gh.DEV)
     moe.permute(s, ids, counts, offsets, sorted_ids, inv, ws)
+    if name != "shared":  # the layer really has experts of both kinds
+        c = counts.cpu().numpy()
+        light = moe.light_experts(c, s)
+        assert light.any() and (~light & (c > 0)).any(), c
     y = torch.empty((T * k, H), dtype=torch.float32, device=gh.DEV)
     moe.grouped_ffn(s, lay.x, sorted_ids, offsets, lay.w_gu, lay.w_dn, None, y, ws)
     ref = torch.empty((T, H), dtype=torch.float32, device=gh.DEV)
-    moe.shared_ffn(s, lay.x, lay.ws_gu, lay.ws_dn, ref, ws)
-    moe.combine(s, y, inv, w, True, ref)
+    if cfg.I_shared:
+        moe.shared_ffn(s, lay.x, lay.ws_gu, lay.ws_dn, ref, ws)
+    moe.combine(s, y, inv, w, bool(cfg.I_shared), ref)
     torch.cuda.synchronize()
     ref = ref.view(torch.int32).cpu()
     st = torch.cuda.Stream()
