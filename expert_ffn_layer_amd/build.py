@@ -26,6 +26,11 @@ SOURCES = ["router.hip", "permute.hip", "ffn.hip", "combine.hip", "mxfp8.hip", "
 # bits with the default build's to cover the cross-tile paths on small shapes.
 GRID16_LIB = os.path.join(PKG, "libmoe_grid16.so")
 GRID16_FLAGS = ["-DMOE_HEAVY_MAX_GRID=16"]
+# The same with the down GEMM's y written from registers instead of staged
+# through LDS: the build in which the down GEMM's cross-tile prefetch runs
+# (staging and the prefetch need the same LDS, so the default build stages).
+GRID16_NS_LIB = os.path.join(PKG, "libmoe_grid16_ns.so")
+GRID16_NS_FLAGS = ["-DMOE_HEAVY_MAX_GRID=16", "-DMOE_HEAVY_STAGED_EPI=0"]
 # Test variant: the light loop as one persistent gate|up -> down launch
 # (off in the default build; kept correct by tests/test_gpu_fused_light.py).
 FUSED_LIB = os.path.join(PKG, "libmoe_fusedlight.so")
@@ -66,11 +71,13 @@ def build(verbose: bool = False, out: str = LIB, objdir: str = OBJDIR, extra=())
 
 
 def build_all(verbose: bool = False) -> None:
-    """The library and its test variants (grid-capped heavy kernels, fused
-    light loop)."""
+    """The library and its test variants (grid-capped heavy kernels with the
+    down GEMM's y staged and unstaged, fused light loop)."""
     build(verbose=verbose)
     build(verbose=verbose, out=GRID16_LIB, objdir=os.path.join(OBJDIR, "grid16"),
           extra=GRID16_FLAGS)
+    build(verbose=verbose, out=GRID16_NS_LIB, objdir=os.path.join(OBJDIR, "grid16_ns"),
+          extra=GRID16_NS_FLAGS)
     build(verbose=verbose, out=FUSED_LIB, objdir=os.path.join(OBJDIR, "fused"),
           extra=FUSED_FLAGS)
 
