@@ -1114,38 +1114,52 @@ __device__ __forceinline__ int tile_tmi(const FfnArgs& a, int tile) {
 }
 
 // Order of the work items of one expert (its row tiles x N blocks, a
-// contiguous range of the work list): 0 = the N block runs fastest, 1 = the
-// row tile runs fastest (the row tiles that read one N block's weights are
-// then neighbours in the list, and so run at the same time).
-#ifndef MOE_HEAVY_ORDER
-#define MOE_HEAVY_ORDER 0
+// contiguous range of the work list), per GEMM: 0 = the N block runs
+// fastest, 1 = the row tile runs fastest (the row tiles that read one N
+// block's weights are then neighbours in the list, and so run at the same
+// time).  Measured at long prefill (three 224-row tiles per expert, 8 N
+// blocks of gate|up and 16 of down per row tile): gate|up with 1 fetches
+// 15.5 GB instead of 23.4 GB and runs 1-2% faster; down with 1 fetches
+// 5.8 GB instead of 10.5 GB but runs 3-4% slower (its 48 items per expert
+// then straddle two rounds of an XCD's blocks, and h rows are read again).
+// Results do not depend on it.
+#ifndef MOE_HEAVY_ORDER_GU
+#define MOE_HEAVY_ORDER_GU 1
+#endif
+#ifndef MOE_HEAVY_ORDER_DN
+#define MOE_HEAVY_ORDER_DN 0
 #endif
 
-// Row tile and N block of work item w.
+// Row tile and N block of work item w of GEMM M.  The expert-major order
+// (MOE_HEAVY_ORDER_* = 1) applies to experts whose items fit one round of an
+// XCD slice's blocks (num_cu / kXcds): their row tiles then run together and
+// share each N block's weights.  An expert with more tiles keeps the N block
+// fastest, so that each row tile's N blocks (which share its A rows) run
+// together instead of over several rounds.
+template <Mode M>
 __device__ __forceinline__ int item_tile(const FfnArgs& a, long long w, int nblk, int& nb) {
     const int tg = (int)(w / nblk);
-    if (MOE_HEAVY_ORDER == 0) {
+    if ((M == Mode::GateUp ? MOE_HEAVY_ORDER_GU : MOE_HEAVY_ORDER_DN) == 0 || !a.plan) {
         nb = (int)(w % nblk);
         return tg;
     }
-    // The expert of tile tg, its tile count and tg's index among its tiles
-    // (the split rule the plan applied); a dense group is one expert.
-    int t0, nt;
-    if (a.plan) {
-        const int base = kPlanHeader + a.E + 2 * tg;
-        const int e = sload(a.plan, base);
-        const int m0 = sload(a.plan, base + 1) & kTileRowMask;
-        const int n = sload(a.offsets, e + 1) - sload(a.offsets, e);
-        int main_tmi, last_tmi;
-        tile_split(n, sload(a.plan, 2), nt, main_tmi, last_tmi);
-        t0 = tg - m0 / tile_height(main_tmi);
-    } else {
-        t0 = 0;
-        nt = (a.dense_rows + a.dense_tm - 1) / a.dense_tm;
+    // The expert of tile tg, its tile count and tg's index among its tiles:
+    // an expert's tiles all have one height (tile_split), so first rows are
+    // multiples of it and the count is the rows over it, rounded up.
+    const int base = kPlanHeader + a.E + 2 * tg;
+    const int e = sload(a.plan, base);
+    const uint32_t ent = (uint32_t)sload(a.plan, base + 1);
+    const int tm = tile_height((int)(ent >> kTileTmShift));
+    const int n = sload(a.offsets, e + 1) - sload(a.offsets, e);
+    const int nt = (n + tm - 1) / tm;
+    if (nt * nblk > a.num_cu / kXcds) {
+        nb = (int)(w % nblk);
+        return tg;
     }
-    const long long q = w - (long long)t0 * nblk;
-    nb = (int)(q / nt);
-    return t0 + (int)(q % nt);
+    const int t0 = tg - (int)(ent & (uint32_t)kTileRowMask) / tm;
+    const int q = (int)(w - (long long)t0 * nblk);
+    nb = q / nt;
+    return t0 + q % nt;
 }
 
 // Runs this block's work items wi, wi + nb_x, ... (below wend) while their
@@ -1224,7 +1238,7 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
     // Where work item w sits (scalar reads only).
     auto locate = [&](long long w) -> Tile {
         Tile t;
-        const int tile = item_tile(a, w, nblk, t.nb);
+        const int tile = item_tile<M>(a, w, nblk, t.nb);
         if (a.plan) {
             const int base = kPlanHeader + a.E + 2 * tile;
             t.e = sload(a.plan, base);
@@ -1504,7 +1518,7 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
         const int t_nb = nb, t_base = r0 + m0, t_rows = rows;
         const long long wnext = wi + nb_x;
         int nb_next;
-        const bool more = wnext < wend && tile_tmi(a, item_tile(a, wnext, nblk, nb_next)) == kTmi;
+        const bool more = wnext < wend && tile_tmi(a, item_tile<M>(a, wnext, nblk, nb_next)) == kTmi;
         const bool pf = pf_ok && more;
         Tile nx{};
         if (pf) nx = locate(wnext);
@@ -1788,7 +1802,7 @@ __global__ __launch_bounds__(kHeavyThreads) void ffn_heavy_kernel(FfnArgs a) {
     long long wi = wbeg + jx;
     while (wi < wend) {
         int nb_i;
-        const int tmi = tile_tmi(a, item_tile(a, wi, nblk, nb_i));
+        const int tmi = tile_tmi(a, item_tile<M>(a, wi, nblk, nb_i));
         if constexpr (BS == kBRecMx) {
             // MXFP8 plans hold tiles of at most 192 rows (the larger bodies
             // spill); the host rejects a forced 224 or 256 with MXFP8 weights.
