@@ -507,6 +507,58 @@ def test_shared_overlap_back_to_back(name):
         assert torch.equal(o.view(torch.int32).cpu(), ref), f"call {i} differs from the stages"
 
 
+def test_shared_overlap_two_host_threads():
+    """Two host threads call moe_forward at once (ctypes releases the GIL),
+    each on its own stream with its own workspace and inputs, three calls
+    each with no wait in between: the library's side stream and its fork and
+    join events are shared per device, so the fork-to-join sections must
+    not interleave.  Every output equals the same call made alone."""
+    import threading
+
+    cfg = OVERLAP["both"]
+    lays = [layer_on_gpu(cfg, seed=s) for s in (11, 12)]
+    s = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_shared)
+
+    def call(lay, ws, out, stream=None):
+        moe.forward(s, lay.x, lay.wg, lay.bias, lay.w_gu, lay.w_dn, lay.ws_gu, lay.ws_dn, out, ws,
+                    stream=stream)
+
+    refs = []
+    for lay in lays:
+        ws = moe.alloc_workspace(s)
+        out = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=gh.DEV)
+        call(lay, ws, out)
+        torch.cuda.synchronize()
+        refs.append(out.view(torch.int32).cpu())
+    streams = [torch.cuda.Stream() for _ in lays]
+    outs = [[torch.full((cfg.T, cfg.H), float("nan"), device=gh.DEV) for _ in range(3)]
+            for _ in lays]
+    wss = [moe.alloc_workspace(s) for _ in lays]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    errors = []
+
+    def worker(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                for o in outs[i]:
+                    call(lays[i], wss[i], o, stream=streams[i])
+        except Exception as e:  # noqa: BLE001 -- reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for st in streams:
+        st.synchronize()
+    for i in range(2):
+        for j, o in enumerate(outs[i]):
+            assert torch.equal(o.view(torch.int32).cpu(), refs[i]), f"thread {i} call {j} differs"
+
+
 # ------------------------------------------------------------ properties
 def test_determinism_and_equivariance():
     cfg = SMALL["mixed"]
