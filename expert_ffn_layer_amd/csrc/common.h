@@ -17,12 +17,14 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t v16) {
     return __uint_as_float(v16 << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+typedef float floatx2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.  One
+// hardware conversion (v_cvt_pk_bf16_f32), no branch.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2_t{f, 0.0f}, bf16x2_t)) &
+           0xffffu;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -45,11 +47,19 @@ __device__ __forceinline__ floatx4_t mfma_16x16x32(bf16x8_t a, bf16x8_t b, float
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// SwiGLU of one (gate, up) pair.  Every path that produces h uses this one
-// function, so the light and heavy loops round identically.
+// SwiGLU of one (gate, up) pair: silu(g) * u, silu(g) = g / (1 + e^-g).
+// e^-g is taken as 2^(-g log2 e) on the hardware exp2 and the quotient as g
+// times the hardware reciprocal: about 1 ulp of fp32 each, far below the
+// bf16 rounding of h, in six instructions without a branch (a correctly
+// rounded expf and division take about 25, two of them on the
+// quarter-rate unit, and the heavy tiles run them for every h element
+// after their K loop).  e^-g = inf (g < -88) gives silu = g * 0 = -0, and
+// g = -inf gives NaN, as the quotient does.  Every path that produces h
+// uses this one function, so the light and heavy loops round identically.
 __device__ __forceinline__ float swiglu(float g, float u) {
 #pragma clang fp contract(off)
-    const float s = g / (1.0f + expf(-g));
+    const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
+    const float s = g * __builtin_amdgcn_rcpf(1.0f + e);
     return s * u;
 }
 

@@ -194,9 +194,7 @@ constexpr int kLightSubTiles = kLightRowsMax / 16;  // 4
 constexpr int kLightWideU = 2;                      // K steps in flight, wide branch
 
 // ------------------------------------------------------- y in 16 bits
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef float floatx2_t __attribute__((ext_vector_type(2)));
 
 // Storage of y (FfnArgs::y_fmt): fp32, bf16 or fp16.
 constexpr int kYF32 = 0, kYBF16 = 1, kYF16 = 2;
@@ -1708,19 +1706,28 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
             const int hc0 = t_nb * (kTN / 2) + wn * 32 + l16;
             uint16_t* hp = a.h + (size_t)(t_base + row0) * hstride + hc0;
             const bool full = t_rows == TM && t_nb * (kTN / 2) + kTN / 2 <= a.I;
+            // SwiGLU of every element first, with no branch around it (gate
+            // tile 2jp and up tile 2jp+1 hold the same (row, i) in the same
+            // lane; h overwrites the gate value), then the stores, each under
+            // its row and column predicate.  (Computed under the store's
+            // predicate, the per-element branches cost more than the work.)
+#pragma unroll
+            for (int i = 0; i < kRF; ++i)
+#pragma unroll
+                for (int jp = 0; jp < 2; ++jp)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[i][2 * jp][r] = swiglu(acc[i][2 * jp][r], acc[i][2 * jp + 1][r]);
 #pragma unroll
             for (int i = 0; i < kRF; ++i) {
 #pragma unroll
                 for (int jp = 0; jp < 2; ++jp) {
-                    // gate tile 2jp and up tile 2jp+1 hold the same (row, i)
-                    // in the same lane
-                    const floatx4_t up = acc[i][2 * jp + 1];
                     const bool col_ok = hc0 + jp * 16 < a.I;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int dr = i * 16 + r;
                         if (full || (row0 + dr < t_rows && col_ok)) {
-                            const float hv = swiglu(acc[i][2 * jp][r], up[r]);
+                            const float hv = acc[i][2 * jp][r];
                             const uint32_t hi = f32_to_bf16_bits(hv);
                             uint16_t* q = hp + (size_t)dr * hstride + jp * 16;
                             q[0] = (uint16_t)hi;

@@ -18,9 +18,6 @@ constexpr int BE = kRouterBE;
 constexpr int BK = kRouterBK;
 constexpr int LDK = BK + 8;  // bf16 row pitch in LDS (80 bytes): spreads rows over the banks
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float floatx2_t __attribute__((ext_vector_type(2)));
-
 // Two fp32 values -> three packed bf16 pairs with hi + mid + lo == v exactly
 // for normal v (each term is the round-to-nearest-even bf16 of the exact fp32
 // remainder of the previous ones; 8 + 8 + 8 significand bits cover fp32's 24).
