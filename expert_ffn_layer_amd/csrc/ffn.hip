@@ -1474,13 +1474,16 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
             raw[j] = *reinterpret_cast<const u32x4_t*>(base + (wn * 4 + j) * 16 * 64 + b8off);
         sc = *reinterpret_cast<const u32x2_t*>(base + kMxCodeBytes + (wn * 16 + l16) * 8);
     };
-    auto cvt_b8 = [&](const u32x4_t (&raw)[4], const u32x2_t& sc, bf16x8_t (&b0)[4],
-                      bf16x8_t (&b1)[4]) {
+    // One 32-wide half of the B fragments from the raw codes: half 0 is
+    // converted after the barrier (its MFMAs come first), half 1 behind the
+    // stage's first MFMA group, so that the two waves of a SIMD (which read
+    // the same fragments) do not stall their MFMAs on all of it at once.
+    auto cvt_b8 = [&](const u32x4_t (&raw)[4], const u32x2_t& sc, int half, bf16x8_t (&b)[4]) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const uint32_t sw = sc[j >> 1] >> (16 * (j & 1));
-            b0[j] = e4m3x8_to_bf16(raw[j][0], raw[j][1], sw & 0xffu);
-            b1[j] = e4m3x8_to_bf16(raw[j][2], raw[j][3], (sw >> 8) & 0xffu);
+            b[j] = half ? e4m3x8_to_bf16(raw[j][2], raw[j][3], (sw >> 8) & 0xffu)
+                        : e4m3x8_to_bf16(raw[j][0], raw[j][1], sw & 0xffu);
         }
     };
     // A fragments in two groups: rows [0, kG0) and [kG0, kRF).
@@ -1545,7 +1548,7 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
             ring_barrier();
             if constexpr (W8) {
                 read_b8(0, raw, sc);
-                cvt_b8(raw, sc, bf0, bf1);
+                cvt_b8(raw, sc, 0, bf0);
             } else {
                 read_b(0, 0, bf0);
             }
@@ -1566,7 +1569,10 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
             const int bn = (bs + 1 == bst) ? 0 : bs + 1;  // B slot of stage st+1
             const int an = (as + 1 == ast) ? 0 : as + 1;  // A slot of stage st+1
             mfma_rows(0, af, bf0);
-            if constexpr (!W8) read_b(bs, 1, bf1);  // W8: both halves came with stage st
+            if constexpr (W8)
+                cvt_b8(raw, sc, 1, bf1);  // raw: both halves came with stage st
+            else
+                read_b(bs, 1, bf1);
             read_a(as, 1, 0, af);
             mfma_rows(1, af, bf0);
             read_a(as, 1, 1, af);
@@ -1599,7 +1605,7 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
             read_a(an, 0, 0, af);
             mfma_rows(1, af, bf1);
             read_a(an, 0, 1, af);
-            if constexpr (W8) cvt_b8(raw, sc, bf0, bf1);
+            if constexpr (W8) cvt_b8(raw, sc, 0, bf0);
             bs = bn;
             as = an;
         }
