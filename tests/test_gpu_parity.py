@@ -377,6 +377,48 @@ def test_ffn_stage_rows(oracle_lib, yf):
         gh.assert_close(y_np[rows], ref, f"expert {e}")
 
 
+@pytest.mark.parametrize("lm", [64, 0])
+def test_swiglu_extreme_gates(oracle_lib, lm):
+    """Gate values out to about +-150: W_gate rows scaled by 128 and W_down by
+    1/8 (both exact in bf16; outputs stay of order 1, so the usual bar
+    applies).  Below g = -88.7 e^-g overflows fp32 and silu(g) is -0 (the
+    oracle's quotient g / inf, the kernels' g * rcp(inf)); just above it
+    1 / (1 + e^-g) falls below the normal range.  The light loop (lm = 64:
+    every expert has 17..64 rows, its wide branch) and the heavy tiles
+    (lm = 0) against the oracle's per-row expert FFN, fp32 y."""
+    print(f"[case] swiglu extreme gates lm={lm}", flush=True)
+    cfg = custom("gates", T=160, H=256, E=8, k=2, I=64)
+    lay = layer_on_gpu(cfg)
+    lay.w_gu[:, :cfg.I] *= 128
+    lay.w_dn *= 0.125
+    s = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, light_max_rows=lm)
+    ws = moe.alloc_workspace(s)
+    A = cfg.T * cfg.k
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=gh.DEV)
+    w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=gh.DEV)
+    moe.router(s, lay.x, lay.wg, lay.bias, ids, w, None, ws)
+    t = lambda n: torch.empty(n, dtype=torch.int32, device=gh.DEV)
+    counts, offsets, srt, inv = t(cfg.E), t(cfg.E + 1), t(A), t(A)
+    moe.permute(s, ids, counts, offsets, srt, inv, ws)
+    y = torch.empty((A, cfg.H), dtype=moe.y_dtype(s), device=gh.DEV)
+    moe.grouped_ffn(s, lay.x, srt, offsets, lay.w_gu, lay.w_dn, None, y, ws)
+    torch.cuda.synchronize()
+    off = offsets.cpu().numpy()
+    srt_np = srt.cpu().numpy()
+    y_np = y.float().cpu().numpy()
+    assert ((np.diff(off) > 16) & (np.diff(off) <= 64)).all()
+    overflow = 0
+    for e in range(cfg.E):
+        rows = np.arange(off[e], off[e + 1])
+        xr = lay.x[torch.as_tensor(srt_np[rows], device=gh.DEV)]
+        # gate values of these rows (to count the overflow region only)
+        g = xr.double() @ lay.w_gu[e, :cfg.I].double().T
+        overflow += int((g < -88.73).sum())
+        ref = oracle_lib.expert_ffn(xr, lay.w_gu[e], lay.w_dn[e])
+        gh.assert_close(y_np[rows], ref, f"expert {e}")
+    assert overflow > 50, overflow
+
+
 @pytest.mark.parametrize("T", [77, 600])
 @pytest.mark.parametrize("yf", ["fp32", "bf16", "fp16"])
 def test_combine_stage(T, yf):
