@@ -186,6 +186,16 @@ PROFILE_COMMANDS = (
 )
 
 
+def composite_lower_bound(router_bytes, router_flops, ffn_bytes, ffn_flops) -> float:
+    """Seconds a layer needs at the least when the router and then the FFN
+    each run at the roofline that binds them: max(router bytes / HBM peak,
+    router FLOPs / fp32 peak) + max(FFN bytes / HBM peak, FFN FLOPs / bf16
+    peak)."""
+    bw = HBM_PEAK_GBS * 1e9
+    return (max(router_bytes / bw, router_flops / (FP32_PEAK_TFLOPS * 1e12)) +
+            max(ffn_bytes / bw, ffn_flops / (BF16_PEAK_TFLOPS * 1e12)))
+
+
 def workload_of(cfg, weights: str) -> str:
     """Workload name: the layer's shape, plus the weight format when not bf16."""
     from expert_ffn_layer_amd import synth
@@ -551,8 +561,15 @@ def main():
         layer_bytes += 3 * H * cfg.I_shared * 2
     layer_flops = 6 * A * H * I + (6 * cfg.T * H * cfg.I_shared if cfg.I_shared else 0)
     t_step = ms_per_step / 1e3
+    # Composite bound: the router (x and W_g read; its FLOPs at the fp32
+    # peak, the precision it is defined in) followed by the FFN (touched and
+    # shared expert weights, out written; expert FLOPs at the bf16 peak),
+    # each at whichever of its two rooflines binds.
+    t_lb = composite_lower_bound(x_bytes + H * cfg.E * 4, 2 * cfg.T * H * cfg.E,
+                                 layer_bytes - x_bytes - H * cfg.E * 4, layer_flops)
     layer = dict(hbm_frac=round(layer_bytes / t_step / (HBM_PEAK_GBS * 1e9), 4),
                  mfma_frac=round(layer_flops / t_step / (BF16_PEAK_TFLOPS * 1e12), 4),
+                 composite_frac=round(t_lb / t_step, 4), composite_lb_us=round(t_lb * 1e6, 2),
                  algorithmic_bytes=int(layer_bytes), expert_flops=int(layer_flops),
                  touched_experts=touched, light_experts=light_experts)
 

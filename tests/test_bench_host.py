@@ -4,7 +4,8 @@
 * ``--summarize-mfma`` turns a kernel trace and a counter run into MFMA pipe
   occupancy: busy cycles over (GRBM_GUI_ACTIVE / 8 XCDs) x 256 CUs x 4 SIMDs,
   and the clock over the dispatch's own start-to-end time;
-* ``moe.light_experts`` follows the library's default rule.
+* ``moe.light_experts`` follows the library's default rule;
+* the composite layer bound adds the router's and the FFN's binding rooflines.
 """
 import csv
 import importlib.util
@@ -99,3 +100,22 @@ def test_light_rule_mirror():
     # a fixed threshold is taken as given
     s = moe.make_shape(100, 256, 512, 2, 64, light_max_rows=16)
     assert np.array_equal(moe.light_experts(counts, s), (counts >= 1) & (counts <= 16))
+
+
+def test_composite_lower_bound():
+    """The composite bound adds the router's and the FFN's binding rooflines:
+    decode-shaped numbers worked by hand (HBM 8 TB/s, fp32 157.3 TFLOP/s,
+    bf16 2.5 PFLOP/s)."""
+    b = load_bench()
+    # router: 512 KiB of x + 8 MiB of W_g (1.11 us at 8 TB/s) against
+    # 268 MFLOP at 157.3 TFLOP/s (1.71 us): the fp32 FLOPs bind
+    rb, rf = 64 * 4096 * 2 + 4096 * 512 * 4, 2 * 64 * 4096 * 512
+    t_router = max(rb / 8e12, rf / 157.3e12)
+    assert abs(t_router - rf / 157.3e12) < 1e-15  # 1.706 us, the FLOPs bind
+    # FFN: 368 touched experts x 24 MiB + out (HBM-bound)
+    fb, ff = 368 * 3 * 4096 * 1024 * 2 + 64 * 4096 * 4, 6 * 640 * 4096 * 1024
+    t_ffn = fb / 8e12
+    assert ff / 2.5e15 < t_ffn
+    assert abs(b.composite_lower_bound(rb, rf, fb, ff) - (t_router + t_ffn)) < 1e-12
+    # an FFN past the ridge takes its FLOPs term
+    assert abs(b.composite_lower_bound(0, 0, 1e6, 1e15) - 1e15 / 2.5e15) < 1e-12
