@@ -1591,19 +1591,30 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
             ring_barrier();
             // Refill the slot stage st used with stage st + depth; stages
             // past this tile's last are the next tile's.
-            if (st + depth < nst) {
-                issue(st + depth, rs);
-            } else if (pf) {
-                if (st + depth == nst) use_tile(nx);
-                issue(st + depth - nst, rs);
-            }
-            rs = (rs + 1 == depth) ? 0 : rs + 1;
+            auto refill = [&]() {
+                if (st + depth < nst) {
+                    issue(st + depth, rs);
+                } else if (pf) {
+                    if (st + depth == nst) use_tile(nx);
+                    issue(st + depth - nst, rs);
+                }
+                rs = (rs + 1 == depth) ? 0 : rs + 1;
+            };
+            // MXFP8 tiles (half the weight bytes per stage, so the MFMAs are
+            // the longer part) issue the refill after the MFMA group below:
+            // the group then starts at once after the barrier instead of
+            // behind the DMA issue (measured on MI355X: gate|up -4.5% at
+            // prefill, -7% skew, -3.5% long prefill).  bf16 tiles keep the
+            // earlier issue (late: -1% at prefill, +2% at long prefill).
+            constexpr bool kLate = W8;
+            if (!kLate) refill();
             if constexpr (W8)
                 read_b8(bn, raw, sc);
             else
                 read_b(bn, 0, bf0);
             read_a(an, 0, 0, af);
             mfma_rows(1, af, bf1);
+            if (kLate) refill();
             read_a(an, 0, 1, af);
             if constexpr (W8) cvt_b8(raw, sc, 0, bf0);
             bs = bn;
