@@ -1600,21 +1600,25 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
                 }
                 rs = (rs + 1 == depth) ? 0 : rs + 1;
             };
-            // MXFP8 tiles (half the weight bytes per stage, so the MFMAs are
-            // the longer part) issue the refill after the MFMA group below:
-            // the group then starts at once after the barrier instead of
-            // behind the DMA issue (measured on MI355X: gate|up -4.5% at
-            // prefill, -7% skew, -3.5% long prefill).  bf16 tiles keep the
-            // earlier issue (late: -1% at prefill, +2% at long prefill).
-            constexpr bool kLate = W8;
-            if (!kLate) refill();
+            // The weight (B) waves, and for MXFP8 tiles (half the weight
+            // bytes per stage, so the MFMAs are the longer part) the A waves
+            // too, issue the refill after the MFMA group below: the group
+            // then starts at once after the barrier instead of behind the
+            // DMA issue.  bf16 A waves refill first: 192- to 256-row tiles
+            // keep a 2-deep A ring, whose one stage of lead a late issue
+            // shortens.  (Measured on MI355X, two interleaved runs: bf16
+            // long prefill gate|up -4%, prefill 0..-3%, skew and Ling-like
+            // unchanged, against +2% at long prefill with every wave late;
+            // MXFP8 gate|up -4.5% at prefill, -7% skew, -3.5% long prefill.)
+            const bool late = W8 || !a_role;  // wave-uniform
+            if (!late) refill();
             if constexpr (W8)
                 read_b8(bn, raw, sc);
             else
                 read_b(bn, 0, bf0);
             read_a(an, 0, 0, af);
             mfma_rows(1, af, bf1);
-            if (kLate) refill();
+            if (late) refill();
             read_a(an, 0, 1, af);
             if constexpr (W8) cvt_b8(raw, sc, 0, bf0);
             bs = bn;
