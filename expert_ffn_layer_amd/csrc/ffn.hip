@@ -1600,17 +1600,18 @@ __device__ __forceinline__ long long ffn_heavy_run(const FfnArgs& a, char* lds, 
                 }
                 rs = (rs + 1 == depth) ? 0 : rs + 1;
             };
-            // The weight (B) waves, and for MXFP8 tiles (half the weight
-            // bytes per stage, so the MFMAs are the longer part) the A waves
-            // too, issue the refill after the MFMA group below: the group
-            // then starts at once after the barrier instead of behind the
-            // DMA issue.  bf16 A waves refill first: 192- to 256-row tiles
-            // keep a 2-deep A ring, whose one stage of lead a late issue
-            // shortens.  (Measured on MI355X, two interleaved runs: bf16
-            // long prefill gate|up -4%, prefill 0..-3%, skew and Ling-like
-            // unchanged, against +2% at long prefill with every wave late;
-            // MXFP8 gate|up -4.5% at prefill, -7% skew, -3.5% long prefill.)
-            const bool late = W8 || !a_role;  // wave-uniform
+            // The weight (B) waves, and the A waves of tiles with a 3-deep A
+            // ring (MXFP8 tiles, bf16 160- and 128-row tiles), issue the
+            // refill after the MFMA group below: the group then starts at
+            // once after the barrier instead of behind the DMA issue.  A
+            // waves with a 2-deep ring (bf16 192- to 256-row tiles) refill
+            // first: a late issue shortens their one stage of lead.
+            // (Measured on MI355X, two interleaved runs each: bf16 long
+            // prefill gate|up -4% with the B waves late, against +2% with
+            // every wave late; prefill -1.7% more with the 3-deep A waves
+            // late; MXFP8 gate|up -4.5% at prefill, -7% skew, -3.5% long
+            // prefill.)
+            const bool late = !a_role || ast >= 3;  // wave-uniform
             if (!late) refill();
             if constexpr (W8)
                 read_b8(bn, raw, sc);
